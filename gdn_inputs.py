@@ -1,0 +1,140 @@
+"""Seeded synthetic inputs for the gated-delta-rule workloads.
+
+This module only draws random numbers in the shapes and distributions of the
+workloads; it holds none of the recurrence's arithmetic.  Both the GPU tests
+and the CPU oracle consume its output, so the two sides always see the same
+values.
+
+The pages describe the models only as 400M-1.3B-parameter Gated DeltaNet
+layers and print no shapes, so the shapes below stand in for them (one
+attention-sized layer: 16 heads of width 128 at 1.3B, 8 heads of width 64
+for a mid-sized one).  Recipe per workload (numpy PCG64, seed 58000 + id,
+draw order: packed lengths (if any), q, k, v, beta logits, alpha logits, S0):
+
+* q, k ~ N(0,1), L2-normalised per (token, head) over d_k in fp64 (no
+  epsilon), then cast to the I/O dtype with round-to-nearest-even;
+* v ~ N(0,1), cast the same way;
+* beta = sigmoid(x), x ~ N(0,1), fp32;
+* log alpha = -softplus(x), x ~ N(mu,1) (mu = 0 for the tiny and mid
+  workloads, 1 for the 1.3B-shaped ones), fp32, so alpha is in (0,1);
+* S0 = 0, or ~ N(0, 0.1^2) in fp32 where the workload starts from a state.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+SEED_BASE = 58000
+
+WORKLOADS = {
+    0: dict(name="tiny-f32", B=1, T=64, H=1, dk=16, dv=16, chunk=16,
+            dtype="f32", alpha_mu=0.0, s0_std=0.0),
+    1: dict(name="mid-bf16", B=4, T=2048, H=8, dk=64, dv=64, chunk=64,
+            dtype="bf16", alpha_mu=0.0, s0_std=0.1),
+    2: dict(name="1.3b-layer-bf16", B=8, T=4096, H=16, dk=128, dv=128,
+            chunk=64, dtype="bf16", alpha_mu=1.0, s0_std=0.0),
+    3: dict(name="varlen-long-bf16", n_seqs=8, total=65536, lmin=1024,
+            lmax=16384, H=16, dk=128, dv=128, chunk=64, dtype="bf16",
+            alpha_mu=1.0, s0_std=0.0),
+    4: dict(name="decode-b64", B=64, H=16, dk=128, dv=128, steps=256,
+            dtype="bf16", alpha_mu=1.0, s0_std=0.1),
+}
+
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _cast(x: np.ndarray, dtype: str) -> torch.Tensor:
+    return torch.from_numpy(x).to(TORCH_DTYPE[dtype])
+
+
+def _unit_rows(rng: np.random.Generator, shape) -> np.ndarray:
+    x = rng.standard_normal(shape)
+    x /= np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def _neg_softplus(x: np.ndarray) -> np.ndarray:
+    return -(np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x))))
+
+
+def packed_lengths(rng: np.random.Generator, n: int, total: int, lo: int,
+                   hi: int) -> list[int]:
+    """n lengths in [lo, hi] summing to total: draw n-1 uniformly, set the
+    last to the remainder, redraw all while the remainder is out of range."""
+    while True:
+        head = rng.integers(lo, hi + 1, size=n - 1)
+        last = total - int(head.sum())
+        if lo <= last <= hi:
+            return [int(x) for x in head] + [last]
+
+
+def chunk_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16",
+                 alpha_mu: float = 1.0, s0_std: float = 0.0, seed: int = 0,
+                 cu_seqlens=None, rng: np.random.Generator | None = None):
+    """Inputs of one chunked forward.  With cu_seqlens (B must be 1) S0 has one
+    state per packed sequence.  Returns a dict of CPU torch tensors."""
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    q = _cast(_unit_rows(rng, (B, T, H, dk)), dtype)
+    k = _cast(_unit_rows(rng, (B, T, H, dk)), dtype)
+    v = _cast(rng.standard_normal((B, T, H, dv)), dtype)
+    beta = torch.from_numpy(_sigmoid(rng.standard_normal((B, T, H)))).float()
+    log_alpha = torch.from_numpy(
+        _neg_softplus(rng.normal(alpha_mu, 1.0, (B, T, H)))).float()
+    units = B if cu_seqlens is None else len(cu_seqlens) - 1
+    S0 = None
+    if s0_std > 0:
+        S0 = torch.from_numpy(rng.normal(0.0, s0_std, (units, H, dv, dk))).float()
+    cu = None
+    if cu_seqlens is not None:
+        cu = torch.tensor(list(cu_seqlens), dtype=torch.int32)
+    return dict(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, S0=S0,
+                cu_seqlens=cu)
+
+
+def decode_inputs(B: int, H: int, dk: int, dv: int, steps: int,
+                  dtype: str = "bf16", alpha_mu: float = 1.0,
+                  s0_std: float = 0.1, seed: int = 0):
+    """Inputs of `steps` consecutive decode steps: q,k [steps,B,H,dk],
+    v [steps,B,H,dv], gates [steps,B,H], initial state [B,H,dv,dk]."""
+    rng = np.random.default_rng(seed)
+    q = _cast(_unit_rows(rng, (steps, B, H, dk)), dtype)
+    k = _cast(_unit_rows(rng, (steps, B, H, dk)), dtype)
+    v = _cast(rng.standard_normal((steps, B, H, dv)), dtype)
+    beta = torch.from_numpy(_sigmoid(rng.standard_normal((steps, B, H)))).float()
+    log_alpha = torch.from_numpy(
+        _neg_softplus(rng.normal(alpha_mu, 1.0, (steps, B, H)))).float()
+    S0 = torch.from_numpy(rng.normal(0.0, s0_std, (B, H, dv, dk))).float()
+    return dict(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, S0=S0)
+
+
+def workload_inputs(wid: int):
+    """The full-size inputs of workload `wid` (0-4)."""
+    w = WORKLOADS[wid]
+    seed = SEED_BASE + wid
+    if wid == 4:
+        return decode_inputs(w["B"], w["H"], w["dk"], w["dv"], w["steps"],
+                             w["dtype"], w["alpha_mu"], w["s0_std"], seed)
+    if wid == 3:
+        rng = np.random.default_rng(seed)
+        lens = packed_lengths(rng, w["n_seqs"], w["total"], w["lmin"], w["lmax"])
+        cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+        return chunk_inputs(1, w["total"], w["H"], w["dk"], w["dv"],
+                            w["dtype"], w["alpha_mu"], w["s0_std"],
+                            cu_seqlens=cu, rng=rng)
+    return chunk_inputs(w["B"], w["T"], w["H"], w["dk"], w["dv"], w["dtype"],
+                        w["alpha_mu"], w["s0_std"], seed)
+
+
+def max_rel_err(x, ref) -> float:
+    """max |x - ref| / RMS(ref), both upcast to fp64 (the parity statistic)."""
+    x = np.asarray(x.detach().cpu().double().numpy() if hasattr(x, "detach") else x,
+                   dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    if rms == 0.0:
+        return float(np.max(np.abs(x - ref))) if x.size else 0.0
+    return float(np.max(np.abs(x - ref)) / rms) if x.size else 0.0
