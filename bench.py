@@ -1,0 +1,218 @@
+"""Benchmark of the gated-delta-rule hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one gdn_chunk_fwd over the 1.3B-layer-shaped workload (B=8,
+T=4096, H=16, d_k=d_v=128, chunk 64, bf16 q/k/v, fp32 gates, fp32 o and
+state) with every input already resident in HBM.  The JSON line reports:
+  value       whole-job tokens/s (B*T tokens per step);
+  roofline    the chunk kernel against the HBM roofline (its algorithmic
+              arithmetic intensity is below the bf16 MFMA ridge point), with
+              the launch time measured by HIP events on the launch stream;
+  mfma        the same launches against the dense bf16 MFMA peak;
+  decode      gdn_step on B=64, H=16, d=128 (fp32 state in place): HBM GB/s
+              with the state evicted from the caches before each step
+              ("cold"), and back to back ("warm");
+  cpu_baseline the fp64 CPU oracle timed on a bounded sample of the same
+              workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "gated-delta chunk-fwd tokens/s at B8 T4096 H16 d128; % MFMA peak; decode GB/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, published
+PMC_FILE = os.path.join(ROOT, "profiles", "chunk_mfma_b8_t4096_h16_d128_traffic.json")
+
+
+def flops_per_token_head(C: int, dk: int, dv: int) -> float:
+    """Algorithmic flops of the chunk algorithm per (token, head): K K^T
+    (strict lower), forward substitution, U, W, Delta + state update + Q S^T,
+    Q K^T (with diagonal) and P Delta; 2 flops per multiply-add."""
+    L, Lp = C * (C - 1) // 2, C * (C + 1) // 2
+    macs = (L * dk + C * (C - 1) * (C - 2) // 6 + L * dv + L * dk + 3 * C * dk * dv
+            + Lp * dk + Lp * dv)
+    return 2.0 * macs / C
+
+
+def bytes_chunk_fwd(B, T, H, dk, dv, io_bytes=2, o_bytes=4, with_s0=False) -> float:
+    """Algorithmic HBM bytes of one forward: q, k, v, gates read once, o and
+    the final states written once (initial states read once if given)."""
+    per_th = (2 * dk + dv) * io_bytes + dv * o_bytes + 8
+    states = B * H * dv * dk * 4 * (2 if with_s0 else 1)
+    return B * T * H * per_th + states
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--cold-steps", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=2,
+                    help="batch rows of the workload the CPU oracle runs")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the "
+              "path has no multi-GPU component to measure.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gdn_inputs as gi
+    import gated_delta_rule_58_amd as gdn
+
+    dev = "cuda:0"
+    w = gi.WORKLOADS[2]
+    B, T, H, dk, dv, C = w["B"], w["T"], w["H"], w["dk"], w["dv"], w["chunk"]
+    print(f"[bench] inputs: workload 2 {w['name']} B={B} T={T} H={H} d={dk}", file=sys.stderr,
+          flush=True)
+    host = gi.workload_inputs(2)
+    d = {k: (v.to(dev) if v is not None else None) for k, v in host.items()}
+    o = torch.empty((B, T, H, dv), device=dev, dtype=torch.float32)
+    st = torch.empty((B, H, dv, dk), device=dev, dtype=torch.float32)
+
+    def step():
+        gdn.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"],
+                      chunk=C, o=o, S_T=st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {args.steps} chunk_fwd steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    tokens = B * T
+    value = tokens / (ms * 1e-3)
+
+    nbytes = bytes_chunk_fwd(B, T, H, dk, dv, with_s0=d["S0"] is not None)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    fl = flops_per_token_head(C, dk, dv) * B * T * H
+    tfs = fl / (ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(PMC_FILE):
+        with open(PMC_FILE) as f:
+            traffic = json.load(f).get("hbm_bytes_per_launch")
+
+    # ---------------- decode (gdn_step) ----------------
+    wd = gi.WORKLOADS[4]
+    print("[bench] decode: workload 4", file=sys.stderr, flush=True)
+    dh = gi.workload_inputs(4)
+    dd = {k: v.to(dev) for k, v in dh.items()}
+    S = dd["S0"].clone()
+    Bd, Hd = wd["B"], wd["H"]
+    od = torch.empty((Bd, Hd, wd["dv"]), device=dev, dtype=torch.float32)
+    nsteps = min(args.decode_steps, wd["steps"])
+
+    def dstep(t):
+        gdn.step(dd["q"][t], dd["k"][t], dd["v"][t], dd["log_alpha"][t], dd["beta"][t], S, o=od)
+
+    for t in range(4):
+        dstep(t)
+    torch.cuda.synchronize()
+    S.copy_(dd["S0"])
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for t in range(nsteps):
+        dstep(t)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm_us = e0.elapsed_time(e1) * 1e3 / nsteps
+    flush = torch.empty(1 << 28, device=dev, dtype=torch.float32)   # 1 GiB > MALL + L2
+    cold = []
+    for t in range(args.cold_steps):
+        flush.fill_(float(t))
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ea.record(stream)
+        dstep(t)
+        eb.record(stream)
+        torch.cuda.synchronize()
+        cold.append(ea.elapsed_time(eb) * 1e3)
+    del flush
+    cold.sort()
+    cold_us = cold[len(cold) // 2]
+    dbytes = (2 * Bd * Hd * wd["dv"] * wd["dk"] * 4 + Bd * Hd * (2 * wd["dk"] + wd["dv"]) * 2
+              + Bd * Hd * wd["dv"] * 4 + Bd * Hd * 8)
+    decode = {
+        "workload": f"{wd['name']}: B={Bd} H={Hd} d_k=d_v={wd['dk']}, bf16 q/k/v, fp32 state",
+        "bytes_per_step": dbytes,
+        "us_per_step_cold": round(cold_us, 2),
+        "GB_s_cold": round(dbytes / (cold_us * 1e-6) / 1e9, 1),
+        "frac_hbm_cold": round(dbytes / (cold_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "us_per_step_warm": round(warm_us, 2),
+        "GB_s_warm": round(dbytes / (warm_us * 1e-6) / 1e9, 1),
+        "note": "cold = 1 GiB cache-evicting write before each timed step (median of "
+                f"{args.cold_steps}); warm = {nsteps} steps back to back, state resident in MALL",
+    }
+
+    # ---------------- CPU oracle baseline ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = max(1, min(args.cpu_rows, B))
+        threads = min(16, os.cpu_count() or 1)
+        print(f"[bench] cpu baseline: oracle on {rows} batch row(s), {threads} threads",
+              file=sys.stderr, flush=True)
+        sub = {k: (v[:rows] if v is not None else None) for k, v in host.items()
+               if k != "cu_seqlens"}
+        c0 = time.perf_counter()
+        oracle.fwd(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["beta"], sub["S0"],
+                   threads=threads)
+        ct = time.perf_counter() - c0
+        cpu = {"value": round(rows * T / ct, 1), "unit": "tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{rows} of {B} batch rows (all {H} heads x {T} tokens), fp64 "
+                         f"token recurrence, {ct:.2f} s wall"}
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w['name']}: B={B} T={T} H={H} d_k=d_v={dk} chunk={C}, "
+                               "bf16 q/k/v, fp32 gates/state/o",
+                   "global_batch": B, "seq_len": T, "heads": H, "d_k": dk, "d_v": dv,
+                   "chunk": C, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "chunk_mfma_kernel<128,float>",
+                     "algorithmic_bytes": nbytes},
+        "mfma": {"achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                 "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "algorithmic_flops": fl},
+        "decode": decode,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+"""ctypes binding of libgdn.so (argument marshalling only).
+
+Every computation happens in the library's HIP kernels; this module only
+checks torch tensor shapes/dtypes, allocates outputs with torch (device
+memory is PyTorch's job) and passes raw device pointers and the current
+HIP stream to the C ABI declared in include/gdn.h.  If the library is not
+built, every call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+_DTYPE = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
+
+# symbol -> (restype, argtypes); this is the whole exported surface of gdn.h
+_c_int, _vp, _sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+
+
+class GdnShape(ctypes.Structure):
+    _fields_ = [("B", _c_int), ("T", _c_int), ("H", _c_int), ("d_k", _c_int),
+                ("d_v", _c_int), ("chunk", _c_int), ("n_seqs", _c_int),
+                ("io_dtype", _c_int), ("o_dtype", _c_int)]
+
+
+SYMBOLS = {
+    "gdn_chunk_fwd_workspace_size": (_c_int, [ctypes.POINTER(GdnShape),
+                                              ctypes.POINTER(_sz)]),
+    "gdn_chunk_fwd": (_c_int, [ctypes.POINTER(GdnShape), _vp, _vp, _vp, _vp, _vp,
+                               _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "gdn_step": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp,
+                          _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "gdn_last_error": (ctypes.c_char_p, []),
+    "gdn_version": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"gdn error {code}: {msg}")
+        self.code = code
+
+
+def lib():
+    """Load libgdn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m gated_delta_rule_58_amd.build` (there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SYMBOLS.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def version() -> str:
+    return lib().gdn_version().decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise GdnError(rc, lib().gdn_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need_cuda(name, t, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def chunk_fwd_workspace_size(B, T, H, d_k, d_v, chunk=64, n_seqs=0,
+                             io_dtype=torch.bfloat16, o_dtype=torch.float32) -> int:
+    shape = GdnShape(B, T, H, d_k, d_v, chunk, n_seqs, _DTYPE[io_dtype], _DTYPE[o_dtype])
+    out = ctypes.c_size_t(0)
+    _check(lib().gdn_chunk_fwd_workspace_size(ctypes.byref(shape), ctypes.byref(out)))
+    return out.value
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, chunk=64,
+              o_dtype=torch.float32, o=None, S_T=None, want_state=True):
+    """Chunkwise forward.  q,k [B,T,H,dk]; v [B,T,H,dv]; log_alpha, beta
+    [B,T,H] fp32; S0 [U,H,dv,dk] fp32 or None; cu_seqlens int32 [N+1] (device)
+    or None.  Returns (o, S_T) (S_T is None when want_state is False)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    io = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need_cuda(name, t, io)
+    for name, t in (("log_alpha", log_alpha), ("beta", beta)):
+        _need_cuda(name, t, torch.float32)
+        if tuple(t.shape) != (B, T, H):
+            raise ValueError(f"{name} must be [B,T,H]")
+    if tuple(k.shape) != (B, T, H, dk) or tuple(v.shape[:3]) != (B, T, H):
+        raise ValueError("q, k, v shapes disagree")
+    n_seqs = 0
+    if cu_seqlens is not None:
+        _need_cuda("cu_seqlens", cu_seqlens, torch.int32)
+        n_seqs = cu_seqlens.shape[0] - 1
+    units = n_seqs if n_seqs > 0 else B
+    if S0 is not None:
+        _need_cuda("S0", S0, torch.float32)
+        if tuple(S0.shape) != (units, H, dv, dk):
+            raise ValueError(f"S0 must be [{units},{H},{dv},{dk}]")
+    if o is None:
+        o = torch.empty((B, T, H, dv), device=q.device, dtype=o_dtype)
+    if S_T is None and want_state:
+        S_T = torch.empty((units, H, dv, dk), device=q.device, dtype=torch.float32)
+    shape = GdnShape(B, T, H, dk, dv, chunk, n_seqs, _DTYPE[io], _DTYPE[o.dtype])
+    ws_bytes = ctypes.c_size_t(0)
+    _check(lib().gdn_chunk_fwd_workspace_size(ctypes.byref(shape), ctypes.byref(ws_bytes)))
+    ws = None
+    if ws_bytes.value:
+        ws = torch.empty(ws_bytes.value, device=q.device, dtype=torch.uint8)
+    _check(lib().gdn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
+                               _ptr(o), _ptr(S_T), _ptr(ws), ws_bytes.value,
+                               _stream(q.device)))
+    return o, S_T
+
+
+def step(q, k, v, log_alpha, beta, S, o_dtype=torch.float32, o=None):
+    """One decode step.  q,k [B,H,dk]; v [B,H,dv]; gates [B,H] fp32; S
+    [B,H,dv,dk] fp32, updated in place.  Returns o [B,H,dv]."""
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    io = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need_cuda(name, t, io)
+    for name, t in (("log_alpha", log_alpha), ("beta", beta), ("S", S)):
+        _need_cuda(name, t, torch.float32)
+    if tuple(S.shape) != (B, H, dv, dk):
+        raise ValueError("S must be [B,H,dv,dk]")
+    if o is None:
+        o = torch.empty((B, H, dv), device=q.device, dtype=o_dtype)
+    _check(lib().gdn_step(B, H, dk, dv, _DTYPE[io], _DTYPE[o.dtype], _ptr(q), _ptr(k),
+                          _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(o),
+                          _stream(q.device)))
+    return o

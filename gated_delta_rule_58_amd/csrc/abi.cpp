@@ -1,0 +1,164 @@
+// C ABI of libgdn.so: host-side validation and kernel dispatch.  Every check
+// runs before anything is enqueued, so a rejected call has no effect.
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+namespace gdn {
+hipError_t launch_step(int B, int H, int DK, int DV, bool io_bf16, bool o_bf16,
+                       const void *q, const void *k, const void *v, const float *la,
+                       const float *beta, float *S, void *o, hipStream_t st);
+bool chunk_f32_supported(int dk, int dv, int chunk);
+hipError_t launch_chunk_f32(int units, int T, int H, int dk, int chunk, bool o_bf16,
+                            const int32_t *cu, const void *q, const void *k, const void *v,
+                            const float *la, const float *beta, const float *S0, void *o,
+                            float *S_T, hipStream_t st);
+bool chunk_mfma_supported(int dk, int dv, int chunk);
+hipError_t launch_chunk_mfma(int units, int T, int H, int dk, bool o_bf16, const int32_t *cu,
+                             const void *q, const void *k, const void *v, const float *la,
+                             const float *beta, const float *S0, void *o, float *S_T,
+                             hipStream_t st);
+}  // namespace gdn
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return GDN_OK;
+}
+
+bool misaligned(const void *p) {
+    return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) != 0;
+}
+
+bool valid_dtype(int d) { return d == GDN_F32 || d == GDN_BF16; }
+
+// Shape checks shared by the workspace query and the forward call.
+int check_shape(const gdn_shape *s) {
+    if (!s) return fail(GDN_ERR_INVALID_ARG, "shape is NULL");
+    if (s->B <= 0 || s->H <= 0 || s->T < 0 || s->d_k <= 0 || s->d_v <= 0 || s->chunk <= 0)
+        return fail(GDN_ERR_INVALID_ARG,
+                    "bad dimensions B=%d T=%d H=%d d_k=%d d_v=%d chunk=%d (need B,H,d_k,d_v,chunk > 0, T >= 0)",
+                    s->B, s->T, s->H, s->d_k, s->d_v, s->chunk);
+    if (s->n_seqs < 0) return fail(GDN_ERR_INVALID_ARG, "n_seqs=%d is negative", s->n_seqs);
+    if (s->n_seqs > 0 && s->B != 1)
+        return fail(GDN_ERR_INVALID_ARG, "packed sequences (n_seqs=%d) need B == 1, got B=%d",
+                    s->n_seqs, s->B);
+    if (!valid_dtype(s->io_dtype) || !valid_dtype(s->o_dtype))
+        return fail(GDN_ERR_INVALID_ARG, "io_dtype=%d / o_dtype=%d is not a gdn_dtype",
+                    s->io_dtype, s->o_dtype);
+    const long units = s->n_seqs > 0 ? s->n_seqs : s->B;
+    if ((long)units * s->H > (1L << 28))
+        return fail(GDN_ERR_INVALID_ARG, "units x heads = %ld is too large", units * (long)s->H);
+    const bool ok_inst = s->io_dtype == GDN_BF16
+                             ? gdn::chunk_mfma_supported(s->d_k, s->d_v, s->chunk)
+                             : gdn::chunk_f32_supported(s->d_k, s->d_v, s->chunk);
+    if (!ok_inst)
+        return fail(GDN_ERR_UNSUPPORTED,
+                    "no kernel for d_k=%d d_v=%d chunk=%d io_dtype=%s (bf16: d_k=d_v in {64,128}, "
+                    "chunk 64; f32: d_k=d_v in {16,32,64}, chunk in {16,32,64})",
+                    s->d_k, s->d_v, s->chunk, s->io_dtype == GDN_BF16 ? "bf16" : "f32");
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_last_error(void) { return g_last_error.c_str(); }
+
+const char *gdn_version(void) { return "gdn-mi355x 0.1.0 (gfx950)"; }
+
+int gdn_chunk_fwd_workspace_size(const gdn_shape *shape, size_t *bytes) {
+    if (!bytes) return fail(GDN_ERR_INVALID_ARG, "bytes is NULL");
+    const int rc = check_shape(shape);
+    if (rc != GDN_OK) return rc;
+    *bytes = 0;
+    return ok();
+}
+
+int gdn_chunk_fwd(const gdn_shape *s, const void *q, const void *k, const void *v,
+                  const float *log_alpha, const float *beta, const float *S0,
+                  const int32_t *cu_seqlens, void *o, float *S_T, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    int rc = check_shape(s);
+    if (rc != GDN_OK) return rc;
+    if (s->n_seqs > 0 && !cu_seqlens)
+        return fail(GDN_ERR_INVALID_ARG, "n_seqs=%d but cu_seqlens is NULL", s->n_seqs);
+    if (s->n_seqs == 0 && cu_seqlens)
+        return fail(GDN_ERR_INVALID_ARG, "cu_seqlens given but n_seqs is 0");
+    if (s->T > 0 && (!q || !k || !v || !log_alpha || !beta || !o))
+        return fail(GDN_ERR_INVALID_ARG, "q, k, v, log_alpha, beta and o are required when T > 0");
+    const void *ptrs[] = {q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, workspace};
+    const char *names[] = {"q", "k", "v", "log_alpha", "beta", "S0", "cu_seqlens", "o", "S_T",
+                           "workspace"};
+    for (int i = 0; i < 10; ++i)
+        if (misaligned(ptrs[i]))
+            return fail(GDN_ERR_ALIGNMENT, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
+    if (o && (o == q || o == k || o == v))
+        return fail(GDN_ERR_INVALID_ARG, "o must not alias q, k or v");
+    size_t need = 0;
+    gdn_chunk_fwd_workspace_size(s, &need);
+    if (workspace_bytes < need)
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    if (s->T == 0 && !S_T) return ok();   // nothing to produce
+
+    const int units = s->n_seqs > 0 ? s->n_seqs : s->B;
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const bool o_bf16 = s->o_dtype == GDN_BF16;
+    hipError_t e;
+    if (s->io_dtype == GDN_BF16)
+        e = gdn::launch_chunk_mfma(units, s->T, s->H, s->d_k, o_bf16, cu_seqlens, q, k, v,
+                                   log_alpha, beta, S0, o, S_T, st);
+    else
+        e = gdn::launch_chunk_f32(units, s->T, s->H, s->d_k, s->chunk, o_bf16, cu_seqlens, q, k,
+                                  v, log_alpha, beta, S0, o, S_T, st);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int gdn_step(int B, int H, int d_k, int d_v, int io_dtype, int o_dtype, const void *q,
+             const void *k, const void *v, const float *log_alpha, const float *beta, float *S,
+             void *o, void *stream) {
+    if (B <= 0 || H <= 0 || d_k <= 0 || d_v <= 0)
+        return fail(GDN_ERR_INVALID_ARG, "bad dimensions B=%d H=%d d_k=%d d_v=%d", B, H, d_k, d_v);
+    if (!valid_dtype(io_dtype) || !valid_dtype(o_dtype))
+        return fail(GDN_ERR_INVALID_ARG, "io_dtype=%d / o_dtype=%d is not a gdn_dtype", io_dtype,
+                    o_dtype);
+    if ((long)B * H > (1L << 30))
+        return fail(GDN_ERR_INVALID_ARG, "B x H = %ld is too large", (long)B * H);
+    if (d_k != 64 && d_k != 128)
+        return fail(GDN_ERR_UNSUPPORTED, "no decode kernel for d_k=%d (64 or 128)", d_k);
+    if (!q || !k || !v || !log_alpha || !beta || !S || !o)
+        return fail(GDN_ERR_INVALID_ARG, "every pointer of gdn_step is required");
+    const void *ptrs[] = {q, k, v, log_alpha, beta, S, o};
+    const char *names[] = {"q", "k", "v", "log_alpha", "beta", "S", "o"};
+    for (int i = 0; i < 7; ++i)
+        if (misaligned(ptrs[i]))
+            return fail(GDN_ERR_ALIGNMENT, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
+    if (o == (void *)S) return fail(GDN_ERR_INVALID_ARG, "o must not alias S");
+    const hipError_t e =
+        gdn::launch_step(B, H, d_k, d_v, io_dtype == GDN_BF16, o_dtype == GDN_BF16, q, k, v,
+                         log_alpha, beta, S, o, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

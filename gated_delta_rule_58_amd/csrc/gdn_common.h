@@ -1,0 +1,115 @@
+// Shared device helpers of the gfx950 gated-delta-rule kernels: bf16
+// conversion, the 16x16 MFMA fragment layouts and LDS fragment loaders.
+//
+// MFMA conventions (v_mfma_f32_16x16x32_bf16, wave64):
+//   A operand (16 x 32): lane l holds 8 k-values of row (l & 15);
+//   B operand (32 x 16): lane l holds 8 k-values of column (l & 15);
+//   D / C (16 x 16 fp32): lane l holds rows 4*(l >> 4) + j, j = 0..3, of
+//   column (l & 15).
+// Which 8 k-values a lane holds only has to agree between A and B, so two
+// k-orders are used:
+//   natural  -- lane group g = l >> 4 holds k = 8g .. 8g+7;
+//   "D-order" -- group g holds k = 4g .. 4g+3 and 16+4g .. 16+4g+3, which is
+//   exactly what two stacked D tiles hold.  A matrix produced by an MFMA in
+//   D layout can therefore feed the next MFMA as a B operand (or, if the
+//   transposed product was computed, as an A operand) straight from
+//   registers; the other operand is then read from LDS in D-order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// 16x16x32 bf16 MFMA, fp32 accumulate: acc += A * B.
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+
+// 16x16x16 bf16 MFMA: lane l holds A[l&15][4(l>>4)..+3], B[4(l>>4)..+3][l&15].
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+        __builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Round two D tiles (rows 0-15 and 16-31 of a 32-row block) to a bf16
+// operand in D-order.
+__device__ __forceinline__ bf16x8 d_to_op(f32x4 d0, f32x4 d1) {
+    return bf16x8{(bf16)d0[0], (bf16)d0[1], (bf16)d0[2], (bf16)d0[3],
+                  (bf16)d1[0], (bf16)d1[1], (bf16)d1[2], (bf16)d1[3]};
+}
+
+// Split x into hi + lo, both bf16: hi = bf16(x), lo = bf16(x - hi).  Products
+// hi*y + lo*y keep about 16 mantissa bits of x.
+__device__ __forceinline__ void split_op(f32x4 d0, f32x4 d1, bf16x8 &hi, bf16x8 &lo) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        bf16 h0 = (bf16)d0[j], h1 = (bf16)d1[j];
+        hi[j] = h0;
+        hi[4 + j] = h1;
+        lo[j] = (bf16)(d0[j] - (float)h0);
+        lo[4 + j] = (bf16)(d1[j] - (float)h1);
+    }
+}
+
+// --- LDS fragment loaders (row-major bf16 arrays with `ld` elements/row) ---
+
+// Rows row0..row0+15, k0..k0+31 in natural order: one 16-byte read.
+__device__ __forceinline__ bf16x8 frag_rows(const bf16 *base, int ld, int row0,
+                                            int k0, int lane) {
+    return *reinterpret_cast<const bf16x8 *>(base + (row0 + (lane & 15)) * ld + k0 +
+                                             8 * (lane >> 4));
+}
+
+// Rows row0..row0+15, k0..k0+31 in D-order: two 8-byte reads.
+__device__ __forceinline__ bf16x8 frag_rows_d(const bf16 *base, int ld, int row0,
+                                              int k0, int lane) {
+    const bf16 *p = base + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
+    return cat(*reinterpret_cast<const bf16x4 *>(p),
+               *reinterpret_cast<const bf16x4 *>(p + 16));
+}
+
+// Transposed access: operand element (m, k) = X[k0 + k][m0 + m] of a
+// row-major X, natural k order (8 two-byte reads).
+__device__ __forceinline__ bf16x8 frag_cols(const bf16 *base, int ld, int m0,
+                                            int k0, int lane) {
+    const bf16 *p = base + (k0 + 8 * (lane >> 4)) * ld + m0 + (lane & 15);
+    bf16x8 r;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) r[s] = p[s * ld];
+    return r;
+}
+
+// Transposed access in D-order.
+__device__ __forceinline__ bf16x8 frag_cols_d(const bf16 *base, int ld, int m0,
+                                              int k0, int lane) {
+    const bf16 *p = base + (k0 + 4 * (lane >> 4)) * ld + m0 + (lane & 15);
+    bf16x8 r;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        r[s] = p[s * ld];
+        r[4 + s] = p[(16 + s) * ld];
+    }
+    return r;
+}
+
+}  // namespace gdn

@@ -1,0 +1,142 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated-delta-rule library, libgdn.so.
+ *
+ * The operation is the gated delta rule of "Gated Delta Networks: Improving
+ * Mamba2 with Delta Rule" (research-map summary, section "Approach"; blog
+ * "Gated DeltaNet: Harmonizing Gating and the Delta Rule for Superior Linear
+ * RNNs", section "Methodology: The Gated Delta Rule"):
+ *
+ *     S_t = S_{t-1} ( alpha_t (I - beta_t k_t k_t^T) ) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t        (read-out of the post-update state, no scale)
+ *
+ * with the state S_t a d_v x d_k fp32 matrix per (sequence, head).  The
+ * pages print no read-out; the one above is the library's definition.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers (HIP device memory of the
+ *     current device), contiguous, row-major, owned by the caller.  The
+ *     library allocates nothing and keeps no device state beyond its loaded
+ *     code objects; it is reentrant across streams.
+ *   - The gate is passed as log(alpha) in fp32 (alpha in (0,1] means
+ *     log_alpha <= 0); beta is fp32.  Any real beta is accepted.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work: it returns before the GPU has run it,
+ *     and faults inside a kernel surface at the caller's next stream sync.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     rejected call has no effect and returns a nonzero gdn_status, with a
+ *     message available from gdn_last_error() (thread-local).
+ *   - Pointers must be 16-byte aligned (GDN_ERR_ALIGNMENT otherwise).
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_dtype {
+    GDN_F32 = 0,   /* q, k, v, o in fp32 */
+    GDN_BF16 = 1   /* q, k, v, o in bfloat16 (fp32 state and accumulation) */
+} gdn_dtype;
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1,  /* null required pointer, negative/zero dims, varlen with B != 1 */
+    GDN_ERR_UNSUPPORTED = 2,  /* (d_k, d_v, chunk, dtype) with no compiled kernel */
+    GDN_ERR_ALIGNMENT = 3,    /* a pointer not 16-byte aligned */
+    GDN_ERR_WORKSPACE = 4,    /* workspace smaller than gdn_chunk_fwd_workspace_size */
+    GDN_ERR_HIP = 5           /* a HIP launch error */
+} gdn_status;
+
+/* Problem descriptor of gdn_chunk_fwd.
+ *   B, T, H   batch, tokens per batch row, heads (T may be 0);
+ *   d_k, d_v  key and value widths;
+ *   chunk     chunk length C of the chunkwise algorithm (any value gives the
+ *             same result up to rounding; only compiled values are accepted);
+ *   n_seqs    0 for a dense batch, else the number of sequences packed into
+ *             one row of T tokens (then B must be 1 and cu_seqlens given);
+ *   io_dtype  a gdn_dtype for q, k, v;
+ *   o_dtype   a gdn_dtype for o.  GDN_F32 is the exact-parity choice: the
+ *             read-outs are heavy-tailed (max |o| is 10-20x RMS(o) on
+ *             random inputs), so rounding o to bf16 alone moves the largest
+ *             outputs by up to ~4% of RMS(o). */
+typedef struct gdn_shape {
+    int B, T, H, d_k, d_v, chunk;
+    int n_seqs;
+    int io_dtype;
+    int o_dtype;
+} gdn_shape;
+
+/* Bytes of device workspace gdn_chunk_fwd needs for `shape` (written to
+ * *bytes).  The current kernels need none (0), but callers should query and
+ * pass it so that future kernels can use one.  Returns a gdn_status. */
+int gdn_chunk_fwd_workspace_size(const gdn_shape *shape, size_t *bytes);
+
+/* Chunkwise-parallel forward pass of the gated delta rule over whole
+ * sequences: the extended WY/UT chunk algorithm (research-map summary,
+ * section "Approach"; blog, section "Hardware-Efficient Training"), which
+ * reaches the token recurrence's result exactly up to rounding.
+ *
+ *   q, k        [B, T, H, d_k]  io_dtype
+ *   v           [B, T, H, d_v]  io_dtype
+ *   log_alpha   [B, T, H]       fp32, log of the gate alpha_t
+ *   beta        [B, T, H]       fp32
+ *   S0          [U, H, d_v, d_k] fp32 initial states, U = B (dense) or
+ *               n_seqs (packed); NULL means zeros.
+ *   cu_seqlens  [n_seqs + 1]    int32 device array of sequence offsets
+ *               (cu[0] = 0, non-decreasing, cu[n_seqs] = T; precondition,
+ *               not checked); NULL for a dense batch.  Empty sequences are
+ *               allowed.  The chunk grid restarts at every sequence start
+ *               and each sequence starts from its own S0.
+ *   o           [B, T, H, d_v]  o_dtype output; must not alias an input.
+ *   S_T         [U, H, d_v, d_k] fp32 final states; NULL = not written.  May
+ *               alias S0 (then S0 is overwritten with the final state).
+ *   workspace   device buffer of at least the queried size (may be NULL
+ *               when that size is 0).
+ *
+ * T = 0 (or an empty sequence) writes no o and copies S0 (or zeros) to S_T.
+ * Compiled instances (d_k, d_v, chunk, io_dtype):
+ *   (64, 64, 64, BF16), (128, 128, 64, BF16) -- MFMA kernels;
+ *   (16|32|64, same, 16|32|64, F32)          -- fp32 kernels.
+ * Returns a gdn_status. */
+int gdn_chunk_fwd(const gdn_shape *shape,
+                  const void *q, const void *k, const void *v,
+                  const float *log_alpha, const float *beta,
+                  const float *S0, const int32_t *cu_seqlens,
+                  void *o, float *S_T,
+                  void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/* One recurrent decode step of the same rule for every (b, h): reads one
+ * token, updates the state in place and returns the read-out -- the
+ * constant-memory decoding of "Gated DeltaNet-2: Decoupling Erase and Write
+ * in Linear Attention" (abstract), for the scalar-gate rule above.
+ *
+ *   q, k       [B, H, d_k]        io_dtype
+ *   v          [B, H, d_v]        io_dtype
+ *   log_alpha  [B, H]             fp32
+ *   beta       [B, H]             fp32
+ *   S          [B, H, d_v, d_k]   fp32, read and overwritten in place
+ *   o          [B, H, d_v]        o_dtype output; must not alias S
+ *
+ * Supported: d_k = 128 or 64, any d_v >= 1; either dtype for the inputs and
+ * for o.  Returns a gdn_status. */
+int gdn_step(int B, int H, int d_k, int d_v, int io_dtype, int o_dtype,
+             const void *q, const void *k, const void *v,
+             const float *log_alpha, const float *beta,
+             float *S, void *o, void *stream);
+
+/* Message describing the last error on the calling thread ("" if none). */
+const char *gdn_last_error(void);
+
+/* Library version string, e.g. "gdn-mi355x 0.1.0 (gfx950)". */
+const char *gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,128 @@
+"""Host-side checks of libgdn.so (CPU only, no kernel is ever launched).
+
+The library must load without a GPU, export every function include/gdn.h
+declares, and reject bad arguments on the host with the documented status
+codes before enqueueing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_58_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE = 0, 1, 2, 3, 4
+P = ctypes.c_void_p(4096)          # stand-in device pointers: never dereferenced
+P2 = ctypes.c_void_p(8192)
+MIS = ctypes.c_void_p(4096 + 4)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_matches_binding():
+    assert declared_functions() == sorted(B.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(B.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version():
+    assert B.version().startswith("gdn-mi355x")
+
+
+def shape(**kw):
+    d = dict(B=2, T=100, H=4, d_k=128, d_v=128, chunk=64, n_seqs=0, io_dtype=1, o_dtype=0)
+    d.update(kw)
+    return B.GdnShape(**d)
+
+
+def ws_size(s):
+    out = ctypes.c_size_t(123)
+    rc = B.lib().gdn_chunk_fwd_workspace_size(ctypes.byref(s) if s is not None else None,
+                                               ctypes.byref(out))
+    return rc, out.value
+
+
+def fwd(s, q=P, k=P, v=P, la=P, be=P, S0=None, cu=None, o=P2, ST=None, ws=None, wsb=0):
+    return B.lib().gdn_chunk_fwd(ctypes.byref(s), q, k, v, la, be, S0, cu, o, ST, ws, wsb, None)
+
+
+def err():
+    return B.lib().gdn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw", [dict(d_k=128, d_v=128, io_dtype=1),
+                                dict(d_k=64, d_v=64, io_dtype=1),
+                                dict(d_k=16, d_v=16, chunk=16, io_dtype=0),
+                                dict(d_k=64, d_v=64, chunk=32, io_dtype=0, o_dtype=1)])
+def test_workspace_query_supported(kw):
+    rc, n = ws_size(shape(**kw))
+    assert rc == OK and n == 0 and err() == ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), INVALID), (dict(H=0), INVALID), (dict(T=-1), INVALID),
+    (dict(d_k=0), INVALID), (dict(chunk=0), INVALID), (dict(n_seqs=-1), INVALID),
+    (dict(n_seqs=3, B=2), INVALID), (dict(io_dtype=7), INVALID), (dict(o_dtype=-1), INVALID),
+    (dict(d_k=96, d_v=96), UNSUPPORTED), (dict(d_k=128, d_v=64), UNSUPPORTED),
+    (dict(chunk=32), UNSUPPORTED), (dict(d_k=128, d_v=128, io_dtype=0), UNSUPPORTED),
+    (dict(d_k=16, d_v=16, chunk=8, io_dtype=0), UNSUPPORTED),
+])
+def test_workspace_query_rejects(kw, code):
+    rc, _ = ws_size(shape(**kw))
+    assert rc == code
+    assert err() != ""
+
+
+def test_null_shape():
+    assert ws_size(None)[0] == INVALID
+
+
+def test_fwd_rejects_before_launch():
+    s = shape()
+    assert fwd(s, q=None) == INVALID and "required" in err()
+    assert fwd(s, o=None) == INVALID
+    assert fwd(s, k=MIS) == ALIGN and "k=" in err()
+    assert fwd(s, S0=MIS) == ALIGN
+    assert fwd(s, o=P) == INVALID and "alias" in err()
+    assert fwd(s, cu=P) == INVALID and "n_seqs" in err()
+    sv = shape(B=1, n_seqs=3)
+    assert fwd(sv, cu=None) == INVALID and "cu_seqlens" in err()
+    assert fwd(shape(d_k=96, d_v=96)) == UNSUPPORTED
+
+
+def test_fwd_empty_without_state_is_a_noop():
+    # T = 0 and no final state requested: nothing to do, nothing launched.
+    assert fwd(shape(T=0), q=None, k=None, v=None, la=None, be=None, o=None) == OK
+    assert err() == ""
+
+
+def step(Bn=2, H=3, dk=128, dv=128, io=1, od=0, q=P, k=P, v=P, la=P, be=P, S=P2, o=P):
+    return B.lib().gdn_step(Bn, H, dk, dv, io, od, q, k, v, la, be, S, o, None)
+
+
+def test_step_rejects_before_launch():
+    assert step(Bn=0) == INVALID
+    assert step(dv=-3) == INVALID
+    assert step(io=5) == INVALID
+    assert step(dk=32) == UNSUPPORTED and "d_k" in err()
+    assert step(S=None) == INVALID
+    assert step(q=MIS) == ALIGN
+    assert step(o=P2) == INVALID and "alias" in err()
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        B.lib()
