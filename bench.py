@@ -52,6 +52,65 @@ def bytes_chunk_fwd(B, T, H, dk, dv, io_bytes=2, o_bytes=4, with_s0=False) -> fl
     return B * T * H * per_th + states
 
 
+def run_decode(args, torch, gi, gdn, dev):
+    """Time gdn_step on the decode workload; returns the JSON sub-object."""
+    wd = gi.WORKLOADS[4]
+    print("[bench] decode: workload 4", file=sys.stderr, flush=True)
+    dh = gi.workload_inputs(4)
+    dd = {k: v.to(dev) for k, v in dh.items()}
+    S = dd["S0"].clone()
+    Bd, Hd = wd["B"], wd["H"]
+    od = torch.empty((Bd, Hd, wd["dv"]), device=dev, dtype=torch.float32)
+    nsteps = min(args.decode_steps, wd["steps"])
+
+    def dstep(t):
+        gdn.step(dd["q"][t], dd["k"][t], dd["v"][t], dd["log_alpha"][t], dd["beta"][t], S, o=od)
+
+    for t in range(4):
+        dstep(t)
+    torch.cuda.synchronize()
+    S.copy_(dd["S0"])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for t in range(nsteps):
+        dstep(t)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm_us = e0.elapsed_time(e1) * 1e3 / nsteps
+    flush = torch.empty(1 << 28, device=dev, dtype=torch.float32)   # 1 GiB > MALL + L2
+    cold = []
+    for t in range(args.cold_steps):
+        flush.fill_(float(t))
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ea.record(stream)
+        dstep(t)
+        eb.record(stream)
+        torch.cuda.synchronize()
+        cold.append(ea.elapsed_time(eb) * 1e3)
+    del flush
+    cold.sort()
+    cold_us = cold[len(cold) // 2]
+    dbytes = (2 * Bd * Hd * wd["dv"] * wd["dk"] * 4 + Bd * Hd * (2 * wd["dk"] + wd["dv"]) * 2
+              + Bd * Hd * wd["dv"] * 4 + Bd * Hd * 8)
+    decode = {
+        "workload": f"{wd['name']}: B={Bd} H={Hd} d_k=d_v={wd['dk']}, bf16 q/k/v, fp32 state",
+        "bytes_per_step": dbytes,
+        "us_per_step_cold": round(cold_us, 2),
+        "GB_s_cold": round(dbytes / (cold_us * 1e-6) / 1e9, 1),
+        "frac_hbm_cold": round(dbytes / (cold_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "us_per_step_warm": round(warm_us, 2),
+        "GB_s_warm": round(dbytes / (warm_us * 1e-6) / 1e9, 1),
+        "note": "cold = 1 GiB cache-evicting write before each timed step (median of "
+                f"{args.cold_steps}); warm = {nsteps} steps back to back, state resident in MALL",
+    }
+
+    if args.only == "decode":
+        print(json.dumps({"decode": decode}))
+    return decode
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -62,6 +121,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2,
                     help="batch rows of the workload the CPU oracle runs")
+    ap.add_argument("--only", choices=["all", "chunk", "decode"], default="all",
+                    help="run one part only (for profiling); the JSON line needs 'all'")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a device-to-device copy of this many MiB (a "
+                         "known-size kernel for calibrating HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the "
@@ -74,6 +138,18 @@ def main():
     import gated_delta_rule_58_amd as gdn
 
     dev = "cuda:0"
+    if args.copy_mib:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copied {args.copy_mib} MiB x3", file=sys.stderr, flush=True)
+        del src, dst
+    if args.only == "decode":
+        run_decode(args, torch, gi, gdn, dev)
+        return
     w = gi.WORKLOADS[2]
     B, T, H, dk, dv, C = w["B"], w["T"], w["H"], w["dk"], w["dv"], w["chunk"]
     print(f"[bench] inputs: workload 2 {w['name']} B={B} T={T} H={H} d={dk}", file=sys.stderr,
@@ -114,56 +190,11 @@ def main():
         with open(PMC_FILE) as f:
             traffic = json.load(f).get("hbm_bytes_per_launch")
 
-    # ---------------- decode (gdn_step) ----------------
-    wd = gi.WORKLOADS[4]
-    print("[bench] decode: workload 4", file=sys.stderr, flush=True)
-    dh = gi.workload_inputs(4)
-    dd = {k: v.to(dev) for k, v in dh.items()}
-    S = dd["S0"].clone()
-    Bd, Hd = wd["B"], wd["H"]
-    od = torch.empty((Bd, Hd, wd["dv"]), device=dev, dtype=torch.float32)
-    nsteps = min(args.decode_steps, wd["steps"])
-
-    def dstep(t):
-        gdn.step(dd["q"][t], dd["k"][t], dd["v"][t], dd["log_alpha"][t], dd["beta"][t], S, o=od)
-
-    for t in range(4):
-        dstep(t)
-    torch.cuda.synchronize()
-    S.copy_(dd["S0"])
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for t in range(nsteps):
-        dstep(t)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    warm_us = e0.elapsed_time(e1) * 1e3 / nsteps
-    flush = torch.empty(1 << 28, device=dev, dtype=torch.float32)   # 1 GiB > MALL + L2
-    cold = []
-    for t in range(args.cold_steps):
-        flush.fill_(float(t))
-        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ea.record(stream)
-        dstep(t)
-        eb.record(stream)
-        torch.cuda.synchronize()
-        cold.append(ea.elapsed_time(eb) * 1e3)
-    del flush
-    cold.sort()
-    cold_us = cold[len(cold) // 2]
-    dbytes = (2 * Bd * Hd * wd["dv"] * wd["dk"] * 4 + Bd * Hd * (2 * wd["dk"] + wd["dv"]) * 2
-              + Bd * Hd * wd["dv"] * 4 + Bd * Hd * 8)
-    decode = {
-        "workload": f"{wd['name']}: B={Bd} H={Hd} d_k=d_v={wd['dk']}, bf16 q/k/v, fp32 state",
-        "bytes_per_step": dbytes,
-        "us_per_step_cold": round(cold_us, 2),
-        "GB_s_cold": round(dbytes / (cold_us * 1e-6) / 1e9, 1),
-        "frac_hbm_cold": round(dbytes / (cold_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-        "us_per_step_warm": round(warm_us, 2),
-        "GB_s_warm": round(dbytes / (warm_us * 1e-6) / 1e9, 1),
-        "note": "cold = 1 GiB cache-evicting write before each timed step (median of "
-                f"{args.cold_steps}); warm = {nsteps} steps back to back, state resident in MALL",
-    }
+    if args.only == "chunk":
+        print(json.dumps({"chunk_ms_per_step": round(ms, 4), "tokens_per_s": round(value, 1),
+                          "GB_s": round(gbs, 1)}))
+        return
+    decode = run_decode(args, torch, gi, gdn, dev)
 
     # ---------------- CPU oracle baseline ----------------
     cpu = None

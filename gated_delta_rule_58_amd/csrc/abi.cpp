@@ -67,6 +67,8 @@ int check_shape(const gdn_shape *s) {
     const long units = s->n_seqs > 0 ? s->n_seqs : s->B;
     if ((long)units * s->H > (1L << 28))
         return fail(GDN_ERR_INVALID_ARG, "units x heads = %ld is too large", units * (long)s->H);
+    if (s->H > 32768)
+        return fail(GDN_ERR_UNSUPPORTED, "H=%d exceeds the supported 32768 heads", s->H);
     const bool ok_inst = s->io_dtype == GDN_BF16
                              ? gdn::chunk_mfma_supported(s->d_k, s->d_v, s->chunk)
                              : gdn::chunk_f32_supported(s->d_k, s->d_v, s->chunk);

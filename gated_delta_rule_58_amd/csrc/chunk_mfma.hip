@@ -5,70 +5,119 @@
 // Improving Mamba2 with Delta Rule", research-map summary, section
 // "Approach"; blog "Gated DeltaNet: Harmonizing Gating and the Delta Rule for
 // Superior Linear RNNs", section "Hardware-Efficient Training").  For one
-// chunk of C = 64 tokens (zero-padded at a ragged end) and the state S that
-// enters it, with g the chunk-local prefix sum of log alpha:
+// chunk of C = 64 tokens (zero-padded at a ragged end) and the state S
+// (d_v x d_k) that enters it, with g the chunk-local prefix sum of log alpha:
 //   (1) g_r = sum_{s<=r} log alpha_s
 //   (2) A[r,i] = beta_r e^{g_r-g_i} (k_r . k_i) for i < r;  T = (I + A)^{-1}
 //   (3) U = T diag(beta) V,  W = T diag(beta e^g) K
 //   (4) Delta = U - W S^T;   S <- e^{g_C} S + Delta^T diag(e^{g_C-g}) K
 //   (5) O = diag(e^g) Q S^T + (tril(Q K^T) o e^{g_r-g_i}) Delta
+// W is never formed: W S^T = (T diag(beta e^g)) (K S^T), so the kernel keeps
+// T_W = T diag(beta e^g) and multiplies it into Y = K S^T.  U is formed as
+// diag(beta) V (fp32) plus (T - I) diag(beta) V on MFMA.
 //
-// One workgroup (4 waves) owns one (sequence, head, 64-wide slice of d_v)
-// and walks the chunks in order, so the whole pass is a single read of
-// q, k, v and the gates, and a single write of o; nothing is staged in HBM.
-// Per chunk:
-//   - stage (1)-(3) are computed cooperatively into LDS: Q K^T and K K^T on
-//     MFMA, the 64x64 unit-lower inverse as four 16x16 diagonal blocks by
-//     forward substitution in fp32 followed by three bands of 16x16 MFMA
-//     block products (T_ij = -T_ii sum_k A_ik T_kj), then W on MFMA;
-//   - stage (4)-(5) is wave-local: wave w owns 16 columns of the d_v slice,
-//     keeps its S^T columns (d_k x 16, fp32) in MFMA accumulators, and feeds
-//     S^T and Delta from accumulator registers straight into the next MFMAs
-//     (see gdn_common.h for the register layouts).
-// Precision: the outputs are heavy-tailed (max |o| is 10-20x its RMS), so
-// plain bf16 operands lose too much.  The operands that carry the state or
-// the corrected values are split into hi + lo bf16 pairs (S^T, Delta, P),
-// the beta-diagonal of U is applied in fp32, and o is written in fp32 (or
-// bf16 on request).
+// Work split.  One workgroup of 8 waves owns one (sequence, head, 64-column
+// slice of d_v) and walks its chunks in order, so q, k, v and the gates are
+// read once and o is written once.  Waves 0-3 ("producers") prepare chunk
+// n+1 -- global prefetch, gate prefix, K K^T and Q K^T on MFMA, the 64x64
+// unit-lower inverse (four 16x16 diagonal blocks by blocked forward
+// substitution in fp32, then the off-diagonal blocks
+// T_ij = -T_ii sum_k A_ik T_kj on 16x16 MFMA), the bf16 factors
+// (T - I) diag(beta), T diag(beta e^g) and K^T -- while waves 4-7
+// ("consumers") run the state chain of chunk n.  Consumer c owns 16 columns
+// of the slice and keeps its S^T columns (d_k x 16, fp32) in MFMA
+// accumulators; S^T, Y and Delta feed the next MFMA straight from registers
+// (layouts in gdn_common.h).  An iteration has four barrier-separated phases;
+// every LDS buffer is written by one phase and read in later ones before it
+// is overwritten, so apart from the gates nothing is double-buffered:
+//   phase  producers (chunk n+1)               consumers (chunk n)
+//   1      store q,k, gate prefix, prefetch    U, Delta, P Delta, write o
+//   2      K K^T, Q K^T -> A, P               S <- e^{g_C} S + K^T Delta~
+//   3      diagonal inverses, store v          Q S^T for chunk n+1
+//   4      off-diagonal T, T diag(.), K^T      Y = K S^T for chunk n+1
+// Global loads and stores go through buffer resources sized to the valid
+// rows of the chunk: rows past a ragged end read as zero and their stores
+// are dropped by the hardware range check, so no lane branches on bounds.
+// Precision: outputs are heavy-tailed (max |o| is 10-20x its RMS), so the
+// operands carrying the state or the corrected values are split into
+// hi + lo bf16 pairs (S^T, Y, Delta, Delta~, P) and o is written in fp32
+// (or bf16 on request).
 #include "gdn_common.h"
 
 namespace gdn {
 
 constexpr int kC = 64;     // chunk length
-constexpr int kDVT = 64;   // d_v columns per workgroup (16 per wave)
+constexpr int kDVT = 64;   // d_v columns per workgroup (16 per consumer wave)
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
+
+__device__ __forceinline__ float exp_neg(float x) {   // e^x for x <= 0
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) {
+    return bf16x4{(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+}
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) { return to_bf16x4(x[0], x[1], x[2], x[3]); }
+
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+__device__ __forceinline__ bf16x8 buf_load16(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load4(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store(float x, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store(bf16 x, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), r, off, 0, 0);
+}
 
 template <int DK, typename TO>
-__global__ __launch_bounds__(256, 1) void chunk_mfma_kernel(
+__global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     int T, int H, int DV, int varlen, int xcd_map, const int32_t *__restrict__ cu_seqlens,
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
     const float *__restrict__ S0, TO *__restrict__ o, float *__restrict__ S_T) {
     constexpr int C = kC;
-    constexpr int NKS = DK / 32;      // 32-wide k-steps over d_k
-    constexpr int NMT = DK / 16;      // 16-row tiles over d_k
-    constexpr int NMW = NMT / 4;      // d_k tiles of W^T per wave
-    constexpr int LDK = DK + 8;       // padded row lengths (elements)
-    constexpr int LDC = C + 8;
-    constexpr int LDV = kDVT + 8;
-    constexpr int LDA = C + 4;
+    constexpr int NKS = DK / 32;        // 32-wide k-steps over d_k
+    constexpr int NMT = DK / 16;        // 16-row tiles over d_k
+    // Padded row lengths (elements).  Operands are read 8 bytes per lane, 16
+    // lanes (16 rows) per LDS cycle: a row stride of 2 mod 4 dwords puts those
+    // 16 rows on 16 distinct bank pairs.
+    constexpr int LDK = DK + 4;
+    constexpr int LDC = C + 4;
+    constexpr int LDV = kDVT + 8;       // v rows are written 16 bytes at a time
+    constexpr int BLK = 260;            // stride of the 16x16 fp32 diagonal blocks (4 banks apart)
+    constexpr int QK_PIECES = C * DK / 8;            // 16-byte pieces of a q or k chunk
+    constexpr int QK_PER_THR = QK_PIECES / 256;
+    constexpr int V_PER_THR = C * kDVT / 8 / 256;
+    static_assert(QK_PIECES % 256 == 0 && V_PER_THR * 256 == C * kDVT / 8, "piece split");
 
     __shared__ __attribute__((aligned(16))) bf16 sQ[C * LDK];
     __shared__ __attribute__((aligned(16))) bf16 sK[C * LDK];
+    __shared__ __attribute__((aligned(16))) bf16 sKT[DK * LDC];     // K^T [d_k][token]
     __shared__ __attribute__((aligned(16))) bf16 sV[C * LDV];
-    __shared__ __attribute__((aligned(16))) float sA[C * LDA];      // A (strict lower)
-    __shared__ __attribute__((aligned(16))) float sAd[4 * 16 * 16]; // diag blocks of A, transposed
-    __shared__ __attribute__((aligned(16))) float sT[C * LDA];      // T, later W (bf16)
-    __shared__ __attribute__((aligned(16))) bf16 sTU[C * LDC];      // strict-lower T diag(beta)
+    __shared__ __attribute__((aligned(16))) bf16 sA[C * LDC];       // A, off-diagonal blocks
+    __shared__ __attribute__((aligned(16))) float sAd[4 * BLK];     // A diag blocks, [b][col][row]
+    __shared__ __attribute__((aligned(16))) float sTd[4 * BLK];     // T diag blocks, [b][row][col]
+    __shared__ __attribute__((aligned(16))) float sTdT[4 * BLK];    // T diag blocks, [b][col][row]
+    __shared__ __attribute__((aligned(16))) bf16 sTU[C * LDC];      // (T - I) diag(beta)
     __shared__ __attribute__((aligned(16))) bf16 sTW[C * LDC];      // T diag(beta e^g)
     __shared__ __attribute__((aligned(16))) bf16 sPh[C * LDC];      // P = tril(QK^T) o decay, hi
     __shared__ __attribute__((aligned(16))) bf16 sPl[C * LDC];      // P, lo
-    __shared__ float sg[C], seg[C], sb[C];
-    bf16 *sW = reinterpret_cast<bf16 *>(sT);
-    static_assert(C * LDK * sizeof(bf16) <= C * LDA * sizeof(float), "sW must fit in sT");
+    // gates of a chunk, double-buffered: g, e^g, beta, e^{g_C - g}
+    __shared__ __attribute__((aligned(16))) float sG[2][4][C];
 
-    // Workgroup -> (unit, head, d_v slice).  With xcd_map the two slices of
-    // one (unit, head) land on the same XCD (workgroups are dealt to the 8
-    // XCDs round-robin), so the second read of q and k hits that XCD's L2.
+    // Workgroup -> (unit, head, d_v slice).  With xcd_map the slices of one
+    // (unit, head) land on the same XCD (workgroups are dealt to the 8 XCDs
+    // round-robin), so the repeated reads of q and k hit that XCD's L2.
     const int ndvt = DV / kDVT;
     int uh, dvt;
     if (xcd_map) {
@@ -82,10 +131,9 @@ __global__ __launch_bounds__(256, 1) void chunk_mfma_kernel(
     const int unit = uh / H, h = uh % H;
     const int dv0 = dvt * kDVT;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
     const int lm = lane & 15, lg = lane >> 4;
-    const int cw = 16 * w;              // wave's first column within the slice
-    const int dvw = dv0 + cw + lm;      // this lane's d_v column
 
     long row0, L;
     if (varlen) {
@@ -95,298 +143,470 @@ __global__ __launch_bounds__(256, 1) void chunk_mfma_kernel(
         row0 = (long)unit * T;
         L = T;
     }
-    const size_t sbase = ((size_t)unit * H + h) * DV * DK;
+    const int N = (int)((L + C - 1) / C);
+    // first token (absolute row) and valid rows of chunk c
+    auto crow = [&](int c) -> size_t { return (size_t)(row0 + (long)c * C); };
+    auto cvalid = [&](int c) -> uint32_t { return (uint32_t)min((long)C, L - (long)c * C); };
 
-    // st[mt][j] = S^T[16 mt + 4 lg + j][dvw] = S[dvw][16 mt + 4 lg + j]
-    f32x4 st[NMT];
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-        if (S0) {
-            const float4 x = *reinterpret_cast<const float4 *>(S0 + sbase + (size_t)dvw * DK +
-                                                               16 * mt + 4 * lg);
-            st[mt] = f32x4{x.x, x.y, x.z, x.w};
-        } else {
-            st[mt] = zero4();
-        }
+    // Upper off-diagonal blocks of the LDS factors are never written: zero them once.
+    for (int e = tid; e < C * LDC / 2; e += 512) {
+        reinterpret_cast<uint32_t *>(sTU)[e] = 0u;
+        reinterpret_cast<uint32_t *>(sTW)[e] = 0u;
+        reinterpret_cast<uint32_t *>(sPh)[e] = 0u;
+        reinterpret_cast<uint32_t *>(sPl)[e] = 0u;
     }
+    __syncthreads();
 
-    for (long c0 = 0; c0 < L; c0 += C) {
-        const int n = (int)((L - c0) < C ? (L - c0) : C);
-        __syncthreads();   // the previous chunk is done with every LDS buffer
-
-        // ---- load: q, k rows and the v slice (zero rows past the end) ----
-        for (int e = tid; e < C * DK / 8; e += 256) {
-            const int r = e / (DK / 8), p = e % (DK / 8);
-            bf16x8 qv = {}, kv = {};
-            if (r < n) {
-                const size_t gi = ((size_t)(row0 + c0 + r) * H + h) * DK + 8 * p;
-                qv = *reinterpret_cast<const bf16x8 *>(q + gi);
-                kv = *reinterpret_cast<const bf16x8 *>(k + gi);
+    // Producers and consumers run separate loops (so each role's registers
+    // are allocated on their own); both pass the same four barriers per
+    // iteration, N + 1 times.
+    if (wave < 4) {
+        const int pw = wave;       // producer wave 0..3
+        const int ptid = tid;      // producer thread 0..255
+        bf16x8 pq[QK_PER_THR], pk[QK_PER_THR], pv[V_PER_THR];
+        float pla = 0.f, pbe = 0.f;
+        auto prefetch_qk = [&](int c) {
+            const size_t t0 = crow(c);
+            const uint32_t nv = cvalid(c);
+            const rsrc_t rq = make_rsrc(q + (t0 * H + h) * DK, nv * H * DK * 2);
+            const rsrc_t rk = make_rsrc(k + (t0 * H + h) * DK, nv * H * DK * 2);
+#pragma unroll
+            for (int i = 0; i < QK_PER_THR; ++i) {
+                const int e = ptid + 256 * i, r = e / (DK / 8), p = e % (DK / 8);
+                const uint32_t off = (uint32_t)(r * H * DK + 8 * p) * 2;
+                pq[i] = buf_load16(rq, off);
+                pk[i] = buf_load16(rk, off);
             }
-            *reinterpret_cast<bf16x8 *>(sQ + r * LDK + 8 * p) = qv;
-            *reinterpret_cast<bf16x8 *>(sK + r * LDK + 8 * p) = kv;
+            if (pw == 0) {
+                const rsrc_t ra = make_rsrc(log_alpha + t0 * H + h, nv * H * 4);
+                const rsrc_t rb = make_rsrc(beta + t0 * H + h, nv * H * 4);
+                pla = buf_load4(ra, (uint32_t)(lane * H) * 4);
+                pbe = buf_load4(rb, (uint32_t)(lane * H) * 4);
+            }
+        };
+        auto prefetch_v = [&](int c) {
+            const size_t t0 = crow(c);
+            const uint32_t nv = cvalid(c);
+            const rsrc_t rv = make_rsrc(v + (t0 * H + h) * DV + dv0, nv * H * DV * 2);
+#pragma unroll
+            for (int i = 0; i < V_PER_THR; ++i) {
+                const int e = ptid + 256 * i, r = e / (kDVT / 8), p = e % (kDVT / 8);
+                pv[i] = buf_load16(rv, (uint32_t)(r * H * DV + 8 * p) * 2);
+            }
+        };
+        if (N > 0) {
+            prefetch_qk(0);
+            prefetch_v(0);
         }
-        for (int e = tid; e < C * kDVT / 8; e += 256) {
-            const int r = e / (kDVT / 8), p = e % (kDVT / 8);
-            bf16x8 vv = {};
-            if (r < n)
-                vv = *reinterpret_cast<const bf16x8 *>(
-                    v + ((size_t)(row0 + c0 + r) * H + h) * DV + dv0 + 8 * p);
-            *reinterpret_cast<bf16x8 *>(sV + r * LDV + 8 * p) = vv;
-        }
-        // ---- (1) gate prefix: one wave, one token per lane ----
-        if (w == 0) {
-            float x = 0.f, bb = 0.f;
-            if (lane < n) {
-                const size_t gi = (size_t)(row0 + c0 + lane) * H + h;
-                x = log_alpha[gi];
-                bb = beta[gi];
-            }
+        for (int n = -1; n < N; ++n) {
+            const int m = n + 1;           // chunk being prepared
+            const bool prep = m < N;
+            const int gb = m & 1;          // gate buffer of chunk m
+            // ================================ phase 1
+            if (prep) {
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off);
-                if (lane >= off) x += y;
-            }
-            sg[lane] = x;
-            seg[lane] = expf(x);
-            sb[lane] = bb;
-        }
-        __syncthreads();
-
-        // ---- (2a) K K^T and Q K^T, tile row w (r in [16w, 16w+16)) ----
-        {
-            bf16x8 fKw[NKS], fQw[NKS];
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                fKw[ks] = frag_rows(sK, LDK, 16 * w, 32 * ks, lane);
-                fQw[ks] = frag_rows(sQ, LDK, 16 * w, 32 * ks, lane);
-            }
-            const int r = 16 * w + lm;
-            const float gr = sg[r], br = sb[r];
-            for (int tj = 0; tj < 4; ++tj) {
-                const int i0 = 16 * tj + 4 * lg;
-                if (tj > w) {   // above the diagonal: P is zero there
-                    *reinterpret_cast<bf16x4 *>(sPh + r * LDC + i0) = bf16x4{};
-                    *reinterpret_cast<bf16x4 *>(sPl + r * LDC + i0) = bf16x4{};
-                    continue;
+                for (int i = 0; i < QK_PER_THR; ++i) {
+                    const int e = ptid + 256 * i, r = e / (DK / 8), p = e % (DK / 8);
+                    bf16 *dq = sQ + r * LDK + 8 * p, *dk = sK + r * LDK + 8 * p;
+                    reinterpret_cast<bf16x4 *>(dq)[0] = bf16x4{pq[i][0], pq[i][1], pq[i][2], pq[i][3]};
+                    reinterpret_cast<bf16x4 *>(dq)[1] = bf16x4{pq[i][4], pq[i][5], pq[i][6], pq[i][7]};
+                    reinterpret_cast<bf16x4 *>(dk)[0] = bf16x4{pk[i][0], pk[i][1], pk[i][2], pk[i][3]};
+                    reinterpret_cast<bf16x4 *>(dk)[1] = bf16x4{pk[i][4], pk[i][5], pk[i][6], pk[i][7]};
                 }
-                f32x4 G = zero4(), PT = zero4();
+                if (pw == 0) {   // gate prefix, one token per lane (padded tokens add 0)
+                    float x = pla;
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const bf16x8 fKj = frag_rows(sK, LDK, 16 * tj, 32 * ks, lane);
-                    G = mfma32(fKj, fKw[ks], G);     // (k_i . k_r), i = i0 + j
-                    PT = mfma32(fKj, fQw[ks], PT);   // (k_i . q_r)
+                    for (int off = 1; off < 64; off <<= 1) {
+                        const float y = __shfl_up(x, off);
+                        if (lane >= off) x += y;
+                    }
+                    const float gC = __shfl(x, 63);
+                    sG[gb][0][lane] = x;
+                    sG[gb][1][lane] = exp_neg(x);
+                    sG[gb][2][lane] = pbe;
+                    sG[gb][3][lane] = exp_neg(gC - x);
                 }
-                f32x4 a4;
-                bf16x4 ph, pl;
+                if (m + 1 < N) prefetch_qk(m + 1);
+            }
+            __syncthreads();
+            // ================================ phase 2
+            if (prep) {
+                // K K^T and Q K^T tiles (ti, tj), tj <= ti, 10 in all, 2-3 per wave;
+                // a wave loads each 16-row block of K or Q it needs once.
+                typedef bf16x8 Frag[NKS];
+                auto load_rows = [&](const bf16 *src, int blk, Frag &f) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int i = i0 + j;
-                    const float dec = (i <= r) ? expf(gr - sg[i]) : 0.f;
-                    a4[j] = (i < r) ? br * dec * G[j] : 0.f;
-                    const float p = dec * PT[j];
-                    ph[j] = (bf16)p;
-                    pl[j] = (bf16)(p - (float)ph[j]);
-                }
-                *reinterpret_cast<f32x4 *>(sA + r * LDA + i0) = a4;
-                *reinterpret_cast<bf16x4 *>(sPh + r * LDC + i0) = ph;
-                *reinterpret_cast<bf16x4 *>(sPl + r * LDC + i0) = pl;
-                if (tj == w) {
-                    // K K^T is symmetric: the same registers hold the diagonal
-                    // block with rows rr = i0 + j, column ii = r; store it
-                    // transposed (column ii contiguous) for the substitution.
-                    f32x4 d4;
+                    for (int ks = 0; ks < NKS; ++ks) f[ks] = frag_rows_d(src, LDK, 16 * blk, 32 * ks, lane);
+                };
+                auto tile = [&](const int ti, const int tj, const Frag &fKj, const Frag &fKi,
+                                const Frag &fQi) {
+                    f32x4 G = zero4(), PT = zero4();
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        G = mfma32(fKj[ks], fKi[ks], G);    // k_i . k_r,  i = 16 tj + 4 lg + j, r = 16 ti + lm
+                        PT = mfma32(fKj[ks], fQi[ks], PT);  // k_i . q_r
+                    }
+                    const int r = 16 * ti + lm, i0 = 16 * tj + 4 * lg;
+                    const float gr = sG[gb][0][r], br = sG[gb][2][r];
+                    const f32x4 gi = ld4(&sG[gb][0][i0]);
+                    bf16x4 ph, pl;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const int rr = i0 + j;
-                        d4[j] = (rr > r) ? sb[rr] * expf(sg[rr] - gr) * G[j] : 0.f;
+                        const float p = (i0 + j <= r) ? exp_neg(gr - gi[j]) * PT[j] : 0.f;
+                        ph[j] = (bf16)p;
+                        pl[j] = (bf16)(p - (float)ph[j]);
                     }
-                    *reinterpret_cast<f32x4 *>(sAd + (16 * w + lm) * 16 + 4 * lg) = d4;
+                    *reinterpret_cast<bf16x4 *>(sPh + r * LDC + i0) = ph;
+                    *reinterpret_cast<bf16x4 *>(sPl + r * LDC + i0) = pl;
+                    if (ti > tj) {
+                        f32x4 a4;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) a4[j] = br * exp_neg(gr - gi[j]) * G[j];
+                        *reinterpret_cast<bf16x4 *>(sA + r * LDC + i0) = to_bf16x4(a4);
+                    } else {
+                        // Diagonal tile: K K^T is symmetric, so the registers also
+                        // hold rows rr = i0 + j of column r; store A's block
+                        // transposed (column contiguous) for the substitution.
+                        const f32x4 brr = ld4(&sG[gb][2][i0]);
+                        f32x4 d4;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            d4[j] = (i0 + j > r) ? brr[j] * exp_neg(gi[j] - gr) * G[j] : 0.f;
+                        *reinterpret_cast<f32x4 *>(sAd + ti * BLK + lm * 16 + 4 * lg) = d4;
+                    }
+                };
+                if (pw == 0) {
+                    Frag k0, q0, k3, q3;
+                    load_rows(sK, 0, k0); load_rows(sQ, 0, q0);
+                    load_rows(sK, 3, k3); load_rows(sQ, 3, q3);
+                    tile(0, 0, k0, k0, q0);
+                    tile(3, 0, k0, k3, q3);
+                } else if (pw == 1) {
+                    Frag k0, k1, q1, k3, q3;
+                    load_rows(sK, 0, k0); load_rows(sK, 1, k1); load_rows(sQ, 1, q1);
+                    load_rows(sK, 3, k3); load_rows(sQ, 3, q3);
+                    tile(1, 0, k0, k1, q1);
+                    tile(1, 1, k1, k1, q1);
+                    tile(3, 1, k1, k3, q3);
+                } else if (pw == 2) {
+                    Frag k0, k1, k2, q2;
+                    load_rows(sK, 0, k0); load_rows(sK, 1, k1);
+                    load_rows(sK, 2, k2); load_rows(sQ, 2, q2);
+                    tile(2, 0, k0, k2, q2);
+                    tile(2, 1, k1, k2, q2);
+                    tile(2, 2, k2, k2, q2);
+                } else {
+                    Frag k2, k3, q3;
+                    load_rows(sK, 2, k2); load_rows(sK, 3, k3); load_rows(sQ, 3, q3);
+                    tile(3, 2, k2, k3, q3);
+                    tile(3, 3, k3, k3, q3);
                 }
             }
-        }
-        __syncthreads();
-
-        // ---- (2b) diagonal 16x16 blocks of T by forward substitution (fp32) ----
-        {
-            float x[16];
+            __syncthreads();
+            // ================================ phase 3
+            if (prep) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = (r == lm) ? 1.f : 0.f;
-            const float *Ad = sAd + w * 256;
-#pragma unroll
-            for (int i = 0; i < 15; ++i) {
-                float col[16];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const float4 c4 = *reinterpret_cast<const float4 *>(Ad + i * 16 + 4 * q4);
-                    col[4 * q4] = c4.x;
-                    col[4 * q4 + 1] = c4.y;
-                    col[4 * q4 + 2] = c4.z;
-                    col[4 * q4 + 3] = c4.w;
+                for (int i = 0; i < V_PER_THR; ++i) {
+                    const int e = ptid + 256 * i, r = e / (kDVT / 8), p = e % (kDVT / 8);
+                    *reinterpret_cast<bf16x8 *>(sV + r * LDV + 8 * p) = pv[i];
                 }
+                if (pw == 0) {
+                    // Diagonal blocks of T = (I + A)^{-1} in fp32, one wave: lane
+                    // (block lg, column lm) solves its column by forward
+                    // substitution in 4-row sub-blocks; the block's columns of A
+                    // are contiguous in sAd.
+                    const f32x4 *Ad = reinterpret_cast<const f32x4 *>(sAd + lg * BLK);
+                    float x[16];
 #pragma unroll
-                for (int r = i + 1; r < 16; ++r) x[r] -= col[r] * x[i];
-            }
-            if (lg == 0) {
+                    for (int r = 0; r < 16; ++r) x[r] = (r == lm) ? 1.f : 0.f;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sT[(16 * w + r) * LDA + 16 * w + lm] = x[r];
-            }
-        }
-        __syncthreads();
-
-        // ---- (2c) off-diagonal blocks, band by band: T_wj = -T_ww sum_k A_wk T_kj ----
-        for (int d = 1; d < 4; ++d) {
-            if (w >= d) {
-                const int jb = w - d;
-                f32x4 Y = zero4();
-                for (int kk = jb; kk < w; ++kk) {
-                    const float4 av = *reinterpret_cast<const float4 *>(
-                        sA + (16 * w + lm) * LDA + 16 * kk + 4 * lg);
-                    const bf16x4 aop = {(bf16)av.x, (bf16)av.y, (bf16)av.z, (bf16)av.w};
-                    bf16x4 bop;
+                    for (int sb = 0; sb < 4; ++sb) {
+                        f32x4 col[4][4];   // columns 4 sb + c, rows in float4 groups
 #pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        bop[s] = (bf16)sT[(16 * kk + 4 * lg + s) * LDA + 16 * jb + lm];
-                    Y = mfma16(aop, bop, Y);
+                        for (int c = 0; c < 4; ++c)
+#pragma unroll
+                            for (int q4 = sb; q4 < 4; ++q4) col[c][q4] = Ad[(4 * sb + c) * 4 + q4];
+                        // solve the 4x4 diagonal sub-block
+#pragma unroll
+                        for (int c = 0; c < 3; ++c)
+#pragma unroll
+                            for (int rr = c + 1; rr < 4; ++rr)
+                                x[4 * sb + rr] -= col[c][sb][rr] * x[4 * sb + c];
+                        // update the rows below with the four new unknowns
+#pragma unroll
+                        for (int r = 4 * sb + 4; r < 16; ++r) {
+                            const float t0 = col[0][r >> 2][r & 3] * x[4 * sb] +
+                                             col[1][r >> 2][r & 3] * x[4 * sb + 1];
+                            const float t1 = col[2][r >> 2][r & 3] * x[4 * sb + 2] +
+                                             col[3][r >> 2][r & 3] * x[4 * sb + 3];
+                            x[r] -= t0 + t1;
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sTd[lg * BLK + r * 16 + lm] = x[r];
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        *reinterpret_cast<f32x4 *>(sTdT + lg * BLK + lm * 16 + 4 * q4) =
+                            f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
+                } else {
+                    // K^T of chunk m for its state update (the consumers finished
+                    // with the previous K^T in phase 2)
+                    for (int e = ptid - 64; e < QK_PIECES; e += 192) {
+                        const int t = e % C, p = e / C;
+                        const bf16x4 *src = reinterpret_cast<const bf16x4 *>(sK + t * LDK + 8 * p);
+                        const bf16x8 kv = cat(src[0], src[1]);
+#pragma unroll
+                        for (int s = 0; s < 8; ++s) sKT[(8 * p + s) * LDC + t] = kv[s];
+                    }
                 }
-                const float4 tv = *reinterpret_cast<const float4 *>(
-                    sT + (16 * w + lm) * LDA + 16 * w + 4 * lg);
-                const bf16x4 top = {(bf16)tv.x, (bf16)tv.y, (bf16)tv.z, (bf16)tv.w};
-                const bf16x4 yop = {(bf16)Y[0], (bf16)Y[1], (bf16)Y[2], (bf16)Y[3]};
-                const f32x4 R = mfma16(top, yop, zero4());
+                if (m + 1 < N) prefetch_v(m + 1);
+            }
+            __syncthreads();
+            // ================================ phase 4
+            if (prep && pw == 0) {
+                // Off-diagonal blocks band by band, all in this wave's registers:
+                // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj  (16x16x16 MFMA).
+                bf16x4 RTd[4], Trow[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) sT[(16 * w + 4 * lg + j) * LDA + 16 * jb + lm] = -R[j];
+                for (int b = 0; b < 4; ++b) {
+                    RTd[b] = to_bf16x4(ld4(sTdT + b * BLK + lm * 16 + 4 * lg));
+                    Trow[b] = to_bf16x4(ld4(sTd + b * BLK + lm * 16 + 4 * lg));
+                }
+                f32x4 RT[4][4];
+#pragma unroll
+                for (int d = 1; d < 4; ++d) {
+#pragma unroll
+                    for (int i = d; i < 4; ++i) {
+                        const int j = i - d;
+                        f32x4 Yb = zero4();
+#pragma unroll
+                        for (int kk = j; kk < i; ++kk) {
+                            const bf16x4 a = *reinterpret_cast<const bf16x4 *>(
+                                sA + (16 * i + lm) * LDC + 16 * kk + 4 * lg);
+                            const bf16x4 b = (kk == j) ? RTd[j] : to_bf16x4(RT[kk][j]);
+                            Yb = mfma16(a, b, Yb);
+                        }
+                        RT[i][j] = -mfma16(Trow[i], to_bf16x4(Yb), zero4());
+                    }
+                }
+                // Scale column c = 16 j + lm by beta_c (and e^{g_c}), round once
+                // to bf16, and transpose with an identity MFMA (exact) so that
+                // each lane writes 4 consecutive columns of one row.
+                bf16x4 eye;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) eye[s] = (bf16)((4 * lg + s == lm) ? 1.f : 0.f);
+#pragma unroll
+                for (int i = 1; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < i; ++j) {
+                        const int c = 16 * j + lm;
+                        const float bc = sG[gb][2][c], wc = bc * sG[gb][1][c];
+                        const f32x4 tu = mfma16(to_bf16x4(RT[i][j] * bc), eye, zero4());
+                        const f32x4 tw = mfma16(to_bf16x4(RT[i][j] * wc), eye, zero4());
+                        const int off = (16 * i + lm) * LDC + 16 * j + 4 * lg;
+                        *reinterpret_cast<bf16x4 *>(sTU + off) = to_bf16x4(tu);
+                        *reinterpret_cast<bf16x4 *>(sTW + off) = to_bf16x4(tw);
+                    }
+            } else if (prep) {
+                const int t3 = ptid - 64;   // 0..191
+                // diagonal blocks of (T - I) diag(beta) and T diag(beta e^g)
+                for (int it = t3; it < 256; it += 192) {
+                    const int b = it >> 6, r = (it >> 2) & 15, c4 = 4 * (it & 3);
+                    const f32x4 tv = ld4(sTd + b * BLK + r * 16 + c4);
+                    const f32x4 bc = ld4(&sG[gb][2][16 * b + c4]);
+                    const f32x4 ec = ld4(&sG[gb][1][16 * b + c4]);
+                    bf16x4 tu, tw;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        tu[s] = (bf16)((c4 + s < r) ? tv[s] * bc[s] : 0.f);
+                        tw[s] = (bf16)((c4 + s <= r) ? tv[s] * bc[s] * ec[s] : 0.f);
+                    }
+                    *reinterpret_cast<bf16x4 *>(sTU + (16 * b + r) * LDC + 16 * b + c4) = tu;
+                    *reinterpret_cast<bf16x4 *>(sTW + (16 * b + r) * LDC + 16 * b + c4) = tw;
+                }
             }
             __syncthreads();
         }
+        return;
+    }
 
-        // ---- (3a) T diag(beta) (strictly lower) and T diag(beta e^g) in bf16 ----
-        for (int e = tid; e < C * C / 4; e += 256) {
-            const int r = e / (C / 4), c4 = 4 * (e % (C / 4));
-            const float4 tv = *reinterpret_cast<const float4 *>(sT + r * LDA + c4);
-            const float t[4] = {tv.x, tv.y, tv.z, tv.w};
-            bf16x4 tu, tw;
+    // ---------------------------------------------------------------- consumers
+    const int cw = 16 * (wave - 4);     // first column of this wave within the slice
+    const int dvw = dv0 + cw + lm;      // this lane's d_v column
+    const size_t sbase = ((size_t)unit * H + h) * DV * DK;
+    f32x4 st[NMT];      // st[mt][j] = S^T[16 mt + 4 lg + j][dvw]
+    f32x4 QS[4], Y[4];  // Q S^T and K S^T of the next chunk, rows 16 mr + 4 lg + j
+    bf16x8 th[2], tl[2];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int c = c4 + s;
-                tu[s] = (bf16)((c < r) ? t[s] * sb[c] : 0.f);
-                tw[s] = (bf16)((c <= r) ? t[s] * sb[c] * seg[c] : 0.f);
+    for (int mt = 0; mt < NMT; ++mt) {
+        st[mt] = zero4();
+        if (S0) st[mt] = ld4(S0 + sbase + (size_t)dvw * DK + 16 * mt + 4 * lg);
+    }
+    for (int n = -1; n < N; ++n) {
+        const int m = n + 1;
+        const bool prep = m < N;
+        const bool chain = n >= 0;
+        const int cb = (m & 1) ^ 1;     // gate buffer of chunk n
+        // ================================ phase 1
+        if (chain) {
+            // Issue every LDS read of the phase first; the VALU work below
+            // overlaps their latency.
+            f32x4 bt[4];   // beta_r at rows 16 mr + 4 lg + j
+#pragma unroll
+            for (int mr = 0; mr < 4; ++mr) bt[mr] = ld4(&sG[cb][2][16 * mr + 4 * lg]);
+            const bf16x8 fV0 = frag_cols_d(sV, LDV, cw, 0, lane);
+            const bf16x8 fV1 = frag_cols_d(sV, LDV, cw, 32, lane);
+            bf16x8 fTU[6], fTW[6];   // fragment (mr, ks), ks <= mr / 2, in that order
+#pragma unroll
+            for (int mr = 0, f = 0; mr < 4; ++mr)
+#pragma unroll
+                for (int ks = 0; ks <= mr / 2; ++ks, ++f) {
+                    fTU[f] = frag_rows_d(sTU, LDC, 16 * mr, 32 * ks, lane);
+                    fTW[f] = frag_rows_d(sTW, LDC, 16 * mr, 32 * ks, lane);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            bf16x8 yh[2], yl[2];
+            split_op(Y[0], Y[1], yh[0], yl[0]);
+            split_op(Y[2], Y[3], yh[1], yl[1]);
+            // U = diag(beta) V + (T - I) diag(beta) V; the D-order V operand
+            // holds exactly this lane's rows, which gives the diagonal term.
+            f32x4 U[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                U[0][j] = bt[0][j] * (float)fV0[j];
+                U[1][j] = bt[1][j] * (float)fV0[4 + j];
+                U[2][j] = bt[2][j] * (float)fV1[j];
+                U[3][j] = bt[3][j] * (float)fV1[4 + j];
             }
-            *reinterpret_cast<bf16x4 *>(sTU + r * LDC + c4) = tu;
-            *reinterpret_cast<bf16x4 *>(sTW + r * LDC + c4) = tw;
-        }
-        __syncthreads();
-
-        // ---- (3b) W^T = K^T (T diag(beta e^g))^T, d_k rows [16 NMW w, +16 NMW) ----
+            // Delta = U - T_W Y
+            f32x4 D[4];
 #pragma unroll
-        for (int mi = 0; mi < NMW; ++mi) {
-            const int mt = w * NMW + mi;
-            const bf16x8 fKT0 = frag_cols(sK, LDK, 16 * mt, 0, lane);
-            const bf16x8 fKT1 = frag_cols(sK, LDK, 16 * mt, 32, lane);
+            for (int mr = 0, f = 0; mr < 4; ++mr) {
+                f32x4 acc = zero4();
 #pragma unroll
-            for (int nr = 0; nr < 4; ++nr) {
-                f32x4 acc = mfma32(fKT0, frag_rows(sTW, LDC, 16 * nr, 0, lane), zero4());
-                if (nr >= 2) acc = mfma32(fKT1, frag_rows(sTW, LDC, 16 * nr, 32, lane), acc);
-                // acc[j] = W[16 nr + lm][16 mt + 4 lg + j]
-                const bf16x4 wv = {(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
-                *reinterpret_cast<bf16x4 *>(sW + (16 * nr + lm) * LDK + 16 * mt + 4 * lg) = wv;
+                for (int ks = 0; ks <= mr / 2; ++ks, ++f) {
+                    U[mr] = mfma32(fTU[f], ks == 0 ? fV0 : fV1, U[mr]);
+                    acc = mfma32(fTW[f], yh[ks], acc);
+                    acc = mfma32(fTW[f], yl[ks], acc);
+                }
+                D[mr] = U[mr] - acc;
             }
-        }
-        // ---- (3c) U for the wave's 16 columns: beta V (fp32) + strict-lower part ----
-        f32x4 U[4];
-        {
-            const bf16x8 fV0 = frag_cols(sV, LDV, cw, 0, lane);
-            const bf16x8 fV1 = frag_cols(sV, LDV, cw, 32, lane);
+            // O = diag(e^g) Q S^T + P Delta, stored through a buffer resource
+            // covering the valid rows of this chunk (padded rows are dropped).
+            f32x4 eg[4], ed[4];   // e^{g_r}, e^{g_C - g_r} at rows 16 mr + 4 lg + j
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr) {
+                eg[mr] = ld4(&sG[cb][1][16 * mr + 4 * lg]);
+                ed[mr] = ld4(&sG[cb][3][16 * mr + 4 * lg]);
+            }
+            bf16x8 fPh[6], fPl[6];
+#pragma unroll
+            for (int mr = 0, f = 0; mr < 4; ++mr)
+#pragma unroll
+                for (int ks = 0; ks <= mr / 2; ++ks, ++f) {
+                    fPh[f] = frag_rows_d(sPh, LDC, 16 * mr, 32 * ks, lane);
+                    fPl[f] = frag_rows_d(sPl, LDC, 16 * mr, 32 * ks, lane);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            bf16x8 dh[2], dl[2];
+            split_op(D[0], D[1], dh[0], dl[0]);
+            split_op(D[2], D[3], dh[1], dl[1]);
+            const size_t t0 = crow(n);
+            const rsrc_t ro = make_rsrc(o + (t0 * H + h) * DV + dv0 + cw,
+                                        cvalid(n) * H * DV * (uint32_t)sizeof(TO));
+#pragma unroll
+            for (int mr = 0; mr < 4; ++mr) {
+                const int f = mr < 2 ? mr : 2 * mr - 2;   // first fragment of row tile mr
+                f32x4 O = eg[mr] * QS[mr];
+#pragma unroll
+                for (int ks = 0; ks <= mr / 2; ++ks) {
+                    O = mfma32(fPh[f + ks], dh[ks], O);
+                    O = mfma32(fPl[f + ks], dh[ks], O);
+                    O = mfma32(fPh[f + ks], dl[ks], O);
+                }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 16 * mr + 4 * lg + j;
-                    U[mr][j] = sb[r] * (float)sV[r * LDV + cw + lm];
+                    buf_store(from_f32<TO>(O[j]), ro, (uint32_t)(r * H * DV + lm) * (uint32_t)sizeof(TO));
                 }
-                U[mr] = mfma32(frag_rows(sTU, LDC, 16 * mr, 0, lane), fV0, U[mr]);
-                if (mr >= 2) U[mr] = mfma32(frag_rows(sTU, LDC, 16 * mr, 32, lane), fV1, U[mr]);
+            }
+            // Delta~ = diag(e^{g_C - g}) Delta for the state update
+            split_op(D[0] * ed[0], D[1] * ed[1], th[0], tl[0]);
+            split_op(D[2] * ed[2], D[3] * ed[3], th[1], tl[1]);
+        }
+        __syncthreads();
+        // ================================ phase 2
+        if (chain) {
+            // S^T <- e^{g_C} S^T + K^T Delta~
+            bf16x8 fk[NMT][2];
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) fk[mt][ks] = frag_rows_d(sKT, LDC, 16 * mt, 32 * ks, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            const float egC = sG[cb][1][C - 1];
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) {
+                st[mt] = st[mt] * egC;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    st[mt] = mfma32(fk[mt][ks], th[ks], st[mt]);
+                    st[mt] = mfma32(fk[mt][ks], tl[ks], st[mt]);
+                }
             }
         }
-        __syncthreads();   // W complete
-
-        // ---- (4)-(5) wave-local: Delta, O, state update ----
+        __syncthreads();
+        // ================================ phase 3
         bf16x8 sh[NKS], sl[NKS];
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) split_op(st[2 * ks], st[2 * ks + 1], sh[ks], sl[ks]);
-
-        f32x4 D[4], O[4];
-#pragma unroll
-        for (int mr = 0; mr < 4; ++mr) {
-            f32x4 ws = zero4(), qs = zero4();
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 fw = frag_rows_d(sW, LDK, 16 * mr, 32 * ks, lane);
-                ws = mfma32(fw, sh[ks], ws);
-                ws = mfma32(fw, sl[ks], ws);
-                const bf16x8 fq = frag_rows_d(sQ, LDK, 16 * mr, 32 * ks, lane);
-                qs = mfma32(fq, sh[ks], qs);
-                qs = mfma32(fq, sl[ks], qs);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                D[mr][j] = U[mr][j] - ws[j];
-                O[mr][j] = seg[16 * mr + 4 * lg + j] * qs[j];
-            }
-        }
-        bf16x8 dh[2], dl[2];
-        split_op(D[0], D[1], dh[0], dl[0]);
-        split_op(D[2], D[3], dh[1], dl[1]);
-#pragma unroll
-        for (int mr = 0; mr < 4; ++mr) {
-#pragma unroll
-            for (int ks = 0; ks <= mr / 2; ++ks) {
-                const bf16x8 fph = frag_rows_d(sPh, LDC, 16 * mr, 32 * ks, lane);
-                const bf16x8 fpl = frag_rows_d(sPl, LDC, 16 * mr, 32 * ks, lane);
-                O[mr] = mfma32(fph, dh[ks], O[mr]);
-                O[mr] = mfma32(fpl, dh[ks], O[mr]);
-                O[mr] = mfma32(fph, dl[ks], O[mr]);
-            }
-        }
-#pragma unroll
-        for (int mr = 0; mr < 4; ++mr) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * mr + 4 * lg + j;
-                if (r < n) o[((size_t)(row0 + c0 + r) * H + h) * DV + dvw] = from_f32<TO>(O[mr][j]);
-            }
-        }
-
-        const float gC = sg[C - 1];
-        bf16x8 th[2], tl[2];
-        {
-            f32x4 Dt[4];
+        if (prep) {
+            // Q S^T for chunk m (state now S_m)
+            bf16x8 fq[4][NKS];
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    Dt[mr][j] = D[mr][j] * expf(gC - sg[16 * mr + 4 * lg + j]);
-            split_op(Dt[0], Dt[1], th[0], tl[0]);
-            split_op(Dt[2], Dt[3], th[1], tl[1]);
-        }
-        const float egC = seg[C - 1];
+                for (int ks = 0; ks < NKS; ++ks) fq[mr][ks] = frag_rows_d(sQ, LDK, 16 * mr, 32 * ks, lane);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
-            st[mt] = st[mt] * egC;
+            for (int ks = 0; ks < NKS; ++ks) split_op(st[2 * ks], st[2 * ks + 1], sh[ks], sl[ks]);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 fk = frag_cols_d(sK, LDK, 16 * mt, 32 * ks, lane);
-                st[mt] = mfma32(fk, th[ks], st[mt]);
-                st[mt] = mfma32(fk, tl[ks], st[mt]);
+            for (int mr = 0; mr < 4; ++mr) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    acc = mfma32(fq[mr][ks], sh[ks], acc);
+                    acc = mfma32(fq[mr][ks], sl[ks], acc);
+                }
+                QS[mr] = acc;
             }
         }
+        __syncthreads();
+        // ================================ phase 4
+        if (prep) {
+            // Y = K S^T for chunk m
+            bf16x8 fk[4][NKS];
+#pragma unroll
+            for (int mr = 0; mr < 4; ++mr)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) fk[mr][ks] = frag_rows_d(sK, LDK, 16 * mr, 32 * ks, lane);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mr = 0; mr < 4; ++mr) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    acc = mfma32(fk[mr][ks], sh[ks], acc);
+                    acc = mfma32(fk[mr][ks], sl[ks], acc);
+                }
+                Y[mr] = acc;
+            }
+        }
+        __syncthreads();
     }
 
     if (S_T) {
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt)
-            *reinterpret_cast<float4 *>(S_T + sbase + (size_t)dvw * DK + 16 * mt + 4 * lg) =
-                float4{st[mt][0], st[mt][1], st[mt][2], st[mt][3]};
+            *reinterpret_cast<f32x4 *>(S_T + sbase + (size_t)dvw * DK + 16 * mt + 4 * lg) = st[mt];
     }
 }
 
@@ -402,7 +622,7 @@ hipError_t launch_chunk_mfma_t(int units, int T, int H, int DV, const int32_t *c
     const int ndvt = DV / kDVT;
     const long nwg = (long)units * H * ndvt;
     const int xcd_map = ((long)units * H) % 8 == 0 ? 1 : 0;
-    hipLaunchKernelGGL((chunk_mfma_kernel<DK, TO>), dim3((unsigned)nwg), dim3(256), 0, st,
+    hipLaunchKernelGGL((chunk_mfma_kernel<DK, TO>), dim3((unsigned)nwg), dim3(512), 0, st,
                        T, H, DV, cu != nullptr ? 1 : 0, xcd_map, cu, (const bf16 *)q,
                        (const bf16 *)k, (const bf16 *)v, la, beta, S0, (TO *)o, S_T);
     return hipGetLastError();
