@@ -79,10 +79,14 @@ def run_decode(args, torch, gi, gdn, dev):
     e1.record(stream)
     torch.cuda.synchronize()
     warm_us = e0.elapsed_time(e1) * 1e3 / nsteps
-    flush = torch.empty(1 << 28, device=dev, dtype=torch.float32)   # 1 GiB > MALL + L2
+    # Evict the state from L2 and the 256 MB MALL by READING 1 GiB before each
+    # timed step (a write-based flush would leave dirty lines that drain to
+    # HBM during the timed step).
+    flush = torch.zeros(1 << 28, device=dev, dtype=torch.float32)
+    torch.cuda.synchronize()
     cold = []
     for t in range(args.cold_steps):
-        flush.fill_(float(t))
+        flush.sum()
         ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ea.record(stream)
         dstep(t)
@@ -102,7 +106,7 @@ def run_decode(args, torch, gi, gdn, dev):
         "frac_hbm_cold": round(dbytes / (cold_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "us_per_step_warm": round(warm_us, 2),
         "GB_s_warm": round(dbytes / (warm_us * 1e-6) / 1e9, 1),
-        "note": "cold = 1 GiB cache-evicting write before each timed step (median of "
+        "note": "cold = 1 GiB cache-evicting read before each timed step (median of "
                 f"{args.cold_steps}); warm = {nsteps} steps back to back, state resident in MALL",
     }
 

@@ -9,41 +9,24 @@
 // and the row is written back once: the kernel streams the fp32 state at the
 // HBM rate and does no other memory traffic worth counting.
 //
-// Mapping: 16 lanes own one row of S (d_k/16 consecutive floats each, so a
-// row is one contiguous 256/512-byte access); a 256-thread workgroup covers
-// 32 rows of one (b, h) in two passes whose loads are issued together.
+// Mapping: 16 lanes own one row of S.  Lane c holds the float4 groups c and
+// 16 + c of the row, so each load or store instruction of a wave covers four
+// contiguous 256-byte half-rows (fully coalesced).  A 256-thread workgroup
+// covers 16 rows of one (b, h); small workgroups keep many independent rows
+// in flight per CU.
 #include "gdn_common.h"
 
 namespace gdn {
 
-constexpr int kStepRowsPerWG = 32;
+constexpr int kStepRowsPerWG = 16;
 
-template <int N, typename TI>
-__device__ __forceinline__ void load_vec(const TI *p, float (&r)[N]);
-
-template <>
-__device__ __forceinline__ void load_vec<8, bf16>(const bf16 *p, float (&r)[8]) {
-    bf16x8 x = *reinterpret_cast<const bf16x8 *>(p);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = (float)x[i];
+// Load 4 consecutive elements as floats.
+__device__ __forceinline__ f32x4 load4(const bf16 *p) {
+    const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
+    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
 }
-template <>
-__device__ __forceinline__ void load_vec<4, bf16>(const bf16 *p, float (&r)[4]) {
-    bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = (float)x[i];
-}
-template <>
-__device__ __forceinline__ void load_vec<8, float>(const float *p, float (&r)[8]) {
-    float4 a = *reinterpret_cast<const float4 *>(p);
-    float4 b = *reinterpret_cast<const float4 *>(p + 4);
-    r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
-    r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
-}
-template <>
-__device__ __forceinline__ void load_vec<4, float>(const float *p, float (&r)[4]) {
-    float4 a = *reinterpret_cast<const float4 *>(p);
-    r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+__device__ __forceinline__ f32x4 load4(const float *p) {
+    return *reinterpret_cast<const f32x4 *>(p);
 }
 
 __device__ __forceinline__ float sum16(float x) {
@@ -54,69 +37,54 @@ __device__ __forceinline__ float sum16(float x) {
     return x;
 }
 
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) {
+    return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+}
+
 template <int DK, typename TI, typename TO>
 __global__ __launch_bounds__(256) void step_kernel(
     int DV, const TI *__restrict__ q, const TI *__restrict__ k,
     const TI *__restrict__ v, const float *__restrict__ log_alpha,
     const float *__restrict__ beta, float *__restrict__ S, TO *__restrict__ o) {
-    constexpr int VEC = DK / 16;   // floats of a row per lane
-    constexpr int NV4 = VEC / 4;
-    constexpr int NP = 2;          // passes of 4 rows per wave
+    constexpr int NV = DK / 64;    // float4 groups of a row per lane
     const int unit = blockIdx.x;   // b * H + h
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c = lane & 15;
+    const int row = blockIdx.y * kStepRowsPerWG + 4 * wave + (lane >> 4);
+    const bool live = row < DV;    // uniform over the 16 lanes of a row
 
-    float kr[VEC], qr[VEC];
-    load_vec<VEC, TI>(k + (size_t)unit * DK + c * VEC, kr);
-    load_vec<VEC, TI>(q + (size_t)unit * DK + c * VEC, qr);
+    f32x4 s[NV];
+    f32x4 *sp = reinterpret_cast<f32x4 *>(S + ((size_t)unit * DV + (live ? row : 0)) * DK);
+    if (live) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) s[i] = sp[16 * i + c];
+    }
+    f32x4 kr[NV], qr[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        kr[i] = load4(k + (size_t)unit * DK + 64 * i + 4 * c);
+        qr[i] = load4(q + (size_t)unit * DK + 64 * i + 4 * c);
+    }
     const float a = expf(log_alpha[unit]);
     const float b = beta[unit];
 
-    int row[NP];
-    float4 s[NP][NV4];
+    float kq = 0.f, pk = 0.f, pq = 0.f;
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        row[p] = blockIdx.y * kStepRowsPerWG + wave * (4 * NP) + p * 4 + (lane >> 4);
-        if (row[p] < DV) {
-            const float4 *sp = reinterpret_cast<const float4 *>(
-                S + ((size_t)unit * DV + row[p]) * DK + c * VEC);
-#pragma unroll
-            for (int i = 0; i < NV4; ++i) s[p][i] = sp[i];
+    for (int i = 0; i < NV; ++i) {
+        kq += dot4(kr[i], qr[i]);
+        if (live) {
+            pk += dot4(s[i], kr[i]);
+            pq += dot4(s[i], qr[i]);
         }
     }
-
-    float kq = 0.f;
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) kq += kr[i] * qr[i];
     kq = sum16(kq);
-
+    pk = sum16(pk);
+    pq = sum16(pq);
+    if (!live) return;
+    const float u = b * (to_f32(v[(size_t)unit * DV + row]) - a * pk);
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        if (row[p] >= DV) continue;   // uniform over the 16 lanes of a row
-        float pk = 0.f, pq = 0.f;
-#pragma unroll
-        for (int i = 0; i < NV4; ++i) {
-            pk += s[p][i].x * kr[4 * i] + s[p][i].y * kr[4 * i + 1] +
-                  s[p][i].z * kr[4 * i + 2] + s[p][i].w * kr[4 * i + 3];
-            pq += s[p][i].x * qr[4 * i] + s[p][i].y * qr[4 * i + 1] +
-                  s[p][i].z * qr[4 * i + 2] + s[p][i].w * qr[4 * i + 3];
-        }
-        pk = sum16(pk);
-        pq = sum16(pq);
-        const float vr = to_f32(v[(size_t)unit * DV + row[p]]);
-        const float u = b * (vr - a * pk);
-        float4 *sp = reinterpret_cast<float4 *>(S + ((size_t)unit * DV + row[p]) * DK + c * VEC);
-#pragma unroll
-        for (int i = 0; i < NV4; ++i) {
-            float4 n;
-            n.x = a * s[p][i].x + u * kr[4 * i];
-            n.y = a * s[p][i].y + u * kr[4 * i + 1];
-            n.z = a * s[p][i].z + u * kr[4 * i + 2];
-            n.w = a * s[p][i].w + u * kr[4 * i + 3];
-            sp[i] = n;
-        }
-        if (c == 0) o[(size_t)unit * DV + row[p]] = from_f32<TO>(a * pq + u * kq);
-    }
+    for (int i = 0; i < NV; ++i) sp[16 * i + c] = a * s[i] + u * kr[i];
+    if (c == 0) o[(size_t)unit * DV + row] = from_f32<TO>(a * pq + u * kq);
 }
 
 template <int DK, typename TI, typename TO>
