@@ -31,10 +31,11 @@
 // every LDS buffer is written by one phase and read in later ones before it
 // is overwritten, so apart from the gates nothing is double-buffered:
 //   phase  producers (chunk n+1)               consumers (chunk n)
-//   1      store q,k, gate prefix, prefetch    U, Delta, P Delta, write o
+//   1      store q,k, prefetch chunk n+2       U, Delta, P Delta, write o
 //   2      K K^T, Q K^T -> A, P               S <- e^{g_C} S + K^T Delta~
-//   3      diagonal inverses, store v          Q S^T for chunk n+1
-//   4      off-diagonal T, T diag(.), K^T      Y = K S^T for chunk n+1
+//   3      diagonal inverses, store v, K^T     Q S^T for chunk n+1
+//   4      off-diagonal T, T diag(.),          Y = K S^T for chunk n+1
+//          gate prefix of chunk n+2
 // Global loads and stores go through buffer resources sized to the valid
 // rows of the chunk: rows past a ragged end read as zero and their stores
 // are dropped by the hardware range check, so no lane branches on bounds.
@@ -45,6 +46,8 @@
 #include "gdn_common.h"
 
 namespace gdn {
+
+template <int N> struct IntC { static constexpr int value = N; };
 
 constexpr int kC = 64;     // chunk length
 constexpr int kDVT = 64;   // d_v columns per workgroup (16 per consumer wave)
@@ -177,12 +180,27 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 pq[i] = buf_load16(rq, off);
                 pk[i] = buf_load16(rk, off);
             }
-            if (pw == 0) {
+            if (pw == 3) {
                 const rsrc_t ra = make_rsrc(log_alpha + t0 * H + h, nv * H * 4);
                 const rsrc_t rb = make_rsrc(beta + t0 * H + h, nv * H * 4);
                 pla = buf_load4(ra, (uint32_t)(lane * H) * 4);
                 pbe = buf_load4(rb, (uint32_t)(lane * H) * 4);
             }
+        };
+        // Gate prefix of the prefetched chunk into gate buffer `buf`, one token
+        // per lane of wave 3 (padded tokens add 0).
+        auto scan_gates = [&](int buf) {
+            float x = pla;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off);
+                if (lane >= off) x += y;
+            }
+            const float gC = __shfl(x, 63);
+            sG[buf][0][lane] = x;
+            sG[buf][1][lane] = exp_neg(x);
+            sG[buf][2][lane] = pbe;
+            sG[buf][3][lane] = exp_neg(gC - x);
         };
         auto prefetch_v = [&](int c) {
             const size_t t0 = crow(c);
@@ -197,6 +215,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
         if (N > 0) {
             prefetch_qk(0);
             prefetch_v(0);
+            if (pw == 3) scan_gates(0);   // later chunks are scanned a phase-4 ahead
         }
         for (int n = -1; n < N; ++n) {
             const int m = n + 1;           // chunk being prepared
@@ -212,19 +231,6 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     reinterpret_cast<bf16x4 *>(dq)[1] = bf16x4{pq[i][4], pq[i][5], pq[i][6], pq[i][7]};
                     reinterpret_cast<bf16x4 *>(dk)[0] = bf16x4{pk[i][0], pk[i][1], pk[i][2], pk[i][3]};
                     reinterpret_cast<bf16x4 *>(dk)[1] = bf16x4{pk[i][4], pk[i][5], pk[i][6], pk[i][7]};
-                }
-                if (pw == 0) {   // gate prefix, one token per lane (padded tokens add 0)
-                    float x = pla;
-#pragma unroll
-                    for (int off = 1; off < 64; off <<= 1) {
-                        const float y = __shfl_up(x, off);
-                        if (lane >= off) x += y;
-                    }
-                    const float gC = __shfl(x, 63);
-                    sG[gb][0][lane] = x;
-                    sG[gb][1][lane] = exp_neg(x);
-                    sG[gb][2][lane] = pbe;
-                    sG[gb][3][lane] = exp_neg(gC - x);
                 }
                 if (m + 1 < N) prefetch_qk(m + 1);
             }
@@ -249,20 +255,16 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     const int r = 16 * ti + lm, i0 = 16 * tj + 4 * lg;
                     const float gr = sG[gb][0][r], br = sG[gb][2][r];
                     const f32x4 gi = ld4(&sG[gb][0][i0]);
-                    bf16x4 ph, pl;
+                    f32x4 dec;   // e^{g_r - g_i} on and below the diagonal, else 0
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float p = (i0 + j <= r) ? exp_neg(gr - gi[j]) * PT[j] : 0.f;
-                        ph[j] = (bf16)p;
-                        pl[j] = (bf16)(p - (float)ph[j]);
-                    }
-                    *reinterpret_cast<bf16x4 *>(sPh + r * LDC + i0) = ph;
-                    *reinterpret_cast<bf16x4 *>(sPl + r * LDC + i0) = pl;
+                    for (int j = 0; j < 4; ++j) dec[j] = (i0 + j <= r) ? exp_neg(gr - gi[j]) : 0.f;
+                    const f32x4 p4 = dec * PT;
+                    bf16x8 ph, pl;
+                    split_op(p4, p4, ph, pl);
+                    *reinterpret_cast<bf16x4 *>(sPh + r * LDC + i0) = bf16x4{ph[0], ph[1], ph[2], ph[3]};
+                    *reinterpret_cast<bf16x4 *>(sPl + r * LDC + i0) = bf16x4{pl[0], pl[1], pl[2], pl[3]};
                     if (ti > tj) {
-                        f32x4 a4;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) a4[j] = br * exp_neg(gr - gi[j]) * G[j];
-                        *reinterpret_cast<bf16x4 *>(sA + r * LDC + i0) = to_bf16x4(a4);
+                        *reinterpret_cast<bf16x4 *>(sA + r * LDC + i0) = to_bf16x4(br * dec * G);
                     } else {
                         // Diagonal tile: K K^T is symmetric, so the registers also
                         // hold rows rr = i0 + j of column r; store A's block
@@ -363,31 +365,27 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             }
             __syncthreads();
             // ================================ phase 4
-            if (prep && pw == 0) {
-                // Off-diagonal blocks band by band, all in this wave's registers:
-                // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj  (16x16x16 MFMA).
-                bf16x4 RTd[4], Trow[4];
+            // Off-diagonal blocks of block column j, top to bottom:
+            // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj (16x16x16 MFMA).  Column j
+            // only needs its own blocks and the diagonal ones, so producer wave
+            // j < 3 computes column j with no exchange between waves.
+            auto column = [&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                bf16x4 Bop[4];   // B operands: T_jj, then T_kj (k > j)
+                f32x4 RT[4];     // RT[k] = T_kj in D layout, k > j
+                Bop[j] = to_bf16x4(ld4(sTdT + j * BLK + lm * 16 + 4 * lg));
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    RTd[b] = to_bf16x4(ld4(sTdT + b * BLK + lm * 16 + 4 * lg));
-                    Trow[b] = to_bf16x4(ld4(sTd + b * BLK + lm * 16 + 4 * lg));
-                }
-                f32x4 RT[4][4];
+                for (int i = j + 1; i < 4; ++i) {
+                    f32x4 Yb = zero4();
 #pragma unroll
-                for (int d = 1; d < 4; ++d) {
-#pragma unroll
-                    for (int i = d; i < 4; ++i) {
-                        const int j = i - d;
-                        f32x4 Yb = zero4();
-#pragma unroll
-                        for (int kk = j; kk < i; ++kk) {
-                            const bf16x4 a = *reinterpret_cast<const bf16x4 *>(
-                                sA + (16 * i + lm) * LDC + 16 * kk + 4 * lg);
-                            const bf16x4 b = (kk == j) ? RTd[j] : to_bf16x4(RT[kk][j]);
-                            Yb = mfma16(a, b, Yb);
-                        }
-                        RT[i][j] = -mfma16(Trow[i], to_bf16x4(Yb), zero4());
+                    for (int kk = j; kk < i; ++kk) {
+                        const bf16x4 a = *reinterpret_cast<const bf16x4 *>(
+                            sA + (16 * i + lm) * LDC + 16 * kk + 4 * lg);
+                        Yb = mfma16(a, Bop[kk], Yb);
                     }
+                    const bf16x4 Trow = to_bf16x4(ld4(sTd + i * BLK + lm * 16 + 4 * lg));
+                    RT[i] = -mfma16(Trow, to_bf16x4(Yb), zero4());
+                    Bop[i] = to_bf16x4(RT[i]);
                 }
                 // Scale column c = 16 j + lm by beta_c (and e^{g_c}), round once
                 // to bf16, and transpose with an identity MFMA (exact) so that
@@ -395,35 +393,43 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 bf16x4 eye;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) eye[s] = (bf16)((4 * lg + s == lm) ? 1.f : 0.f);
+                const int c = 16 * j + lm;
+                const float bc = sG[gb][2][c], wc = bc * sG[gb][1][c];
 #pragma unroll
-                for (int i = 1; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < i; ++j) {
-                        const int c = 16 * j + lm;
-                        const float bc = sG[gb][2][c], wc = bc * sG[gb][1][c];
-                        const f32x4 tu = mfma16(to_bf16x4(RT[i][j] * bc), eye, zero4());
-                        const f32x4 tw = mfma16(to_bf16x4(RT[i][j] * wc), eye, zero4());
-                        const int off = (16 * i + lm) * LDC + 16 * j + 4 * lg;
-                        *reinterpret_cast<bf16x4 *>(sTU + off) = to_bf16x4(tu);
-                        *reinterpret_cast<bf16x4 *>(sTW + off) = to_bf16x4(tw);
-                    }
-            } else if (prep) {
-                const int t3 = ptid - 64;   // 0..191
-                // diagonal blocks of (T - I) diag(beta) and T diag(beta e^g)
-                for (int it = t3; it < 256; it += 192) {
-                    const int b = it >> 6, r = (it >> 2) & 15, c4 = 4 * (it & 3);
-                    const f32x4 tv = ld4(sTd + b * BLK + r * 16 + c4);
-                    const f32x4 bc = ld4(&sG[gb][2][16 * b + c4]);
-                    const f32x4 ec = ld4(&sG[gb][1][16 * b + c4]);
-                    bf16x4 tu, tw;
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        tu[s] = (bf16)((c4 + s < r) ? tv[s] * bc[s] : 0.f);
-                        tw[s] = (bf16)((c4 + s <= r) ? tv[s] * bc[s] * ec[s] : 0.f);
-                    }
-                    *reinterpret_cast<bf16x4 *>(sTU + (16 * b + r) * LDC + 16 * b + c4) = tu;
-                    *reinterpret_cast<bf16x4 *>(sTW + (16 * b + r) * LDC + 16 * b + c4) = tw;
+                for (int i = j + 1; i < 4; ++i) {
+                    const f32x4 tu = mfma16(to_bf16x4(RT[i] * bc), eye, zero4());
+                    const f32x4 tw = mfma16(to_bf16x4(RT[i] * wc), eye, zero4());
+                    const int off = (16 * i + lm) * LDC + 16 * j + 4 * lg;
+                    *reinterpret_cast<bf16x4 *>(sTU + off) = to_bf16x4(tu);
+                    *reinterpret_cast<bf16x4 *>(sTW + off) = to_bf16x4(tw);
                 }
+            };
+            if (prep) {
+                if (pw == 0) column(IntC<0>{});
+                else if (pw == 1) column(IntC<1>{});
+                else if (pw == 2) column(IntC<2>{});
+            }
+            // Diagonal block b of (T - I) diag(beta) and T diag(beta e^g), one
+            // (row, 4 columns) per lane.
+            auto diag_conv = [&](int b) {
+                const int r = lane >> 2, c4 = 4 * (lane & 3);
+                const f32x4 tv = ld4(sTd + b * BLK + r * 16 + c4);
+                const f32x4 bc = ld4(&sG[gb][2][16 * b + c4]);
+                const f32x4 ec = ld4(&sG[gb][1][16 * b + c4]);
+                bf16x4 tu, tw;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    tu[s] = (bf16)((c4 + s < r) ? tv[s] * bc[s] : 0.f);
+                    tw[s] = (bf16)((c4 + s <= r) ? tv[s] * bc[s] * ec[s] : 0.f);
+                }
+                *reinterpret_cast<bf16x4 *>(sTU + (16 * b + r) * LDC + 16 * b + c4) = tu;
+                *reinterpret_cast<bf16x4 *>(sTW + (16 * b + r) * LDC + 16 * b + c4) = tw;
+            };
+            if (prep) {
+                diag_conv(pw);
+                // chunk m+1's gates go to the buffer chunk n used (the consumers
+                // are done with it)
+                if (pw == 3 && m + 1 < N) scan_gates(gb ^ 1);
             }
             __syncthreads();
         }
