@@ -64,6 +64,14 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) { return to_bf16x4(x[0], x[
 
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
+// K, V and the transposed T factors sit in LDS unpadded with their 8-byte
+// chunks permuted within each row: chunk c of row r is stored at chunk
+// c ^ swz(r).  Both kinds of access then hit 16 distinct bank pairs per 16
+// lanes: 16 rows x one chunk (row fragments, D-layout stores) and 4
+// consecutive rows x 4 consecutive chunks (transpose reads, which start at a
+// multiple of 4 rows and 4 chunks).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
@@ -93,10 +101,9 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     constexpr int NMT = DK / 16;        // 16-row tiles over d_k
     // Padded row lengths (elements).  Operands are read 8 bytes per lane, 16
     // lanes (16 rows) per LDS cycle: a row stride of 2 mod 4 dwords puts those
-    // 16 rows on 16 distinct bank pairs.
+    // 16 rows on 16 distinct bank pairs.  (K and V are swizzled instead.)
     constexpr int LDK = DK + 4;
     constexpr int LDC = C + 4;
-    constexpr int LDV = kDVT + 8;       // v rows are written 16 bytes at a time
     constexpr int BLK = 260;            // stride of the 16x16 fp32 diagonal blocks (4 banks apart)
     constexpr int QK_PIECES = C * DK / 8;            // 16-byte pieces of a q or k chunk
     constexpr int QK_PER_THR = QK_PIECES / 256;
@@ -104,15 +111,15 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     static_assert(QK_PIECES % 256 == 0 && V_PER_THR * 256 == C * kDVT / 8, "piece split");
 
     __shared__ __attribute__((aligned(16))) bf16 sQ[C * LDK];
-    __shared__ __attribute__((aligned(16))) bf16 sK[C * LDK];
-    __shared__ __attribute__((aligned(16))) bf16 sKT[DK * LDC];     // K^T [d_k][token]
-    __shared__ __attribute__((aligned(16))) bf16 sV[C * LDV];
+    __shared__ __attribute__((aligned(16))) bf16 sK[2][C * DK];     // K of chunks m, m-1 (swizzled)
+    __shared__ __attribute__((aligned(16))) bf16 sV[C * kDVT];      // V slice (swizzled)
     __shared__ __attribute__((aligned(16))) bf16 sA[C * LDC];       // A, off-diagonal blocks
     __shared__ __attribute__((aligned(16))) float sAd[4 * BLK];     // A diag blocks, [b][col][row]
     __shared__ __attribute__((aligned(16))) float sTd[4 * BLK];     // T diag blocks, [b][row][col]
     __shared__ __attribute__((aligned(16))) float sTdT[4 * BLK];    // T diag blocks, [b][col][row]
-    __shared__ __attribute__((aligned(16))) bf16 sTU[C * LDC];      // (T - I) diag(beta)
-    __shared__ __attribute__((aligned(16))) bf16 sTW[C * LDC];      // T diag(beta e^g)
+    // transposed, swizzled: row c holds column c of the factor
+    __shared__ __attribute__((aligned(16))) bf16 sTUt[C * C];       // ((T - I) diag(beta))^T
+    __shared__ __attribute__((aligned(16))) bf16 sTWt[C * C];       // (T diag(beta e^g))^T
     __shared__ __attribute__((aligned(16))) bf16 sPh[C * LDC];      // P = tril(QK^T) o decay, hi
     __shared__ __attribute__((aligned(16))) bf16 sPl[C * LDC];      // P, lo
     // gates of a chunk, double-buffered: g, e^g, beta, e^{g_C - g}
@@ -138,6 +145,23 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
     const int lm = lane & 15, lg = lane >> 4;
 
+    // Operand element (i, k) = X[32 ks + k][16 cb + i] of a swizzled row-major
+    // X with `ld` elements per row, k in D-order: a column gather by two
+    // transpose reads (K^T, V and the T factors from their transposes).
+    auto tr_frag = [&](const bf16 *x, int ld, int cb, int ks) {
+        const int j = lm >> 2, q4 = lm & 3;
+        const bf16 *p = x + (32 * ks + 4 * lg + j) * ld + 4 * ((4 * cb + q4) ^ ((j << 2) | lg));
+        return cat(lds_read_tr(p), lds_read_tr(p + 16 * ld));
+    };
+    // Row fragment of a swizzled K tile: rows row0..row0+15 (row0 a multiple
+    // of 16), k0..k0+31 in D-order.
+    auto k_rows = [&](const bf16 *kb, int row0, int k0) {
+        const bf16 *p = kb + (row0 + lm) * DK;
+        const int f = swz(lm), c = (k0 >> 2) + lg;
+        return cat(*reinterpret_cast<const bf16x4 *>(p + 4 * (c ^ f)),
+                   *reinterpret_cast<const bf16x4 *>(p + 4 * ((c + 4) ^ f)));
+    };
+
     long row0, L;
     if (varlen) {
         row0 = cu_seqlens[unit];
@@ -153,8 +177,10 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 
     // Upper off-diagonal blocks of the LDS factors are never written: zero them once.
     for (int e = tid; e < C * LDC / 2; e += 512) {
-        reinterpret_cast<uint32_t *>(sTU)[e] = 0u;
-        reinterpret_cast<uint32_t *>(sTW)[e] = 0u;
+        if (e < C * C / 2) {
+            reinterpret_cast<uint32_t *>(sTUt)[e] = 0u;
+            reinterpret_cast<uint32_t *>(sTWt)[e] = 0u;
+        }
         reinterpret_cast<uint32_t *>(sPh)[e] = 0u;
         reinterpret_cast<uint32_t *>(sPl)[e] = 0u;
     }
@@ -226,11 +252,13 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 #pragma unroll
                 for (int i = 0; i < QK_PER_THR; ++i) {
                     const int e = ptid + 256 * i, r = e / (DK / 8), p = e % (DK / 8);
-                    bf16 *dq = sQ + r * LDK + 8 * p, *dk = sK + r * LDK + 8 * p;
+                    bf16 *dq = sQ + r * LDK + 8 * p;
+                    bf16 *dk = sK[m & 1] + r * DK;
+                    const int f = swz(r);
                     reinterpret_cast<bf16x4 *>(dq)[0] = bf16x4{pq[i][0], pq[i][1], pq[i][2], pq[i][3]};
                     reinterpret_cast<bf16x4 *>(dq)[1] = bf16x4{pq[i][4], pq[i][5], pq[i][6], pq[i][7]};
-                    reinterpret_cast<bf16x4 *>(dk)[0] = bf16x4{pk[i][0], pk[i][1], pk[i][2], pk[i][3]};
-                    reinterpret_cast<bf16x4 *>(dk)[1] = bf16x4{pk[i][4], pk[i][5], pk[i][6], pk[i][7]};
+                    *reinterpret_cast<bf16x4 *>(dk + 4 * ((2 * p) ^ f)) = bf16x4{pk[i][0], pk[i][1], pk[i][2], pk[i][3]};
+                    *reinterpret_cast<bf16x4 *>(dk + 4 * ((2 * p + 1) ^ f)) = bf16x4{pk[i][4], pk[i][5], pk[i][6], pk[i][7]};
                 }
                 if (m + 1 < N) prefetch_qk(m + 1);
             }
@@ -240,9 +268,14 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 // K K^T and Q K^T tiles (ti, tj), tj <= ti, 10 in all, 2-3 per wave;
                 // a wave loads each 16-row block of K or Q it needs once.
                 typedef bf16x8 Frag[NKS];
-                auto load_rows = [&](const bf16 *src, int blk, Frag &f) {
+                const bf16 *sKm = sK[m & 1];
+                auto load_q = [&](int blk, Frag &f) {
 #pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) f[ks] = frag_rows_d(src, LDK, 16 * blk, 32 * ks, lane);
+                    for (int ks = 0; ks < NKS; ++ks) f[ks] = frag_rows_d(sQ, LDK, 16 * blk, 32 * ks, lane);
+                };
+                auto load_k = [&](int blk, Frag &f) {
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) f[ks] = k_rows(sKm, 16 * blk, 32 * ks);
                 };
                 auto tile = [&](const int ti, const int tj, const Frag &fKj, const Frag &fKi,
                                 const Frag &fQi) {
@@ -279,27 +312,27 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 };
                 if (pw == 0) {
                     Frag k0, q0, k3, q3;
-                    load_rows(sK, 0, k0); load_rows(sQ, 0, q0);
-                    load_rows(sK, 3, k3); load_rows(sQ, 3, q3);
+                    load_k(0, k0); load_q(0, q0);
+                    load_k(3, k3); load_q(3, q3);
                     tile(0, 0, k0, k0, q0);
                     tile(3, 0, k0, k3, q3);
                 } else if (pw == 1) {
                     Frag k0, k1, q1, k3, q3;
-                    load_rows(sK, 0, k0); load_rows(sK, 1, k1); load_rows(sQ, 1, q1);
-                    load_rows(sK, 3, k3); load_rows(sQ, 3, q3);
+                    load_k(0, k0); load_k(1, k1); load_q(1, q1);
+                    load_k(3, k3); load_q(3, q3);
                     tile(1, 0, k0, k1, q1);
                     tile(1, 1, k1, k1, q1);
                     tile(3, 1, k1, k3, q3);
                 } else if (pw == 2) {
                     Frag k0, k1, k2, q2;
-                    load_rows(sK, 0, k0); load_rows(sK, 1, k1);
-                    load_rows(sK, 2, k2); load_rows(sQ, 2, q2);
+                    load_k(0, k0); load_k(1, k1);
+                    load_k(2, k2); load_q(2, q2);
                     tile(2, 0, k0, k2, q2);
                     tile(2, 1, k1, k2, q2);
                     tile(2, 2, k2, k2, q2);
                 } else {
                     Frag k2, k3, q3;
-                    load_rows(sK, 2, k2); load_rows(sK, 3, k3); load_rows(sQ, 3, q3);
+                    load_k(2, k2); load_k(3, k3); load_q(3, q3);
                     tile(3, 2, k2, k3, q3);
                     tile(3, 3, k3, k3, q3);
                 }
@@ -310,7 +343,10 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 #pragma unroll
                 for (int i = 0; i < V_PER_THR; ++i) {
                     const int e = ptid + 256 * i, r = e / (kDVT / 8), p = e % (kDVT / 8);
-                    *reinterpret_cast<bf16x8 *>(sV + r * LDV + 8 * p) = pv[i];
+                    bf16 *dv = sV + r * kDVT;
+                    const int f = swz(r);
+                    *reinterpret_cast<bf16x4 *>(dv + 4 * ((2 * p) ^ f)) = bf16x4{pv[i][0], pv[i][1], pv[i][2], pv[i][3]};
+                    *reinterpret_cast<bf16x4 *>(dv + 4 * ((2 * p + 1) ^ f)) = bf16x4{pv[i][4], pv[i][5], pv[i][6], pv[i][7]};
                 }
                 if (pw == 0) {
                     // Diagonal blocks of T = (I + A)^{-1} in fp32, one wave: lane
@@ -350,16 +386,6 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     for (int q4 = 0; q4 < 4; ++q4)
                         *reinterpret_cast<f32x4 *>(sTdT + lg * BLK + lm * 16 + 4 * q4) =
                             f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
-                } else {
-                    // K^T of chunk m for its state update (the consumers finished
-                    // with the previous K^T in phase 2)
-                    for (int e = ptid - 64; e < QK_PIECES; e += 192) {
-                        const int t = e % C, p = e / C;
-                        const bf16x4 *src = reinterpret_cast<const bf16x4 *>(sK + t * LDK + 8 * p);
-                        const bf16x8 kv = cat(src[0], src[1]);
-#pragma unroll
-                        for (int s = 0; s < 8; ++s) sKT[(8 * p + s) * LDC + t] = kv[s];
-                    }
                 }
                 if (m + 1 < N) prefetch_v(m + 1);
             }
@@ -387,21 +413,16 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     RT[i] = -mfma16(Trow, to_bf16x4(Yb), zero4());
                     Bop[i] = to_bf16x4(RT[i]);
                 }
-                // Scale column c = 16 j + lm by beta_c (and e^{g_c}), round once
-                // to bf16, and transpose with an identity MFMA (exact) so that
-                // each lane writes 4 consecutive columns of one row.
-                bf16x4 eye;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) eye[s] = (bf16)((4 * lg + s == lm) ? 1.f : 0.f);
+                // Scale column c = 16 j + lm by beta_c (and e^{g_c}) and round
+                // once to bf16; the lane's 4 rows are 4 consecutive entries of
+                // row c of the transposed factors.
                 const int c = 16 * j + lm;
                 const float bc = sG[gb][2][c], wc = bc * sG[gb][1][c];
 #pragma unroll
                 for (int i = j + 1; i < 4; ++i) {
-                    const f32x4 tu = mfma16(to_bf16x4(RT[i] * bc), eye, zero4());
-                    const f32x4 tw = mfma16(to_bf16x4(RT[i] * wc), eye, zero4());
-                    const int off = (16 * i + lm) * LDC + 16 * j + 4 * lg;
-                    *reinterpret_cast<bf16x4 *>(sTU + off) = to_bf16x4(tu);
-                    *reinterpret_cast<bf16x4 *>(sTW + off) = to_bf16x4(tw);
+                    const int off = c * C + 4 * ((4 * i + lg) ^ swz(c));
+                    *reinterpret_cast<bf16x4 *>(sTUt + off) = to_bf16x4(RT[i] * bc);
+                    *reinterpret_cast<bf16x4 *>(sTWt + off) = to_bf16x4(RT[i] * wc);
                 }
             };
             if (prep) {
@@ -410,20 +431,20 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 else if (pw == 2) column(IntC<2>{});
             }
             // Diagonal block b of (T - I) diag(beta) and T diag(beta e^g), one
-            // (row, 4 columns) per lane.
+            // (column, 4 rows) per lane.
             auto diag_conv = [&](int b) {
-                const int r = lane >> 2, c4 = 4 * (lane & 3);
-                const f32x4 tv = ld4(sTd + b * BLK + r * 16 + c4);
-                const f32x4 bc = ld4(&sG[gb][2][16 * b + c4]);
-                const f32x4 ec = ld4(&sG[gb][1][16 * b + c4]);
+                const int cl = lane >> 2, r4 = 4 * (lane & 3), c = 16 * b + cl;
+                const f32x4 tv = ld4(sTdT + b * BLK + cl * 16 + r4);   // T[16 b + r4 + s][c]
+                const float bc = sG[gb][2][c], wc = bc * sG[gb][1][c];
                 bf16x4 tu, tw;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    tu[s] = (bf16)((c4 + s < r) ? tv[s] * bc[s] : 0.f);
-                    tw[s] = (bf16)((c4 + s <= r) ? tv[s] * bc[s] * ec[s] : 0.f);
+                    tu[s] = (bf16)((r4 + s > cl) ? tv[s] * bc : 0.f);
+                    tw[s] = (bf16)((r4 + s >= cl) ? tv[s] * wc : 0.f);
                 }
-                *reinterpret_cast<bf16x4 *>(sTU + (16 * b + r) * LDC + 16 * b + c4) = tu;
-                *reinterpret_cast<bf16x4 *>(sTW + (16 * b + r) * LDC + 16 * b + c4) = tw;
+                const int off = c * C + 4 * ((4 * b + (lane & 3)) ^ swz(c));
+                *reinterpret_cast<bf16x4 *>(sTUt + off) = tu;
+                *reinterpret_cast<bf16x4 *>(sTWt + off) = tw;
             };
             if (prep) {
                 diag_conv(pw);
@@ -441,7 +462,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     const int dvw = dv0 + cw + lm;      // this lane's d_v column
     const size_t sbase = ((size_t)unit * H + h) * DV * DK;
     f32x4 st[NMT];      // st[mt][j] = S^T[16 mt + 4 lg + j][dvw]
-    f32x4 QS[4], Y[4];  // Q S^T and K S^T of the next chunk, rows 16 mr + 4 lg + j
+    f32x4 QS[4];        // diag(e^g) Q S^T of the next chunk, rows 16 mr + 4 lg + j
+    bf16x8 yh[2], yl[2];  // K S^T of the next chunk, hi + lo bf16 (D order)
     bf16x8 th[2], tl[2];
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
@@ -460,20 +482,17 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             f32x4 bt[4];   // beta_r at rows 16 mr + 4 lg + j
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr) bt[mr] = ld4(&sG[cb][2][16 * mr + 4 * lg]);
-            const bf16x8 fV0 = frag_cols_d(sV, LDV, cw, 0, lane);
-            const bf16x8 fV1 = frag_cols_d(sV, LDV, cw, 32, lane);
+            const bf16x8 fV0 = tr_frag(sV, kDVT, cw / 16, 0);
+            const bf16x8 fV1 = tr_frag(sV, kDVT, cw / 16, 1);
             bf16x8 fTU[6], fTW[6];   // fragment (mr, ks), ks <= mr / 2, in that order
 #pragma unroll
             for (int mr = 0, f = 0; mr < 4; ++mr)
 #pragma unroll
                 for (int ks = 0; ks <= mr / 2; ++ks, ++f) {
-                    fTU[f] = frag_rows_d(sTU, LDC, 16 * mr, 32 * ks, lane);
-                    fTW[f] = frag_rows_d(sTW, LDC, 16 * mr, 32 * ks, lane);
+                    fTU[f] = tr_frag(sTUt, C, mr, ks);
+                    fTW[f] = tr_frag(sTWt, C, mr, ks);
                 }
             __builtin_amdgcn_sched_barrier(0);
-            bf16x8 yh[2], yl[2];
-            split_op(Y[0], Y[1], yh[0], yl[0]);
-            split_op(Y[2], Y[3], yh[1], yl[1]);
             // U = diag(beta) V + (T - I) diag(beta) V; the D-order V operand
             // holds exactly this lane's rows, which gives the diagonal term.
             f32x4 U[4];
@@ -499,12 +518,9 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             }
             // O = diag(e^g) Q S^T + P Delta, stored through a buffer resource
             // covering the valid rows of this chunk (padded rows are dropped).
-            f32x4 eg[4], ed[4];   // e^{g_r}, e^{g_C - g_r} at rows 16 mr + 4 lg + j
+            f32x4 ed[4];   // e^{g_C - g_r} at rows 16 mr + 4 lg + j
 #pragma unroll
-            for (int mr = 0; mr < 4; ++mr) {
-                eg[mr] = ld4(&sG[cb][1][16 * mr + 4 * lg]);
-                ed[mr] = ld4(&sG[cb][3][16 * mr + 4 * lg]);
-            }
+            for (int mr = 0; mr < 4; ++mr) ed[mr] = ld4(&sG[cb][3][16 * mr + 4 * lg]);
             bf16x8 fPh[6], fPl[6];
 #pragma unroll
             for (int mr = 0, f = 0; mr < 4; ++mr)
@@ -523,7 +539,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr) {
                 const int f = mr < 2 ? mr : 2 * mr - 2;   // first fragment of row tile mr
-                f32x4 O = eg[mr] * QS[mr];
+                f32x4 O = QS[mr];
 #pragma unroll
                 for (int ks = 0; ks <= mr / 2; ++ks) {
                     O = mfma32(fPh[f + ks], dh[ks], O);
@@ -548,7 +564,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) fk[mt][ks] = frag_rows_d(sKT, LDC, 16 * mt, 32 * ks, lane);
+                for (int ks = 0; ks < 2; ++ks) fk[mt][ks] = tr_frag(sK[n & 1], DK, mt, ks);
             __builtin_amdgcn_sched_barrier(0);
             const float egC = sG[cb][1][C - 1];
 #pragma unroll
@@ -565,7 +581,10 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
         // ================================ phase 3
         bf16x8 sh[NKS], sl[NKS];
         if (prep) {
-            // Q S^T for chunk m (state now S_m)
+            // diag(e^g) Q S^T for chunk m (state now S_m)
+            f32x4 eg[4];   // e^{g_r} of chunk m at rows 16 mr + 4 lg + j
+#pragma unroll
+            for (int mr = 0; mr < 4; ++mr) eg[mr] = ld4(&sG[m & 1][1][16 * mr + 4 * lg]);
             bf16x8 fq[4][NKS];
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr)
@@ -582,18 +601,19 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     acc = mfma32(fq[mr][ks], sh[ks], acc);
                     acc = mfma32(fq[mr][ks], sl[ks], acc);
                 }
-                QS[mr] = acc;
+                QS[mr] = acc * eg[mr];
             }
         }
         __syncthreads();
         // ================================ phase 4
         if (prep) {
-            // Y = K S^T for chunk m
+            // Y = K S^T for chunk m, kept as a hi + lo pair
+            f32x4 Y[4];
             bf16x8 fk[4][NKS];
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr)
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) fk[mr][ks] = frag_rows_d(sK, LDK, 16 * mr, 32 * ks, lane);
+                for (int ks = 0; ks < NKS; ++ks) fk[mr][ks] = k_rows(sK[m & 1], 16 * mr, 32 * ks);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr) {
@@ -605,6 +625,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 }
                 Y[mr] = acc;
             }
+            split_op(Y[0], Y[1], yh[0], yl[0]);
+            split_op(Y[2], Y[3], yh[1], yl[1]);
         }
         __syncthreads();
     }

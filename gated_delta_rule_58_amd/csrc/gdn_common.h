@@ -121,4 +121,16 @@ __device__ __forceinline__ bf16x8 frag_cols_d(const bf16 *base, int ld, int m0,
     return r;
 }
 
+// LDS transpose read of 16-bit elements (gfx950 ds_read_b64_tr_b16).  Within
+// each group of 16 lanes, lane 4j + q passes the address of 4 consecutive
+// elements (8 bytes); lane i of the group gets, as its element j, element i % 4
+// of the 8 bytes addressed by lane 4j + i / 4.  So if lane 4j + q points at
+// row r_j, columns c0 + 4q .. c0 + 4q + 3 of a row-major matrix, lane i gets
+// column c0 + i of rows r_0..r_3: a column gather in one instruction.
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16 *p) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(
+        bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p));
+}
+
 }  // namespace gdn
