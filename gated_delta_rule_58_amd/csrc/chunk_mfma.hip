@@ -348,44 +348,55 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     *reinterpret_cast<bf16x4 *>(dv + 4 * ((2 * p) ^ f)) = bf16x4{pv[i][0], pv[i][1], pv[i][2], pv[i][3]};
                     *reinterpret_cast<bf16x4 *>(dv + 4 * ((2 * p + 1) ^ f)) = bf16x4{pv[i][4], pv[i][5], pv[i][6], pv[i][7]};
                 }
-                if (pw == 0) {
-                    // Diagonal blocks of T = (I + A)^{-1} in fp32, one wave: lane
-                    // (block lg, column lm) solves its column by forward
-                    // substitution in 4-row sub-blocks; the block's columns of A
-                    // are contiguous in sAd.
-                    const f32x4 *Ad = reinterpret_cast<const f32x4 *>(sAd + lg * BLK);
-                    float x[16];
+                {
+                    // Diagonal block b = pw of T = (I + A)^{-1} in fp32.  Lane
+                    // (column cl, row group g) holds rows 4g..4g+3 of column cl;
+                    // blocked forward substitution over the four row groups, with
+                    // each solved group broadcast within its lane quad by DPP.
+                    // The block's columns of A are contiguous in sAd.
+                    const int b = pw, cl = lane >> 2, g = lane & 3;
+                    const float *Ad = sAd + b * BLK;
+                    f32x4 x;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) x[r] = (r == lm) ? 1.f : 0.f;
+                    for (int rr = 0; rr < 4; ++rr) x[rr] = (4 * g + rr == cl) ? 1.f : 0.f;
+                    // all loads first: acol[s][k][rr] = A[4 g + rr][4 s + k] of the block
+                    f32x4 acol[4][4];
 #pragma unroll
-                    for (int sb = 0; sb < 4; ++sb) {
-                        f32x4 col[4][4];   // columns 4 sb + c, rows in float4 groups
+                    for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
-                        for (int c = 0; c < 4; ++c)
-#pragma unroll
-                            for (int q4 = sb; q4 < 4; ++q4) col[c][q4] = Ad[(4 * sb + c) * 4 + q4];
-                        // solve the 4x4 diagonal sub-block
+                        for (int kk = 0; kk < 4; ++kk) acol[sb][kk] = ld4(Ad + (4 * sb + kk) * 16 + 4 * g);
+                    auto group = [&](auto sbc) {
+                        constexpr int sb = decltype(sbc)::value;
+                        const f32x4 *col = acol[sb];
+                        // rows of group sb: solve the 4x4 diagonal sub-block
+                        f32x4 t = x;
 #pragma unroll
                         for (int c = 0; c < 3; ++c)
 #pragma unroll
-                            for (int rr = c + 1; rr < 4; ++rr)
-                                x[4 * sb + rr] -= col[c][sb][rr] * x[4 * sb + c];
-                        // update the rows below with the four new unknowns
+                            for (int rr = c + 1; rr < 4; ++rr) t[rr] -= col[c][rr] * t[c];
+                        if (g == sb) x = t;
+                        if constexpr (sb < 3) {
+                            f32x4 xb;   // the solved rows 4 sb..4 sb+3 of this column
 #pragma unroll
-                        for (int r = 4 * sb + 4; r < 16; ++r) {
-                            const float t0 = col[0][r >> 2][r & 3] * x[4 * sb] +
-                                             col[1][r >> 2][r & 3] * x[4 * sb + 1];
-                            const float t1 = col[2][r >> 2][r & 3] * x[4 * sb + 2] +
-                                             col[3][r >> 2][r & 3] * x[4 * sb + 3];
-                            x[r] -= t0 + t1;
+                            for (int kk = 0; kk < 4; ++kk)
+                                xb[kk] = __int_as_float(__builtin_amdgcn_mov_dpp(
+                                    __float_as_int(x[kk]), sb * 0x55, 0xf, 0xf, false));
+                            // later groups subtract their rows' share of it
+                            if (g > sb) {
+#pragma unroll
+                                for (int rr = 0; rr < 4; ++rr)
+                                    x[rr] -= (col[0][rr] * xb[0] + col[1][rr] * xb[1]) +
+                                             (col[2][rr] * xb[2] + col[3][rr] * xb[3]);
+                            }
                         }
-                    }
+                    };
+                    group(IntC<0>{});
+                    group(IntC<1>{});
+                    group(IntC<2>{});
+                    group(IntC<3>{});
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) sTd[lg * BLK + r * 16 + lm] = x[r];
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        *reinterpret_cast<f32x4 *>(sTdT + lg * BLK + lm * 16 + 4 * q4) =
-                            f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
+                    for (int rr = 0; rr < 4; ++rr) sTd[b * BLK + (4 * g + rr) * 16 + cl] = x[rr];
+                    *reinterpret_cast<f32x4 *>(sTdT + b * BLK + cl * 16 + 4 * g) = x;
                 }
                 if (m + 1 < N) prefetch_v(m + 1);
             }
