@@ -64,12 +64,20 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) { return to_bf16x4(x[0], x[
 
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
-// K, V and the transposed T factors sit in LDS unpadded with their 8-byte
+// Operand tiles in LDS ("D-order rows").  An MFMA operand fragment takes, per
+// lane group lg, the k values 4lg..4lg+3 and 16+4lg..16+4lg+3 of a 32-wide
+// k block (the order in which D-layout results feed the next product).  Row
+// tiles store each 32-column block with its 4-column chunks in the order
+// 0,4,1,5,2,6,3,7, so such a fragment is one 16-byte read, and rows are
+// padded to an odd multiple of 32 bytes, which keeps the 16-byte reads of 16
+// rows free of bank conflicts.
+__device__ __forceinline__ int dcol(int c) {   // stored position of column c
+    return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
+}
+// The V slice, read only as a column gather, sits unpadded with its 8-byte
 // chunks permuted within each row: chunk c of row r is stored at chunk
-// c ^ swz(r).  Both kinds of access then hit 16 distinct bank pairs per 16
-// lanes: 16 rows x one chunk (row fragments, D-layout stores) and 4
-// consecutive rows x 4 consecutive chunks (transpose reads, which start at a
-// multiple of 4 rows and 4 chunks).
+// c ^ swz(r), which keeps the transpose reads (4 consecutive rows x 4
+// consecutive chunks per 16 lanes) on distinct banks.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -99,29 +107,33 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     constexpr int C = kC;
     constexpr int NKS = DK / 32;        // 32-wide k-steps over d_k
     constexpr int NMT = DK / 16;        // 16-row tiles over d_k
-    // Padded row lengths (elements).  Operands are read 8 bytes per lane, 16
-    // lanes (16 rows) per LDS cycle: a row stride of 2 mod 4 dwords puts those
-    // 16 rows on 16 distinct bank pairs.  (K and V are swizzled instead.)
-    constexpr int LDK = DK + 4;
+    // Row lengths (elements) of the D-order row tiles (d_k wide and C wide),
+    // and of A, whose 16x16x16 operands are 8-byte reads of 16 rows (2 mod 4
+    // dwords puts those on distinct bank pairs).
+    constexpr int LDK = DK + 16;
+    constexpr int LDT = C + 16;
     constexpr int LDC = C + 4;
     constexpr int BLK = 260;            // stride of the 16x16 fp32 diagonal blocks (4 banks apart)
     constexpr int QK_PIECES = C * DK / 8;            // 16-byte pieces of a q or k chunk
     constexpr int QK_PER_THR = QK_PIECES / 256;
+    constexpr int QK_PPR = DK / 8;                   // 16-byte pieces per row
+    static_assert(QK_PER_THR * (64 / QK_PPR) == 16, "a producer wave owns 16 rows of q and k");
     constexpr int V_PER_THR = C * kDVT / 8 / 256;
     static_assert(QK_PIECES % 256 == 0 && V_PER_THR * 256 == C * kDVT / 8, "piece split");
 
-    __shared__ __attribute__((aligned(16))) bf16 sQ[C * LDK];
-    __shared__ __attribute__((aligned(16))) bf16 sK[2][C * DK];     // K of chunks m, m-1 (swizzled)
+    __shared__ __attribute__((aligned(16))) bf16 sQ[C * LDK];       // Q, D-order rows
+    __shared__ __attribute__((aligned(16))) bf16 sK[C * LDK];       // K, D-order rows
+    __shared__ __attribute__((aligned(16))) bf16 sKT[2][DK * LDT];  // K^T of chunks m and m-1
     __shared__ __attribute__((aligned(16))) bf16 sV[C * kDVT];      // V slice (swizzled)
     __shared__ __attribute__((aligned(16))) bf16 sA[C * LDC];       // A, off-diagonal blocks
     __shared__ __attribute__((aligned(16))) float sAd[4 * BLK];     // A diag blocks, [b][col][row]
     __shared__ __attribute__((aligned(16))) float sTd[4 * BLK];     // T diag blocks, [b][row][col]
     __shared__ __attribute__((aligned(16))) float sTdT[4 * BLK];    // T diag blocks, [b][col][row]
-    // transposed, swizzled: row c holds column c of the factor
-    __shared__ __attribute__((aligned(16))) bf16 sTUt[C * C];       // ((T - I) diag(beta))^T
-    __shared__ __attribute__((aligned(16))) bf16 sTWt[C * C];       // (T diag(beta e^g))^T
-    __shared__ __attribute__((aligned(16))) bf16 sPh[C * LDC];      // P = tril(QK^T) o decay, hi
-    __shared__ __attribute__((aligned(16))) bf16 sPl[C * LDC];      // P, lo
+    // the C x C factors, D-order rows
+    __shared__ __attribute__((aligned(16))) bf16 sTU[C * LDT];      // (T - I) diag(beta)
+    __shared__ __attribute__((aligned(16))) bf16 sTW[C * LDT];      // T diag(beta e^g)
+    __shared__ __attribute__((aligned(16))) bf16 sPh[C * LDT];      // P = tril(QK^T) o decay, hi
+    __shared__ __attribute__((aligned(16))) bf16 sPl[C * LDT];      // P, lo
     // gates of a chunk, double-buffered: g, e^g, beta, e^{g_C - g}
     __shared__ __attribute__((aligned(16))) float sG[2][4][C];
 
@@ -145,22 +157,23 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
     const int lm = lane & 15, lg = lane >> 4;
 
-    // Operand element (i, k) = X[32 ks + k][16 cb + i] of a swizzled row-major
-    // X with `ld` elements per row, k in D-order: a column gather by two
-    // transpose reads (K^T, V and the T factors from their transposes).
-    auto tr_frag = [&](const bf16 *x, int ld, int cb, int ks) {
+    // Operand fragment of a D-order row tile: rows row0..row0+15, k block ks.
+    auto frag = [&](const bf16 *x, int ld, int row0, int ks) {
+        return *reinterpret_cast<const bf16x8 *>(x + (row0 + lm) * ld + 32 * ks + 8 * lg);
+    };
+    // Operand element (i, k) = V[32 ks + k][16 cb + i] (k in D-order) of the
+    // swizzled V slice: a column gather by two transpose reads.
+    auto v_frag = [&](int cb, int ks) {
         const int j = lm >> 2, q4 = lm & 3;
-        const bf16 *p = x + (32 * ks + 4 * lg + j) * ld + 4 * ((4 * cb + q4) ^ ((j << 2) | lg));
-        return cat(lds_read_tr(p), lds_read_tr(p + 16 * ld));
+        const bf16 *p = sV + (32 * ks + 4 * lg + j) * kDVT + 4 * ((4 * cb + q4) ^ ((j << 2) | lg));
+        return cat(lds_read_tr(p), lds_read_tr(p + 16 * kDVT));
     };
-    // Row fragment of a swizzled K tile: rows row0..row0+15 (row0 a multiple
-    // of 16), k0..k0+31 in D-order.
-    auto k_rows = [&](const bf16 *kb, int row0, int k0) {
-        const bf16 *p = kb + (row0 + lm) * DK;
-        const int f = swz(lm), c = (k0 >> 2) + lg;
-        return cat(*reinterpret_cast<const bf16x4 *>(p + 4 * (c ^ f)),
-                   *reinterpret_cast<const bf16x4 *>(p + 4 * ((c + 4) ^ f)));
-    };
+    // 16x16x16 operand holding the identity: D = X I turns X (given as an A
+    // operand: lane (lm, lg) holds row lm, columns 4lg..4lg+3) into D layout
+    // (lane holds rows 4lg..4lg+3 of column lm), i.e. transposes lane data.
+    bf16x4 eye;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) eye[s] = (bf16)((4 * lg + s == lm) ? 1.f : 0.f);
 
     long row0, L;
     if (varlen) {
@@ -176,11 +189,9 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     auto cvalid = [&](int c) -> uint32_t { return (uint32_t)min((long)C, L - (long)c * C); };
 
     // Upper off-diagonal blocks of the LDS factors are never written: zero them once.
-    for (int e = tid; e < C * LDC / 2; e += 512) {
-        if (e < C * C / 2) {
-            reinterpret_cast<uint32_t *>(sTUt)[e] = 0u;
-            reinterpret_cast<uint32_t *>(sTWt)[e] = 0u;
-        }
+    for (int e = tid; e < C * LDT / 2; e += 512) {
+        reinterpret_cast<uint32_t *>(sTU)[e] = 0u;
+        reinterpret_cast<uint32_t *>(sTW)[e] = 0u;
         reinterpret_cast<uint32_t *>(sPh)[e] = 0u;
         reinterpret_cast<uint32_t *>(sPl)[e] = 0u;
     }
@@ -201,7 +212,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             const rsrc_t rk = make_rsrc(k + (t0 * H + h) * DK, nv * H * DK * 2);
 #pragma unroll
             for (int i = 0; i < QK_PER_THR; ++i) {
-                const int e = ptid + 256 * i, r = e / (DK / 8), p = e % (DK / 8);
+                const int r = 16 * pw + i * (64 / QK_PPR) + lane / QK_PPR, p = lane % QK_PPR;
                 const uint32_t off = (uint32_t)(r * H * DK + 8 * p) * 2;
                 pq[i] = buf_load16(rq, off);
                 pk[i] = buf_load16(rk, off);
@@ -251,16 +262,25 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             if (prep) {
 #pragma unroll
                 for (int i = 0; i < QK_PER_THR; ++i) {
-                    const int e = ptid + 256 * i, r = e / (DK / 8), p = e % (DK / 8);
-                    bf16 *dq = sQ + r * LDK + 8 * p;
-                    bf16 *dk = sK[m & 1] + r * DK;
-                    const int f = swz(r);
-                    reinterpret_cast<bf16x4 *>(dq)[0] = bf16x4{pq[i][0], pq[i][1], pq[i][2], pq[i][3]};
-                    reinterpret_cast<bf16x4 *>(dq)[1] = bf16x4{pq[i][4], pq[i][5], pq[i][6], pq[i][7]};
-                    *reinterpret_cast<bf16x4 *>(dk + 4 * ((2 * p) ^ f)) = bf16x4{pk[i][0], pk[i][1], pk[i][2], pk[i][3]};
-                    *reinterpret_cast<bf16x4 *>(dk + 4 * ((2 * p + 1) ^ f)) = bf16x4{pk[i][4], pk[i][5], pk[i][6], pk[i][7]};
+                    const int r = 16 * pw + i * (64 / QK_PPR) + lane / QK_PPR, p = lane % QK_PPR;
+                    const int c0 = r * LDK + dcol(8 * p), c1 = r * LDK + dcol(8 * p + 4);
+                    *reinterpret_cast<bf16x4 *>(sQ + c0) = bf16x4{pq[i][0], pq[i][1], pq[i][2], pq[i][3]};
+                    *reinterpret_cast<bf16x4 *>(sQ + c1) = bf16x4{pq[i][4], pq[i][5], pq[i][6], pq[i][7]};
+                    *reinterpret_cast<bf16x4 *>(sK + c0) = bf16x4{pk[i][0], pk[i][1], pk[i][2], pk[i][3]};
+                    *reinterpret_cast<bf16x4 *>(sK + c1) = bf16x4{pk[i][4], pk[i][5], pk[i][6], pk[i][7]};
                 }
                 if (m + 1 < N) prefetch_qk(m + 1);
+                // K^T of chunk m for its state update: this wave's 16 tokens,
+                // all of d_k, by identity products on 16x16 blocks (the wave
+                // reads back only rows it wrote itself).
+#pragma unroll
+                for (int cb = 0; cb < DK / 16; ++cb) {
+                    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(
+                        sK + (16 * pw + lm) * LDK + dcol(16 * cb + 4 * lg));
+                    const f32x4 kt = mfma16(a, eye, zero4());
+                    *reinterpret_cast<bf16x4 *>(sKT[m & 1] + (16 * cb + lm) * LDT + dcol(16 * pw + 4 * lg)) =
+                        to_bf16x4(kt);
+                }
             }
             __syncthreads();
             // ================================ phase 2
@@ -268,14 +288,13 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 // K K^T and Q K^T tiles (ti, tj), tj <= ti, 10 in all, 2-3 per wave;
                 // a wave loads each 16-row block of K or Q it needs once.
                 typedef bf16x8 Frag[NKS];
-                const bf16 *sKm = sK[m & 1];
                 auto load_q = [&](int blk, Frag &f) {
 #pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) f[ks] = frag_rows_d(sQ, LDK, 16 * blk, 32 * ks, lane);
+                    for (int ks = 0; ks < NKS; ++ks) f[ks] = frag(sQ, LDK, 16 * blk, ks);
                 };
                 auto load_k = [&](int blk, Frag &f) {
 #pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) f[ks] = k_rows(sKm, 16 * blk, 32 * ks);
+                    for (int ks = 0; ks < NKS; ++ks) f[ks] = frag(sK, LDK, 16 * blk, ks);
                 };
                 auto tile = [&](const int ti, const int tj, const Frag &fKj, const Frag &fKi,
                                 const Frag &fQi) {
@@ -294,8 +313,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     const f32x4 p4 = dec * PT;
                     bf16x8 ph, pl;
                     split_op(p4, p4, ph, pl);
-                    *reinterpret_cast<bf16x4 *>(sPh + r * LDC + i0) = bf16x4{ph[0], ph[1], ph[2], ph[3]};
-                    *reinterpret_cast<bf16x4 *>(sPl + r * LDC + i0) = bf16x4{pl[0], pl[1], pl[2], pl[3]};
+                    *reinterpret_cast<bf16x4 *>(sPh + r * LDT + dcol(i0)) = bf16x4{ph[0], ph[1], ph[2], ph[3]};
+                    *reinterpret_cast<bf16x4 *>(sPl + r * LDT + dcol(i0)) = bf16x4{pl[0], pl[1], pl[2], pl[3]};
                     if (ti > tj) {
                         *reinterpret_cast<bf16x4 *>(sA + r * LDC + i0) = to_bf16x4(br * dec * G);
                     } else {
@@ -424,16 +443,18 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     RT[i] = -mfma16(Trow, to_bf16x4(Yb), zero4());
                     Bop[i] = to_bf16x4(RT[i]);
                 }
-                // Scale column c = 16 j + lm by beta_c (and e^{g_c}) and round
-                // once to bf16; the lane's 4 rows are 4 consecutive entries of
-                // row c of the transposed factors.
+                // Scale column c = 16 j + lm by beta_c (and e^{g_c}), round once
+                // to bf16, and transpose with an identity product (exact) so that
+                // each lane writes 4 consecutive columns of one row.
                 const int c = 16 * j + lm;
                 const float bc = sG[gb][2][c], wc = bc * sG[gb][1][c];
 #pragma unroll
                 for (int i = j + 1; i < 4; ++i) {
-                    const int off = c * C + 4 * ((4 * i + lg) ^ swz(c));
-                    *reinterpret_cast<bf16x4 *>(sTUt + off) = to_bf16x4(RT[i] * bc);
-                    *reinterpret_cast<bf16x4 *>(sTWt + off) = to_bf16x4(RT[i] * wc);
+                    const f32x4 tu = mfma16(to_bf16x4(RT[i] * bc), eye, zero4());
+                    const f32x4 tw = mfma16(to_bf16x4(RT[i] * wc), eye, zero4());
+                    const int off = (16 * i + lm) * LDT + dcol(16 * j + 4 * lg);
+                    *reinterpret_cast<bf16x4 *>(sTU + off) = to_bf16x4(tu);
+                    *reinterpret_cast<bf16x4 *>(sTW + off) = to_bf16x4(tw);
                 }
             };
             if (prep) {
@@ -442,20 +463,21 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 else if (pw == 2) column(IntC<2>{});
             }
             // Diagonal block b of (T - I) diag(beta) and T diag(beta e^g), one
-            // (column, 4 rows) per lane.
+            // (row, 4 columns) per lane.
             auto diag_conv = [&](int b) {
-                const int cl = lane >> 2, r4 = 4 * (lane & 3), c = 16 * b + cl;
-                const f32x4 tv = ld4(sTdT + b * BLK + cl * 16 + r4);   // T[16 b + r4 + s][c]
-                const float bc = sG[gb][2][c], wc = bc * sG[gb][1][c];
+                const int r = lane >> 2, c4 = 4 * (lane & 3);
+                const f32x4 tv = ld4(sTd + b * BLK + r * 16 + c4);
+                const f32x4 bc = ld4(&sG[gb][2][16 * b + c4]);
+                const f32x4 ec = ld4(&sG[gb][1][16 * b + c4]);
                 bf16x4 tu, tw;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    tu[s] = (bf16)((r4 + s > cl) ? tv[s] * bc : 0.f);
-                    tw[s] = (bf16)((r4 + s >= cl) ? tv[s] * wc : 0.f);
+                    tu[s] = (bf16)((c4 + s < r) ? tv[s] * bc[s] : 0.f);
+                    tw[s] = (bf16)((c4 + s <= r) ? tv[s] * bc[s] * ec[s] : 0.f);
                 }
-                const int off = c * C + 4 * ((4 * b + (lane & 3)) ^ swz(c));
-                *reinterpret_cast<bf16x4 *>(sTUt + off) = tu;
-                *reinterpret_cast<bf16x4 *>(sTWt + off) = tw;
+                const int off = (16 * b + r) * LDT + dcol(16 * b + c4);
+                *reinterpret_cast<bf16x4 *>(sTU + off) = tu;
+                *reinterpret_cast<bf16x4 *>(sTW + off) = tw;
             };
             if (prep) {
                 diag_conv(pw);
@@ -493,15 +515,15 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             f32x4 bt[4];   // beta_r at rows 16 mr + 4 lg + j
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr) bt[mr] = ld4(&sG[cb][2][16 * mr + 4 * lg]);
-            const bf16x8 fV0 = tr_frag(sV, kDVT, cw / 16, 0);
-            const bf16x8 fV1 = tr_frag(sV, kDVT, cw / 16, 1);
+            const bf16x8 fV0 = v_frag(cw / 16, 0);
+            const bf16x8 fV1 = v_frag(cw / 16, 1);
             bf16x8 fTU[6], fTW[6];   // fragment (mr, ks), ks <= mr / 2, in that order
 #pragma unroll
             for (int mr = 0, f = 0; mr < 4; ++mr)
 #pragma unroll
                 for (int ks = 0; ks <= mr / 2; ++ks, ++f) {
-                    fTU[f] = tr_frag(sTUt, C, mr, ks);
-                    fTW[f] = tr_frag(sTWt, C, mr, ks);
+                    fTU[f] = frag(sTU, LDT, 16 * mr, ks);
+                    fTW[f] = frag(sTW, LDT, 16 * mr, ks);
                 }
             __builtin_amdgcn_sched_barrier(0);
             // U = diag(beta) V + (T - I) diag(beta) V; the D-order V operand
@@ -537,8 +559,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             for (int mr = 0, f = 0; mr < 4; ++mr)
 #pragma unroll
                 for (int ks = 0; ks <= mr / 2; ++ks, ++f) {
-                    fPh[f] = frag_rows_d(sPh, LDC, 16 * mr, 32 * ks, lane);
-                    fPl[f] = frag_rows_d(sPl, LDC, 16 * mr, 32 * ks, lane);
+                    fPh[f] = frag(sPh, LDT, 16 * mr, ks);
+                    fPl[f] = frag(sPl, LDT, 16 * mr, ks);
                 }
             __builtin_amdgcn_sched_barrier(0);
             bf16x8 dh[2], dl[2];
@@ -575,7 +597,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) fk[mt][ks] = tr_frag(sK[n & 1], DK, mt, ks);
+                for (int ks = 0; ks < 2; ++ks) fk[mt][ks] = frag(sKT[n & 1], LDT, 16 * mt, ks);
             __builtin_amdgcn_sched_barrier(0);
             const float egC = sG[cb][1][C - 1];
 #pragma unroll
@@ -600,7 +622,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr)
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) fq[mr][ks] = frag_rows_d(sQ, LDK, 16 * mr, 32 * ks, lane);
+                for (int ks = 0; ks < NKS; ++ks) fq[mr][ks] = frag(sQ, LDK, 16 * mr, ks);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) split_op(st[2 * ks], st[2 * ks + 1], sh[ks], sl[ks]);
@@ -624,7 +646,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr)
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) fk[mr][ks] = k_rows(sK[m & 1], 16 * mr, 32 * ks);
+                for (int ks = 0; ks < NKS; ++ks) fk[mr][ks] = frag(sK, LDK, 16 * mr, ks);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr) {
