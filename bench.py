@@ -118,8 +118,8 @@ def run_decode(args, torch, gi, gdn, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--cold-steps", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -21,18 +21,20 @@
 // read once and o is written once.  Waves 0-3 ("producers") prepare chunk
 // n+1 -- global prefetch, gate prefix, K K^T and Q K^T on MFMA, the 64x64
 // unit-lower inverse (four 16x16 diagonal blocks by blocked forward
-// substitution in fp32, then the off-diagonal blocks
-// T_ij = -T_ii sum_k A_ik T_kj on 16x16 MFMA), the bf16 factors
-// (T - I) diag(beta), T diag(beta e^g) and K^T -- while waves 4-7
-// ("consumers") run the state chain of chunk n.  Consumer c owns 16 columns
-// of the slice and keeps its S^T columns (d_k x 16, fp32) in MFMA
+// substitution in fp32, one per wave, then the off-diagonal blocks
+// T_ij = -T_ii sum_k A_ik T_kj on 16x16 MFMA, one block column per wave), the
+// bf16 factors (T - I) diag(beta), T diag(beta e^g) and K^T -- while waves
+// 4-7 ("consumers") run the state chain of chunk n.  Consumer c owns 16
+// columns of the slice and keeps its S^T columns (d_k x 16, fp32) in MFMA
 // accumulators; S^T, Y and Delta feed the next MFMA straight from registers
 // (layouts in gdn_common.h).  An iteration has four barrier-separated phases;
 // every LDS buffer is written by one phase and read in later ones before it
-// is overwritten, so apart from the gates nothing is double-buffered:
+// is overwritten (P and the gates are double-buffered, so P Delta can wait
+// for phase 2):
 //   phase  producers (chunk n+1)               consumers (chunk n)
-//   1      store q,k, prefetch chunk n+2       U, Delta, P Delta, write o
-//   2      K K^T, Q K^T -> A, P               S <- e^{g_C} S + K^T Delta~
+//   1      store q,k, prefetch chunk n+2       U, Delta, Delta~
+//   2      K K^T, Q K^T -> A, P               S <- e^{g_C} S + K^T Delta~,
+//                                              P Delta, write o
 //   3      diagonal inverses, store v, K^T     Q S^T for chunk n+1
 //   4      off-diagonal T, T diag(.),          Y = K S^T for chunk n+1
 //          gate prefix of chunk n+2
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 
     __shared__ __attribute__((aligned(16))) bf16 sQ[C * LDK];       // Q, D-order rows
     __shared__ __attribute__((aligned(16))) bf16 sK[C * LDK];       // K, D-order rows
-    __shared__ __attribute__((aligned(16))) bf16 sKT[2][DK * LDT];  // K^T of chunks m and m-1
+    __shared__ __attribute__((aligned(16))) bf16 sKT[DK * LDT];     // K^T
     __shared__ __attribute__((aligned(16))) bf16 sV[C * kDVT];      // V slice (swizzled)
     __shared__ __attribute__((aligned(16))) bf16 sA[C * LDC];       // A, off-diagonal blocks
     __shared__ __attribute__((aligned(16))) float sAd[4 * BLK];     // A diag blocks, [b][col][row]
@@ -132,8 +134,9 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     // the C x C factors, D-order rows
     __shared__ __attribute__((aligned(16))) bf16 sTU[C * LDT];      // (T - I) diag(beta)
     __shared__ __attribute__((aligned(16))) bf16 sTW[C * LDT];      // T diag(beta e^g)
-    __shared__ __attribute__((aligned(16))) bf16 sPh[C * LDT];      // P = tril(QK^T) o decay, hi
-    __shared__ __attribute__((aligned(16))) bf16 sPl[C * LDT];      // P, lo
+    // P = tril(QK^T) o decay as hi + lo, chunks m and m-1
+    __shared__ __attribute__((aligned(16))) bf16 sPh[2][C * LDT];
+    __shared__ __attribute__((aligned(16))) bf16 sPl[2][C * LDT];
     // gates of a chunk, double-buffered: g, e^g, beta, e^{g_C - g}
     __shared__ __attribute__((aligned(16))) float sG[2][4][C];
 
@@ -192,8 +195,11 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     for (int e = tid; e < C * LDT / 2; e += 512) {
         reinterpret_cast<uint32_t *>(sTU)[e] = 0u;
         reinterpret_cast<uint32_t *>(sTW)[e] = 0u;
-        reinterpret_cast<uint32_t *>(sPh)[e] = 0u;
-        reinterpret_cast<uint32_t *>(sPl)[e] = 0u;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            reinterpret_cast<uint32_t *>(sPh[b])[e] = 0u;
+            reinterpret_cast<uint32_t *>(sPl[b])[e] = 0u;
+        }
     }
     __syncthreads();
 
@@ -270,17 +276,6 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     *reinterpret_cast<bf16x4 *>(sK + c1) = bf16x4{pk[i][4], pk[i][5], pk[i][6], pk[i][7]};
                 }
                 if (m + 1 < N) prefetch_qk(m + 1);
-                // K^T of chunk m for its state update: this wave's 16 tokens,
-                // all of d_k, by identity products on 16x16 blocks (the wave
-                // reads back only rows it wrote itself).
-#pragma unroll
-                for (int cb = 0; cb < DK / 16; ++cb) {
-                    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(
-                        sK + (16 * pw + lm) * LDK + dcol(16 * cb + 4 * lg));
-                    const f32x4 kt = mfma16(a, eye, zero4());
-                    *reinterpret_cast<bf16x4 *>(sKT[m & 1] + (16 * cb + lm) * LDT + dcol(16 * pw + 4 * lg)) =
-                        to_bf16x4(kt);
-                }
             }
             __syncthreads();
             // ================================ phase 2
@@ -313,8 +308,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     const f32x4 p4 = dec * PT;
                     bf16x8 ph, pl;
                     split_op(p4, p4, ph, pl);
-                    *reinterpret_cast<bf16x4 *>(sPh + r * LDT + dcol(i0)) = bf16x4{ph[0], ph[1], ph[2], ph[3]};
-                    *reinterpret_cast<bf16x4 *>(sPl + r * LDT + dcol(i0)) = bf16x4{pl[0], pl[1], pl[2], pl[3]};
+                    *reinterpret_cast<bf16x4 *>(sPh[m & 1] + r * LDT + dcol(i0)) = bf16x4{ph[0], ph[1], ph[2], ph[3]};
+                    *reinterpret_cast<bf16x4 *>(sPl[m & 1] + r * LDT + dcol(i0)) = bf16x4{pl[0], pl[1], pl[2], pl[3]};
                     if (ti > tj) {
                         *reinterpret_cast<bf16x4 *>(sA + r * LDC + i0) = to_bf16x4(br * dec * G);
                     } else {
@@ -417,6 +412,20 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     for (int rr = 0; rr < 4; ++rr) sTd[b * BLK + (4 * g + rr) * 16 + cl] = x[rr];
                     *reinterpret_cast<f32x4 *>(sTdT + b * BLK + cl * 16 + 4 * g) = x;
                 }
+                // K^T of chunk m for its state update (the consumers finished
+                // with the previous one in phase 2): tokens 16 pw..16 pw+15, all
+                // of d_k, by identity products on 16x16 blocks.
+                bf16x4 kb[DK / 16];
+#pragma unroll
+                for (int cb = 0; cb < DK / 16; ++cb)
+                    kb[cb] = *reinterpret_cast<const bf16x4 *>(sK + (16 * pw + lm) * LDK + dcol(16 * cb + 4 * lg));
+                f32x4 kt[DK / 16];
+#pragma unroll
+                for (int cb = 0; cb < DK / 16; ++cb) kt[cb] = mfma16(kb[cb], eye, zero4());
+                bf16 *dkt = sKT + lm * LDT + dcol(16 * pw + 4 * lg);
+#pragma unroll
+                for (int cb = 0; cb < DK / 16; ++cb)
+                    *reinterpret_cast<bf16x4 *>(dkt + 16 * cb * LDT) = to_bf16x4(kt[cb]);
                 if (m + 1 < N) prefetch_v(m + 1);
             }
             __syncthreads();
@@ -497,7 +506,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     f32x4 st[NMT];      // st[mt][j] = S^T[16 mt + 4 lg + j][dvw]
     f32x4 QS[4];        // diag(e^g) Q S^T of the next chunk, rows 16 mr + 4 lg + j
     bf16x8 yh[2], yl[2];  // K S^T of the next chunk, hi + lo bf16 (D order)
-    bf16x8 th[2], tl[2];
+    bf16x8 th[2], tl[2];  // Delta~ = diag(e^{g_C - g}) Delta, hi + lo (D order)
+    bf16x8 dh[2], dl[2];  // Delta, hi + lo
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
         st[mt] = zero4();
@@ -549,23 +559,47 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 }
                 D[mr] = U[mr] - acc;
             }
-            // O = diag(e^g) Q S^T + P Delta, stored through a buffer resource
-            // covering the valid rows of this chunk (padded rows are dropped).
             f32x4 ed[4];   // e^{g_C - g_r} at rows 16 mr + 4 lg + j
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr) ed[mr] = ld4(&sG[cb][3][16 * mr + 4 * lg]);
-            bf16x8 fPh[6], fPl[6];
+            split_op(D[0], D[1], dh[0], dl[0]);
+            split_op(D[2], D[3], dh[1], dl[1]);
+            // Delta~ for the state update
+            split_op(D[0] * ed[0], D[1] * ed[1], th[0], tl[0]);
+            split_op(D[2] * ed[2], D[3] * ed[3], th[1], tl[1]);
+        }
+        __syncthreads();
+        // ================================ phase 2
+        if (chain) {
+            // S^T <- e^{g_C} S^T + K^T Delta~
+            bf16x8 fk[NMT][2];
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) fk[mt][ks] = frag(sKT, LDT, 16 * mt, ks);
+            __builtin_amdgcn_sched_barrier(0);
+            const float egC = sG[cb][1][C - 1];
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) {
+                st[mt] = st[mt] * egC;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    st[mt] = mfma32(fk[mt][ks], th[ks], st[mt]);
+                    st[mt] = mfma32(fk[mt][ks], tl[ks], st[mt]);
+                }
+            }
+            // O = diag(e^g) Q S^T + P Delta (P of chunk n stays in its buffer
+            // until phase 2 of the next iteration), stored through a buffer
+            // resource covering the valid rows of this chunk (padded rows are
+            // dropped).
+            bf16x8 fPh[6], fPl[6];   // fragment (mr, ks), ks <= mr / 2, in that order
 #pragma unroll
             for (int mr = 0, f = 0; mr < 4; ++mr)
 #pragma unroll
                 for (int ks = 0; ks <= mr / 2; ++ks, ++f) {
-                    fPh[f] = frag(sPh, LDT, 16 * mr, ks);
-                    fPl[f] = frag(sPl, LDT, 16 * mr, ks);
+                    fPh[f] = frag(sPh[n & 1], LDT, 16 * mr, ks);
+                    fPl[f] = frag(sPl[n & 1], LDT, 16 * mr, ks);
                 }
-            __builtin_amdgcn_sched_barrier(0);
-            bf16x8 dh[2], dl[2];
-            split_op(D[0], D[1], dh[0], dl[0]);
-            split_op(D[2], D[3], dh[1], dl[1]);
             const size_t t0 = crow(n);
             const rsrc_t ro = make_rsrc(o + (t0 * H + h) * DV + dv0 + cw,
                                         cvalid(n) * H * DV * (uint32_t)sizeof(TO));
@@ -583,30 +617,6 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 for (int j = 0; j < 4; ++j) {
                     const int r = 16 * mr + 4 * lg + j;
                     buf_store(from_f32<TO>(O[j]), ro, (uint32_t)(r * H * DV + lm) * (uint32_t)sizeof(TO));
-                }
-            }
-            // Delta~ = diag(e^{g_C - g}) Delta for the state update
-            split_op(D[0] * ed[0], D[1] * ed[1], th[0], tl[0]);
-            split_op(D[2] * ed[2], D[3] * ed[3], th[1], tl[1]);
-        }
-        __syncthreads();
-        // ================================ phase 2
-        if (chain) {
-            // S^T <- e^{g_C} S^T + K^T Delta~
-            bf16x8 fk[NMT][2];
-#pragma unroll
-            for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) fk[mt][ks] = frag(sKT[n & 1], LDT, 16 * mt, ks);
-            __builtin_amdgcn_sched_barrier(0);
-            const float egC = sG[cb][1][C - 1];
-#pragma unroll
-            for (int mt = 0; mt < NMT; ++mt) {
-                st[mt] = st[mt] * egC;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    st[mt] = mfma32(fk[mt][ks], th[ks], st[mt]);
-                    st[mt] = mfma32(fk[mt][ks], tl[ks], st[mt]);
                 }
             }
         }
