@@ -123,8 +123,10 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--cold-steps", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2,
+    ap.add_argument("--cpu-rows", type=int, default=8,
                     help="batch rows of the workload the CPU oracle runs")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the CPU oracle until it has run this long")
     ap.add_argument("--only", choices=["all", "chunk", "decode"], default="all",
                     help="run one part only (for profiling); the JSON line needs 'all'")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -206,18 +208,21 @@ def main():
         import oracle
         rows = max(1, min(args.cpu_rows, B))
         threads = min(16, os.cpu_count() or 1)
-        print(f"[bench] cpu baseline: oracle on {rows} batch row(s), {threads} threads",
-              file=sys.stderr, flush=True)
+        print(f"[bench] cpu baseline: oracle on {rows} batch row(s), {threads} threads, "
+              f"repeated for >= {args.cpu_seconds:g} s", file=sys.stderr, flush=True)
         sub = {k: (v[:rows] if v is not None else None) for k, v in host.items()
                if k != "cu_seqlens"}
-        c0 = time.perf_counter()
-        oracle.fwd(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["beta"], sub["S0"],
-                   threads=threads)
-        ct = time.perf_counter() - c0
-        cpu = {"value": round(rows * T / ct, 1), "unit": "tokens/s", "cores": threads,
+        reps, ct = 0, 0.0
+        while ct < args.cpu_seconds and (reps == 0 or ct / reps * (reps + 1) <= 3 * args.cpu_seconds):
+            c0 = time.perf_counter()
+            oracle.fwd(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["beta"], sub["S0"],
+                       threads=threads)
+            ct += time.perf_counter() - c0
+            reps += 1
+        cpu = {"value": round(reps * rows * T / ct, 1), "unit": "tokens/s", "cores": threads,
                "kind": "oracle",
                "sample": f"{rows} of {B} batch rows (all {H} heads x {T} tokens), fp64 "
-                         f"token recurrence, {ct:.2f} s wall"}
+                         f"token recurrence, run {reps} times, {ct:.2f} s wall"}
 
     line = {
         "metric": METRIC,
