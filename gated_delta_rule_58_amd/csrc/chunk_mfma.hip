@@ -70,11 +70,29 @@ __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<
 // lane group lg, the k values 4lg..4lg+3 and 16+4lg..16+4lg+3 of a 32-wide
 // k block (the order in which D-layout results feed the next product).  Row
 // tiles store each 32-column block with its 4-column chunks in the order
-// 0,4,1,5,2,6,3,7, so such a fragment is one 16-byte read, and rows are
-// padded to an odd multiple of 32 bytes, which keeps the 16-byte reads of 16
-// rows free of bank conflicts.
-__device__ __forceinline__ int dcol(int c) {   // stored position of column c
+// 0,4,1,5,2,6,3,7, so such a fragment is one 16-byte read.
+__device__ __forceinline__ int dcol(int c) {   // D-order position of column c
     return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
+}
+// Rows are unpadded, W elements long, with their 16-byte chunks XOR-permuted
+// by row: 16 consecutive rows then put a 16-byte chunk (fragment reads) or
+// an 8-byte piece (stores of D-layout results, 16 rows x 8 bytes) on
+// distinct banks.  (Padded rows measured 1.2-1.3x slower for the reads and
+// about 2x slower for the 8-byte stores.)
+template <int W> __device__ __forceinline__ int tswz(int r) {
+    return W == 64 ? ((r >> 1) & 7) : (r & 15);
+}
+template <int W> __device__ __forceinline__ int tposd(int r, int d) {   // D-order position d
+    return r * W + 8 * ((d >> 3) ^ tswz<W>(r)) + (d & 7);
+}
+template <int W> __device__ __forceinline__ int tpos(int r, int c) {    // natural column c
+    return tposd<W>(r, dcol(c));
+}
+// Operand fragment of a D-order row tile of width W: rows row0..row0+15
+// (row0 a multiple of 16), k block ks.
+template <int W>
+__device__ __forceinline__ bf16x8 tfrag(const bf16 *x, int row0, int ks, int lane) {
+    return *reinterpret_cast<const bf16x8 *>(x + tposd<W>(row0 + (lane & 15), 32 * ks + 8 * (lane >> 4)));
 }
 // The V slice, read only as a column gather, sits unpadded with its 8-byte
 // chunks permuted within each row: chunk c of row r is stored at chunk
@@ -109,11 +127,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     constexpr int C = kC;
     constexpr int NKS = DK / 32;        // 32-wide k-steps over d_k
     constexpr int NMT = DK / 16;        // 16-row tiles over d_k
-    // Row lengths (elements) of the D-order row tiles (d_k wide and C wide),
-    // and of A, whose 16x16x16 operands are 8-byte reads of 16 rows (2 mod 4
-    // dwords puts those on distinct bank pairs).
-    constexpr int LDK = DK + 16;
-    constexpr int LDT = C + 16;
+    // Row length (elements) of A, whose 16x16x16 operands are 8-byte reads of
+    // 16 rows (2 mod 4 dwords puts those on distinct bank pairs).
     constexpr int LDC = C + 4;
     constexpr int BLK = 260;            // stride of the 16x16 fp32 diagonal blocks (4 banks apart)
     constexpr int QK_PIECES = C * DK / 8;            // 16-byte pieces of a q or k chunk
@@ -123,20 +138,20 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     constexpr int V_PER_THR = C * kDVT / 8 / 256;
     static_assert(QK_PIECES % 256 == 0 && V_PER_THR * 256 == C * kDVT / 8, "piece split");
 
-    __shared__ __attribute__((aligned(16))) bf16 sQ[C * LDK];       // Q, D-order rows
-    __shared__ __attribute__((aligned(16))) bf16 sK[C * LDK];       // K, D-order rows
-    __shared__ __attribute__((aligned(16))) bf16 sKT[DK * LDT];     // K^T
+    __shared__ __attribute__((aligned(16))) bf16 sQ[C * DK];        // Q, D-order rows
+    __shared__ __attribute__((aligned(16))) bf16 sK[C * DK];        // K, D-order rows
+    __shared__ __attribute__((aligned(16))) bf16 sKT[DK * C];       // K^T
     __shared__ __attribute__((aligned(16))) bf16 sV[C * kDVT];      // V slice (swizzled)
     __shared__ __attribute__((aligned(16))) bf16 sA[C * LDC];       // A, off-diagonal blocks
     __shared__ __attribute__((aligned(16))) float sAd[4 * BLK];     // A diag blocks, [b][col][row]
     __shared__ __attribute__((aligned(16))) float sTd[4 * BLK];     // T diag blocks, [b][row][col]
     __shared__ __attribute__((aligned(16))) float sTdT[4 * BLK];    // T diag blocks, [b][col][row]
     // the C x C factors, D-order rows
-    __shared__ __attribute__((aligned(16))) bf16 sTU[C * LDT];      // (T - I) diag(beta)
-    __shared__ __attribute__((aligned(16))) bf16 sTW[C * LDT];      // T diag(beta e^g)
+    __shared__ __attribute__((aligned(16))) bf16 sTU[C * C];        // (T - I) diag(beta)
+    __shared__ __attribute__((aligned(16))) bf16 sTW[C * C];        // T diag(beta e^g)
     // P = tril(QK^T) o decay as hi + lo, chunks m and m-1
-    __shared__ __attribute__((aligned(16))) bf16 sPh[2][C * LDT];
-    __shared__ __attribute__((aligned(16))) bf16 sPl[2][C * LDT];
+    __shared__ __attribute__((aligned(16))) bf16 sPh[2][C * C];
+    __shared__ __attribute__((aligned(16))) bf16 sPl[2][C * C];
     // gates of a chunk, double-buffered: g, e^g, beta, e^{g_C - g}
     __shared__ __attribute__((aligned(16))) float sG[2][4][C];
 
@@ -160,10 +175,6 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
     const int lm = lane & 15, lg = lane >> 4;
 
-    // Operand fragment of a D-order row tile: rows row0..row0+15, k block ks.
-    auto frag = [&](const bf16 *x, int ld, int row0, int ks) {
-        return *reinterpret_cast<const bf16x8 *>(x + (row0 + lm) * ld + 32 * ks + 8 * lg);
-    };
     // Operand element (i, k) = V[32 ks + k][16 cb + i] (k in D-order) of the
     // swizzled V slice: a column gather by two transpose reads.
     auto v_frag = [&](int cb, int ks) {
@@ -192,7 +203,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     auto cvalid = [&](int c) -> uint32_t { return (uint32_t)min((long)C, L - (long)c * C); };
 
     // Upper off-diagonal blocks of the LDS factors are never written: zero them once.
-    for (int e = tid; e < C * LDT / 2; e += 512) {
+    for (int e = tid; e < C * C / 2; e += 512) {
         reinterpret_cast<uint32_t *>(sTU)[e] = 0u;
         reinterpret_cast<uint32_t *>(sTW)[e] = 0u;
 #pragma unroll
@@ -269,7 +280,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 #pragma unroll
                 for (int i = 0; i < QK_PER_THR; ++i) {
                     const int r = 16 * pw + i * (64 / QK_PPR) + lane / QK_PPR, p = lane % QK_PPR;
-                    const int c0 = r * LDK + dcol(8 * p), c1 = r * LDK + dcol(8 * p + 4);
+                    const int c0 = tpos<DK>(r, 8 * p), c1 = tpos<DK>(r, 8 * p + 4);
                     *reinterpret_cast<bf16x4 *>(sQ + c0) = bf16x4{pq[i][0], pq[i][1], pq[i][2], pq[i][3]};
                     *reinterpret_cast<bf16x4 *>(sQ + c1) = bf16x4{pq[i][4], pq[i][5], pq[i][6], pq[i][7]};
                     *reinterpret_cast<bf16x4 *>(sK + c0) = bf16x4{pk[i][0], pk[i][1], pk[i][2], pk[i][3]};
@@ -285,11 +296,11 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 typedef bf16x8 Frag[NKS];
                 auto load_q = [&](int blk, Frag &f) {
 #pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) f[ks] = frag(sQ, LDK, 16 * blk, ks);
+                    for (int ks = 0; ks < NKS; ++ks) f[ks] = tfrag<DK>(sQ, 16 * blk, ks, lane);
                 };
                 auto load_k = [&](int blk, Frag &f) {
 #pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) f[ks] = frag(sK, LDK, 16 * blk, ks);
+                    for (int ks = 0; ks < NKS; ++ks) f[ks] = tfrag<DK>(sK, 16 * blk, ks, lane);
                 };
                 auto tile = [&](const int ti, const int tj, const Frag &fKj, const Frag &fKi,
                                 const Frag &fQi) {
@@ -308,8 +319,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     const f32x4 p4 = dec * PT;
                     bf16x8 ph, pl;
                     split_op(p4, p4, ph, pl);
-                    *reinterpret_cast<bf16x4 *>(sPh[m & 1] + r * LDT + dcol(i0)) = bf16x4{ph[0], ph[1], ph[2], ph[3]};
-                    *reinterpret_cast<bf16x4 *>(sPl[m & 1] + r * LDT + dcol(i0)) = bf16x4{pl[0], pl[1], pl[2], pl[3]};
+                    *reinterpret_cast<bf16x4 *>(sPh[m & 1] + tpos<C>(r, i0)) = bf16x4{ph[0], ph[1], ph[2], ph[3]};
+                    *reinterpret_cast<bf16x4 *>(sPl[m & 1] + tpos<C>(r, i0)) = bf16x4{pl[0], pl[1], pl[2], pl[3]};
                     if (ti > tj) {
                         *reinterpret_cast<bf16x4 *>(sA + r * LDC + i0) = to_bf16x4(br * dec * G);
                     } else {
@@ -418,14 +429,13 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 bf16x4 kb[DK / 16];
 #pragma unroll
                 for (int cb = 0; cb < DK / 16; ++cb)
-                    kb[cb] = *reinterpret_cast<const bf16x4 *>(sK + (16 * pw + lm) * LDK + dcol(16 * cb + 4 * lg));
+                    kb[cb] = *reinterpret_cast<const bf16x4 *>(sK + tpos<DK>(16 * pw + lm, 16 * cb + 4 * lg));
                 f32x4 kt[DK / 16];
 #pragma unroll
                 for (int cb = 0; cb < DK / 16; ++cb) kt[cb] = mfma16(kb[cb], eye, zero4());
-                bf16 *dkt = sKT + lm * LDT + dcol(16 * pw + 4 * lg);
 #pragma unroll
                 for (int cb = 0; cb < DK / 16; ++cb)
-                    *reinterpret_cast<bf16x4 *>(dkt + 16 * cb * LDT) = to_bf16x4(kt[cb]);
+                    *reinterpret_cast<bf16x4 *>(sKT + tpos<C>(16 * cb + lm, 16 * pw + 4 * lg)) = to_bf16x4(kt[cb]);
                 if (m + 1 < N) prefetch_v(m + 1);
             }
             __syncthreads();
@@ -461,7 +471,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 for (int i = j + 1; i < 4; ++i) {
                     const f32x4 tu = mfma16(to_bf16x4(RT[i] * bc), eye, zero4());
                     const f32x4 tw = mfma16(to_bf16x4(RT[i] * wc), eye, zero4());
-                    const int off = (16 * i + lm) * LDT + dcol(16 * j + 4 * lg);
+                    const int off = tpos<C>(16 * i + lm, 16 * j + 4 * lg);
                     *reinterpret_cast<bf16x4 *>(sTU + off) = to_bf16x4(tu);
                     *reinterpret_cast<bf16x4 *>(sTW + off) = to_bf16x4(tw);
                 }
@@ -484,7 +494,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     tu[s] = (bf16)((c4 + s < r) ? tv[s] * bc[s] : 0.f);
                     tw[s] = (bf16)((c4 + s <= r) ? tv[s] * bc[s] * ec[s] : 0.f);
                 }
-                const int off = (16 * b + r) * LDT + dcol(16 * b + c4);
+                const int off = tpos<C>(16 * b + r, 16 * b + c4);
                 *reinterpret_cast<bf16x4 *>(sTU + off) = tu;
                 *reinterpret_cast<bf16x4 *>(sTW + off) = tw;
             };
@@ -532,8 +542,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             for (int mr = 0, f = 0; mr < 4; ++mr)
 #pragma unroll
                 for (int ks = 0; ks <= mr / 2; ++ks, ++f) {
-                    fTU[f] = frag(sTU, LDT, 16 * mr, ks);
-                    fTW[f] = frag(sTW, LDT, 16 * mr, ks);
+                    fTU[f] = tfrag<C>(sTU, 16 * mr, ks, lane);
+                    fTW[f] = tfrag<C>(sTW, 16 * mr, ks, lane);
                 }
             __builtin_amdgcn_sched_barrier(0);
             // U = diag(beta) V + (T - I) diag(beta) V; the D-order V operand
@@ -576,7 +586,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) fk[mt][ks] = frag(sKT, LDT, 16 * mt, ks);
+                for (int ks = 0; ks < 2; ++ks) fk[mt][ks] = tfrag<C>(sKT, 16 * mt, ks, lane);
             __builtin_amdgcn_sched_barrier(0);
             const float egC = sG[cb][1][C - 1];
 #pragma unroll
@@ -597,8 +607,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             for (int mr = 0, f = 0; mr < 4; ++mr)
 #pragma unroll
                 for (int ks = 0; ks <= mr / 2; ++ks, ++f) {
-                    fPh[f] = frag(sPh[n & 1], LDT, 16 * mr, ks);
-                    fPl[f] = frag(sPl[n & 1], LDT, 16 * mr, ks);
+                    fPh[f] = tfrag<C>(sPh[n & 1], 16 * mr, ks, lane);
+                    fPl[f] = tfrag<C>(sPl[n & 1], 16 * mr, ks, lane);
                 }
             const size_t t0 = crow(n);
             const rsrc_t ro = make_rsrc(o + (t0 * H + h) * DV + dv0 + cw,
@@ -632,7 +642,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr)
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) fq[mr][ks] = frag(sQ, LDK, 16 * mr, ks);
+                for (int ks = 0; ks < NKS; ++ks) fq[mr][ks] = tfrag<DK>(sQ, 16 * mr, ks, lane);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) split_op(st[2 * ks], st[2 * ks + 1], sh[ks], sl[ks]);
@@ -656,7 +666,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr)
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) fk[mr][ks] = frag(sK, LDK, 16 * mr, ks);
+                for (int ks = 0; ks < NKS; ++ks) fk[mr][ks] = tfrag<DK>(sK, 16 * mr, ks, lane);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr) {
