@@ -27,17 +27,17 @@
 // 4-7 ("consumers") run the state chain of chunk n.  Consumer c owns 16
 // columns of the slice and keeps its S^T columns (d_k x 16, fp32) in MFMA
 // accumulators; S^T, Y and Delta feed the next MFMA straight from registers
-// (layouts in gdn_common.h).  An iteration has four barrier-separated phases;
-// every LDS buffer is written by one phase and read in later ones before it
-// is overwritten (P and the gates are double-buffered, so P Delta can wait
-// for phase 2):
+// (layouts in gdn_common.h).  An iteration has three barrier-separated
+// phases; every LDS buffer is written by one phase and read in later ones
+// before it is overwritten (P and the gates are double-buffered):
 //   phase  producers (chunk n+1)               consumers (chunk n)
 //   1      store q,k, prefetch chunk n+2       U, Delta, Delta~
-//   2      K K^T, Q K^T -> A, P               S <- e^{g_C} S + K^T Delta~,
-//                                              P Delta, write o
-//   3      diagonal inverses, store v, K^T     Q S^T for chunk n+1
-//   4      off-diagonal T, T diag(.),          Y = K S^T for chunk n+1
-//          gate prefix of chunk n+2
+//   2      K K^T, Q K^T -> A, P; each wave     S <- e^{g_C} S + K^T Delta~,
+//          inverts and converts the diagonal   P Delta, write o
+//          block of A it computed
+//   3      store v, K^T, off-diagonal T and    Q S^T, Y = K S^T for chunk n+1
+//          its conversions, gate prefix of
+//          chunk n+2
 // Global loads and stores go through buffer resources sized to the valid
 // rows of the chunk: rows past a ragged end read as zero and their stores
 // are dropped by the hardware range check, so no lane branches on bounds.
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
         if (N > 0) {
             prefetch_qk(0);
             prefetch_v(0);
-            if (pw == 3) scan_gates(0);   // later chunks are scanned a phase-4 ahead
+            if (pw == 3) scan_gates(0);   // later chunks are scanned a phase ahead
         }
         for (int n = -1; n < N; ++n) {
             const int m = n + 1;           // chunk being prepared
@@ -289,6 +289,23 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 if (m + 1 < N) prefetch_qk(m + 1);
             }
             __syncthreads();
+            // Diagonal block b of (T - I) diag(beta) and T diag(beta e^g), one
+            // (row, 4 columns) per lane.
+            auto diag_conv = [&](int b) {
+                const int r = lane >> 2, c4 = 4 * (lane & 3);
+                const f32x4 tv = ld4(sTd + b * BLK + r * 16 + c4);
+                const f32x4 bc = ld4(&sG[gb][2][16 * b + c4]);
+                const f32x4 ec = ld4(&sG[gb][1][16 * b + c4]);
+                bf16x4 tu, tw;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    tu[s] = (bf16)((c4 + s < r) ? tv[s] * bc[s] : 0.f);
+                    tw[s] = (bf16)((c4 + s <= r) ? tv[s] * bc[s] * ec[s] : 0.f);
+                }
+                const int off = tpos<C>(16 * b + r, 16 * b + c4);
+                *reinterpret_cast<bf16x4 *>(sTU + off) = tu;
+                *reinterpret_cast<bf16x4 *>(sTW + off) = tw;
+            };
             // ================================ phase 2
             if (prep) {
                 // K K^T and Q K^T tiles (ti, tj), tj <= ti, 10 in all, 2-3 per wave;
@@ -361,18 +378,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     tile(3, 2, k2, k3, q3);
                     tile(3, 3, k3, k3, q3);
                 }
-            }
-            __syncthreads();
-            // ================================ phase 3
-            if (prep) {
-#pragma unroll
-                for (int i = 0; i < V_PER_THR; ++i) {
-                    const int e = ptid + 256 * i, r = e / (kDVT / 8), p = e % (kDVT / 8);
-                    bf16 *dv = sV + r * kDVT;
-                    const int f = swz(r);
-                    *reinterpret_cast<bf16x4 *>(dv + 4 * ((2 * p) ^ f)) = bf16x4{pv[i][0], pv[i][1], pv[i][2], pv[i][3]};
-                    *reinterpret_cast<bf16x4 *>(dv + 4 * ((2 * p + 1) ^ f)) = bf16x4{pv[i][4], pv[i][5], pv[i][6], pv[i][7]};
-                }
+                // Diagonal blocks: this wave computed tile (pw, pw) of A above and
+                // inverts and converts that block itself (no barrier needed).
                 {
                     // Diagonal block b = pw of T = (I + A)^{-1} in fp32.  Lane
                     // (column cl, row group g) holds rows 4g..4g+3 of column cl;
@@ -423,23 +430,10 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     for (int rr = 0; rr < 4; ++rr) sTd[b * BLK + (4 * g + rr) * 16 + cl] = x[rr];
                     *reinterpret_cast<f32x4 *>(sTdT + b * BLK + cl * 16 + 4 * g) = x;
                 }
-                // K^T of chunk m for its state update (the consumers finished
-                // with the previous one in phase 2): tokens 16 pw..16 pw+15, all
-                // of d_k, by identity products on 16x16 blocks.
-                bf16x4 kb[DK / 16];
-#pragma unroll
-                for (int cb = 0; cb < DK / 16; ++cb)
-                    kb[cb] = *reinterpret_cast<const bf16x4 *>(sK + tpos<DK>(16 * pw + lm, 16 * cb + 4 * lg));
-                f32x4 kt[DK / 16];
-#pragma unroll
-                for (int cb = 0; cb < DK / 16; ++cb) kt[cb] = mfma16(kb[cb], eye, zero4());
-#pragma unroll
-                for (int cb = 0; cb < DK / 16; ++cb)
-                    *reinterpret_cast<bf16x4 *>(sKT + tpos<C>(16 * cb + lm, 16 * pw + 4 * lg)) = to_bf16x4(kt[cb]);
-                if (m + 1 < N) prefetch_v(m + 1);
+                diag_conv(pw);
             }
             __syncthreads();
-            // ================================ phase 4
+            // ================================ phase 3
             // Off-diagonal blocks of block column j, top to bottom:
             // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj (16x16x16 MFMA).  Column j
             // only needs its own blocks and the diagonal ones, so producer wave
@@ -477,32 +471,34 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 }
             };
             if (prep) {
+#pragma unroll
+                for (int i = 0; i < V_PER_THR; ++i) {
+                    const int e = ptid + 256 * i, r = e / (kDVT / 8), p = e % (kDVT / 8);
+                    bf16 *dv = sV + r * kDVT;
+                    const int f = swz(r);
+                    *reinterpret_cast<bf16x4 *>(dv + 4 * ((2 * p) ^ f)) = bf16x4{pv[i][0], pv[i][1], pv[i][2], pv[i][3]};
+                    *reinterpret_cast<bf16x4 *>(dv + 4 * ((2 * p + 1) ^ f)) = bf16x4{pv[i][4], pv[i][5], pv[i][6], pv[i][7]};
+                }
+                // K^T of chunk m for its state update (the consumers finished
+                // with the previous one in phase 2): tokens 16 pw..16 pw+15, all
+                // of d_k, by identity products on 16x16 blocks.
+                bf16x4 kb[DK / 16];
+#pragma unroll
+                for (int cb = 0; cb < DK / 16; ++cb)
+                    kb[cb] = *reinterpret_cast<const bf16x4 *>(sK + tpos<DK>(16 * pw + lm, 16 * cb + 4 * lg));
+                f32x4 kt[DK / 16];
+#pragma unroll
+                for (int cb = 0; cb < DK / 16; ++cb) kt[cb] = mfma16(kb[cb], eye, zero4());
+#pragma unroll
+                for (int cb = 0; cb < DK / 16; ++cb)
+                    *reinterpret_cast<bf16x4 *>(sKT + tpos<C>(16 * cb + lm, 16 * pw + 4 * lg)) = to_bf16x4(kt[cb]);
                 if (pw == 0) column(IntC<0>{});
                 else if (pw == 1) column(IntC<1>{});
                 else if (pw == 2) column(IntC<2>{});
-            }
-            // Diagonal block b of (T - I) diag(beta) and T diag(beta e^g), one
-            // (row, 4 columns) per lane.
-            auto diag_conv = [&](int b) {
-                const int r = lane >> 2, c4 = 4 * (lane & 3);
-                const f32x4 tv = ld4(sTd + b * BLK + r * 16 + c4);
-                const f32x4 bc = ld4(&sG[gb][2][16 * b + c4]);
-                const f32x4 ec = ld4(&sG[gb][1][16 * b + c4]);
-                bf16x4 tu, tw;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    tu[s] = (bf16)((c4 + s < r) ? tv[s] * bc[s] : 0.f);
-                    tw[s] = (bf16)((c4 + s <= r) ? tv[s] * bc[s] * ec[s] : 0.f);
-                }
-                const int off = tpos<C>(16 * b + r, 16 * b + c4);
-                *reinterpret_cast<bf16x4 *>(sTU + off) = tu;
-                *reinterpret_cast<bf16x4 *>(sTW + off) = tw;
-            };
-            if (prep) {
-                diag_conv(pw);
                 // chunk m+1's gates go to the buffer chunk n used (the consumers
                 // are done with it)
-                if (pw == 3 && m + 1 < N) scan_gates(gb ^ 1);
+                else if (m + 1 < N) scan_gates(gb ^ 1);
+                if (m + 1 < N) prefetch_v(m + 1);
             }
             __syncthreads();
         }
@@ -530,8 +526,6 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
         const int cb = (m & 1) ^ 1;     // gate buffer of chunk n
         // ================================ phase 1
         if (chain) {
-            // Issue every LDS read of the phase first; the VALU work below
-            // overlaps their latency.
             f32x4 bt[4];   // beta_r at rows 16 mr + 4 lg + j
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr) bt[mr] = ld4(&sG[cb][2][16 * mr + 4 * lg]);
@@ -545,7 +539,6 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     fTU[f] = tfrag<C>(sTU, 16 * mr, ks, lane);
                     fTW[f] = tfrag<C>(sTW, 16 * mr, ks, lane);
                 }
-            __builtin_amdgcn_sched_barrier(0);
             // U = diag(beta) V + (T - I) diag(beta) V; the D-order V operand
             // holds exactly this lane's rows, which gives the diagonal term.
             f32x4 U[4];
@@ -587,7 +580,6 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) fk[mt][ks] = tfrag<C>(sKT, 16 * mt, ks, lane);
-            __builtin_amdgcn_sched_barrier(0);
             const float egC = sG[cb][1][C - 1];
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt) {
@@ -643,7 +635,6 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             for (int mr = 0; mr < 4; ++mr)
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) fq[mr][ks] = tfrag<DK>(sQ, 16 * mr, ks, lane);
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) split_op(st[2 * ks], st[2 * ks + 1], sh[ks], sl[ks]);
 #pragma unroll
@@ -657,8 +648,6 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 QS[mr] = acc * eg[mr];
             }
         }
-        __syncthreads();
-        // ================================ phase 4
         if (prep) {
             // Y = K S^T for chunk m, kept as a hi + lo pair
             f32x4 Y[4];
@@ -667,7 +656,6 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             for (int mr = 0; mr < 4; ++mr)
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) fk[mr][ks] = tfrag<DK>(sK, 16 * mr, ks, lane);
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr) {
                 f32x4 acc = zero4();
