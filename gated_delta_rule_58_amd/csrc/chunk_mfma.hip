@@ -514,6 +514,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     bf16x8 yh[2], yl[2];  // K S^T of the next chunk, hi + lo bf16 (D order)
     bf16x8 th[2], tl[2];  // Delta~ = diag(e^{g_C - g}) Delta, hi + lo (D order)
     bf16x8 dh[2], dl[2];  // Delta, hi + lo
+    bf16x8 sh[NKS], sl[NKS];  // S^T, hi + lo
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
         st[mt] = zero4();
@@ -622,9 +623,14 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 }
             }
         }
+        if (prep) {
+            // hi + lo split of the updated state for the next phase's products
+            // (here it overlaps the output products of this phase)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) split_op(st[2 * ks], st[2 * ks + 1], sh[ks], sl[ks]);
+        }
         __syncthreads();
         // ================================ phase 3
-        bf16x8 sh[NKS], sl[NKS];
         if (prep) {
             // diag(e^g) Q S^T for chunk m (state now S_m)
             f32x4 eg[4];   // e^{g_r} of chunk m at rows 16 mr + 4 lg + j
@@ -635,8 +641,6 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             for (int mr = 0; mr < 4; ++mr)
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) fq[mr][ks] = tfrag<DK>(sQ, 16 * mr, ks, lane);
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) split_op(st[2 * ks], st[2 * ks + 1], sh[ks], sl[ks]);
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr) {
                 f32x4 acc = zero4();
