@@ -511,7 +511,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     const size_t sbase = ((size_t)unit * H + h) * DV * DK;
     f32x4 st[NMT];      // st[mt][j] = S^T[16 mt + 4 lg + j][dvw]
     f32x4 QS[4];        // diag(e^g) Q S^T of the next chunk, rows 16 mr + 4 lg + j
-    bf16x8 yh[2], yl[2];  // K S^T of the next chunk, hi + lo bf16 (D order)
+    bf16x8 yb[2];         // K S^T of the next chunk, bf16 (D order)
     bf16x8 th[2], tl[2];  // Delta~ = diag(e^{g_C - g}) Delta, hi + lo (D order)
     bf16x8 dh[2], dl[2];  // Delta, hi + lo
     bf16x8 sh[NKS], sl[NKS];  // S^T, hi + lo
@@ -558,8 +558,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 #pragma unroll
                 for (int ks = 0; ks <= mr / 2; ++ks, ++f) {
                     U[mr] = mfma32(fTU[f], ks == 0 ? fV0 : fV1, U[mr]);
-                    acc = mfma32(fTW[f], yh[ks], acc);
-                    acc = mfma32(fTW[f], yl[ks], acc);
+                    acc = mfma32(fTW[f], yb[ks], acc);
                 }
                 D[mr] = U[mr] - acc;
             }
@@ -653,7 +652,9 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             }
         }
         if (prep) {
-            // Y = K S^T for chunk m, kept as a hi + lo pair
+            // Y = K S^T for chunk m from the hi part of S^T, rounded once to
+            // bf16: it only meets T diag(beta e^g), itself bf16, so extra bits
+            // of Y do not reach o or the state (same errors in emulation).
             f32x4 Y[4];
             bf16x8 fk[4][NKS];
 #pragma unroll
@@ -664,14 +665,11 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             for (int mr = 0; mr < 4; ++mr) {
                 f32x4 acc = zero4();
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    acc = mfma32(fk[mr][ks], sh[ks], acc);
-                    acc = mfma32(fk[mr][ks], sl[ks], acc);
-                }
+                for (int ks = 0; ks < NKS; ++ks) acc = mfma32(fk[mr][ks], sh[ks], acc);
                 Y[mr] = acc;
             }
-            split_op(Y[0], Y[1], yh[0], yl[0]);
-            split_op(Y[2], Y[3], yh[1], yl[1]);
+            yb[0] = d_to_op(Y[0], Y[1]);
+            yb[1] = d_to_op(Y[2], Y[3]);
         }
         __syncthreads();
     }

@@ -58,26 +58,26 @@ __device__ __forceinline__ bf16x8 d_to_op(f32x4 d0, f32x4 d1) {
                   (bf16)d1[0], (bf16)d1[1], (bf16)d1[2], (bf16)d1[3]};
 }
 
-// Split x into hi + lo, both bf16, with x - (hi + lo) below 2^-16 |x|: hi is
-// x truncated to its upper 16 bits (exact as a float), lo = bf16(x - hi).
-// Products hi*y + lo*y then keep about 16 mantissa bits of x.  Truncating
-// (instead of rounding) hi lets one byte permute pack two hi halves.
-__device__ __forceinline__ uint32_t hi_pair(float a, float b) {
-    // upper halves of a (low result half) and b (high result half)
-    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a),
-                                 0x07060302u);
-}
-__device__ __forceinline__ float lo_part(float x) {
-    return x - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) & 0xffff0000u);
+// Split x into hi + lo, both bf16: hi = bf16(x) (round to nearest even),
+// lo = bf16(x - hi).  x - (hi + lo) is below 2^-16 |x|, so products
+// hi*y + lo*y keep about 16 mantissa bits of x, and hi alone is x rounded
+// to bf16.
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t &hi, uint32_t &lo) {
+    typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    hi = __builtin_bit_cast(uint32_t, bf16x2{(bf16)a, (bf16)b});
+    const float ha = __builtin_bit_cast(float, hi << 16);
+    const float hb = __builtin_bit_cast(float, hi & 0xffff0000u);
+    lo = __builtin_bit_cast(uint32_t, bf16x2{(bf16)(a - ha), (bf16)(b - hb)});
 }
 __device__ __forceinline__ void split_op(f32x4 d0, f32x4 d1, bf16x8 &hi, bf16x8 &lo) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 h = {hi_pair(d0[0], d0[1]), hi_pair(d0[2], d0[3]), hi_pair(d1[0], d1[1]),
-                     hi_pair(d1[2], d1[3])};
-    hi = __builtin_bit_cast(bf16x8, h);
-    lo = bf16x8{(bf16)lo_part(d0[0]), (bf16)lo_part(d0[1]), (bf16)lo_part(d0[2]),
-                (bf16)lo_part(d0[3]), (bf16)lo_part(d1[0]), (bf16)lo_part(d1[1]),
-                (bf16)lo_part(d1[2]), (bf16)lo_part(d1[3])};
+    uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+    split_pair(d0[0], d0[1], h0, l0);
+    split_pair(d0[2], d0[3], h1, l1);
+    split_pair(d1[0], d1[1], h2, l2);
+    split_pair(d1[2], d1[3], h3, l3);
+    hi = __builtin_bit_cast(bf16x8, u32x4{h0, h1, h2, h3});
+    lo = __builtin_bit_cast(bf16x8, u32x4{l0, l1, l2, l3});
 }
 
 // --- LDS fragment loaders (row-major bf16 arrays with `ld` elements/row) ---

@@ -9,7 +9,11 @@ statistic max|x - oracle| / RMS(oracle) for o and for the final state on the
 "split" keeps it as a hi + lo pair of bfloat16 (about 16 mantissa bits),
 "fp32" rounds to float, "diag" keeps the diagonal of the beta-scaled T in
 full precision (the kernel forms beta V exactly and only the strictly lower
-part of T diag(beta) goes through bf16).
+part of T diag(beta) goes through bf16).  The last variant is the kernel's
+scheme: the state is split only where it multiplies Q; K S^T uses the hi
+part alone and is rounded once to bf16 before T diag(beta e^g) multiplies
+it (that product's left factor is bf16 anyway, so the extra bits do not
+show in o or the state).
 """
 from __future__ import annotations
 
@@ -59,7 +63,7 @@ def emulate_unit(Q, K, V, la, be, S0, cfg, C=64):
         TU = _r(cfg["TU"], T * b[None, :], cfg["TU_diag"])
         TW = _bf(T * (b * np.exp(g))[None, :])
         ST = _r(cfg["S"], S.T)
-        Y = k @ ST
+        Y = k @ _r(cfg.get("SY", cfg["S"]), S.T)
         D = TU @ v - TW @ _r(cfg["Y"], Y)
         P = _r(cfg["P"], (q @ k.T) * np.exp(np.where(lower, diff, -np.inf)))
         O[s:e] = _r(cfg["O"], np.exp(g)[:, None] * (q @ ST) + P @ _r(cfg["D"], D))
@@ -74,7 +78,8 @@ VARIANTS = {
     "+ beta diagonal exact": dict(TU="bf16", TU_diag=True, S="bf16", Y="bf16", P="bf16", D="bf16", O="fp32"),
     "+ Delta split": dict(TU="bf16", TU_diag=True, S="bf16", Y="bf16", P="bf16", D="split", O="fp32"),
     "+ P split": dict(TU="bf16", TU_diag=True, S="bf16", Y="bf16", P="split", D="split", O="fp32"),
-    "+ S^T, Y split (kernel)": dict(TU="bf16", TU_diag=True, S="split", Y="split", P="split", D="split", O="fp32"),
+    "+ S^T, Y split": dict(TU="bf16", TU_diag=True, S="split", Y="split", P="split", D="split", O="fp32"),
+    "S^T split for Q S^T only (kernel)": dict(TU="bf16", TU_diag=True, S="split", SY="bf16", Y="bf16", P="split", D="split", O="fp32"),
 }
 
 
