@@ -18,6 +18,12 @@ draw order: packed lengths (if any), q, k, v, beta logits, alpha logits, S0):
 * log alpha = -softplus(x), x ~ N(mu,1) (mu = 0 for the tiny and mid
   workloads, 1 for the 1.3B-shaped ones), fp32, so alpha is in (0,1);
 * S0 = 0, or ~ N(0, 0.1^2) in fp32 where the workload starts from a state.
+
+The ``raw_*`` generators draw the same numbers in the same order but stop
+before the normalisation and the gate activations, for the path's fused
+input prologue: q, k ~ N(0,1) cast to the I/O dtype as they are, and the
+gate pre-activations b ~ N(0,1) (for beta) and a ~ N(mu,1) (for alpha) in
+fp32, returned under the names ``beta`` and ``log_alpha``.
 """
 from __future__ import annotations
 
@@ -93,6 +99,41 @@ def chunk_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16",
         cu = torch.tensor(list(cu_seqlens), dtype=torch.int32)
     return dict(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, S0=S0,
                 cu_seqlens=cu)
+
+
+def raw_chunk_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16",
+                     alpha_mu: float = 1.0, s0_std: float = 0.0, seed: int = 0,
+                     cu_seqlens=None, rng: np.random.Generator | None = None):
+    """Like chunk_inputs, but q, k unnormalised and the gates as
+    pre-activations (a under "log_alpha", b under "beta")."""
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    q = _cast(rng.standard_normal((B, T, H, dk)), dtype)
+    k = _cast(rng.standard_normal((B, T, H, dk)), dtype)
+    v = _cast(rng.standard_normal((B, T, H, dv)), dtype)
+    b = torch.from_numpy(rng.standard_normal((B, T, H))).float()
+    a = torch.from_numpy(rng.normal(alpha_mu, 1.0, (B, T, H))).float()
+    units = B if cu_seqlens is None else len(cu_seqlens) - 1
+    S0 = None
+    if s0_std > 0:
+        S0 = torch.from_numpy(rng.normal(0.0, s0_std, (units, H, dv, dk))).float()
+    cu = None
+    if cu_seqlens is not None:
+        cu = torch.tensor(list(cu_seqlens), dtype=torch.int32)
+    return dict(q=q, k=k, v=v, log_alpha=a, beta=b, S0=S0, cu_seqlens=cu)
+
+
+def raw_decode_inputs(B: int, H: int, dk: int, dv: int, steps: int,
+                      dtype: str = "bf16", alpha_mu: float = 1.0,
+                      s0_std: float = 0.1, seed: int = 0):
+    """Like decode_inputs, with unnormalised q, k and gate pre-activations."""
+    rng = np.random.default_rng(seed)
+    q = _cast(rng.standard_normal((steps, B, H, dk)), dtype)
+    k = _cast(rng.standard_normal((steps, B, H, dk)), dtype)
+    v = _cast(rng.standard_normal((steps, B, H, dv)), dtype)
+    b = torch.from_numpy(rng.standard_normal((steps, B, H))).float()
+    a = torch.from_numpy(rng.normal(alpha_mu, 1.0, (steps, B, H))).float()
+    S0 = torch.from_numpy(rng.normal(0.0, s0_std, (B, H, dv, dk))).float()
+    return dict(q=q, k=k, v=v, log_alpha=a, beta=b, S0=S0)
 
 
 def decode_inputs(B: int, H: int, dk: int, dv: int, steps: int,
