@@ -16,6 +16,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 
 GDN_F32, GDN_BF16 = 0, 1
+PROLOGUE_NORM_QK, PROLOGUE_GATES = 1, 2
 _DTYPE = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
 
 # symbol -> (restype, argtypes); this is the whole exported surface of gdn.h
@@ -25,7 +26,7 @@ _c_int, _vp, _sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
 class GdnShape(ctypes.Structure):
     _fields_ = [("B", _c_int), ("T", _c_int), ("H", _c_int), ("d_k", _c_int),
                 ("d_v", _c_int), ("chunk", _c_int), ("n_seqs", _c_int),
-                ("io_dtype", _c_int), ("o_dtype", _c_int)]
+                ("io_dtype", _c_int), ("o_dtype", _c_int), ("prologue", _c_int)]
 
 
 SYMBOLS = {
@@ -33,8 +34,8 @@ SYMBOLS = {
                                               ctypes.POINTER(_sz)]),
     "gdn_chunk_fwd": (_c_int, [ctypes.POINTER(GdnShape), _vp, _vp, _vp, _vp, _vp,
                                _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "gdn_step": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp,
-                          _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "gdn_step": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "gdn_last_error": (ctypes.c_char_p, []),
     "gdn_version": (ctypes.c_char_p, []),
 }
@@ -90,19 +91,29 @@ def _need_cuda(name, t, dtype=None):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _prologue(norm_qk: bool, gates: bool) -> int:
+    return (PROLOGUE_NORM_QK if norm_qk else 0) | (PROLOGUE_GATES if gates else 0)
+
+
 def chunk_fwd_workspace_size(B, T, H, d_k, d_v, chunk=64, n_seqs=0,
-                             io_dtype=torch.bfloat16, o_dtype=torch.float32) -> int:
-    shape = GdnShape(B, T, H, d_k, d_v, chunk, n_seqs, _DTYPE[io_dtype], _DTYPE[o_dtype])
+                             io_dtype=torch.bfloat16, o_dtype=torch.float32,
+                             prologue=0) -> int:
+    shape = GdnShape(B, T, H, d_k, d_v, chunk, n_seqs, _DTYPE[io_dtype], _DTYPE[o_dtype],
+                     prologue)
     out = ctypes.c_size_t(0)
     _check(lib().gdn_chunk_fwd_workspace_size(ctypes.byref(shape), ctypes.byref(out)))
     return out.value
 
 
 def chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, chunk=64,
-              o_dtype=torch.float32, o=None, S_T=None, want_state=True):
+              o_dtype=torch.float32, o=None, S_T=None, want_state=True,
+              norm_qk=False, gates=False):
     """Chunkwise forward.  q,k [B,T,H,dk]; v [B,T,H,dv]; log_alpha, beta
     [B,T,H] fp32; S0 [U,H,dv,dk] fp32 or None; cu_seqlens int32 [N+1] (device)
-    or None.  Returns (o, S_T) (S_T is None when want_state is False)."""
+    or None.  norm_qk / gates turn on the fused input prologue (q, k
+    L2-normalised in the kernel; log_alpha, beta passed as pre-activations a,
+    b with log alpha = -softplus(a), beta = sigmoid(b)).  Returns (o, S_T)
+    (S_T is None when want_state is False)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     io = q.dtype
@@ -127,7 +138,8 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, chunk=64,
         o = torch.empty((B, T, H, dv), device=q.device, dtype=o_dtype)
     if S_T is None and want_state:
         S_T = torch.empty((units, H, dv, dk), device=q.device, dtype=torch.float32)
-    shape = GdnShape(B, T, H, dk, dv, chunk, n_seqs, _DTYPE[io], _DTYPE[o.dtype])
+    shape = GdnShape(B, T, H, dk, dv, chunk, n_seqs, _DTYPE[io], _DTYPE[o.dtype],
+                     _prologue(norm_qk, gates))
     ws_bytes = ctypes.c_size_t(0)
     _check(lib().gdn_chunk_fwd_workspace_size(ctypes.byref(shape), ctypes.byref(ws_bytes)))
     ws = None
@@ -140,9 +152,11 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, chunk=64,
     return o, S_T
 
 
-def step(q, k, v, log_alpha, beta, S, o_dtype=torch.float32, o=None):
+def step(q, k, v, log_alpha, beta, S, o_dtype=torch.float32, o=None, norm_qk=False,
+         gates=False):
     """One decode step.  q,k [B,H,dk]; v [B,H,dv]; gates [B,H] fp32; S
-    [B,H,dv,dk] fp32, updated in place.  Returns o [B,H,dv]."""
+    [B,H,dv,dk] fp32, updated in place; norm_qk / gates as in chunk_fwd.
+    Returns o [B,H,dv]."""
     B, H, dk = q.shape
     dv = v.shape[-1]
     io = q.dtype
@@ -154,7 +168,8 @@ def step(q, k, v, log_alpha, beta, S, o_dtype=torch.float32, o=None):
         raise ValueError("S must be [B,H,dv,dk]")
     if o is None:
         o = torch.empty((B, H, dv), device=q.device, dtype=o_dtype)
-    _check(lib().gdn_step(B, H, dk, dv, _DTYPE[io], _DTYPE[o.dtype], _ptr(q), _ptr(k),
+    _check(lib().gdn_step(B, H, dk, dv, _DTYPE[io], _DTYPE[o.dtype],
+                          _prologue(norm_qk, gates), _ptr(q), _ptr(k),
                           _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(o),
                           _stream(q.device)))
     return o

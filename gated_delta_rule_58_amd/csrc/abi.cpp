@@ -11,18 +11,19 @@
 
 namespace gdn {
 hipError_t launch_step(int B, int H, int DK, int DV, bool io_bf16, bool o_bf16,
-                       const void *q, const void *k, const void *v, const float *la,
-                       const float *beta, float *S, void *o, hipStream_t st);
+                       bool norm_qk, bool gates, const void *q, const void *k, const void *v,
+                       const float *la, const float *beta, float *S, void *o, hipStream_t st);
 bool chunk_f32_supported(int dk, int dv, int chunk);
 hipError_t launch_chunk_f32(int units, int T, int H, int dk, int chunk, bool o_bf16,
+                            bool norm_qk, bool gates,
                             const int32_t *cu, const void *q, const void *k, const void *v,
                             const float *la, const float *beta, const float *S0, void *o,
                             float *S_T, hipStream_t st);
 bool chunk_mfma_supported(int dk, int dv, int chunk);
-hipError_t launch_chunk_mfma(int units, int T, int H, int dk, bool o_bf16, const int32_t *cu,
-                             const void *q, const void *k, const void *v, const float *la,
-                             const float *beta, const float *S0, void *o, float *S_T,
-                             hipStream_t st);
+hipError_t launch_chunk_mfma(int units, int T, int H, int dk, bool o_bf16, bool norm_qk,
+                             bool gates, const int32_t *cu, const void *q, const void *k,
+                             const void *v, const float *la, const float *beta,
+                             const float *S0, void *o, float *S_T, hipStream_t st);
 }  // namespace gdn
 
 namespace {
@@ -50,6 +51,8 @@ bool misaligned(const void *p) {
 
 bool valid_dtype(int d) { return d == GDN_F32 || d == GDN_BF16; }
 
+bool valid_prologue(int p) { return (p & ~(GDN_PROLOGUE_NORM_QK | GDN_PROLOGUE_GATES)) == 0; }
+
 // Shape checks shared by the workspace query and the forward call.
 int check_shape(const gdn_shape *s) {
     if (!s) return fail(GDN_ERR_INVALID_ARG, "shape is NULL");
@@ -64,6 +67,9 @@ int check_shape(const gdn_shape *s) {
     if (!valid_dtype(s->io_dtype) || !valid_dtype(s->o_dtype))
         return fail(GDN_ERR_INVALID_ARG, "io_dtype=%d / o_dtype=%d is not a gdn_dtype",
                     s->io_dtype, s->o_dtype);
+    if (!valid_prologue(s->prologue))
+        return fail(GDN_ERR_INVALID_ARG, "prologue=%d has bits outside gdn_prologue",
+                    s->prologue);
     const long units = s->n_seqs > 0 ? s->n_seqs : s->B;
     if ((long)units * s->H > (1L << 28))
         return fail(GDN_ERR_INVALID_ARG, "units x heads = %ld is too large", units * (long)s->H);
@@ -125,25 +131,29 @@ int gdn_chunk_fwd(const gdn_shape *s, const void *q, const void *k, const void *
     const int units = s->n_seqs > 0 ? s->n_seqs : s->B;
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const bool o_bf16 = s->o_dtype == GDN_BF16;
+    const bool norm_qk = (s->prologue & GDN_PROLOGUE_NORM_QK) != 0;
+    const bool gates = (s->prologue & GDN_PROLOGUE_GATES) != 0;
     hipError_t e;
     if (s->io_dtype == GDN_BF16)
-        e = gdn::launch_chunk_mfma(units, s->T, s->H, s->d_k, o_bf16, cu_seqlens, q, k, v,
-                                   log_alpha, beta, S0, o, S_T, st);
+        e = gdn::launch_chunk_mfma(units, s->T, s->H, s->d_k, o_bf16, norm_qk, gates, cu_seqlens,
+                                   q, k, v, log_alpha, beta, S0, o, S_T, st);
     else
-        e = gdn::launch_chunk_f32(units, s->T, s->H, s->d_k, s->chunk, o_bf16, cu_seqlens, q, k,
-                                  v, log_alpha, beta, S0, o, S_T, st);
+        e = gdn::launch_chunk_f32(units, s->T, s->H, s->d_k, s->chunk, o_bf16, norm_qk, gates,
+                                  cu_seqlens, q, k, v, log_alpha, beta, S0, o, S_T, st);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 
-int gdn_step(int B, int H, int d_k, int d_v, int io_dtype, int o_dtype, const void *q,
-             const void *k, const void *v, const float *log_alpha, const float *beta, float *S,
-             void *o, void *stream) {
+int gdn_step(int B, int H, int d_k, int d_v, int io_dtype, int o_dtype, int prologue,
+             const void *q, const void *k, const void *v, const float *log_alpha,
+             const float *beta, float *S, void *o, void *stream) {
     if (B <= 0 || H <= 0 || d_k <= 0 || d_v <= 0)
         return fail(GDN_ERR_INVALID_ARG, "bad dimensions B=%d H=%d d_k=%d d_v=%d", B, H, d_k, d_v);
     if (!valid_dtype(io_dtype) || !valid_dtype(o_dtype))
         return fail(GDN_ERR_INVALID_ARG, "io_dtype=%d / o_dtype=%d is not a gdn_dtype", io_dtype,
                     o_dtype);
+    if (!valid_prologue(prologue))
+        return fail(GDN_ERR_INVALID_ARG, "prologue=%d has bits outside gdn_prologue", prologue);
     if ((long)B * H > (1L << 30))
         return fail(GDN_ERR_INVALID_ARG, "B x H = %ld is too large", (long)B * H);
     if (d_k != 64 && d_k != 128)
@@ -157,8 +167,10 @@ int gdn_step(int B, int H, int d_k, int d_v, int io_dtype, int o_dtype, const vo
             return fail(GDN_ERR_ALIGNMENT, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
     if (o == (void *)S) return fail(GDN_ERR_INVALID_ARG, "o must not alias S");
     const hipError_t e =
-        gdn::launch_step(B, H, d_k, d_v, io_dtype == GDN_BF16, o_dtype == GDN_BF16, q, k, v,
-                         log_alpha, beta, S, o, reinterpret_cast<hipStream_t>(stream));
+        gdn::launch_step(B, H, d_k, d_v, io_dtype == GDN_BF16, o_dtype == GDN_BF16,
+                         (prologue & GDN_PROLOGUE_NORM_QK) != 0,
+                         (prologue & GDN_PROLOGUE_GATES) != 0, q, k, v, log_alpha, beta, S, o,
+                         reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }

@@ -15,14 +15,17 @@
 // Only exponentials of non-positive arguments are formed.
 //
 // One 256-thread workgroup per (sequence, head) walks its chunks in order;
-// every intermediate lives in LDS.
+// every intermediate lives in LDS.  With the input prologue, q and k rows are
+// L2-normalised in LDS after loading (norm clamped below at 1e-6) and the
+// gates arrive as pre-activations a, b: log alpha = -softplus(a),
+// beta = sigmoid(b).
 #include "gdn_common.h"
 
 namespace gdn {
 
 template <int DK, int DV, int C, typename TO>
 __global__ __launch_bounds__(256) void chunk_f32_kernel(
-    int T, int H, int varlen, const int32_t *__restrict__ cu_seqlens,
+    int T, int H, int varlen, int norm_qk, int gates, const int32_t *__restrict__ cu_seqlens,
     const float *__restrict__ q, const float *__restrict__ k,
     const float *__restrict__ v, const float *__restrict__ log_alpha,
     const float *__restrict__ beta, const float *__restrict__ S0,
@@ -63,10 +66,22 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
         }
         if (tid < n) {
             const size_t g = (size_t)(row0 + c0 + tid) * H + h;
-            sg[tid] = log_alpha[g];
-            sb[tid] = beta[g];
+            float a = log_alpha[g], b = beta[g];
+            if (gates) {
+                a = -(fmaxf(a, 0.f) + log1pf(expf(-fabsf(a))));
+                b = 1.f / (1.f + expf(-b));
+            }
+            sg[tid] = a;
+            sb[tid] = b;
         }
         __syncthreads();
+        if (norm_qk && tid < 2 * n) {   // one thread per q or k row
+            float *x = tid < n ? sQ[tid] : sK[tid - n];
+            float ss = 0.f;
+            for (int d = 0; d < DK; ++d) ss += x[d] * x[d];
+            const float inv = 1.f / sqrtf(fmaxf(ss, 1e-12f));
+            for (int d = 0; d < DK; ++d) x[d] *= inv;
+        }
         if (tid == 0)   // chunk-local prefix sum of log alpha
             for (int r = 1; r < n; ++r) sg[r] += sg[r - 1];
         __syncthreads();
@@ -153,12 +168,12 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
 }
 
 template <int DK, int C, typename TO>
-hipError_t launch_chunk_f32_t(int units, int T, int H, const int32_t *cu,
+hipError_t launch_chunk_f32_t(int units, int T, int H, int norm_qk, int gates, const int32_t *cu,
                               const void *q, const void *k, const void *v,
                               const float *la, const float *beta, const float *S0,
                               void *o, float *S_T, hipStream_t st) {
     hipLaunchKernelGGL((chunk_f32_kernel<DK, DK, C, TO>), dim3(units * H), dim3(256),
-                       0, st, T, H, cu != nullptr ? 1 : 0, cu, (const float *)q,
+                       0, st, T, H, cu != nullptr ? 1 : 0, norm_qk, gates, cu, (const float *)q,
                        (const float *)k, (const float *)v, la, beta, S0, (TO *)o, S_T);
     return hipGetLastError();
 }
@@ -170,15 +185,16 @@ bool chunk_f32_supported(int dk, int dv, int chunk) {
 }
 
 hipError_t launch_chunk_f32(int units, int T, int H, int dk, int chunk, bool o_bf16,
+                            bool norm_qk, bool gates,
                             const int32_t *cu, const void *q, const void *k,
                             const void *v, const float *la, const float *beta,
                             const float *S0, void *o, float *S_T, hipStream_t st) {
 #define GDN_F32_CASE(DKV, CV)                                                        \
     if (dk == DKV && chunk == CV)                                                    \
-        return o_bf16 ? launch_chunk_f32_t<DKV, CV, bf16>(units, T, H, cu, q, k, v,  \
-                                                          la, beta, S0, o, S_T, st)  \
-                      : launch_chunk_f32_t<DKV, CV, float>(units, T, H, cu, q, k, v, \
-                                                           la, beta, S0, o, S_T, st);
+        return o_bf16 ? launch_chunk_f32_t<DKV, CV, bf16>(units, T, H, norm_qk, gates, cu, \
+                                                          q, k, v, la, beta, S0, o, S_T, st) \
+                      : launch_chunk_f32_t<DKV, CV, float>(units, T, H, norm_qk, gates, cu, \
+                                                           q, k, v, la, beta, S0, o, S_T, st);
     GDN_F32_CASE(16, 16) GDN_F32_CASE(16, 32) GDN_F32_CASE(16, 64)
     GDN_F32_CASE(32, 16) GDN_F32_CASE(32, 32) GDN_F32_CASE(32, 64)
     GDN_F32_CASE(64, 16) GDN_F32_CASE(64, 32) GDN_F32_CASE(64, 64)

@@ -59,6 +59,22 @@ __device__ __forceinline__ float exp_neg(float x) {   // e^x for x <= 0
     return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 
+// Gate prologue on the hardware transcendentals (v_exp_f32, v_log_f32,
+// v_rcp_f32, each within a few ulp).  -softplus(a) = -(max(a, 0) + log1p(y))
+// with y = e^{-|a|} in (0, 1]; log1p(y) = ln(t) y / (t - 1) with t = 1 + y
+// undoes the rounding of t (and is y itself once t rounds to 1).
+__device__ __forceinline__ float neg_softplus_hw(float a) {
+    const float y = exp_neg(-fabsf(a));
+    const float t = 1.f + y;
+    const float l1p = t == 1.f ? y
+                               : __builtin_amdgcn_logf(t) * 0.6931471805599453f * y *
+                                     __builtin_amdgcn_rcpf(t - 1.f);
+    return -(fmaxf(a, 0.f) + l1p);
+}
+__device__ __forceinline__ float sigmoid_hw(float b) {   // 1 / (1 + e^{-b}); 0 as b -> -inf
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-b * 1.4426950408889634f));
+}
+
 __device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) {
     return bf16x4{(bf16)a, (bf16)b, (bf16)c, (bf16)d};
 }
@@ -118,13 +134,19 @@ __device__ __forceinline__ void buf_store(bf16 x, rsrc_t r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), r, off, 0, 0);
 }
 
-template <int DK, typename TO>
+// Input prologue, PRO bit 0 (NQK): q and k arrive unnormalised and the
+// kernel L2-normalises them per token; bit 1 (GATES): log_alpha and beta hold
+// the pre-activations a and b, and the kernel uses log alpha = -softplus(a),
+// beta = sigmoid(b).
+template <int DK, typename TO, int PRO>
 __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
-    int T, int H, int DV, int varlen, int xcd_map, const int32_t *__restrict__ cu_seqlens,
+    int T, int H, int DV, int varlen, int xcd_map,
+    const int32_t *__restrict__ cu_seqlens,
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
     const float *__restrict__ S0, TO *__restrict__ o, float *__restrict__ S_T) {
     constexpr int C = kC;
+    constexpr bool NQK = (PRO & 1) != 0, GATES = (PRO & 2) != 0;
     constexpr int NKS = DK / 32;        // 32-wide k-steps over d_k
     constexpr int NMT = DK / 16;        // 16-row tiles over d_k
     // Row length (elements) of A, whose 16x16x16 operands are 8-byte reads of
@@ -152,8 +174,9 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     // P = tril(QK^T) o decay as hi + lo, chunks m and m-1
     __shared__ __attribute__((aligned(16))) bf16 sPh[2][C * C];
     __shared__ __attribute__((aligned(16))) bf16 sPl[2][C * C];
-    // gates of a chunk, double-buffered: g, e^g, beta, e^{g_C - g}
-    __shared__ __attribute__((aligned(16))) float sG[2][4][C];
+    // per-token values of a chunk, double-buffered: g, e^g, beta,
+    // e^{g_C - g}, and (prologue) 1/|q|, 1/|k|
+    __shared__ __attribute__((aligned(16))) float sG[2][6][C];
 
     // Workgroup -> (unit, head, d_v slice).  With xcd_map the slices of one
     // (unit, head) land on the same XCD (workgroups are dealt to the 8 XCDs
@@ -222,6 +245,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
         const int ptid = tid;      // producer thread 0..255
         bf16x8 pq[QK_PER_THR], pk[QK_PER_THR], pv[V_PER_THR];
         float pla = 0.f, pbe = 0.f;
+        bool pvalid = false;   // this lane's token exists (gate pre-activations)
         auto prefetch_qk = [&](int c) {
             const size_t t0 = crow(c);
             const uint32_t nv = cvalid(c);
@@ -239,12 +263,17 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 const rsrc_t rb = make_rsrc(beta + t0 * H + h, nv * H * 4);
                 pla = buf_load4(ra, (uint32_t)(lane * H) * 4);
                 pbe = buf_load4(rb, (uint32_t)(lane * H) * 4);
+                pvalid = (uint32_t)lane < nv;
             }
         };
         // Gate prefix of the prefetched chunk into gate buffer `buf`, one token
         // per lane of wave 3 (padded tokens add 0).
         auto scan_gates = [&](int buf) {
-            float x = pla;
+            float x = pla, b = pbe;
+            if constexpr (GATES) {   // padded tokens keep log alpha = beta = 0
+                x = pvalid ? neg_softplus_hw(x) : 0.f;
+                b = pvalid ? sigmoid_hw(b) : 0.f;
+            }
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(x, off);
@@ -253,7 +282,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             const float gC = __shfl(x, 63);
             sG[buf][0][lane] = x;
             sG[buf][1][lane] = exp_neg(x);
-            sG[buf][2][lane] = pbe;
+            sG[buf][2][lane] = b;
             sG[buf][3][lane] = exp_neg(gC - x);
         };
         auto prefetch_v = [&](int c) {
@@ -287,6 +316,27 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     *reinterpret_cast<bf16x4 *>(sK + c1) = bf16x4{pk[i][4], pk[i][5], pk[i][6], pk[i][7]};
                 }
                 if (m + 1 < N) prefetch_qk(m + 1);
+                if constexpr (NQK) {
+                    // |q_r|^2 and |k_r|^2 of this wave's 16 rows: the diagonal of
+                    // Q_b Q_b^T and K_b K_b^T (one fragment serves as both
+                    // operands).  Row lm's entry sits in lane (lm, lm >> 2),
+                    // register lm & 3.
+                    f32x4 nq = zero4(), nk = zero4();
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        const bf16x8 fq = tfrag<DK>(sQ, 16 * pw, ks, lane);
+                        const bf16x8 fk = tfrag<DK>(sK, 16 * pw, ks, lane);
+                        nq = mfma32(fq, fq, nq);
+                        nk = mfma32(fk, fk, nk);
+                    }
+                    if ((lm >> 2) == lg) {
+                        const int j = lm & 3;
+                        const float sq = j == 0 ? nq[0] : j == 1 ? nq[1] : j == 2 ? nq[2] : nq[3];
+                        const float sk = j == 0 ? nk[0] : j == 1 ? nk[1] : j == 2 ? nk[2] : nk[3];
+                        sG[m & 1][4][16 * pw + lm] = __builtin_amdgcn_rsqf(fmaxf(sq, 1e-12f));
+                        sG[m & 1][5][16 * pw + lm] = __builtin_amdgcn_rsqf(fmaxf(sk, 1e-12f));
+                    }
+                }
             }
             __syncthreads();
             // Diagonal block b of (T - I) diag(beta) and T diag(beta e^g), one
@@ -295,7 +345,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 const int r = lane >> 2, c4 = 4 * (lane & 3);
                 const f32x4 tv = ld4(sTd + b * BLK + r * 16 + c4);
                 const f32x4 bc = ld4(&sG[gb][2][16 * b + c4]);
-                const f32x4 ec = ld4(&sG[gb][1][16 * b + c4]);
+                f32x4 ec = ld4(&sG[gb][1][16 * b + c4]);
+                if constexpr (NQK) ec = ec * ld4(&sG[gb][5][16 * b + c4]);
                 bf16x4 tu, tw;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
@@ -330,6 +381,11 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     const int r = 16 * ti + lm, i0 = 16 * tj + 4 * lg;
                     const float gr = sG[gb][0][r], br = sG[gb][2][r];
                     const f32x4 gi = ld4(&sG[gb][0][i0]);
+                    if constexpr (NQK) {   // normalised rows: scale the Gram entries
+                        const f32x4 iki = ld4(&sG[gb][5][i0]);
+                        G = G * (sG[gb][5][r] * iki);
+                        PT = PT * (sG[gb][4][r] * iki);
+                    }
                     f32x4 dec;   // e^{g_r - g_i} on and below the diagonal, else 0
 #pragma unroll
                     for (int j = 0; j < 4; ++j) dec[j] = (i0 + j <= r) ? exp_neg(gr - gi[j]) : 0.f;
@@ -460,7 +516,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 // to bf16, and transpose with an identity product (exact) so that
                 // each lane writes 4 consecutive columns of one row.
                 const int c = 16 * j + lm;
-                const float bc = sG[gb][2][c], wc = bc * sG[gb][1][c];
+                const float bc = sG[gb][2][c];
+                const float wc = bc * sG[gb][1][c] * (NQK ? sG[gb][5][c] : 1.f);
 #pragma unroll
                 for (int i = j + 1; i < 4; ++i) {
                     const f32x4 tu = mfma16(to_bf16x4(RT[i] * bc), eye, zero4());
@@ -564,7 +621,10 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             }
             f32x4 ed[4];   // e^{g_C - g_r} at rows 16 mr + 4 lg + j
 #pragma unroll
-            for (int mr = 0; mr < 4; ++mr) ed[mr] = ld4(&sG[cb][3][16 * mr + 4 * lg]);
+            for (int mr = 0; mr < 4; ++mr) {
+                ed[mr] = ld4(&sG[cb][3][16 * mr + 4 * lg]);
+                if constexpr (NQK) ed[mr] = ed[mr] * ld4(&sG[cb][5][16 * mr + 4 * lg]);
+            }
             split_op(D[0], D[1], dh[0], dl[0]);
             split_op(D[2], D[3], dh[1], dl[1]);
             // Delta~ for the state update
@@ -634,7 +694,10 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             // diag(e^g) Q S^T for chunk m (state now S_m)
             f32x4 eg[4];   // e^{g_r} of chunk m at rows 16 mr + 4 lg + j
 #pragma unroll
-            for (int mr = 0; mr < 4; ++mr) eg[mr] = ld4(&sG[m & 1][1][16 * mr + 4 * lg]);
+            for (int mr = 0; mr < 4; ++mr) {
+                eg[mr] = ld4(&sG[m & 1][1][16 * mr + 4 * lg]);
+                if constexpr (NQK) eg[mr] = eg[mr] * ld4(&sG[m & 1][4][16 * mr + 4 * lg]);
+            }
             bf16x8 fq[4][NKS];
 #pragma unroll
             for (int mr = 0; mr < 4; ++mr)
@@ -685,7 +748,7 @@ bool chunk_mfma_supported(int dk, int dv, int chunk) {
     return chunk == kC && dk == dv && (dk == 64 || dk == 128);
 }
 
-template <int DK, typename TO>
+template <int DK, typename TO, int PRO>
 hipError_t launch_chunk_mfma_t(int units, int T, int H, int DV, const int32_t *cu,
                                const void *q, const void *k, const void *v,
                                const float *la, const float *beta, const float *S0,
@@ -693,22 +756,33 @@ hipError_t launch_chunk_mfma_t(int units, int T, int H, int DV, const int32_t *c
     const int ndvt = DV / kDVT;
     const long nwg = (long)units * H * ndvt;
     const int xcd_map = ((long)units * H) % 8 == 0 ? 1 : 0;
-    hipLaunchKernelGGL((chunk_mfma_kernel<DK, TO>), dim3((unsigned)nwg), dim3(512), 0, st,
+    hipLaunchKernelGGL((chunk_mfma_kernel<DK, TO, PRO>), dim3((unsigned)nwg), dim3(512), 0, st,
                        T, H, DV, cu != nullptr ? 1 : 0, xcd_map, cu, (const bf16 *)q,
                        (const bf16 *)k, (const bf16 *)v, la, beta, S0, (TO *)o, S_T);
     return hipGetLastError();
 }
 
-hipError_t launch_chunk_mfma(int units, int T, int H, int dk, bool o_bf16, const int32_t *cu,
-                             const void *q, const void *k, const void *v, const float *la,
-                             const float *beta, const float *S0, void *o, float *S_T,
-                             hipStream_t st) {
-    if (dk == 128)
-        return o_bf16 ? launch_chunk_mfma_t<128, bf16>(units, T, H, dk, cu, q, k, v, la, beta, S0, o, S_T, st)
-                      : launch_chunk_mfma_t<128, float>(units, T, H, dk, cu, q, k, v, la, beta, S0, o, S_T, st);
-    if (dk == 64)
-        return o_bf16 ? launch_chunk_mfma_t<64, bf16>(units, T, H, dk, cu, q, k, v, la, beta, S0, o, S_T, st)
-                      : launch_chunk_mfma_t<64, float>(units, T, H, dk, cu, q, k, v, la, beta, S0, o, S_T, st);
+hipError_t launch_chunk_mfma(int units, int T, int H, int dk, bool o_bf16, bool norm_qk,
+                             bool gates, const int32_t *cu, const void *q, const void *k,
+                             const void *v, const float *la, const float *beta,
+                             const float *S0, void *o, float *S_T, hipStream_t st) {
+    const int pro = (norm_qk ? 1 : 0) | (gates ? 2 : 0);
+#define GDN_MFMA_CASE(DKV, TOV, PV)                                                          \
+    if (pro == PV)                                                                           \
+        return launch_chunk_mfma_t<DKV, TOV, PV>(units, T, H, dk, cu, q, k, v, la, beta, S0, o, \
+                                                 S_T, st)
+#define GDN_MFMA_TO(DKV, TOV) \
+    GDN_MFMA_CASE(DKV, TOV, 0); GDN_MFMA_CASE(DKV, TOV, 1); GDN_MFMA_CASE(DKV, TOV, 2); \
+    GDN_MFMA_CASE(DKV, TOV, 3)
+#define GDN_MFMA_DK(DKV)                                         \
+    if (dk == DKV) {                                             \
+        if (o_bf16) { GDN_MFMA_TO(DKV, bf16); } else { GDN_MFMA_TO(DKV, float); } \
+    }
+    GDN_MFMA_DK(128)
+    GDN_MFMA_DK(64)
+#undef GDN_MFMA_DK
+#undef GDN_MFMA_TO
+#undef GDN_MFMA_CASE
     return hipErrorInvalidValue;
 }
 

@@ -9,6 +9,13 @@
 // and the row is written back once: the kernel streams the fp32 state at the
 // HBM rate and does no other memory traffic worth counting.
 //
+// Input prologue (optional): q and k arrive unnormalised and the gates as
+// pre-activations.  Then k^ = k / |k| and q^ = q / |q| (norms clamped below
+// at 1e-6) enter only through the dot products, so the kernel scales those:
+// p = (S k) / |k|, u = beta (v - alpha p), S' = alpha S + (u / |k|) k^T and
+// o = alpha (S q) / |q| + u (k . q) / (|k| |q|); log alpha = -softplus(a),
+// beta = sigmoid(b).
+//
 // Mapping: 16 lanes own one row of S.  Lane c holds the float4 groups c and
 // 16 + c of the row, so each load or store instruction of a wave covers four
 // contiguous 256-byte half-rows (fully coalesced).  A 256-thread workgroup
@@ -43,7 +50,7 @@ __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) {
 
 template <int DK, typename TI, typename TO>
 __global__ __launch_bounds__(256) void step_kernel(
-    int DV, const TI *__restrict__ q, const TI *__restrict__ k,
+    int DV, int norm_qk, int gates, const TI *__restrict__ q, const TI *__restrict__ k,
     const TI *__restrict__ v, const float *__restrict__ log_alpha,
     const float *__restrict__ beta, float *__restrict__ S, TO *__restrict__ o) {
     constexpr int NV = DK / 64;    // float4 groups of a row per lane
@@ -65,8 +72,12 @@ __global__ __launch_bounds__(256) void step_kernel(
         kr[i] = load4(k + (size_t)unit * DK + 64 * i + 4 * c);
         qr[i] = load4(q + (size_t)unit * DK + 64 * i + 4 * c);
     }
-    const float a = expf(log_alpha[unit]);
-    const float b = beta[unit];
+    float la = log_alpha[unit], b = beta[unit];
+    if (gates) {
+        la = -(fmaxf(la, 0.f) + log1pf(expf(-fabsf(la))));
+        b = 1.f / (1.f + expf(-b));
+    }
+    const float a = expf(la);
 
     float kq = 0.f, pk = 0.f, pq = 0.f;
 #pragma unroll
@@ -80,19 +91,31 @@ __global__ __launch_bounds__(256) void step_kernel(
     kq = sum16(kq);
     pk = sum16(pk);
     pq = sum16(pq);
-    if (!live) return;
-    const float u = b * (to_f32(v[(size_t)unit * DV + row]) - a * pk);
+    float ik = 1.f, iq = 1.f;   // 1/|k|, 1/|q| (prologue), else 1
+    if (norm_qk) {
+        float kk = 0.f, qq = 0.f;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) sp[16 * i + c] = a * s[i] + u * kr[i];
-    if (c == 0) o[(size_t)unit * DV + row] = from_f32<TO>(a * pq + u * kq);
+        for (int i = 0; i < NV; ++i) {
+            kk += dot4(kr[i], kr[i]);
+            qq += dot4(qr[i], qr[i]);
+        }
+        ik = 1.f / sqrtf(fmaxf(sum16(kk), 1e-12f));
+        iq = 1.f / sqrtf(fmaxf(sum16(qq), 1e-12f));
+    }
+    if (!live) return;
+    const float u = b * (to_f32(v[(size_t)unit * DV + row]) - a * pk * ik);
+    const float uk = u * ik;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) sp[16 * i + c] = a * s[i] + uk * kr[i];
+    if (c == 0) o[(size_t)unit * DV + row] = from_f32<TO>((a * pq + uk * kq) * iq);
 }
 
 template <int DK, typename TI, typename TO>
-hipError_t launch_step_t(int B, int H, int DV, const void *q, const void *k,
+hipError_t launch_step_t(int B, int H, int DV, int norm_qk, int gates, const void *q, const void *k,
                          const void *v, const float *la, const float *beta,
                          float *S, void *o, hipStream_t st) {
     dim3 grid(B * H, (DV + kStepRowsPerWG - 1) / kStepRowsPerWG);
-    hipLaunchKernelGGL((step_kernel<DK, TI, TO>), grid, dim3(256), 0, st, DV,
+    hipLaunchKernelGGL((step_kernel<DK, TI, TO>), grid, dim3(256), 0, st, DV, norm_qk, gates,
                        (const TI *)q, (const TI *)k, (const TI *)v, la, beta, S,
                        (TO *)o);
     return hipGetLastError();
@@ -100,11 +123,12 @@ hipError_t launch_step_t(int B, int H, int DV, const void *q, const void *k,
 
 // io_bf16 / o_bf16 select bfloat16 (else fp32) for q,k,v and for o.
 hipError_t launch_step(int B, int H, int DK, int DV, bool io_bf16, bool o_bf16,
-                       const void *q, const void *k, const void *v,
+                       bool norm_qk, bool gates, const void *q, const void *k, const void *v,
                        const float *la, const float *beta, float *S, void *o,
                        hipStream_t st) {
 #define GDN_STEP_CASE(DKV, TI, TO)                                                 \
-    return launch_step_t<DKV, TI, TO>(B, H, DV, q, k, v, la, beta, S, o, st)
+    return launch_step_t<DKV, TI, TO>(B, H, DV, norm_qk ? 1 : 0, gates ? 1 : 0, q, k, v, la, \
+                                      beta, S, o, st)
     if (DK == 128) {
         if (io_bf16) { if (o_bf16) GDN_STEP_CASE(128, bf16, bf16); GDN_STEP_CASE(128, bf16, float); }
         if (o_bf16) GDN_STEP_CASE(128, float, bf16);

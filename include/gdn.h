@@ -42,9 +42,26 @@ typedef enum gdn_dtype {
     GDN_BF16 = 1   /* q, k, v, o in bfloat16 (fp32 state and accumulation) */
 } gdn_dtype;
 
+/* Optional input prologue, fused into the kernels (bit flags, OR-ed): the
+ * step just before the recurrence, which turns raw projections into its
+ * inputs.  The pages define no normalisation of q and k and no
+ * parametrisation of alpha and beta; the library's definitions are
+ *   GDN_PROLOGUE_NORM_QK  q <- q / max(|q|, 1e-6), k <- k / max(|k|, 1e-6)
+ *                         per token and head, in fp32 on the loaded values;
+ *   GDN_PROLOGUE_GATES    the log_alpha argument carries a pre-activation a
+ *                         and beta carries a pre-activation b;
+ *                         log alpha = -softplus(a), beta = sigmoid(b).
+ * 0 means q, k, log_alpha and beta are used as given. */
+typedef enum gdn_prologue {
+    GDN_PROLOGUE_NONE = 0,
+    GDN_PROLOGUE_NORM_QK = 1,
+    GDN_PROLOGUE_GATES = 2
+} gdn_prologue;
+
 typedef enum gdn_status {
     GDN_OK = 0,
-    GDN_ERR_INVALID_ARG = 1,  /* null required pointer, negative/zero dims, varlen with B != 1 */
+    GDN_ERR_INVALID_ARG = 1,  /* null required pointer, negative/zero dims, varlen with B != 1,
+                                 unknown prologue bits */
     GDN_ERR_UNSUPPORTED = 2,  /* (d_k, d_v, chunk, dtype) with no compiled kernel */
     GDN_ERR_ALIGNMENT = 3,    /* a pointer not 16-byte aligned */
     GDN_ERR_WORKSPACE = 4,    /* workspace smaller than gdn_chunk_fwd_workspace_size */
@@ -62,12 +79,14 @@ typedef enum gdn_status {
  *   o_dtype   a gdn_dtype for o.  GDN_F32 is the exact-parity choice: the
  *             read-outs are heavy-tailed (max |o| is 10-20x RMS(o) on
  *             random inputs), so rounding o to bf16 alone moves the largest
- *             outputs by up to ~4% of RMS(o). */
+ *             outputs by up to ~4% of RMS(o);
+ *   prologue  OR of gdn_prologue flags (0: inputs used as given). */
 typedef struct gdn_shape {
     int B, T, H, d_k, d_v, chunk;
     int n_seqs;
     int io_dtype;
     int o_dtype;
+    int prologue;
 } gdn_shape;
 
 /* Bytes of device workspace gdn_chunk_fwd needs for `shape` (written to
@@ -121,10 +140,11 @@ int gdn_chunk_fwd(const gdn_shape *shape,
  *   beta       [B, H]             fp32
  *   S          [B, H, d_v, d_k]   fp32, read and overwritten in place
  *   o          [B, H, d_v]        o_dtype output; must not alias S
+ *   prologue   OR of gdn_prologue flags, as in gdn_shape
  *
  * Supported: d_k = 128 or 64, any d_v >= 1; either dtype for the inputs and
  * for o.  Returns a gdn_status. */
-int gdn_step(int B, int H, int d_k, int d_v, int io_dtype, int o_dtype,
+int gdn_step(int B, int H, int d_k, int d_v, int io_dtype, int o_dtype, int prologue,
              const void *q, const void *k, const void *v,
              const float *log_alpha, const float *beta,
              float *S, void *o, void *stream);

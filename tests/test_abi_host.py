@@ -41,7 +41,8 @@ def test_version():
 
 
 def shape(**kw):
-    d = dict(B=2, T=100, H=4, d_k=128, d_v=128, chunk=64, n_seqs=0, io_dtype=1, o_dtype=0)
+    d = dict(B=2, T=100, H=4, d_k=128, d_v=128, chunk=64, n_seqs=0, io_dtype=1, o_dtype=0,
+             prologue=0)
     d.update(kw)
     return B.GdnShape(**d)
 
@@ -107,8 +108,8 @@ def test_fwd_empty_without_state_is_a_noop():
     assert err() == ""
 
 
-def step(Bn=2, H=3, dk=128, dv=128, io=1, od=0, q=P, k=P, v=P, la=P, be=P, S=P2, o=P):
-    return B.lib().gdn_step(Bn, H, dk, dv, io, od, q, k, v, la, be, S, o, None)
+def step(Bn=2, H=3, dk=128, dv=128, io=1, od=0, q=P, k=P, v=P, la=P, be=P, S=P2, o=P, pro=0):
+    return B.lib().gdn_step(Bn, H, dk, dv, io, od, pro, q, k, v, la, be, S, o, None)
 
 
 def test_step_rejects_before_launch():
@@ -119,6 +120,17 @@ def test_step_rejects_before_launch():
     assert step(S=None) == INVALID
     assert step(q=MIS) == ALIGN
     assert step(o=P2) == INVALID and "alias" in err()
+
+
+def test_prologue_flags_are_validated():
+    # bits 0 and 1 are the only prologue flags; anything else is rejected
+    for bad in (4, 8, -1, 1 << 30):
+        assert ws_size(shape(prologue=bad))[0] == INVALID and "prologue" in err()
+        assert fwd(shape(prologue=bad)) == INVALID
+        assert step(pro=bad) == INVALID and "prologue" in err()
+    for good in (0, 1, 2, 3):
+        assert ws_size(shape(prologue=good)) == (OK, 0)
+        assert ws_size(shape(prologue=good, io_dtype=0, d_k=32, d_v=32, chunk=32)) == (OK, 0)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
