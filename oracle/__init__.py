@@ -41,8 +41,10 @@ def build(src: str = _SRC, out: str = LIB_PATH) -> str:
 
 
 def load(path: str = LIB_PATH):
-    """Load a compiled oracle library (building the default one if absent)."""
-    if path == LIB_PATH and not os.path.exists(path):
+    """Load a compiled oracle library (building the default one if it is
+    absent or older than its source)."""
+    if path == LIB_PATH and (not os.path.exists(path)
+                             or os.path.getmtime(path) < os.path.getmtime(_SRC)):
         build()
     lib = ctypes.CDLL(path)
     dp = ctypes.POINTER(ctypes.c_double)
@@ -55,6 +57,12 @@ def load(path: str = LIB_PATH):
                                     ctypes.c_int, dp, dp, dp, dp, dp, dp, dp,
                                     ctypes.c_int]
     lib.gdn_oracle_step.restype = ctypes.c_int
+    if hasattr(lib, "gdn_oracle_bwd"):
+        lib.gdn_oracle_bwd.argtypes = [ctypes.c_int, ctypes.c_long, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ip,
+                                       dp, dp, dp, dp, dp, dp, dp, dp,
+                                       dp, dp, dp, dp, dp, dp, ctypes.c_int]
+        lib.gdn_oracle_bwd.restype = ctypes.c_int
     return lib
 
 
@@ -111,6 +119,42 @@ def fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, threads: int = 0,
     if rc != 0:
         raise ValueError("oracle: bad arguments")
     return o, st
+
+
+def bwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, dO=None, dS_T=None,
+        threads: int = 0, lib=None):
+    """Reverse-mode gradients of L = <dO, o> + <dS_T, S_T> through the fp64
+    token recurrence (same layouts as ``fwd``; dS_T None means zero).
+
+    Returns (dq, dk, dv, dlog_alpha, dbeta, dS0) as fp64 numpy arrays.
+    """
+    lib = lib or _lib_default()
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    la, be = as_f64(log_alpha), as_f64(beta)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens,
+            dtype=np.int32))
+        n_seqs = cu.shape[0] - 1
+        units = n_seqs
+        cu_p = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    else:
+        n_seqs, units, cu_p = 0, B, None
+    s0 = as_f64(S0) if S0 is not None else None
+    do = as_f64(dO)
+    dst = as_f64(dS_T) if dS_T is not None else None
+    dq, dk_, dv_ = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dla, dbe = np.zeros_like(la), np.zeros_like(be)
+    ds0 = np.zeros((units, H, dv, dk), dtype=np.float64)
+    rc = lib.gdn_oracle_bwd(B, T, H, dk, dv, n_seqs, cu_p,
+                            _ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be), _ptr(s0),
+                            _ptr(do), _ptr(dst), _ptr(dq), _ptr(dk_), _ptr(dv_),
+                            _ptr(dla), _ptr(dbe), _ptr(ds0), int(threads))
+    if rc != 0:
+        raise ValueError("oracle: bad arguments")
+    return dq, dk_, dv_, dla, dbe, ds0
 
 
 def step(q, k, v, log_alpha, beta, S, threads: int = 0, lib=None):

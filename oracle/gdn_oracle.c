@@ -154,3 +154,185 @@ int gdn_oracle_step(int B, int H, int dk, int dv,
     return gdn_oracle_fwd(B, 1, H, dk, dv, 0, NULL, q, k, v, log_alpha, beta,
                           S, o, S, n_threads);
 }
+
+/* ------------------------------------------------------------------------
+ * Backward pass (reverse mode of the recurrence above), fp64.
+ *
+ * The pages name a backward pass as part of efficient parallel training
+ * ("Gated DeltaNet-2: Decoupling Erase and Write in Linear Attention",
+ * abstract: a gate-aware backward pass; blog "Gated DeltaNet: Harmonizing
+ * Gating and the Delta Rule for Superior Linear RNNs", section
+ * "Hardware-Efficient Training") but print none; a backward pass is fixed by
+ * its forward: the gradient of L = sum_t <dO_t, o_t> + <dS_T, S_T> with
+ * respect to every input.  Written here as the chain rule through each token
+ * in reverse order, for the step
+ *
+ *     p = S_{t-1} k,  u = beta (v - alpha p),  S_t = alpha S_{t-1} + u k^T,
+ *     o_t = S_t q,    alpha = e^{log_alpha}.
+ *
+ * With G the gradient of L with respect to S_t (dS_T after the last token):
+ *     G   += dO_t q^T                  (o_t reads the post-update state)
+ *     dq   = S_t^T dO_t
+ *     du   = G k,       dk = G^T u + S_{t-1}^T dp,   dp = -alpha beta du
+ *     dv   = beta du,   dbeta = du . (v - alpha p)
+ *     dalpha = <G, S_{t-1}> - beta du . p,           dlog_alpha = alpha dalpha
+ *     G_{t-1} = alpha G + dp k^T
+ * and dS0 = G_0.  The states S_{t-1} are recomputed forward from
+ * checkpoints taken every kSeg tokens, one segment at a time.
+ * ------------------------------------------------------------------------ */
+enum { kSeg = 32 };
+
+static void bwd_unit(long L, int dk, int dv,
+                     const double *q, const double *k, const double *v,
+                     const double *log_alpha, const double *beta,
+                     long ts_k, long ts_v, long ts_g,
+                     const double *S0, const double *dO, const double *dS_T,
+                     double *dq, double *dk_out, double *dv_out,
+                     double *dla, double *dbeta, double *dS0,
+                     double *ck, double *seg, double *G, double *p, double *du, double *dp)
+{
+    const long n = (long)dv * dk;
+    const long nck = (L + kSeg - 1) / kSeg;
+    /* forward: checkpoint j holds the state before token j * kSeg */
+    double *S = seg;   /* scratch for the running state */
+    for (long e = 0; e < n; ++e) S[e] = S0 ? S0[e] : 0.0;
+    for (long t = 0; t < L; ++t) {
+        if (t % kSeg == 0) memcpy(ck + (t / kSeg) * n, S, sizeof(double) * n);
+        const double *kt = k + t * ts_k, *vt = v + t * ts_v;
+        const double a = exp(log_alpha[t * ts_g]), b = beta[t * ts_g];
+        for (int r = 0; r < dv; ++r) {
+            double acc = 0.0;
+            for (int c = 0; c < dk; ++c) acc += S[(long)r * dk + c] * kt[c];
+            const double w = b * vt[r] - a * b * acc;
+            for (int c = 0; c < dk; ++c) S[(long)r * dk + c] = a * S[(long)r * dk + c] + w * kt[c];
+        }
+    }
+    for (long e = 0; e < n; ++e) G[e] = dS_T ? dS_T[e] : 0.0;
+
+    for (long j = nck - 1; j >= 0; --j) {
+        const long t0 = j * kSeg, t1 = (t0 + kSeg < L) ? t0 + kSeg : L;
+        /* seg[i] = state after token t0 + i - 1, i.e. seg[0] = checkpoint */
+        memcpy(seg, ck + j * n, sizeof(double) * n);
+        for (long t = t0; t < t1; ++t) {
+            const double *Sp = seg + (t - t0) * n;
+            double *Sn = seg + (t - t0 + 1) * n;
+            const double *kt = k + t * ts_k, *vt = v + t * ts_v;
+            const double a = exp(log_alpha[t * ts_g]), b = beta[t * ts_g];
+            for (int r = 0; r < dv; ++r) {
+                double acc = 0.0;
+                for (int c = 0; c < dk; ++c) acc += Sp[(long)r * dk + c] * kt[c];
+                const double w = b * vt[r] - a * b * acc;
+                for (int c = 0; c < dk; ++c)
+                    Sn[(long)r * dk + c] = a * Sp[(long)r * dk + c] + w * kt[c];
+            }
+        }
+        for (long t = t1 - 1; t >= t0; --t) {
+            const double *Sp = seg + (t - t0) * n;       /* S_{t-1} */
+            const double *Sn = seg + (t - t0 + 1) * n;   /* S_t */
+            const double *kt = k + t * ts_k, *qt = q + t * ts_k, *vt = v + t * ts_v;
+            const double *dot = dO + t * ts_v;
+            const double a = exp(log_alpha[t * ts_g]), b = beta[t * ts_g];
+            double *dqt = dq + t * ts_k, *dkt = dk_out + t * ts_k, *dvt = dv_out + t * ts_v;
+            /* G += dO_t q^T */
+            for (int r = 0; r < dv; ++r)
+                for (int c = 0; c < dk; ++c) G[(long)r * dk + c] += dot[r] * qt[c];
+            /* dq = S_t^T dO_t */
+            for (int c = 0; c < dk; ++c) {
+                double acc = 0.0;
+                for (int r = 0; r < dv; ++r) acc += Sn[(long)r * dk + c] * dot[r];
+                dqt[c] = acc;
+            }
+            /* p = S_{t-1} k, du = G k */
+            for (int r = 0; r < dv; ++r) {
+                double ap = 0.0, ag = 0.0;
+                for (int c = 0; c < dk; ++c) {
+                    ap += Sp[(long)r * dk + c] * kt[c];
+                    ag += G[(long)r * dk + c] * kt[c];
+                }
+                p[r] = ap;
+                du[r] = ag;
+            }
+            double db = 0.0, dup = 0.0;
+            for (int r = 0; r < dv; ++r) {
+                db += du[r] * (vt[r] - a * p[r]);
+                dup += du[r] * p[r];
+                dvt[r] = b * du[r];
+                dp[r] = -a * b * du[r];
+            }
+            /* dk = G^T u + S_{t-1}^T dp, with u = beta (v - alpha p) */
+            for (int c = 0; c < dk; ++c) {
+                double acc = 0.0;
+                for (int r = 0; r < dv; ++r)
+                    acc += G[(long)r * dk + c] * b * (vt[r] - a * p[r]) + Sp[(long)r * dk + c] * dp[r];
+                dkt[c] = acc;
+            }
+            /* dalpha = <G, S_{t-1}> - beta du . p */
+            double gs = 0.0;
+            for (long e = 0; e < n; ++e) gs += G[e] * Sp[e];
+            dla[t * ts_g] = a * (gs - b * dup);
+            dbeta[t * ts_g] = db;
+            /* G_{t-1} = alpha G + dp k^T */
+            for (int r = 0; r < dv; ++r)
+                for (int c = 0; c < dk; ++c)
+                    G[(long)r * dk + c] = a * G[(long)r * dk + c] + dp[r] * kt[c];
+        }
+    }
+    if (dS0)
+        for (long e = 0; e < n; ++e) dS0[e] = G[e];
+}
+
+/* Gradients of L = sum <dO, o> + <dS_T, S_T> for the forward of
+ * gdn_oracle_fwd (same layouts; dS_T may be NULL = zero).  Outputs dq, dk
+ * [B,T,H,d_k]; dv [B,T,H,d_v]; dlog_alpha, dbeta [B,T,H]; dS0 [units,H,d_v,d_k]
+ * (may be NULL).  Returns 0 on success, -1 on a bad argument or allocation. */
+int gdn_oracle_bwd(int B, long T, int H, int dk, int dv,
+                   int n_seqs, const int32_t *cu_seqlens,
+                   const double *q, const double *k, const double *v,
+                   const double *log_alpha, const double *beta, const double *S0,
+                   const double *dO, const double *dS_T,
+                   double *dq, double *dk_out, double *dv_out,
+                   double *dlog_alpha, double *dbeta, double *dS0, int n_threads)
+{
+    if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    if (!q || !k || !v || !log_alpha || !beta || !dO) return -1;
+    if (!dq || !dk_out || !dv_out || !dlog_alpha || !dbeta) return -1;
+    const int varlen = (cu_seqlens != NULL && n_seqs > 0);
+    if (varlen && B != 1) return -1;
+    const int units = varlen ? n_seqs : B;
+    const long n_work = (long)units * H;
+    int bad = 0;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (long w = 0; w < n_work; ++w) {
+        const int u = (int)(w / H), h = (int)(w % H);
+        long t0, L;
+        if (varlen) {
+            t0 = cu_seqlens[u];
+            L = (long)cu_seqlens[u + 1] - cu_seqlens[u];
+            if (t0 < 0 || L < 0 || t0 + L > T) { bad |= 1; continue; }
+        } else {
+            t0 = (long)u * T;
+            L = T;
+        }
+        const size_t n = (size_t)dv * dk;
+        const long nck = (L + kSeg - 1) / kSeg;
+        double *mem = (double *)malloc(sizeof(double) *
+                                       (n * (size_t)(nck + kSeg + 2) + 3 * (size_t)dv));
+        if (!mem) { bad |= 1; continue; }
+        double *ck = mem, *seg = ck + n * (size_t)nck, *G = seg + n * (kSeg + 1);
+        double *p = G + n, *du = p + dv, *dp = du + dv;
+        const long gk = t0 * H + h;
+        const long unit_state = ((long)u * H + h) * (long)n;
+        bwd_unit(L, dk, dv, q + gk * dk, k + gk * dk, v + gk * dv, log_alpha + gk, beta + gk,
+                 (long)H * dk, (long)H * dv, H,
+                 S0 ? S0 + unit_state : NULL, dO + gk * dv, dS_T ? dS_T + unit_state : NULL,
+                 dq + gk * dk, dk_out + gk * dk, dv_out + gk * dv, dlog_alpha + gk, dbeta + gk,
+                 dS0 ? dS0 + unit_state : NULL, ck, seg, G, p, du, dp);
+        free(mem);
+    }
+    return bad ? -1 : 0;
+}
