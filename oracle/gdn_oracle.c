@@ -194,17 +194,18 @@ static void bwd_unit(long L, int dk, int dv,
     const long n = (long)dv * dk;
     const long nck = (L + kSeg - 1) / kSeg;
     /* forward: checkpoint j holds the state before token j * kSeg */
-    double *S = seg;   /* scratch for the running state */
-    for (long e = 0; e < n; ++e) S[e] = S0 ? S0[e] : 0.0;
+    double *run = seg;   /* scratch for the running state */
+    for (long e = 0; e < n; ++e) run[e] = (S0 != NULL) ? S0[e] : 0.0;
     for (long t = 0; t < L; ++t) {
-        if (t % kSeg == 0) memcpy(ck + (t / kSeg) * n, S, sizeof(double) * n);
+        if (t % kSeg == 0) memcpy(ck + (t / kSeg) * n, run, sizeof(double) * n);
         const double *kt = k + t * ts_k, *vt = v + t * ts_v;
         const double a = exp(log_alpha[t * ts_g]), b = beta[t * ts_g];
         for (int r = 0; r < dv; ++r) {
             double acc = 0.0;
-            for (int c = 0; c < dk; ++c) acc += S[(long)r * dk + c] * kt[c];
+            for (int c = 0; c < dk; ++c) acc += run[(long)r * dk + c] * kt[c];
             const double w = b * vt[r] - a * b * acc;
-            for (int c = 0; c < dk; ++c) S[(long)r * dk + c] = a * S[(long)r * dk + c] + w * kt[c];
+            for (int c = 0; c < dk; ++c)
+                run[(long)r * dk + c] = a * run[(long)r * dk + c] + w * kt[c];
         }
     }
     for (long e = 0; e < n; ++e) G[e] = dS_T ? dS_T[e] : 0.0;
