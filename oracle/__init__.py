@@ -12,7 +12,9 @@ Two independent CPU forms live here:
   Delta Rule" (research-map summary, section "Approach") with the read-out
   o_t = S_t q_t on the post-update state (the pages print no read-out).
 * ``chunk_form``: the chunkwise WY/UT form in NumPy fp64, used to check that
-  the chunk algorithm reaches the recurrence's result for every chunk size.
+  the chunk algorithm reaches the recurrence's result for every chunk size,
+  forward and backward.
+* ``bwd``: reverse-mode gradients through the fp64 token recurrence (C).
 
 Neither form has values printed on the pages to compare against; both are
 pinned by the closed forms and invariants in ``tests/test_oracle_pins.py``.

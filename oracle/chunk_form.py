@@ -110,3 +110,127 @@ def fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, chunk: int = 64):
             o[b, t0:t1, h] = O
             st[u, h] = S
     return o, st
+
+
+# ---------------------------------------------------------------------------
+# Backward of the chunk form (reverse mode, fp64).
+#
+# The pages name a gate-aware backward pass for the chunkwise algorithm
+# ("Gated DeltaNet-2: Decoupling Erase and Write in Linear Attention",
+# abstract) but print none; this is the chain rule taken through steps 1-6
+# above, one chunk at a time.  With S the state entering a chunk, dS' the
+# gradient of the state leaving it, dO the output gradient, and
+# P = tril(Q K^T) o E, K~ = diag(e^{g_n - g}) K:
+#
+#   dDelta = P^T dO + K~ dS'^T
+#   dS     = e^{g_n} dS' + dO^T diag(e^g) Q - dDelta^T W     (to the previous chunk)
+#
+# so the state gradients run over the chunks in reverse order, and every
+# other gradient of a chunk needs only its (S, dS'):
+#
+#   dP   = tril(dO Delta^T),  dQK = dP o E
+#   dQ   = diag(e^g) dO S + dQK K
+#   dW   = -dDelta S,  dU = dDelta,  dV = diag(beta) T^T dU
+#   dK   = dQK^T Q + diag(e^{g_n - g}) Delta dS' + diag(beta e^g) T^T dW + dG K + dG^T K
+#   dT   = dU V^T diag(beta) + dW K^T diag(beta e^g),  dA = -strict(T^T dT T^T)
+#   dG   = dA o beta_r E  (strictly lower)
+#   dbeta = rows(T^T dU . V) + e^g rows(T^T dW . K) + rowsum(dA o E o K K^T)
+#   dg   = e^g rows(dO . Q S^T) + rowsum(dP o P) - colsum(dP o P)
+#          + beta e^g rows(T^T dW . K) + rowsum(dA o A) - colsum(dA o A)
+#          - s + [last] (sum(s) + e^{g_n} <dS', S>),   s_r = rows(Delta dS' . K~)_r
+#   dlog_alpha = reverse cumulative sum of dg within the chunk.
+# ---------------------------------------------------------------------------
+def chunk_grads(Q, K, V, la, beta, S, dO, dSn):
+    """Gradients of one chunk given the entering state S and the gradient dSn
+    of the leaving state.  Returns (dQ, dK, dV, dla, dbeta, dS)."""
+    n = Q.shape[0]
+    g = np.cumsum(la)
+    eg = np.exp(g)
+    diff = g[:, None] - g[None, :]
+    strict = np.tril(np.ones((n, n), dtype=bool), -1)
+    lower = np.tril(np.ones((n, n), dtype=bool), 0)
+    E = np.exp(np.where(lower, diff, -np.inf))
+    KK = K @ K.T
+    A = beta[:, None] * np.where(strict, E, 0.0) * KK
+    T = unit_lower_inverse(np.eye(n) + A)
+    U = T @ (beta[:, None] * V)
+    W = T @ ((beta * eg)[:, None] * K)
+    D = U - W @ S.T
+    P = (Q @ K.T) * E
+    Kt = np.exp(g[-1] - g)[:, None] * K
+    dD = P.T @ dO + Kt @ dSn.T
+    dS = np.exp(g[-1]) * dSn + dO.T @ (eg[:, None] * Q) - dD.T @ W
+    dP = np.where(lower, dO @ D.T, 0.0)
+    dQK = dP * E
+    dQ = eg[:, None] * (dO @ S) + dQK @ K
+    dW = -dD @ S
+    TdU, TdW = T.T @ dD, T.T @ dW
+    dV = beta[:, None] * TdU
+    dKt = D @ dSn
+    dT = dD @ (beta[:, None] * V).T + dW @ ((beta * eg)[:, None] * K).T
+    dA = np.where(strict, -(T.T @ dT @ T.T), 0.0)
+    dG = dA * beta[:, None] * E
+    dK = (dQK.T @ Q + np.exp(g[-1] - g)[:, None] * dKt
+          + (beta * eg)[:, None] * TdW + dG @ K + dG.T @ K)
+    rw = np.sum(TdW * K, axis=1)
+    dbeta = np.sum(TdU * V, axis=1) + eg * rw + np.sum(dA * E * KK, axis=1)
+    s = np.sum(dKt * Kt, axis=1)
+    dg = (eg * np.sum(dO * (Q @ S.T), axis=1)
+          + np.sum(dP * P, axis=1) - np.sum(dP * P, axis=0)
+          + beta * eg * rw
+          + np.sum(dA * A, axis=1) - np.sum(dA * A, axis=0)
+          - s)
+    dg[-1] += np.sum(s) + np.exp(g[-1]) * np.sum(dSn * S)
+    dla = np.cumsum(dg[::-1])[::-1]
+    return dQ, dK, dV, dla, dbeta, dS
+
+
+def unit_bwd(Q, K, V, la, beta, S0, dO, dST, C: int):
+    """Backward of ``unit_fwd``: forward states per chunk, reverse state
+    gradients, then each chunk's gradients."""
+    L = Q.shape[0]
+    starts = list(range(0, L, C))
+    states = []
+    S = np.array(S0, dtype=np.float64, copy=True)
+    for s in starts:
+        e = min(s + C, L)
+        states.append(S)
+        S = chunk_step(Q[s:e], K[s:e], V[s:e], la[s:e], beta[s:e], S)[1]
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    dla, dbeta = np.zeros_like(la), np.zeros_like(beta)
+    G = np.array(dST, dtype=np.float64, copy=True)
+    for ci in range(len(starts) - 1, -1, -1):
+        s, e = starts[ci], min(starts[ci] + C, L)
+        r = chunk_grads(Q[s:e], K[s:e], V[s:e], la[s:e], beta[s:e], states[ci], dO[s:e], G)
+        dQ[s:e], dK[s:e], dV[s:e], dla[s:e], dbeta[s:e], G = r
+    return dQ, dK, dV, dla, dbeta, G
+
+
+def bwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, dO=None, dS_T=None,
+        chunk: int = 64):
+    """Chunkwise backward over the same layouts as ``oracle.bwd``."""
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    la, be = as_f64(log_alpha), as_f64(beta)
+    do = as_f64(dO)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens is not None:
+        cu = np.asarray(cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu")
+                        else cu_seqlens, dtype=np.int64)
+        spans = [(0, int(cu[i]), int(cu[i + 1])) for i in range(len(cu) - 1)]
+    else:
+        spans = [(b, 0, T) for b in range(B)]
+    s0 = as_f64(S0) if S0 is not None else None
+    dst = as_f64(dS_T) if dS_T is not None else None
+    out = [np.zeros_like(q), np.zeros_like(k), np.zeros_like(v), np.zeros_like(la),
+           np.zeros_like(be), np.zeros((len(spans), H, dv, dk))]
+    for u, (b, t0, t1) in enumerate(spans):
+        for h in range(H):
+            init = s0[u, h] if s0 is not None else np.zeros((dv, dk))
+            gS = dst[u, h] if dst is not None else np.zeros((dv, dk))
+            r = unit_bwd(q[b, t0:t1, h], k[b, t0:t1, h], v[b, t0:t1, h], la[b, t0:t1, h],
+                         be[b, t0:t1, h], init, do[b, t0:t1, h], gS, chunk)
+            for i in range(5):
+                out[i][b, t0:t1, h] = r[i]
+            out[5][u, h] = r[5]
+    return tuple(out)

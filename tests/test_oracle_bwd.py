@@ -89,3 +89,25 @@ def test_planted_bwd_mistake_is_caught(tmp_path, name):
     assert text.count(old) == 1, f"mutation anchor not found: {old}"
     rc, out = _run_pins(tmp_path, name, text.replace(old, new))
     assert rc != 0, f"no pin caught the planted mistake {name!r}"
+
+
+@pytest.mark.parametrize("C", [1, 3, 16, 64])
+def test_chunk_form_backward_equals_recurrence_backward(C):
+    """The chunkwise backward (reverse state gradients across chunks, then
+    each chunk's gradients) reaches the token recurrence's gradients."""
+    import numpy as np
+    from oracle import chunk_form
+    rng = np.random.default_rng(40 + C)
+    cu = np.array([0, 70, 70, 131, 200], dtype=np.int32)
+    x = pins._inputs(rng, 1, 200, 2, 8, 6, units=4)
+    x["k"] /= np.linalg.norm(x["k"], axis=-1, keepdims=True)
+    for c in (None, cu):
+        if c is None:
+            y = pins._inputs(rng, 2, 150, 2, 8, 6)
+        else:
+            y = x
+        a = oracle.bwd(y["q"], y["k"], y["v"], y["la"], y["be"], y["S0"], c, y["dO"], y["dS_T"])
+        b = chunk_form.bwd(y["q"], y["k"], y["v"], y["la"], y["be"], y["S0"], c, y["dO"],
+                           y["dS_T"], chunk=C)
+        for ga, gb in zip(a, b):
+            assert np.max(np.abs(ga - gb)) <= 1e-11 * max(1.0, np.max(np.abs(ga)))
