@@ -9,8 +9,9 @@ with the read-out o_t = S_t q_t ("Gated Delta Networks: Improving Mamba2 with
 Delta Rule", research-map summary, section "Approach").  All arithmetic runs
 in the HIP kernels of libgdn.so; see include/gdn.h for the C ABI.
 """
-from ._binding import (GDN_BF16, GDN_F32, GdnError, chunk_fwd,  # noqa: F401
-                       chunk_fwd_workspace_size, lib, step, version)
+from ._binding import (GDN_BF16, GDN_F32, GdnError, chunk_bwd,  # noqa: F401
+                       chunk_bwd_workspace_size, chunk_fwd, chunk_fwd_workspace_size, lib,
+                       step, version)
 
-__all__ = ["chunk_fwd", "step", "chunk_fwd_workspace_size", "version", "lib",
-           "GdnError", "GDN_F32", "GDN_BF16"]
+__all__ = ["chunk_fwd", "chunk_bwd", "step", "chunk_fwd_workspace_size",
+           "chunk_bwd_workspace_size", "version", "lib", "GdnError", "GDN_F32", "GDN_BF16"]

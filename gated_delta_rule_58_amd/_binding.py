@@ -34,6 +34,9 @@ SYMBOLS = {
                                               ctypes.POINTER(_sz)]),
     "gdn_chunk_fwd": (_c_int, [ctypes.POINTER(GdnShape), _vp, _vp, _vp, _vp, _vp,
                                _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "gdn_chunk_bwd_workspace_size": (_c_int, [ctypes.POINTER(GdnShape),
+                                              ctypes.POINTER(_sz)]),
+    "gdn_chunk_bwd": (_c_int, [ctypes.POINTER(GdnShape)] + [_vp] * 16 + [_sz, _vp]),
     "gdn_step": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "gdn_last_error": (ctypes.c_char_p, []),
@@ -150,6 +153,62 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, chunk=64,
                                _ptr(o), _ptr(S_T), _ptr(ws), ws_bytes.value,
                                _stream(q.device)))
     return o, S_T
+
+
+def chunk_bwd_workspace_size(B, T, H, d_k, d_v, chunk=64, n_seqs=0,
+                             io_dtype=torch.bfloat16, o_dtype=torch.float32) -> int:
+    shape = GdnShape(B, T, H, d_k, d_v, chunk, n_seqs, _DTYPE[io_dtype], _DTYPE[o_dtype], 0)
+    out = ctypes.c_size_t(0)
+    _check(lib().gdn_chunk_bwd_workspace_size(ctypes.byref(shape), ctypes.byref(out)))
+    return out.value
+
+
+def chunk_bwd(q, k, v, log_alpha, beta, dO, S0=None, cu_seqlens=None, dS_T=None, chunk=64,
+              want_dS0=True, workspace=None):
+    """Backward of chunk_fwd: gradients of <dO, o> + <dS_T, S_T>.  dO
+    [B,T,H,dv] (fp32 or bf16; the q/k/v gradients take its dtype); dS_T
+    [U,H,dv,dk] fp32 or None.  Returns (dq, dk, dv, dlog_alpha, dbeta, dS0)
+    (dS0 is None when want_dS0 is False)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    io = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need_cuda(name, t, io)
+    for name, t in (("log_alpha", log_alpha), ("beta", beta)):
+        _need_cuda(name, t, torch.float32)
+        if tuple(t.shape) != (B, T, H):
+            raise ValueError(f"{name} must be [B,T,H]")
+    _need_cuda("dO", dO)
+    if tuple(dO.shape) != (B, T, H, dv) or dO.dtype not in _DTYPE:
+        raise ValueError("dO must be [B,T,H,dv] fp32 or bf16")
+    n_seqs = 0
+    if cu_seqlens is not None:
+        _need_cuda("cu_seqlens", cu_seqlens, torch.int32)
+        n_seqs = cu_seqlens.shape[0] - 1
+    units = n_seqs if n_seqs > 0 else B
+    for name, t in (("S0", S0), ("dS_T", dS_T)):
+        if t is not None:
+            _need_cuda(name, t, torch.float32)
+            if tuple(t.shape) != (units, H, dv, dk):
+                raise ValueError(f"{name} must be [{units},{H},{dv},{dk}]")
+    gd = dO.dtype
+    dq = torch.empty((B, T, H, dk), device=q.device, dtype=gd)
+    dk_ = torch.empty((B, T, H, dk), device=q.device, dtype=gd)
+    dv_ = torch.empty((B, T, H, dv), device=q.device, dtype=gd)
+    dla = torch.empty((B, T, H), device=q.device, dtype=torch.float32)
+    dbe = torch.empty((B, T, H), device=q.device, dtype=torch.float32)
+    dS0 = (torch.empty((units, H, dv, dk), device=q.device, dtype=torch.float32)
+           if want_dS0 else None)
+    shape = GdnShape(B, T, H, dk, dv, chunk, n_seqs, _DTYPE[io], _DTYPE[gd], 0)
+    need = ctypes.c_size_t(0)
+    _check(lib().gdn_chunk_bwd_workspace_size(ctypes.byref(shape), ctypes.byref(need)))
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty(max(need.value, 1), device=q.device, dtype=torch.uint8)
+    _check(lib().gdn_chunk_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                               _ptr(beta), _ptr(S0), _ptr(cu_seqlens), _ptr(dO), _ptr(dS_T),
+                               _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dla), _ptr(dbe), _ptr(dS0),
+                               _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return dq, dk_, dv_, dla, dbe, dS0
 
 
 def step(q, k, v, log_alpha, beta, S, o_dtype=torch.float32, o=None, norm_qk=False,

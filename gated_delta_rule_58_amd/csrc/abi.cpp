@@ -24,6 +24,13 @@ hipError_t launch_chunk_mfma(int units, int T, int H, int dk, bool o_bf16, bool 
                              bool gates, const int32_t *cu, const void *q, const void *k,
                              const void *v, const float *la, const float *beta,
                              const float *S0, void *o, float *S_T, hipStream_t st);
+bool chunk_bwd_supported(int dk, int dv, int chunk, bool io_bf16);
+size_t chunk_bwd_ws_bytes(int units, int T, int H, int d, bool varlen);
+hipError_t launch_chunk_bwd(int units, int T, int H, int d, bool io_bf16, bool g_bf16,
+                            const int32_t *cu, const void *q, const void *k, const void *v,
+                            const float *la, const float *beta, const float *S0,
+                            const void *dO, const float *dST, void *dq, void *dk, void *dv,
+                            float *dla, float *dbeta, float *dS0, void *ws, hipStream_t st);
 }  // namespace gdn
 
 namespace {
@@ -86,6 +93,38 @@ int check_shape(const gdn_shape *s) {
     return GDN_OK;
 }
 
+// Shape checks of the backward (its own supported set, no prologue).
+int check_bwd_shape(const gdn_shape *s) {
+    if (!s) return fail(GDN_ERR_INVALID_ARG, "shape is NULL");
+    if (s->B <= 0 || s->H <= 0 || s->T < 0 || s->d_k <= 0 || s->d_v <= 0 || s->chunk <= 0)
+        return fail(GDN_ERR_INVALID_ARG,
+                    "bad dimensions B=%d T=%d H=%d d_k=%d d_v=%d chunk=%d (need B,H,d_k,d_v,chunk > 0, T >= 0)",
+                    s->B, s->T, s->H, s->d_k, s->d_v, s->chunk);
+    if (s->n_seqs < 0) return fail(GDN_ERR_INVALID_ARG, "n_seqs=%d is negative", s->n_seqs);
+    if (s->n_seqs > 0 && s->B != 1)
+        return fail(GDN_ERR_INVALID_ARG, "packed sequences (n_seqs=%d) need B == 1, got B=%d",
+                    s->n_seqs, s->B);
+    if (!valid_dtype(s->io_dtype) || !valid_dtype(s->o_dtype))
+        return fail(GDN_ERR_INVALID_ARG, "io_dtype=%d / o_dtype=%d is not a gdn_dtype",
+                    s->io_dtype, s->o_dtype);
+    if (!valid_prologue(s->prologue))
+        return fail(GDN_ERR_INVALID_ARG, "prologue=%d has bits outside gdn_prologue",
+                    s->prologue);
+    if (s->prologue != 0)
+        return fail(GDN_ERR_UNSUPPORTED, "the backward takes no input prologue (prologue=%d)",
+                    s->prologue);
+    const long units = s->n_seqs > 0 ? s->n_seqs : s->B;
+    if ((long)units * s->H > (1L << 24) || (long)s->T * s->H > (1L << 31) / 64)
+        return fail(GDN_ERR_INVALID_ARG, "problem too large for the backward (units x heads = %ld)",
+                    units * (long)s->H);
+    if (!gdn::chunk_bwd_supported(s->d_k, s->d_v, s->chunk, s->io_dtype == GDN_BF16))
+        return fail(GDN_ERR_UNSUPPORTED,
+                    "no backward kernel for d_k=%d d_v=%d chunk=%d io_dtype=%s (bf16: d_k=d_v in "
+                    "{64,128}; f32: d_k=d_v=64; chunk 64)",
+                    s->d_k, s->d_v, s->chunk, s->io_dtype == GDN_BF16 ? "bf16" : "f32");
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -140,6 +179,56 @@ int gdn_chunk_fwd(const gdn_shape *s, const void *q, const void *k, const void *
     else
         e = gdn::launch_chunk_f32(units, s->T, s->H, s->d_k, s->chunk, o_bf16, norm_qk, gates,
                                   cu_seqlens, q, k, v, log_alpha, beta, S0, o, S_T, st);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int gdn_chunk_bwd_workspace_size(const gdn_shape *shape, size_t *bytes) {
+    if (!bytes) return fail(GDN_ERR_INVALID_ARG, "bytes is NULL");
+    const int rc = check_bwd_shape(shape);
+    if (rc != GDN_OK) return rc;
+    const int units = shape->n_seqs > 0 ? shape->n_seqs : shape->B;
+    *bytes = gdn::chunk_bwd_ws_bytes(units, shape->T, shape->H, shape->d_k, shape->n_seqs > 0);
+    return ok();
+}
+
+int gdn_chunk_bwd(const gdn_shape *s, const void *q, const void *k, const void *v,
+                  const float *log_alpha, const float *beta, const float *S0,
+                  const int32_t *cu_seqlens, const void *dO, const float *dS_T, void *dq,
+                  void *dk, void *dv, float *dlog_alpha, float *dbeta, float *dS0,
+                  void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = check_bwd_shape(s);
+    if (rc != GDN_OK) return rc;
+    if (s->n_seqs > 0 && !cu_seqlens)
+        return fail(GDN_ERR_INVALID_ARG, "n_seqs=%d but cu_seqlens is NULL", s->n_seqs);
+    if (s->n_seqs == 0 && cu_seqlens)
+        return fail(GDN_ERR_INVALID_ARG, "cu_seqlens given but n_seqs is 0");
+    if (s->T > 0 && (!q || !k || !v || !log_alpha || !beta || !dO || !dq || !dk || !dv ||
+                     !dlog_alpha || !dbeta))
+        return fail(GDN_ERR_INVALID_ARG,
+                    "q, k, v, log_alpha, beta, dO and every token gradient are required when T > 0");
+    const void *ptrs[] = {q, k, v, log_alpha, beta, S0, cu_seqlens, dO, dS_T, dq, dk, dv,
+                          dlog_alpha, dbeta, dS0, workspace};
+    const char *names[] = {"q", "k", "v", "log_alpha", "beta", "S0", "cu_seqlens", "dO", "dS_T",
+                           "dq", "dk", "dv", "dlog_alpha", "dbeta", "dS0", "workspace"};
+    for (int i = 0; i < 16; ++i)
+        if (misaligned(ptrs[i]))
+            return fail(GDN_ERR_ALIGNMENT, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
+    const void *ins[] = {q, k, v, log_alpha, beta, S0, dO, dS_T};
+    const void *outs[] = {dq, dk, dv, dlog_alpha, dbeta, dS0};
+    for (const void *o : outs)
+        for (const void *in : ins)
+            if (o && o == in) return fail(GDN_ERR_INVALID_ARG, "a gradient output aliases an input");
+    size_t need = 0;
+    gdn_chunk_bwd_workspace_size(s, &need);
+    if (workspace_bytes < need)
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    if (need > 0 && !workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL");
+    const int units = s->n_seqs > 0 ? s->n_seqs : s->B;
+    const hipError_t e = gdn::launch_chunk_bwd(
+        units, s->T, s->H, s->d_k, s->io_dtype == GDN_BF16, s->o_dtype == GDN_BF16, cu_seqlens, q,
+        k, v, log_alpha, beta, S0, dO, dS_T, dq, dk, dv, dlog_alpha, dbeta, dS0, workspace,
+        reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }

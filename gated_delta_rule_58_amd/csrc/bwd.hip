@@ -1,0 +1,827 @@
+// Backward pass of the chunkwise gated delta rule on gfx950 (fp32 MFMA).
+//
+// The pages name a gate-aware backward pass for the chunkwise algorithm
+// ("Gated DeltaNet-2: Decoupling Erase and Write in Linear Attention",
+// abstract) but print none; this is the chain rule taken through the WY/UT
+// chunk steps (research-map summary of "Gated Delta Networks: Improving
+// Mamba2 with Delta Rule", section "Approach"; blog "Gated DeltaNet:
+// Harmonizing Gating and the Delta Rule for Superior Linear RNNs", section
+// "Hardware-Efficient Training").  Per chunk of n <= 64 tokens, with S the
+// state entering it, dS' the gradient of the state leaving it, g the
+// chunk-local prefix of log alpha, G[r,i] = e^{g_r - g_i} (i <= r),
+// A = strict(beta G o K K^T), T = (I + A)^{-1}, P = tril(Q K^T) o G:
+//
+//   Delta  = T diag(beta) (V - diag(e^g) K S^T)            (forward values)
+//   dDelta = P^T dO + diag(e^{g_n - g}) K dS'^T
+//   dS     = e^{g_n} dS' + dO^T diag(e^g) Q - F^T K,  F = diag(beta e^g) T^T dDelta
+//
+// so the state gradients run over the chunks in reverse, and each chunk's
+// gradients need only (S, dS'):
+//
+//   dP = tril(dO Delta^T), dQK = dP o G, dW = -dDelta S
+//   dQ = diag(e^g) dO S + dQK K
+//   dV = diag(beta) T^T dDelta
+//   dT = dDelta (beta V)^T + dW (beta e^g K)^T,  dA = -strict(T^T dT T^T)
+//   dK = dQK^T Q + diag(e^{g_n - g}) Delta dS' + diag(beta e^g) T^T dW
+//        + dG K + dG^T K,  dG = dA o beta_r G
+//   dbeta, dg: row sums of the same products; dlog_alpha = reverse
+//   cumulative sum of dg within the chunk.
+//
+// Five launches, all fp32 arithmetic on v_mfma_f32_16x16x4_f32 (inputs are
+// exact in fp32, so no operand splitting is needed):
+//   1. prep     (one workgroup per chunk and head): T and P;
+//   2. states   (one per sequence, head and 64-column d_v slice, chunks in
+//               order): the state entering every chunk and Delta;
+//   3. dstates  (same grid, chunks in reverse): dS' of every chunk, dDelta,
+//               and dS0;
+//   4. sprod    (per chunk and head): dO S, -dDelta S, Delta dS', <dS', S>;
+//   5. grads    (per chunk and head): dq, dk, dv, dlog_alpha, dbeta.
+// Intermediates go through the caller's workspace (layout in bwd_ws_bytes).
+//
+// fp32 MFMA layout (v_mfma_f32_16x16x4_f32): lane l supplies A[l & 15][l >> 4]
+// and B[l >> 4][l & 15] and holds D[4 (l >> 4) + j][l & 15], j = 0..3.
+#include "gdn_common.h"
+
+namespace gdn {
+namespace {
+
+constexpr int BC = 64;         // chunk length
+constexpr int LDN = BC + 4;    // row stride (floats) of 64 x 64 fp32 LDS matrices
+
+// Row stride (elements) of a 64 x D LDS matrix of type X: 4 floats or 8
+// bf16 of padding put consecutive rows 4 banks apart.
+template <typename X, int D> constexpr int ldx() { return sizeof(X) == 2 ? D + 8 : D + 4; }
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// acc += sum_{k < K} A(i, k) B(k, j) on one 16 x 16 tile, with
+// A(i, k) = A[i * ar + k * ak] and B(k, j) = B[k * bk + j * bj] (pointers at
+// the tile's origin, any layout).  Lane (i = l & 15, q = l >> 4) ends with
+// rows 4q..4q+3 of column i.
+template <int K, typename TA, typename TB>
+__device__ __forceinline__ f32x4 mm(const TA *A, int ar, int ak, const TB *B, int bk, int bj,
+                                    f32x4 acc, int lane) {
+    const int i = lane & 15, q = lane >> 4;
+    const TA *pa = A + i * ar + q * ak;
+    const TB *pb = B + q * bk + i * bj;
+#pragma unroll 8
+    for (int k = 0; k < K; k += 4) acc = mfma_f32(to_f32(pa[k * ak]), to_f32(pb[k * bk]), acc);
+    return acc;
+}
+
+__device__ __forceinline__ float sum16(float x) {   // over the 16 lanes of a row group
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    return x;
+}
+
+template <typename X> __device__ __forceinline__ X cvt(float x);
+template <> __device__ __forceinline__ float cvt<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 cvt<bf16>(float x) { return (bf16)x; }
+
+// --- chunk geometry -------------------------------------------------------
+// Chunk slots: a dense batch has NC = ceil(T / 64) slots per sequence,
+// sequence u starting at slot u NC; packed sequences start at slot
+// floor(cu[u] / 64) + u, which leaves room for every sequence's
+// ceil(L / 64) chunks (slots between sequences stay unused).
+__device__ __forceinline__ int unit_base(int u, int NC, int varlen, const int32_t *cu) {
+    return varlen ? cu[u] / BC + u : u * NC;
+}
+
+__device__ __forceinline__ void unit_span(int u, int T, int varlen, const int32_t *cu,
+                                          long &start, long &L) {
+    if (varlen) {
+        start = cu[u];
+        L = (long)cu[u + 1] - cu[u];
+    } else {
+        start = (long)u * T;
+        L = T;
+    }
+}
+
+// Slot -> (first token, valid rows); false for an unused slot.
+__device__ __forceinline__ bool slot_chunk(int slot, int units, int T, int NC, int varlen,
+                                           const int32_t *cu, long &row0, int &n) {
+    if (!varlen) {
+        const int u = slot / NC, c = slot % NC;
+        if (u >= units) return false;
+        row0 = (long)u * T + (long)c * BC;
+        n = min(BC, T - c * BC);
+        return true;
+    }
+    int lo = 0, hi = units - 1;   // largest u with base(u) <= slot (base(0) = 0)
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] / BC + mid <= slot) lo = mid;
+        else hi = mid - 1;
+    }
+    const int c = slot - (cu[lo] / BC + lo);
+    const long L = (long)cu[lo + 1] - cu[lo];
+    if ((long)c * BC >= L) return false;
+    row0 = cu[lo] + (long)c * BC;
+    n = (int)min((long)BC, L - (long)c * BC);
+    return true;
+}
+
+// Gates of one chunk, by one wave: sg[0] = g (chunk-local prefix of log
+// alpha; padded tokens add 0), sg[1] = e^g, sg[2] = beta (0 when padded),
+// sg[3] = e^{g_n - g} with g_n the prefix at the last valid token.
+__device__ __forceinline__ void chunk_gates(float (*sg)[BC], const float *la, const float *beta,
+                                            long row0, int n, int H, int h, int lane) {
+    float x = 0.f, b = 0.f;
+    if (lane < n) {
+        const size_t idx = (size_t)(row0 + lane) * H + h;
+        x = la[idx];
+        b = beta[idx];
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    const float gn = __shfl(x, 63);
+    sg[0][lane] = x;
+    sg[1][lane] = expf(x);
+    sg[2][lane] = b;
+    sg[3][lane] = expf(gn - x);
+}
+
+// Rows [row0, row0 + n) of a [tokens, H, D] tensor into a 64-row LDS matrix
+// (row stride ld); rows n..63 are zero.
+template <int D, typename TS, typename TG>
+__device__ __forceinline__ void load_rows(TS *dst, int ld, const TG *src, long row0, int n, int H,
+                                          int h, int col0, int width, int tid, int nthr) {
+    for (int e = tid; e < BC * width; e += nthr) {
+        const int r = e / width, d = e % width;
+        float x = 0.f;
+        if (r < n) x = to_f32(src[((size_t)(row0 + r) * H + h) * D + col0 + d]);
+        dst[r * ld + d] = cvt<TS>(x);
+    }
+}
+// Rows of a [64, D] workspace block (rows >= n are zero).
+template <int D>
+__device__ __forceinline__ void load_ws_rows(float *dst, int ld, const float *src, int n, int tid,
+                                             int nthr) {
+    for (int e = tid; e < BC * D; e += nthr) {
+        const int r = e / D, d = e % D;
+        dst[r * ld + d] = r < n ? src[(size_t)r * D + d] : 0.f;
+    }
+}
+__device__ __forceinline__ void load_nn(float *dst, const float *src, int tid, int nthr) {
+    for (int e = tid; e < BC * BC; e += nthr) dst[(e >> 6) * LDN + (e & 63)] = src[e];
+}
+
+// ---------------------------------------------------------------- 1. prep
+template <int D, typename TI>
+__global__ __launch_bounds__(512) void bwd_prep_kernel(
+    int T, int H, int units, int NC, int varlen, const int32_t *__restrict__ cu,
+    const TI *__restrict__ q, const TI *__restrict__ k, const float *__restrict__ la,
+    const float *__restrict__ beta, float *__restrict__ wsT, float *__restrict__ wsP) {
+    constexpr int LI = ldx<TI, D>();
+    __shared__ __attribute__((aligned(16))) TI sK[BC * LI];
+    __shared__ __attribute__((aligned(16))) TI sQ[BC * LI];
+    __shared__ __attribute__((aligned(16))) float sA[BC * LDN];
+    __shared__ __attribute__((aligned(16))) float sX[BC * LDN];
+    __shared__ float sg[4][BC];
+    const int slot = blockIdx.x / H, h = blockIdx.x % H;
+    long row0;
+    int n;
+    if (!slot_chunk(slot, units, T, NC, varlen, cu, row0, n)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const size_t ch = blockIdx.x;
+    load_rows<D>(sK, LI, k, row0, n, H, h, 0, D, tid, 512);
+    load_rows<D>(sQ, LI, q, row0, n, H, h, 0, D, tid, 512);
+    if (wave == 0) chunk_gates(sg, la, beta, row0, n, H, h, lane);
+    __syncthreads();
+    // waves 0-3: rows 16w.. of K K^T -> A; waves 4-7: the same rows of Q K^T -> P
+    {
+        const int tr = wave & 3;
+        const bool isP = wave >= 4;
+        const TI *Ar = (isP ? sQ : sK) + 16 * tr * LI;
+        float *P = wsP + ch * BC * BC;
+        for (int tj = 0; tj < 4; ++tj) {
+            f32x4 acc = zero4();
+            if (tj <= tr) acc = mm<D>(Ar, LI, 1, sK + 16 * tj * LI, 1, LI, acc, lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * tr + 4 * (lane >> 4) + j, i = 16 * tj + (lane & 15);
+                const float dec = i <= r ? __expf(sg[0][r] - sg[0][i]) : 0.f;
+                if (isP) P[r * BC + i] = dec * acc[j];
+                else sA[r * LDN + i] = i < r ? sg[2][r] * dec * acc[j] : 0.f;
+            }
+        }
+    }
+    __syncthreads();
+    // T = (I + A)^{-1} by forward substitution, X[r][j] = [r == j] - sum_{i<r}
+    // A[r][i] X[i][j]: column j on 4 lanes of waves 0-3 (lane part p sums
+    // i = p mod 4), the rows found so far kept in LDS.  The lanes of a
+    // column are in one wave, whose LDS accesses complete in order, so the
+    // row written by part 0 is seen by the other parts' later reads (the
+    // wave barrier keeps the compiler from moving them across).
+    if (tid < 256) {
+        const int j = tid >> 2, p = tid & 3;
+        float *Tm = wsT + ch * BC * BC;
+        for (int r = 0; r < BC; ++r) {
+            float s = 0.f;
+            for (int i = p; i < r; i += 4) s += sA[r * LDN + i] * sX[i * LDN + j];
+            s += __shfl_xor(s, 1);
+            s += __shfl_xor(s, 2);
+            const float x = r == j ? 1.f : -s;
+            if (p == 0) {
+                sX[r * LDN + j] = x;
+                Tm[r * BC + j] = x;
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
+// ---------------------------------------------------------------- 2. states
+template <int D, typename TI>
+__global__ __launch_bounds__(512) void bwd_states_kernel(
+    int T, int H, int NC, int varlen, const int32_t *__restrict__ cu,
+    const TI *__restrict__ k, const TI *__restrict__ v, const float *__restrict__ la,
+    const float *__restrict__ beta, const float *__restrict__ S0, const float *__restrict__ wsT,
+    float *__restrict__ wsH, float *__restrict__ wsDl) {
+    constexpr int LI = ldx<TI, D>(), LF = D + 4, NTC = D / 32, NSL = D / 64;
+    __shared__ __attribute__((aligned(16))) TI sK[BC * LI];
+    __shared__ __attribute__((aligned(16))) float sS[BC * LF];   // state slice: d_v rows x d_k
+    __shared__ __attribute__((aligned(16))) float sT[BC * LDN];
+    __shared__ __attribute__((aligned(16))) float sZ[BC * LDN];
+    __shared__ __attribute__((aligned(16))) float sD[BC * LDN];
+    __shared__ float sg[4][BC];
+    const int uh = blockIdx.x / NSL, dv0 = 64 * (blockIdx.x % NSL);
+    const int H_ = H, u = uh / H_, h = uh % H_;
+    long start, L;
+    unit_span(u, T, varlen, cu, start, L);
+    const int N = (int)((L + BC - 1) / BC);
+    const int base = unit_base(u, NC, varlen, cu);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lq = lane >> 4;
+    const int tr = wave & 3, tc0 = (wave >> 2) * NTC;
+    f32x4 st[NTC];   // st[t][j] = S[dv0 + 16 tr + 4 lq + j][16 (tc0 + t) + li]
+#pragma unroll
+    for (int t = 0; t < NTC; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
+            st[t][j] = S0 ? S0[((size_t)uh * D + dv0 + row) * D + col] : 0.f;
+        }
+    for (int c = 0; c < N; ++c) {
+        const size_t ch = (size_t)(base + c) * H + h;
+        const long row0 = start + (long)c * BC;
+        const int n = (int)min((long)BC, L - (long)c * BC);
+        float *Hm = wsH + ch * D * D;
+#pragma unroll
+        for (int t = 0; t < NTC; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
+                sS[row * LF + col] = st[t][j];
+                Hm[(size_t)(dv0 + row) * D + col] = st[t][j];
+            }
+        load_rows<D>(sK, LI, k, row0, n, H, h, 0, D, tid, 512);
+        load_nn(sT, wsT + ch * BC * BC, tid, 512);
+        if (wave == 0) chunk_gates(sg, la, beta, row0, n, H, h, lane);
+        __syncthreads();
+        // Z = diag(beta) (V - diag(e^g) K S^T), 64 tokens x 64 slice columns
+        for (int x = 0; x < 2; ++x) {
+            const int ty = tr, tx = 2 * (wave >> 2) + x;
+            const f32x4 y = mm<D>(sK + 16 * ty * LI, LI, 1, sS + 16 * tx * LF, 1, LF, zero4(), lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * ty + 4 * lq + j, col = 16 * tx + li;
+                const float vv =
+                    r < n ? to_f32(v[((size_t)(row0 + r) * H + h) * D + dv0 + col]) : 0.f;
+                sZ[r * LDN + col] = sg[2][r] * (vv - sg[1][r] * y[j]);
+            }
+        }
+        __syncthreads();
+        // Delta = T Z; the state update uses diag(e^{g_n - g}) Delta
+        for (int x = 0; x < 2; ++x) {
+            const int ty = tr, tx = 2 * (wave >> 2) + x;
+            const f32x4 d = mm<BC>(sT + 16 * ty * LDN, LDN, 1, sZ + 16 * tx, LDN, 1, zero4(), lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * ty + 4 * lq + j, col = 16 * tx + li;
+                sD[r * LDN + col] = d[j] * sg[3][r];
+                if (r < n) wsDl[(ch * BC + r) * D + dv0 + col] = d[j];
+            }
+        }
+        __syncthreads();
+        // S <- e^{g_n} S + (diag(e^{g_n - g}) Delta)^T K
+        const float egn = sg[1][BC - 1];
+#pragma unroll
+        for (int t = 0; t < NTC; ++t) {
+            st[t] = st[t] * egn;
+            st[t] = mm<BC>(sD + 16 * tr, 1, LDN, sK + 16 * (tc0 + t), LI, 1, st[t], lane);
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------- 3. dstates
+template <int D, typename TI, typename TG>
+__global__ __launch_bounds__(512) void bwd_dstates_kernel(
+    int T, int H, int NC, int varlen, const int32_t *__restrict__ cu,
+    const TI *__restrict__ q, const TI *__restrict__ k, const TG *__restrict__ dO,
+    const float *__restrict__ la, const float *__restrict__ beta, const float *__restrict__ dST,
+    const float *__restrict__ wsT, const float *__restrict__ wsP, float *__restrict__ wsDH,
+    float *__restrict__ wsE, float *__restrict__ dS0) {
+    constexpr int LI = ldx<TI, D>(), LF = D + 4, NTC = D / 32, NSL = D / 64;
+    __shared__ __attribute__((aligned(16))) TI sK[BC * LI];
+    __shared__ __attribute__((aligned(16))) TI sQ[BC * LI];
+    __shared__ __attribute__((aligned(16))) float sG[BC * LF];   // dS' slice: d_v rows x d_k
+    __shared__ __attribute__((aligned(16))) float sP[BC * LDN];  // P, then F
+    __shared__ __attribute__((aligned(16))) float sT[BC * LDN];
+    __shared__ __attribute__((aligned(16))) float sO[BC * LDN];  // dO slice, then e^g dO
+    __shared__ __attribute__((aligned(16))) float sE[BC * LDN];
+    __shared__ float sg[4][BC];
+    const int uh = blockIdx.x / NSL, dv0 = 64 * (blockIdx.x % NSL);
+    const int u = uh / H, h = uh % H;
+    long start, L;
+    unit_span(u, T, varlen, cu, start, L);
+    const int N = (int)((L + BC - 1) / BC);
+    const int base = unit_base(u, NC, varlen, cu);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lq = lane >> 4;
+    const int tr = wave & 3, tc0 = (wave >> 2) * NTC;
+    f32x4 st[NTC];   // st[t][j] = dS'[dv0 + 16 tr + 4 lq + j][16 (tc0 + t) + li]
+#pragma unroll
+    for (int t = 0; t < NTC; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
+            st[t][j] = dST ? dST[((size_t)uh * D + dv0 + row) * D + col] : 0.f;
+        }
+    for (int c = N - 1; c >= 0; --c) {
+        const size_t ch = (size_t)(base + c) * H + h;
+        const long row0 = start + (long)c * BC;
+        const int n = (int)min((long)BC, L - (long)c * BC);
+        float *DHm = wsDH + ch * D * D;
+#pragma unroll
+        for (int t = 0; t < NTC; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
+                sG[row * LF + col] = st[t][j];
+                DHm[(size_t)(dv0 + row) * D + col] = st[t][j];
+            }
+        load_rows<D>(sK, LI, k, row0, n, H, h, 0, D, tid, 512);
+        load_rows<D>(sQ, LI, q, row0, n, H, h, 0, D, tid, 512);
+        load_rows<D>(sO, LDN, dO, row0, n, H, h, dv0, 64, tid, 512);
+        load_nn(sP, wsP + ch * BC * BC, tid, 512);
+        load_nn(sT, wsT + ch * BC * BC, tid, 512);
+        if (wave == 0) chunk_gates(sg, la, beta, row0, n, H, h, lane);
+        __syncthreads();
+        // dDelta = P^T dO + diag(e^{g_n - g}) K dS'^T
+        for (int x = 0; x < 2; ++x) {
+            const int ty = tr, tx = 2 * (wave >> 2) + x;
+            const f32x4 e1 = mm<BC>(sP + 16 * ty, 1, LDN, sO + 16 * tx, LDN, 1, zero4(), lane);
+            const f32x4 e2 = mm<D>(sK + 16 * ty * LI, LI, 1, sG + 16 * tx * LF, 1, LF, zero4(), lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * ty + 4 * lq + j, col = 16 * tx + li;
+                const float e = e1[j] + sg[3][r] * e2[j];
+                sE[r * LDN + col] = e;
+                if (r < n) wsE[(ch * BC + r) * D + dv0 + col] = e;
+            }
+        }
+        __syncthreads();
+        // F = diag(beta e^g) T^T dDelta (into sP); dO rows scaled by e^g
+        for (int x = 0; x < 2; ++x) {
+            const int ty = tr, tx = 2 * (wave >> 2) + x;
+            const f32x4 f = mm<BC>(sT + 16 * ty, 1, LDN, sE + 16 * tx, LDN, 1, zero4(), lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * ty + 4 * lq + j, col = 16 * tx + li;
+                sP[r * LDN + col] = sg[2][r] * sg[1][r] * f[j];
+                sO[r * LDN + col] *= sg[1][r];
+            }
+        }
+        __syncthreads();
+        // dS <- e^{g_n} dS' + (e^g dO)^T Q - F^T K
+        const float egn = sg[1][BC - 1];
+#pragma unroll
+        for (int t = 0; t < NTC; ++t) {
+            st[t] = st[t] * egn;
+            st[t] = mm<BC>(sO + 16 * tr, 1, LDN, sQ + 16 * (tc0 + t), LI, 1, st[t], lane);
+            const f32x4 f = mm<BC>(sP + 16 * tr, 1, LDN, sK + 16 * (tc0 + t), LI, 1, zero4(), lane);
+            st[t] = st[t] - f;
+        }
+        __syncthreads();
+    }
+    if (dS0) {
+#pragma unroll
+        for (int t = 0; t < NTC; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
+                dS0[((size_t)uh * D + dv0 + row) * D + col] = st[t][j];
+            }
+    }
+}
+
+// ---------------------------------------------------------------- 4. sprod
+template <int D, typename TG>
+__global__ __launch_bounds__(512) void bwd_sprod_kernel(
+    int T, int H, int units, int NC, int varlen, const int32_t *__restrict__ cu,
+    const TG *__restrict__ dO, const float *__restrict__ wsH, const float *__restrict__ wsDH,
+    const float *__restrict__ wsDl, const float *__restrict__ wsE, float *__restrict__ wsOS,
+    float *__restrict__ wsW, float *__restrict__ wsKt, float *__restrict__ wsSc) {
+    constexpr int LF = D + 4, NTC = D / 32;
+    __shared__ __attribute__((aligned(16))) float sB[D * LF];    // S, then dS'
+    __shared__ __attribute__((aligned(16))) float sA1[BC * LF];  // dO, then Delta
+    __shared__ __attribute__((aligned(16))) float sA2[BC * LF];  // dDelta
+    __shared__ float sred[8];
+    const int slot = blockIdx.x / H, h = blockIdx.x % H;
+    long row0;
+    int n;
+    if (!slot_chunk(slot, units, T, NC, varlen, cu, row0, n)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lq = lane >> 4;
+    const int tr = wave & 3, tc0 = (wave >> 2) * NTC;
+    const size_t ch = blockIdx.x;
+    const float *Sm = wsH + ch * D * D, *DSm = wsDH + ch * D * D;
+    for (int e = tid; e < D * D; e += 512) sB[(e / D) * LF + e % D] = Sm[e];
+    load_rows<D>(sA1, LF, dO, row0, n, H, h, 0, D, tid, 512);
+    load_ws_rows<D>(sA2, LF, wsE + ch * BC * D, n, tid, 512);
+    __syncthreads();
+    // dO S and -dDelta S (64 x d_k)
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) {
+        const int tc = tc0 + t;
+        const f32x4 a = mm<D>(sA1 + 16 * tr * LF, LF, 1, sB + 16 * tc, LF, 1, zero4(), lane);
+        const f32x4 b = mm<D>(sA2 + 16 * tr * LF, LF, 1, sB + 16 * tc, LF, 1, zero4(), lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
+            if (r < n) {
+                wsOS[(ch * BC + r) * D + col] = a[j];
+                wsW[(ch * BC + r) * D + col] = -b[j];
+            }
+        }
+    }
+    __syncthreads();
+    // dS' replaces S; <dS', S> on the way
+    float dot = 0.f;
+    for (int e = tid; e < D * D; e += 512) {
+        const int at = (e / D) * LF + e % D;
+        const float x = DSm[e];
+        dot += x * sB[at];
+        sB[at] = x;
+    }
+    load_ws_rows<D>(sA1, LF, wsDl + ch * BC * D, n, tid, 512);
+    dot = sum16(dot);
+    dot += __shfl_xor(dot, 16);
+    dot += __shfl_xor(dot, 32);
+    if (lane == 0) sred[wave] = dot;
+    __syncthreads();
+    if (tid == 0) {
+        float s = 0.f;
+        for (int w = 0; w < 8; ++w) s += sred[w];
+        wsSc[ch] = s;
+    }
+    // Delta dS' (64 x d_k)
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) {
+        const int tc = tc0 + t;
+        const f32x4 a = mm<D>(sA1 + 16 * tr * LF, LF, 1, sB + 16 * tc, LF, 1, zero4(), lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
+            if (r < n) wsKt[(ch * BC + r) * D + col] = a[j];
+        }
+    }
+}
+
+// ---------------------------------------------------------------- 5. grads
+template <int D, typename TI, typename TG>
+__global__ __launch_bounds__(512) void bwd_grads_kernel(
+    int T, int H, int units, int NC, int varlen, const int32_t *__restrict__ cu,
+    const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v,
+    const TG *__restrict__ dO, const float *__restrict__ la, const float *__restrict__ beta,
+    const float *__restrict__ wsT, const float *__restrict__ wsP, const float *__restrict__ wsDl,
+    const float *__restrict__ wsE, const float *__restrict__ wsOS, const float *__restrict__ wsW,
+    const float *__restrict__ wsKt, const float *__restrict__ wsSc, TG *__restrict__ dq,
+    TG *__restrict__ dk, TG *__restrict__ dv, float *__restrict__ dla,
+    float *__restrict__ dbeta) {
+    constexpr int LI = ldx<TI, D>(), LF = D + 4, NTC = D / 32;
+    __shared__ __attribute__((aligned(16))) TI sK[BC * LI];
+    __shared__ __attribute__((aligned(16))) TI sQ[BC * LI];
+    __shared__ __attribute__((aligned(16))) float sT[BC * LDN];
+    __shared__ __attribute__((aligned(16))) float sP[BC * LDN];   // P, then T^T dT
+    __shared__ __attribute__((aligned(16))) float sN[BC * LDN];   // dQK = dP o G
+    __shared__ __attribute__((aligned(16))) float sX[BC * LF];    // dO, V, dT
+    __shared__ __attribute__((aligned(16))) float sY[BC * LF];    // Delta, dDelta, dW, dG
+    __shared__ float sg[4][BC];
+    // per-wave partial row sums of dbeta and dg, added in a fixed order at the
+    // end (no atomics: the result does not depend on wave timing)
+    __shared__ float sdb[8][BC], sdg[8][BC];
+    const int slot = blockIdx.x / H, h = blockIdx.x % H;
+    long row0;
+    int n;
+    if (!slot_chunk(slot, units, T, NC, varlen, cu, row0, n)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lq = lane >> 4;
+    const int tr = wave & 3, tc0 = (wave >> 2) * NTC;   // 64 x D tiles: row tr, columns tc0..
+    const int ty = wave & 3, tx0 = 2 * (wave >> 2);     // 64 x 64 tiles: row ty, columns tx0, tx0+1
+    const size_t ch = blockIdx.x;
+    // one wave's contribution: distinct rows per lane within an instruction
+#define ADDG(row, x) (sdg[wave][(row)] += (x))
+#define ADDB(row, x) (sdb[wave][(row)] += (x))
+    for (int e = tid; e < 8 * BC; e += 512) {
+        sdb[e / BC][e % BC] = 0.f;
+        sdg[e / BC][e % BC] = 0.f;
+    }
+    load_rows<D>(sK, LI, k, row0, n, H, h, 0, D, tid, 512);
+    load_rows<D>(sQ, LI, q, row0, n, H, h, 0, D, tid, 512);
+    load_nn(sT, wsT + ch * BC * BC, tid, 512);
+    load_nn(sP, wsP + ch * BC * BC, tid, 512);
+    load_rows<D>(sX, LF, dO, row0, n, H, h, 0, D, tid, 512);
+    load_ws_rows<D>(sY, LF, wsDl + ch * BC * D, n, tid, 512);
+    if (wave == 0) chunk_gates(sg, la, beta, row0, n, H, h, lane);
+    __syncthreads();
+
+    // dP = tril(dO Delta^T); dQK = dP o G; dg += rowsum(dP o P) - colsum(dP o P)
+    f32x4 dqk[2];
+    for (int x = 0; x < 2; ++x) {
+        const int tx = tx0 + x;
+        const f32x4 a = mm<D>(sX + 16 * ty * LF, LF, 1, sY + 16 * tx * LF, 1, LF, zero4(), lane);
+        float col = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * ty + 4 * lq + j, i = 16 * tx + li;
+            const float dp = i <= r ? a[j] : 0.f;
+            const float gm = i <= r ? __expf(sg[0][r] - sg[0][i]) : 0.f;
+            dqk[x][j] = dp * gm;
+            const float m = dp * sP[r * LDN + i];
+            const float rs = sum16(m);
+            if (li == 0) ADDG(r, rs);
+            col += m;
+        }
+        col += __shfl_xor(col, 16);
+        col += __shfl_xor(col, 32);
+        if (lq == 0) ADDG(16 * tx + li, -col);
+    }
+    __syncthreads();
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            sN[(16 * ty + 4 * lq + j) * LDN + 16 * (tx0 + x) + li] = dqk[x][j];
+    load_ws_rows<D>(sY, LF, wsE + ch * BC * D, n, tid, 512);
+    load_rows<D>(sX, LF, v, row0, n, H, h, 0, D, tid, 512);
+    __syncthreads();
+
+    // dT = dDelta (beta V)^T + ...; dV = diag(beta) T^T dDelta; dbeta += rows(T^T dDelta . V)
+    f32x4 dt[2];
+    for (int x = 0; x < 2; ++x) {
+        const int tx = tx0 + x;
+        const f32x4 a = mm<D>(sY + 16 * ty * LF, LF, 1, sX + 16 * tx * LF, 1, LF, zero4(), lane);
+        const float bi = sg[2][16 * tx + li];
+        dt[x] = a * bi;
+    }
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) {
+        const int tc = tc0 + t;
+        const f32x4 a = mm<BC>(sT + 16 * tr, 1, LDN, sY + 16 * tc, LF, 1, zero4(), lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
+            if (r < n) dv[((size_t)(row0 + r) * H + h) * D + col] = cvt<TG>(sg[2][r] * a[j]);
+            const float rs = sum16(a[j] * sX[r * LF + col]);
+            if (li == 0) ADDB(r, rs);
+        }
+    }
+    __syncthreads();
+    load_ws_rows<D>(sY, LF, wsW + ch * BC * D, n, tid, 512);
+    __syncthreads();
+
+    // dT += dW (beta e^g K)^T; dK = diag(beta e^g) T^T dW + ...
+    for (int x = 0; x < 2; ++x) {
+        const int tx = tx0 + x;
+        const f32x4 a = mm<D>(sY + 16 * ty * LF, LF, 1, sK + 16 * tx * LI, 1, LI, zero4(), lane);
+        const int i = 16 * tx + li;
+        dt[x] = dt[x] + a * (sg[2][i] * sg[1][i]);
+    }
+    f32x4 dka[NTC];
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) {
+        const int tc = tc0 + t;
+        const f32x4 a = mm<BC>(sT + 16 * tr, 1, LDN, sY + 16 * tc, LF, 1, zero4(), lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
+            const float be = sg[2][r] * sg[1][r];
+            dka[t][j] = be * a[j];
+            const float rw = sum16(a[j] * to_f32(sK[r * LI + col]));
+            if (li == 0) {
+                ADDB(r, sg[1][r] * rw);
+                ADDG(r, be * rw);
+            }
+        }
+    }
+    __syncthreads();
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            sX[(16 * ty + 4 * lq + j) * LDN + 16 * (tx0 + x) + li] = dt[x][j];
+    __syncthreads();
+    // M = T^T dT (into sP)
+    for (int x = 0; x < 2; ++x) {
+        const int tx = tx0 + x;
+        const f32x4 a = mm<BC>(sT + 16 * ty, 1, LDN, sX + 16 * tx, LDN, 1, zero4(), lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sP[(16 * ty + 4 * lq + j) * LDN + 16 * tx + li] = a[j];
+    }
+    __syncthreads();
+    // dA = -strict(M T^T); dG = dA o beta_r G (into sY);
+    // dbeta += rowsum(dA o G o K K^T); dg += rowsum(dA o A) - colsum(dA o A)
+    for (int x = 0; x < 2; ++x) {
+        const int tx = tx0 + x;
+        const f32x4 a = mm<BC>(sP + 16 * ty * LDN, LDN, 1, sT + 16 * tx * LDN, 1, LDN, zero4(), lane);
+        const f32x4 kk = mm<D>(sK + 16 * ty * LI, LI, 1, sK + 16 * tx * LI, 1, LI, zero4(), lane);
+        float col = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * ty + 4 * lq + j, i = 16 * tx + li;
+            const float gm = i < r ? __expf(sg[0][r] - sg[0][i]) : 0.f;
+            const float da = i < r ? -a[j] : 0.f;
+            const float br = sg[2][r];
+            sY[r * LDN + i] = da * br * gm;
+            const float t1 = da * gm * kk[j];
+            const float rb = sum16(t1);
+            const float m = br * t1;   // dA o A
+            const float rg = sum16(m);
+            if (li == 0) {
+                ADDB(r, rb);
+                ADDG(r, rg);
+            }
+            col += m;
+        }
+        col += __shfl_xor(col, 16);
+        col += __shfl_xor(col, 32);
+        if (lq == 0) ADDG(16 * tx + li, -col);
+    }
+    __syncthreads();
+
+    // dQ = diag(e^g) dO S + dQK K;  dg += e^g rows(dO S . Q)
+    const float *OS = wsOS + ch * BC * D, *Kt = wsKt + ch * BC * D;
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) {
+        const int tc = tc0 + t;
+        f32x4 acc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
+            const float os = r < n ? OS[(size_t)r * D + col] : 0.f;
+            acc[j] = sg[1][r] * os;
+            const float rg = sum16(acc[j] * to_f32(sQ[r * LI + col]));
+            if (li == 0) ADDG(r, rg);
+        }
+        acc = mm<BC>(sN + 16 * tr * LDN, LDN, 1, sK + 16 * tc, LI, 1, acc, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
+            if (r < n) dq[((size_t)(row0 + r) * H + h) * D + col] = cvt<TG>(acc[j]);
+        }
+    }
+    // dK = dQK^T Q + diag(e^{g_n - g}) Delta dS' + diag(beta e^g) T^T dW + dG K + dG^T K
+    // dg -= s_r, dg_{n-1} += sum_r s_r with s = rows(Delta dS' . K~)
+    float ssum = 0.f;
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) {
+        const int tc = tc0 + t;
+        f32x4 acc = dka[t];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
+            const float kt = r < n ? sg[3][r] * Kt[(size_t)r * D + col] : 0.f;
+            acc[j] += kt;
+            const float s = sum16(kt * to_f32(sK[r * LI + col]));
+            if (li == 0) ADDG(r, -s);
+            ssum += s;   // the same in all 16 lanes of the group
+        }
+        acc = mm<BC>(sN + 16 * tr, 1, LDN, sQ + 16 * tc, LI, 1, acc, lane);
+        acc = mm<BC>(sY + 16 * tr * LDN, LDN, 1, sK + 16 * tc, LI, 1, acc, lane);
+        acc = mm<BC>(sY + 16 * tr, 1, LDN, sK + 16 * tc, LI, 1, acc, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
+            if (r < n) dk[((size_t)(row0 + r) * H + h) * D + col] = cvt<TG>(acc[j]);
+        }
+    }
+    ssum += __shfl_xor(ssum, 16);
+    ssum += __shfl_xor(ssum, 32);
+    if (lane == 0 && n > 0) ADDG(n - 1, ssum);
+#undef ADDG
+#undef ADDB
+    __syncthreads();
+    // dg_{n-1} += e^{g_n} <dS', S>; dlog_alpha = reverse cumulative sum of dg
+    if (wave == 0) {
+        float x = 0.f, db = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            x += sdg[w][lane];
+            db += sdb[w][lane];
+        }
+        if (lane >= n) x = 0.f;
+        if (lane == n - 1) x += sg[1][BC - 1] * wsSc[ch];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_down(x, off);
+            if (lane + off < 64) x += y;
+        }
+        if (lane < n) {
+            const size_t idx = (size_t)(row0 + lane) * H + h;
+            dla[idx] = x;
+            dbeta[idx] = db;
+        }
+    }
+}
+
+template <int D, typename TI, typename TG>
+hipError_t launch_bwd_t(int units, int T, int H, const int32_t *cu, const void *q, const void *k,
+                        const void *v, const float *la, const float *beta, const float *S0,
+                        const void *dO, const float *dST, void *dq, void *dk, void *dv,
+                        float *dla, float *dbeta, float *dS0, float *ws, long nslots,
+                        hipStream_t st) {
+    const int varlen = cu != nullptr;
+    const int NC = varlen ? 0 : (T + BC - 1) / BC;
+    const size_t nch = (size_t)nslots * H;
+    float *wsT = ws;
+    float *wsP = wsT + nch * BC * BC;
+    float *wsH = wsP + nch * BC * BC;
+    float *wsDH = wsH + nch * D * D;
+    float *wsDl = wsDH + nch * D * D;
+    float *wsE = wsDl + nch * BC * D;
+    float *wsOS = wsE + nch * BC * D;
+    float *wsW = wsOS + nch * BC * D;
+    float *wsKt = wsW + nch * BC * D;
+    float *wsSc = wsKt + nch * BC * D;
+    const TI *qi = (const TI *)q, *ki = (const TI *)k, *vi = (const TI *)v;
+    const TG *dOg = (const TG *)dO;
+    const unsigned seq_grid = (unsigned)((long)units * H * (D / 64));
+    if (nch > 0)
+        hipLaunchKernelGGL((bwd_prep_kernel<D, TI>), dim3((unsigned)nch), dim3(512), 0, st, T, H,
+                           units, NC, varlen, cu, qi, ki, la, beta, wsT, wsP);
+    if (nch > 0)
+        hipLaunchKernelGGL((bwd_states_kernel<D, TI>), dim3(seq_grid), dim3(512), 0, st, T, H, NC,
+                           varlen, cu, ki, vi, la, beta, S0, wsT, wsH, wsDl);
+    hipLaunchKernelGGL((bwd_dstates_kernel<D, TI, TG>), dim3(seq_grid), dim3(512), 0, st, T, H,
+                       NC, varlen, cu, qi, ki, dOg, la, beta, dST, wsT, wsP, wsDH, wsE, dS0);
+    if (nch > 0) {
+        hipLaunchKernelGGL((bwd_sprod_kernel<D, TG>), dim3((unsigned)nch), dim3(512), 0, st, T, H,
+                           units, NC, varlen, cu, dOg, wsH, wsDH, wsDl, wsE, wsOS, wsW, wsKt, wsSc);
+        hipLaunchKernelGGL((bwd_grads_kernel<D, TI, TG>), dim3((unsigned)nch), dim3(512), 0, st, T,
+                           H, units, NC, varlen, cu, qi, ki, vi, dOg, la, beta, wsT, wsP, wsDl, wsE,
+                           wsOS, wsW, wsKt, wsSc, (TG *)dq, (TG *)dk, (TG *)dv, dla, dbeta);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool chunk_bwd_supported(int dk, int dv, int chunk, bool io_bf16) {
+    if (chunk != BC || dk != dv) return false;
+    return io_bf16 ? (dk == 64 || dk == 128) : dk == 64;
+}
+
+// Chunk slots of the workspace: units * ceil(T / 64) for a dense batch,
+// floor(T / 64) + n_seqs + 1 for packed sequences.
+long chunk_bwd_slots(int units, int T, bool varlen) {
+    return varlen ? (long)T / BC + units + 1 : (long)units * ((T + BC - 1) / BC);
+}
+
+size_t chunk_bwd_ws_bytes(int units, int T, int H, int d, bool varlen) {
+    const size_t nch = (size_t)chunk_bwd_slots(units, T, varlen) * H;
+    return sizeof(float) * nch *
+           (2 * (size_t)BC * BC + 2 * (size_t)d * d + 5 * (size_t)BC * d + 1);
+}
+
+hipError_t launch_chunk_bwd(int units, int T, int H, int d, bool io_bf16, bool g_bf16,
+                            const int32_t *cu, const void *q, const void *k, const void *v,
+                            const float *la, const float *beta, const float *S0,
+                            const void *dO, const float *dST, void *dq, void *dk, void *dv,
+                            float *dla, float *dbeta, float *dS0, void *ws, hipStream_t st) {
+    const long nslots = chunk_bwd_slots(units, T, cu != nullptr);
+    float *w = (float *)ws;
+#define GDN_BWD(DV, TI, TG)                                                                   \
+    return launch_bwd_t<DV, TI, TG>(units, T, H, cu, q, k, v, la, beta, S0, dO, dST, dq, dk, \
+                                    dv, dla, dbeta, dS0, w, nslots, st)
+    if (io_bf16) {
+        if (d == 128) { if (g_bf16) GDN_BWD(128, bf16, bf16); GDN_BWD(128, bf16, float); }
+        if (d == 64) { if (g_bf16) GDN_BWD(64, bf16, bf16); GDN_BWD(64, bf16, float); }
+    } else if (d == 64) {
+        if (g_bf16) GDN_BWD(64, float, bf16);
+        GDN_BWD(64, float, float);
+    }
+#undef GDN_BWD
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

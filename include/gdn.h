@@ -129,6 +129,44 @@ int gdn_chunk_fwd(const gdn_shape *shape,
                   void *workspace, size_t workspace_bytes,
                   void *stream);
 
+/* Bytes of device workspace gdn_chunk_bwd needs for `shape` (written to
+ * *bytes): per chunk of 64 tokens and head, fp32 copies of T and P, the
+ * state entering the chunk and its gradient, and five 64 x d intermediates
+ * -- about (2 d^2 + 5 * 64 d + 2 * 64^2) * 4 bytes (288 KiB at d = 128).
+ * Returns a gdn_status (the backward's own supported set, see below). */
+int gdn_chunk_bwd_workspace_size(const gdn_shape *shape, size_t *bytes);
+
+/* Backward pass of gdn_chunk_fwd: the gradients of
+ *     L = sum_t <dO_t, o_t> + sum_units <dS_T, S_T>
+ * with respect to q, k, v, log_alpha, beta and S0, for the same shape and
+ * inputs.  The pages name a gate-aware backward pass for the chunkwise
+ * algorithm ("Gated DeltaNet-2: Decoupling Erase and Write in Linear
+ * Attention", abstract) but print none; the gradient is the one of the
+ * forward defined above, computed chunkwise (state gradients in reverse
+ * chunk order, each chunk's gradients from the state entering it and the
+ * gradient of the state leaving it) in fp32.
+ *
+ *   q, k, v, log_alpha, beta, S0, cu_seqlens   as in gdn_chunk_fwd
+ *   dO          [B, T, H, d_v]  o_dtype, gradient of o
+ *   dS_T        [U, H, d_v, d_k] fp32 gradient of the final states; NULL = 0
+ *   dq, dk      [B, T, H, d_k]  o_dtype outputs
+ *   dv          [B, T, H, d_v]  o_dtype output
+ *   dlog_alpha, dbeta [B, T, H] fp32 outputs
+ *   dS0         [U, H, d_v, d_k] fp32 output; NULL = not written
+ *   workspace   device buffer of at least gdn_chunk_bwd_workspace_size bytes
+ * No output may alias an input.  Supported: chunk 64, prologue 0, d_k = d_v
+ * in {64, 128} with bf16 inputs or d_k = d_v = 64 with fp32 inputs.
+ * Returns a gdn_status. */
+int gdn_chunk_bwd(const gdn_shape *shape,
+                  const void *q, const void *k, const void *v,
+                  const float *log_alpha, const float *beta,
+                  const float *S0, const int32_t *cu_seqlens,
+                  const void *dO, const float *dS_T,
+                  void *dq, void *dk, void *dv,
+                  float *dlog_alpha, float *dbeta, float *dS0,
+                  void *workspace, size_t workspace_bytes,
+                  void *stream);
+
 /* One recurrent decode step of the same rule for every (b, h): reads one
  * token, updates the state in place and returns the read-out -- the
  * constant-memory decoding of "Gated DeltaNet-2: Decoupling Erase and Write

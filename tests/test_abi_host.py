@@ -138,3 +138,46 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         B.lib()
+
+
+def bws(s):
+    out = ctypes.c_size_t(123)
+    rc = B.lib().gdn_chunk_bwd_workspace_size(ctypes.byref(s), ctypes.byref(out))
+    return rc, out.value
+
+
+def bwd(s, ws=P, wsb=1 << 40, **kw):
+    a = dict(q=P, k=P, v=P, la=P, be=P, S0=None, cu=None, dO=P, dST=None, dq=P2, dk=P2, dv=P2,
+             dla=P2, dbe=P2, dS0=None)
+    a.update(kw)
+    return B.lib().gdn_chunk_bwd(ctypes.byref(s), a["q"], a["k"], a["v"], a["la"], a["be"],
+                                 a["S0"], a["cu"], a["dO"], a["dST"], a["dq"], a["dk"], a["dv"],
+                                 a["dla"], a["dbe"], a["dS0"], ws, wsb, None)
+
+
+def test_bwd_workspace_size_formula():
+    # per (chunk, head): T and P (64x64), state and its gradient (d x d), five 64 x d blocks, 1
+    for d, io in ((128, 1), (64, 1), (64, 0)):
+        rc, n = bws(shape(T=130, d_k=d, d_v=d, io_dtype=io))
+        nch = 2 * 3 * 4                                 # B * ceil(130/64) * H
+        assert rc == OK and n == 4 * nch * (2 * 64 * 64 + 2 * d * d + 5 * 64 * d + 1)
+    # packed: floor(T/64) + n_seqs + 1 slots per head
+    rc, n = bws(shape(B=1, T=300, n_seqs=5))
+    assert rc == OK and n == 4 * (300 // 64 + 5 + 1) * 4 * (2 * 4096 + 2 * 16384 + 5 * 8192 + 1)
+
+
+def test_bwd_rejects_before_launch():
+    assert bws(shape(prologue=1))[0] == UNSUPPORTED and "prologue" in err()
+    assert bws(shape(prologue=8))[0] == INVALID
+    assert bws(shape(chunk=32))[0] == UNSUPPORTED
+    assert bws(shape(io_dtype=0))[0] == UNSUPPORTED          # fp32 inputs: d = 64 only
+    assert bws(shape(io_dtype=0, d_k=64, d_v=64))[0] == OK
+    assert bws(shape(d_k=128, d_v=64))[0] == UNSUPPORTED
+    assert bws(shape(B=0))[0] == INVALID
+    s = shape()
+    assert bwd(s, dq=None) == INVALID
+    assert bwd(s, dO=None) == INVALID
+    assert bwd(s, dq=MIS) == ALIGN and "dq" in err()
+    assert bwd(s, dv=P) == INVALID and "alias" in err()
+    assert bwd(s, wsb=16) == WORKSPACE
+    assert bwd(shape(n_seqs=2, B=1)) == INVALID and "cu_seqlens" in err()
