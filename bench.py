@@ -13,6 +13,8 @@ state) with every input already resident in HBM.  The JSON line reports:
   decode      gdn_step on B=64, H=16, d=128 (fp32 state in place): HBM GB/s
               with the state evicted from the caches before each step
               ("cold"), and back to back ("warm");
+  backward    gdn_chunk_bwd on the same workload: ms, tokens/s and its fp32
+              MFMA roofline (the arithmetic its kernels execute);
   fused_prologue the same forward on raw projections with the input
               prologue (L2 norm of q, k; gate activations) inside the kernel,
               beside the same prologue done as separate torch ops;
@@ -34,6 +36,7 @@ if ROOT not in sys.path:
 METRIC = "gated-delta chunk-fwd tokens/s at B8 T4096 H16 d128; % MFMA peak; decode GB/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, published
+MFMA_FP32_PEAK_TFS = 157.3     # MI355X dense fp32 (matrix and vector), published
 PMC_FILE = os.path.join(ROOT, "profiles", "chunk_mfma_b8_t4096_h16_d128_traffic.json")
 
 
@@ -126,6 +129,62 @@ def run_decode(args, torch, gi, gdn, dev):
     if args.only == "decode":
         print(json.dumps({"decode": decode}))
     return decode
+
+
+def bwd_flops_per_chunk_head(d: int, C: int = 64) -> float:
+    """fp32 MFMA flops the backward launches execute per (chunk, head): the
+    tiles of each product, 2 flop per multiply-add (prep: the lower 10 of 16
+    tiles of K K^T and Q K^T; states: K S^T, T Z, the update; dstates: P^T dO,
+    K dS'^T, T^T dDelta, two update products; sprod: three C x d x d
+    products; grads: ten C-row products and two C^3 ones)."""
+    cdd = 2.0 * C * d * d
+    ccd = 2.0 * C * C * d
+    prep = 2 * 10 * 2.0 * 16 * 16 * d
+    states = cdd + ccd + cdd
+    dstates = ccd + cdd + ccd + 2 * cdd
+    sprod = 3 * cdd
+    grads = 10 * ccd + 2 * 2.0 * C ** 3
+    return prep + states + dstates + sprod + grads
+
+
+def run_backward(args, torch, gi, gdn, dev, w, host):
+    """Time gdn_chunk_bwd on the same workload (dO ~ N(0,1) fp32, no final
+    state gradient), workspace and inputs resident."""
+    B, T, H, dk, dv, C = w["B"], w["T"], w["H"], w["dk"], w["dv"], w["chunk"]
+    print("[bench] backward", file=sys.stderr, flush=True)
+    d = {k: (v.to(dev) if v is not None else None) for k, v in host.items()}
+    g = torch.Generator(device=dev).manual_seed(gi.SEED_BASE + 20)
+    dO = torch.randn((B, T, H, dv), device=dev, dtype=torch.float32, generator=g)
+    nbytes = gdn.chunk_bwd_workspace_size(B, T, H, dk, dv, C)
+    ws = torch.empty(nbytes, device=dev, dtype=torch.uint8)
+    steps, warm = max(1, args.steps // 10), max(1, args.warmup // 10)
+
+    def step():
+        gdn.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], dO, S0=d["S0"],
+                      chunk=C, workspace=ws)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nch = B * H * ((T + C - 1) // C)
+    fl = bwd_flops_per_chunk_head(dk, C) * nch
+    tfs = fl / (ms * 1e-3) / 1e12
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "steps": steps, "workspace_bytes": nbytes,
+            "roofline": {"bound": "mfma", "achieved": round(tfs, 1),
+                         "peak": MFMA_FP32_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": round(tfs / MFMA_FP32_PEAK_TFS, 4), "dtype": "f32",
+                         "flops_per_step": fl},
+            "note": "gdn_chunk_bwd = 5 launches (prep, states, dstates, sprod, grads), all "
+                    "fp32 MFMA; dO fp32 ~ N(0,1), dS_T = 0"}
 
 
 def run_prologue(args, torch, gi, gdn, dev, w, plain_ms):
@@ -264,6 +323,7 @@ def main():
                           "GB_s": round(gbs, 1)}))
         return
     prologue = run_prologue(args, torch, gi, gdn, dev, w, ms)
+    backward = run_backward(args, torch, gi, gdn, dev, w, host)
     decode = run_decode(args, torch, gi, gdn, dev)
 
     # ---------------- CPU oracle baseline ----------------
@@ -313,6 +373,7 @@ def main():
                  "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "algorithmic_flops": fl},
         "decode": decode,
         "fused_prologue": prologue,
+        "backward": backward,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }

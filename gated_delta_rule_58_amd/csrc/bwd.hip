@@ -56,19 +56,27 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// acc += sum_{k < K} A(i, k) B(k, j) on one 16 x 16 tile, with
-// A(i, k) = A[i * ar + k * ak] and B(k, j) = B[k * bk + j * bj] (pointers at
-// the tile's origin, any layout).  Lane (i = l & 15, q = l >> 4) ends with
-// rows 4q..4q+3 of column i.
-template <int K, typename TA, typename TB>
-__device__ __forceinline__ f32x4 mm(const TA *A, int ar, int ak, const TB *B, int bk, int bj,
-                                    f32x4 acc, int lane) {
+// acc[t] += sum_{k < K} A(i, k) B_t(k, j) on NT 16 x 16 tiles side by side,
+// with A(i, k) = A[i * ar + k * ak] and B_t(k, j) = B[t * bt + k * bk + j * bj]
+// (pointers at the tiles' origin, any layout).  Lane (i = l & 15, q = l >> 4)
+// ends with rows 4q..4q+3 of column i.  One A read per k step feeds NT
+// independent accumulation chains.
+template <int K, int NT, typename TA, typename TB>
+__device__ __forceinline__ void mmn(const TA *A, int ar, int ak, const TB *B, int bk, int bj,
+                                    int bt, f32x4 (&acc)[NT], int lane) {
     const int i = lane & 15, q = lane >> 4;
     const TA *pa = A + i * ar + q * ak;
     const TB *pb = B + q * bk + i * bj;
-#pragma unroll 8
-    for (int k = 0; k < K; k += 4) acc = mfma_f32(to_f32(pa[k * ak]), to_f32(pb[k * bk]), acc);
-    return acc;
+#pragma unroll 4
+    for (int k = 0; k < K; k += 4) {
+        const float a = to_f32(pa[k * ak]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = mfma_f32(a, to_f32(pb[t * bt + k * bk]), acc[t]);
+    }
+}
+template <int NT> __device__ __forceinline__ void zero_n(f32x4 (&acc)[NT]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = zero4();
 }
 
 __device__ __forceinline__ float sum16(float x) {   // over the 16 lanes of a row group
@@ -150,29 +158,57 @@ __device__ __forceinline__ void chunk_gates(float (*sg)[BC], const float *la, co
     sg[3][lane] = expf(gn - x);
 }
 
-// Rows [row0, row0 + n) of a [tokens, H, D] tensor into a 64-row LDS matrix
-// (row stride ld); rows n..63 are zero.
+// 16-byte vector copies between global memory and LDS.  Every row start
+// used below is 16-byte aligned: global rows are d_k or d_v elements of a
+// 16-byte aligned tensor, LDS rows are padded to multiples of 16 bytes.
+__device__ __forceinline__ void put8(float *dst, bf16x8 x) {
+    *reinterpret_cast<f32x4 *>(dst) = f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+    *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{(float)x[4], (float)x[5], (float)x[6], (float)x[7]};
+}
+__device__ __forceinline__ void put8(bf16 *dst, bf16x8 x) { *reinterpret_cast<bf16x8 *>(dst) = x; }
+__device__ __forceinline__ void put4(float *dst, f32x4 x) { *reinterpret_cast<f32x4 *>(dst) = x; }
+
+// Rows [row0, row0 + n) of a [tokens, H, D] tensor, columns col0..col0+width,
+// into a 64-row LDS matrix (row stride ld); rows n..63 are zero.
 template <int D, typename TS, typename TG>
 __device__ __forceinline__ void load_rows(TS *dst, int ld, const TG *src, long row0, int n, int H,
                                           int h, int col0, int width, int tid, int nthr) {
-    for (int e = tid; e < BC * width; e += nthr) {
-        const int r = e / width, d = e % width;
-        float x = 0.f;
-        if (r < n) x = to_f32(src[((size_t)(row0 + r) * H + h) * D + col0 + d]);
-        dst[r * ld + d] = cvt<TS>(x);
+    constexpr int V = sizeof(TG) == 2 ? 8 : 4;   // elements per 16-byte load
+    const int per_row = width / V;
+    for (int e = tid; e < BC * per_row; e += nthr) {
+        const int r = e / per_row, c = (e % per_row) * V;
+        TS *d = dst + r * ld + c;
+        const TG *sp = src + ((size_t)(row0 + r) * H + h) * D + col0 + c;
+        if constexpr (V == 8) {
+            bf16x8 x = {};
+            if (r < n) x = *reinterpret_cast<const bf16x8 *>(sp);
+            put8(d, x);
+        } else {
+            f32x4 x = zero4();
+            if (r < n) x = *reinterpret_cast<const f32x4 *>(sp);
+            if constexpr (sizeof(TS) == 4) {
+                put4(reinterpret_cast<float *>(d), x);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) d[j] = cvt<TS>(x[j]);
+            }
+        }
     }
 }
-// Rows of a [64, D] workspace block (rows >= n are zero).
+// Rows of a [64, D] fp32 workspace block (rows >= n are zero).
 template <int D>
 __device__ __forceinline__ void load_ws_rows(float *dst, int ld, const float *src, int n, int tid,
                                              int nthr) {
-    for (int e = tid; e < BC * D; e += nthr) {
-        const int r = e / D, d = e % D;
-        dst[r * ld + d] = r < n ? src[(size_t)r * D + d] : 0.f;
+    for (int e = tid; e < BC * D / 4; e += nthr) {
+        const int r = e / (D / 4), c = (e % (D / 4)) * 4;
+        f32x4 x = zero4();
+        if (r < n) x = *reinterpret_cast<const f32x4 *>(src + (size_t)r * D + c);
+        put4(dst + r * ld + c, x);
     }
 }
 __device__ __forceinline__ void load_nn(float *dst, const float *src, int tid, int nthr) {
-    for (int e = tid; e < BC * BC; e += nthr) dst[(e >> 6) * LDN + (e & 63)] = src[e];
+    for (int e = tid; e < BC * BC / 4; e += nthr)
+        put4(dst + (e >> 4) * LDN + (e & 15) * 4, *reinterpret_cast<const f32x4 *>(src + 4 * e));
 }
 
 // ---------------------------------------------------------------- 1. prep
@@ -203,9 +239,11 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(
         const bool isP = wave >= 4;
         const TI *Ar = (isP ? sQ : sK) + 16 * tr * LI;
         float *P = wsP + ch * BC * BC;
+        f32x4 g4[4];
+        zero_n(g4);
+        mmn<D, 4>(Ar, LI, 1, sK, 1, LI, 16 * LI, g4, lane);   // all 4 tiles (upper ones unused)
         for (int tj = 0; tj < 4; ++tj) {
-            f32x4 acc = zero4();
-            if (tj <= tr) acc = mm<D>(Ar, LI, 1, sK + 16 * tj * LI, 1, LI, acc, lane);
+            const f32x4 acc = g4[tj];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * tr + 4 * (lane >> 4) + j, i = 16 * tj + (lane & 15);
@@ -282,44 +320,52 @@ __global__ __launch_bounds__(512) void bwd_states_kernel(
             for (int j = 0; j < 4; ++j) {
                 const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
                 sS[row * LF + col] = st[t][j];
-                Hm[(size_t)(dv0 + row) * D + col] = st[t][j];
             }
         load_rows<D>(sK, LI, k, row0, n, H, h, 0, D, tid, 512);
         load_nn(sT, wsT + ch * BC * BC, tid, 512);
         if (wave == 0) chunk_gates(sg, la, beta, row0, n, H, h, lane);
         __syncthreads();
+        for (int e = tid; e < BC * D / 4; e += 512) {   // the state entering chunk c
+            const int row = e / (D / 4), c4 = (e % (D / 4)) * 4;
+            *reinterpret_cast<f32x4 *>(Hm + (size_t)(dv0 + row) * D + c4) =
+                *reinterpret_cast<const f32x4 *>(sS + row * LF + c4);
+        }
         // Z = diag(beta) (V - diag(e^g) K S^T), 64 tokens x 64 slice columns
-        for (int x = 0; x < 2; ++x) {
-            const int ty = tr, tx = 2 * (wave >> 2) + x;
-            const f32x4 y = mm<D>(sK + 16 * ty * LI, LI, 1, sS + 16 * tx * LF, 1, LF, zero4(), lane);
+        {
+            const int ty = tr, tx0 = 2 * (wave >> 2);
+            f32x4 y[2];
+            zero_n(y);
+            mmn<D, 2>(sK + 16 * ty * LI, LI, 1, sS + 16 * tx0 * LF, 1, LF, 16 * LF, y, lane);
+            for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * ty + 4 * lq + j, col = 16 * tx + li;
-                const float vv =
-                    r < n ? to_f32(v[((size_t)(row0 + r) * H + h) * D + dv0 + col]) : 0.f;
-                sZ[r * LDN + col] = sg[2][r] * (vv - sg[1][r] * y[j]);
-            }
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * ty + 4 * lq + j, col = 16 * (tx0 + x) + li;
+                    const float vv =
+                        r < n ? to_f32(v[((size_t)(row0 + r) * H + h) * D + dv0 + col]) : 0.f;
+                    sZ[r * LDN + col] = sg[2][r] * (vv - sg[1][r] * y[x][j]);
+                }
         }
         __syncthreads();
         // Delta = T Z; the state update uses diag(e^{g_n - g}) Delta
-        for (int x = 0; x < 2; ++x) {
-            const int ty = tr, tx = 2 * (wave >> 2) + x;
-            const f32x4 d = mm<BC>(sT + 16 * ty * LDN, LDN, 1, sZ + 16 * tx, LDN, 1, zero4(), lane);
+        {
+            const int ty = tr, tx0 = 2 * (wave >> 2);
+            f32x4 d[2];
+            zero_n(d);
+            mmn<BC, 2>(sT + 16 * ty * LDN, LDN, 1, sZ + 16 * tx0, LDN, 1, 16, d, lane);
+            for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * ty + 4 * lq + j, col = 16 * tx + li;
-                sD[r * LDN + col] = d[j] * sg[3][r];
-                if (r < n) wsDl[(ch * BC + r) * D + dv0 + col] = d[j];
-            }
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * ty + 4 * lq + j, col = 16 * (tx0 + x) + li;
+                    sD[r * LDN + col] = d[x][j] * sg[3][r];
+                    if (r < n) wsDl[(ch * BC + r) * D + dv0 + col] = d[x][j];
+                }
         }
         __syncthreads();
         // S <- e^{g_n} S + (diag(e^{g_n - g}) Delta)^T K
         const float egn = sg[1][BC - 1];
 #pragma unroll
-        for (int t = 0; t < NTC; ++t) {
-            st[t] = st[t] * egn;
-            st[t] = mm<BC>(sD + 16 * tr, 1, LDN, sK + 16 * (tc0 + t), LI, 1, st[t], lane);
-        }
+        for (int t = 0; t < NTC; ++t) st[t] = st[t] * egn;
+        mmn<BC, NTC>(sD + 16 * tr, 1, LDN, sK + 16 * tc0, LI, 1, 16, st, lane);
         __syncthreads();
     }
 }
@@ -369,7 +415,6 @@ __global__ __launch_bounds__(512) void bwd_dstates_kernel(
             for (int j = 0; j < 4; ++j) {
                 const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
                 sG[row * LF + col] = st[t][j];
-                DHm[(size_t)(dv0 + row) * D + col] = st[t][j];
             }
         load_rows<D>(sK, LI, k, row0, n, H, h, 0, D, tid, 512);
         load_rows<D>(sQ, LI, q, row0, n, H, h, 0, D, tid, 512);
@@ -378,41 +423,54 @@ __global__ __launch_bounds__(512) void bwd_dstates_kernel(
         load_nn(sT, wsT + ch * BC * BC, tid, 512);
         if (wave == 0) chunk_gates(sg, la, beta, row0, n, H, h, lane);
         __syncthreads();
+        for (int e = tid; e < BC * D / 4; e += 512) {   // gradient of the state leaving chunk c
+            const int row = e / (D / 4), c4 = (e % (D / 4)) * 4;
+            *reinterpret_cast<f32x4 *>(DHm + (size_t)(dv0 + row) * D + c4) =
+                *reinterpret_cast<const f32x4 *>(sG + row * LF + c4);
+        }
         // dDelta = P^T dO + diag(e^{g_n - g}) K dS'^T
-        for (int x = 0; x < 2; ++x) {
-            const int ty = tr, tx = 2 * (wave >> 2) + x;
-            const f32x4 e1 = mm<BC>(sP + 16 * ty, 1, LDN, sO + 16 * tx, LDN, 1, zero4(), lane);
-            const f32x4 e2 = mm<D>(sK + 16 * ty * LI, LI, 1, sG + 16 * tx * LF, 1, LF, zero4(), lane);
+        {
+            const int ty = tr, tx0 = 2 * (wave >> 2);
+            f32x4 e1[2], e2[2];
+            zero_n(e1);
+            zero_n(e2);
+            mmn<BC, 2>(sP + 16 * ty, 1, LDN, sO + 16 * tx0, LDN, 1, 16, e1, lane);
+            mmn<D, 2>(sK + 16 * ty * LI, LI, 1, sG + 16 * tx0 * LF, 1, LF, 16 * LF, e2, lane);
+            for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * ty + 4 * lq + j, col = 16 * tx + li;
-                const float e = e1[j] + sg[3][r] * e2[j];
-                sE[r * LDN + col] = e;
-                if (r < n) wsE[(ch * BC + r) * D + dv0 + col] = e;
-            }
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * ty + 4 * lq + j, col = 16 * (tx0 + x) + li;
+                    const float e = e1[x][j] + sg[3][r] * e2[x][j];
+                    sE[r * LDN + col] = e;
+                    if (r < n) wsE[(ch * BC + r) * D + dv0 + col] = e;
+                }
         }
         __syncthreads();
         // F = diag(beta e^g) T^T dDelta (into sP); dO rows scaled by e^g
-        for (int x = 0; x < 2; ++x) {
-            const int ty = tr, tx = 2 * (wave >> 2) + x;
-            const f32x4 f = mm<BC>(sT + 16 * ty, 1, LDN, sE + 16 * tx, LDN, 1, zero4(), lane);
+        {
+            const int ty = tr, tx0 = 2 * (wave >> 2);
+            f32x4 f[2];
+            zero_n(f);
+            mmn<BC, 2>(sT + 16 * ty, 1, LDN, sE + 16 * tx0, LDN, 1, 16, f, lane);
+            for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * ty + 4 * lq + j, col = 16 * tx + li;
-                sP[r * LDN + col] = sg[2][r] * sg[1][r] * f[j];
-                sO[r * LDN + col] *= sg[1][r];
-            }
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * ty + 4 * lq + j, col = 16 * (tx0 + x) + li;
+                    sP[r * LDN + col] = sg[2][r] * sg[1][r] * f[x][j];
+                    sO[r * LDN + col] *= sg[1][r];
+                }
         }
         __syncthreads();
         // dS <- e^{g_n} dS' + (e^g dO)^T Q - F^T K
         const float egn = sg[1][BC - 1];
+        f32x4 fk[NTC];
 #pragma unroll
-        for (int t = 0; t < NTC; ++t) {
-            st[t] = st[t] * egn;
-            st[t] = mm<BC>(sO + 16 * tr, 1, LDN, sQ + 16 * (tc0 + t), LI, 1, st[t], lane);
-            const f32x4 f = mm<BC>(sP + 16 * tr, 1, LDN, sK + 16 * (tc0 + t), LI, 1, zero4(), lane);
-            st[t] = st[t] - f;
-        }
+        for (int t = 0; t < NTC; ++t) st[t] = st[t] * egn;
+        zero_n(fk);
+        mmn<BC, NTC>(sO + 16 * tr, 1, LDN, sQ + 16 * tc0, LI, 1, 16, st, lane);
+        mmn<BC, NTC>(sP + 16 * tr, 1, LDN, sK + 16 * tc0, LI, 1, 16, fk, lane);
+#pragma unroll
+        for (int t = 0; t < NTC; ++t) st[t] = st[t] - fk[t];
         __syncthreads();
     }
     if (dS0) {
@@ -447,33 +505,38 @@ __global__ __launch_bounds__(512) void bwd_sprod_kernel(
     const int tr = wave & 3, tc0 = (wave >> 2) * NTC;
     const size_t ch = blockIdx.x;
     const float *Sm = wsH + ch * D * D, *DSm = wsDH + ch * D * D;
-    for (int e = tid; e < D * D; e += 512) sB[(e / D) * LF + e % D] = Sm[e];
+    for (int e = tid; e < D * D / 4; e += 512)
+        put4(sB + (e / (D / 4)) * LF + (e % (D / 4)) * 4, *reinterpret_cast<const f32x4 *>(Sm + 4 * e));
     load_rows<D>(sA1, LF, dO, row0, n, H, h, 0, D, tid, 512);
     load_ws_rows<D>(sA2, LF, wsE + ch * BC * D, n, tid, 512);
     __syncthreads();
     // dO S and -dDelta S (64 x d_k)
+    {
+        f32x4 a[NTC], b[NTC];
+        zero_n(a);
+        zero_n(b);
+        mmn<D, NTC>(sA1 + 16 * tr * LF, LF, 1, sB + 16 * tc0, LF, 1, 16, a, lane);
+        mmn<D, NTC>(sA2 + 16 * tr * LF, LF, 1, sB + 16 * tc0, LF, 1, 16, b, lane);
 #pragma unroll
-    for (int t = 0; t < NTC; ++t) {
-        const int tc = tc0 + t;
-        const f32x4 a = mm<D>(sA1 + 16 * tr * LF, LF, 1, sB + 16 * tc, LF, 1, zero4(), lane);
-        const f32x4 b = mm<D>(sA2 + 16 * tr * LF, LF, 1, sB + 16 * tc, LF, 1, zero4(), lane);
+        for (int t = 0; t < NTC; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
-            if (r < n) {
-                wsOS[(ch * BC + r) * D + col] = a[j];
-                wsW[(ch * BC + r) * D + col] = -b[j];
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
+                if (r < n) {
+                    wsOS[(ch * BC + r) * D + col] = a[t][j];
+                    wsW[(ch * BC + r) * D + col] = -b[t][j];
+                }
             }
-        }
     }
     __syncthreads();
     // dS' replaces S; <dS', S> on the way
     float dot = 0.f;
-    for (int e = tid; e < D * D; e += 512) {
-        const int at = (e / D) * LF + e % D;
-        const float x = DSm[e];
-        dot += x * sB[at];
-        sB[at] = x;
+    for (int e = tid; e < D * D / 4; e += 512) {
+        float *at = sB + (e / (D / 4)) * LF + (e % (D / 4)) * 4;
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(DSm + 4 * e);
+        const f32x4 y = *reinterpret_cast<const f32x4 *>(at);
+        dot += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+        put4(at, x);
     }
     load_ws_rows<D>(sA1, LF, wsDl + ch * BC * D, n, tid, 512);
     dot = sum16(dot);
@@ -487,15 +550,17 @@ __global__ __launch_bounds__(512) void bwd_sprod_kernel(
         wsSc[ch] = s;
     }
     // Delta dS' (64 x d_k)
+    {
+        f32x4 a[NTC];
+        zero_n(a);
+        mmn<D, NTC>(sA1 + 16 * tr * LF, LF, 1, sB + 16 * tc0, LF, 1, 16, a, lane);
 #pragma unroll
-    for (int t = 0; t < NTC; ++t) {
-        const int tc = tc0 + t;
-        const f32x4 a = mm<D>(sA1 + 16 * tr * LF, LF, 1, sB + 16 * tc, LF, 1, zero4(), lane);
+        for (int t = 0; t < NTC; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
-            if (r < n) wsKt[(ch * BC + r) * D + col] = a[j];
-        }
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
+                if (r < n) wsKt[(ch * BC + r) * D + col] = a[t][j];
+            }
     }
 }
 
@@ -549,9 +614,12 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
 
     // dP = tril(dO Delta^T); dQK = dP o G; dg += rowsum(dP o P) - colsum(dP o P)
     f32x4 dqk[2];
+    f32x4 a2[2];
+    zero_n(a2);
+    mmn<D, 2>(sX + 16 * ty * LF, LF, 1, sY + 16 * tx0 * LF, 1, LF, 16 * LF, a2, lane);
     for (int x = 0; x < 2; ++x) {
         const int tx = tx0 + x;
-        const f32x4 a = mm<D>(sX + 16 * ty * LF, LF, 1, sY + 16 * tx * LF, 1, LF, zero4(), lane);
+        const f32x4 a = a2[x];
         float col = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -579,16 +647,16 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
 
     // dT = dDelta (beta V)^T + ...; dV = diag(beta) T^T dDelta; dbeta += rows(T^T dDelta . V)
     f32x4 dt[2];
-    for (int x = 0; x < 2; ++x) {
-        const int tx = tx0 + x;
-        const f32x4 a = mm<D>(sY + 16 * ty * LF, LF, 1, sX + 16 * tx * LF, 1, LF, zero4(), lane);
-        const float bi = sg[2][16 * tx + li];
-        dt[x] = a * bi;
-    }
+    zero_n(dt);
+    mmn<D, 2>(sY + 16 * ty * LF, LF, 1, sX + 16 * tx0 * LF, 1, LF, 16 * LF, dt, lane);
+    for (int x = 0; x < 2; ++x) dt[x] = dt[x] * sg[2][16 * (tx0 + x) + li];
+    f32x4 an[NTC];
+    zero_n(an);
+    mmn<BC, NTC>(sT + 16 * tr, 1, LDN, sY + 16 * tc0, LF, 1, 16, an, lane);
 #pragma unroll
     for (int t = 0; t < NTC; ++t) {
         const int tc = tc0 + t;
-        const f32x4 a = mm<BC>(sT + 16 * tr, 1, LDN, sY + 16 * tc, LF, 1, zero4(), lane);
+        const f32x4 a = an[t];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
@@ -602,17 +670,19 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
     __syncthreads();
 
     // dT += dW (beta e^g K)^T; dK = diag(beta e^g) T^T dW + ...
+    zero_n(a2);
+    mmn<D, 2>(sY + 16 * ty * LF, LF, 1, sK + 16 * tx0 * LI, 1, LI, 16 * LI, a2, lane);
     for (int x = 0; x < 2; ++x) {
-        const int tx = tx0 + x;
-        const f32x4 a = mm<D>(sY + 16 * ty * LF, LF, 1, sK + 16 * tx * LI, 1, LI, zero4(), lane);
-        const int i = 16 * tx + li;
-        dt[x] = dt[x] + a * (sg[2][i] * sg[1][i]);
+        const int i = 16 * (tx0 + x) + li;
+        dt[x] = dt[x] + a2[x] * (sg[2][i] * sg[1][i]);
     }
     f32x4 dka[NTC];
+    zero_n(an);
+    mmn<BC, NTC>(sT + 16 * tr, 1, LDN, sY + 16 * tc0, LF, 1, 16, an, lane);
 #pragma unroll
     for (int t = 0; t < NTC; ++t) {
         const int tc = tc0 + t;
-        const f32x4 a = mm<BC>(sT + 16 * tr, 1, LDN, sY + 16 * tc, LF, 1, zero4(), lane);
+        const f32x4 a = an[t];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
@@ -632,19 +702,22 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
             sX[(16 * ty + 4 * lq + j) * LDN + 16 * (tx0 + x) + li] = dt[x][j];
     __syncthreads();
     // M = T^T dT (into sP)
-    for (int x = 0; x < 2; ++x) {
-        const int tx = tx0 + x;
-        const f32x4 a = mm<BC>(sT + 16 * ty, 1, LDN, sX + 16 * tx, LDN, 1, zero4(), lane);
+    zero_n(a2);
+    mmn<BC, 2>(sT + 16 * ty, 1, LDN, sX + 16 * tx0, LDN, 1, 16, a2, lane);
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sP[(16 * ty + 4 * lq + j) * LDN + 16 * tx + li] = a[j];
-    }
+        for (int j = 0; j < 4; ++j) sP[(16 * ty + 4 * lq + j) * LDN + 16 * (tx0 + x) + li] = a2[x][j];
     __syncthreads();
     // dA = -strict(M T^T); dG = dA o beta_r G (into sY);
     // dbeta += rowsum(dA o G o K K^T); dg += rowsum(dA o A) - colsum(dA o A)
+    f32x4 kk2[2];
+    zero_n(a2);
+    zero_n(kk2);
+    mmn<BC, 2>(sP + 16 * ty * LDN, LDN, 1, sT + 16 * tx0 * LDN, 1, LDN, 16 * LDN, a2, lane);
+    mmn<D, 2>(sK + 16 * ty * LI, LI, 1, sK + 16 * tx0 * LI, 1, LI, 16 * LI, kk2, lane);
     for (int x = 0; x < 2; ++x) {
         const int tx = tx0 + x;
-        const f32x4 a = mm<BC>(sP + 16 * ty * LDN, LDN, 1, sT + 16 * tx * LDN, 1, LDN, zero4(), lane);
-        const f32x4 kk = mm<D>(sK + 16 * ty * LI, LI, 1, sK + 16 * tx * LI, 1, LI, zero4(), lane);
+        const f32x4 a = a2[x], kk = kk2[x];
         float col = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -674,47 +747,49 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
 #pragma unroll
     for (int t = 0; t < NTC; ++t) {
         const int tc = tc0 + t;
-        f32x4 acc;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
             const float os = r < n ? OS[(size_t)r * D + col] : 0.f;
-            acc[j] = sg[1][r] * os;
-            const float rg = sum16(acc[j] * to_f32(sQ[r * LI + col]));
+            an[t][j] = sg[1][r] * os;
+            const float rg = sum16(an[t][j] * to_f32(sQ[r * LI + col]));
             if (li == 0) ADDG(r, rg);
         }
-        acc = mm<BC>(sN + 16 * tr * LDN, LDN, 1, sK + 16 * tc, LI, 1, acc, lane);
+    }
+    mmn<BC, NTC>(sN + 16 * tr * LDN, LDN, 1, sK + 16 * tc0, LI, 1, 16, an, lane);
+#pragma unroll
+    for (int t = 0; t < NTC; ++t)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
-            if (r < n) dq[((size_t)(row0 + r) * H + h) * D + col] = cvt<TG>(acc[j]);
+            const int r = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
+            if (r < n) dq[((size_t)(row0 + r) * H + h) * D + col] = cvt<TG>(an[t][j]);
         }
-    }
     // dK = dQK^T Q + diag(e^{g_n - g}) Delta dS' + diag(beta e^g) T^T dW + dG K + dG^T K
     // dg -= s_r, dg_{n-1} += sum_r s_r with s = rows(Delta dS' . K~)
     float ssum = 0.f;
 #pragma unroll
     for (int t = 0; t < NTC; ++t) {
         const int tc = tc0 + t;
-        f32x4 acc = dka[t];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
             const float kt = r < n ? sg[3][r] * Kt[(size_t)r * D + col] : 0.f;
-            acc[j] += kt;
+            dka[t][j] += kt;
             const float s = sum16(kt * to_f32(sK[r * LI + col]));
             if (li == 0) ADDG(r, -s);
             ssum += s;   // the same in all 16 lanes of the group
         }
-        acc = mm<BC>(sN + 16 * tr, 1, LDN, sQ + 16 * tc, LI, 1, acc, lane);
-        acc = mm<BC>(sY + 16 * tr * LDN, LDN, 1, sK + 16 * tc, LI, 1, acc, lane);
-        acc = mm<BC>(sY + 16 * tr, 1, LDN, sK + 16 * tc, LI, 1, acc, lane);
+    }
+    mmn<BC, NTC>(sN + 16 * tr, 1, LDN, sQ + 16 * tc0, LI, 1, 16, dka, lane);
+    mmn<BC, NTC>(sY + 16 * tr * LDN, LDN, 1, sK + 16 * tc0, LI, 1, 16, dka, lane);
+    mmn<BC, NTC>(sY + 16 * tr, 1, LDN, sK + 16 * tc0, LI, 1, 16, dka, lane);
+#pragma unroll
+    for (int t = 0; t < NTC; ++t)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
-            if (r < n) dk[((size_t)(row0 + r) * H + h) * D + col] = cvt<TG>(acc[j]);
+            const int r = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
+            if (r < n) dk[((size_t)(row0 + r) * H + h) * D + col] = cvt<TG>(dka[t][j]);
         }
-    }
     ssum += __shfl_xor(ssum, 16);
     ssum += __shfl_xor(ssum, 32);
     if (lane == 0 && n > 0) ADDG(n - 1, ssum);
