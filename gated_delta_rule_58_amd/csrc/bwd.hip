@@ -206,6 +206,67 @@ __device__ __forceinline__ void load_ws_rows(float *dst, int ld, const float *sr
         put4(dst + r * ld + c, x);
     }
 }
+__device__ __forceinline__ void put4(bf16 *dst, f32x4 x) {
+    *reinterpret_cast<bf16x4 *>(dst) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+}
+
+template <typename X> struct Vec16;
+template <> struct Vec16<bf16> { typedef bf16x8 type; static constexpr int n = 8; };
+template <> struct Vec16<float> { typedef f32x4 type; static constexpr int n = 4; };
+
+// A 64-row block (W elements per row, rows >= n zero) fetched into registers
+// by a 512-thread workgroup, 16 bytes at a time, and written to LDS later:
+// the sequential kernels fetch the next chunk's operands while they work on
+// the current one.
+template <int W, typename TG> struct Prefetch {
+    typedef typename Vec16<TG>::type VT;
+    static constexpr int V = Vec16<TG>::n, PR = W / V, NP = (BC * PR + 511) / 512;
+    VT buf[NP];
+    __device__ __forceinline__ void fetch(const TG *src, size_t row_stride, int n, int tid) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int e = tid + 512 * i, r = e / PR, c = (e % PR) * V;
+            buf[i] = VT{};
+            if (e < BC * PR && r < n) buf[i] = *reinterpret_cast<const VT *>(src + r * row_stride + c);
+        }
+    }
+    template <typename TS> __device__ __forceinline__ void commit(TS *dst, int ld, int tid) const {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int e = tid + 512 * i, r = e / PR, c = (e % PR) * V;
+            if (e < BC * PR) {
+                if constexpr (V == 8) put8(dst + r * ld + c, buf[i]);
+                else put4(dst + r * ld + c, buf[i]);
+            }
+        }
+    }
+};
+
+// The chunk's log alpha and beta for lane `lane` of one wave (0 past n),
+// then the scan that chunk_gates does.
+__device__ __forceinline__ void gate_fetch(const float *la, const float *beta, long row0, int n,
+                                           int H, int h, int lane, float &x, float &b) {
+    x = 0.f;
+    b = 0.f;
+    if (lane < n) {
+        const size_t idx = (size_t)(row0 + lane) * H + h;
+        x = la[idx];
+        b = beta[idx];
+    }
+}
+__device__ __forceinline__ void gate_scan(float (*sg)[BC], float x, float b, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    const float gn = __shfl(x, 63);
+    sg[0][lane] = x;
+    sg[1][lane] = expf(x);
+    sg[2][lane] = b;
+    sg[3][lane] = expf(gn - x);
+}
+
 __device__ __forceinline__ void load_nn(float *dst, const float *src, int tid, int nthr) {
     for (int e = tid; e < BC * BC / 4; e += nthr)
         put4(dst + (e >> 4) * LDN + (e & 15) * 4, *reinterpret_cast<const f32x4 *>(src + 4 * e));
@@ -231,6 +292,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(
     const size_t ch = blockIdx.x;
     load_rows<D>(sK, LI, k, row0, n, H, h, 0, D, tid, 512);
     load_rows<D>(sQ, LI, q, row0, n, H, h, 0, D, tid, 512);
+    for (int e = tid; e < BC * LDN; e += 512) sX[e] = 0.f;
     if (wave == 0) chunk_gates(sg, la, beta, row0, n, H, h, lane);
     __syncthreads();
     // waves 0-3: rows 16w.. of K K^T -> A; waves 4-7: the same rows of Q K^T -> P
@@ -254,27 +316,53 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(
         }
     }
     __syncthreads();
-    // T = (I + A)^{-1} by forward substitution, X[r][j] = [r == j] - sum_{i<r}
-    // A[r][i] X[i][j]: column j on 4 lanes of waves 0-3 (lane part p sums
-    // i = p mod 4), the rows found so far kept in LDS.  The lanes of a
-    // column are in one wave, whose LDS accesses complete in order, so the
-    // row written by part 0 is seen by the other parts' later reads (the
-    // wave barrier keeps the compiler from moving them across).
-    if (tid < 256) {
-        const int j = tid >> 2, p = tid & 3;
-        float *Tm = wsT + ch * BC * BC;
-        for (int r = 0; r < BC; ++r) {
-            float s = 0.f;
-            for (int i = p; i < r; i += 4) s += sA[r * LDN + i] * sX[i * LDN + j];
-            s += __shfl_xor(s, 1);
-            s += __shfl_xor(s, 2);
-            const float x = r == j ? 1.f : -s;
-            if (p == 0) {
-                sX[r * LDN + j] = x;
-                Tm[r * BC + j] = x;
-            }
+    // T = (I + A)^{-1}, blocked: the four 16 x 16 diagonal blocks by forward
+    // substitution (wave b inverts block b: column j on 4 lanes, lane part p
+    // sums i = p mod 4; the lanes of a column are in one wave, whose LDS
+    // accesses complete in order, and the wave barrier keeps the compiler from
+    // moving them), then the blocks below the diagonal level by level,
+    // T_ij = -T_ii sum_{j <= k < i} A_ik T_kj, on MFMA.
+    if (wave < 4) {
+        const int b = wave, j = lane >> 2, p = lane & 3;
+        const float *Ab = sA + 16 * b * LDN + 16 * b;
+        float *Xb = sX + 16 * b * LDN + 16 * b;
+        for (int r = 0; r < 16; ++r) {
+            float sum = 0.f;
+            for (int i = p; i < r; i += 4) sum += Ab[r * LDN + i] * Xb[i * LDN + j];
+            sum += __shfl_xor(sum, 1);
+            sum += __shfl_xor(sum, 2);
+            if (p == 0) Xb[r * LDN + j] = r == j ? 1.f : -sum;
             __builtin_amdgcn_wave_barrier();
         }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int lev = 1; lev < 4; ++lev) {
+        if (wave < 4 - lev) {
+            const int jb = wave, ib = wave + lev;   // block (ib, jb)
+            f32x4 m[1];
+            zero_n(m);
+            for (int kb = jb; kb < ib; ++kb)
+                mmn<16, 1>(sA + 16 * ib * LDN + 16 * kb, LDN, 1, sX + 16 * kb * LDN + 16 * jb, LDN,
+                           1, 0, m, lane);
+            float *blk = sX + 16 * ib * LDN + 16 * jb;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) blk[(4 * (lane >> 4) + jj) * LDN + (lane & 15)] = m[0][jj];
+            __builtin_amdgcn_wave_barrier();
+            f32x4 t[1];
+            zero_n(t);
+            mmn<16, 1>(sX + 16 * ib * LDN + 16 * ib, LDN, 1, blk, LDN, 1, 0, t, lane);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) blk[(4 * (lane >> 4) + jj) * LDN + (lane & 15)] = -t[0][jj];
+        }
+        __syncthreads();
+    }
+    {
+        float *Tm = wsT + ch * BC * BC;
+        for (int e = tid; e < BC * BC / 4; e += 512)
+            *reinterpret_cast<f32x4 *>(Tm + 4 * e) =
+                *reinterpret_cast<const f32x4 *>(sX + (e >> 4) * LDN + (e & 15) * 4);
     }
 }
 
@@ -291,9 +379,10 @@ __global__ __launch_bounds__(512) void bwd_states_kernel(
     __shared__ __attribute__((aligned(16))) float sT[BC * LDN];
     __shared__ __attribute__((aligned(16))) float sZ[BC * LDN];
     __shared__ __attribute__((aligned(16))) float sD[BC * LDN];
+    __shared__ __attribute__((aligned(16))) float sV[BC * LDN];  // V slice
     __shared__ float sg[4][BC];
     const int uh = blockIdx.x / NSL, dv0 = 64 * (blockIdx.x % NSL);
-    const int H_ = H, u = uh / H_, h = uh % H_;
+    const int u = uh / H, h = uh % H;
     long start, L;
     unit_span(u, T, varlen, cu, start, L);
     const int N = (int)((L + BC - 1) / BC);
@@ -309,9 +398,22 @@ __global__ __launch_bounds__(512) void bwd_states_kernel(
             const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
             st[t][j] = S0 ? S0[((size_t)uh * D + dv0 + row) * D + col] : 0.f;
         }
+    Prefetch<D, TI> pk;
+    Prefetch<64, TI> pv;
+    Prefetch<BC, float> pt;
+    float gx = 0.f, gb = 0.f;
+    auto fetch = [&](int c) {
+        const long row0 = start + (long)c * BC;
+        const int n = (int)min((long)BC, L - (long)c * BC);
+        const size_t ch = (size_t)(base + c) * H + h;
+        pk.fetch(k + ((size_t)row0 * H + h) * D, (size_t)H * D, n, tid);
+        pv.fetch(v + ((size_t)row0 * H + h) * D + dv0, (size_t)H * D, n, tid);
+        pt.fetch(wsT + ch * BC * BC, BC, BC, tid);
+        if (wave == 0) gate_fetch(la, beta, row0, n, H, h, lane, gx, gb);
+    };
+    if (N > 0) fetch(0);
     for (int c = 0; c < N; ++c) {
         const size_t ch = (size_t)(base + c) * H + h;
-        const long row0 = start + (long)c * BC;
         const int n = (int)min((long)BC, L - (long)c * BC);
         float *Hm = wsH + ch * D * D;
 #pragma unroll
@@ -321,10 +423,12 @@ __global__ __launch_bounds__(512) void bwd_states_kernel(
                 const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
                 sS[row * LF + col] = st[t][j];
             }
-        load_rows<D>(sK, LI, k, row0, n, H, h, 0, D, tid, 512);
-        load_nn(sT, wsT + ch * BC * BC, tid, 512);
-        if (wave == 0) chunk_gates(sg, la, beta, row0, n, H, h, lane);
+        pk.commit(sK, LI, tid);
+        pv.commit(sV, LDN, tid);
+        pt.commit(sT, LDN, tid);
+        if (wave == 0) gate_scan(sg, gx, gb, lane);
         __syncthreads();
+        if (c + 1 < N) fetch(c + 1);   // next chunk's operands load during this one
         for (int e = tid; e < BC * D / 4; e += 512) {   // the state entering chunk c
             const int row = e / (D / 4), c4 = (e % (D / 4)) * 4;
             *reinterpret_cast<f32x4 *>(Hm + (size_t)(dv0 + row) * D + c4) =
@@ -340,9 +444,7 @@ __global__ __launch_bounds__(512) void bwd_states_kernel(
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 16 * ty + 4 * lq + j, col = 16 * (tx0 + x) + li;
-                    const float vv =
-                        r < n ? to_f32(v[((size_t)(row0 + r) * H + h) * D + dv0 + col]) : 0.f;
-                    sZ[r * LDN + col] = sg[2][r] * (vv - sg[1][r] * y[x][j]);
+                    sZ[r * LDN + col] = sg[2][r] * (sV[r * LDN + col] - sg[1][r] * y[x][j]);
                 }
         }
         __syncthreads();
@@ -404,9 +506,24 @@ __global__ __launch_bounds__(512) void bwd_dstates_kernel(
             const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
             st[t][j] = dST ? dST[((size_t)uh * D + dv0 + row) * D + col] : 0.f;
         }
+    Prefetch<D, TI> pk, pq;
+    Prefetch<64, TG> po;
+    Prefetch<BC, float> pp, pt;
+    float gx = 0.f, gb = 0.f;
+    auto fetch = [&](int c) {
+        const long row0 = start + (long)c * BC;
+        const int n = (int)min((long)BC, L - (long)c * BC);
+        const size_t ch = (size_t)(base + c) * H + h;
+        pk.fetch(k + ((size_t)row0 * H + h) * D, (size_t)H * D, n, tid);
+        pq.fetch(q + ((size_t)row0 * H + h) * D, (size_t)H * D, n, tid);
+        po.fetch(dO + ((size_t)row0 * H + h) * D + dv0, (size_t)H * D, n, tid);
+        pp.fetch(wsP + ch * BC * BC, BC, BC, tid);
+        pt.fetch(wsT + ch * BC * BC, BC, BC, tid);
+        if (wave == 0) gate_fetch(la, beta, row0, n, H, h, lane, gx, gb);
+    };
+    if (N > 0) fetch(N - 1);
     for (int c = N - 1; c >= 0; --c) {
         const size_t ch = (size_t)(base + c) * H + h;
-        const long row0 = start + (long)c * BC;
         const int n = (int)min((long)BC, L - (long)c * BC);
         float *DHm = wsDH + ch * D * D;
 #pragma unroll
@@ -416,13 +533,14 @@ __global__ __launch_bounds__(512) void bwd_dstates_kernel(
                 const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
                 sG[row * LF + col] = st[t][j];
             }
-        load_rows<D>(sK, LI, k, row0, n, H, h, 0, D, tid, 512);
-        load_rows<D>(sQ, LI, q, row0, n, H, h, 0, D, tid, 512);
-        load_rows<D>(sO, LDN, dO, row0, n, H, h, dv0, 64, tid, 512);
-        load_nn(sP, wsP + ch * BC * BC, tid, 512);
-        load_nn(sT, wsT + ch * BC * BC, tid, 512);
-        if (wave == 0) chunk_gates(sg, la, beta, row0, n, H, h, lane);
+        pk.commit(sK, LI, tid);
+        pq.commit(sQ, LI, tid);
+        po.commit(sO, LDN, tid);
+        pp.commit(sP, LDN, tid);
+        pt.commit(sT, LDN, tid);
+        if (wave == 0) gate_scan(sg, gx, gb, lane);
         __syncthreads();
+        if (c > 0) fetch(c - 1);   // previous chunk's operands load during this one
         for (int e = tid; e < BC * D / 4; e += 512) {   // gradient of the state leaving chunk c
             const int row = e / (D / 4), c4 = (e % (D / 4)) * 4;
             *reinterpret_cast<f32x4 *>(DHm + (size_t)(dv0 + row) * D + c4) =
@@ -603,6 +721,19 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
         sdb[e / BC][e % BC] = 0.f;
         sdg[e / BC][e % BC] = 0.f;
     }
+    // this lane's elements of dO S and Delta dS' (used last; loaded first)
+    f32x4 osv[NTC], ktv[NTC];
+    {
+        const float *OS = wsOS + ch * BC * D, *Kt = wsKt + ch * BC * D;
+#pragma unroll
+        for (int t = 0; t < NTC; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
+                osv[t][j] = r < n ? OS[(size_t)r * D + col] : 0.f;
+                ktv[t][j] = r < n ? Kt[(size_t)r * D + col] : 0.f;
+            }
+    }
     load_rows<D>(sK, LI, k, row0, n, H, h, 0, D, tid, 512);
     load_rows<D>(sQ, LI, q, row0, n, H, h, 0, D, tid, 512);
     load_nn(sT, wsT + ch * BC * BC, tid, 512);
@@ -743,15 +874,13 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
     __syncthreads();
 
     // dQ = diag(e^g) dO S + dQK K;  dg += e^g rows(dO S . Q)
-    const float *OS = wsOS + ch * BC * D, *Kt = wsKt + ch * BC * D;
 #pragma unroll
     for (int t = 0; t < NTC; ++t) {
         const int tc = tc0 + t;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
-            const float os = r < n ? OS[(size_t)r * D + col] : 0.f;
-            an[t][j] = sg[1][r] * os;
+            an[t][j] = sg[1][r] * osv[t][j];
             const float rg = sum16(an[t][j] * to_f32(sQ[r * LI + col]));
             if (li == 0) ADDG(r, rg);
         }
@@ -773,7 +902,7 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
-            const float kt = r < n ? sg[3][r] * Kt[(size_t)r * D + col] : 0.f;
+            const float kt = sg[3][r] * ktv[t][j];
             dka[t][j] += kt;
             const float s = sum16(kt * to_f32(sK[r * LI + col]));
             if (li == 0) ADDG(r, -s);
