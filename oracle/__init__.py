@@ -15,6 +15,7 @@ Two independent CPU forms live here:
   the chunk algorithm reaches the recurrence's result for every chunk size,
   forward and backward.
 * ``bwd``: reverse-mode gradients through the fp64 token recurrence (C).
+* ``kda_fwd``: the recurrence with channel-wise decay (C).
 
 Neither form has values printed on the pages to compare against; both are
 pinned by the closed forms and invariants in ``tests/test_oracle_pins.py``.
@@ -59,6 +60,9 @@ def load(path: str = LIB_PATH):
                                     ctypes.c_int, dp, dp, dp, dp, dp, dp, dp,
                                     ctypes.c_int]
     lib.gdn_oracle_step.restype = ctypes.c_int
+    if hasattr(lib, "gdn_oracle_kda_fwd"):
+        lib.gdn_oracle_kda_fwd.argtypes = lib.gdn_oracle_fwd.argtypes
+        lib.gdn_oracle_kda_fwd.restype = ctypes.c_int
     if hasattr(lib, "gdn_oracle_bwd"):
         lib.gdn_oracle_bwd.argtypes = [ctypes.c_int, ctypes.c_long, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ip,
@@ -157,6 +161,35 @@ def bwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, dO=None, dS_T=None,
     if rc != 0:
         raise ValueError("oracle: bad arguments")
     return dq, dk_, dv_, dla, dbe, ds0
+
+
+def kda_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, threads: int = 0, lib=None):
+    """Token-by-token fp64 forward with channel-wise decay (log_alpha
+    [B,T,H,dk]); other layouts as in ``fwd``.  Returns (o, S_T)."""
+    lib = lib or _lib_default()
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    la, be = as_f64(log_alpha), as_f64(beta)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if la.shape != (B, T, H, dk):
+        raise ValueError("log_alpha must be [B,T,H,dk]")
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens,
+            dtype=np.int32))
+        n_seqs = cu.shape[0] - 1
+        units = n_seqs
+        cu_p = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    else:
+        n_seqs, units, cu_p = 0, B, None
+    s0 = as_f64(S0) if S0 is not None else None
+    o = np.zeros((B, T, H, dv), dtype=np.float64)
+    st = np.zeros((units, H, dv, dk), dtype=np.float64)
+    rc = lib.gdn_oracle_kda_fwd(B, T, H, dk, dv, n_seqs, cu_p, _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(la), _ptr(be), _ptr(s0), _ptr(o), _ptr(st), int(threads))
+    if rc != 0:
+        raise ValueError("oracle: bad arguments")
+    return o, st
 
 
 def step(q, k, v, log_alpha, beta, S, threads: int = 0, lib=None):

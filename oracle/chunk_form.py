@@ -234,3 +234,62 @@ def bwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, dO=None, dS_T=None,
                 out[i][b, t0:t1, h] = r[i]
             out[5][u, h] = r[5]
     return tuple(out)
+
+
+# ---------------------------------------------------------------------------
+# Channel-wise decay (KDA) in chunk form, fp64.
+#
+# With the decay acting on the key channels, G_r = sum_{s<=r} log alpha_s is
+# a vector (d_k) and every e^{g_r - g_i} of the scalar form becomes the
+# channel-wise weight Diag(e^{G_r - G_i}) inside the key products:
+#
+#   A[r,i] = beta_r sum_c k_rc k_ic e^{G_rc - G_ic}   (i < r),  T = (I + A)^{-1}
+#   Delta  = T diag(beta) (V - (K o e^G) S^T)
+#   O      = (Q o e^G) S^T + P Delta,  P[r,i] = sum_c q_rc k_ic e^{G_rc - G_ic} (i <= r)
+#   S'     = S Diag(e^{G_n}) + Delta^T (K o e^{G_n - G})
+#
+# (the same unrolling as the scalar steps above, with Diag(e^{G}) in place
+# of e^g).  Only exponentials of non-positive arguments are formed.
+# ---------------------------------------------------------------------------
+def kda_chunk_step(Q, K, V, LA, beta, S):
+    """One chunk: Q,K [n,dk]; V [n,dv]; LA [n,dk] log alpha; beta [n]; S [dv,dk]."""
+    n = Q.shape[0]
+    G = np.cumsum(LA, axis=0)
+    diff = G[:, None, :] - G[None, :, :]                  # [r, i, c]
+    strict = np.tril(np.ones((n, n), dtype=bool), -1)
+    lower = np.tril(np.ones((n, n), dtype=bool), 0)
+    W = np.exp(np.where(lower[:, :, None], diff, -np.inf))
+    A = beta[:, None] * np.einsum("rc,ic,ric->ri", K, K, W) * strict
+    T = unit_lower_inverse(np.eye(n) + A)
+    Z = beta[:, None] * (V - (K * np.exp(G)) @ S.T)
+    D = T @ Z
+    P = np.einsum("rc,ic,ric->ri", Q, K, W)
+    O = (Q * np.exp(G)) @ S.T + P @ D
+    S_next = S * np.exp(G[-1])[None, :] + D.T @ (K * np.exp(G[-1][None, :] - G))
+    return O, S_next
+
+
+def kda_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, chunk: int = 64):
+    """Chunkwise forward with channel-wise decay, layouts as ``oracle.kda_fwd``."""
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    la, be = as_f64(log_alpha), as_f64(beta)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens is not None:
+        cu = np.asarray(cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu")
+                        else cu_seqlens, dtype=np.int64)
+        spans = [(0, int(cu[i]), int(cu[i + 1])) for i in range(len(cu) - 1)]
+    else:
+        spans = [(b, 0, T) for b in range(B)]
+    s0 = as_f64(S0) if S0 is not None else None
+    o = np.zeros((B, T, H, dv))
+    st = np.zeros((len(spans), H, dv, dk))
+    for u, (b, t0, t1) in enumerate(spans):
+        for h in range(H):
+            S = s0[u, h].copy() if s0 is not None else np.zeros((dv, dk))
+            for s in range(t0, t1, chunk):
+                e = min(s + chunk, t1)
+                o[b, s:e, h], S = kda_chunk_step(q[b, s:e, h], k[b, s:e, h], v[b, s:e, h],
+                                                 la[b, s:e, h], be[b, s:e, h], S)
+            st[u, h] = S
+    return o, st

@@ -337,3 +337,85 @@ int gdn_oracle_bwd(int B, long T, int H, int dk, int dv,
     }
     return bad ? -1 : 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Channel-wise decay (KDA), fp64, token by token.
+ *
+ * "Gated DeltaNet-2: Decoupling Erase and Write in Linear Attention"
+ * (abstract) describes Kimi Delta Attention as the delta rule with
+ * channel-wise decay, and states that it reduces to Gated DeltaNet when the
+ * decay collapses to a scalar.  The pages print no equation; the reading
+ * used here keeps the scalar-gate rule above and lets the gate act on the
+ * key channels (the columns of S):
+ *
+ *     S~  = S_{t-1} Diag(alpha_t)            alpha_t in (0,1]^{d_k}
+ *     p   = S~ k_t
+ *     S_t = S~ + beta_t (v_t - p) k_t^T,     o_t = S_t q_t
+ *
+ * which is S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ * and equals the scalar rule when every channel of alpha_t is the same.
+ * log_alpha is [B,T,H,d_k]; every other layout is as in gdn_oracle_fwd.
+ * ------------------------------------------------------------------------ */
+int gdn_oracle_kda_fwd(int B, long T, int H, int dk, int dv,
+                       int n_seqs, const int32_t *cu_seqlens,
+                       const double *q, const double *k, const double *v,
+                       const double *log_alpha, const double *beta,
+                       const double *S0, double *o, double *S_T, int n_threads)
+{
+    if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    if (!q || !k || !v || !log_alpha || !beta) return -1;
+    const int varlen = (cu_seqlens != NULL && n_seqs > 0);
+    if (varlen && B != 1) return -1;
+    const int units = varlen ? n_seqs : B;
+    const long n_work = (long)units * H;
+    int bad = 0;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (long w = 0; w < n_work; ++w) {
+        const int u = (int)(w / H), h = (int)(w % H);
+        long t0, L;
+        if (varlen) {
+            t0 = cu_seqlens[u];
+            L = (long)cu_seqlens[u + 1] - cu_seqlens[u];
+            if (t0 < 0 || L < 0 || t0 + L > T) { bad |= 1; continue; }
+        } else {
+            t0 = (long)u * T;
+            L = T;
+        }
+        double *St = (double *)malloc(sizeof(double) * ((size_t)dv * dk + dk));
+        if (!St) { bad |= 1; continue; }
+        double *decay = St + (size_t)dv * dk;
+        const long unit_state = ((long)u * H + h) * dv * dk;
+        for (long e = 0; e < (long)dv * dk; ++e) St[e] = S0 ? S0[unit_state + e] : 0.0;
+        for (long t = 0; t < L; ++t) {
+            const long row = (t0 + t) * H + h;           /* token-head index */
+            const double *kt = k + row * dk, *qt = q + row * dk, *vt = v + row * dv;
+            const double *lat = log_alpha + row * dk;
+            const double b = beta[row];
+            for (int c = 0; c < dk; ++c) decay[c] = exp(lat[c]);
+            for (int r = 0; r < dv; ++r) {
+                double *Sr = St + (long)r * dk;
+                double read = 0.0;
+                for (int c = 0; c < dk; ++c) {
+                    Sr[c] *= decay[c];                   /* S~ = S Diag(alpha) */
+                    read += Sr[c] * kt[c];
+                }
+                const double wr = b * (vt[r] - read);
+                double out = 0.0;
+                for (int c = 0; c < dk; ++c) {
+                    Sr[c] += wr * kt[c];
+                    out += Sr[c] * qt[c];
+                }
+                if (o) o[row * dv + r] = out;
+            }
+        }
+        if (S_T)
+            for (long e = 0; e < (long)dv * dk; ++e) S_T[unit_state + e] = St[e];
+        free(St);
+    }
+    return bad ? -1 : 0;
+}
