@@ -1,0 +1,288 @@
+// fp32-MFMA tile helpers shared by the backward and the channel-wise decay
+// kernels: 64-token chunks, 16 x 16 fp32 tiles on v_mfma_f32_16x16x4_f32
+// (lane l supplies A[l & 15][l >> 4] and B[l >> 4][l & 15] and holds
+// D[4 (l >> 4) + j][l & 15], j = 0..3), chunk-slot geometry, gate scans and
+// 16-byte staging copies.
+#pragma once
+
+#include "gdn_common.h"
+
+namespace gdn {
+namespace tiles {
+
+constexpr int BC = 64;         // chunk length
+constexpr int LDN = BC + 4;    // row stride (floats) of 64 x 64 fp32 LDS matrices
+
+// Row stride (elements) of a 64 x D LDS matrix of type X: 4 floats or 8
+// bf16 of padding put consecutive rows 4 banks apart.
+template <typename X, int D> constexpr int ldx() { return sizeof(X) == 2 ? D + 8 : D + 4; }
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// acc[t] += sum_{k < K} A(i, k) B_t(k, j) on NT 16 x 16 tiles side by side,
+// with A(i, k) = A[i * ar + k * ak] and B_t(k, j) = B[t * bt + k * bk + j * bj]
+// (pointers at the tiles' origin, any layout).  Lane (i = l & 15, q = l >> 4)
+// ends with rows 4q..4q+3 of column i.  One A read per k step feeds NT
+// independent accumulation chains.
+template <int K, int NT, typename TA, typename TB>
+__device__ __forceinline__ void mmn(const TA *A, int ar, int ak, const TB *B, int bk, int bj,
+                                    int bt, f32x4 (&acc)[NT], int lane) {
+    const int i = lane & 15, q = lane >> 4;
+    const TA *pa = A + i * ar + q * ak;
+    const TB *pb = B + q * bk + i * bj;
+#pragma unroll 4
+    for (int k = 0; k < K; k += 4) {
+        const float a = to_f32(pa[k * ak]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = mfma_f32(a, to_f32(pb[t * bt + k * bk]), acc[t]);
+    }
+}
+template <int NT> __device__ __forceinline__ void zero_n(f32x4 (&acc)[NT]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = zero4();
+}
+
+__device__ __forceinline__ float sum16(float x) {   // over the 16 lanes of a row group
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    return x;
+}
+
+template <typename X> __device__ __forceinline__ X cvt(float x);
+template <> __device__ __forceinline__ float cvt<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 cvt<bf16>(float x) { return (bf16)x; }
+
+// --- chunk geometry -------------------------------------------------------
+// Chunk slots: a dense batch has NC = ceil(T / 64) slots per sequence,
+// sequence u starting at slot u NC; packed sequences start at slot
+// floor(cu[u] / 64) + u, which leaves room for every sequence's
+// ceil(L / 64) chunks (slots between sequences stay unused).
+__device__ __forceinline__ int unit_base(int u, int NC, int varlen, const int32_t *cu) {
+    return varlen ? cu[u] / BC + u : u * NC;
+}
+
+__device__ __forceinline__ void unit_span(int u, int T, int varlen, const int32_t *cu,
+                                          long &start, long &L) {
+    if (varlen) {
+        start = cu[u];
+        L = (long)cu[u + 1] - cu[u];
+    } else {
+        start = (long)u * T;
+        L = T;
+    }
+}
+
+// Slot -> (first token, valid rows); false for an unused slot.
+__device__ __forceinline__ bool slot_chunk(int slot, int units, int T, int NC, int varlen,
+                                           const int32_t *cu, long &row0, int &n) {
+    if (!varlen) {
+        const int u = slot / NC, c = slot % NC;
+        if (u >= units) return false;
+        row0 = (long)u * T + (long)c * BC;
+        n = min(BC, T - c * BC);
+        return true;
+    }
+    int lo = 0, hi = units - 1;   // largest u with base(u) <= slot (base(0) = 0)
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] / BC + mid <= slot) lo = mid;
+        else hi = mid - 1;
+    }
+    const int c = slot - (cu[lo] / BC + lo);
+    const long L = (long)cu[lo + 1] - cu[lo];
+    if ((long)c * BC >= L) return false;
+    row0 = cu[lo] + (long)c * BC;
+    n = (int)min((long)BC, L - (long)c * BC);
+    return true;
+}
+
+// Gates of one chunk, by one wave: sg[0] = g (chunk-local prefix of log
+// alpha; padded tokens add 0), sg[1] = e^g, sg[2] = beta (0 when padded),
+// sg[3] = e^{g_n - g} with g_n the prefix at the last valid token.
+__device__ __forceinline__ void chunk_gates(float (*sg)[BC], const float *la, const float *beta,
+                                            long row0, int n, int H, int h, int lane) {
+    float x = 0.f, b = 0.f;
+    if (lane < n) {
+        const size_t idx = (size_t)(row0 + lane) * H + h;
+        x = la[idx];
+        b = beta[idx];
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    const float gn = __shfl(x, 63);
+    sg[0][lane] = x;
+    sg[1][lane] = expf(x);
+    sg[2][lane] = b;
+    sg[3][lane] = expf(gn - x);
+}
+
+// 16-byte vector copies between global memory and LDS.  Every row start
+// used below is 16-byte aligned: global rows are d_k or d_v elements of a
+// 16-byte aligned tensor, LDS rows are padded to multiples of 16 bytes.
+__device__ __forceinline__ void put8(float *dst, bf16x8 x) {
+    *reinterpret_cast<f32x4 *>(dst) = f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+    *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{(float)x[4], (float)x[5], (float)x[6], (float)x[7]};
+}
+__device__ __forceinline__ void put8(bf16 *dst, bf16x8 x) { *reinterpret_cast<bf16x8 *>(dst) = x; }
+__device__ __forceinline__ void put4(float *dst, f32x4 x) { *reinterpret_cast<f32x4 *>(dst) = x; }
+
+// Rows [row0, row0 + n) of a [tokens, H, D] tensor, columns col0..col0+width,
+// into a 64-row LDS matrix (row stride ld); rows n..63 are zero.
+template <int D, typename TS, typename TG>
+__device__ __forceinline__ void load_rows(TS *dst, int ld, const TG *src, long row0, int n, int H,
+                                          int h, int col0, int width, int tid, int nthr) {
+    constexpr int V = sizeof(TG) == 2 ? 8 : 4;   // elements per 16-byte load
+    const int per_row = width / V;
+    for (int e = tid; e < BC * per_row; e += nthr) {
+        const int r = e / per_row, c = (e % per_row) * V;
+        TS *d = dst + r * ld + c;
+        const TG *sp = src + ((size_t)(row0 + r) * H + h) * D + col0 + c;
+        if constexpr (V == 8) {
+            bf16x8 x = {};
+            if (r < n) x = *reinterpret_cast<const bf16x8 *>(sp);
+            put8(d, x);
+        } else {
+            f32x4 x = zero4();
+            if (r < n) x = *reinterpret_cast<const f32x4 *>(sp);
+            if constexpr (sizeof(TS) == 4) {
+                put4(reinterpret_cast<float *>(d), x);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) d[j] = cvt<TS>(x[j]);
+            }
+        }
+    }
+}
+// Rows of a [64, D] fp32 workspace block (rows >= n are zero).
+template <int D>
+__device__ __forceinline__ void load_ws_rows(float *dst, int ld, const float *src, int n, int tid,
+                                             int nthr) {
+    for (int e = tid; e < BC * D / 4; e += nthr) {
+        const int r = e / (D / 4), c = (e % (D / 4)) * 4;
+        f32x4 x = zero4();
+        if (r < n) x = *reinterpret_cast<const f32x4 *>(src + (size_t)r * D + c);
+        put4(dst + r * ld + c, x);
+    }
+}
+__device__ __forceinline__ void put4(bf16 *dst, f32x4 x) {
+    *reinterpret_cast<bf16x4 *>(dst) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+}
+
+template <typename X> struct Vec16;
+template <> struct Vec16<bf16> { typedef bf16x8 type; static constexpr int n = 8; };
+template <> struct Vec16<float> { typedef f32x4 type; static constexpr int n = 4; };
+
+// A 64-row block (W elements per row, rows >= n zero) fetched into registers
+// by a 512-thread workgroup, 16 bytes at a time, and written to LDS later:
+// the sequential kernels fetch the next chunk's operands while they work on
+// the current one.
+template <int W, typename TG> struct Prefetch {
+    typedef typename Vec16<TG>::type VT;
+    static constexpr int V = Vec16<TG>::n, PR = W / V, NP = (BC * PR + 511) / 512;
+    VT buf[NP];
+    __device__ __forceinline__ void fetch(const TG *src, size_t row_stride, int n, int tid) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int e = tid + 512 * i, r = e / PR, c = (e % PR) * V;
+            buf[i] = VT{};
+            if (e < BC * PR && r < n) buf[i] = *reinterpret_cast<const VT *>(src + r * row_stride + c);
+        }
+    }
+    template <typename TS> __device__ __forceinline__ void commit(TS *dst, int ld, int tid) const {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int e = tid + 512 * i, r = e / PR, c = (e % PR) * V;
+            if (e < BC * PR) {
+                if constexpr (V == 8) put8(dst + r * ld + c, buf[i]);
+                else put4(dst + r * ld + c, buf[i]);
+            }
+        }
+    }
+};
+
+// The chunk's log alpha and beta for lane `lane` of one wave (0 past n),
+// then the scan that chunk_gates does.
+__device__ __forceinline__ void gate_fetch(const float *la, const float *beta, long row0, int n,
+                                           int H, int h, int lane, float &x, float &b) {
+    x = 0.f;
+    b = 0.f;
+    if (lane < n) {
+        const size_t idx = (size_t)(row0 + lane) * H + h;
+        x = la[idx];
+        b = beta[idx];
+    }
+}
+__device__ __forceinline__ void gate_scan(float (*sg)[BC], float x, float b, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    const float gn = __shfl(x, 63);
+    sg[0][lane] = x;
+    sg[1][lane] = expf(x);
+    sg[2][lane] = b;
+    sg[3][lane] = expf(gn - x);
+}
+
+__device__ __forceinline__ void load_nn(float *dst, const float *src, int tid, int nthr) {
+    for (int e = tid; e < BC * BC / 4; e += nthr)
+        put4(dst + (e >> 4) * LDN + (e & 15) * 4, *reinterpret_cast<const f32x4 *>(src + 4 * e));
+}
+
+// T = (I + A)^{-1} for a strictly lower 64 x 64 A in LDS (row stride LDN)
+// into X (zeroed by the caller; row stride LDN), by all 512 threads of the
+// workgroup (it contains workgroup barriers): the four 16 x 16 diagonal
+// blocks by forward substitution (wave b inverts block b: column j on 4
+// lanes, lane part p sums i = p mod 4; the lanes of a column are in one
+// wave, whose LDS accesses complete in order, and the wave barrier keeps the
+// compiler from moving them), then the blocks below the diagonal level by
+// level, T_ij = -T_ii sum_{j <= k < i} A_ik T_kj, on MFMA.
+__device__ __forceinline__ void block_inverse64(const float *sA, float *sX, int wave, int lane) {
+    if (wave < 4) {
+        const int b = wave, j = lane >> 2, p = lane & 3;
+        const float *Ab = sA + 16 * b * LDN + 16 * b;
+        float *Xb = sX + 16 * b * LDN + 16 * b;
+        for (int r = 0; r < 16; ++r) {
+            float sum = 0.f;
+            for (int i = p; i < r; i += 4) sum += Ab[r * LDN + i] * Xb[i * LDN + j];
+            sum += __shfl_xor(sum, 1);
+            sum += __shfl_xor(sum, 2);
+            if (p == 0) Xb[r * LDN + j] = r == j ? 1.f : -sum;
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int lev = 1; lev < 4; ++lev) {
+        if (wave < 4 - lev) {
+            const int jb = wave, ib = wave + lev;   // block (ib, jb)
+            f32x4 m[1];
+            zero_n(m);
+            for (int kb = jb; kb < ib; ++kb)
+                mmn<16, 1>(sA + 16 * ib * LDN + 16 * kb, LDN, 1, sX + 16 * kb * LDN + 16 * jb, LDN,
+                           1, 0, m, lane);
+            float *blk = sX + 16 * ib * LDN + 16 * jb;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) blk[(4 * (lane >> 4) + jj) * LDN + (lane & 15)] = m[0][jj];
+            __builtin_amdgcn_wave_barrier();
+            f32x4 t[1];
+            zero_n(t);
+            mmn<16, 1>(sX + 16 * ib * LDN + 16 * ib, LDN, 1, blk, LDN, 1, 0, t, lane);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) blk[(4 * (lane >> 4) + jj) * LDN + (lane & 15)] = -t[0][jj];
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace tiles
+}  // namespace gdn

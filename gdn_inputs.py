@@ -122,6 +122,18 @@ def raw_chunk_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf1
     return dict(q=q, k=k, v=v, log_alpha=a, beta=b, S0=S0, cu_seqlens=cu)
 
 
+def kda_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16",
+               alpha_mu: float = 1.0, alpha_sd: float = 1.0, s0_std: float = 0.0,
+               seed: int = 0, cu_seqlens=None):
+    """Inputs of the channel-wise decay forward: as chunk_inputs, with
+    log_alpha [B,T,H,dk] = -softplus(N(alpha_mu, alpha_sd)) per channel."""
+    rng = np.random.default_rng(seed)
+    inp = chunk_inputs(B, T, H, dk, dv, dtype, alpha_mu, s0_std, seed, cu_seqlens, rng=rng)
+    inp["log_alpha"] = torch.from_numpy(
+        _neg_softplus(rng.normal(alpha_mu, alpha_sd, (B, T, H, dk)))).float()
+    return inp
+
+
 def raw_decode_inputs(B: int, H: int, dk: int, dv: int, steps: int,
                       dtype: str = "bf16", alpha_mu: float = 1.0,
                       s0_std: float = 0.1, seed: int = 0):

@@ -167,6 +167,36 @@ int gdn_chunk_bwd(const gdn_shape *shape,
                   void *workspace, size_t workspace_bytes,
                   void *stream);
 
+/* Bytes of device workspace gdn_kda_fwd needs for `shape`: per chunk of 64
+ * tokens and head, fp32 T and P (64 x 64), K o e^G, Q o e^G and
+ * K o e^{G_n - G} (64 x d), e^{G_n} (d) and beta (64) -- about
+ * (2 * 64^2 + 3 * 64 d + d + 64) * 4 bytes (128 KiB at d = 128).
+ * Returns a gdn_status. */
+int gdn_kda_fwd_workspace_size(const gdn_shape *shape, size_t *bytes);
+
+/* Chunkwise forward of the delta rule with channel-wise decay (KDA).  The
+ * pages describe it only in words ("Gated DeltaNet-2: Decoupling Erase and
+ * Write in Linear Attention", abstract: the delta rule with channel-wise
+ * decay, reducing to Gated DeltaNet when the decay is a scalar); the rule
+ * computed here lets the decay act on the key channels before the update:
+ *
+ *     S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,     alpha_t in (0,1]^{d_k}
+ *
+ * with every argument as in gdn_chunk_fwd except
+ *   log_alpha   [B, T, H, d_k]  fp32, log of the channel-wise gate
+ * and a required workspace (gdn_kda_fwd_workspace_size).  With equal
+ * channels it computes gdn_chunk_fwd's rule.  fp32 arithmetic throughout.
+ * Supported: chunk 64, prologue 0, d_k = d_v in {64, 128} with bf16 inputs
+ * or d_k = d_v = 64 with fp32 inputs.  Returns a gdn_status. */
+int gdn_kda_fwd(const gdn_shape *shape,
+                const void *q, const void *k, const void *v,
+                const float *log_alpha, const float *beta,
+                const float *S0, const int32_t *cu_seqlens,
+                void *o, float *S_T,
+                void *workspace, size_t workspace_bytes,
+                void *stream);
+
 /* One recurrent decode step of the same rule for every (b, h): reads one
  * token, updates the state in place and returns the read-out -- the
  * constant-memory decoding of "Gated DeltaNet-2: Decoupling Erase and Write

@@ -181,3 +181,22 @@ def test_bwd_rejects_before_launch():
     assert bwd(s, dv=P) == INVALID and "alias" in err()
     assert bwd(s, wsb=16) == WORKSPACE
     assert bwd(shape(n_seqs=2, B=1)) == INVALID and "cu_seqlens" in err()
+
+
+def test_kda_workspace_and_rejects():
+    def kws(s):
+        out = ctypes.c_size_t(7)
+        return B.lib().gdn_kda_fwd_workspace_size(ctypes.byref(s), ctypes.byref(out)), out.value
+    rc, nb = kws(shape(T=130))
+    nch = 2 * 3 * 4
+    assert rc == OK and nb == 4 * nch * (2 * 64 * 64 + 3 * 64 * 128 + 128 + 64)
+    assert kws(shape(prologue=2))[0] == UNSUPPORTED
+    assert kws(shape(io_dtype=0))[0] == UNSUPPORTED
+    assert kws(shape(chunk=16))[0] == UNSUPPORTED
+    s = shape()
+    call = lambda **kw: B.lib().gdn_kda_fwd(
+        ctypes.byref(s), kw.get("q", P), P, P, P, P, None, None, kw.get("o", P2), None,
+        kw.get("ws", P), kw.get("wsb", 16), None)
+    assert call(wsb=16) == WORKSPACE
+    assert call(q=None, wsb=1 << 40) == INVALID
+    assert call(o=P, wsb=1 << 40) == INVALID and "alias" in err()
