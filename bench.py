@@ -15,6 +15,8 @@ state) with every input already resident in HBM.  The JSON line reports:
               ("cold"), and back to back ("warm");
   backward    gdn_chunk_bwd on the same workload: ms, tokens/s and its fp32
               MFMA roofline (the arithmetic its kernels execute);
+  kda_forward the channel-wise decay forward (gdn_kda_fwd) on the same
+              shape: ms, tokens/s, fp32 MFMA roofline;
   fused_prologue the same forward on raw projections with the input
               prologue (L2 norm of q, k; gate activations) inside the kernel,
               beside the same prologue done as separate torch ops;
@@ -187,6 +189,57 @@ def run_backward(args, torch, gi, gdn, dev, w, host):
                     "fp32 MFMA; dO fp32 ~ N(0,1), dS_T = 0"}
 
 
+def kda_flops_per_chunk_head(d: int, C: int = 64) -> float:
+    """fp32 MFMA flops of gdn_kda_fwd per (chunk, head): prep -- the 6 blocks
+    below the diagonal of A and of P (C/4 x C/4 x d each ... 16 x 16 x d) --
+    and the sequential launch: (K o e^G) S^T and (Q o e^G) S^T (C x d x d
+    each), T Z and P Delta (C x C x d each), the state update (d x C x d).
+    The diagonal blocks of A and P (term-by-term VALU) are not counted."""
+    cdd = 2.0 * C * d * d
+    ccd = 2.0 * C * C * d
+    prep = 2 * 6 * 2.0 * 16 * 16 * d
+    return prep + 2 * cdd + 2 * ccd + cdd
+
+
+def run_kda(args, torch, gi, gdn, dev, w):
+    """Time gdn_kda_fwd on the headline shape with channel-wise decays
+    (log alpha = -softplus(N(1,1)) per channel), inputs resident."""
+    B, T, H, dk, dv, C = w["B"], w["T"], w["H"], w["dk"], w["dv"], w["chunk"]
+    print("[bench] channel-wise decay forward", file=sys.stderr, flush=True)
+    inp = gi.kda_inputs(B, T, H, dk, dv, "bf16", alpha_mu=1.0, seed=gi.SEED_BASE + 30)
+    d = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
+    o = torch.empty((B, T, H, dv), device=dev, dtype=torch.float32)
+    st = torch.empty((B, H, dv, dk), device=dev, dtype=torch.float32)
+    ws = torch.empty(gdn.kda_fwd_workspace_size(B, T, H, dk, dv, C), device=dev,
+                     dtype=torch.uint8)
+    steps, warm = max(1, args.steps // 4), max(1, args.warmup // 4)
+
+    def step():
+        gdn.kda_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], None, chunk=C, o=o,
+                    S_T=st, workspace=ws)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    fl = kda_flops_per_chunk_head(dk, C) * B * H * ((T + C - 1) // C)
+    tfs = fl / (ms * 1e-3) / 1e12
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "steps": steps,
+            "roofline": {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_FP32_PEAK_TFS,
+                         "unit": "TFLOP/s", "frac": round(tfs / MFMA_FP32_PEAK_TFS, 4),
+                         "dtype": "f32", "flops_per_step": fl},
+            "note": "gdn_kda_fwd = prep + sequential launch, fp32 MFMA; bf16 q/k/v, fp32 "
+                    "channel-wise log alpha [B,T,H,d_k], fp32 o and state"}
+
+
 def run_prologue(args, torch, gi, gdn, dev, w, plain_ms):
     """Time the forward with the fused input prologue on raw projections of
     the same workload (q, k unnormalised, gates as pre-activations), and, for
@@ -324,6 +377,7 @@ def main():
         return
     prologue = run_prologue(args, torch, gi, gdn, dev, w, ms)
     backward = run_backward(args, torch, gi, gdn, dev, w, host)
+    kda = run_kda(args, torch, gi, gdn, dev, w)
     decode = run_decode(args, torch, gi, gdn, dev)
 
     # ---------------- CPU oracle baseline ----------------
@@ -374,6 +428,7 @@ def main():
         "decode": decode,
         "fused_prologue": prologue,
         "backward": backward,
+        "kda_forward": kda,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }

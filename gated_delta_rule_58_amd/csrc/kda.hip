@@ -33,6 +33,13 @@ namespace {
 
 using namespace tiles;
 
+// Four consecutive elements (8- or 16-byte aligned) as floats.
+__device__ __forceinline__ f32x4 ld4f(const bf16 *p) {
+    const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
+    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+__device__ __forceinline__ f32x4 ld4f(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+
 // Workspace block sizes (floats) per chunk and head.
 template <int D> struct KdaWs {
     static constexpr size_t T = BC * BC, P = BC * BC, KG = BC * D, QG = BC * D, KT = BC * D,
@@ -47,11 +54,14 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
     const TI *__restrict__ q, const TI *__restrict__ k, const float *__restrict__ la,
     const float *__restrict__ beta, float *__restrict__ ws) {
     constexpr int LI = ldx<TI, D>(), LF = D + 4;
-    __shared__ __attribute__((aligned(16))) TI sK[BC * LI];
-    __shared__ __attribute__((aligned(16))) TI sQ[BC * LI];
-    __shared__ __attribute__((aligned(16))) float sG[BC * LF];   // channel-wise prefix G
-    __shared__ __attribute__((aligned(16))) float sA[BC * LDN];
-    __shared__ __attribute__((aligned(16))) float sX[BC * LDN];
+    // K, Q and G, then A over G and T over Q once those are consumed (68 KB
+    // for d = 128, so two workgroups share a CU)
+    constexpr int BK = BC * LI * sizeof(TI), BNN = BC * LDN * 4;
+    constexpr int BQ = BK > BNN ? BK : BNN, BG = BC * LF * 4 > BNN ? BC * LF * 4 : BNN;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[BK + BQ + BG];
+    TI *sK = reinterpret_cast<TI *>(smem), *sQ = reinterpret_cast<TI *>(smem + BK);
+    float *sG = reinterpret_cast<float *>(smem + BK + BQ);
+    float *sA = sG, *sX = reinterpret_cast<float *>(smem + BK);
     __shared__ float sb[BC];
     const int slot = blockIdx.x / H, h = blockIdx.x % H;
     long row0;
@@ -65,10 +75,6 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
     load_rows<D>(sK, LI, k, row0, n, H, h, 0, D, tid, 512);
     load_rows<D>(sQ, LI, q, row0, n, H, h, 0, D, tid, 512);
     load_rows<D>(sG, LF, la, row0, n, H, h, 0, D, tid, 512);
-    for (int e = tid; e < BC * LDN; e += 512) {
-        sA[e] = 0.f;
-        sX[e] = 0.f;
-    }
     if (tid < BC) {
         const float b = tid < n ? beta[(size_t)(row0 + tid) * H + h] : 0.f;
         sb[tid] = b;
@@ -85,60 +91,102 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
     }
     __syncthreads();
     // rescaled operands for the sequential kernel
-    for (int e = tid; e < BC * D; e += 512) {
-        const int r = e / D, c = e % D;
-        const float g = sG[r * LF + c], gn = sG[(BC - 1) * LF + c];
-        const float kv = to_f32(sK[r * LI + c]), qv = to_f32(sQ[r * LI + c]);
-        wKG[e] = kv * __expf(g);
-        wQG[e] = qv * __expf(g);
-        wKT[e] = kv * __expf(gn - g);
+    for (int e = tid; e < BC * D / 4; e += 512) {
+        const int r = e / (D / 4), c = (e % (D / 4)) * 4;
+        const f32x4 g = *reinterpret_cast<const f32x4 *>(sG + r * LF + c);
+        const f32x4 gn = *reinterpret_cast<const f32x4 *>(sG + (BC - 1) * LF + c);
+        f32x4 kg, qg, kt;
+        const f32x4 k4 = ld4f(sK + r * LI + c), q4 = ld4f(sQ + r * LI + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float kv = k4[j], qv = q4[j];
+            const float eg = __expf(g[j]);
+            kg[j] = kv * eg;
+            qg[j] = qv * eg;
+            kt[j] = kv * __expf(gn[j] - g[j]);
+        }
+        *reinterpret_cast<f32x4 *>(wKG + 4 * e) = kg;
+        *reinterpret_cast<f32x4 *>(wQG + 4 * e) = qg;
+        *reinterpret_cast<f32x4 *>(wKT + 4 * e) = kt;
     }
-    // A and P, 16 x 16 blocks (br, bi), bi <= br: 10 blocks each, 20 tasks
-    // over 8 waves.  Below the diagonal the reference token is the last one
-    // of block br - 1 (G_i >= G_ref >= G_r channel by channel), so both
-    // rescaled operands are products with e^{<= 0}.
-    for (int task = wave; task < 20; task += 8) {
-        const bool isP = task >= 10;
-        int blk = isP ? task - 10 : task, br = 0;
-        while (blk > br) blk -= ++br;   // blk in 0..br
-        const int bi = blk;
+    // A and P, 16 x 16 blocks (br, bi), bi <= br: 10 blocks each.  The 8
+    // diagonal blocks (one per wave) are formed term by term, 4 channels per
+    // step; the 12 blocks below the diagonal are MFMA products whose operands
+    // are rescaled to the last token of block br - 1 (G_i >= G_ref >= G_r
+    // channel by channel, so both factors are e^{<= 0}).
+    f32x4 adiag, aoff = zero4();   // this wave's A entries (diagonal block; a block below,
+                                   // waves 0-5: A's six blocks below are tasks 0-5)
+    {
+        const bool isP = wave >= 4;
+        const int b = wave & 3;
         const TI *X = isP ? sQ : sK;
-        f32x4 acc = zero4();
-        if (bi < br) {
-            const float *gref = sG + (16 * br - 1) * LF;
-            const int ra = 16 * br + li, rb = 16 * bi + li;
-#pragma unroll 4
-            for (int c0 = 0; c0 < D; c0 += 4) {
-                const int c = c0 + lq;
-                const float gr = gref[c];
-                const float a = to_f32(X[ra * LI + c]) * __expf(sG[ra * LF + c] - gr);
-                const float b = to_f32(sK[rb * LI + c]) * __expf(gr - sG[rb * LF + c]);
-                acc = mfma_f32(a, b, acc);
-            }
-        } else {
-            // diagonal block: lane (li, lq) forms entries (16 br + 4 lq + j, 16 br + li)
+        const int i = 16 * b + li;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < D; c += 4) {
+            const f32x4 gi = *reinterpret_cast<const f32x4 *>(sG + i * LF + c);
+            const f32x4 ki = ld4f(sK + i * LI + c);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 16 * br + 4 * lq + j, i = 16 * br + li;
-                float s = 0.f;
-                if (i <= r)
-                    for (int c = 0; c < D; ++c)
-                        s += to_f32(X[r * LI + c]) * to_f32(sK[i * LI + c]) *
-                             __expf(sG[r * LF + c] - sG[i * LF + c]);
-                acc[j] = s;
+                const int r = 16 * b + 4 * lq + j;
+                const f32x4 gr = *reinterpret_cast<const f32x4 *>(sG + r * LF + c);
+                const f32x4 xr = ld4f(X + r * LI + c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[j] += xr[e] * ki[e] * __expf(fminf(gr[e] - gi[e], 0.f));
             }
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int r = 16 * br + 4 * lq + j, i = 16 * bi + li;
+            const int r = 16 * b + 4 * lq + j;
             if (isP) wP[r * BC + i] = i <= r ? acc[j] : 0.f;
-            else sA[r * LDN + i] = i < r ? sb[r] * acc[j] : 0.f;
+            adiag[j] = i < r ? sb[r] * acc[j] : 0.f;
+        }
+    }
+    for (int task = wave; task < 12; task += 8) {
+        const bool isP = task >= 6;
+        int blk = isP ? task - 6 : task, br = 1;   // blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+        while (blk >= br) blk -= br++;
+        const int bi = blk;
+        const TI *X = isP ? sQ : sK;
+        f32x4 acc = zero4();
+        const float *gref = sG + (16 * br - 1) * LF;
+        const int ra = 16 * br + li, rb = 16 * bi + li;
+#pragma unroll 4
+        for (int c0 = 0; c0 < D; c0 += 4) {
+            const int c = c0 + lq;
+            const float gr = gref[c];
+            const float a = to_f32(X[ra * LI + c]) * __expf(sG[ra * LF + c] - gr);
+            const float bb = to_f32(sK[rb * LI + c]) * __expf(gr - sG[rb * LF + c]);
+            acc = mfma_f32(a, bb, acc);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * br + 4 * lq + j, ii = 16 * bi + li;
+            if (isP) wP[r * BC + ii] = acc[j];
+            if (!isP) aoff[j] = sb[r] * acc[j];
         }
     }
     // upper blocks of P are zero
     for (int e = tid; e < BC * BC; e += 512) {
         const int r = e >> 6, i = e & 63;
         if ((i >> 4) > (r >> 4)) wP[e] = 0.f;
+    }
+    __syncthreads();   // G, K, Q consumed: A goes over G, T over Q
+    for (int e = tid; e < BC * LDN; e += 512) {
+        sA[e] = 0.f;
+        sX[e] = 0.f;
+    }
+    __syncthreads();
+    if (wave < 4) {
+        const int b = wave;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sA[(16 * b + 4 * lq + j) * LDN + 16 * b + li] = adiag[j];
+    }
+    if (wave < 6) {
+        int blk = wave, br = 1;
+        while (blk >= br) blk -= br++;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sA[(16 * br + 4 * lq + j) * LDN + 16 * blk + li] = aoff[j];
     }
     __syncthreads();
     block_inverse64(sA, sX, wave, lane);
