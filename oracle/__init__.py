@@ -16,6 +16,8 @@ Two independent CPU forms live here:
   forward and backward.
 * ``bwd``: reverse-mode gradients through the fp64 token recurrence (C).
 * ``kda_fwd``: the recurrence with channel-wise decay (C).
+* ``gdn2_fwd``: the recurrence with channel-wise decay and separate erase
+  and write gates (C).
 
 Neither form has values printed on the pages to compare against; both are
 pinned by the closed forms and invariants in ``tests/test_oracle_pins.py``.
@@ -63,6 +65,11 @@ def load(path: str = LIB_PATH):
     if hasattr(lib, "gdn_oracle_kda_fwd"):
         lib.gdn_oracle_kda_fwd.argtypes = lib.gdn_oracle_fwd.argtypes
         lib.gdn_oracle_kda_fwd.restype = ctypes.c_int
+    if hasattr(lib, "gdn_oracle_gdn2_fwd"):
+        lib.gdn_oracle_gdn2_fwd.argtypes = [ctypes.c_int, ctypes.c_long, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_int, ip,
+                                            dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+        lib.gdn_oracle_gdn2_fwd.restype = ctypes.c_int
     if hasattr(lib, "gdn_oracle_bwd"):
         lib.gdn_oracle_bwd.argtypes = [ctypes.c_int, ctypes.c_long, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ip,
@@ -187,6 +194,38 @@ def kda_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, threads: int = 0
     st = np.zeros((units, H, dv, dk), dtype=np.float64)
     rc = lib.gdn_oracle_kda_fwd(B, T, H, dk, dv, n_seqs, cu_p, _ptr(q), _ptr(k), _ptr(v),
                                 _ptr(la), _ptr(be), _ptr(s0), _ptr(o), _ptr(st), int(threads))
+    if rc != 0:
+        raise ValueError("oracle: bad arguments")
+    return o, st
+
+
+def gdn2_fwd(q, k, v, log_alpha, erase, write, S0=None, cu_seqlens=None, threads: int = 0,
+             lib=None):
+    """Token-by-token fp64 Gated DeltaNet-2 forward: log_alpha and erase
+    [B,T,H,dk], write [B,T,H,dv]; other layouts as in ``fwd``.  Returns
+    (o, S_T)."""
+    lib = lib or _lib_default()
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    la, eb, wg = as_f64(log_alpha), as_f64(erase), as_f64(write)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if la.shape != (B, T, H, dk) or eb.shape != (B, T, H, dk) or wg.shape != (B, T, H, dv):
+        raise ValueError("log_alpha, erase must be [B,T,H,dk] and write [B,T,H,dv]")
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens,
+            dtype=np.int32))
+        n_seqs = cu.shape[0] - 1
+        units = n_seqs
+        cu_p = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    else:
+        n_seqs, units, cu_p = 0, B, None
+    s0 = as_f64(S0) if S0 is not None else None
+    o = np.zeros((B, T, H, dv), dtype=np.float64)
+    st = np.zeros((units, H, dv, dk), dtype=np.float64)
+    rc = lib.gdn_oracle_gdn2_fwd(B, T, H, dk, dv, n_seqs, cu_p, _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(la), _ptr(eb), _ptr(wg), _ptr(s0), _ptr(o), _ptr(st),
+                                 int(threads))
     if rc != 0:
         raise ValueError("oracle: bad arguments")
     return o, st

@@ -293,3 +293,64 @@ def kda_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, chunk: int = 64)
                                                  la[b, s:e, h], be[b, s:e, h], S)
             st[u, h] = S
     return o, st
+
+
+# ---------------------------------------------------------------------------
+# Gated DeltaNet-2 in chunk form, fp64.
+#
+# Step: S~ = S Diag(alpha_r), S_r = S~ - (S~ k_r)(b_r o k_r)^T + (w_r o v_r) k_r^T.
+# With x_r = -S~_r k_r (the erased read), e_r = b_r o k_r, z_r = w_r o v_r and
+# the channel-wise prefix G, the state inside a chunk is
+#   S_r = S Diag(e^{G_r}) + sum_{i<=r} (x_i e_i^T + z_i k_i^T) Diag(e^{G_r - G_i}),
+# so the reads solve a unit lower triangular system with asymmetric factors:
+#   A_e[r,i] = sum_c k_rc e_ic e^{G_rc - G_ic},  A_k[r,i] = sum_c k_rc k_ic e^{...}  (i < r)
+#   X  = -(I + A_e)^{-1} ((K o e^G) S^T + A_k Z)
+#   O  = (Q o e^G) S^T + P_e X + P_k Z,  P_e, P_k as A_e, A_k with q_r, i <= r
+#   S' = S Diag(e^{G_n}) + X^T (E o e^{G_n - G}) + Z^T (K o e^{G_n - G})
+# ---------------------------------------------------------------------------
+def gdn2_chunk_step(Q, K, V, LA, Bg, Wg, S):
+    """One chunk: Q,K,Bg,LA [n,dk]; V,Wg [n,dv]; S [dv,dk]."""
+    n = Q.shape[0]
+    G = np.cumsum(LA, axis=0)
+    diff = G[:, None, :] - G[None, :, :]
+    strict = np.tril(np.ones((n, n), dtype=bool), -1)
+    lower = np.tril(np.ones((n, n), dtype=bool), 0)
+    W = np.exp(np.where(lower[:, :, None], diff, -np.inf))
+    E = Bg * K
+    Z = Wg * V
+    Ae = np.einsum("rc,ic,ric->ri", K, E, W) * strict
+    Ak = np.einsum("rc,ic,ric->ri", K, K, W) * strict
+    Pe = np.einsum("rc,ic,ric->ri", Q, E, W)
+    Pk = np.einsum("rc,ic,ric->ri", Q, K, W)
+    Te = unit_lower_inverse(np.eye(n) + Ae)
+    X = -Te @ ((K * np.exp(G)) @ S.T + Ak @ Z)
+    O = (Q * np.exp(G)) @ S.T + Pe @ X + Pk @ Z
+    tail = np.exp(G[-1][None, :] - G)
+    S_next = S * np.exp(G[-1])[None, :] + X.T @ (E * tail) + Z.T @ (K * tail)
+    return O, S_next
+
+
+def gdn2_fwd(q, k, v, log_alpha, erase, write, S0=None, cu_seqlens=None, chunk: int = 64):
+    """Chunkwise Gated DeltaNet-2 forward, layouts as ``oracle.gdn2_fwd``."""
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    la, eb, wg = as_f64(log_alpha), as_f64(erase), as_f64(write)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens is not None:
+        cu = np.asarray(cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu")
+                        else cu_seqlens, dtype=np.int64)
+        spans = [(0, int(cu[i]), int(cu[i + 1])) for i in range(len(cu) - 1)]
+    else:
+        spans = [(b, 0, T) for b in range(B)]
+    s0 = as_f64(S0) if S0 is not None else None
+    o = np.zeros((B, T, H, dv))
+    st = np.zeros((len(spans), H, dv, dk))
+    for u, (b, t0, t1) in enumerate(spans):
+        for h in range(H):
+            S = s0[u, h].copy() if s0 is not None else np.zeros((dv, dk))
+            for s in range(t0, t1, chunk):
+                e = min(s + chunk, t1)
+                o[b, s:e, h], S = gdn2_chunk_step(q[b, s:e, h], k[b, s:e, h], v[b, s:e, h],
+                                                  la[b, s:e, h], eb[b, s:e, h], wg[b, s:e, h], S)
+            st[u, h] = S
+    return o, st

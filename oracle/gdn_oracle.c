@@ -419,3 +419,89 @@ int gdn_oracle_kda_fwd(int B, long T, int H, int dk, int dv,
     }
     return bad ? -1 : 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Gated DeltaNet-2, fp64, token by token.
+ *
+ * "Gated DeltaNet-2: Decoupling Erase and Write in Linear Attention"
+ * (abstract): the delta rule's single scalar gate, which sets both how much
+ * old content is erased on the key side and how much new content is
+ * committed on the value side, is split into a channel-wise erase gate b_t
+ * and a channel-wise write gate w_t; with both equal to one scalar the rule
+ * is KDA, with a scalar decay too it is Gated DeltaNet.  The pages print no
+ * equation; the reading here replaces beta in the erase term of the KDA
+ * step by b_t on the key side and beta in the write term by w_t on the
+ * value side:
+ *
+ *     S~  = S_{t-1} Diag(alpha_t)
+ *     S_t = S~ - (S~ k_t)(b_t o k_t)^T + (w_t o v_t) k_t^T,   o_t = S_t q_t
+ *
+ * erase [B,T,H,d_k] holds b_t, write [B,T,H,d_v] holds w_t; log_alpha is
+ * [B,T,H,d_k]; every other layout is as in gdn_oracle_fwd.
+ * ------------------------------------------------------------------------ */
+int gdn_oracle_gdn2_fwd(int B, long T, int H, int dk, int dv,
+                        int n_seqs, const int32_t *cu_seqlens,
+                        const double *q, const double *k, const double *v,
+                        const double *log_alpha, const double *erase, const double *write,
+                        const double *S0, double *o, double *S_T, int n_threads)
+{
+    if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    if (!q || !k || !v || !log_alpha || !erase || !write) return -1;
+    const int varlen = (cu_seqlens != NULL && n_seqs > 0);
+    if (varlen && B != 1) return -1;
+    const int units = varlen ? n_seqs : B;
+    const long n_work = (long)units * H;
+    int bad = 0;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (long w = 0; w < n_work; ++w) {
+        const int u = (int)(w / H), h = (int)(w % H);
+        long t0, L;
+        if (varlen) {
+            t0 = cu_seqlens[u];
+            L = (long)cu_seqlens[u + 1] - cu_seqlens[u];
+            if (t0 < 0 || L < 0 || t0 + L > T) { bad |= 1; continue; }
+        } else {
+            t0 = (long)u * T;
+            L = T;
+        }
+        double *St = (double *)malloc(sizeof(double) * ((size_t)dv * dk + 2 * (size_t)dk));
+        if (!St) { bad |= 1; continue; }
+        double *decay = St + (size_t)dv * dk, *ek = decay + dk;
+        const long unit_state = ((long)u * H + h) * dv * dk;
+        for (long e = 0; e < (long)dv * dk; ++e) St[e] = S0 ? S0[unit_state + e] : 0.0;
+        for (long t = 0; t < L; ++t) {
+            const long row = (t0 + t) * H + h;
+            const double *kt = k + row * dk, *qt = q + row * dk, *vt = v + row * dv;
+            const double *lat = log_alpha + row * dk, *bt = erase + row * dk;
+            const double *wt = write + row * dv;
+            for (int c = 0; c < dk; ++c) {
+                decay[c] = exp(lat[c]);
+                ek[c] = bt[c] * kt[c];                   /* erase direction b o k */
+            }
+            for (int r = 0; r < dv; ++r) {
+                double *Sr = St + (long)r * dk;
+                double rd = 0.0;
+                for (int c = 0; c < dk; ++c) {
+                    Sr[c] *= decay[c];
+                    rd += Sr[c] * kt[c];                 /* read (S~ k)_r */
+                }
+                const double wv = wt[r] * vt[r];
+                double out = 0.0;
+                for (int c = 0; c < dk; ++c) {
+                    Sr[c] += wv * kt[c] - rd * ek[c];
+                    out += Sr[c] * qt[c];
+                }
+                if (o) o[row * dv + r] = out;
+            }
+        }
+        if (S_T)
+            for (long e = 0; e < (long)dv * dk; ++e) S_T[unit_state + e] = St[e];
+        free(St);
+    }
+    return bad ? -1 : 0;
+}
