@@ -11,7 +11,9 @@ in the HIP kernels of libgdn.so; see include/gdn.h for the C ABI.
 """
 from ._binding import (GDN_BF16, GDN_F32, GdnError, chunk_bwd,  # noqa: F401
                        chunk_bwd_workspace_size, chunk_fwd, chunk_fwd_workspace_size,
-                       kda_fwd, kda_fwd_workspace_size, lib, step, version)
+                       gdn2_fwd, gdn2_fwd_workspace_size, kda_fwd, kda_fwd_workspace_size, lib,
+                       step, version)
 
 __all__ = ["chunk_fwd", "chunk_bwd", "step", "chunk_fwd_workspace_size",
-           "chunk_bwd_workspace_size", "kda_fwd", "kda_fwd_workspace_size", "version", "lib", "GdnError", "GDN_F32", "GDN_BF16"]
+           "chunk_bwd_workspace_size", "kda_fwd", "kda_fwd_workspace_size", "gdn2_fwd",
+           "gdn2_fwd_workspace_size", "version", "lib", "GdnError", "GDN_F32", "GDN_BF16"]

@@ -40,6 +40,9 @@ SYMBOLS = {
     "gdn_kda_fwd_workspace_size": (_c_int, [ctypes.POINTER(GdnShape),
                                             ctypes.POINTER(_sz)]),
     "gdn_kda_fwd": (_c_int, [ctypes.POINTER(GdnShape)] + [_vp] * 10 + [_sz, _vp]),
+    "gdn_gdn2_fwd_workspace_size": (_c_int, [ctypes.POINTER(GdnShape),
+                                             ctypes.POINTER(_sz)]),
+    "gdn_gdn2_fwd": (_c_int, [ctypes.POINTER(GdnShape)] + [_vp] * 11 + [_sz, _vp]),
     "gdn_step": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "gdn_last_error": (ctypes.c_char_p, []),
@@ -249,6 +252,50 @@ def kda_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, chunk=64,
                              _ptr(beta), _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(S_T),
                              _ptr(workspace), workspace.numel(), _stream(q.device)))
     return o, S_T
+
+
+def gdn2_fwd(q, k, v, log_alpha, erase, write, S0=None, cu_seqlens=None, chunk=64,
+             o_dtype=torch.float32, o=None, S_T=None, want_state=True, workspace=None):
+    """Gated DeltaNet-2 forward: log_alpha, erase [B,T,H,dk], write [B,T,H,dv]
+    fp32; other arguments as in chunk_fwd.  Returns (o, S_T)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    io = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need_cuda(name, t, io)
+    for name, t, last in (("log_alpha", log_alpha, dk), ("erase", erase, dk),
+                          ("write", write, dv)):
+        _need_cuda(name, t, torch.float32)
+        if tuple(t.shape) != (B, T, H, last):
+            raise ValueError(f"{name} must be [B,T,H,{last}]")
+    n_seqs = 0
+    if cu_seqlens is not None:
+        _need_cuda("cu_seqlens", cu_seqlens, torch.int32)
+        n_seqs = cu_seqlens.shape[0] - 1
+    units = n_seqs if n_seqs > 0 else B
+    if S0 is not None:
+        _need_cuda("S0", S0, torch.float32)
+    if o is None:
+        o = torch.empty((B, T, H, dv), device=q.device, dtype=o_dtype)
+    if S_T is None and want_state:
+        S_T = torch.empty((units, H, dv, dk), device=q.device, dtype=torch.float32)
+    shape = GdnShape(B, T, H, dk, dv, chunk, n_seqs, _DTYPE[io], _DTYPE[o.dtype], 0)
+    need = ctypes.c_size_t(0)
+    _check(lib().gdn_gdn2_fwd_workspace_size(ctypes.byref(shape), ctypes.byref(need)))
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty(max(need.value, 1), device=q.device, dtype=torch.uint8)
+    _check(lib().gdn_gdn2_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                              _ptr(erase), _ptr(write), _ptr(S0), _ptr(cu_seqlens), _ptr(o),
+                              _ptr(S_T), _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return o, S_T
+
+
+def gdn2_fwd_workspace_size(B, T, H, d_k, d_v, chunk=64, n_seqs=0, io_dtype=torch.bfloat16,
+                            o_dtype=torch.float32) -> int:
+    shape = GdnShape(B, T, H, d_k, d_v, chunk, n_seqs, _DTYPE[io_dtype], _DTYPE[o_dtype], 0)
+    out = ctypes.c_size_t(0)
+    _check(lib().gdn_gdn2_fwd_workspace_size(ctypes.byref(shape), ctypes.byref(out)))
+    return out.value
 
 
 def kda_fwd_workspace_size(B, T, H, d_k, d_v, chunk=64, n_seqs=0, io_dtype=torch.bfloat16,

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["abi.cpp", "step.hip", "chunk_f32.hip", "chunk_mfma.hip", "bwd.hip", "kda.hip"]
+SOURCES = ["abi.cpp", "step.hip", "chunk_f32.hip", "chunk_mfma.hip", "bwd.hip", "kda.hip", "gdn2.hip"]
 
 # -packed-fp32-ops off: no packed fp32 VALU instructions are generated.
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -37,7 +37,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every HIP source for gfx950 and link libgdn.so.  Always rebuilds."""
     os.makedirs(OBJDIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(7, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]

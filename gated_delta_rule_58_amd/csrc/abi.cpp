@@ -37,6 +37,12 @@ hipError_t launch_kda_fwd(int units, int T, int H, int d, bool io_bf16, bool o_b
                           const int32_t *cu, const void *q, const void *k, const void *v,
                           const float *la, const float *beta, const float *S0, void *o,
                           float *S_T, void *ws, hipStream_t st);
+bool gdn2_supported(int dk, int dv, int chunk, bool io_bf16);
+size_t gdn2_ws_bytes(int units, int T, int H, int d, bool varlen);
+hipError_t launch_gdn2_fwd(int units, int T, int H, int d, bool io_bf16, bool o_bf16,
+                           const int32_t *cu, const void *q, const void *k, const void *v,
+                           const float *la, const float *erase, const float *write,
+                           const float *S0, void *o, float *S_T, void *ws, hipStream_t st);
 }  // namespace gdn
 
 namespace {
@@ -101,7 +107,8 @@ int check_shape(const gdn_shape *s) {
 
 // Shape checks shared by the backward and the channel-wise decay forward
 // (their own supported sets, no prologue).
-int check_fp32tile_shape(const gdn_shape *s, bool kda) {
+int check_fp32tile_shape(const gdn_shape *s, int kind) {   // 0 bwd, 1 KDA, 2 GDN-2
+    const bool kda = kind != 0;
     if (!s) return fail(GDN_ERR_INVALID_ARG, "shape is NULL");
     if (s->B <= 0 || s->H <= 0 || s->T < 0 || s->d_k <= 0 || s->d_v <= 0 || s->chunk <= 0)
         return fail(GDN_ERR_INVALID_ARG,
@@ -119,14 +126,16 @@ int check_fp32tile_shape(const gdn_shape *s, bool kda) {
                     s->prologue);
     if (s->prologue != 0)
         return fail(GDN_ERR_UNSUPPORTED, "%s takes no input prologue (prologue=%d)",
-                    kda ? "gdn_kda_fwd" : "the backward", s->prologue);
+                    kind == 2 ? "gdn_gdn2_fwd" : kda ? "gdn_kda_fwd" : "the backward",
+                    s->prologue);
     const long units = s->n_seqs > 0 ? s->n_seqs : s->B;
     if ((long)units * s->H > (1L << 24) || (long)s->T * s->H > (1L << 31) / 64)
         return fail(GDN_ERR_INVALID_ARG, "problem too large for the backward (units x heads = %ld)",
                     units * (long)s->H);
-    const bool okk = kda ? gdn::kda_supported(s->d_k, s->d_v, s->chunk, s->io_dtype == GDN_BF16)
-                         : gdn::chunk_bwd_supported(s->d_k, s->d_v, s->chunk,
-                                                    s->io_dtype == GDN_BF16);
+    const bool bf = s->io_dtype == GDN_BF16;
+    const bool okk = kind == 2 ? gdn::gdn2_supported(s->d_k, s->d_v, s->chunk, bf)
+                     : kda     ? gdn::kda_supported(s->d_k, s->d_v, s->chunk, bf)
+                               : gdn::chunk_bwd_supported(s->d_k, s->d_v, s->chunk, bf);
     if (!okk)
         return fail(GDN_ERR_UNSUPPORTED,
                     "no %s kernel for d_k=%d d_v=%d chunk=%d io_dtype=%s (bf16: d_k=d_v in "
@@ -135,7 +144,7 @@ int check_fp32tile_shape(const gdn_shape *s, bool kda) {
                     s->io_dtype == GDN_BF16 ? "bf16" : "f32");
     return GDN_OK;
 }
-int check_bwd_shape(const gdn_shape *s) { return check_fp32tile_shape(s, false); }
+int check_bwd_shape(const gdn_shape *s) { return check_fp32tile_shape(s, 0); }
 
 }  // namespace
 
@@ -247,7 +256,7 @@ int gdn_chunk_bwd(const gdn_shape *s, const void *q, const void *k, const void *
 
 int gdn_kda_fwd_workspace_size(const gdn_shape *shape, size_t *bytes) {
     if (!bytes) return fail(GDN_ERR_INVALID_ARG, "bytes is NULL");
-    const int rc = check_fp32tile_shape(shape, true);
+    const int rc = check_fp32tile_shape(shape, 1);
     if (rc != GDN_OK) return rc;
     const int units = shape->n_seqs > 0 ? shape->n_seqs : shape->B;
     *bytes = gdn::kda_ws_bytes(units, shape->T, shape->H, shape->d_k, shape->n_seqs > 0);
@@ -258,7 +267,7 @@ int gdn_kda_fwd(const gdn_shape *s, const void *q, const void *k, const void *v,
                 const float *log_alpha, const float *beta, const float *S0,
                 const int32_t *cu_seqlens, void *o, float *S_T, void *workspace,
                 size_t workspace_bytes, void *stream) {
-    int rc = check_fp32tile_shape(s, true);
+    int rc = check_fp32tile_shape(s, 1);
     if (rc != GDN_OK) return rc;
     if (s->n_seqs > 0 && !cu_seqlens)
         return fail(GDN_ERR_INVALID_ARG, "n_seqs=%d but cu_seqlens is NULL", s->n_seqs);
@@ -283,6 +292,50 @@ int gdn_kda_fwd(const gdn_shape *s, const void *q, const void *k, const void *v,
     const hipError_t e = gdn::launch_kda_fwd(
         units, s->T, s->H, s->d_k, s->io_dtype == GDN_BF16, s->o_dtype == GDN_BF16, cu_seqlens, q,
         k, v, log_alpha, beta, S0, o, S_T, workspace, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int gdn_gdn2_fwd_workspace_size(const gdn_shape *shape, size_t *bytes) {
+    if (!bytes) return fail(GDN_ERR_INVALID_ARG, "bytes is NULL");
+    const int rc = check_fp32tile_shape(shape, 2);
+    if (rc != GDN_OK) return rc;
+    const int units = shape->n_seqs > 0 ? shape->n_seqs : shape->B;
+    *bytes = gdn::gdn2_ws_bytes(units, shape->T, shape->H, shape->d_k, shape->n_seqs > 0);
+    return ok();
+}
+
+int gdn_gdn2_fwd(const gdn_shape *s, const void *q, const void *k, const void *v,
+                 const float *log_alpha, const float *erase, const float *write,
+                 const float *S0, const int32_t *cu_seqlens, void *o, float *S_T,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = check_fp32tile_shape(s, 2);
+    if (rc != GDN_OK) return rc;
+    if (s->n_seqs > 0 && !cu_seqlens)
+        return fail(GDN_ERR_INVALID_ARG, "n_seqs=%d but cu_seqlens is NULL", s->n_seqs);
+    if (s->n_seqs == 0 && cu_seqlens)
+        return fail(GDN_ERR_INVALID_ARG, "cu_seqlens given but n_seqs is 0");
+    if (s->T > 0 && (!q || !k || !v || !log_alpha || !erase || !write || !o))
+        return fail(GDN_ERR_INVALID_ARG,
+                    "q, k, v, log_alpha, erase, write and o are required when T > 0");
+    const void *ptrs[] = {q, k, v, log_alpha, erase, write, S0, cu_seqlens, o, S_T, workspace};
+    const char *names[] = {"q", "k", "v", "log_alpha", "erase", "write", "S0", "cu_seqlens",
+                           "o", "S_T", "workspace"};
+    for (int i = 0; i < 11; ++i)
+        if (misaligned(ptrs[i]))
+            return fail(GDN_ERR_ALIGNMENT, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
+    if (o && (o == q || o == k || o == v))
+        return fail(GDN_ERR_INVALID_ARG, "o must not alias q, k or v");
+    size_t need = 0;
+    gdn_gdn2_fwd_workspace_size(s, &need);
+    if (workspace_bytes < need)
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    if (need > 0 && !workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL");
+    const int units = s->n_seqs > 0 ? s->n_seqs : s->B;
+    const hipError_t e = gdn::launch_gdn2_fwd(
+        units, s->T, s->H, s->d_k, s->io_dtype == GDN_BF16, s->o_dtype == GDN_BF16, cu_seqlens, q,
+        k, v, log_alpha, erase, write, S0, o, S_T, workspace,
+        reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }

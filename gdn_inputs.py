@@ -134,6 +134,18 @@ def kda_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16",
     return inp
 
 
+def gdn2_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16",
+                alpha_mu: float = 1.0, alpha_sd: float = 1.0, s0_std: float = 0.0,
+                seed: int = 0, cu_seqlens=None):
+    """Inputs of the Gated DeltaNet-2 forward: as kda_inputs, plus erase
+    [B,T,H,dk] = sigmoid(N(0,1)) and write [B,T,H,dv] = sigmoid(N(0,1))."""
+    inp = kda_inputs(B, T, H, dk, dv, dtype, alpha_mu, alpha_sd, s0_std, seed, cu_seqlens)
+    rng = np.random.default_rng(seed + 12345)
+    inp["erase"] = torch.from_numpy(_sigmoid(rng.standard_normal((B, T, H, dk)))).float()
+    inp["write"] = torch.from_numpy(_sigmoid(rng.standard_normal((B, T, H, dv)))).float()
+    return inp
+
+
 def raw_decode_inputs(B: int, H: int, dk: int, dv: int, steps: int,
                       dtype: str = "bf16", alpha_mu: float = 1.0,
                       s0_std: float = 0.1, seed: int = 0):

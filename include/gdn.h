@@ -197,6 +197,37 @@ int gdn_kda_fwd(const gdn_shape *shape,
                 void *workspace, size_t workspace_bytes,
                 void *stream);
 
+/* Bytes of device workspace gdn_gdn2_fwd needs for `shape`: per chunk of 64
+ * tokens and head, two 64 x 64 and four 64 x d fp32 blocks and e^{G_n}
+ * (about 160 KiB at d = 128).  Returns a gdn_status. */
+int gdn_gdn2_fwd_workspace_size(const gdn_shape *shape, size_t *bytes);
+
+/* Chunkwise forward of Gated DeltaNet-2: channel-wise decay, a channel-wise
+ * erase gate on the key side and a channel-wise write gate on the value
+ * side.  The pages describe it in words only ("Gated DeltaNet-2: Decoupling
+ * Erase and Write in Linear Attention", abstract: the delta rule's scalar
+ * gate split into an erase and a write gate, reducing to KDA when both are
+ * one scalar); the rule computed here:
+ *
+ *     S~  = S_{t-1} Diag(alpha_t)
+ *     S_t = S~ - (S~ k_t)(b_t o k_t)^T + (w_t o v_t) k_t^T,   o_t = S_t q_t
+ *
+ * with every argument as in gdn_kda_fwd except
+ *   erase   [B, T, H, d_k]  fp32, b_t
+ *   write   [B, T, H, d_v]  fp32, w_t
+ * and its own workspace (gdn_gdn2_fwd_workspace_size).  With b_t and w_t
+ * equal to beta_t in every channel it computes gdn_kda_fwd's rule.  fp32
+ * arithmetic throughout.  Supported: chunk 64, prologue 0, d_k = d_v in
+ * {64, 128} with bf16 inputs or d_k = d_v = 64 with fp32 inputs.  Returns a
+ * gdn_status. */
+int gdn_gdn2_fwd(const gdn_shape *shape,
+                 const void *q, const void *k, const void *v,
+                 const float *log_alpha, const float *erase, const float *write,
+                 const float *S0, const int32_t *cu_seqlens,
+                 void *o, float *S_T,
+                 void *workspace, size_t workspace_bytes,
+                 void *stream);
+
 /* One recurrent decode step of the same rule for every (b, h): reads one
  * token, updates the state in place and returns the read-out -- the
  * constant-memory decoding of "Gated DeltaNet-2: Decoupling Erase and Write

@@ -200,3 +200,20 @@ def test_kda_workspace_and_rejects():
     assert call(wsb=16) == WORKSPACE
     assert call(q=None, wsb=1 << 40) == INVALID
     assert call(o=P, wsb=1 << 40) == INVALID and "alias" in err()
+
+
+def test_gdn2_workspace_and_rejects():
+    def gws(s):
+        out = ctypes.c_size_t(7)
+        return B.lib().gdn_gdn2_fwd_workspace_size(ctypes.byref(s), ctypes.byref(out)), out.value
+    rc, nb = gws(shape(T=130))
+    assert rc == OK and nb == 4 * 2 * 3 * 4 * (2 * 64 * 64 + 4 * 64 * 128 + 128)
+    assert gws(shape(prologue=1))[0] == UNSUPPORTED
+    assert gws(shape(io_dtype=0))[0] == UNSUPPORTED
+    s = shape()
+    call = lambda **kw: B.lib().gdn_gdn2_fwd(
+        ctypes.byref(s), P, P, P, P, kw.get("erase", P), P, None, None, kw.get("o", P2), None,
+        kw.get("ws", P), kw.get("wsb", 16), None)
+    assert call(wsb=16) == WORKSPACE
+    assert call(erase=None, wsb=1 << 40) == INVALID
+    assert call(erase=MIS, wsb=1 << 40) == ALIGN
