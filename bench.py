@@ -17,6 +17,7 @@ state) with every input already resident in HBM.  The JSON line reports:
               MFMA roofline (the arithmetic its kernels execute);
   kda_forward the channel-wise decay forward (gdn_kda_fwd) on the same
               shape: ms, tokens/s, fp32 MFMA roofline;
+  gdn2_forward the Gated DeltaNet-2 forward (gdn_gdn2_fwd) on the same shape;
   fused_prologue the same forward on raw projections with the input
               prologue (L2 norm of q, k; gate activations) inside the kernel,
               beside the same prologue done as separate torch ops;
@@ -240,6 +241,58 @@ def run_kda(args, torch, gi, gdn, dev, w):
                     "channel-wise log alpha [B,T,H,d_k], fp32 o and state"}
 
 
+def gdn2_flops_per_chunk_head(d: int, C: int = 64) -> float:
+    """fp32 MFMA flops of gdn_gdn2_fwd per (chunk, head): prep -- the 6
+    blocks below the diagonal of each of A_e, A_k, P_e, P_k, the folds
+    M = P_e T_e, N1 = T_e A_k, N2 (C^3 each), F1 and Qh (C x C x d each) --
+    and the sequential launch: F1 S^T, Qh S^T (C x d x d), N1 Z, N2 Z (C^2 x d)
+    and the two update products (d x C x d).  Diagonal blocks (term-by-term
+    VALU) are not counted."""
+    cdd = 2.0 * C * d * d
+    ccd = 2.0 * C * C * d
+    prep = 4 * 6 * 2.0 * 16 * 16 * d + 3 * 2.0 * C ** 3 + 2 * ccd
+    return prep + 2 * cdd + 2 * ccd + 2 * cdd
+
+
+def run_gdn2(args, torch, gi, gdn, dev, w):
+    """Time gdn_gdn2_fwd on the headline shape (channel-wise decays, erase and
+    write gates sigmoid(N(0,1))), inputs resident."""
+    B, T, H, dk, dv, C = w["B"], w["T"], w["H"], w["dk"], w["dv"], w["chunk"]
+    print("[bench] Gated DeltaNet-2 forward", file=sys.stderr, flush=True)
+    inp = gi.gdn2_inputs(B, T, H, dk, dv, "bf16", alpha_mu=1.0, seed=gi.SEED_BASE + 40)
+    d = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
+    o = torch.empty((B, T, H, dv), device=dev, dtype=torch.float32)
+    st = torch.empty((B, H, dv, dk), device=dev, dtype=torch.float32)
+    ws = torch.empty(gdn.gdn2_fwd_workspace_size(B, T, H, dk, dv, C), device=dev,
+                     dtype=torch.uint8)
+    steps, warm = max(1, args.steps // 4), max(1, args.warmup // 4)
+
+    def step():
+        gdn.gdn2_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["erase"], d["write"], None,
+                     chunk=C, o=o, S_T=st, workspace=ws)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    fl = gdn2_flops_per_chunk_head(dk, C) * B * H * ((T + C - 1) // C)
+    tfs = fl / (ms * 1e-3) / 1e12
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "steps": steps,
+            "roofline": {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_FP32_PEAK_TFS,
+                         "unit": "TFLOP/s", "frac": round(tfs / MFMA_FP32_PEAK_TFS, 4),
+                         "dtype": "f32", "flops_per_step": fl},
+            "note": "gdn_gdn2_fwd = prep + sequential launch, fp32 MFMA; bf16 q/k/v, fp32 "
+                    "log alpha and erase gates [B,T,H,d_k], write gates [B,T,H,d_v]"}
+
+
 def run_prologue(args, torch, gi, gdn, dev, w, plain_ms):
     """Time the forward with the fused input prologue on raw projections of
     the same workload (q, k unnormalised, gates as pre-activations), and, for
@@ -378,6 +431,7 @@ def main():
     prologue = run_prologue(args, torch, gi, gdn, dev, w, ms)
     backward = run_backward(args, torch, gi, gdn, dev, w, host)
     kda = run_kda(args, torch, gi, gdn, dev, w)
+    gdn2 = run_gdn2(args, torch, gi, gdn, dev, w)
     decode = run_decode(args, torch, gi, gdn, dev)
 
     # ---------------- CPU oracle baseline ----------------
@@ -429,6 +483,7 @@ def main():
         "fused_prologue": prologue,
         "backward": backward,
         "kda_forward": kda,
+        "gdn2_forward": gdn2,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }
