@@ -284,5 +284,60 @@ __device__ __forceinline__ void block_inverse64(const float *sA, float *sX, int 
     }
 }
 
+// Four consecutive elements (8- or 16-byte aligned) as floats.
+__device__ __forceinline__ f32x4 ld4f(const bf16 *p) {
+    const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
+    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+__device__ __forceinline__ f32x4 ld4f(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+
+// Diagonal 16 x 16 block b of the channel-weighted product
+//   M[r][i] = sum_c X[r][c] Y[i][c] e^{G[r][c] - G[i][c]},  r, i in 16b..16b+15,
+// by one wave, every entry (the caller masks the upper part); lane (li, lq)
+// gets rows 16b + 4lq + j of column 16b + li.  G is the chunk's per-channel
+// prefix (non-increasing down the rows).  With G_ref the prefix just before
+// the block (0 for the first), the weight factors as e^{G_r - G_ref} (<= 1)
+// times e^{G_ref - G_i} (>= 1): when the block's span max_c (G_ref - G_last)
+// is at most 60 both factors are normal floats and the block is one MFMA
+// product; otherwise it is formed term by term (exponentials of r >= i only).
+template <int D, typename TX, typename TY>
+__device__ __forceinline__ f32x4 diag_block(const TX *X, int lx, const TY *Y, int ly,
+                                            const float *G, int lg, int b, int lane) {
+    const int li = lane & 15, lq = lane >> 4;
+    const float *gref = b > 0 ? G + (16 * b - 1) * lg : nullptr;
+    const float *glast = G + (16 * b + 15) * lg;
+    float span = 0.f;
+    for (int c = lane; c < D; c += 64) span = fmaxf(span, (gref ? gref[c] : 0.f) - glast[c]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) span = fmaxf(span, __shfl_xor(span, off));
+    f32x4 acc = zero4();
+    if (span <= 60.f) {
+        const int rw = 16 * b + li;
+#pragma unroll 4
+        for (int c0 = 0; c0 < D; c0 += 4) {
+            const int c = c0 + lq;
+            const float gr = gref ? gref[c] : 0.f, gw = G[rw * lg + c];
+            const float a = to_f32(X[rw * lx + c]) * __expf(gw - gr);
+            const float y = to_f32(Y[rw * ly + c]) * __expf(gr - gw);
+            acc = mfma_f32(a, y, acc);
+        }
+        return acc;
+    }
+    const int i = 16 * b + li;
+    for (int c = 0; c < D; c += 4) {
+        const f32x4 gi = *reinterpret_cast<const f32x4 *>(G + i * lg + c);
+        const f32x4 yi = ld4f(Y + i * ly + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * b + 4 * lq + j;
+            const f32x4 gr = *reinterpret_cast<const f32x4 *>(G + r * lg + c);
+            const f32x4 xr = ld4f(X + r * lx + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[j] += xr[e] * yi[e] * __expf(fminf(gr[e] - gi[e], 0.f));
+        }
+    }
+    return acc;
+}
+
 }  // namespace tiles
 }  // namespace gdn

@@ -28,11 +28,6 @@ namespace {
 
 using namespace tiles;
 
-__device__ __forceinline__ f32x4 ld4f(const bf16 *p) {
-    const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
-    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
-}
-__device__ __forceinline__ f32x4 ld4f(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
 // Workspace blocks (floats) per chunk and head.
 template <int D> struct G2Ws {
@@ -106,9 +101,9 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
     }
     // The four channel-weighted products, 16 x 16 blocks (br, bi), bi <= br:
     // matrix mx = 0 A_e (rows K, columns E), 1 A_k (K, K), 2 P_e (Q, E),
-    // 3 P_k (Q, K).  40 tasks, 5 per wave: the 16 diagonal blocks term by
-    // term (4 channels per step), the 24 blocks below on MFMA from operands
-    // rescaled to the last token of block br - 1 (every factor e^{<= 0}).
+    // 3 P_k (Q, K).  40 tasks, 5 per wave: the 16 diagonal blocks by
+    // diag_block, the 24 blocks below on MFMA from operands rescaled to the
+    // last token of block br - 1 (every factor e^{<= 0}).
     f32x4 res[5];
 #pragma unroll
     for (int s = 0; s < 5; ++s) {
@@ -132,21 +127,8 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
                 acc = mfma_f32(a, y * __expf(gr - sG[rb * LF + c]), acc);
             }
         } else {
-            const int i = 16 * br + li;
-            for (int c = 0; c < D; c += 4) {
-                const f32x4 gi = *reinterpret_cast<const f32x4 *>(sG + i * LF + c);
-                const f32x4 yi = colE ? *reinterpret_cast<const f32x4 *>(sE + i * LE + c)
-                                      : ld4f(sK + i * LI + c);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * br + 4 * lq + j;
-                    const f32x4 gr = *reinterpret_cast<const f32x4 *>(sG + r * LF + c);
-                    const f32x4 xr = ld4f(Xr + r * LI + c);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        acc[j] += xr[e] * yi[e] * __expf(fminf(gr[e] - gi[e], 0.f));
-                }
-            }
+            acc = colE ? diag_block<D>(Xr, LI, sE, LE, sG, LF, br, lane)
+                       : diag_block<D>(Xr, LI, sK, LI, sG, LF, br, lane);
         }
         // keep strict (A) or inclusive (P) lower entries
 #pragma unroll

@@ -33,12 +33,6 @@ namespace {
 
 using namespace tiles;
 
-// Four consecutive elements (8- or 16-byte aligned) as floats.
-__device__ __forceinline__ f32x4 ld4f(const bf16 *p) {
-    const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
-    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
-}
-__device__ __forceinline__ f32x4 ld4f(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
 // Workspace block sizes (floats) per chunk and head.
 template <int D> struct KdaWs {
@@ -110,8 +104,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
         *reinterpret_cast<f32x4 *>(wKT + 4 * e) = kt;
     }
     // A and P, 16 x 16 blocks (br, bi), bi <= br: 10 blocks each.  The 8
-    // diagonal blocks (one per wave) are formed term by term, 4 channels per
-    // step; the 12 blocks below the diagonal are MFMA products whose operands
+    // diagonal blocks (one per wave) by diag_block; the 12 blocks below the
+    // diagonal are MFMA products whose operands
     // are rescaled to the last token of block br - 1 (G_i >= G_ref >= G_r
     // channel by channel, so both factors are e^{<= 0}).
     f32x4 adiag, aoff = zero4();   // this wave's A entries (diagonal block; a block below,
@@ -121,20 +115,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
         const int b = wave & 3;
         const TI *X = isP ? sQ : sK;
         const int i = 16 * b + li;
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int c = 0; c < D; c += 4) {
-            const f32x4 gi = *reinterpret_cast<const f32x4 *>(sG + i * LF + c);
-            const f32x4 ki = ld4f(sK + i * LI + c);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * b + 4 * lq + j;
-                const f32x4 gr = *reinterpret_cast<const f32x4 *>(sG + r * LF + c);
-                const f32x4 xr = ld4f(X + r * LI + c);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    acc[j] += xr[e] * ki[e] * __expf(fminf(gr[e] - gi[e], 0.f));
-            }
-        }
+        const f32x4 acc = diag_block<D>(X, LI, sK, LI, sG, LF, b, lane);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * b + 4 * lq + j;
