@@ -337,16 +337,45 @@ __global__ __launch_bounds__(512) void bwd_dstates_kernel(
 }
 
 // ---------------------------------------------------------------- 4. sprod
+// A-operand fragment of rows 16 tr + (l & 15) of a 64 x D row-major block,
+// held in registers: frag[s] = A[row][16 s + 4 (l >> 4) .. + 3] (the k order
+// of these products is 16 s + 4 lq + m, the same for the B operand, so the B
+// rows read by the four lane groups are 4 rows apart: distinct LDS banks with
+// a row stride of D + 4 floats).  Rows past n are zero.
 template <int D, typename TG>
-__global__ __launch_bounds__(512) void bwd_sprod_kernel(
+__device__ __forceinline__ void afrag_rows(f32x4 (&frag)[D / 16], const TG *rowp, bool valid,
+                                           int lq) {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+        frag[s] = zero4();
+        if (valid) frag[s] = ld4f(rowp + 16 * s + 4 * lq);
+    }
+}
+// acc[t] += A_frag B_t with B_t(k, j) = B[k * ldb + 16 t + j], k in the fragment order.
+template <int D, int NT>
+__device__ __forceinline__ void mm_afrag(const f32x4 (&frag)[D / 16], const float *B, int ldb,
+                                         f32x4 (&acc)[NT], int lane) {
+    const int li = lane & 15, lq = lane >> 4;
+#pragma unroll 2
+    for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float *bp = B + (16 * s + 4 * lq + m) * ldb + li;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[t] = mfma_f32(frag[s][m], bp[16 * t], acc[t]);
+        }
+}
+
+template <int D, typename TG>
+__global__ __launch_bounds__(512, 2) void bwd_sprod_kernel(
     int T, int H, int units, int NC, int varlen, const int32_t *__restrict__ cu,
     const TG *__restrict__ dO, const float *__restrict__ wsH, const float *__restrict__ wsDH,
     const float *__restrict__ wsDl, const float *__restrict__ wsE, float *__restrict__ wsOS,
     float *__restrict__ wsW, float *__restrict__ wsKt, float *__restrict__ wsSc) {
     constexpr int LF = D + 4, NTC = D / 32;
+    // only the d x d matrix sits in LDS (the row operands are register
+    // fragments), so two workgroups share a CU
     __shared__ __attribute__((aligned(16))) float sB[D * LF];    // S, then dS'
-    __shared__ __attribute__((aligned(16))) float sA1[BC * LF];  // dO, then Delta
-    __shared__ __attribute__((aligned(16))) float sA2[BC * LF];  // dDelta
     __shared__ float sred[8];
     const int slot = blockIdx.x / H, h = blockIdx.x % H;
     long row0;
@@ -357,18 +386,21 @@ __global__ __launch_bounds__(512) void bwd_sprod_kernel(
     const int tr = wave & 3, tc0 = (wave >> 2) * NTC;
     const size_t ch = blockIdx.x;
     const float *Sm = wsH + ch * D * D, *DSm = wsDH + ch * D * D;
+    const int arow = 16 * tr + li;
+    const bool avalid = arow < n;
+    f32x4 fa[D / 16], fb[D / 16];
+    afrag_rows<D>(fa, dO + ((size_t)(row0 + (avalid ? arow : 0)) * H + h) * D, avalid, lq);
+    afrag_rows<D>(fb, wsE + (ch * BC + arow) * D, avalid, lq);
     for (int e = tid; e < D * D / 4; e += 512)
         put4(sB + (e / (D / 4)) * LF + (e % (D / 4)) * 4, *reinterpret_cast<const f32x4 *>(Sm + 4 * e));
-    load_rows<D>(sA1, LF, dO, row0, n, H, h, 0, D, tid, 512);
-    load_ws_rows<D>(sA2, LF, wsE + ch * BC * D, n, tid, 512);
     __syncthreads();
     // dO S and -dDelta S (64 x d_k)
     {
         f32x4 a[NTC], b[NTC];
         zero_n(a);
         zero_n(b);
-        mmn<D, NTC>(sA1 + 16 * tr * LF, LF, 1, sB + 16 * tc0, LF, 1, 16, a, lane);
-        mmn<D, NTC>(sA2 + 16 * tr * LF, LF, 1, sB + 16 * tc0, LF, 1, 16, b, lane);
+        mm_afrag<D, NTC>(fa, sB + 16 * tc0, LF, a, lane);
+        mm_afrag<D, NTC>(fb, sB + 16 * tc0, LF, b, lane);
 #pragma unroll
         for (int t = 0; t < NTC; ++t)
 #pragma unroll
@@ -380,6 +412,7 @@ __global__ __launch_bounds__(512) void bwd_sprod_kernel(
                 }
             }
     }
+    afrag_rows<D>(fa, wsDl + (ch * BC + arow) * D, avalid, lq);   // Delta rows
     __syncthreads();
     // dS' replaces S; <dS', S> on the way
     float dot = 0.f;
@@ -390,7 +423,6 @@ __global__ __launch_bounds__(512) void bwd_sprod_kernel(
         dot += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
         put4(at, x);
     }
-    load_ws_rows<D>(sA1, LF, wsDl + ch * BC * D, n, tid, 512);
     dot = sum16(dot);
     dot += __shfl_xor(dot, 16);
     dot += __shfl_xor(dot, 32);
@@ -405,7 +437,7 @@ __global__ __launch_bounds__(512) void bwd_sprod_kernel(
     {
         f32x4 a[NTC];
         zero_n(a);
-        mmn<D, NTC>(sA1 + 16 * tr * LF, LF, 1, sB + 16 * tc0, LF, 1, 16, a, lane);
+        mm_afrag<D, NTC>(fa, sB + 16 * tc0, LF, a, lane);
 #pragma unroll
         for (int t = 0; t < NTC; ++t)
 #pragma unroll
