@@ -449,8 +449,82 @@ __global__ __launch_bounds__(512, 2) void bwd_sprod_kernel(
 }
 
 // ---------------------------------------------------------------- 5. grads
+// Products of two row-major operands, A B^T, with both read by rows: lane
+// (li, lq) of a 16-row tile supplies the W consecutive elements
+// row[4 W s + W lq .. + W - 1] for s < K / (4 W), and MFMA step (s, m) takes
+// element m of them, so the k order is the same for every operand whatever
+// its source (registers loaded straight from global memory, 16 bytes per
+// lane, or LDS rows).
+// W elements of X per lane and group: 16 bytes of the input tensors' type.
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+template <typename X, int W> struct RowVec;
+template <> struct RowVec<bf16, 4> { typedef bf16x4 type; };
+template <> struct RowVec<bf16, 8> { typedef bf16x8 type; };
+template <> struct RowVec<float, 4> { typedef f32x4 type; };
+template <> struct RowVec<float, 8> { typedef f32x8 type; };
+template <typename X> constexpr int row_w() { return sizeof(X) == 2 ? 8 : 4; }
+
+// W fp32 elements of an LDS row (16-byte aligned)
+template <int W> __device__ __forceinline__ auto lds_w(const float *p) {
+    if constexpr (W == 4) {
+        return *reinterpret_cast<const f32x4 *>(p);
+    } else {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+        return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+}
+// Fragments of row r of a chunk of a [tokens, H, D] tensor (zero past n);
+// src points at the chunk's row 0, rows are `stride` elements apart.
+template <int D, int W, typename X>
+__device__ __forceinline__ void row_frags(typename RowVec<X, W>::type (&f)[D / (4 * W)],
+                                          const X *src, int stride, int r, int n, int lq) {
+    typedef typename RowVec<X, W>::type VT;
+    const X *p = src + (r < n ? r : 0) * stride + W * lq;
+#pragma unroll
+    for (int s = 0; s < D / (4 * W); ++s) {
+        f[s] = VT{};
+        if (r < n) f[s] = *reinterpret_cast<const VT *>(p + 4 * W * s);
+    }
+}
+// acc[t] += sum_k A(li, k) B_t(li, k) over k < K: fa(s) and fb(t, s) give
+// the lane's W elements of group s.
+// The operands of group s + 1 are read before the products of group s (they
+// stay in their source type until an MFMA takes them), and no instruction
+// moves across groups, which bounds the live registers to two groups'
+// operands.
+template <int K, int W, int NT, typename FA, typename FB>
+__device__ __forceinline__ void mm_rows(FA fa, FB fb, f32x4 (&acc)[NT]) {
+    constexpr int NS = K / (4 * W);
+    auto a = fa(0);
+    decltype(fb(0, 0)) b[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) b[t] = fb(t, 0);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        decltype(a) an = a;
+        decltype(fb(0, 0)) bn[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) bn[t] = b[t];
+        if (s + 1 < NS) {
+            an = fa(s + 1);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) bn[t] = fb(t, s + 1);
+        }
+#pragma unroll
+        for (int m = 0; m < W; ++m)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[t] = mfma_f32(to_f32(a[m]), to_f32(b[t][m]), acc[t]);
+        a = an;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) b[t] = bn[t];
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <int D, typename TI, typename TG>
-__global__ __launch_bounds__(512) void bwd_grads_kernel(
+__global__ __launch_bounds__(512, 4) void bwd_grads_kernel(
     int T, int H, int units, int NC, int varlen, const int32_t *__restrict__ cu,
     const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v,
     const TG *__restrict__ dO, const float *__restrict__ la, const float *__restrict__ beta,
@@ -460,17 +534,27 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
     TG *__restrict__ dk, TG *__restrict__ dv, float *__restrict__ dla,
     float *__restrict__ dbeta) {
     constexpr int LI = ldx<TI, D>(), LF = D + 4, NTC = D / 32;
-    __shared__ __attribute__((aligned(16))) TI sK[BC * LI];
-    __shared__ __attribute__((aligned(16))) TI sQ[BC * LI];
-    __shared__ __attribute__((aligned(16))) float sT[BC * LDN];
-    __shared__ __attribute__((aligned(16))) float sP[BC * LDN];   // P, then T^T dT
-    __shared__ __attribute__((aligned(16))) float sN[BC * LDN];   // dQK = dP o G
-    __shared__ __attribute__((aligned(16))) float sX[BC * LF];    // dO, V, dT
-    __shared__ __attribute__((aligned(16))) float sY[BC * LF];    // Delta, dDelta, dW, dG
+    constexpr int NN = BC * LDN;                                  // a 64 x 64 fp32 block
+    constexpr int NB = BC * LF > 2 * NN ? BC * LF : 2 * NN;
+    // one group width for every product, so that the summation order (and
+    // with it every fp32 result) is the same whichever type dO has
+    constexpr int WI = row_w<TI>();
+    static_assert(BC * LI * sizeof(TI) <= NN * sizeof(float), "a K or Q tile fits a 64 x 64 block");
+    // 73 KB of LDS, so two workgroups share a CU; operands read only by rows
+    // (dO, V, K in the first products) come from global memory as fragments.
+    //   sN   dQK = dP o G, from the first product to the last
+    //   sT   T, then K
+    //   sB   Delta, dDelta, dW (64 x d), then dT | M, then dG | Q
+    __shared__ __attribute__((aligned(16))) float sN[NN];
+    __shared__ __attribute__((aligned(16))) float sT[NN];
+    __shared__ __attribute__((aligned(16))) float sB[NB];
     __shared__ float sg[4][BC];
     // per-wave partial row sums of dbeta and dg, added in a fixed order at the
     // end (no atomics: the result does not depend on wave timing)
     __shared__ float sdb[8][BC], sdg[8][BC];
+    float *const sB1 = sB + NN;
+    TI *const sK = reinterpret_cast<TI *>(sT);
+    TI *const sQ = reinterpret_cast<TI *>(sB1);
     const int slot = blockIdx.x / H, h = blockIdx.x % H;
     long row0;
     int n;
@@ -480,40 +564,37 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
     const int tr = wave & 3, tc0 = (wave >> 2) * NTC;   // 64 x D tiles: row tr, columns tc0..
     const int ty = wave & 3, tx0 = 2 * (wave >> 2);     // 64 x 64 tiles: row ty, columns tx0, tx0+1
     const size_t ch = blockIdx.x;
-    // one wave's contribution: distinct rows per lane within an instruction
+    // chunk origins of the [tokens, H, D] tensors; rows are HD elements apart
+    const int HD = H * D;
+    const size_t gb = (size_t)row0 * HD + (size_t)h * D;
+    const TI *const qc = q + gb, *const kc = k + gb, *const vc = v + gb;
+    const TG *const dOc = dO + gb;
+    TG *const dqc = dq + gb, *const dkc = dk + gb, *const dvc = dv + gb;
+    const float *const Pc = wsP + ch * BC * BC;
 #define ADDG(row, x) (sdg[wave][(row)] += (x))
 #define ADDB(row, x) (sdb[wave][(row)] += (x))
     for (int e = tid; e < 8 * BC; e += 512) {
         sdb[e / BC][e % BC] = 0.f;
         sdg[e / BC][e % BC] = 0.f;
     }
-    // this lane's elements of dO S and Delta dS' (used last; loaded first)
-    f32x4 osv[NTC], ktv[NTC];
-    {
-        const float *OS = wsOS + ch * BC * D, *Kt = wsKt + ch * BC * D;
-#pragma unroll
-        for (int t = 0; t < NTC; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-                osv[t][j] = r < n ? OS[(size_t)r * D + col] : 0.f;
-                ktv[t][j] = r < n ? Kt[(size_t)r * D + col] : 0.f;
-            }
-    }
-    load_rows<D>(sK, LI, k, row0, n, H, h, 0, D, tid, 512);
-    load_rows<D>(sQ, LI, q, row0, n, H, h, 0, D, tid, 512);
+    typename RowVec<TG, WI>::type fo[D / (4 * WI)];
+    row_frags<D, WI>(fo, dOc, HD, 16 * ty + li, n, lq);
+    load_ws_rows<D>(sB, LF, wsDl + ch * BC * D, n, tid, 512);   // Delta
     load_nn(sT, wsT + ch * BC * BC, tid, 512);
-    load_nn(sP, wsP + ch * BC * BC, tid, 512);
-    load_rows<D>(sX, LF, dO, row0, n, H, h, 0, D, tid, 512);
-    load_ws_rows<D>(sY, LF, wsDl + ch * BC * D, n, tid, 512);
+    Prefetch<D, float> pf;
+    pf.fetch(wsE + ch * BC * D, D, n, tid);                     // dDelta, for the next stage
     if (wave == 0) chunk_gates(sg, la, beta, row0, n, H, h, lane);
     __syncthreads();
 
     // dP = tril(dO Delta^T); dQK = dP o G; dg += rowsum(dP o P) - colsum(dP o P)
-    f32x4 dqk[2];
     f32x4 a2[2];
     zero_n(a2);
-    mmn<D, 2>(sX + 16 * ty * LF, LF, 1, sY + 16 * tx0 * LF, 1, LF, 16 * LF, a2, lane);
+    {
+        const float *pb = sB + (16 * tx0 + li) * LF + WI * lq;
+        mm_rows<D, WI, 2>([&](int s) { return fo[s]; },
+                          [&](int t, int s) { return lds_w<WI>(pb + 16 * t * LF + 4 * WI * s); },
+                          a2);
+    }
     for (int x = 0; x < 2; ++x) {
         const int tx = tx0 + x;
         const f32x4 a = a2[x];
@@ -523,8 +604,8 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
             const int r = 16 * ty + 4 * lq + j, i = 16 * tx + li;
             const float dp = i <= r ? a[j] : 0.f;
             const float gm = i <= r ? __expf(sg[0][r] - sg[0][i]) : 0.f;
-            dqk[x][j] = dp * gm;
-            const float m = dp * sP[r * LDN + i];
+            sN[r * LDN + i] = dp * gm;
+            const float m = dp * Pc[r * BC + i];
             const float rs = sum16(m);
             if (li == 0) ADDG(r, rs);
             col += m;
@@ -533,23 +614,26 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
         col += __shfl_xor(col, 32);
         if (lq == 0) ADDG(16 * tx + li, -col);
     }
-    __syncthreads();
-    for (int x = 0; x < 2; ++x)
+    typename RowVec<TI, WI>::type fb[2][D / (4 * WI)];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            sN[(16 * ty + 4 * lq + j) * LDN + 16 * (tx0 + x) + li] = dqk[x][j];
-    load_ws_rows<D>(sY, LF, wsE + ch * BC * D, n, tid, 512);
-    load_rows<D>(sX, LF, v, row0, n, H, h, 0, D, tid, 512);
+    for (int x = 0; x < 2; ++x) row_frags<D, WI>(fb[x], vc, HD, 16 * (tx0 + x) + li, n, lq);
+    __syncthreads();   // Delta no longer read
+    pf.commit(sB, LF, tid);
+    pf.fetch(wsW + ch * BC * D, D, n, tid);                     // dW, for the next stage
     __syncthreads();
 
     // dT = dDelta (beta V)^T + ...; dV = diag(beta) T^T dDelta; dbeta += rows(T^T dDelta . V)
     f32x4 dt[2];
     zero_n(dt);
-    mmn<D, 2>(sY + 16 * ty * LF, LF, 1, sX + 16 * tx0 * LF, 1, LF, 16 * LF, dt, lane);
+    {
+        const float *pa = sB + (16 * ty + li) * LF + WI * lq;
+        mm_rows<D, WI, 2>([&](int s) { return lds_w<WI>(pa + 4 * WI * s); },
+                          [&](int t, int s) { return fb[t][s]; }, dt);
+    }
     for (int x = 0; x < 2; ++x) dt[x] = dt[x] * sg[2][16 * (tx0 + x) + li];
     f32x4 an[NTC];
     zero_n(an);
-    mmn<BC, NTC>(sT + 16 * tr, 1, LDN, sY + 16 * tc0, LF, 1, 16, an, lane);
+    mmn<BC, NTC>(sT + 16 * tr, 1, LDN, sB + 16 * tc0, LF, 1, 16, an, lane);
 #pragma unroll
     for (int t = 0; t < NTC; ++t) {
         const int tc = tc0 + t;
@@ -557,25 +641,41 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
-            if (r < n) dv[((size_t)(row0 + r) * H + h) * D + col] = cvt<TG>(sg[2][r] * a[j]);
-            const float rs = sum16(a[j] * sX[r * LF + col]);
+            float vv = 0.f;
+            if (r < n) {
+                dvc[r * HD + col] = cvt<TG>(sg[2][r] * a[j]);
+                vv = to_f32(vc[r * HD + col]);
+            }
+            const float rs = sum16(a[j] * vv);
             if (li == 0) ADDB(r, rs);
         }
     }
-    __syncthreads();
-    load_ws_rows<D>(sY, LF, wsW + ch * BC * D, n, tid, 512);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) row_frags<D, WI>(fb[x], kc, HD, 16 * (tx0 + x) + li, n, lq);
+    typename RowVec<TI, WI>::type fk[D / (4 * WI)];
+    row_frags<D, WI>(fk, kc, HD, 16 * ty + li, n, lq);
+    __syncthreads();   // dDelta no longer read
+    pf.commit(sB, LF, tid);
     __syncthreads();
 
-    // dT += dW (beta e^g K)^T; dK = diag(beta e^g) T^T dW + ...
+    // dT += dW (beta e^g K)^T; dK = diag(beta e^g) T^T dW + ...; K K^T for dA below
     zero_n(a2);
-    mmn<D, 2>(sY + 16 * ty * LF, LF, 1, sK + 16 * tx0 * LI, 1, LI, 16 * LI, a2, lane);
+    f32x4 kk2[2];
+    zero_n(kk2);
+    {
+        const float *pa = sB + (16 * ty + li) * LF + WI * lq;
+        mm_rows<D, WI, 2>([&](int s) { return lds_w<WI>(pa + 4 * WI * s); },
+                          [&](int t, int s) { return fb[t][s]; }, a2);
+        mm_rows<D, WI, 2>([&](int s) { return fk[s]; },
+                          [&](int t, int s) { return fb[t][s]; }, kk2);
+    }
     for (int x = 0; x < 2; ++x) {
         const int i = 16 * (tx0 + x) + li;
         dt[x] = dt[x] + a2[x] * (sg[2][i] * sg[1][i]);
     }
     f32x4 dka[NTC];
     zero_n(an);
-    mmn<BC, NTC>(sT + 16 * tr, 1, LDN, sY + 16 * tc0, LF, 1, 16, an, lane);
+    mmn<BC, NTC>(sT + 16 * tr, 1, LDN, sB + 16 * tc0, LF, 1, 16, an, lane);
 #pragma unroll
     for (int t = 0; t < NTC; ++t) {
         const int tc = tc0 + t;
@@ -585,33 +685,36 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
             const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
             const float be = sg[2][r] * sg[1][r];
             dka[t][j] = be * a[j];
-            const float rw = sum16(a[j] * to_f32(sK[r * LI + col]));
+            const float kv = r < n ? to_f32(kc[r * HD + col]) : 0.f;
+            const float rw = sum16(a[j] * kv);
             if (li == 0) {
                 ADDB(r, sg[1][r] * rw);
                 ADDG(r, be * rw);
             }
         }
     }
-    __syncthreads();
+    __syncthreads();   // dW no longer read
+#pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            sX[(16 * ty + 4 * lq + j) * LDN + 16 * (tx0 + x) + li] = dt[x][j];
+            sB[(16 * ty + 4 * lq + j) * LDN + 16 * (tx0 + x) + li] = dt[x][j];
     __syncthreads();
-    // M = T^T dT (into sP)
+    // M = T^T dT (into sB1)
     zero_n(a2);
-    mmn<BC, 2>(sT + 16 * ty, 1, LDN, sX + 16 * tx0, LDN, 1, 16, a2, lane);
+    mmn<BC, 2>(sT + 16 * ty, 1, LDN, sB + 16 * tx0, LDN, 1, 16, a2, lane);
     for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sP[(16 * ty + 4 * lq + j) * LDN + 16 * (tx0 + x) + li] = a2[x][j];
-    __syncthreads();
-    // dA = -strict(M T^T); dG = dA o beta_r G (into sY);
+        for (int j = 0; j < 4; ++j)
+            sB1[(16 * ty + 4 * lq + j) * LDN + 16 * (tx0 + x) + li] = a2[x][j];
+    Prefetch<D, TI> pk, pq;
+    pk.fetch(kc, HD, n, tid);
+    pq.fetch(qc, HD, n, tid);
+    __syncthreads();   // M complete; dT no longer read
+    // dA = -strict(M T^T); dG = dA o beta_r G (into sB, over dT);
     // dbeta += rowsum(dA o G o K K^T); dg += rowsum(dA o A) - colsum(dA o A)
-    f32x4 kk2[2];
     zero_n(a2);
-    zero_n(kk2);
-    mmn<BC, 2>(sP + 16 * ty * LDN, LDN, 1, sT + 16 * tx0 * LDN, 1, LDN, 16 * LDN, a2, lane);
-    mmn<D, 2>(sK + 16 * ty * LI, LI, 1, sK + 16 * tx0 * LI, 1, LI, 16 * LI, kk2, lane);
+    mmn<BC, 2>(sB1 + 16 * ty * LDN, LDN, 1, sT + 16 * tx0 * LDN, 1, LDN, 16 * LDN, a2, lane);
     for (int x = 0; x < 2; ++x) {
         const int tx = tx0 + x;
         const f32x4 a = a2[x], kk = kk2[x];
@@ -622,7 +725,7 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
             const float gm = i < r ? __expf(sg[0][r] - sg[0][i]) : 0.f;
             const float da = i < r ? -a[j] : 0.f;
             const float br = sg[2][r];
-            sY[r * LDN + i] = da * br * gm;
+            sB[r * LDN + i] = da * br * gm;
             const float t1 = da * gm * kk[j];
             const float rb = sum16(t1);
             const float m = br * t1;   // dA o A
@@ -637,8 +740,50 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
         col += __shfl_xor(col, 32);
         if (lq == 0) ADDG(16 * tx + li, -col);
     }
+    // this lane's elements of dO S and Delta dS'
+    f32x4 osv[NTC], ktv[NTC];
+    {
+        const float *OS = wsOS + ch * BC * D, *Kt = wsKt + ch * BC * D;
+#pragma unroll
+        for (int t = 0; t < NTC; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
+                osv[t][j] = r < n ? OS[(size_t)r * D + col] : 0.f;
+                ktv[t][j] = r < n ? Kt[(size_t)r * D + col] : 0.f;
+            }
+    }
+    __syncthreads();   // T and M no longer read
+    pk.commit(sK, LI, tid);
+    pq.commit(sQ, LI, tid);
     __syncthreads();
 
+    // dK = dQK^T Q + diag(e^{g_n - g}) Delta dS' + diag(beta e^g) T^T dW + dG K + dG^T K
+    // dg -= s_r, dg_{n-1} += sum_r s_r with s = rows(Delta dS' . K~)
+    float ssum = 0.f;
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) {
+        const int tc = tc0 + t;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
+            const float kt = sg[3][r] * ktv[t][j];
+            dka[t][j] += kt;
+            const float s = sum16(kt * to_f32(sK[r * LI + col]));
+            if (li == 0) ADDG(r, -s);
+            ssum += s;   // the same in all 16 lanes of the group
+        }
+    }
+    mmn<BC, NTC>(sN + 16 * tr, 1, LDN, sQ + 16 * tc0, LI, 1, 16, dka, lane);
+    mmn<BC, NTC>(sB + 16 * tr * LDN, LDN, 1, sK + 16 * tc0, LI, 1, 16, dka, lane);
+    mmn<BC, NTC>(sB + 16 * tr, 1, LDN, sK + 16 * tc0, LI, 1, 16, dka, lane);
+#pragma unroll
+    for (int t = 0; t < NTC; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
+            if (r < n) dkc[r * HD + col] = cvt<TG>(dka[t][j]);
+        }
     // dQ = diag(e^g) dO S + dQK K;  dg += e^g rows(dO S . Q)
 #pragma unroll
     for (int t = 0; t < NTC; ++t) {
@@ -657,33 +802,7 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-            if (r < n) dq[((size_t)(row0 + r) * H + h) * D + col] = cvt<TG>(an[t][j]);
-        }
-    // dK = dQK^T Q + diag(e^{g_n - g}) Delta dS' + diag(beta e^g) T^T dW + dG K + dG^T K
-    // dg -= s_r, dg_{n-1} += sum_r s_r with s = rows(Delta dS' . K~)
-    float ssum = 0.f;
-#pragma unroll
-    for (int t = 0; t < NTC; ++t) {
-        const int tc = tc0 + t;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
-            const float kt = sg[3][r] * ktv[t][j];
-            dka[t][j] += kt;
-            const float s = sum16(kt * to_f32(sK[r * LI + col]));
-            if (li == 0) ADDG(r, -s);
-            ssum += s;   // the same in all 16 lanes of the group
-        }
-    }
-    mmn<BC, NTC>(sN + 16 * tr, 1, LDN, sQ + 16 * tc0, LI, 1, 16, dka, lane);
-    mmn<BC, NTC>(sY + 16 * tr * LDN, LDN, 1, sK + 16 * tc0, LI, 1, 16, dka, lane);
-    mmn<BC, NTC>(sY + 16 * tr, 1, LDN, sK + 16 * tc0, LI, 1, 16, dka, lane);
-#pragma unroll
-    for (int t = 0; t < NTC; ++t)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-            if (r < n) dk[((size_t)(row0 + r) * H + h) * D + col] = cvt<TG>(dka[t][j]);
+            if (r < n) dqc[r * HD + col] = cvt<TG>(an[t][j]);
         }
     ssum += __shfl_xor(ssum, 16);
     ssum += __shfl_xor(ssum, 32);
