@@ -300,29 +300,23 @@ __device__ __forceinline__ f32x4 ld4f(const float *p) { return *reinterpret_cast
 // times e^{G_ref - G_i} (>= 1): when the block's span max_c (G_ref - G_last)
 // is at most 60 both factors are normal floats and the block is one MFMA
 // product; otherwise it is formed term by term (exponentials of r >= i only).
-template <int D, typename TX, typename TY>
-__device__ __forceinline__ f32x4 diag_block(const TX *X, int lx, const TY *Y, int ly,
-                                            const float *G, int lg, int b, int lane) {
-    const int li = lane & 15, lq = lane >> 4;
+// Decay span max_c (G_ref - G_last) of diagonal block b (all lanes get it).
+template <int D>
+__device__ __forceinline__ float diag_span(const float *G, int lg, int b, int lane) {
     const float *gref = b > 0 ? G + (16 * b - 1) * lg : nullptr;
     const float *glast = G + (16 * b + 15) * lg;
     float span = 0.f;
     for (int c = lane; c < D; c += 64) span = fmaxf(span, (gref ? gref[c] : 0.f) - glast[c]);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) span = fmaxf(span, __shfl_xor(span, off));
+    return span;
+}
+// The same block term by term (exponentials of r >= i only), for any span.
+template <int D, typename TX, typename TY>
+__device__ __forceinline__ f32x4 diag_terms(const TX *X, int lx, const TY *Y, int ly,
+                                            const float *G, int lg, int b, int lane) {
+    const int li = lane & 15, lq = lane >> 4;
     f32x4 acc = zero4();
-    if (span <= 60.f) {
-        const int rw = 16 * b + li;
-#pragma unroll 4
-        for (int c0 = 0; c0 < D; c0 += 4) {
-            const int c = c0 + lq;
-            const float gr = gref ? gref[c] : 0.f, gw = G[rw * lg + c];
-            const float a = to_f32(X[rw * lx + c]) * __expf(gw - gr);
-            const float y = to_f32(Y[rw * ly + c]) * __expf(gr - gw);
-            acc = mfma_f32(a, y, acc);
-        }
-        return acc;
-    }
     const int i = 16 * b + li;
     for (int c = 0; c < D; c += 4) {
         const f32x4 gi = *reinterpret_cast<const f32x4 *>(G + i * lg + c);
@@ -335,6 +329,24 @@ __device__ __forceinline__ f32x4 diag_block(const TX *X, int lx, const TY *Y, in
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[j] += xr[e] * yi[e] * __expf(fminf(gr[e] - gi[e], 0.f));
         }
+    }
+    return acc;
+}
+template <int D, typename TX, typename TY>
+__device__ __forceinline__ f32x4 diag_block(const TX *X, int lx, const TY *Y, int ly,
+                                            const float *G, int lg, int b, int lane) {
+    const int li = lane & 15, lq = lane >> 4;
+    if (diag_span<D>(G, lg, b, lane) > 60.f) return diag_terms<D>(X, lx, Y, ly, G, lg, b, lane);
+    const float *gref = b > 0 ? G + (16 * b - 1) * lg : nullptr;
+    f32x4 acc = zero4();
+    const int rw = 16 * b + li;
+#pragma unroll 4
+    for (int c0 = 0; c0 < D; c0 += 4) {
+        const int c = c0 + lq;
+        const float gr = gref ? gref[c] : 0.f, gw = G[rw * lg + c];
+        const float a = to_f32(X[rw * lx + c]) * __expf(gw - gr);
+        const float y = to_f32(Y[rw * ly + c]) * __expf(gr - gw);
+        acc = mfma_f32(a, y, acc);
     }
     return acc;
 }

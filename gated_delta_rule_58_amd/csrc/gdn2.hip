@@ -101,42 +101,61 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
     }
     // The four channel-weighted products, 16 x 16 blocks (br, bi), bi <= br:
     // matrix mx = 0 A_e (rows K, columns E), 1 A_k (K, K), 2 P_e (Q, E),
-    // 3 P_k (Q, K).  40 tasks, 5 per wave: the 16 diagonal blocks by
-    // diag_block, the 24 blocks below on MFMA from operands rescaled to the
-    // last token of block br - 1 (every factor e^{<= 0}).
+    // 3 P_k (Q, K).  40 tasks, 5 per wave (2 diagonal, 3 below): waves 0-3
+    // the E-column matrices, waves 4-7 the K-column ones.  Each block is one
+    // MFMA product of operands rescaled to the prefix just before block br
+    // (the last token of block br - 1, or 0): every factor is e^{<= 0} below
+    // the diagonal, and on it too unless the block's decay span exceeds 60,
+    // when the block is formed term by term instead.  The wave's five
+    // chains run interleaved, one MFMA of each per channel step.
     f32x4 res[5];
+    {
+        const int half = wave >> 2, w4 = wave & 3;   // half 0: E columns, 1: K columns
+        int ra[5], rb[5], gro[5], mxs[5];
+        float gon[5];
+        bool terms[5];
 #pragma unroll
-    for (int s = 0; s < 5; ++s) {
-        const int task = wave + 8 * s;
-        const int mx = task / 10;
-        int blk = task % 10, br = 0;
-        while (blk > br) blk -= ++br;
-        const int bi = blk;
-        const TI *Xr = mx < 2 ? sK : sQ;
-        const bool colE = (mx & 1) == 0;
-        f32x4 acc = zero4();
-        if (bi < br) {
-            const float *gref = sG + (16 * br - 1) * LF;
-            const int ra = 16 * br + li, rb = 16 * bi + li;
-#pragma unroll 4
+        for (int s = 0; s < 5; ++s) {
+            const int e = w4 + 4 * s;   // 0..19 within the half
+            int blk = e % 10, br = 0;
+            while (blk > br) blk -= ++br;
+            mxs[s] = 2 * (e / 10) + half;
+            ra[s] = 16 * br + li;
+            rb[s] = 16 * blk + li;
+            gro[s] = br > 0 ? 16 * br - 1 : 0;
+            gon[s] = br > 0 ? 1.f : 0.f;   // reference prefix 0 for the first block
+            terms[s] = blk == br && diag_span<D>(sG, LF, br, lane) > 60.f;
+        }
+        auto chains = [&](const auto *Y, int ly) {
+#pragma unroll
+            for (int s = 0; s < 5; ++s) res[s] = zero4();
+#pragma unroll 2
             for (int c0 = 0; c0 < D; c0 += 4) {
                 const int c = c0 + lq;
-                const float gr = gref[c];
-                const float a = to_f32(Xr[ra * LI + c]) * __expf(sG[ra * LF + c] - gr);
-                const float y = colE ? sE[rb * LE + c] : to_f32(sK[rb * LI + c]);
-                acc = mfma_f32(a, y * __expf(gr - sG[rb * LF + c]), acc);
+#pragma unroll
+                for (int s = 0; s < 5; ++s) {
+                    const float gr = gon[s] * sG[gro[s] * LF + c];
+                    const TI *Xr = mxs[s] < 2 ? sK : sQ;
+                    const float a = to_f32(Xr[ra[s] * LI + c]) * __expf(sG[ra[s] * LF + c] - gr);
+                    const float y = to_f32(Y[rb[s] * ly + c]) * __expf(gr - sG[rb[s] * LF + c]);
+                    res[s] = mfma_f32(a, y, res[s]);
+                }
             }
-        } else {
-            acc = colE ? diag_block<D>(Xr, LI, sE, LE, sG, LF, br, lane)
-                       : diag_block<D>(Xr, LI, sK, LI, sG, LF, br, lane);
-        }
+#pragma unroll
+            for (int s = 0; s < 5; ++s)
+                if (terms[s])
+                    res[s] = diag_terms<D>(mxs[s] < 2 ? sK : sQ, LI, Y, ly, sG, LF, (ra[s] - li) / 16, lane);
+        };
+        if (half == 0) chains(static_cast<const float *>(sE), LE);
+        else chains(static_cast<const TI *>(sK), LI);
         // keep strict (A) or inclusive (P) lower entries
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * br + 4 * lq + j, i = 16 * bi + li;
-            if (mx < 2 ? i >= r : i > r) acc[j] = 0.f;
-        }
-        res[s] = acc;
+        for (int s = 0; s < 5; ++s)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = ra[s] - li + 4 * lq + j, i = rb[s];
+                if (mxs[s] < 2 ? i >= r : i > r) res[s][j] = 0.f;
+            }
     }
     __syncthreads();   // E consumed: A_e and A_k go over it
     for (int e = tid; e < 2 * BC * LDN; e += 512) sE[e] = 0.f;
@@ -147,9 +166,8 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < 5; ++s) {
-        const int task = wave + 8 * s;
-        const int mx = task / 10;
-        int blk = task % 10, br = 0;
+        const int e = (wave & 3) + 4 * s, mx = 2 * (e / 10) + (wave >> 2);
+        int blk = e % 10, br = 0;
         while (blk > br) blk -= ++br;
         float *dst = mx == 0 ? sAe : mx == 1 ? sAk : mx == 2 ? sPe : sPk;
 #pragma unroll
