@@ -43,7 +43,7 @@ template <int D, typename TI>
 __global__ __launch_bounds__(512) void gdn2_prep_kernel(
     int T, int H, int units, int NC, int varlen, const int32_t *__restrict__ cu,
     const TI *__restrict__ q, const TI *__restrict__ k, const float *__restrict__ la,
-    const float *__restrict__ erase, float *__restrict__ ws) {
+    const float *__restrict__ erase, float *__restrict__ ws, int nch) {
     constexpr int LI = ldx<TI, D>(), LF = D + 4, LE = D + 8;
     constexpr int NE = BC * LE > 2 * BC * LDN ? BC * LE : 2 * BC * LDN;   // E, then A_e | A_k
     __shared__ __attribute__((aligned(16))) TI sK[BC * LI];
@@ -54,19 +54,41 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
     __shared__ __attribute__((aligned(16))) float sPk[BC * LDN];
     __shared__ __attribute__((aligned(16))) float sTe[BC * LDN];
     float *sAe = sE, *sAk = sE + BC * LDN;
-    const int slot = blockIdx.x / H, h = blockIdx.x % H;
-    long row0;
-    int n;
-    if (!slot_chunk(slot, units, T, NC, varlen, cu, row0, n)) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, wave = tid >> 6;
+    // Persistent over the (chunk slot, head) pairs ci = blockIdx.x + j gridDim.x:
+    // the inputs of the next pair load into registers while this one is
+    // computed.
+    Prefetch<D, TI> pk, pq;
+    Prefetch<D, float> pg, pe;
+    auto next = [&](int c) {   // first pair >= c with a chunk (unused slots skipped), and fetch it
+        long r0;
+        int nv;
+        for (; c < nch; c += gridDim.x) {
+            if (!slot_chunk(c / H, units, T, NC, varlen, cu, r0, nv)) continue;
+            const size_t g0 = (size_t)r0 * H * D + (size_t)(c % H) * D;
+            pk.fetch(k + g0, (size_t)H * D, nv, tid);
+            pq.fetch(q + g0, (size_t)H * D, nv, tid);
+            pg.fetch(la + g0, (size_t)H * D, nv, tid);
+            pe.fetch(erase + g0, (size_t)H * D, nv, tid);
+            break;
+        }
+        return c;
+    };
+    for (int ci = next(blockIdx.x); ci < nch;) {
+    // the lane index passes through an empty asm statement each iteration, so
+    // the per-lane LDS addresses below are recomputed rather than hoisted out
+    // of the loop and kept live in registers across it
+    int lane = tid & 63;
+    asm volatile("" : "+v"(lane));
     const int li = lane & 15, lq = lane >> 4;
-    float *W = ws + (size_t)blockIdx.x * G2Ws<D>::total;
-    load_rows<D>(sK, LI, k, row0, n, H, h, 0, D, tid, 512);
-    load_rows<D>(sQ, LI, q, row0, n, H, h, 0, D, tid, 512);
-    load_rows<D>(sG, LF, la, row0, n, H, h, 0, D, tid, 512);
-    load_rows<D>(sE, LE, erase, row0, n, H, h, 0, D, tid, 512);
+    float *W = ws + (size_t)ci * G2Ws<D>::total;
+    pk.commit(sK, LI, tid);
+    pq.commit(sQ, LI, tid);
+    pg.commit(sG, LF, tid);
+    pe.commit(sE, LE, tid);
     for (int e = tid; e < BC * LDN; e += 512) sTe[e] = 0.f;
     __syncthreads();
+    const int cn = next(ci + gridDim.x);
     if (tid < D) {   // prefix over the chunk per channel (padded rows add 0)
         float g = 0.f;
         for (int r = 0; r < BC; ++r) {
@@ -235,6 +257,9 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
                     to_f32(sQ[r * LI + c]) * __expf(sG[r * LF + c]) - qh[t][j];
             }
     }
+    __syncthreads();   // every LDS operand consumed before the next pair's commit
+    ci = cn;
+    }
 }
 
 // ---------------------------------------------------------------- 2. fwd
@@ -370,8 +395,9 @@ hipError_t launch_gdn2_t(int units, int T, int H, const int32_t *cu, const void 
     const int NC = varlen ? 0 : (T + BC - 1) / BC;
     const size_t nch = (size_t)nslots * H;
     if (nch > 0)
-        hipLaunchKernelGGL((gdn2_prep_kernel<D, TI>), dim3((unsigned)nch), dim3(512), 0, st, T, H,
-                           units, NC, varlen, cu, (const TI *)q, (const TI *)k, la, erase, ws);
+        hipLaunchKernelGGL((gdn2_prep_kernel<D, TI>), dim3((unsigned)std::min<size_t>(nch, 256)),
+                           dim3(512), 0, st, T, H, units, NC, varlen, cu, (const TI *)q,
+                           (const TI *)k, la, erase, ws, (int)nch);
     hipLaunchKernelGGL((gdn2_fwd_kernel<D, TI, TO>), dim3((unsigned)((long)units * H * (D / 64))),
                        dim3(512), 0, st, T, H, NC, varlen, cu, (const TI *)v, write, S0, ws,
                        (TO *)o, S_T);
