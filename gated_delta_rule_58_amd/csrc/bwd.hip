@@ -76,9 +76,23 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(
         const bool isP = wave >= 4;
         const TI *Ar = (isP ? sQ : sK) + 16 * tr * LI;
         float *P = wsP + ch * BC * BC;
-        f32x4 g4[4];
+        f32x4 g4[4];   // all 4 tiles (upper ones unused)
         zero_n(g4);
-        mmn<D, 4>(Ar, LI, 1, sK, 1, LI, 16 * LI, g4, lane);   // all 4 tiles (upper ones unused)
+        if constexpr (sizeof(TI) == 2) {
+            // bf16 inputs: the products are exact in fp32, so the 16x16x32
+            // bf16 MFMA (fp32 accumulation) computes the same sums as fp32
+            // MFMA; row fragments of 8 consecutive k per lane group
+            const int li = lane & 15, lq = lane >> 4;
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Ar + li * LI + 32 * ks + 8 * lq);
+#pragma unroll
+                for (int tj = 0; tj < 4; ++tj)
+                    g4[tj] = mfma32(a, *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + li) * LI + 32 * ks + 8 * lq), g4[tj]);
+            }
+        } else {
+            mmn<D, 4>(Ar, LI, 1, sK, 1, LI, 16 * LI, g4, lane);
+        }
         for (int tj = 0; tj < 4; ++tj) {
             const f32x4 acc = g4[tj];
 #pragma unroll
@@ -666,8 +680,17 @@ __global__ __launch_bounds__(512, 4) void bwd_grads_kernel(
         const float *pa = sB + (16 * ty + li) * LF + WI * lq;
         mm_rows<D, WI, 2>([&](int s) { return lds_w<WI>(pa + 4 * WI * s); },
                           [&](int t, int s) { return fb[t][s]; }, a2);
-        mm_rows<D, WI, 2>([&](int s) { return fk[s]; },
-                          [&](int t, int s) { return fb[t][s]; }, kk2);
+        if constexpr (sizeof(TI) == 2) {
+            // K K^T of bf16 inputs: exact products, so one 16x16x32 bf16 MFMA
+            // per group (the fragments are already in its operand layout)
+#pragma unroll
+            for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) kk2[t] = mfma32(fk[s], fb[t][s], kk2[t]);
+        } else {
+            mm_rows<D, WI, 2>([&](int s) { return fk[s]; },
+                              [&](int t, int s) { return fb[t][s]; }, kk2);
+        }
     }
     for (int x = 0; x < 2; ++x) {
         const int i = 16 * (tx0 + x) + li;
