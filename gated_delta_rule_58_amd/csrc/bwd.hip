@@ -220,6 +220,153 @@ __global__ __launch_bounds__(512) void bwd_states_kernel(
     }
 }
 
+// The same launch for bf16 inputs.  K S^T and the state update have a bf16
+// operand (K), whose products with bf16 values are exact in fp32; the fp32
+// operand (S, Delta~) is written as three bf16 pieces hi + mid + lo that add
+// up to it exactly (split3), so 16x16x32 bf16 MFMAs over the three pieces
+// give the fp32 sums at 3 bf16 MFMAs per 8 fp32 ones.  T Z stays fp32.
+__device__ __forceinline__ void split3(float x, bf16 &h, bf16 &m, bf16 &l) {
+    h = (bf16)x;
+    const float r = x - (float)h;
+    m = (bf16)r;
+    l = (bf16)(r - (float)m);
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void bwd_states_x3_kernel(
+    int T, int H, int NC, int varlen, const int32_t *__restrict__ cu,
+    const bf16 *__restrict__ k, const bf16 *__restrict__ v, const float *__restrict__ la,
+    const float *__restrict__ beta, const float *__restrict__ S0, const float *__restrict__ wsT,
+    float *__restrict__ wsH, float *__restrict__ wsDl) {
+    constexpr int LI = D + 8, LT = BC + 8, NTC = D / 32, NSL = D / 64;
+    __shared__ __attribute__((aligned(16))) bf16 sK[BC * LI];        // K rows
+    __shared__ __attribute__((aligned(16))) bf16 sKT[D * LT];        // K^T rows (d_k x tokens)
+    __shared__ __attribute__((aligned(16))) bf16 sS3[3][BC * LI];    // S slice pieces, d_v rows x d_k
+    __shared__ __attribute__((aligned(16))) bf16 sD3[3][BC * LT];    // Delta~^T pieces, d_v rows x tokens
+    __shared__ __attribute__((aligned(16))) bf16 sV[BC * LT];        // V slice
+    __shared__ __attribute__((aligned(16))) float sT[BC * LDN];
+    __shared__ __attribute__((aligned(16))) float sZ[BC * LDN];
+    __shared__ float sg[4][BC];
+    const int uh = blockIdx.x / NSL, dv0 = 64 * (blockIdx.x % NSL);
+    const int u = uh / H, h = uh % H;
+    long start, L;
+    unit_span(u, T, varlen, cu, start, L);
+    const int N = (int)((L + BC - 1) / BC);
+    const int base = unit_base(u, NC, varlen, cu);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lq = lane >> 4;
+    const int tr = wave & 3, tc0 = (wave >> 2) * NTC;
+    const int ty = tr, tx0 = 2 * (wave >> 2);
+    f32x4 st[NTC];   // st[t][j] = S[dv0 + 16 tr + 4 lq + j][16 (tc0 + t) + li]
+#pragma unroll
+    for (int t = 0; t < NTC; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
+            st[t][j] = S0 ? S0[((size_t)uh * D + dv0 + row) * D + col] : 0.f;
+        }
+    Prefetch<D, bf16> pk;
+    Prefetch<64, bf16> pv;
+    Prefetch<BC, float> pt;
+    float gx = 0.f, gb = 0.f;
+    auto fetch = [&](int c) {
+        const long row0 = start + (long)c * BC;
+        const int n = (int)min((long)BC, L - (long)c * BC);
+        const size_t ch = (size_t)(base + c) * H + h;
+        pk.fetch(k + ((size_t)row0 * H + h) * D, (size_t)H * D, n, tid);
+        pv.fetch(v + ((size_t)row0 * H + h) * D + dv0, (size_t)H * D, n, tid);
+        pt.fetch(wsT + ch * BC * BC, BC, BC, tid);
+        if (wave == 0) gate_fetch(la, beta, row0, n, H, h, lane, gx, gb);
+    };
+    if (N > 0) fetch(0);
+    for (int c = 0; c < N; ++c) {
+        const size_t ch = (size_t)(base + c) * H + h;
+        const int n = (int)min((long)BC, L - (long)c * BC);
+        float *Hm = wsH + ch * D * D;
+        // the state entering chunk c: to the workspace, and as pieces to LDS
+#pragma unroll
+        for (int t = 0; t < NTC; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
+                Hm[(size_t)(dv0 + row) * D + col] = st[t][j];
+                bf16 a, b, e;
+                split3(st[t][j], a, b, e);
+                sS3[0][row * LI + col] = a;
+                sS3[1][row * LI + col] = b;
+                sS3[2][row * LI + col] = e;
+            }
+        pk.commit(sK, LI, tid);
+#pragma unroll
+        for (int i = 0; i < Prefetch<D, bf16>::NP; ++i) {   // and transposed
+            const int e = tid + 512 * i, r = e / (D / 8), c8 = (e % (D / 8)) * 8;
+            if (e < BC * D / 8)
+#pragma unroll
+                for (int m = 0; m < 8; ++m) sKT[(c8 + m) * LT + r] = pk.buf[i][m];
+        }
+        pv.commit(sV, LT, tid);
+        pt.commit(sT, LDN, tid);
+        if (wave == 0) gate_scan(sg, gx, gb, lane);
+        __syncthreads();
+        if (c + 1 < N) fetch(c + 1);   // next chunk's operands load during this one
+        // Z = diag(beta) (V - diag(e^g) K S^T), 64 tokens x 64 slice columns
+        {
+            f32x4 y[2];
+            zero_n(y);
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sK + (16 * ty + li) * LI + 32 * ks + 8 * lq);
+#pragma unroll
+                for (int x = 0; x < 2; ++x)
+#pragma unroll
+                    for (int p = 0; p < 3; ++p)
+                        y[x] = mfma32(a, *reinterpret_cast<const bf16x8 *>(
+                                             sS3[p] + (16 * (tx0 + x) + li) * LI + 32 * ks + 8 * lq), y[x]);
+            }
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * ty + 4 * lq + j, col = 16 * (tx0 + x) + li;
+                    sZ[r * LDN + col] = sg[2][r] * ((float)sV[r * LT + col] - sg[1][r] * y[x][j]);
+                }
+        }
+        __syncthreads();
+        // Delta = T Z (fp32); the state update uses diag(e^{g_n - g}) Delta
+        {
+            f32x4 d[2];
+            zero_n(d);
+            mmn<BC, 2>(sT + 16 * ty * LDN, LDN, 1, sZ + 16 * tx0, LDN, 1, 16, d, lane);
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * ty + 4 * lq + j, col = 16 * (tx0 + x) + li;
+                    if (r < n) wsDl[(ch * BC + r) * D + dv0 + col] = d[x][j];
+                    bf16 a, b, e;
+                    split3(d[x][j] * sg[3][r], a, b, e);
+                    sD3[0][col * LT + r] = a;
+                    sD3[1][col * LT + r] = b;
+                    sD3[2][col * LT + r] = e;
+                }
+        }
+        __syncthreads();
+        // S <- e^{g_n} S + (diag(e^{g_n - g}) Delta)^T K
+        const float egn = sg[1][BC - 1];
+#pragma unroll
+        for (int t = 0; t < NTC; ++t) st[t] = st[t] * egn;
+#pragma unroll
+        for (int ks = 0; ks < BC / 32; ++ks)
+#pragma unroll
+            for (int p = 0; p < 3; ++p) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sD3[p] + (16 * tr + li) * LT + 32 * ks + 8 * lq);
+#pragma unroll
+                for (int t = 0; t < NTC; ++t)
+                    st[t] = mfma32(a, *reinterpret_cast<const bf16x8 *>(
+                                          sKT + (16 * (tc0 + t) + li) * LT + 32 * ks + 8 * lq), st[t]);
+            }
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------- 3. dstates
 template <int D, typename TI, typename TG>
 __global__ __launch_bounds__(512) void bwd_dstates_kernel(
@@ -881,9 +1028,14 @@ hipError_t launch_bwd_t(int units, int T, int H, const int32_t *cu, const void *
     if (nch > 0)
         hipLaunchKernelGGL((bwd_prep_kernel<D, TI>), dim3((unsigned)nch), dim3(512), 0, st, T, H,
                            units, NC, varlen, cu, qi, ki, la, beta, wsT, wsP);
-    if (nch > 0)
-        hipLaunchKernelGGL((bwd_states_kernel<D, TI>), dim3(seq_grid), dim3(512), 0, st, T, H, NC,
-                           varlen, cu, ki, vi, la, beta, S0, wsT, wsH, wsDl);
+    if (nch > 0) {
+        if constexpr (sizeof(TI) == 2)
+            hipLaunchKernelGGL((bwd_states_x3_kernel<D>), dim3(seq_grid), dim3(512), 0, st, T, H,
+                               NC, varlen, cu, ki, vi, la, beta, S0, wsT, wsH, wsDl);
+        else
+            hipLaunchKernelGGL((bwd_states_kernel<D, TI>), dim3(seq_grid), dim3(512), 0, st, T, H,
+                               NC, varlen, cu, ki, vi, la, beta, S0, wsT, wsH, wsDl);
+    }
     hipLaunchKernelGGL((bwd_dstates_kernel<D, TI, TG>), dim3(seq_grid), dim3(512), 0, st, T, H,
                        NC, varlen, cu, qi, ki, dOg, la, beta, dST, wsT, wsP, wsDH, wsE, dS0);
     if (nch > 0) {
