@@ -497,6 +497,172 @@ __global__ __launch_bounds__(512) void bwd_dstates_kernel(
     }
 }
 
+// The same launch for bf16 inputs: K dS'^T and F^T K on bf16 MFMA over three
+// exact bf16 pieces of their fp32 operand (as in bwd_states_x3_kernel);
+// P^T dO, T^T dDelta and (e^g dO)^T Q stay fp32.  dDelta goes over the K
+// rows once those are consumed, and the pieces of F over those of dS'.
+template <int D, typename TG>
+__global__ __launch_bounds__(512) void bwd_dstates_x3_kernel(
+    int T, int H, int NC, int varlen, const int32_t *__restrict__ cu,
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const TG *__restrict__ dO,
+    const float *__restrict__ la, const float *__restrict__ beta, const float *__restrict__ dST,
+    const float *__restrict__ wsT, const float *__restrict__ wsP, float *__restrict__ wsDH,
+    float *__restrict__ wsE, float *__restrict__ dS0) {
+    constexpr int LI = D + 8, LT = BC + 8, NTC = D / 32, NSL = D / 64;
+    constexpr int NKE = BC * LI > 2 * BC * LDN ? BC * LI : 2 * BC * LDN;   // bf16 elements
+    static_assert(LI >= LT, "a piece of F^T fits a piece of dS'");
+    __shared__ __attribute__((aligned(16))) bf16 sKE[NKE];
+    __shared__ __attribute__((aligned(16))) bf16 sKT[D * LT];        // K^T rows (d_k x tokens)
+    __shared__ __attribute__((aligned(16))) bf16 sQ[BC * LI];        // Q rows
+    __shared__ __attribute__((aligned(16))) bf16 sG3[3][BC * LI];    // dS' slice pieces, then F^T pieces
+    __shared__ __attribute__((aligned(16))) float sP[BC * LDN];
+    __shared__ __attribute__((aligned(16))) float sT[BC * LDN];
+    __shared__ __attribute__((aligned(16))) float sO[BC * LDN];      // dO slice, then e^g dO
+    __shared__ float sg[4][BC];
+    bf16 *const sK = sKE;                                // K rows, then
+    float *const sE = reinterpret_cast<float *>(sKE);    // dDelta
+    const int uh = blockIdx.x / NSL, dv0 = 64 * (blockIdx.x % NSL);
+    const int u = uh / H, h = uh % H;
+    long start, L;
+    unit_span(u, T, varlen, cu, start, L);
+    const int N = (int)((L + BC - 1) / BC);
+    const int base = unit_base(u, NC, varlen, cu);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lq = lane >> 4;
+    const int tr = wave & 3, tc0 = (wave >> 2) * NTC;
+    const int ty = tr, tx0 = 2 * (wave >> 2);
+    f32x4 st[NTC];   // st[t][j] = dS'[dv0 + 16 tr + 4 lq + j][16 (tc0 + t) + li]
+#pragma unroll
+    for (int t = 0; t < NTC; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
+            st[t][j] = dST ? dST[((size_t)uh * D + dv0 + row) * D + col] : 0.f;
+        }
+    Prefetch<D, bf16> pk, pq;
+    Prefetch<64, TG> po;
+    Prefetch<BC, float> pp, pt;
+    float gx = 0.f, gb = 0.f;
+    auto fetch = [&](int c) {
+        const long row0 = start + (long)c * BC;
+        const int n = (int)min((long)BC, L - (long)c * BC);
+        const size_t ch = (size_t)(base + c) * H + h;
+        pk.fetch(k + ((size_t)row0 * H + h) * D, (size_t)H * D, n, tid);
+        pq.fetch(q + ((size_t)row0 * H + h) * D, (size_t)H * D, n, tid);
+        po.fetch(dO + ((size_t)row0 * H + h) * D + dv0, (size_t)H * D, n, tid);
+        pp.fetch(wsP + ch * BC * BC, BC, BC, tid);
+        pt.fetch(wsT + ch * BC * BC, BC, BC, tid);
+        if (wave == 0) gate_fetch(la, beta, row0, n, H, h, lane, gx, gb);
+    };
+    if (N > 0) fetch(N - 1);
+    for (int c = N - 1; c >= 0; --c) {
+        const size_t ch = (size_t)(base + c) * H + h;
+        const int n = (int)min((long)BC, L - (long)c * BC);
+        float *DHm = wsDH + ch * D * D;
+        // gradient of the state leaving chunk c: to the workspace, and as pieces
+#pragma unroll
+        for (int t = 0; t < NTC; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
+                DHm[(size_t)(dv0 + row) * D + col] = st[t][j];
+                bf16 a, b, e;
+                split3(st[t][j], a, b, e);
+                sG3[0][row * LI + col] = a;
+                sG3[1][row * LI + col] = b;
+                sG3[2][row * LI + col] = e;
+            }
+        pk.commit(sK, LI, tid);
+#pragma unroll
+        for (int i = 0; i < Prefetch<D, bf16>::NP; ++i) {   // and transposed
+            const int e = tid + 512 * i, r = e / (D / 8), c8 = (e % (D / 8)) * 8;
+            if (e < BC * D / 8)
+#pragma unroll
+                for (int m = 0; m < 8; ++m) sKT[(c8 + m) * LT + r] = pk.buf[i][m];
+        }
+        pq.commit(sQ, LI, tid);
+        po.commit(sO, LDN, tid);
+        pp.commit(sP, LDN, tid);
+        pt.commit(sT, LDN, tid);
+        if (wave == 0) gate_scan(sg, gx, gb, lane);
+        __syncthreads();
+        if (c > 0) fetch(c - 1);   // previous chunk's operands load during this one
+        // dDelta = P^T dO + diag(e^{g_n - g}) K dS'^T
+        f32x4 e1[2], e2[2];
+        zero_n(e1);
+        zero_n(e2);
+        mmn<BC, 2>(sP + 16 * ty, 1, LDN, sO + 16 * tx0, LDN, 1, 16, e1, lane);
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sK + (16 * ty + li) * LI + 32 * ks + 8 * lq);
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+                    e2[x] = mfma32(a, *reinterpret_cast<const bf16x8 *>(
+                                          sG3[p] + (16 * (tx0 + x) + li) * LI + 32 * ks + 8 * lq), e2[x]);
+        }
+        __syncthreads();   // K rows consumed: dDelta goes over them
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * ty + 4 * lq + j, col = 16 * (tx0 + x) + li;
+                const float e = e1[x][j] + sg[3][r] * e2[x][j];
+                sE[r * LDN + col] = e;
+                if (r < n) wsE[(ch * BC + r) * D + dv0 + col] = e;
+            }
+        __syncthreads();
+        // F = diag(beta e^g) T^T dDelta, as pieces of F^T over those of dS';
+        // dO rows scaled by e^g
+        {
+            f32x4 f[2];
+            zero_n(f);
+            mmn<BC, 2>(sT + 16 * ty, 1, LDN, sE + 16 * tx0, LDN, 1, 16, f, lane);
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * ty + 4 * lq + j, col = 16 * (tx0 + x) + li;
+                    bf16 a, b, e;
+                    split3(sg[2][r] * sg[1][r] * f[x][j], a, b, e);
+                    sG3[0][col * LT + r] = a;
+                    sG3[1][col * LT + r] = b;
+                    sG3[2][col * LT + r] = e;
+                    sO[r * LDN + col] *= sg[1][r];
+                }
+        }
+        __syncthreads();
+        // dS <- e^{g_n} dS' + (e^g dO)^T Q - F^T K
+        const float egn = sg[1][BC - 1];
+        f32x4 fk[NTC];
+#pragma unroll
+        for (int t = 0; t < NTC; ++t) st[t] = st[t] * egn;
+        zero_n(fk);
+        mmn<BC, NTC>(sO + 16 * tr, 1, LDN, sQ + 16 * tc0, LI, 1, 16, st, lane);
+#pragma unroll
+        for (int ks = 0; ks < BC / 32; ++ks)
+#pragma unroll
+            for (int p = 0; p < 3; ++p) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sG3[p] + (16 * tr + li) * LT + 32 * ks + 8 * lq);
+#pragma unroll
+                for (int t = 0; t < NTC; ++t)
+                    fk[t] = mfma32(a, *reinterpret_cast<const bf16x8 *>(
+                                          sKT + (16 * (tc0 + t) + li) * LT + 32 * ks + 8 * lq), fk[t]);
+            }
+#pragma unroll
+        for (int t = 0; t < NTC; ++t) st[t] = st[t] - fk[t];
+        __syncthreads();
+    }
+    if (dS0) {
+#pragma unroll
+        for (int t = 0; t < NTC; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
+                dS0[((size_t)uh * D + dv0 + row) * D + col] = st[t][j];
+            }
+    }
+}
+
 // ---------------------------------------------------------------- 4. sprod
 // A-operand fragment of rows 16 tr + (l & 15) of a 64 x D row-major block,
 // held in registers: frag[s] = A[row][16 s + 4 (l >> 4) .. + 3] (the k order
@@ -1036,8 +1202,12 @@ hipError_t launch_bwd_t(int units, int T, int H, const int32_t *cu, const void *
             hipLaunchKernelGGL((bwd_states_kernel<D, TI>), dim3(seq_grid), dim3(512), 0, st, T, H,
                                NC, varlen, cu, ki, vi, la, beta, S0, wsT, wsH, wsDl);
     }
-    hipLaunchKernelGGL((bwd_dstates_kernel<D, TI, TG>), dim3(seq_grid), dim3(512), 0, st, T, H,
-                       NC, varlen, cu, qi, ki, dOg, la, beta, dST, wsT, wsP, wsDH, wsE, dS0);
+    if constexpr (sizeof(TI) == 2)
+        hipLaunchKernelGGL((bwd_dstates_x3_kernel<D, TG>), dim3(seq_grid), dim3(512), 0, st, T,
+                           H, NC, varlen, cu, qi, ki, dOg, la, beta, dST, wsT, wsP, wsDH, wsE, dS0);
+    else
+        hipLaunchKernelGGL((bwd_dstates_kernel<D, TI, TG>), dim3(seq_grid), dim3(512), 0, st, T,
+                           H, NC, varlen, cu, qi, ki, dOg, la, beta, dST, wsT, wsP, wsDH, wsE, dS0);
     if (nch > 0) {
         hipLaunchKernelGGL((bwd_sprod_kernel<D, TG>), dim3((unsigned)nch), dim3(512), 0, st, T, H,
                            units, NC, varlen, cu, dOg, wsH, wsDH, wsDl, wsE, wsOS, wsW, wsKt, wsSc);
