@@ -850,6 +850,35 @@ __device__ __forceinline__ void mm_rows(FA fa, FB fb, f32x4 (&acc)[NT]) {
     }
 }
 
+// A B^T with B exact in bf16 (row fragments as above, W = 8) and A fp32
+// rows in LDS, split on the fly into three exact bf16 pieces: the fp32 sums
+// on 3 bf16 MFMAs per 8 fp32 ones.
+__device__ __forceinline__ void split3x8(f32x8 x, bf16x8 &h, bf16x8 &m, bf16x8 &l) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        bf16 a, b, c;
+        split3(x[e], a, b, c);
+        h[e] = a;
+        m[e] = b;
+        l[e] = c;
+    }
+}
+// acc[t] += A B_t^T, A the fp32 rows at pa (lane offset included), B_t exact
+template <int K, int NT>
+__device__ __forceinline__ void mm_x3_a(const float *pa, const bf16x8 (&fb)[NT][K / 32],
+                                        f32x4 (&acc)[NT]) {
+#pragma unroll
+    for (int s = 0; s < K / 32; ++s) {
+        bf16x8 h, m, l;
+        split3x8(lds_w<8>(pa + 32 * s), h, m, l);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            acc[t] = mfma32(h, fb[t][s], acc[t]);
+            acc[t] = mfma32(m, fb[t][s], acc[t]);
+            acc[t] = mfma32(l, fb[t][s], acc[t]);
+        }
+    }
+}
 template <int D, typename TI, typename TG>
 __global__ __launch_bounds__(512, 4) void bwd_grads_kernel(
     int T, int H, int units, int NC, int varlen, const int32_t *__restrict__ cu,
@@ -954,8 +983,11 @@ __global__ __launch_bounds__(512, 4) void bwd_grads_kernel(
     zero_n(dt);
     {
         const float *pa = sB + (16 * ty + li) * LF + WI * lq;
-        mm_rows<D, WI, 2>([&](int s) { return lds_w<WI>(pa + 4 * WI * s); },
-                          [&](int t, int s) { return fb[t][s]; }, dt);
+        if constexpr (sizeof(TI) == 2)
+            mm_x3_a<D, 2>(pa, fb, dt);
+        else
+            mm_rows<D, WI, 2>([&](int s) { return lds_w<WI>(pa + 4 * WI * s); },
+                              [&](int t, int s) { return fb[t][s]; }, dt);
     }
     for (int x = 0; x < 2; ++x) dt[x] = dt[x] * sg[2][16 * (tx0 + x) + li];
     f32x4 an[NTC];
@@ -991,8 +1023,11 @@ __global__ __launch_bounds__(512, 4) void bwd_grads_kernel(
     zero_n(kk2);
     {
         const float *pa = sB + (16 * ty + li) * LF + WI * lq;
-        mm_rows<D, WI, 2>([&](int s) { return lds_w<WI>(pa + 4 * WI * s); },
-                          [&](int t, int s) { return fb[t][s]; }, a2);
+        if constexpr (sizeof(TI) == 2)
+            mm_x3_a<D, 2>(pa, fb, a2);
+        else
+            mm_rows<D, WI, 2>([&](int s) { return lds_w<WI>(pa + 4 * WI * s); },
+                              [&](int t, int s) { return fb[t][s]; }, a2);
         if constexpr (sizeof(TI) == 2) {
             // K K^T of bf16 inputs: exact products, so one 16x16x32 bf16 MFMA
             // per group (the fragments are already in its operand layout)
