@@ -186,8 +186,10 @@ def run_backward(args, torch, gi, gdn, dev, w, host):
                          "peak": MFMA_FP32_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": round(tfs / MFMA_FP32_PEAK_TFS, 4), "dtype": "f32",
                          "flops_per_step": fl},
-            "note": "gdn_chunk_bwd = 5 launches (prep, states, dstates, sprod, grads), all "
-                    "fp32 MFMA; dO fp32 ~ N(0,1), dS_T = 0"}
+            "note": "gdn_chunk_bwd = 5 launches (prep, states, dstates, sprod, grads); "
+                    "fp32-accurate products, counted as fp32 MFMA work (those with a bf16 "
+                    "input operand run on the bf16 MFMA, the fp32 side as three exact bf16 "
+                    "pieces); dO fp32 ~ N(0,1), dS_T = 0"}
 
 
 def kda_flops_per_chunk_head(d: int, C: int = 64) -> float:
