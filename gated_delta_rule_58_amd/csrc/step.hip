@@ -16,16 +16,20 @@
 // o = alpha (S q) / |q| + u (k . q) / (|k| |q|); log alpha = -softplus(a),
 // beta = sigmoid(b).
 //
-// Mapping: 16 lanes own one row of S.  Lane c holds the float4 groups c and
-// 16 + c of the row, so each load or store instruction of a wave covers four
-// contiguous 256-byte half-rows (fully coalesced).  A 256-thread workgroup
-// covers 16 rows of one (b, h); small workgroups keep many independent rows
-// in flight per CU.
+// Mapping: 16 lanes own two rows of S, 16 apart.  Lane c holds the float4
+// groups c and 16 + c of each row, so each load or store instruction of a
+// wave covers four contiguous 256-byte half-rows (fully coalesced).  A
+// 256-thread workgroup covers 32 rows of one (b, h); both rows' loads are in
+// flight before the first reduction, and the updated rows are written with
+// nontemporal stores (the state is not read again within the step).
+// Measured at B=64 H=16 d=128 against one row per lane group: 6% faster
+// from a cold cache, 2% faster with the state resident in the MALL.
 #include "gdn_common.h"
 
 namespace gdn {
 
-constexpr int kStepRowsPerWG = 16;
+constexpr int kStepRows = 2;                      // rows per 16-lane group
+constexpr int kStepRowsPerWG = 16 * kStepRows;
 
 // Load 4 consecutive elements as floats.
 __device__ __forceinline__ f32x4 load4(const bf16 *p) {
@@ -57,14 +61,19 @@ __global__ __launch_bounds__(256) void step_kernel(
     const int unit = blockIdx.x;   // b * H + h
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c = lane & 15;
-    const int row = blockIdx.y * kStepRowsPerWG + 4 * wave + (lane >> 4);
-    const bool live = row < DV;    // uniform over the 16 lanes of a row
-
-    f32x4 s[NV];
-    f32x4 *sp = reinterpret_cast<f32x4 *>(S + ((size_t)unit * DV + (live ? row : 0)) * DK);
-    if (live) {
+    int row[kStepRows];
+    bool live[kStepRows];          // uniform over the 16 lanes of a row
+    f32x4 s[kStepRows][NV];
+    f32x4 *sp[kStepRows];
 #pragma unroll
-        for (int i = 0; i < NV; ++i) s[i] = sp[16 * i + c];
+    for (int rr = 0; rr < kStepRows; ++rr) {
+        row[rr] = blockIdx.y * kStepRowsPerWG + 16 * rr + 4 * wave + (lane >> 4);
+        live[rr] = row[rr] < DV;
+        sp[rr] = reinterpret_cast<f32x4 *>(S + ((size_t)unit * DV + (live[rr] ? row[rr] : 0)) * DK);
+        if (live[rr]) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) s[rr][i] = sp[rr][16 * i + c];
+        }
     }
     f32x4 kr[NV], qr[NV];
 #pragma unroll
@@ -79,18 +88,10 @@ __global__ __launch_bounds__(256) void step_kernel(
     }
     const float a = expf(la);
 
-    float kq = 0.f, pk = 0.f, pq = 0.f;
+    float kq = 0.f;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        kq += dot4(kr[i], qr[i]);
-        if (live) {
-            pk += dot4(s[i], kr[i]);
-            pq += dot4(s[i], qr[i]);
-        }
-    }
+    for (int i = 0; i < NV; ++i) kq += dot4(kr[i], qr[i]);
     kq = sum16(kq);
-    pk = sum16(pk);
-    pq = sum16(pq);
     float ik = 1.f, iq = 1.f;   // 1/|k|, 1/|q| (prologue), else 1
     if (norm_qk) {
         float kk = 0.f, qq = 0.f;
@@ -102,12 +103,26 @@ __global__ __launch_bounds__(256) void step_kernel(
         ik = 1.f / sqrtf(fmaxf(sum16(kk), 1e-12f));
         iq = 1.f / sqrtf(fmaxf(sum16(qq), 1e-12f));
     }
-    if (!live) return;
-    const float u = b * (to_f32(v[(size_t)unit * DV + row]) - a * pk * ik);
-    const float uk = u * ik;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) sp[16 * i + c] = a * s[i] + uk * kr[i];
-    if (c == 0) o[(size_t)unit * DV + row] = from_f32<TO>((a * pq + uk * kq) * iq);
+    for (int rr = 0; rr < kStepRows; ++rr) {
+        float pk = 0.f, pq = 0.f;
+        if (live[rr]) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                pk += dot4(s[rr][i], kr[i]);
+                pq += dot4(s[rr][i], qr[i]);
+            }
+        }
+        pk = sum16(pk);
+        pq = sum16(pq);
+        if (!live[rr]) continue;
+        const float u = b * (to_f32(v[(size_t)unit * DV + row[rr]]) - a * pk * ik);
+        const float uk = u * ik;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            __builtin_nontemporal_store(a * s[rr][i] + uk * kr[i], &sp[rr][16 * i + c]);
+        if (c == 0) o[(size_t)unit * DV + row[rr]] = from_f32<TO>((a * pq + uk * kq) * iq);
+    }
 }
 
 template <int DK, typename TI, typename TO>
