@@ -1145,16 +1145,6 @@ __global__ __launch_bounds__(512, 4) void bwd_grads_kernel(
             ssum += s;   // the same in all 16 lanes of the group
         }
     }
-    mmn<BC, NTC>(sN + 16 * tr, 1, LDN, sQ + 16 * tc0, LI, 1, 16, dka, lane);
-    mmn<BC, NTC>(sB + 16 * tr * LDN, LDN, 1, sK + 16 * tc0, LI, 1, 16, dka, lane);
-    mmn<BC, NTC>(sB + 16 * tr, 1, LDN, sK + 16 * tc0, LI, 1, 16, dka, lane);
-#pragma unroll
-    for (int t = 0; t < NTC; ++t)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-            if (r < n) dkc[r * HD + col] = cvt<TG>(dka[t][j]);
-        }
     // dQ = diag(e^g) dO S + dQK K;  dg += e^g rows(dO S . Q)
 #pragma unroll
     for (int t = 0; t < NTC; ++t) {
@@ -1167,13 +1157,67 @@ __global__ __launch_bounds__(512, 4) void bwd_grads_kernel(
             if (li == 0) ADDG(r, rg);
         }
     }
-    mmn<BC, NTC>(sN + 16 * tr * LDN, LDN, 1, sK + 16 * tc0, LI, 1, 16, an, lane);
+    if constexpr (sizeof(TI) == 2) {
+        // bf16 inputs: K and Q enter by columns (B fragments of 8 consecutive
+        // tokens of one d_k column, exact), dQK and dG by rows or columns as
+        // three exact bf16 pieces; one 32-token block at a time
+        auto colfrag = [&](const TI *X, int s, int t) {
+            bf16x8 f;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) f[m] = X[(32 * s + 8 * lq + m) * LI + 16 * (tc0 + t) + li];
+            return f;
+        };
+        // rows (unit stride along k) or columns (stride LDN) of a 64 x 64 fp32 block
+        auto apieces = [&](const float *X, bool bycol, int s, bf16x8 &h, bf16x8 &m, bf16x8 &l) {
+            f32x8 a;
+            if (bycol) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[e] = X[(32 * s + 8 * lq + e) * LDN + 16 * tr + li];
+            } else {
+                a = lds_w<8>(X + (16 * tr + li) * LDN + 32 * s + 8 * lq);
+            }
+            split3x8(a, h, m, l);
+        };
+        auto acc3 = [&](f32x4 (&acc)[NTC], const bf16x8 &h, const bf16x8 &m, const bf16x8 &l,
+                        const bf16x8 (&bf)[NTC]) {
+#pragma unroll
+            for (int t = 0; t < NTC; ++t) {
+                acc[t] = mfma32(h, bf[t], acc[t]);
+                acc[t] = mfma32(m, bf[t], acc[t]);
+                acc[t] = mfma32(l, bf[t], acc[t]);
+            }
+        };
+#pragma unroll
+        for (int s = 0; s < BC / 32; ++s) {
+            bf16x8 kf[NTC], qf[NTC], h, m, l;
+#pragma unroll
+            for (int t = 0; t < NTC; ++t) kf[t] = colfrag(sK, s, t);
+            apieces(sN, false, s, h, m, l);   // dQK K
+            acc3(an, h, m, l, kf);
+            apieces(sB, false, s, h, m, l);   // dG K
+            acc3(dka, h, m, l, kf);
+            apieces(sB, true, s, h, m, l);    // dG^T K
+            acc3(dka, h, m, l, kf);
+#pragma unroll
+            for (int t = 0; t < NTC; ++t) qf[t] = colfrag(sQ, s, t);
+            apieces(sN, true, s, h, m, l);    // dQK^T Q
+            acc3(dka, h, m, l, qf);
+        }
+    } else {
+        mmn<BC, NTC>(sN + 16 * tr * LDN, LDN, 1, sK + 16 * tc0, LI, 1, 16, an, lane);
+        mmn<BC, NTC>(sN + 16 * tr, 1, LDN, sQ + 16 * tc0, LI, 1, 16, dka, lane);
+        mmn<BC, NTC>(sB + 16 * tr * LDN, LDN, 1, sK + 16 * tc0, LI, 1, 16, dka, lane);
+        mmn<BC, NTC>(sB + 16 * tr, 1, LDN, sK + 16 * tc0, LI, 1, 16, dka, lane);
+    }
 #pragma unroll
     for (int t = 0; t < NTC; ++t)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-            if (r < n) dqc[r * HD + col] = cvt<TG>(an[t][j]);
+            if (r < n) {
+                dkc[r * HD + col] = cvt<TG>(dka[t][j]);
+                dqc[r * HD + col] = cvt<TG>(an[t][j]);
+            }
         }
     ssum += __shfl_xor(ssum, 16);
     ssum += __shfl_xor(ssum, 32);
