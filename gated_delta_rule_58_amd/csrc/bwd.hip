@@ -978,7 +978,7 @@ __global__ __launch_bounds__(512, 4) void bwd_grads_kernel(
     pf.fetch(wsW + ch * BC * D, D, n, tid);                     // dW, for the next stage
     __syncthreads();
 
-    // dT = dDelta (beta V)^T + ...; dV = diag(beta) T^T dDelta; dbeta += rows(T^T dDelta . V)
+    // dT = dDelta (beta V)^T + ...; dV = diag(beta) T^T dDelta
     f32x4 dt[2];
     zero_n(dt);
     {
@@ -988,6 +988,23 @@ __global__ __launch_bounds__(512, 4) void bwd_grads_kernel(
         else
             mm_rows<D, WI, 2>([&](int s) { return lds_w<WI>(pa + 4 * WI * s); },
                               [&](int t, int s) { return fb[t][s]; }, dt);
+    }
+    // T[k][r] at this lane's dT positions (k = 16 ty + 4 lq + j, r = 16 (tx0 + x) + li):
+    // a row sum of T^T X o Y is a column sum of T o (X Y^T), and X Y^T is the
+    // dT term just formed, so the dbeta and dg row sums below need no
+    // elements of V or K
+    auto tcolsum = [&](const f32x4 (&w)[2], int x) {
+        float cs = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cs += sT[(16 * ty + 4 * lq + j) * LDN + 16 * (tx0 + x) + li] * w[x][j];
+        cs += __shfl_xor(cs, 16);
+        cs += __shfl_xor(cs, 32);
+        return cs;   // for column r = 16 (tx0 + x) + li, in every lane group
+    };
+    // dbeta += rows(T^T dDelta . V) = column sums of T o (dDelta V^T)
+    for (int x = 0; x < 2; ++x) {
+        const float cs = tcolsum(dt, x);
+        if (lq == 0) ADDB(16 * (tx0 + x) + li, cs);
     }
     for (int x = 0; x < 2; ++x) dt[x] = dt[x] * sg[2][16 * (tx0 + x) + li];
     f32x4 an[NTC];
@@ -1000,13 +1017,7 @@ __global__ __launch_bounds__(512, 4) void bwd_grads_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
-            float vv = 0.f;
-            if (r < n) {
-                dvc[r * HD + col] = cvt<TG>(sg[2][r] * a[j]);
-                vv = to_f32(vc[r * HD + col]);
-            }
-            const float rs = sum16(a[j] * vv);
-            if (li == 0) ADDB(r, rs);
+            if (r < n) dvc[r * HD + col] = cvt<TG>(sg[2][r] * a[j]);
         }
     }
 #pragma unroll
@@ -1040,30 +1051,26 @@ __global__ __launch_bounds__(512, 4) void bwd_grads_kernel(
                               [&](int t, int s) { return fb[t][s]; }, kk2);
         }
     }
+    // rows(T^T dW . K) = column sums of T o (dW K^T): dbeta += e^g x, dg += beta e^g x
     for (int x = 0; x < 2; ++x) {
         const int i = 16 * (tx0 + x) + li;
+        const float cs = tcolsum(a2, x);
+        if (lq == 0) {
+            ADDB(i, sg[1][i] * cs);
+            ADDG(i, sg[2][i] * sg[1][i] * cs);
+        }
         dt[x] = dt[x] + a2[x] * (sg[2][i] * sg[1][i]);
     }
     f32x4 dka[NTC];
     zero_n(an);
     mmn<BC, NTC>(sT + 16 * tr, 1, LDN, sB + 16 * tc0, LF, 1, 16, an, lane);
 #pragma unroll
-    for (int t = 0; t < NTC; ++t) {
-        const int tc = tc0 + t;
-        const f32x4 a = an[t];
+    for (int t = 0; t < NTC; ++t)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int r = 16 * tr + 4 * lq + j, col = 16 * tc + li;
-            const float be = sg[2][r] * sg[1][r];
-            dka[t][j] = be * a[j];
-            const float kv = r < n ? to_f32(kc[r * HD + col]) : 0.f;
-            const float rw = sum16(a[j] * kv);
-            if (li == 0) {
-                ADDB(r, sg[1][r] * rw);
-                ADDG(r, be * rw);
-            }
+            const int r = 16 * tr + 4 * lq + j;
+            dka[t][j] = sg[2][r] * sg[1][r] * an[t][j];
         }
-    }
     __syncthreads();   // dW no longer read
 #pragma unroll
     for (int x = 0; x < 2; ++x)
