@@ -729,15 +729,16 @@ __global__ __launch_bounds__(512, 2) void bwd_sprod_kernel(
         mm_afrag<D, NTC>(fa, sB + 16 * tc0, LF, a, lane);
         mm_afrag<D, NTC>(fb, sB + 16 * tc0, LF, b, lane);
 #pragma unroll
-        for (int t = 0; t < NTC; ++t)
+        for (int t = 0; t < NTC; ++t) {
+            // dO S in the gradient kernel's register layout (lane-blocked, rows
+            // past n are zero); -dDelta S row-major
+            *reinterpret_cast<f32x4 *>(wsOS + ch * BC * D + 4 * (tid * NTC + t)) = a[t];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-                if (r < n) {
-                    wsOS[(ch * BC + r) * D + col] = a[t][j];
-                    wsW[(ch * BC + r) * D + col] = -b[t][j];
-                }
+                if (r < n) wsW[(ch * BC + r) * D + col] = -b[t][j];
             }
+        }
     }
     afrag_rows<D>(fa, wsDl + (ch * BC + arow) * D, avalid, lq);   // Delta rows
     __syncthreads();
@@ -766,12 +767,8 @@ __global__ __launch_bounds__(512, 2) void bwd_sprod_kernel(
         zero_n(a);
         mm_afrag<D, NTC>(fa, sB + 16 * tc0, LF, a, lane);
 #pragma unroll
-        for (int t = 0; t < NTC; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-                if (r < n) wsKt[(ch * BC + r) * D + col] = a[t][j];
-            }
+        for (int t = 0; t < NTC; ++t)   // lane-blocked, as dO S
+            *reinterpret_cast<f32x4 *>(wsKt + ch * BC * D + 4 * (tid * NTC + t)) = a[t];
     }
 }
 
@@ -1118,18 +1115,13 @@ __global__ __launch_bounds__(512, 4) void bwd_grads_kernel(
         col += __shfl_xor(col, 32);
         if (lq == 0) ADDG(16 * tx + li, -col);
     }
-    // this lane's elements of dO S and Delta dS'
+    // this lane's elements of dO S and Delta dS' (stored lane-blocked by the
+    // state-product kernel, whose workgroups tile the chunk the same way)
     f32x4 osv[NTC], ktv[NTC];
-    {
-        const float *OS = wsOS + ch * BC * D, *Kt = wsKt + ch * BC * D;
 #pragma unroll
-        for (int t = 0; t < NTC; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-                osv[t][j] = r < n ? OS[(size_t)r * D + col] : 0.f;
-                ktv[t][j] = r < n ? Kt[(size_t)r * D + col] : 0.f;
-            }
+    for (int t = 0; t < NTC; ++t) {
+        osv[t] = *reinterpret_cast<const f32x4 *>(wsOS + ch * BC * D + 4 * (tid * NTC + t));
+        ktv[t] = *reinterpret_cast<const f32x4 *>(wsKt + ch * BC * D + 4 * (tid * NTC + t));
     }
     __syncthreads();   // T and M no longer read
     pk.commit(sK, LI, tid);
@@ -1264,6 +1256,10 @@ hipError_t launch_bwd_t(int units, int T, int H, const int32_t *cu, const void *
     const int varlen = cu != nullptr;
     const int NC = varlen ? 0 : (T + BC - 1) / BC;
     const size_t nch = (size_t)nslots * H;
+    // Workspace, per chunk slot and head: T and P (64 x 64), the state entering
+    // the chunk and the gradient of the state leaving it (d x d), Delta, dDelta,
+    // dO S, -dDelta S and Delta dS' (64 x d; dO S and Delta dS' lane-blocked in
+    // the gradient kernel's register layout, the others row-major), <dS', S>.
     float *wsT = ws;
     float *wsP = wsT + nch * BC * BC;
     float *wsH = wsP + nch * BC * BC;
