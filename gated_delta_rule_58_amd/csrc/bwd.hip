@@ -1,4 +1,4 @@
-// Backward pass of the chunkwise gated delta rule on gfx950 (fp32 MFMA).
+// Backward pass of the chunkwise gated delta rule on gfx950 (fp32-accurate MFMA).
 //
 // The pages name a gate-aware backward pass for the chunkwise algorithm
 // ("Gated DeltaNet-2: Decoupling Erase and Write in Linear Attention",
@@ -27,8 +27,11 @@
 //   dbeta, dg: row sums of the same products; dlog_alpha = reverse
 //   cumulative sum of dg within the chunk.
 //
-// Five launches, all fp32 arithmetic on v_mfma_f32_16x16x4_f32 (inputs are
-// exact in fp32, so no operand splitting is needed):
+// Five launches.  Every product is fp32-accurate: most run on
+// v_mfma_f32_16x16x4_f32 (inputs are exact in fp32); with bf16 inputs, the
+// products that have a bf16 input (K, Q, V) as one operand run on the
+// 16x16x32 bf16 MFMA, exact when both operands are inputs and otherwise over
+// three bf16 pieces that add up to the fp32 operand exactly (split3):
 //   1. prep     (one workgroup per chunk and head): T and P;
 //   2. states   (one per sequence, head and 64-column d_v slice, chunks in
 //               order): the state entering every chunk and Delta;
