@@ -115,6 +115,30 @@ def run_decode(args, torch, gi, gdn, dev):
     del flush
     cold.sort()
     cold_us = cold[len(cold) // 2]
+    # the same steps replayed from one HIP graph (a serving loop captures its
+    # decode steps once): no launch gaps between steps, state in the MALL
+    gsteps = min(nsteps, 64)
+    S.copy_(dd["S0"])
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for t in range(gsteps):
+            dstep(t)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t in range(gsteps):
+            dstep(t)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1e3 / gsteps
+    del graph
     dbytes = (2 * Bd * Hd * wd["dv"] * wd["dk"] * 4 + Bd * Hd * (2 * wd["dk"] + wd["dv"]) * 2
               + Bd * Hd * wd["dv"] * 4 + Bd * Hd * 8)
     decode = {
@@ -125,8 +149,11 @@ def run_decode(args, torch, gi, gdn, dev):
         "frac_hbm_cold": round(dbytes / (cold_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "us_per_step_warm": round(warm_us, 2),
         "GB_s_warm": round(dbytes / (warm_us * 1e-6) / 1e9, 1),
+        "us_per_step_graph": round(graph_us, 2),
+        "GB_s_graph": round(dbytes / (graph_us * 1e-6) / 1e9, 1),
         "note": "cold = 1 GiB cache-evicting read before each timed step (median of "
-                f"{args.cold_steps}); warm = {nsteps} steps back to back, state resident in MALL",
+                f"{args.cold_steps}); warm = {nsteps} steps back to back, state resident in "
+                f"MALL; graph = {gsteps} steps replayed from one captured HIP graph",
     }
 
     if args.only == "decode":
