@@ -291,6 +291,34 @@ __device__ __forceinline__ f32x4 ld4f(const bf16 *p) {
 }
 __device__ __forceinline__ f32x4 ld4f(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
+// acc1[t] += A1 B_t^T and acc2[t] += A2 B_t^T for fp32 operands read by
+// rows from LDS (pointers at the tiles' first rows, row strides lda and ldb,
+// 16-byte aligned; tile t of B starts 16 t rows down).  Lane (li, lq) reads
+// the 4 consecutive k values 16 s + 4 lq .. + 3 of its row in one 16-byte
+// read, so the k order of each MFMA step is the same for both operands, and
+// the two products share the B reads.
+template <int K, int NT>
+__device__ __forceinline__ void mm_rows2(const float *A1, const float *A2, int lda, const float *B,
+                                         int ldb, f32x4 (&acc1)[NT], f32x4 (&acc2)[NT], int lane) {
+    const int li = lane & 15, lq = lane >> 4;
+    const float *pa1 = A1 + li * lda + 4 * lq, *pa2 = A2 + li * lda + 4 * lq;
+    const float *pb = B + li * ldb + 4 * lq;
+#pragma unroll 2
+    for (int s = 0; s < K / 16; ++s) {
+        const f32x4 a1 = ld4f(pa1 + 16 * s), a2 = ld4f(pa2 + 16 * s);
+        f32x4 b[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) b[t] = ld4f(pb + 16 * t * ldb + 16 * s);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                acc1[t] = mfma_f32(a1[m], b[t][m], acc1[t]);
+                acc2[t] = mfma_f32(a2[m], b[t][m], acc2[t]);
+            }
+    }
+}
+
 // Diagonal 16 x 16 block b of the channel-weighted product
 //   M[r][i] = sum_c X[r][c] Y[i][c] e^{G[r][c] - G[i][c]},  r, i in 16b..16b+15,
 // by one wave, every entry (the caller masks the upper part); lane (li, lq)

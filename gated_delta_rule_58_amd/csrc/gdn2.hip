@@ -347,8 +347,8 @@ __global__ __launch_bounds__(512) void gdn2_fwd_kernel(
         f32x4 xa[2], oa[2];
         zero_n(xa);
         zero_n(oa);
-        mmn<D, 2>(sX1 + 16 * ty * LF, LF, 1, sS + 16 * tx0 * LF, 1, LF, 16 * LF, xa, lane);
-        mmn<D, 2>(sX2 + 16 * ty * LF, LF, 1, sS + 16 * tx0 * LF, 1, LF, 16 * LF, oa, lane);
+        mm_rows2<D, 2>(sX1 + 16 * ty * LF, sX2 + 16 * ty * LF, LF, sS + 16 * tx0 * LF, LF, xa, oa,
+                       lane);
 #pragma unroll
         for (int m = 0; m < 16; ++m)
 #pragma unroll

@@ -257,8 +257,8 @@ __global__ __launch_bounds__(512) void kda_fwd_kernel(
         f32x4 y[2], qs[2];
         zero_n(y);
         zero_n(qs);
-        mmn<D, 2>(sX1 + 16 * ty * LF, LF, 1, sS + 16 * tx0 * LF, 1, LF, 16 * LF, y, lane);
-        mmn<D, 2>(sX2 + 16 * ty * LF, LF, 1, sS + 16 * tx0 * LF, 1, LF, 16 * LF, qs, lane);
+        mm_rows2<D, 2>(sX1 + 16 * ty * LF, sX2 + 16 * ty * LF, LF, sS + 16 * tx0 * LF, LF, y, qs,
+                       lane);
         for (int x = 0; x < 2; ++x)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
