@@ -216,7 +216,8 @@ def run_backward(args, torch, gi, gdn, dev, w, host):
             "note": "gdn_chunk_bwd = 5 launches (prep, states, dstates, sprod, grads); "
                     "fp32-accurate products, counted as fp32 MFMA work (those with a bf16 "
                     "input operand run on the bf16 MFMA, the fp32 side as three exact bf16 "
-                    "pieces); dO fp32 ~ N(0,1), dS_T = 0"}
+                    "pieces; sprod's fp32 x fp32 products as six products of such pieces); "
+                    "dO fp32 ~ N(0,1), dS_T = 0"}
 
 
 def kda_flops_per_chunk_head(d: int, C: int = 64) -> float:

@@ -31,7 +31,8 @@
 // v_mfma_f32_16x16x4_f32 (inputs are exact in fp32); with bf16 inputs, the
 // products that have a bf16 input (K, Q, V) as one operand run on the
 // 16x16x32 bf16 MFMA, exact when both operands are inputs and otherwise over
-// three bf16 pieces that add up to the fp32 operand exactly (split3):
+// three bf16 pieces that add up to the fp32 operand exactly (split3); the
+// sprod products split both fp32 operands so and sum six piece products:
 //   1. prep     (one workgroup per chunk and head): T and P;
 //   2. states   (one per sequence, head and 64-column d_v slice, chunks in
 //               order): the state entering every chunk and Delta;
@@ -667,33 +668,62 @@ __global__ __launch_bounds__(512) void bwd_dstates_x3_kernel(
 }
 
 // ---------------------------------------------------------------- 4. sprod
-// A-operand fragment of rows 16 tr + (l & 15) of a 64 x D row-major block,
-// held in registers: frag[s] = A[row][16 s + 4 (l >> 4) .. + 3] (the k order
-// of these products is 16 s + 4 lq + m, the same for the B operand, so the B
-// rows read by the four lane groups are 4 rows apart: distinct LDS banks with
-// a row stride of D + 4 floats).  Rows past n are zero.
-template <int D, typename TG>
-__device__ __forceinline__ void afrag_rows(f32x4 (&frag)[D / 16], const TG *rowp, bool valid,
-                                           int lq) {
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-        frag[s] = zero4();
-        if (valid) frag[s] = ld4f(rowp + 16 * s + 4 * lq);
+// X M for 64 x D row blocks X and a D x D fp32 matrix M, both with up to 24
+// significant bits: each operand is written as three bf16 pieces that add up
+// to it exactly (split3), and the six piece products down to 2^-16 of the
+// leading one run on the 16x16x32 bf16 MFMA with fp32 sums; the three left
+// out are below 2^-23 of it, under the fp32 rounding of the sums.  (Eight
+// fp32 16x16x4 MFMAs of 32 cycles become six bf16 ones of 16.)  M passes
+// through LDS 64 rows (k) at a time as its three pieces, row-major with the
+// 8-byte chunks of row r permuted by sp_swz(r), and reaches the MFMA by
+// column gathers (transpose reads), whose k order within a 32-step is
+// 4 lq + j, then 16 + 4 lq + j; the X fragments follow that order.
+constexpr int SP_KR = 64;   // rows of M per LDS round
+__device__ __forceinline__ int sp_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+template <int W> __device__ __forceinline__ int sp_pos(int r, int c) {   // element (r, c)
+    return r * W + 4 * ((c >> 2) ^ sp_swz(r)) + (c & 3);
+}
+// B operand of output columns 16 cb .. 16 cb + 15 and k step ks of a piece:
+// element (i, e) = piece[32 ks + k(e)][16 cb + i].
+template <int W>
+__device__ __forceinline__ bf16x8 sp_bfrag(const bf16 *piece, int cb, int ks, int lane) {
+    const int lm = lane & 15, lg = lane >> 4, j = lm >> 2, q4 = lm & 3;
+    const int r = 32 * ks + 4 * lg + j;
+    const bf16 *p = piece + r * W + 4 * ((4 * cb + q4) ^ sp_swz(r));
+    return cat(lds_read_tr(p), lds_read_tr(p + 16 * W));   // rows r and r + 16 permute alike
+}
+// A operand of row `row` (zero when !valid), k step ks: elements
+// X[row][32 ks + 4 lq + j] and X[row][32 ks + 16 + 4 lq + j], loaded as fp32
+// and later split into its three pieces.
+template <typename TX>
+__device__ __forceinline__ void sp_aload(const TX *rowp, bool valid, int ks, int lq,
+                                         f32x4 (&x)[2]) {
+    x[0] = zero4();
+    x[1] = zero4();
+    if (valid) {
+        x[0] = ld4f(rowp + 32 * ks + 4 * lq);
+        x[1] = ld4f(rowp + 32 * ks + 16 + 4 * lq);
     }
 }
-// acc[t] += A_frag B_t with B_t(k, j) = B[k * ldb + 16 t + j], k in the fragment order.
-template <int D, int NT>
-__device__ __forceinline__ void mm_afrag(const f32x4 (&frag)[D / 16], const float *B, int ldb,
-                                         f32x4 (&acc)[NT], int lane) {
-    const int li = lane & 15, lq = lane >> 4;
-#pragma unroll 2
-    for (int s = 0; s < D / 16; ++s)
+__device__ __forceinline__ void sp_asplit(const f32x4 (&x)[2], bf16x8 (&a)[3]) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const float *bp = B + (16 * s + 4 * lq + m) * ldb + li;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) acc[t] = mfma_f32(frag[s][m], bp[16 * t], acc[t]);
-        }
+    for (int e = 0; e < 8; ++e) {
+        bf16 h, m, l;
+        split3(e < 4 ? x[0][e] : x[1][e - 4], h, m, l);
+        a[0][e] = h;
+        a[1][e] = m;
+        a[2][e] = l;
+    }
+}
+// acc += A B over one k step, six piece products (leading terms first).
+__device__ __forceinline__ f32x4 sp_mma6(const bf16x8 (&a)[3], const bf16x8 (&b)[3], f32x4 acc) {
+    acc = mfma32(a[0], b[0], acc);
+    acc = mfma32(a[0], b[1], acc);
+    acc = mfma32(a[1], b[0], acc);
+    acc = mfma32(a[0], b[2], acc);
+    acc = mfma32(a[1], b[1], acc);
+    acc = mfma32(a[2], b[0], acc);
+    return acc;
 }
 
 template <int D, typename TG>
@@ -702,10 +732,12 @@ __global__ __launch_bounds__(512, 2) void bwd_sprod_kernel(
     const TG *__restrict__ dO, const float *__restrict__ wsH, const float *__restrict__ wsDH,
     const float *__restrict__ wsDl, const float *__restrict__ wsE, float *__restrict__ wsOS,
     float *__restrict__ wsW, float *__restrict__ wsKt, float *__restrict__ wsSc) {
-    constexpr int LF = D + 4, NTC = D / 32;
-    // only the d x d matrix sits in LDS (the row operands are register
-    // fragments), so two workgroups share a CU
-    __shared__ __attribute__((aligned(16))) float sB[D * LF];    // S, then dS'
+    constexpr int NTC = D / 32;                  // 16-column output tiles per wave
+    constexpr int NR = D / SP_KR;                // LDS rounds per matrix
+    constexpr int PER = SP_KR * D / 4 / 512;     // 4-element groups of a round per thread
+    static_assert(PER * 512 * 4 == SP_KR * D, "round split");
+    // three pieces of 64 rows of M (48 KB at d = 128): two workgroups per CU
+    __shared__ __attribute__((aligned(16))) bf16 sM[3][SP_KR * D];
     __shared__ float sred[8];
     const int slot = blockIdx.x / H, h = blockIdx.x % H;
     long row0;
@@ -715,45 +747,114 @@ __global__ __launch_bounds__(512, 2) void bwd_sprod_kernel(
     const int li = lane & 15, lq = lane >> 4;
     const int tr = wave & 3, tc0 = (wave >> 2) * NTC;
     const size_t ch = blockIdx.x;
-    const float *Sm = wsH + ch * D * D, *DSm = wsDH + ch * D * D;
+    const float *const Sm = wsH + ch * D * D, *const DSm = wsDH + ch * D * D;
     const int arow = 16 * tr + li;
     const bool avalid = arow < n;
-    f32x4 fa[D / 16], fb[D / 16];
-    afrag_rows<D>(fa, dO + ((size_t)(row0 + (avalid ? arow : 0)) * H + h) * D, avalid, lq);
-    afrag_rows<D>(fb, wsE + (ch * BC + arow) * D, avalid, lq);
-    for (int e = tid; e < D * D / 4; e += 512)
-        put4(sB + (e / (D / 4)) * LF + (e % (D / 4)) * 4, *reinterpret_cast<const f32x4 *>(Sm + 4 * e));
-    __syncthreads();
-    // dO S and -dDelta S (64 x d_k)
-    {
-        f32x4 a[NTC], b[NTC];
-        zero_n(a);
-        zero_n(b);
-        mm_afrag<D, NTC>(fa, sB + 16 * tc0, LF, a, lane);
-        mm_afrag<D, NTC>(fb, sB + 16 * tc0, LF, b, lane);
+    const TG *const dOr = dO + ((size_t)(row0 + (avalid ? arow : 0)) * H + h) * D;
+    const float *const dEr = wsE + (ch * BC + arow) * D;
+    const float *const dLr = wsDl + (ch * BC + arow) * D;
+    // this thread's 4-element groups of a round: row e / (D / 4), columns 4 (e % (D / 4)) + 0..3
+    auto grp = [&](int q) { return tid + 512 * q; };
+    f32x4 mreg[PER];
+    auto fetch = [&](const float *M, int rd) {
 #pragma unroll
-        for (int t = 0; t < NTC; ++t) {
-            // dO S in the gradient kernel's register layout (lane-blocked, rows
-            // past n are zero); -dDelta S row-major
-            *reinterpret_cast<f32x4 *>(wsOS + ch * BC * D + 4 * (tid * NTC + t)) = a[t];
+        for (int q = 0; q < PER; ++q)
+            mreg[q] = *reinterpret_cast<const f32x4 *>(M + (size_t)rd * SP_KR * D + 4 * grp(q));
+    };
+    auto put = [&]() {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int e = grp(q), r = e / (D / 4), c = 4 * (e % (D / 4));
+            bf16x4 p0, p1, p2;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-                if (r < n) wsW[(ch * BC + r) * D + col] = -b[t][j];
+                bf16 a, b, c3;
+                split3(mreg[q][j], a, b, c3);
+                p0[j] = a;
+                p1[j] = b;
+                p2[j] = c3;
+            }
+            const int at = sp_pos<D>(r, c);
+            *reinterpret_cast<bf16x4 *>(&sM[0][at]) = p0;
+            *reinterpret_cast<bf16x4 *>(&sM[1][at]) = p1;
+            *reinterpret_cast<bf16x4 *>(&sM[2][at]) = p2;
+        }
+    };
+
+    // dO S and -dDelta S (64 x d_k), then Delta dS' with <dS', S> on the way
+    f32x4 a[NTC], b[NTC];
+    zero_n(a);
+    zero_n(b);
+    fetch(Sm, 0);
+#pragma unroll 1
+    for (int rd = 0; rd < NR; ++rd) {
+        put();
+        __syncthreads();
+        if (rd + 1 < NR) fetch(Sm, rd + 1);
+        else fetch(DSm, 0);
+        // (X fragments loaded a round ahead would take the registers of two
+        // workgroups per CU)
+#pragma unroll
+        for (int kl = 0; kl < 2; ++kl) {
+            f32x4 xr[2];
+            bf16x8 xo[3], xe[3];
+            sp_aload(dOr, avalid, 2 * rd + kl, lq, xr);
+            sp_asplit(xr, xo);
+            sp_aload(dEr, avalid, 2 * rd + kl, lq, xr);
+            sp_asplit(xr, xe);
+#pragma unroll
+            for (int t = 0; t < NTC; ++t) {
+                const bf16x8 bm[3] = {sp_bfrag<D>(sM[0], tc0 + t, kl, lane),
+                                      sp_bfrag<D>(sM[1], tc0 + t, kl, lane),
+                                      sp_bfrag<D>(sM[2], tc0 + t, kl, lane)};
+                a[t] = sp_mma6(xo, bm, a[t]);
+                b[t] = sp_mma6(xe, bm, b[t]);
             }
         }
+        __syncthreads();   // sM is rewritten next round
     }
-    afrag_rows<D>(fa, wsDl + (ch * BC + arow) * D, avalid, lq);   // Delta rows
-    __syncthreads();
-    // dS' replaces S; <dS', S> on the way
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) {
+        // dO S in the gradient kernel's register layout (lane-blocked, rows
+        // past n are zero); -dDelta S row-major
+        *reinterpret_cast<f32x4 *>(wsOS + ch * BC * D + 4 * (tid * NTC + t)) = a[t];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
+            if (r < n) wsW[(ch * BC + r) * D + col] = -b[t][j];
+        }
+    }
+    zero_n(a);
     float dot = 0.f;
-    for (int e = tid; e < D * D / 4; e += 512) {
-        float *at = sB + (e / (D / 4)) * LF + (e % (D / 4)) * 4;
-        const f32x4 x = *reinterpret_cast<const f32x4 *>(DSm + 4 * e);
-        const f32x4 y = *reinterpret_cast<const f32x4 *>(at);
-        dot += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
-        put4(at, x);
+#pragma unroll 1
+    for (int rd = 0; rd < NR; ++rd) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {   // <dS', S> over this thread's groups
+            const f32x4 y = *reinterpret_cast<const f32x4 *>(Sm + (size_t)rd * SP_KR * D + 4 * grp(q));
+            dot += mreg[q][0] * y[0] + mreg[q][1] * y[1] + mreg[q][2] * y[2] + mreg[q][3] * y[3];
+        }
+        put();
+        __syncthreads();
+        if (rd + 1 < NR) fetch(DSm, rd + 1);
+#pragma unroll
+        for (int kl = 0; kl < 2; ++kl) {
+            f32x4 xr[2];
+            bf16x8 xd[3];
+            sp_aload(dLr, avalid, 2 * rd + kl, lq, xr);
+            sp_asplit(xr, xd);
+#pragma unroll
+            for (int t = 0; t < NTC; ++t) {
+                const bf16x8 bm[3] = {sp_bfrag<D>(sM[0], tc0 + t, kl, lane),
+                                      sp_bfrag<D>(sM[1], tc0 + t, kl, lane),
+                                      sp_bfrag<D>(sM[2], tc0 + t, kl, lane)};
+                a[t] = sp_mma6(xd, bm, a[t]);
+            }
+        }
+        if (rd + 1 < NR) __syncthreads();
     }
+#pragma unroll
+    for (int t = 0; t < NTC; ++t)   // Delta dS', lane-blocked as dO S
+        *reinterpret_cast<f32x4 *>(wsKt + ch * BC * D + 4 * (tid * NTC + t)) = a[t];
     dot = sum16(dot);
     dot += __shfl_xor(dot, 16);
     dot += __shfl_xor(dot, 32);
@@ -763,15 +864,6 @@ __global__ __launch_bounds__(512, 2) void bwd_sprod_kernel(
         float s = 0.f;
         for (int w = 0; w < 8; ++w) s += sred[w];
         wsSc[ch] = s;
-    }
-    // Delta dS' (64 x d_k)
-    {
-        f32x4 a[NTC];
-        zero_n(a);
-        mm_afrag<D, NTC>(fa, sB + 16 * tc0, LF, a, lane);
-#pragma unroll
-        for (int t = 0; t < NTC; ++t)   // lane-blocked, as dO S
-            *reinterpret_cast<f32x4 *>(wsKt + ch * BC * D + 4 * (tid * NTC + t)) = a[t];
     }
 }
 
