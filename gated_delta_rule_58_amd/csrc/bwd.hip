@@ -501,10 +501,11 @@ __global__ __launch_bounds__(512) void bwd_dstates_kernel(
     }
 }
 
-// The same launch for bf16 inputs: K dS'^T and F^T K on bf16 MFMA over three
-// exact bf16 pieces of their fp32 operand (as in bwd_states_x3_kernel);
-// P^T dO, T^T dDelta and (e^g dO)^T Q stay fp32.  dDelta goes over the K
-// rows once those are consumed, and the pieces of F over those of dS'.
+// The same launch for bf16 inputs: K dS'^T, F^T K and (e^g dO)^T Q on bf16
+// MFMA over three exact bf16 pieces of their fp32 operand (as in
+// bwd_states_x3_kernel; Q reaches the last one by column gathers, transpose
+// reads of its rows); P^T dO and T^T dDelta stay fp32.  dDelta goes over the
+// K rows once those are consumed, and the pieces of F over those of dS'.
 template <int D, typename TG>
 __global__ __launch_bounds__(512) void bwd_dstates_x3_kernel(
     int T, int H, int NC, int varlen, const int32_t *__restrict__ cu,
@@ -641,7 +642,30 @@ __global__ __launch_bounds__(512) void bwd_dstates_x3_kernel(
 #pragma unroll
         for (int t = 0; t < NTC; ++t) st[t] = st[t] * egn;
         zero_n(fk);
-        mmn<BC, NTC>(sO + 16 * tr, 1, LDN, sQ + 16 * tc0, LI, 1, 16, st, lane);
+        // (e^g dO)^T Q: rows 16 tr + li of (e^g dO)^T are columns of sO, taken
+        // in the k order of the transpose reads of Q (tokens 4 lq + j, then
+        // 16 + 4 lq + j, of each 32-token step)
+#pragma unroll
+        for (int ks = 0; ks < BC / 32; ++ks) {
+            bf16x8 ao[3];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int tok = 32 * ks + 4 * lq + (e & 3) + (e < 4 ? 0 : 16);
+                bf16 x0, x1, x2;
+                split3(sO[tok * LDN + 16 * tr + li], x0, x1, x2);
+                ao[0][e] = x0;
+                ao[1][e] = x1;
+                ao[2][e] = x2;
+            }
+            const int tq = 32 * ks + 4 * lq + (li >> 2);
+#pragma unroll
+            for (int t = 0; t < NTC; ++t) {
+                const bf16 *pq = sQ + tq * LI + 16 * (tc0 + t) + 4 * (li & 3);
+                const bf16x8 bq = cat(lds_read_tr(pq), lds_read_tr(pq + 16 * LI));
+#pragma unroll
+                for (int pc = 0; pc < 3; ++pc) st[t] = mfma32(ao[pc], bq, st[t]);
+            }
+        }
 #pragma unroll
         for (int ks = 0; ks < BC / 32; ++ks)
 #pragma unroll
