@@ -56,24 +56,44 @@ template <int D, typename TI>
 __global__ __launch_bounds__(512) void bwd_prep_kernel(
     int T, int H, int units, int NC, int varlen, const int32_t *__restrict__ cu,
     const TI *__restrict__ q, const TI *__restrict__ k, const float *__restrict__ la,
-    const float *__restrict__ beta, float *__restrict__ wsT, float *__restrict__ wsP) {
+    const float *__restrict__ beta, float *__restrict__ wsT, float *__restrict__ wsP, int nch) {
     constexpr int LI = ldx<TI, D>();
     __shared__ __attribute__((aligned(16))) TI sK[BC * LI];
     __shared__ __attribute__((aligned(16))) TI sQ[BC * LI];
     __shared__ __attribute__((aligned(16))) float sA[BC * LDN];
     __shared__ __attribute__((aligned(16))) float sX[BC * LDN];
     __shared__ float sg[4][BC];
-    const int slot = blockIdx.x / H, h = blockIdx.x % H;
-    long row0;
-    int n;
-    if (!slot_chunk(slot, units, T, NC, varlen, cu, row0, n)) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const size_t ch = blockIdx.x;
-    load_rows<D>(sK, LI, k, row0, n, H, h, 0, D, tid, 512);
-    load_rows<D>(sQ, LI, q, row0, n, H, h, 0, D, tid, 512);
+    const int tid = threadIdx.x, wave = tid >> 6;
+    // Persistent over the (chunk slot, head) pairs ci = blockIdx.x + j gridDim.x:
+    // the next pair's K, Q rows and gates load into registers while this one
+    // is computed (rows past a ragged end are zero).
+    Prefetch<D, TI> pk, pq;
+    float gx = 0.f, gb = 0.f;
+    auto next = [&](int c) {   // first pair >= c with a chunk (unused slots skipped), and fetch it
+        long r0;
+        int nv;
+        for (; c < nch; c += gridDim.x) {
+            if (!slot_chunk(c / H, units, T, NC, varlen, cu, r0, nv)) continue;
+            const size_t g0 = (size_t)r0 * H * D + (size_t)(c % H) * D;
+            pk.fetch(k + g0, (size_t)H * D, nv, tid);
+            pq.fetch(q + g0, (size_t)H * D, nv, tid);
+            if (wave == 0) gate_fetch(la, beta, r0, nv, H, c % H, tid & 63, gx, gb);
+            break;
+        }
+        return c;
+    };
+    for (int ci = next(blockIdx.x); ci < nch;) {
+    // the lane index passes through an empty asm statement each iteration, so
+    // per-lane addresses are recomputed rather than kept live across the loop
+    int lane = tid & 63;
+    asm volatile("" : "+v"(lane));
+    const size_t ch = ci;
+    pk.commit(sK, LI, tid);
+    pq.commit(sQ, LI, tid);
     for (int e = tid; e < BC * LDN; e += 512) sX[e] = 0.f;
-    if (wave == 0) chunk_gates(sg, la, beta, row0, n, H, h, lane);
+    if (wave == 0) gate_scan(sg, gx, gb, lane);
     __syncthreads();
+    const int cn = next(ci + (int)gridDim.x);
     // waves 0-3: rows 16w.. of K K^T -> A; waves 4-7: the same rows of Q K^T -> P
     {
         const int tr = wave & 3;
@@ -115,6 +135,9 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(
         for (int e = tid; e < BC * BC / 4; e += 512)
             *reinterpret_cast<f32x4 *>(Tm + 4 * e) =
                 *reinterpret_cast<const f32x4 *>(sX + (e >> 4) * LDN + (e & 15) * 4);
+    }
+    __syncthreads();   // the next pair overwrites every LDS buffer
+    ci = cn;
     }
 }
 
@@ -1393,8 +1416,10 @@ hipError_t launch_bwd_t(int units, int T, int H, const int32_t *cu, const void *
     const TG *dOg = (const TG *)dO;
     const unsigned seq_grid = (unsigned)((long)units * H * (D / 64));
     if (nch > 0)
-        hipLaunchKernelGGL((bwd_prep_kernel<D, TI>), dim3((unsigned)nch), dim3(512), 0, st, T, H,
-                           units, NC, varlen, cu, qi, ki, la, beta, wsT, wsP);
+        // persistent: two workgroups per CU (70 KB of LDS each)
+        hipLaunchKernelGGL((bwd_prep_kernel<D, TI>), dim3((unsigned)std::min<size_t>(nch, 512)),
+                           dim3(512), 0, st, T, H, units, NC, varlen, cu, qi, ki, la, beta, wsT,
+                           wsP, (int)nch);
     if (nch > 0) {
         if constexpr (sizeof(TI) == 2)
             hipLaunchKernelGGL((bwd_states_x3_kernel<D>), dim3(seq_grid), dim3(512), 0, st, T, H,
