@@ -63,12 +63,55 @@ def flops_per_token_head(C: int, dk: int, dv: int) -> float:
     return 2.0 * macs / C
 
 
-def bytes_chunk_fwd(B, T, H, dk, dv, io_bytes=2, o_bytes=4, with_s0=False) -> float:
-    """Algorithmic HBM bytes of one forward: q, k, v, gates read once, o and
-    the final states written once (initial states read once if given)."""
+def bytes_chunk_fwd(B, T, H, dk, dv, io_bytes=2, o_bytes=4, with_s0=False,
+                    units=None) -> float:
+    """Algorithmic HBM bytes of one forward over B*T tokens: q, k, v, gates read
+    once, o and the final states written once (initial states read once if
+    given); `units` states (default B: one per batch row or packed sequence)."""
     per_th = (2 * dk + dv) * io_bytes + dv * o_bytes + 8
-    states = B * H * dv * dk * 4 * (2 if with_s0 else 1)
+    units = B if units is None else units
+    states = units * H * dv * dk * 4 * (2 if with_s0 else 1)
     return B * T * H * per_th + states
+
+
+PREHEAT_MS = 250.0   # GPU time run before each leg's counted warm-up
+MIN_TIMED = 10       # timed calls of every sub-leg, at least
+
+
+def preheat(torch, fn, min_ms=PREHEAT_MS):
+    """Run fn back to back until at least min_ms of GPU time has passed.  The
+    GPU needs tens of milliseconds of sustained load to reach its steady
+    clock; without this a short counted warm-up ends while the clock is still
+    ramping.  Returns (GPU ms, calls)."""
+    stream = torch.cuda.current_stream()
+    total, calls = 0.0, 0
+    while total < min_ms:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(4):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        total += e0.elapsed_time(e1)
+        calls += 4
+    return total, calls
+
+
+def time_calls(torch, fn, n, warm=0):
+    """ms per call of fn over n back-to-back calls (HIP events on the stream
+    the calls are launched on), after a pre-heat and `warm` untimed calls."""
+    preheat(torch, fn)
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
 
 
 def run_decode(args, torch, gi, gdn, dev):
@@ -85,8 +128,7 @@ def run_decode(args, torch, gi, gdn, dev):
     def dstep(t):
         gdn.step(dd["q"][t], dd["k"][t], dd["v"][t], dd["log_alpha"][t], dd["beta"][t], S, o=od)
 
-    for t in range(4):
-        dstep(t)
+    preheat(torch, lambda: dstep(0))
     torch.cuda.synchronize()
     S.copy_(dd["S0"])
     torch.cuda.synchronize()
@@ -187,23 +229,13 @@ def run_backward(args, torch, gi, gdn, dev, w, host):
     dO = torch.randn((B, T, H, dv), device=dev, dtype=torch.float32, generator=g)
     nbytes = gdn.chunk_bwd_workspace_size(B, T, H, dk, dv, C)
     ws = torch.empty(nbytes, device=dev, dtype=torch.uint8)
-    steps, warm = max(1, args.steps // 10), max(1, args.warmup // 10)
+    steps, warm = max(MIN_TIMED, args.steps // 10), max(1, args.warmup // 10)
 
     def step():
         gdn.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], dO, S0=d["S0"],
                       chunk=C, workspace=ws)
 
-    for _ in range(warm):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = time_calls(torch, step, steps, warm)
     nch = B * H * ((T + C - 1) // C)
     fl = bwd_flops_per_chunk_head(dk, C) * nch
     tfs = fl / (ms * 1e-3) / 1e12
@@ -243,23 +275,13 @@ def run_kda(args, torch, gi, gdn, dev, w):
     st = torch.empty((B, H, dv, dk), device=dev, dtype=torch.float32)
     ws = torch.empty(gdn.kda_fwd_workspace_size(B, T, H, dk, dv, C), device=dev,
                      dtype=torch.uint8)
-    steps, warm = max(1, args.steps // 4), max(1, args.warmup // 4)
+    steps, warm = max(MIN_TIMED, args.steps // 4), max(1, args.warmup // 4)
 
     def step():
         gdn.kda_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], None, chunk=C, o=o,
                     S_T=st, workspace=ws)
 
-    for _ in range(warm):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = time_calls(torch, step, steps, warm)
     fl = kda_flops_per_chunk_head(dk, C) * B * H * ((T + C - 1) // C)
     tfs = fl / (ms * 1e-3) / 1e12
     return {"ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
@@ -295,23 +317,13 @@ def run_gdn2(args, torch, gi, gdn, dev, w):
     st = torch.empty((B, H, dv, dk), device=dev, dtype=torch.float32)
     ws = torch.empty(gdn.gdn2_fwd_workspace_size(B, T, H, dk, dv, C), device=dev,
                      dtype=torch.uint8)
-    steps, warm = max(1, args.steps // 4), max(1, args.warmup // 4)
+    steps, warm = max(MIN_TIMED, args.steps // 4), max(1, args.warmup // 4)
 
     def step():
         gdn.gdn2_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["erase"], d["write"], None,
                      chunk=C, o=o, S_T=st, workspace=ws)
 
-    for _ in range(warm):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = time_calls(torch, step, steps, warm)
     fl = gdn2_flops_per_chunk_head(dk, C) * B * H * ((T + C - 1) // C)
     tfs = fl / (ms * 1e-3) / 1e12
     return {"ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
@@ -334,7 +346,7 @@ def run_prologue(args, torch, gi, gdn, dev, w, plain_ms):
     d = {k: (v.to(dev) if v is not None else None) for k, v in raw.items()}
     o = torch.empty((B, T, H, dv), device=dev, dtype=torch.float32)
     st = torch.empty((B, H, dv, dk), device=dev, dtype=torch.float32)
-    steps, warm = max(1, args.steps // 2), max(1, args.warmup // 2)
+    steps, warm = max(MIN_TIMED, args.steps // 2), max(1, args.warmup // 2)
 
     def fused():
         gdn.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], None, chunk=C,
@@ -349,18 +361,8 @@ def run_prologue(args, torch, gi, gdn, dev, w, plain_ms):
         gdn.chunk_fwd(q, k, d["v"], la, be, None, chunk=C, o=o, S_T=st)
 
     res = {}
-    stream = torch.cuda.current_stream()
-    for name, fn, n in (("fused", fused, steps), ("separate", separate, max(1, steps // 4))):
-        for _ in range(warm):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(n):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        res[name] = e0.elapsed_time(e1) / n
+    for name, fn, n in (("fused", fused, steps), ("separate", separate, MIN_TIMED)):
+        res[name] = time_calls(torch, fn, n, warm)
     fms = res["fused"]
     return {"ms_per_step": round(fms, 4), "tokens_per_s": round(B * T / (fms * 1e-3), 1),
             "vs_plain_call": round(fms / plain_ms, 4),
@@ -368,6 +370,102 @@ def run_prologue(args, torch, gi, gdn, dev, w, plain_ms):
             "kernel": "chunk_mfma_kernel<128,float,3>", "steps": steps,
             "inputs": "raw projections of the same workload: q, k ~ N(0,1) unnormalised, "
                       "gate pre-activations a ~ N(1,1), b ~ N(0,1)"}
+
+
+def run_other_workloads(args, torch, gi, gdn, dev, headline_ns_per_th):
+    """The mid workload (B=4 T=2048 H=8 d=64) and the packed long-context
+    workload (8 sequences of 1 024-16 384 tokens, 65 536 in all, H=16 d=128)
+    through the same entry point: ms per call, tokens/s and the HBM fraction
+    of their algorithmic bytes; for the packed one also the time per
+    token-head relative to the headline workload's (a longest sequence that
+    sets the launch time shows up as a ratio above 1)."""
+    out = {}
+    for wid in (1, 3):
+        w = gi.WORKLOADS[wid]
+        print(f"[bench] workload {wid} ({w['name']})", file=sys.stderr, flush=True)
+        host = gi.workload_inputs(wid)
+        d = {k: (v.to(dev) if v is not None else None) for k, v in host.items()}
+        B, T, H = d["q"].shape[:3]
+        dk, dv = w["dk"], w["dv"]
+        cu = d["cu_seqlens"]
+        units = B if cu is None else cu.shape[0] - 1
+        o = torch.empty((B, T, H, dv), device=dev, dtype=torch.float32)
+        st = torch.empty((units, H, dv, dk), device=dev, dtype=torch.float32)
+
+        def fn():
+            gdn.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"], cu,
+                          chunk=w["chunk"], o=o, S_T=st)
+
+        ms = time_calls(torch, fn, max(MIN_TIMED, args.steps // 4), 2)
+        nbytes = bytes_chunk_fwd(B, T, H, dk, dv, with_s0=d["S0"] is not None, units=units)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        rec = {"workload": w["name"], "ms_per_call": round(ms, 4),
+               "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+               "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                            "algorithmic_bytes": nbytes}}
+        if cu is not None:
+            lens = [int(b - a) for a, b in zip(host["cu_seqlens"][:-1], host["cu_seqlens"][1:])]
+            rec["seq_lens"] = lens
+            rec["ns_per_token_head"] = round(ms * 1e6 / (B * T * H), 4)
+            rec["vs_headline_per_token_head"] = round(
+                ms * 1e6 / (B * T * H) / headline_ns_per_th, 3)
+        else:
+            rec["note"] = "35 MB of algorithmic bytes: resident in the 256 MB MALL between calls"
+        out[w["name"]] = rec
+        del d, o, st
+    return out
+
+
+def cpu_info():
+    """CPU model, logical CPUs and the CPUs this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "cpus_available": avail}
+
+
+def run_cpu_baseline(args, host, B, T, H):
+    """The fp64 oracle on a bounded sample of the headline workload (batch
+    rows, every head and token), at the threads this process may use (16 at
+    most) and at one thread."""
+    import oracle
+    info = cpu_info()
+    rows = max(1, min(args.cpu_rows, B))
+    threads = max(1, min(16, info["cpus_available"] or 1))
+    sub = {k: (v[:rows] if v is not None else None) for k, v in host.items()
+           if k != "cu_seqlens"}
+
+    def timed(n_rows, nthreads, seconds):
+        part = {k: (v[:n_rows] if v is not None else None) for k, v in sub.items()}
+        reps, ct = 0, 0.0
+        while ct < seconds and (reps == 0 or ct / reps * (reps + 1) <= 3 * seconds):
+            c0 = time.perf_counter()
+            oracle.fwd(part["q"], part["k"], part["v"], part["log_alpha"], part["beta"],
+                       part["S0"], threads=nthreads)
+            ct += time.perf_counter() - c0
+            reps += 1
+        return reps * n_rows * T / ct, reps, ct
+
+    print(f"[bench] cpu baseline: oracle on {rows} batch row(s), {threads} threads, "
+          f">= {args.cpu_seconds:g} s, then 1 row on 1 thread", file=sys.stderr, flush=True)
+    v, reps, ct = timed(rows, threads, args.cpu_seconds)
+    v1, reps1, ct1 = timed(1, 1, args.cpu_seconds / 2)
+    return {"value": round(v, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "threads": threads, "value_1thread": round(v1, 1), **info,
+            "sample": f"{rows} of {B} batch rows (all {H} heads x {T} tokens), fp64 token "
+                      f"recurrence, run {reps} times in {ct:.2f} s on {threads} threads; "
+                      f"1 row on 1 thread {reps1} times in {ct1:.2f} s"}
 
 
 def main():
@@ -424,6 +522,7 @@ def main():
         gdn.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"],
                       chunk=C, o=o, S_T=st)
 
+    pre_ms, pre_calls = preheat(torch, step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -458,6 +557,7 @@ def main():
         print(json.dumps({"chunk_ms_per_step": round(ms, 4), "tokens_per_s": round(value, 1),
                           "GB_s": round(gbs, 1)}))
         return
+    others = run_other_workloads(args, torch, gi, gdn, dev, ms * 1e6 / (B * T * H))
     prologue = run_prologue(args, torch, gi, gdn, dev, w, ms)
     backward = run_backward(args, torch, gi, gdn, dev, w, host)
     kda = run_kda(args, torch, gi, gdn, dev, w)
@@ -465,26 +565,7 @@ def main():
     decode = run_decode(args, torch, gi, gdn, dev)
 
     # ---------------- CPU oracle baseline ----------------
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        rows = max(1, min(args.cpu_rows, B))
-        threads = min(16, os.cpu_count() or 1)
-        print(f"[bench] cpu baseline: oracle on {rows} batch row(s), {threads} threads, "
-              f"repeated for >= {args.cpu_seconds:g} s", file=sys.stderr, flush=True)
-        sub = {k: (v[:rows] if v is not None else None) for k, v in host.items()
-               if k != "cu_seqlens"}
-        reps, ct = 0, 0.0
-        while ct < args.cpu_seconds and (reps == 0 or ct / reps * (reps + 1) <= 3 * args.cpu_seconds):
-            c0 = time.perf_counter()
-            oracle.fwd(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["beta"], sub["S0"],
-                       threads=threads)
-            ct += time.perf_counter() - c0
-            reps += 1
-        cpu = {"value": round(reps * rows * T / ct, 1), "unit": "tokens/s", "cores": threads,
-               "kind": "oracle",
-               "sample": f"{rows} of {B} batch rows (all {H} heads x {T} tokens), fp64 "
-                         f"token recurrence, run {reps} times, {ct:.2f} s wall"}
+    cpu = None if args.no_cpu_baseline else run_cpu_baseline(args, host, B, T, H)
 
     line = {
         "metric": METRIC,
@@ -493,6 +574,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "preheat_ms": round(pre_ms, 1),
+        "preheat_calls": pre_calls,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -509,6 +592,7 @@ def main():
                      "algorithmic_bytes": nbytes},
         "mfma": {"achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                  "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "algorithmic_flops": fl},
+        "other_workloads": others,
         "decode": decode,
         "fused_prologue": prologue,
         "backward": backward,

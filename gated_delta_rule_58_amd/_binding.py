@@ -100,6 +100,35 @@ def _need_cuda(name, t, dtype=None):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _need_shape(name, t, shape, dtype=None, device=None):
+    """t must be a contiguous GPU tensor of exactly `shape` (and dtype, and on
+    `device`): the C ABI only sees pointers, so a smaller buffer would be read
+    or written out of bounds by the kernels."""
+    _need_cuda(name, t, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _state_or_new(name, t, shape, device, want):
+    """Caller-supplied fp32 state buffer (checked), or a new one, or None."""
+    if t is not None:
+        _need_shape(name, t, shape, torch.float32, device)
+        return t
+    return torch.empty(shape, device=device, dtype=torch.float32) if want else None
+
+
+def _out_or_new(t, shape, device, dtype):
+    """Caller-supplied output buffer (checked: fp32 or bf16), or a new one."""
+    if t is None:
+        return torch.empty(shape, device=device, dtype=dtype)
+    if t.dtype not in _DTYPE:
+        raise ValueError(f"o must be float32 or bfloat16, got {t.dtype}")
+    _need_shape("o", t, shape, None, device)
+    return t
+
+
 def _prologue(norm_qk: bool, gates: bool) -> int:
     return (PROLOGUE_NORM_QK if norm_qk else 0) | (PROLOGUE_GATES if gates else 0)
 
@@ -139,14 +168,11 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, chunk=64,
         _need_cuda("cu_seqlens", cu_seqlens, torch.int32)
         n_seqs = cu_seqlens.shape[0] - 1
     units = n_seqs if n_seqs > 0 else B
+    st_shape = (units, H, dv, dk)
     if S0 is not None:
-        _need_cuda("S0", S0, torch.float32)
-        if tuple(S0.shape) != (units, H, dv, dk):
-            raise ValueError(f"S0 must be [{units},{H},{dv},{dk}]")
-    if o is None:
-        o = torch.empty((B, T, H, dv), device=q.device, dtype=o_dtype)
-    if S_T is None and want_state:
-        S_T = torch.empty((units, H, dv, dk), device=q.device, dtype=torch.float32)
+        _need_shape("S0", S0, st_shape, torch.float32, q.device)
+    o = _out_or_new(o, (B, T, H, dv), q.device, o_dtype)
+    S_T = _state_or_new("S_T", S_T, st_shape, q.device, want_state)
     shape = GdnShape(B, T, H, dk, dv, chunk, n_seqs, _DTYPE[io], _DTYPE[o.dtype],
                      _prologue(norm_qk, gates))
     ws_bytes = ctypes.c_size_t(0)
@@ -170,11 +196,12 @@ def chunk_bwd_workspace_size(B, T, H, d_k, d_v, chunk=64, n_seqs=0,
 
 
 def chunk_bwd(q, k, v, log_alpha, beta, dO, S0=None, cu_seqlens=None, dS_T=None, chunk=64,
-              want_dS0=True, workspace=None):
+              want_dS0=True, workspace=None, out=None):
     """Backward of chunk_fwd: gradients of <dO, o> + <dS_T, S_T>.  dO
     [B,T,H,dv] (fp32 or bf16; the q/k/v gradients take its dtype); dS_T
-    [U,H,dv,dk] fp32 or None.  Returns (dq, dk, dv, dlog_alpha, dbeta, dS0)
-    (dS0 is None when want_dS0 is False)."""
+    [U,H,dv,dk] fp32 or None.  `out` optionally supplies the six gradient
+    buffers (checked like every other output).  Returns (dq, dk, dv,
+    dlog_alpha, dbeta, dS0) (dS0 is None when want_dS0 is False)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     io = q.dtype
@@ -198,13 +225,22 @@ def chunk_bwd(q, k, v, log_alpha, beta, dO, S0=None, cu_seqlens=None, dS_T=None,
             if tuple(t.shape) != (units, H, dv, dk):
                 raise ValueError(f"{name} must be [{units},{H},{dv},{dk}]")
     gd = dO.dtype
-    dq = torch.empty((B, T, H, dk), device=q.device, dtype=gd)
-    dk_ = torch.empty((B, T, H, dk), device=q.device, dtype=gd)
-    dv_ = torch.empty((B, T, H, dv), device=q.device, dtype=gd)
-    dla = torch.empty((B, T, H), device=q.device, dtype=torch.float32)
-    dbe = torch.empty((B, T, H), device=q.device, dtype=torch.float32)
-    dS0 = (torch.empty((units, H, dv, dk), device=q.device, dtype=torch.float32)
-           if want_dS0 else None)
+    shapes = (((B, T, H, dk), gd), ((B, T, H, dk), gd), ((B, T, H, dv), gd),
+              ((B, T, H), torch.float32), ((B, T, H), torch.float32),
+              ((units, H, dv, dk), torch.float32))
+    if out is None:
+        out = [torch.empty(sh, device=q.device, dtype=dt) for sh, dt in shapes]
+        if not want_dS0:
+            out[5] = None
+    else:
+        out = list(out)
+        if len(out) != 6:
+            raise ValueError("out must hold six gradient buffers (dS0 may be None)")
+        for name, t, (sh, dt) in zip(("dq", "dk", "dv", "dlog_alpha", "dbeta", "dS0"),
+                                     out, shapes):
+            if t is not None or name != "dS0":
+                _need_shape(name, t, sh, dt, q.device)
+    dq, dk_, dv_, dla, dbe, dS0 = out
     shape = GdnShape(B, T, H, dk, dv, chunk, n_seqs, _DTYPE[io], _DTYPE[gd], 0)
     need = ctypes.c_size_t(0)
     _check(lib().gdn_chunk_bwd_workspace_size(ctypes.byref(shape), ctypes.byref(need)))
@@ -237,12 +273,11 @@ def kda_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, chunk=64,
         _need_cuda("cu_seqlens", cu_seqlens, torch.int32)
         n_seqs = cu_seqlens.shape[0] - 1
     units = n_seqs if n_seqs > 0 else B
+    st_shape = (units, H, dv, dk)
     if S0 is not None:
-        _need_cuda("S0", S0, torch.float32)
-    if o is None:
-        o = torch.empty((B, T, H, dv), device=q.device, dtype=o_dtype)
-    if S_T is None and want_state:
-        S_T = torch.empty((units, H, dv, dk), device=q.device, dtype=torch.float32)
+        _need_shape("S0", S0, st_shape, torch.float32, q.device)
+    o = _out_or_new(o, (B, T, H, dv), q.device, o_dtype)
+    S_T = _state_or_new("S_T", S_T, st_shape, q.device, want_state)
     shape = GdnShape(B, T, H, dk, dv, chunk, n_seqs, _DTYPE[io], _DTYPE[o.dtype], 0)
     need = ctypes.c_size_t(0)
     _check(lib().gdn_kda_fwd_workspace_size(ctypes.byref(shape), ctypes.byref(need)))
@@ -273,12 +308,11 @@ def gdn2_fwd(q, k, v, log_alpha, erase, write, S0=None, cu_seqlens=None, chunk=6
         _need_cuda("cu_seqlens", cu_seqlens, torch.int32)
         n_seqs = cu_seqlens.shape[0] - 1
     units = n_seqs if n_seqs > 0 else B
+    st_shape = (units, H, dv, dk)
     if S0 is not None:
-        _need_cuda("S0", S0, torch.float32)
-    if o is None:
-        o = torch.empty((B, T, H, dv), device=q.device, dtype=o_dtype)
-    if S_T is None and want_state:
-        S_T = torch.empty((units, H, dv, dk), device=q.device, dtype=torch.float32)
+        _need_shape("S0", S0, st_shape, torch.float32, q.device)
+    o = _out_or_new(o, (B, T, H, dv), q.device, o_dtype)
+    S_T = _state_or_new("S_T", S_T, st_shape, q.device, want_state)
     shape = GdnShape(B, T, H, dk, dv, chunk, n_seqs, _DTYPE[io], _DTYPE[o.dtype], 0)
     need = ctypes.c_size_t(0)
     _check(lib().gdn_gdn2_fwd_workspace_size(ctypes.byref(shape), ctypes.byref(need)))
@@ -311,17 +345,18 @@ def step(q, k, v, log_alpha, beta, S, o_dtype=torch.float32, o=None, norm_qk=Fal
     """One decode step.  q,k [B,H,dk]; v [B,H,dv]; gates [B,H] fp32; S
     [B,H,dv,dk] fp32, updated in place; norm_qk / gates as in chunk_fwd.
     Returns o [B,H,dv]."""
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k must be [B,H,dk] and v [B,H,dv]")
     B, H, dk = q.shape
     dv = v.shape[-1]
     io = q.dtype
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _need_cuda(name, t, io)
-    for name, t in (("log_alpha", log_alpha), ("beta", beta), ("S", S)):
-        _need_cuda(name, t, torch.float32)
-    if tuple(S.shape) != (B, H, dv, dk):
-        raise ValueError("S must be [B,H,dv,dk]")
-    if o is None:
-        o = torch.empty((B, H, dv), device=q.device, dtype=o_dtype)
+    _need_shape("q", q, (B, H, dk), io)
+    _need_shape("k", k, (B, H, dk), io, q.device)
+    _need_shape("v", v, (B, H, dv), io, q.device)
+    for name, t in (("log_alpha", log_alpha), ("beta", beta)):
+        _need_shape(name, t, (B, H), torch.float32, q.device)
+    _need_shape("S", S, (B, H, dv, dk), torch.float32, q.device)
+    o = _out_or_new(o, (B, H, dv), q.device, o_dtype)
     _check(lib().gdn_step(B, H, dk, dv, _DTYPE[io], _DTYPE[o.dtype],
                           _prologue(norm_qk, gates), _ptr(q), _ptr(k),
                           _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(o),

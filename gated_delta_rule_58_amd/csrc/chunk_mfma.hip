@@ -80,6 +80,16 @@ __device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) 
 }
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) { return to_bf16x4(x[0], x[1], x[2], x[3]); }
 
+// x = hi + lo (+ below 2^-16 |x|), both bf16 (split_pair in gdn_common.h).
+__device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    uint32_t h0, h1, l0, l1;
+    split_pair(x[0], x[1], h0, l0);
+    split_pair(x[2], x[3], h1, l1);
+    hi = __builtin_bit_cast(bf16x4, u32x2{h0, h1});
+    lo = __builtin_bit_cast(bf16x4, u32x2{l0, l1});
+}
+
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
 // Operand tiles in LDS ("D-order rows").  An MFMA operand fragment takes, per
@@ -164,13 +174,17 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     __shared__ __attribute__((aligned(16))) bf16 sK[C * DK];        // K, D-order rows
     __shared__ __attribute__((aligned(16))) bf16 sKT[DK * C];       // K^T
     __shared__ __attribute__((aligned(16))) bf16 sV[C * kDVT];      // V slice (swizzled)
-    __shared__ __attribute__((aligned(16))) bf16 sA[C * LDC];       // A, off-diagonal blocks
+    __shared__ __attribute__((aligned(16))) bf16 sA[C * LDC];       // A, off-diagonal blocks, hi
+    __shared__ __attribute__((aligned(16))) bf16 sAl[C * LDC];      //   and lo parts
     __shared__ __attribute__((aligned(16))) float sAd[4 * BLK];     // A diag blocks, [b][col][row]
     __shared__ __attribute__((aligned(16))) float sTd[4 * BLK];     // T diag blocks, [b][row][col]
     __shared__ __attribute__((aligned(16))) float sTdT[4 * BLK];    // T diag blocks, [b][col][row]
     // the C x C factors, D-order rows
-    __shared__ __attribute__((aligned(16))) bf16 sTU[C * C];        // (T - I) diag(beta)
-    __shared__ __attribute__((aligned(16))) bf16 sTW[C * C];        // T diag(beta e^g)
+    // as hi + lo pairs
+    __shared__ __attribute__((aligned(16))) bf16 sTU[C * C];        // (T - I) diag(beta), hi
+    __shared__ __attribute__((aligned(16))) bf16 sTUl[C * C];       //   lo
+    __shared__ __attribute__((aligned(16))) bf16 sTW[C * C];        // T diag(beta e^g), hi
+    __shared__ __attribute__((aligned(16))) bf16 sTWl[C * C];       //   lo
     // P = tril(QK^T) o decay as hi + lo, chunks m and m-1
     __shared__ __attribute__((aligned(16))) bf16 sPh[2][C * C];
     __shared__ __attribute__((aligned(16))) bf16 sPl[2][C * C];
@@ -228,7 +242,9 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     // Upper off-diagonal blocks of the LDS factors are never written: zero them once.
     for (int e = tid; e < C * C / 2; e += 512) {
         reinterpret_cast<uint32_t *>(sTU)[e] = 0u;
+        reinterpret_cast<uint32_t *>(sTUl)[e] = 0u;
         reinterpret_cast<uint32_t *>(sTW)[e] = 0u;
+        reinterpret_cast<uint32_t *>(sTWl)[e] = 0u;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             reinterpret_cast<uint32_t *>(sPh[b])[e] = 0u;
@@ -347,15 +363,20 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 const f32x4 bc = ld4(&sG[gb][2][16 * b + c4]);
                 f32x4 ec = ld4(&sG[gb][1][16 * b + c4]);
                 if constexpr (NQK) ec = ec * ld4(&sG[gb][5][16 * b + c4]);
-                bf16x4 tu, tw;
+                f32x4 tu, tw;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    tu[s] = (bf16)((c4 + s < r) ? tv[s] * bc[s] : 0.f);
-                    tw[s] = (bf16)((c4 + s <= r) ? tv[s] * bc[s] * ec[s] : 0.f);
+                    tu[s] = (c4 + s < r) ? tv[s] * bc[s] : 0.f;
+                    tw[s] = (c4 + s <= r) ? tv[s] * bc[s] * ec[s] : 0.f;
                 }
+                bf16x4 uh, ul, wh, wl;
+                split4(tu, uh, ul);
+                split4(tw, wh, wl);
                 const int off = tpos<C>(16 * b + r, 16 * b + c4);
-                *reinterpret_cast<bf16x4 *>(sTU + off) = tu;
-                *reinterpret_cast<bf16x4 *>(sTW + off) = tw;
+                *reinterpret_cast<bf16x4 *>(sTU + off) = uh;
+                *reinterpret_cast<bf16x4 *>(sTUl + off) = ul;
+                *reinterpret_cast<bf16x4 *>(sTW + off) = wh;
+                *reinterpret_cast<bf16x4 *>(sTWl + off) = wl;
             };
             // ================================ phase 2
             if (prep) {
@@ -395,7 +416,10 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     *reinterpret_cast<bf16x4 *>(sPh[m & 1] + tpos<C>(r, i0)) = bf16x4{ph[0], ph[1], ph[2], ph[3]};
                     *reinterpret_cast<bf16x4 *>(sPl[m & 1] + tpos<C>(r, i0)) = bf16x4{pl[0], pl[1], pl[2], pl[3]};
                     if (ti > tj) {
-                        *reinterpret_cast<bf16x4 *>(sA + r * LDC + i0) = to_bf16x4(br * dec * G);
+                        bf16x4 ah, al;
+                        split4(br * dec * G, ah, al);
+                        *reinterpret_cast<bf16x4 *>(sA + r * LDC + i0) = ah;
+                        *reinterpret_cast<bf16x4 *>(sAl + r * LDC + i0) = al;
                     } else {
                         // Diagonal tile: K K^T is symmetric, so the registers also
                         // hold rows rr = i0 + j of column r; store A's block
@@ -494,23 +518,36 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj (16x16x16 MFMA).  Column j
             // only needs its own blocks and the diagonal ones, so producer wave
             // j < 3 computes column j with no exchange between waves.
+            // Every factor is carried as a hi + lo pair and each product as the
+            // three piece products hi*hi + lo*hi + hi*lo: with keys repeated or
+            // nearly collinear inside a chunk the entries of A approach beta
+            // and T's products cancel, so single bf16 roundings of A, T or the
+            // factors cost several per cent of o.
             auto column = [&](auto jc) {
                 constexpr int j = decltype(jc)::value;
-                bf16x4 Bop[4];   // B operands: T_jj, then T_kj (k > j)
-                f32x4 RT[4];     // RT[k] = T_kj in D layout, k > j
-                Bop[j] = to_bf16x4(ld4(sTdT + j * BLK + lm * 16 + 4 * lg));
+                bf16x4 Bh[4], Bl[4];   // B operands: T_jj, then T_kj (k > j), hi + lo
+                f32x4 RT[4];           // RT[k] = T_kj in D layout, k > j
+                split4(ld4(sTdT + j * BLK + lm * 16 + 4 * lg), Bh[j], Bl[j]);
 #pragma unroll
                 for (int i = j + 1; i < 4; ++i) {
                     f32x4 Yb = zero4();
 #pragma unroll
                     for (int kk = j; kk < i; ++kk) {
-                        const bf16x4 a = *reinterpret_cast<const bf16x4 *>(
-                            sA + (16 * i + lm) * LDC + 16 * kk + 4 * lg);
-                        Yb = mfma16(a, Bop[kk], Yb);
+                        const int aoff = (16 * i + lm) * LDC + 16 * kk + 4 * lg;
+                        const bf16x4 ah = *reinterpret_cast<const bf16x4 *>(sA + aoff);
+                        const bf16x4 al = *reinterpret_cast<const bf16x4 *>(sAl + aoff);
+                        Yb = mfma16(ah, Bh[kk], Yb);
+                        Yb = mfma16(al, Bh[kk], Yb);
+                        Yb = mfma16(ah, Bl[kk], Yb);
                     }
-                    const bf16x4 Trow = to_bf16x4(ld4(sTd + i * BLK + lm * 16 + 4 * lg));
-                    RT[i] = -mfma16(Trow, to_bf16x4(Yb), zero4());
-                    Bop[i] = to_bf16x4(RT[i]);
+                    bf16x4 trh, trl, ybh, ybl;
+                    split4(ld4(sTd + i * BLK + lm * 16 + 4 * lg), trh, trl);
+                    split4(Yb, ybh, ybl);
+                    f32x4 r = mfma16(trh, ybh, zero4());
+                    r = mfma16(trl, ybh, r);
+                    r = mfma16(trh, ybl, r);
+                    RT[i] = -r;
+                    split4(RT[i], Bh[i], Bl[i]);
                 }
                 // Scale column c = 16 j + lm by beta_c (and e^{g_c}), round once
                 // to bf16, and transpose with an identity product (exact) so that
@@ -520,11 +557,14 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 const float wc = bc * sG[gb][1][c] * (NQK ? sG[gb][5][c] : 1.f);
 #pragma unroll
                 for (int i = j + 1; i < 4; ++i) {
-                    const f32x4 tu = mfma16(to_bf16x4(RT[i] * bc), eye, zero4());
-                    const f32x4 tw = mfma16(to_bf16x4(RT[i] * wc), eye, zero4());
+                    bf16x4 uh, ul, wh, wl;
+                    split4(RT[i] * bc, uh, ul);
+                    split4(RT[i] * wc, wh, wl);
                     const int off = tpos<C>(16 * i + lm, 16 * j + 4 * lg);
-                    *reinterpret_cast<bf16x4 *>(sTU + off) = to_bf16x4(tu);
-                    *reinterpret_cast<bf16x4 *>(sTW + off) = to_bf16x4(tw);
+                    *reinterpret_cast<bf16x4 *>(sTU + off) = to_bf16x4(mfma16(uh, eye, zero4()));
+                    *reinterpret_cast<bf16x4 *>(sTUl + off) = to_bf16x4(mfma16(ul, eye, zero4()));
+                    *reinterpret_cast<bf16x4 *>(sTW + off) = to_bf16x4(mfma16(wh, eye, zero4()));
+                    *reinterpret_cast<bf16x4 *>(sTWl + off) = to_bf16x4(mfma16(wl, eye, zero4()));
                 }
             };
             if (prep) {
@@ -589,13 +629,16 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             for (int mr = 0; mr < 4; ++mr) bt[mr] = ld4(&sG[cb][2][16 * mr + 4 * lg]);
             const bf16x8 fV0 = v_frag(cw / 16, 0);
             const bf16x8 fV1 = v_frag(cw / 16, 1);
-            bf16x8 fTU[6], fTW[6];   // fragment (mr, ks), ks <= mr / 2, in that order
+            // fragment (mr, ks), ks <= mr / 2, in that order; hi and lo parts
+            bf16x8 fTU[6], fTW[6], fTUl[6], fTWl[6];
 #pragma unroll
             for (int mr = 0, f = 0; mr < 4; ++mr)
 #pragma unroll
                 for (int ks = 0; ks <= mr / 2; ++ks, ++f) {
                     fTU[f] = tfrag<C>(sTU, 16 * mr, ks, lane);
                     fTW[f] = tfrag<C>(sTW, 16 * mr, ks, lane);
+                    fTUl[f] = tfrag<C>(sTUl, 16 * mr, ks, lane);
+                    fTWl[f] = tfrag<C>(sTWl, 16 * mr, ks, lane);
                 }
             // U = diag(beta) V + (T - I) diag(beta) V; the D-order V operand
             // holds exactly this lane's rows, which gives the diagonal term.
@@ -615,7 +658,9 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 #pragma unroll
                 for (int ks = 0; ks <= mr / 2; ++ks, ++f) {
                     U[mr] = mfma32(fTU[f], ks == 0 ? fV0 : fV1, U[mr]);
+                    U[mr] = mfma32(fTUl[f], ks == 0 ? fV0 : fV1, U[mr]);
                     acc = mfma32(fTW[f], yb[ks], acc);
+                    acc = mfma32(fTWl[f], yb[ks], acc);
                 }
                 D[mr] = U[mr] - acc;
             }

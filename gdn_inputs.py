@@ -122,6 +122,69 @@ def raw_chunk_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf1
     return dict(q=q, k=k, v=v, log_alpha=a, beta=b, S0=S0, cu_seqlens=cu)
 
 
+def structured_keys(rng: np.random.Generator, B: int, T: int, H: int, dk: int,
+                    mode: str, param: float, window: int = 64,
+                    cos: float = 0.99) -> np.ndarray:
+    """Keys [B,T,H,dk] (fp64, unit rows) with the structure of repeated tokens,
+    drawn per (batch row, head) and per `window` consecutive tokens (windows
+    start at token 0, so with the chunk length as window they are the chunks):
+
+    * "repeat": runs of `param` consecutive tokens share one random unit key;
+    * "scatter": the window draws window/param distinct unit keys and each
+      token takes one of them uniformly at random (repeats at any distance);
+    * "cluster": the window draws `param` random unit directions u_j; each
+      token takes one of them at random and its key is u_j + e n,
+      renormalised, with n a random unit vector and e = sqrt(1/cos^2 - 1), so
+      the key is at cosine about `cos` from its direction (keys of one
+      cluster are nearly collinear).
+    """
+    k = np.empty((B, T, H, dk))
+    eps = np.sqrt(1.0 / cos ** 2 - 1.0)
+    for b in range(B):
+        for h in range(H):
+            for t0 in range(0, T, window):
+                n = min(window, T - t0)
+                if mode == "repeat":
+                    g = int(param)
+                    base = _unit_rows(rng, ((n + g - 1) // g, dk))
+                    x = base[np.arange(n) // g]
+                elif mode == "scatter":
+                    base = _unit_rows(rng, (max(1, window // int(param)), dk))
+                    x = base[rng.integers(0, base.shape[0], n)]
+                elif mode == "cluster":
+                    base = _unit_rows(rng, (int(param), dk))
+                    x = base[rng.integers(0, int(param), n)] + eps * _unit_rows(rng, (n, dk))
+                    x /= np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+                else:
+                    raise ValueError(f"unknown key structure {mode!r}")
+                k[b, t0:t0 + n, h] = x
+    return k
+
+
+def structured_chunk_inputs(B: int, T: int, H: int, dk: int, dv: int, mode: str,
+                            param: float, dtype: str = "bf16", alpha_mu: float = 1.0,
+                            s0_std: float = 0.0, beta_shift: float = 0.0,
+                            seed: int = 0, cu_seqlens=None, window: int = 64):
+    """chunk_inputs with the keys replaced by `structured_keys` (drawn after
+    everything else, from the same generator, per packed sequence when
+    cu_seqlens is given so windows start at each sequence start), and
+    beta + beta_shift (a shift of 1 gives beta in (1, 2))."""
+    rng = np.random.default_rng(seed)
+    inp = chunk_inputs(B, T, H, dk, dv, dtype, alpha_mu, s0_std, seed, cu_seqlens, rng=rng)
+    if cu_seqlens is None:
+        k = structured_keys(rng, B, T, H, dk, mode, param, window)
+    else:
+        k = np.empty((1, T, H, dk))
+        for s in range(len(cu_seqlens) - 1):
+            a, e = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+            if e > a:
+                k[:, a:e] = structured_keys(rng, 1, e - a, H, dk, mode, param, window)
+    inp["k"] = _cast(k, dtype)
+    if beta_shift:
+        inp["beta"] = inp["beta"] + float(beta_shift)
+    return inp
+
+
 def kda_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16",
                alpha_mu: float = 1.0, alpha_sd: float = 1.0, s0_std: float = 0.0,
                seed: int = 0, cu_seqlens=None):

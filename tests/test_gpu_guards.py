@@ -1,0 +1,171 @@
+"""Every output and workspace write stays inside its buffer, every entry point
+is bitwise deterministic, and the binding rejects mis-shaped buffers before
+anything is launched.
+
+Guard bands: each output (and each workspace) is a view into a larger buffer
+whose margins hold a sentinel; after the call the margins must be intact.
+Bad shapes: the C ABI sees only pointers, so a short buffer would be read or
+written out of bounds; the binding must raise ValueError first (no kernel is
+launched in those tests).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+import gated_delta_rule_58_amd as gdn
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+PAD = 256
+SENTINEL = 12345.0
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def dev(x):
+    return None if x is None else x.to(DEV)
+
+
+def guarded(shape, dtype=torch.float32):
+    """(view of `shape`, the whole padded buffer)."""
+    n = int(np.prod(shape))
+    buf = torch.full((n + 2 * PAD,), SENTINEL, device=DEV, dtype=dtype)
+    return buf[PAD:PAD + n].view(shape), buf
+
+
+def guarded_bytes(nbytes):
+    buf = torch.full((nbytes + 2 * PAD,), 0xA5, device=DEV, dtype=torch.uint8)
+    return buf[PAD:PAD + nbytes], buf
+
+
+def margins_intact(buf, fill):
+    c = buf.cpu()
+    return bool(torch.all(c[:PAD] == fill)) and bool(torch.all(c[-PAD:] == fill))
+
+
+def test_step_guard_bands_and_determinism():
+    d = gi.decode_inputs(3, 5, 128, 128, steps=2, seed=40)
+    outs = []
+    for rep in range(2):
+        S, sbuf = guarded((3, 5, 128, 128))
+        S.copy_(dev(d["S0"]))
+        o, obuf = guarded((3, 5, 128))
+        say(f"step guard bands rep {rep}")
+        for t in range(2):
+            gdn.step(*(dev(d[x][t]) for x in ("q", "k", "v", "log_alpha", "beta")), S, o=o)
+        torch.cuda.synchronize()
+        assert margins_intact(sbuf, SENTINEL) and margins_intact(obuf, SENTINEL)
+        outs.append((o.cpu(), S.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_chunk_fwd_bf16_o_guard_band():
+    inp = gi.chunk_inputs(2, 130, 3, 128, 128, "bf16", s0_std=0.1, seed=41)
+    o, obuf = guarded((2, 130, 3, 128), torch.bfloat16)
+    say("chunk_fwd bf16 o guard band")
+    gdn.chunk_fwd(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["log_alpha"]),
+                  dev(inp["beta"]), dev(inp["S0"]), o=o)
+    torch.cuda.synchronize()
+    assert margins_intact(obuf, SENTINEL)
+
+
+def test_chunk_bwd_guard_bands_and_determinism():
+    B, T, H, d = 2, 150, 3, 128
+    inp = gi.chunk_inputs(B, T, H, d, d, "bf16", s0_std=0.1, seed=42)
+    dO = torch.randn((B, T, H, d), generator=torch.Generator().manual_seed(1)).to(DEV)
+    nbytes = gdn.chunk_bwd_workspace_size(B, T, H, d, d)
+    res = []
+    for rep in range(2):
+        views, bufs = zip(*(guarded(sh) for sh in ((B, T, H, d), (B, T, H, d), (B, T, H, d),
+                                                     (B, T, H), (B, T, H), (B, H, d, d))))
+        ws, wsbuf = guarded_bytes(nbytes)
+        say(f"chunk_bwd guard bands rep {rep}")
+        g = gdn.chunk_bwd(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["log_alpha"]),
+                          dev(inp["beta"]), dO, S0=dev(inp["S0"]), workspace=ws, out=views)
+        torch.cuda.synchronize()
+        assert all(margins_intact(b, SENTINEL) for b in bufs)
+        assert margins_intact(wsbuf, 0xA5)
+        res.append([x.cpu() for x in g])
+    assert all(torch.equal(a, b) for a, b in zip(*res))
+
+
+@pytest.mark.parametrize("which", ["kda", "gdn2"])
+def test_channel_forwards_guard_bands_and_determinism(which):
+    B, T, H, d = 2, 150, 3, 128
+    if which == "kda":
+        inp = gi.kda_inputs(B, T, H, d, d, "bf16", s0_std=0.1, seed=43)
+        nbytes = gdn.kda_fwd_workspace_size(B, T, H, d, d)
+    else:
+        inp = gi.gdn2_inputs(B, T, H, d, d, "bf16", s0_std=0.1, seed=44)
+        nbytes = gdn.gdn2_fwd_workspace_size(B, T, H, d, d)
+    res = []
+    for rep in range(2):
+        o, obuf = guarded((B, T, H, d))
+        st, sbuf = guarded((B, H, d, d))
+        ws, wsbuf = guarded_bytes(nbytes)
+        say(f"{which} guard bands rep {rep}")
+        args = [dev(inp[x]) for x in ("q", "k", "v", "log_alpha")]
+        if which == "kda":
+            gdn.kda_fwd(*args, dev(inp["beta"]), dev(inp["S0"]), o=o, S_T=st, workspace=ws)
+        else:
+            gdn.gdn2_fwd(*args, dev(inp["erase"]), dev(inp["write"]), dev(inp["S0"]), o=o,
+                         S_T=st, workspace=ws)
+        torch.cuda.synchronize()
+        assert margins_intact(obuf, SENTINEL) and margins_intact(sbuf, SENTINEL)
+        assert margins_intact(wsbuf, 0xA5)
+        res.append((o.cpu(), st.cpu()))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+# ---------------------------------------------------------------- bad shapes
+def _fwd_args(seed=45, B=2, T=70, H=2, d=128):
+    return {k: dev(v) for k, v in gi.chunk_inputs(B, T, H, d, d, "bf16", s0_std=0.1,
+                                                 seed=seed).items()}
+
+
+def test_binding_rejects_bad_state_shapes():
+    a = _fwd_args()
+    bad = torch.zeros((2, 2, 128, 64), device=DEV)
+    with pytest.raises(ValueError):
+        gdn.chunk_fwd(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], bad)
+    with pytest.raises(ValueError):
+        gdn.chunk_fwd(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["S0"], S_T=bad)
+    with pytest.raises(ValueError):
+        gdn.chunk_fwd(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["S0"],
+                      o=torch.zeros((2, 70, 2, 64), device=DEV))
+    ka = {k: dev(v) for k, v in gi.kda_inputs(2, 70, 2, 128, 128, "bf16", s0_std=0.1,
+                                             seed=46).items()}
+    for S0 in (bad, torch.zeros((1, 2, 128, 128), device=DEV)):
+        with pytest.raises(ValueError):
+            gdn.kda_fwd(ka["q"], ka["k"], ka["v"], ka["log_alpha"], ka["beta"], S0)
+    with pytest.raises(ValueError):
+        gdn.kda_fwd(ka["q"], ka["k"], ka["v"], ka["log_alpha"], ka["beta"], ka["S0"], S_T=bad)
+    g2 = {k: dev(v) for k, v in gi.gdn2_inputs(2, 70, 2, 128, 128, "bf16", s0_std=0.1,
+                                              seed=47).items()}
+    with pytest.raises(ValueError):
+        gdn.gdn2_fwd(g2["q"], g2["k"], g2["v"], g2["log_alpha"], g2["erase"], g2["write"], bad)
+    with pytest.raises(ValueError):
+        gdn.gdn2_fwd(g2["q"], g2["k"], g2["v"], g2["log_alpha"], g2["erase"], g2["write"],
+                     g2["S0"], o=torch.zeros((2, 70, 2, 128), device=DEV, dtype=torch.float16))
+
+
+def test_binding_rejects_bad_step_shapes():
+    d = {k: dev(v) for k, v in gi.decode_inputs(3, 4, 128, 128, steps=1, seed=48).items()}
+    q, k, v, la, be = (d[x][0] for x in ("q", "k", "v", "log_alpha", "beta"))
+    S = d["S0"].clone()
+    with pytest.raises(ValueError):
+        gdn.step(q, k[:2], v, la, be, S)
+    with pytest.raises(ValueError):
+        gdn.step(q, k, v[:, :, :64], la, be, S)
+    with pytest.raises(ValueError):
+        gdn.step(q, k, v, la[:, :2], be, S)
+    with pytest.raises(ValueError):
+        gdn.step(q, k, v, la, be.reshape(-1), S)
+    with pytest.raises(ValueError):
+        gdn.step(q, k, v, la, be, S, o=torch.zeros((3, 4, 64), device=DEV))
+    with pytest.raises(ValueError):
+        gdn.step(q, k, v, la, be, S[:, :, :64].contiguous())
