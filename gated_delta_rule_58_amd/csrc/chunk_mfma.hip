@@ -14,7 +14,7 @@
 //   (5) O = diag(e^g) Q S^T + (tril(Q K^T) o e^{g_r-g_i}) Delta
 // W is never formed: W S^T = (T diag(beta e^g)) (K S^T), so the kernel keeps
 // T_W = T diag(beta e^g) and multiplies it into Y = K S^T.  U is formed as
-// diag(beta) V (fp32) plus (T - I) diag(beta) V on MFMA.
+// T_U V with T_U = T diag(beta) on MFMA.
 //
 // Work split.  One workgroup of 8 waves owns one (sequence, head, 64-column
 // slice of d_v) and walks its chunks in order, so q, k, v and the gates are
@@ -23,7 +23,7 @@
 // unit-lower inverse (four 16x16 diagonal blocks by blocked forward
 // substitution in fp32, one per wave, then the off-diagonal blocks
 // T_ij = -T_ii sum_k A_ik T_kj on 16x16 MFMA, one block column per wave), the
-// bf16 factors (T - I) diag(beta), T diag(beta e^g) and K^T -- while waves
+// bf16 factors T diag(beta), T diag(beta e^g) and K^T -- while waves
 // 4-7 ("consumers") run the state chain of chunk n.  Consumer c owns 16
 // columns of the slice and keeps its S^T columns (d_k x 16, fp32) in MFMA
 // accumulators; S^T, Y and Delta feed the next MFMA straight from registers
@@ -80,14 +80,47 @@ __device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) 
 }
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) { return to_bf16x4(x[0], x[1], x[2], x[3]); }
 
-// x = hi + lo (+ below 2^-16 |x|), both bf16 (split_pair in gdn_common.h).
-__device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo) {
+// hi + lo splits (x = hi + lo + below 2^-16 |x|, hi = bf16(x) rounded to
+// nearest even, lo = bf16(x - hi)) with the residual x - hi taken by one
+// v_dot2_f32_bf16 per element: hi_pair . (-1, 0) + a and hi_pair . (0, -1) + b
+// are exact (the products are exact and x - hi is representable), in place
+// of rebuilding hi as fp32 and subtracting.  The two selector pairs live in
+// registers: as an inline constant the compiler encodes (-1, 0) as the fp32
+// -1.0, which the hardware reads as the pair (0, -1).
+struct SplitSel {
+    uint32_t lo, hi;   // bf16 pairs (-1, 0) and (0, -1)
+};
+__device__ __forceinline__ SplitSel split_sel() {
+    SplitSel m;
+    asm("v_mov_b32 %0, 0xbf80" : "=v"(m.lo));
+    asm("v_mov_b32 %0, 0xbf800000" : "=v"(m.hi));
+    return m;
+}
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_pair2(float a, float b, const SplitSel &m, uint32_t &hi,
+                                            uint32_t &lo) {
+    const bf16x2 h = bf16x2{(bf16)a, (bf16)b};
+    hi = __builtin_bit_cast(uint32_t, h);
+    const float ra = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, m.lo), a, false);
+    const float rb = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, m.hi), b, false);
+    lo = __builtin_bit_cast(uint32_t, bf16x2{(bf16)ra, (bf16)rb});
+}
+__device__ __forceinline__ void split4(f32x4 x, const SplitSel &m, bf16x4 &hi, bf16x4 &lo) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     uint32_t h0, h1, l0, l1;
-    split_pair(x[0], x[1], h0, l0);
-    split_pair(x[2], x[3], h1, l1);
+    split_pair2(x[0], x[1], m, h0, l0);
+    split_pair2(x[2], x[3], m, h1, l1);
     hi = __builtin_bit_cast(bf16x4, u32x2{h0, h1});
     lo = __builtin_bit_cast(bf16x4, u32x2{l0, l1});
+}
+// Two D tiles (rows 0-15 and 16-31 of a 32-row block) as a D-order operand pair.
+__device__ __forceinline__ void split8(f32x4 d0, f32x4 d1, const SplitSel &m, bf16x8 &hi,
+                                       bf16x8 &lo) {
+    bf16x4 h0, l0, h1, l1;
+    split4(d0, m, h0, l0);
+    split4(d1, m, h1, l1);
+    hi = cat(h0, h1);
+    lo = cat(l0, l1);
 }
 
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
@@ -181,7 +214,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     __shared__ __attribute__((aligned(16))) float sTdT[4 * BLK];    // T diag blocks, [b][col][row]
     // the C x C factors, D-order rows
     // as hi + lo pairs
-    __shared__ __attribute__((aligned(16))) bf16 sTU[C * C];        // (T - I) diag(beta), hi
+    __shared__ __attribute__((aligned(16))) bf16 sTU[C * C];        // T diag(beta), hi
     __shared__ __attribute__((aligned(16))) bf16 sTUl[C * C];       //   lo
     __shared__ __attribute__((aligned(16))) bf16 sTW[C * C];        // T diag(beta e^g), hi
     __shared__ __attribute__((aligned(16))) bf16 sTWl[C * C];       //   lo
@@ -211,6 +244,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
     const int lm = lane & 15, lg = lane >> 4;
+    const SplitSel sm = split_sel();
 
     // Operand element (i, k) = V[32 ks + k][16 cb + i] (k in D-order) of the
     // swizzled V slice: a column gather by two transpose reads.
@@ -237,7 +271,10 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     const int N = (int)((L + C - 1) / C);
     // first token (absolute row) and valid rows of chunk c
     auto crow = [&](int c) -> size_t { return (size_t)(row0 + (long)c * C); };
-    auto cvalid = [&](int c) -> uint32_t { return (uint32_t)min((long)C, L - (long)c * C); };
+    // (0 past the last chunk: prefetches there read nothing and return zeros)
+    auto cvalid = [&](int c) -> uint32_t {
+        return (uint32_t)max(0L, min((long)C, L - (long)c * C));
+    };
 
     // Upper off-diagonal blocks of the LDS factors are never written: zero them once.
     for (int e = tid; e < C * C / 2; e += 512) {
@@ -262,9 +299,14 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
         bf16x8 pq[QK_PER_THR], pk[QK_PER_THR], pv[V_PER_THR];
         float pla = 0.f, pbe = 0.f;
         bool pvalid = false;   // this lane's token exists (gate pre-activations)
+        // The next chunk's loads are issued on every iteration, also past the
+        // last chunk (zero valid rows: the range check turns them into zeros
+        // without a memory access), so the compiler's wait counts can rely on
+        // them: a conditional load makes it wait for every outstanding load
+        // before the stores of the current chunk.
         auto prefetch_qk = [&](int c) {
-            const size_t t0 = crow(c);
             const uint32_t nv = cvalid(c);
+            const size_t t0 = nv ? crow(c) : crow(0);
             const rsrc_t rq = make_rsrc(q + (t0 * H + h) * DK, nv * H * DK * 2);
             const rsrc_t rk = make_rsrc(k + (t0 * H + h) * DK, nv * H * DK * 2);
 #pragma unroll
@@ -302,8 +344,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             sG[buf][3][lane] = exp_neg(gC - x);
         };
         auto prefetch_v = [&](int c) {
-            const size_t t0 = crow(c);
             const uint32_t nv = cvalid(c);
+            const size_t t0 = nv ? crow(c) : crow(0);
             const rsrc_t rv = make_rsrc(v + (t0 * H + h) * DV + dv0, nv * H * DV * 2);
 #pragma unroll
             for (int i = 0; i < V_PER_THR; ++i) {
@@ -316,9 +358,13 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             prefetch_v(0);
             if (pw == 3) scan_gates(0);   // later chunks are scanned a phase ahead
         }
-        for (int n = -1; n < N; ++n) {
+        // Iterations n = -1 .. N-2 prepare chunk m = n + 1; the last one
+        // (n = N - 1, nothing left to prepare) only passes the barriers, after
+        // the loop, so that every load and store inside the loop is
+        // unconditional and the compiler's wait counts stay exact.
+        for (int n = -1; n < N - 1; ++n) {
             const int m = n + 1;           // chunk being prepared
-            const bool prep = m < N;
+            constexpr bool prep = true;
             const int gb = m & 1;          // gate buffer of chunk m
             // ================================ phase 1
             if (prep) {
@@ -331,7 +377,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     *reinterpret_cast<bf16x4 *>(sK + c0) = bf16x4{pk[i][0], pk[i][1], pk[i][2], pk[i][3]};
                     *reinterpret_cast<bf16x4 *>(sK + c1) = bf16x4{pk[i][4], pk[i][5], pk[i][6], pk[i][7]};
                 }
-                if (m + 1 < N) prefetch_qk(m + 1);
+                prefetch_qk(m + 1);
                 if constexpr (NQK) {
                     // |q_r|^2 and |k_r|^2 of this wave's 16 rows: the diagonal of
                     // Q_b Q_b^T and K_b K_b^T (one fragment serves as both
@@ -355,7 +401,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 }
             }
             __syncthreads();
-            // Diagonal block b of (T - I) diag(beta) and T diag(beta e^g), one
+            // Diagonal block b of T diag(beta) and T diag(beta e^g), one
             // (row, 4 columns) per lane.
             auto diag_conv = [&](int b) {
                 const int r = lane >> 2, c4 = 4 * (lane & 3);
@@ -366,12 +412,12 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 f32x4 tu, tw;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    tu[s] = (c4 + s < r) ? tv[s] * bc[s] : 0.f;
+                    tu[s] = (c4 + s <= r) ? tv[s] * bc[s] : 0.f;
                     tw[s] = (c4 + s <= r) ? tv[s] * bc[s] * ec[s] : 0.f;
                 }
                 bf16x4 uh, ul, wh, wl;
-                split4(tu, uh, ul);
-                split4(tw, wh, wl);
+                split4(tu, sm, uh, ul);
+                split4(tw, sm, wh, wl);
                 const int off = tpos<C>(16 * b + r, 16 * b + c4);
                 *reinterpret_cast<bf16x4 *>(sTU + off) = uh;
                 *reinterpret_cast<bf16x4 *>(sTUl + off) = ul;
@@ -410,14 +456,13 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     f32x4 dec;   // e^{g_r - g_i} on and below the diagonal, else 0
 #pragma unroll
                     for (int j = 0; j < 4; ++j) dec[j] = (i0 + j <= r) ? exp_neg(gr - gi[j]) : 0.f;
-                    const f32x4 p4 = dec * PT;
-                    bf16x8 ph, pl;
-                    split_op(p4, p4, ph, pl);
-                    *reinterpret_cast<bf16x4 *>(sPh[m & 1] + tpos<C>(r, i0)) = bf16x4{ph[0], ph[1], ph[2], ph[3]};
-                    *reinterpret_cast<bf16x4 *>(sPl[m & 1] + tpos<C>(r, i0)) = bf16x4{pl[0], pl[1], pl[2], pl[3]};
+                    bf16x4 ph, pl;
+                    split4(dec * PT, sm, ph, pl);
+                    *reinterpret_cast<bf16x4 *>(sPh[m & 1] + tpos<C>(r, i0)) = ph;
+                    *reinterpret_cast<bf16x4 *>(sPl[m & 1] + tpos<C>(r, i0)) = pl;
                     if (ti > tj) {
                         bf16x4 ah, al;
-                        split4(br * dec * G, ah, al);
+                        split4(br * dec * G, sm, ah, al);
                         *reinterpret_cast<bf16x4 *>(sA + r * LDC + i0) = ah;
                         *reinterpret_cast<bf16x4 *>(sAl + r * LDC + i0) = al;
                     } else {
@@ -527,27 +572,45 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 constexpr int j = decltype(jc)::value;
                 bf16x4 Bh[4], Bl[4];   // B operands: T_jj, then T_kj (k > j), hi + lo
                 f32x4 RT[4];           // RT[k] = T_kj in D layout, k > j
-                split4(ld4(sTdT + j * BLK + lm * 16 + 4 * lg), Bh[j], Bl[j]);
+                bf16x4 Ah[4][4], Al[4][4], Th[4], Tl[4];   // A_ik and T_ii (i > j), hi + lo
+                split4(ld4(sTdT + j * BLK + lm * 16 + 4 * lg), sm, Bh[j], Bl[j]);
 #pragma unroll
                 for (int i = j + 1; i < 4; ++i) {
-                    f32x4 Yb = zero4();
 #pragma unroll
                     for (int kk = j; kk < i; ++kk) {
                         const int aoff = (16 * i + lm) * LDC + 16 * kk + 4 * lg;
-                        const bf16x4 ah = *reinterpret_cast<const bf16x4 *>(sA + aoff);
-                        const bf16x4 al = *reinterpret_cast<const bf16x4 *>(sAl + aoff);
-                        Yb = mfma16(ah, Bh[kk], Yb);
-                        Yb = mfma16(al, Bh[kk], Yb);
-                        Yb = mfma16(ah, Bl[kk], Yb);
+                        Ah[i][kk] = *reinterpret_cast<const bf16x4 *>(sA + aoff);
+                        Al[i][kk] = *reinterpret_cast<const bf16x4 *>(sAl + aoff);
                     }
-                    bf16x4 trh, trl, ybh, ybl;
-                    split4(ld4(sTd + i * BLK + lm * 16 + 4 * lg), trh, trl);
-                    split4(Yb, ybh, ybl);
-                    f32x4 r = mfma16(trh, ybh, zero4());
-                    r = mfma16(trl, ybh, r);
-                    r = mfma16(trh, ybl, r);
-                    RT[i] = -r;
-                    split4(RT[i], Bh[i], Bl[i]);
+                    split4(ld4(sTd + i * BLK + lm * 16 + 4 * lg), sm, Th[i], Tl[i]);
+                }
+                // Y_i = sum_k A_ik T_kj, kept as two accumulators per block (the
+                // hi*hi + lo*hi and the hi*lo pieces): the T_jj terms of every
+                // block start at once, and each solved block T_kj is added to
+                // all later blocks before the next one is solved, so only one
+                // product per block sits on the column's dependency chain.
+                f32x4 Ya[4], Yc[4];
+#pragma unroll
+                for (int i = j + 1; i < 4; ++i) {
+                    Ya[i] = mfma16(Ah[i][j], Bh[j], zero4());
+                    Yc[i] = mfma16(Ah[i][j], Bl[j], zero4());
+                    Ya[i] = mfma16(Al[i][j], Bh[j], Ya[i]);
+                }
+#pragma unroll
+                for (int k = j + 1; k < 4; ++k) {
+                    bf16x4 ybh, ybl;
+                    split4(Ya[k] + Yc[k], sm, ybh, ybl);
+                    f32x4 r = mfma16(Th[k], ybh, zero4());
+                    const f32x4 r2 = mfma16(Th[k], ybl, zero4());
+                    r = mfma16(Tl[k], ybh, r);
+                    RT[k] = -(r + r2);
+                    split4(RT[k], sm, Bh[k], Bl[k]);
+#pragma unroll
+                    for (int i = k + 1; i < 4; ++i) {
+                        Ya[i] = mfma16(Ah[i][k], Bh[k], Ya[i]);
+                        Yc[i] = mfma16(Ah[i][k], Bl[k], Yc[i]);
+                        Ya[i] = mfma16(Al[i][k], Bh[k], Ya[i]);
+                    }
                 }
                 // Scale column c = 16 j + lm by beta_c (and e^{g_c}), round once
                 // to bf16, and transpose with an identity product (exact) so that
@@ -558,8 +621,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 #pragma unroll
                 for (int i = j + 1; i < 4; ++i) {
                     bf16x4 uh, ul, wh, wl;
-                    split4(RT[i] * bc, uh, ul);
-                    split4(RT[i] * wc, wh, wl);
+                    split4(RT[i] * bc, sm, uh, ul);
+                    split4(RT[i] * wc, sm, wh, wl);
                     const int off = tpos<C>(16 * i + lm, 16 * j + 4 * lg);
                     *reinterpret_cast<bf16x4 *>(sTU + off) = to_bf16x4(mfma16(uh, eye, zero4()));
                     *reinterpret_cast<bf16x4 *>(sTUl + off) = to_bf16x4(mfma16(ul, eye, zero4()));
@@ -577,26 +640,42 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     *reinterpret_cast<bf16x4 *>(dv + 4 * ((2 * p + 1) ^ f)) = bf16x4{pv[i][4], pv[i][5], pv[i][6], pv[i][7]};
                 }
                 // K^T of chunk m for its state update (the consumers finished
-                // with the previous one in phase 2): tokens 16 pw..16 pw+15, all
-                // of d_k, by identity products on 16x16 blocks.
-                bf16x4 kb[DK / 16];
+                // with the previous one in phase 2), 16 tokens at a time, all of
+                // d_k, by identity products on 16x16 blocks.  Wave j < 3 forms
+                // T's block column j (column 0 is the longest), so the token
+                // groups go to the other waves: wave 3 transposes groups 0 and
+                // 3, waves 1 and 2 their own.
+                auto ktrans = [&](int grp) {
+                    bf16x4 kb[DK / 16];
 #pragma unroll
-                for (int cb = 0; cb < DK / 16; ++cb)
-                    kb[cb] = *reinterpret_cast<const bf16x4 *>(sK + tpos<DK>(16 * pw + lm, 16 * cb + 4 * lg));
-                f32x4 kt[DK / 16];
+                    for (int cb = 0; cb < DK / 16; ++cb)
+                        kb[cb] = *reinterpret_cast<const bf16x4 *>(sK + tpos<DK>(16 * grp + lm, 16 * cb + 4 * lg));
+                    f32x4 kt[DK / 16];
 #pragma unroll
-                for (int cb = 0; cb < DK / 16; ++cb) kt[cb] = mfma16(kb[cb], eye, zero4());
+                    for (int cb = 0; cb < DK / 16; ++cb) kt[cb] = mfma16(kb[cb], eye, zero4());
 #pragma unroll
-                for (int cb = 0; cb < DK / 16; ++cb)
-                    *reinterpret_cast<bf16x4 *>(sKT + tpos<C>(16 * cb + lm, 16 * pw + 4 * lg)) = to_bf16x4(kt[cb]);
+                    for (int cb = 0; cb < DK / 16; ++cb)
+                        *reinterpret_cast<bf16x4 *>(sKT + tpos<C>(16 * cb + lm, 16 * grp + 4 * lg)) = to_bf16x4(kt[cb]);
+                };
+                if (pw == 3) {
+                    ktrans(0);
+                    ktrans(3);
+                } else if (pw != 0) {
+                    ktrans(pw);
+                }
                 if (pw == 0) column(IntC<0>{});
                 else if (pw == 1) column(IntC<1>{});
                 else if (pw == 2) column(IntC<2>{});
                 // chunk m+1's gates go to the buffer chunk n used (the consumers
-                // are done with it)
-                else if (m + 1 < N) scan_gates(gb ^ 1);
-                if (m + 1 < N) prefetch_v(m + 1);
+                // are done with it; past the last chunk they are unused)
+                else scan_gates(gb ^ 1);
+                prefetch_v(m + 1);
             }
+            __syncthreads();
+        }
+        if (N > 0) {   // iteration n = N - 1: the consumers finish the last chunk
+            __syncthreads();
+            __syncthreads();
             __syncthreads();
         }
         return;
@@ -624,9 +703,6 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
         const int cb = (m & 1) ^ 1;     // gate buffer of chunk n
         // ================================ phase 1
         if (chain) {
-            f32x4 bt[4];   // beta_r at rows 16 mr + 4 lg + j
-#pragma unroll
-            for (int mr = 0; mr < 4; ++mr) bt[mr] = ld4(&sG[cb][2][16 * mr + 4 * lg]);
             const bf16x8 fV0 = v_frag(cw / 16, 0);
             const bf16x8 fV1 = v_frag(cw / 16, 1);
             // fragment (mr, ks), ks <= mr / 2, in that order; hi and lo parts
@@ -640,16 +716,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     fTUl[f] = tfrag<C>(sTUl, 16 * mr, ks, lane);
                     fTWl[f] = tfrag<C>(sTWl, 16 * mr, ks, lane);
                 }
-            // U = diag(beta) V + (T - I) diag(beta) V; the D-order V operand
-            // holds exactly this lane's rows, which gives the diagonal term.
-            f32x4 U[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                U[0][j] = bt[0][j] * (float)fV0[j];
-                U[1][j] = bt[1][j] * (float)fV0[4 + j];
-                U[2][j] = bt[2][j] * (float)fV1[j];
-                U[3][j] = bt[3][j] * (float)fV1[4 + j];
-            }
+            // U = T diag(beta) V (the factor's diagonal holds beta)
+            f32x4 U[4] = {zero4(), zero4(), zero4(), zero4()};
             // Delta = U - T_W Y
             f32x4 D[4];
 #pragma unroll
@@ -670,11 +738,11 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 ed[mr] = ld4(&sG[cb][3][16 * mr + 4 * lg]);
                 if constexpr (NQK) ed[mr] = ed[mr] * ld4(&sG[cb][5][16 * mr + 4 * lg]);
             }
-            split_op(D[0], D[1], dh[0], dl[0]);
-            split_op(D[2], D[3], dh[1], dl[1]);
+            split8(D[0], D[1], sm, dh[0], dl[0]);
+            split8(D[2], D[3], sm, dh[1], dl[1]);
             // Delta~ for the state update
-            split_op(D[0] * ed[0], D[1] * ed[1], th[0], tl[0]);
-            split_op(D[2] * ed[2], D[3] * ed[3], th[1], tl[1]);
+            split8(D[0] * ed[0], D[1] * ed[1], sm, th[0], tl[0]);
+            split8(D[2] * ed[2], D[3] * ed[3], sm, th[1], tl[1]);
         }
         __syncthreads();
         // ================================ phase 2
@@ -731,7 +799,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             // hi + lo split of the updated state for the next phase's products
             // (here it overlaps the output products of this phase)
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) split_op(st[2 * ks], st[2 * ks + 1], sh[ks], sl[ks]);
+            for (int ks = 0; ks < NKS; ++ks) split8(st[2 * ks], st[2 * ks + 1], sm, sh[ks], sl[ks]);
         }
         __syncthreads();
         // ================================ phase 3
@@ -787,6 +855,11 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
         for (int mt = 0; mt < NMT; ++mt)
             *reinterpret_cast<f32x4 *>(S_T + sbase + (size_t)dvw * DK + 16 * mt + 4 * lg) = st[mt];
     }
+    // The compiler may join this exit with the producers' entry block; with
+    // nothing outstanding here its wait counts in the producer loop stay
+    // exact (otherwise the loads above count as pending there, and the
+    // producers wait for all their prefetches before each store).
+    __builtin_amdgcn_s_waitcnt(0);
 }
 
 bool chunk_mfma_supported(int dk, int dv, int chunk) {
