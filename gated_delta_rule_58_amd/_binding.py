@@ -40,6 +40,8 @@ SYMBOLS = {
     "gdn_kda_fwd_workspace_size": (_c_int, [ctypes.POINTER(GdnShape),
                                             ctypes.POINTER(_sz)]),
     "gdn_kda_fwd": (_c_int, [ctypes.POINTER(GdnShape)] + [_vp] * 10 + [_sz, _vp]),
+    "gdn_kda_fwd_noalloc": (_c_int, [ctypes.POINTER(GdnShape)] + [_vp] * 9 + [_vp]),
+    "gdn_kda_fwd_noalloc_max_workspace": (_sz, []),
     "gdn_gdn2_fwd_workspace_size": (_c_int, [ctypes.POINTER(GdnShape),
                                              ctypes.POINTER(_sz)]),
     "gdn_gdn2_fwd": (_c_int, [ctypes.POINTER(GdnShape)] + [_vp] * 11 + [_sz, _vp]),
@@ -287,6 +289,41 @@ def kda_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, chunk=64,
                              _ptr(beta), _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(S_T),
                              _ptr(workspace), workspace.numel(), _stream(q.device)))
     return o, S_T
+
+
+def kda_fwd_noalloc(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, chunk=64,
+                    o_dtype=torch.float32, o=None, S_T=None, want_state=True):
+    """kda_fwd with the workspace taken from the library's device array
+    (gdn_kda_fwd_noalloc): no workspace argument and no device allocation in
+    the library.  Outputs are allocated here (torch) unless o / S_T are
+    given, so a caller that must not allocate passes both.  Returns (o, S_T)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    io = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need_shape(name, t, (B, T, H, dk if name != "v" else dv), io, q.device)
+    _need_shape("log_alpha", log_alpha, (B, T, H, dk), torch.float32, q.device)
+    _need_shape("beta", beta, (B, T, H), torch.float32, q.device)
+    n_seqs = 0
+    if cu_seqlens is not None:
+        _need_cuda("cu_seqlens", cu_seqlens, torch.int32)
+        n_seqs = cu_seqlens.shape[0] - 1
+    units = n_seqs if n_seqs > 0 else B
+    st_shape = (units, H, dv, dk)
+    if S0 is not None:
+        _need_shape("S0", S0, st_shape, torch.float32, q.device)
+    o = _out_or_new(o, (B, T, H, dv), q.device, o_dtype)
+    S_T = _state_or_new("S_T", S_T, st_shape, q.device, want_state)
+    shape = GdnShape(B, T, H, dk, dv, chunk, n_seqs, _DTYPE[io], _DTYPE[o.dtype], 0)
+    _check(lib().gdn_kda_fwd_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
+                                     _ptr(o), _ptr(S_T), _stream(q.device)))
+    return o, S_T
+
+
+def kda_fwd_noalloc_max_workspace() -> int:
+    """Bytes of the library's device array behind kda_fwd_noalloc."""
+    return int(lib().gdn_kda_fwd_noalloc_max_workspace())
 
 
 def gdn2_fwd(q, k, v, log_alpha, erase, write, S0=None, cu_seqlens=None, chunk=64,

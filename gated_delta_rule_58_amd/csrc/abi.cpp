@@ -33,6 +33,8 @@ hipError_t launch_chunk_bwd(int units, int T, int H, int d, bool io_bf16, bool g
                             float *dla, float *dbeta, float *dS0, void *ws, hipStream_t st);
 bool kda_supported(int dk, int dv, int chunk, bool io_bf16);
 size_t kda_ws_bytes(int units, int T, int H, int d, bool varlen);
+size_t kda_scratch_bytes();
+hipError_t kda_scratch_ptr(void **ptr);
 hipError_t launch_kda_fwd(int units, int T, int H, int d, bool io_bf16, bool o_bf16,
                           const int32_t *cu, const void *q, const void *k, const void *v,
                           const float *la, const float *beta, const float *S0, void *o,
@@ -263,10 +265,13 @@ int gdn_kda_fwd_workspace_size(const gdn_shape *shape, size_t *bytes) {
     return ok();
 }
 
-int gdn_kda_fwd(const gdn_shape *s, const void *q, const void *k, const void *v,
-                const float *log_alpha, const float *beta, const float *S0,
-                const int32_t *cu_seqlens, void *o, float *S_T, void *workspace,
-                size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+// Argument checks of gdn_kda_fwd and gdn_kda_fwd_noalloc (all but the workspace).
+int check_kda_args(const gdn_shape *s, const void *q, const void *k, const void *v,
+                   const float *log_alpha, const float *beta, const float *S0,
+                   const int32_t *cu_seqlens, void *o, float *S_T, void *workspace) {
     int rc = check_fp32tile_shape(s, 1);
     if (rc != GDN_OK) return rc;
     if (s->n_seqs > 0 && !cu_seqlens)
@@ -283,6 +288,18 @@ int gdn_kda_fwd(const gdn_shape *s, const void *q, const void *k, const void *v,
             return fail(GDN_ERR_ALIGNMENT, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
     if (o && (o == q || o == k || o == v))
         return fail(GDN_ERR_INVALID_ARG, "o must not alias q, k or v");
+    return GDN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int gdn_kda_fwd(const gdn_shape *s, const void *q, const void *k, const void *v,
+                const float *log_alpha, const float *beta, const float *S0,
+                const int32_t *cu_seqlens, void *o, float *S_T, void *workspace,
+                size_t workspace_bytes, void *stream) {
+    int rc = check_kda_args(s, q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, workspace);
+    if (rc != GDN_OK) return rc;
     size_t need = 0;
     gdn_kda_fwd_workspace_size(s, &need);
     if (workspace_bytes < need)
@@ -292,6 +309,33 @@ int gdn_kda_fwd(const gdn_shape *s, const void *q, const void *k, const void *v,
     const hipError_t e = gdn::launch_kda_fwd(
         units, s->T, s->H, s->d_k, s->io_dtype == GDN_BF16, s->o_dtype == GDN_BF16, cu_seqlens, q,
         k, v, log_alpha, beta, S0, o, S_T, workspace, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t gdn_kda_fwd_noalloc_max_workspace(void) { return gdn::kda_scratch_bytes(); }
+
+int gdn_kda_fwd_noalloc(const gdn_shape *s, const void *q, const void *k, const void *v,
+                        const float *log_alpha, const float *beta, const float *S0,
+                        const int32_t *cu_seqlens, void *o, float *S_T, void *stream) {
+    int rc = check_kda_args(s, q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T, nullptr);
+    if (rc != GDN_OK) return rc;
+    size_t need = 0;
+    gdn_kda_fwd_workspace_size(s, &need);
+    const size_t cap = gdn::kda_scratch_bytes();
+    if (need > cap)
+        return fail(GDN_ERR_WORKSPACE,
+                    "gdn_kda_fwd_noalloc: this shape needs %zu bytes of workspace, the library's "
+                    "device scratch holds %zu; use gdn_kda_fwd with a caller workspace",
+                    need, cap);
+    void *ws = nullptr;
+    hipError_t e = gdn::kda_scratch_ptr(&ws);
+    if (e != hipSuccess)
+        return fail(GDN_ERR_HIP, "device scratch address unavailable: %s", hipGetErrorString(e));
+    const int units = s->n_seqs > 0 ? s->n_seqs : s->B;
+    e = gdn::launch_kda_fwd(units, s->T, s->H, s->d_k, s->io_dtype == GDN_BF16,
+                            s->o_dtype == GDN_BF16, cu_seqlens, q, k, v, log_alpha, beta, S0, o,
+                            S_T, ws, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }

@@ -28,6 +28,8 @@
 //      chunks in order): the state recurrence and the outputs.
 #include "fp32_tiles.h"
 
+#include <mutex>
+
 namespace gdn {
 namespace {
 
@@ -335,6 +337,38 @@ size_t kda_ws_bytes(int units, int T, int H, int d, bool varlen) {
     const long nslots = varlen ? (long)T / BC + units + 1 : (long)units * ((T + BC - 1) / BC);
     const size_t per = d == 128 ? KdaWs<128>::total : KdaWs<64>::total;
     return sizeof(float) * (size_t)nslots * H * per;
+}
+
+// ---------------------------------------------------------------- no allocation
+// Workspace of gdn_kda_fwd_noalloc: a file-scope device array, one copy per
+// GPU the library runs on, held until the process ends.  Host code never
+// passes `scratch` itself (on the host it only names the symbol); it asks
+// the runtime for this device's address once and keeps it per device.
+constexpr size_t kKdaScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kKdaScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+size_t kda_scratch_bytes() { return kKdaScratchBytes; }
+
+hipError_t kda_scratch_ptr(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_kda_fwd(int units, int T, int H, int d, bool io_bf16, bool o_bf16,

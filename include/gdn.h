@@ -197,6 +197,31 @@ int gdn_kda_fwd(const gdn_shape *shape,
                 void *workspace, size_t workspace_bytes,
                 void *stream);
 
+/* gdn_kda_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and results, with the workspace taken from a device
+ * array inside the library (64 MiB, one per GPU the library runs on, held
+ * until the process ends) instead of a caller buffer.  Every argument as in
+ * gdn_kda_fwd; the caller still supplies o and S_T.  Shapes whose
+ * gdn_kda_fwd_workspace_size exceeds gdn_kda_fwd_noalloc_max_workspace()
+ * are rejected with GDN_ERR_WORKSPACE before anything is enqueued (64 MiB
+ * holds 512 chunk-heads at d = 128, e.g. one sequence of 2048 tokens with 16
+ * heads).  The device current on the calling thread must be the one the
+ * pointers and the stream belong to; the first call on a device looks up
+ * that device's copy of the array (no allocation).  Calls on one GPU share
+ * its array: calls that overlap in time on one GPU (different streams, or
+ * host threads) race and give wrong results; calls ordered on one stream
+ * are safe.  Allocates nothing.  Returns a gdn_status. */
+int gdn_kda_fwd_noalloc(const gdn_shape *shape,
+                        const void *q, const void *k, const void *v,
+                        const float *log_alpha, const float *beta,
+                        const float *S0, const int32_t *cu_seqlens,
+                        void *o, float *S_T,
+                        void *stream);
+
+/* Size in bytes of the device array gdn_kda_fwd_noalloc uses as workspace. */
+size_t gdn_kda_fwd_noalloc_max_workspace(void);
+
 /* Bytes of device workspace gdn_gdn2_fwd needs for `shape`: per chunk of 64
  * tokens and head, two 64 x 64 and four 64 x d fp32 blocks and e^{G_n}
  * (about 160 KiB at d = 128).  Returns a gdn_status. */

@@ -217,3 +217,24 @@ def test_gdn2_workspace_and_rejects():
     assert call(wsb=16) == WORKSPACE
     assert call(erase=None, wsb=1 << 40) == INVALID
     assert call(erase=MIS, wsb=1 << 40) == ALIGN
+
+
+def test_kda_noalloc_rejects_before_launch():
+    """The no-allocation KDA entry point checks its arguments and its array
+    size on the host: nothing here reaches the GPU."""
+    L = B.lib()
+    cap = L.gdn_kda_fwd_noalloc_max_workspace()
+    assert cap == 64 << 20
+    shape = B.GdnShape(1, 8192, 16, 128, 128, 64, 0, B.GDN_BF16, B.GDN_F32, 0)
+    need = ctypes.c_size_t(0)
+    assert L.gdn_kda_fwd_workspace_size(ctypes.byref(shape), ctypes.byref(need)) == 0
+    assert need.value > cap
+    fake = ctypes.c_void_p(1 << 20)
+    out = ctypes.c_void_p(1 << 21)
+    rc = L.gdn_kda_fwd_noalloc(ctypes.byref(shape), fake, fake, fake, fake, fake, None, None,
+                               out, None, None)
+    assert rc == 4 and b"scratch" in L.gdn_last_error()
+    bad = B.GdnShape(1, 64, 2, 128, 96, 64, 0, B.GDN_BF16, B.GDN_F32, 0)
+    rc = L.gdn_kda_fwd_noalloc(ctypes.byref(bad), fake, fake, fake, fake, fake, None, None,
+                               out, None, None)
+    assert rc == 2   # GDN_ERR_UNSUPPORTED (d_k != d_v)
