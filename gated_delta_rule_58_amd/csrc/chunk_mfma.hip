@@ -12,9 +12,9 @@
 //   (3) U = T diag(beta) V,  W = T diag(beta e^g) K
 //   (4) Delta = U - W S^T;   S <- e^{g_C} S + Delta^T diag(e^{g_C-g}) K
 //   (5) O = diag(e^g) Q S^T + (tril(Q K^T) o e^{g_r-g_i}) Delta
-// W is never formed: W S^T = (T diag(beta e^g)) (K S^T), so the kernel keeps
-// T_W = T diag(beta e^g) and multiplies it into Y = K S^T.  U is formed as
-// T_U V with T_U = T diag(beta) on MFMA.
+// Neither U nor W is formed: U - W S^T = T diag(beta) (V - diag(e^g) K S^T),
+// so the kernel keeps the one factor T_U = T diag(beta) and multiplies it
+// into Z = V - diag(e^g) Y with Y = K S^T.
 //
 // Work split.  One workgroup of 8 waves owns one (sequence, head, 64-column
 // slice of d_v) and walks its chunks in order, so q, k, v and the gates are
@@ -23,7 +23,7 @@
 // unit-lower inverse (four 16x16 diagonal blocks by blocked forward
 // substitution in fp32, one per wave, then the off-diagonal blocks
 // T_ij = -T_ii sum_k A_ik T_kj on 16x16 MFMA, one block column per wave), the
-// bf16 factors T diag(beta), T diag(beta e^g) and K^T -- while waves
+// factor T diag(beta) as a bf16 hi + lo pair and K^T -- while waves
 // 4-7 ("consumers") run the state chain of chunk n.  Consumer c owns 16
 // columns of the slice and keeps its S^T columns (d_k x 16, fp32) in MFMA
 // accumulators; S^T, Y and Delta feed the next MFMA straight from registers
@@ -31,7 +31,7 @@
 // phases; every LDS buffer is written by one phase and read in later ones
 // before it is overwritten (P and the gates are double-buffered):
 //   phase  producers (chunk n+1)               consumers (chunk n)
-//   1      store q,k, prefetch chunk n+2       U, Delta, Delta~
+//   1      store q,k, prefetch chunk n+2       Z, Delta, Delta~
 //   2      K K^T, Q K^T -> A, P; each wave     S <- e^{g_C} S + K^T Delta~,
 //          inverts and converts the diagonal   P Delta, write o
 //          block of A it computed
@@ -43,7 +43,8 @@
 // are dropped by the hardware range check, so no lane branches on bounds.
 // Precision: outputs are heavy-tailed (max |o| is 10-20x its RMS), so the
 // operands carrying the state or the corrected values are split into
-// hi + lo bf16 pairs (S^T, Y, Delta, Delta~, P) and o is written in fp32
+// hi + lo bf16 pairs (S^T, Z, Delta, Delta~, P, and A, T and T diag(beta)
+// in the UT transform) and o is written in fp32
 // (or bf16 on request).
 #include "gdn_common.h"
 
@@ -216,8 +217,6 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     // as hi + lo pairs
     __shared__ __attribute__((aligned(16))) bf16 sTU[C * C];        // T diag(beta), hi
     __shared__ __attribute__((aligned(16))) bf16 sTUl[C * C];       //   lo
-    __shared__ __attribute__((aligned(16))) bf16 sTW[C * C];        // T diag(beta e^g), hi
-    __shared__ __attribute__((aligned(16))) bf16 sTWl[C * C];       //   lo
     // P = tril(QK^T) o decay as hi + lo, chunks m and m-1
     __shared__ __attribute__((aligned(16))) bf16 sPh[2][C * C];
     __shared__ __attribute__((aligned(16))) bf16 sPl[2][C * C];
@@ -280,8 +279,6 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     for (int e = tid; e < C * C / 2; e += 512) {
         reinterpret_cast<uint32_t *>(sTU)[e] = 0u;
         reinterpret_cast<uint32_t *>(sTUl)[e] = 0u;
-        reinterpret_cast<uint32_t *>(sTW)[e] = 0u;
-        reinterpret_cast<uint32_t *>(sTWl)[e] = 0u;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             reinterpret_cast<uint32_t *>(sPh[b])[e] = 0u;
@@ -401,28 +398,19 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 }
             }
             __syncthreads();
-            // Diagonal block b of T diag(beta) and T diag(beta e^g), one
-            // (row, 4 columns) per lane.
+            // Diagonal block b of T diag(beta), one (row, 4 columns) per lane.
             auto diag_conv = [&](int b) {
                 const int r = lane >> 2, c4 = 4 * (lane & 3);
                 const f32x4 tv = ld4(sTd + b * BLK + r * 16 + c4);
                 const f32x4 bc = ld4(&sG[gb][2][16 * b + c4]);
-                f32x4 ec = ld4(&sG[gb][1][16 * b + c4]);
-                if constexpr (NQK) ec = ec * ld4(&sG[gb][5][16 * b + c4]);
-                f32x4 tu, tw;
+                f32x4 tu;
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    tu[s] = (c4 + s <= r) ? tv[s] * bc[s] : 0.f;
-                    tw[s] = (c4 + s <= r) ? tv[s] * bc[s] * ec[s] : 0.f;
-                }
-                bf16x4 uh, ul, wh, wl;
+                for (int s = 0; s < 4; ++s) tu[s] = (c4 + s <= r) ? tv[s] * bc[s] : 0.f;
+                bf16x4 uh, ul;
                 split4(tu, sm, uh, ul);
-                split4(tw, sm, wh, wl);
                 const int off = tpos<C>(16 * b + r, 16 * b + c4);
                 *reinterpret_cast<bf16x4 *>(sTU + off) = uh;
                 *reinterpret_cast<bf16x4 *>(sTUl + off) = ul;
-                *reinterpret_cast<bf16x4 *>(sTW + off) = wh;
-                *reinterpret_cast<bf16x4 *>(sTWl + off) = wl;
             };
             // ================================ phase 2
             if (prep) {
@@ -612,22 +600,17 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                         Ya[i] = mfma16(Al[i][k], Bh[k], Ya[i]);
                     }
                 }
-                // Scale column c = 16 j + lm by beta_c (and e^{g_c}), round once
-                // to bf16, and transpose with an identity product (exact) so that
-                // each lane writes 4 consecutive columns of one row.
-                const int c = 16 * j + lm;
-                const float bc = sG[gb][2][c];
-                const float wc = bc * sG[gb][1][c] * (NQK ? sG[gb][5][c] : 1.f);
+                // Scale column c = 16 j + lm by beta_c, split into a hi + lo pair,
+                // and transpose with identity products (exact) so that each lane
+                // writes 4 consecutive columns of one row.
+                const float bc = sG[gb][2][16 * j + lm];
 #pragma unroll
                 for (int i = j + 1; i < 4; ++i) {
-                    bf16x4 uh, ul, wh, wl;
+                    bf16x4 uh, ul;
                     split4(RT[i] * bc, sm, uh, ul);
-                    split4(RT[i] * wc, sm, wh, wl);
                     const int off = tpos<C>(16 * i + lm, 16 * j + 4 * lg);
                     *reinterpret_cast<bf16x4 *>(sTU + off) = to_bf16x4(mfma16(uh, eye, zero4()));
                     *reinterpret_cast<bf16x4 *>(sTUl + off) = to_bf16x4(mfma16(ul, eye, zero4()));
-                    *reinterpret_cast<bf16x4 *>(sTW + off) = to_bf16x4(mfma16(wh, eye, zero4()));
-                    *reinterpret_cast<bf16x4 *>(sTWl + off) = to_bf16x4(mfma16(wl, eye, zero4()));
                 }
             };
             if (prep) {
@@ -687,7 +670,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     const size_t sbase = ((size_t)unit * H + h) * DV * DK;
     f32x4 st[NMT];      // st[mt][j] = S^T[16 mt + 4 lg + j][dvw]
     f32x4 QS[4];        // diag(e^g) Q S^T of the next chunk, rows 16 mr + 4 lg + j
-    bf16x8 yb[2];         // K S^T of the next chunk, bf16 (D order)
+    f32x4 Yf[4];          // K S^T of the next chunk (D layout, rows 16 mr + 4 lg + j)
     bf16x8 th[2], tl[2];  // Delta~ = diag(e^{g_C - g}) Delta, hi + lo (D order)
     bf16x8 dh[2], dl[2];  // Delta, hi + lo
     bf16x8 sh[NKS], sl[NKS];  // S^T, hi + lo
@@ -706,31 +689,40 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             const bf16x8 fV0 = v_frag(cw / 16, 0);
             const bf16x8 fV1 = v_frag(cw / 16, 1);
             // fragment (mr, ks), ks <= mr / 2, in that order; hi and lo parts
-            bf16x8 fTU[6], fTW[6], fTUl[6], fTWl[6];
+            bf16x8 fTU[6], fTUl[6];
 #pragma unroll
             for (int mr = 0, f = 0; mr < 4; ++mr)
 #pragma unroll
                 for (int ks = 0; ks <= mr / 2; ++ks, ++f) {
                     fTU[f] = tfrag<C>(sTU, 16 * mr, ks, lane);
-                    fTW[f] = tfrag<C>(sTW, 16 * mr, ks, lane);
                     fTUl[f] = tfrag<C>(sTUl, 16 * mr, ks, lane);
-                    fTWl[f] = tfrag<C>(sTWl, 16 * mr, ks, lane);
                 }
-            // U = T diag(beta) V (the factor's diagonal holds beta)
-            f32x4 U[4] = {zero4(), zero4(), zero4(), zero4()};
-            // Delta = U - T_W Y
+            // Z = V - diag(e^g) K S^T (rows of this lane: the D-order V
+            // operand and the D layout of Y hold the same rows), as a pair
+            f32x4 Z[4];
+#pragma unroll
+            for (int mr = 0; mr < 4; ++mr) {
+                f32x4 eg = ld4(&sG[cb][1][16 * mr + 4 * lg]);
+                if constexpr (NQK) eg = eg * ld4(&sG[cb][5][16 * mr + 4 * lg]);
+                const bf16x8 &fv = mr < 2 ? fV0 : fV1;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Z[mr][j] = (float)fv[4 * (mr & 1) + j] - eg[j] * Yf[mr][j];
+            }
+            bf16x8 zh[2], zl[2];
+            split8(Z[0], Z[1], sm, zh[0], zl[0]);
+            split8(Z[2], Z[3], sm, zh[1], zl[1]);
+            // Delta = T diag(beta) Z (the factor's diagonal holds beta)
             f32x4 D[4];
 #pragma unroll
             for (int mr = 0, f = 0; mr < 4; ++mr) {
-                f32x4 acc = zero4();
+                f32x4 a = zero4(), c = zero4();
 #pragma unroll
                 for (int ks = 0; ks <= mr / 2; ++ks, ++f) {
-                    U[mr] = mfma32(fTU[f], ks == 0 ? fV0 : fV1, U[mr]);
-                    U[mr] = mfma32(fTUl[f], ks == 0 ? fV0 : fV1, U[mr]);
-                    acc = mfma32(fTW[f], yb[ks], acc);
-                    acc = mfma32(fTWl[f], yb[ks], acc);
+                    a = mfma32(fTU[f], zh[ks], a);
+                    c = mfma32(fTUl[f], zh[ks], c);
+                    a = mfma32(fTU[f], zl[ks], a);
                 }
-                D[mr] = U[mr] - acc;
+                D[mr] = a + c;
             }
             f32x4 ed[4];   // e^{g_C - g_r} at rows 16 mr + 4 lg + j
 #pragma unroll
@@ -828,9 +820,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             }
         }
         if (prep) {
-            // Y = K S^T for chunk m from the hi part of S^T, rounded once to
-            // bf16: it only meets T diag(beta e^g), itself bf16, so extra bits
-            // of Y do not reach o or the state (same errors in emulation).
+            // Y = K S^T for chunk m from the hi part of S^T (kept in fp32 for
+            // Z = V - diag(e^g) Y)
             f32x4 Y[4];
             bf16x8 fk[4][NKS];
 #pragma unroll
@@ -844,8 +835,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 for (int ks = 0; ks < NKS; ++ks) acc = mfma32(fk[mr][ks], sh[ks], acc);
                 Y[mr] = acc;
             }
-            yb[0] = d_to_op(Y[0], Y[1]);
-            yb[1] = d_to_op(Y[2], Y[3]);
+#pragma unroll
+            for (int mr = 0; mr < 4; ++mr) Yf[mr] = Y[mr];
         }
         __syncthreads();
     }
