@@ -29,15 +29,16 @@
 // accumulators; S^T, Y and Delta feed the next MFMA straight from registers
 // (layouts in gdn_common.h).  An iteration has three barrier-separated
 // phases; every LDS buffer is written by one phase and read in later ones
-// before it is overwritten (P and the gates are double-buffered):
+// before it is overwritten (P, K^T and the gates are double-buffered):
 //   phase  producers (chunk n+1)               consumers (chunk n)
-//   1      store q,k, prefetch chunk n+2       Z, Delta, Delta~
-//   2      K K^T, Q K^T -> A, P; each wave     S <- e^{g_C} S + K^T Delta~,
-//          inverts and converts the diagonal   P Delta, write o
-//          block of A it computed
-//   3      store v, K^T, off-diagonal T and    Q S^T, Y = K S^T for chunk n+1
-//          its conversions, gate prefix of
-//          chunk n+2
+//   1      store q,k; each wave forms K^T of   Delta = T diag(beta) Z, Delta~
+//          its own 16 tokens; prefetch q,k
+//   2      store v, prefetch v; K K^T, Q K^T   S <- e^{g_C} S + K^T Delta~,
+//          -> A, P; each wave inverts and      P Delta, write o
+//          converts the diagonal block of A
+//          it computed
+//   3      off-diagonal T and its conversion,  Q S^T, Y = K S^T and
+//          gate prefix of chunk n+2            Z = V - diag(e^g) Y, chunk n+1
 // Global loads and stores go through buffer resources sized to the valid
 // rows of the chunk: rows past a ragged end read as zero and their stores
 // are dropped by the hardware range check, so no lane branches on bounds.
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 
     __shared__ __attribute__((aligned(16))) bf16 sQ[C * DK];        // Q, D-order rows
     __shared__ __attribute__((aligned(16))) bf16 sK[C * DK];        // K, D-order rows
-    __shared__ __attribute__((aligned(16))) bf16 sKT[DK * C];       // K^T
+    __shared__ __attribute__((aligned(16))) bf16 sKT[2][DK * C];    // K^T, chunks m and m-1
     __shared__ __attribute__((aligned(16))) bf16 sV[C * kDVT];      // V slice (swizzled)
     __shared__ __attribute__((aligned(16))) bf16 sA[C * LDC];       // A, off-diagonal blocks, hi
     __shared__ __attribute__((aligned(16))) bf16 sAl[C * LDC];      //   and lo parts
@@ -375,6 +376,22 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     *reinterpret_cast<bf16x4 *>(sK + c1) = bf16x4{pk[i][4], pk[i][5], pk[i][6], pk[i][7]};
                 }
                 prefetch_qk(m + 1);
+                // K^T of this wave's 16 tokens (the rows it has just stored), all
+                // of d_k, by identity products on 16x16 blocks, into the buffer
+                // of chunk m (the consumers read chunk n's in phase 2).
+                {
+                    bf16x4 kb[DK / 16];
+#pragma unroll
+                    for (int cb = 0; cb < DK / 16; ++cb)
+                        kb[cb] = *reinterpret_cast<const bf16x4 *>(sK + tpos<DK>(16 * pw + lm, 16 * cb + 4 * lg));
+                    f32x4 kt[DK / 16];
+#pragma unroll
+                    for (int cb = 0; cb < DK / 16; ++cb) kt[cb] = mfma16(kb[cb], eye, zero4());
+#pragma unroll
+                    for (int cb = 0; cb < DK / 16; ++cb)
+                        *reinterpret_cast<bf16x4 *>(sKT[m & 1] + tpos<C>(16 * cb + lm, 16 * pw + 4 * lg)) =
+                            to_bf16x4(kt[cb]);
+                }
                 if constexpr (NQK) {
                     // |q_r|^2 and |k_r|^2 of this wave's 16 rows: the diagonal of
                     // Q_b Q_b^T and K_b K_b^T (one fragment serves as both
@@ -414,6 +431,17 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             };
             // ================================ phase 2
             if (prep) {
+                // V slice of chunk m (the consumers read chunk n's in phase 1),
+                // then the next chunk's loads
+#pragma unroll
+                for (int i = 0; i < V_PER_THR; ++i) {
+                    const int e = ptid + 256 * i, r = e / (kDVT / 8), p = e % (kDVT / 8);
+                    bf16 *dv = sV + r * kDVT;
+                    const int f = swz(r);
+                    *reinterpret_cast<bf16x4 *>(dv + 4 * ((2 * p) ^ f)) = bf16x4{pv[i][0], pv[i][1], pv[i][2], pv[i][3]};
+                    *reinterpret_cast<bf16x4 *>(dv + 4 * ((2 * p + 1) ^ f)) = bf16x4{pv[i][4], pv[i][5], pv[i][6], pv[i][7]};
+                }
+                prefetch_v(m + 1);
                 // K K^T and Q K^T tiles (ti, tj), tj <= ti, 10 in all, 2-3 per wave;
                 // a wave loads each 16-row block of K or Q it needs once.
                 typedef bf16x8 Frag[NKS];
@@ -614,45 +642,12 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 }
             };
             if (prep) {
-#pragma unroll
-                for (int i = 0; i < V_PER_THR; ++i) {
-                    const int e = ptid + 256 * i, r = e / (kDVT / 8), p = e % (kDVT / 8);
-                    bf16 *dv = sV + r * kDVT;
-                    const int f = swz(r);
-                    *reinterpret_cast<bf16x4 *>(dv + 4 * ((2 * p) ^ f)) = bf16x4{pv[i][0], pv[i][1], pv[i][2], pv[i][3]};
-                    *reinterpret_cast<bf16x4 *>(dv + 4 * ((2 * p + 1) ^ f)) = bf16x4{pv[i][4], pv[i][5], pv[i][6], pv[i][7]};
-                }
-                // K^T of chunk m for its state update (the consumers finished
-                // with the previous one in phase 2), 16 tokens at a time, all of
-                // d_k, by identity products on 16x16 blocks.  Wave j < 3 forms
-                // T's block column j (column 0 is the longest), so the token
-                // groups go to the other waves: wave 3 transposes groups 0 and
-                // 3, waves 1 and 2 their own.
-                auto ktrans = [&](int grp) {
-                    bf16x4 kb[DK / 16];
-#pragma unroll
-                    for (int cb = 0; cb < DK / 16; ++cb)
-                        kb[cb] = *reinterpret_cast<const bf16x4 *>(sK + tpos<DK>(16 * grp + lm, 16 * cb + 4 * lg));
-                    f32x4 kt[DK / 16];
-#pragma unroll
-                    for (int cb = 0; cb < DK / 16; ++cb) kt[cb] = mfma16(kb[cb], eye, zero4());
-#pragma unroll
-                    for (int cb = 0; cb < DK / 16; ++cb)
-                        *reinterpret_cast<bf16x4 *>(sKT + tpos<C>(16 * cb + lm, 16 * grp + 4 * lg)) = to_bf16x4(kt[cb]);
-                };
-                if (pw == 3) {
-                    ktrans(0);
-                    ktrans(3);
-                } else if (pw != 0) {
-                    ktrans(pw);
-                }
                 if (pw == 0) column(IntC<0>{});
                 else if (pw == 1) column(IntC<1>{});
                 else if (pw == 2) column(IntC<2>{});
                 // chunk m+1's gates go to the buffer chunk n used (the consumers
                 // are done with it; past the last chunk they are unused)
                 else scan_gates(gb ^ 1);
-                prefetch_v(m + 1);
             }
             __syncthreads();
         }
@@ -670,7 +665,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     const size_t sbase = ((size_t)unit * H + h) * DV * DK;
     f32x4 st[NMT];      // st[mt][j] = S^T[16 mt + 4 lg + j][dvw]
     f32x4 QS[4];        // diag(e^g) Q S^T of the next chunk, rows 16 mr + 4 lg + j
-    f32x4 Yf[4];          // K S^T of the next chunk (D layout, rows 16 mr + 4 lg + j)
+    bf16x8 zh[2], zl[2];  // Z = V - diag(e^g) K S^T of the next chunk, hi + lo (D order)
     bf16x8 th[2], tl[2];  // Delta~ = diag(e^{g_C - g}) Delta, hi + lo (D order)
     bf16x8 dh[2], dl[2];  // Delta, hi + lo
     bf16x8 sh[NKS], sl[NKS];  // S^T, hi + lo
@@ -686,8 +681,6 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
         const int cb = (m & 1) ^ 1;     // gate buffer of chunk n
         // ================================ phase 1
         if (chain) {
-            const bf16x8 fV0 = v_frag(cw / 16, 0);
-            const bf16x8 fV1 = v_frag(cw / 16, 1);
             // fragment (mr, ks), ks <= mr / 2, in that order; hi and lo parts
             bf16x8 fTU[6], fTUl[6];
 #pragma unroll
@@ -697,20 +690,6 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     fTU[f] = tfrag<C>(sTU, 16 * mr, ks, lane);
                     fTUl[f] = tfrag<C>(sTUl, 16 * mr, ks, lane);
                 }
-            // Z = V - diag(e^g) K S^T (rows of this lane: the D-order V
-            // operand and the D layout of Y hold the same rows), as a pair
-            f32x4 Z[4];
-#pragma unroll
-            for (int mr = 0; mr < 4; ++mr) {
-                f32x4 eg = ld4(&sG[cb][1][16 * mr + 4 * lg]);
-                if constexpr (NQK) eg = eg * ld4(&sG[cb][5][16 * mr + 4 * lg]);
-                const bf16x8 &fv = mr < 2 ? fV0 : fV1;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) Z[mr][j] = (float)fv[4 * (mr & 1) + j] - eg[j] * Yf[mr][j];
-            }
-            bf16x8 zh[2], zl[2];
-            split8(Z[0], Z[1], sm, zh[0], zl[0]);
-            split8(Z[2], Z[3], sm, zh[1], zl[1]);
             // Delta = T diag(beta) Z (the factor's diagonal holds beta)
             f32x4 D[4];
 #pragma unroll
@@ -744,7 +723,7 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) fk[mt][ks] = tfrag<C>(sKT, 16 * mt, ks, lane);
+                for (int ks = 0; ks < 2; ++ks) fk[mt][ks] = tfrag<C>(sKT[n & 1], 16 * mt, ks, lane);
             const float egC = sG[cb][1][C - 1];
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt) {
@@ -820,8 +799,10 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             }
         }
         if (prep) {
-            // Y = K S^T for chunk m from the hi part of S^T (kept in fp32 for
-            // Z = V - diag(e^g) Y)
+            // Y = K S^T for chunk m from the hi part of S^T, then
+            // Z = V - diag(e^g) Y (the V slice of chunk m went to LDS in phase
+            // 2; the rows of this lane in the D-order V operand and in the D
+            // layout of Y are the same)
             f32x4 Y[4];
             bf16x8 fk[4][NKS];
 #pragma unroll
@@ -835,8 +816,19 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 for (int ks = 0; ks < NKS; ++ks) acc = mfma32(fk[mr][ks], sh[ks], acc);
                 Y[mr] = acc;
             }
+            const bf16x8 fV0 = v_frag(cw / 16, 0);
+            const bf16x8 fV1 = v_frag(cw / 16, 1);
+            f32x4 Z[4];
 #pragma unroll
-            for (int mr = 0; mr < 4; ++mr) Yf[mr] = Y[mr];
+            for (int mr = 0; mr < 4; ++mr) {
+                f32x4 eg = ld4(&sG[m & 1][1][16 * mr + 4 * lg]);
+                if constexpr (NQK) eg = eg * ld4(&sG[m & 1][5][16 * mr + 4 * lg]);
+                const bf16x8 &fv = mr < 2 ? fV0 : fV1;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Z[mr][j] = (float)fv[4 * (mr & 1) + j] - eg[j] * Y[mr][j];
+            }
+            split8(Z[0], Z[1], sm, zh[0], zl[0]);
+            split8(Z[2], Z[3], sm, zh[1], zl[1]);
         }
         __syncthreads();
     }
