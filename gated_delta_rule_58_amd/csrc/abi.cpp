@@ -110,7 +110,7 @@ int check_shape(const gdn_shape *s) {
 // Shape checks shared by the backward and the channel-wise decay forward
 // (their own supported sets, no prologue).
 int check_fp32tile_shape(const gdn_shape *s, int kind) {   // 0 bwd, 1 KDA, 2 GDN-2
-    const bool kda = kind != 0;
+    const char *entry = kind == 2 ? "gdn_gdn2_fwd" : kind == 1 ? "gdn_kda_fwd" : "gdn_chunk_bwd";
     if (!s) return fail(GDN_ERR_INVALID_ARG, "shape is NULL");
     if (s->B <= 0 || s->H <= 0 || s->T < 0 || s->d_k <= 0 || s->d_v <= 0 || s->chunk <= 0)
         return fail(GDN_ERR_INVALID_ARG,
@@ -128,21 +128,21 @@ int check_fp32tile_shape(const gdn_shape *s, int kind) {   // 0 bwd, 1 KDA, 2 GD
                     s->prologue);
     if (s->prologue != 0)
         return fail(GDN_ERR_UNSUPPORTED, "%s takes no input prologue (prologue=%d)",
-                    kind == 2 ? "gdn_gdn2_fwd" : kda ? "gdn_kda_fwd" : "the backward",
-                    s->prologue);
+                    entry, s->prologue);
     const long units = s->n_seqs > 0 ? s->n_seqs : s->B;
     if ((long)units * s->H > (1L << 24) || (long)s->T * s->H > (1L << 31) / 64)
-        return fail(GDN_ERR_INVALID_ARG, "problem too large for the backward (units x heads = %ld)",
-                    units * (long)s->H);
+        return fail(GDN_ERR_INVALID_ARG,
+                    "problem too large for %s (units x heads = %ld, T x heads = %ld)", entry,
+                    units * (long)s->H, (long)s->T * s->H);
     const bool bf = s->io_dtype == GDN_BF16;
     const bool okk = kind == 2 ? gdn::gdn2_supported(s->d_k, s->d_v, s->chunk, bf)
-                     : kda     ? gdn::kda_supported(s->d_k, s->d_v, s->chunk, bf)
+                     : kind == 1 ? gdn::kda_supported(s->d_k, s->d_v, s->chunk, bf)
                                : gdn::chunk_bwd_supported(s->d_k, s->d_v, s->chunk, bf);
     if (!okk)
         return fail(GDN_ERR_UNSUPPORTED,
                     "no %s kernel for d_k=%d d_v=%d chunk=%d io_dtype=%s (bf16: d_k=d_v in "
                     "{64,128}; f32: d_k=d_v=64; chunk 64)",
-                    kda ? "channel-wise decay" : "backward", s->d_k, s->d_v, s->chunk,
+                    entry, s->d_k, s->d_v, s->chunk,
                     s->io_dtype == GDN_BF16 ? "bf16" : "f32");
     return GDN_OK;
 }
