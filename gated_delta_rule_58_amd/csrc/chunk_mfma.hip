@@ -453,13 +453,17 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks) f[ks] = tfrag<DK>(sK, 16 * blk, ks, lane);
                 };
+                // A tile forms both its K K^T part (A) and its Q K^T part (P), or
+                // one of them (DO: 1 = A only, 2 = P only, 3 = both).
                 auto tile = [&](const int ti, const int tj, const Frag &fKj, const Frag &fKi,
-                                const Frag &fQi) {
+                                const Frag &fQi, auto doc) {
+                    constexpr int DO = decltype(doc)::value;
+                    constexpr bool doA = (DO & 1) != 0, doP = (DO & 2) != 0;
                     f32x4 G = zero4(), PT = zero4();
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks) {
-                        G = mfma32(fKj[ks], fKi[ks], G);    // k_i . k_r,  i = 16 tj + 4 lg + j, r = 16 ti + lm
-                        PT = mfma32(fKj[ks], fQi[ks], PT);  // k_i . q_r
+                        if constexpr (doA) G = mfma32(fKj[ks], fKi[ks], G);    // k_i . k_r,  i = 16 tj + 4 lg + j, r = 16 ti + lm
+                        if constexpr (doP) PT = mfma32(fKj[ks], fQi[ks], PT);  // k_i . q_r
                     }
                     const int r = 16 * ti + lm, i0 = 16 * tj + 4 * lg;
                     const float gr = sG[gb][0][r], br = sG[gb][2][r];
@@ -472,11 +476,14 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     f32x4 dec;   // e^{g_r - g_i} on and below the diagonal, else 0
 #pragma unroll
                     for (int j = 0; j < 4; ++j) dec[j] = (i0 + j <= r) ? exp_neg(gr - gi[j]) : 0.f;
-                    bf16x4 ph, pl;
-                    split4(dec * PT, sm, ph, pl);
-                    *reinterpret_cast<bf16x4 *>(sPh[m & 1] + tpos<C>(r, i0)) = ph;
-                    *reinterpret_cast<bf16x4 *>(sPl[m & 1] + tpos<C>(r, i0)) = pl;
-                    if (ti > tj) {
+                    if constexpr (doP) {
+                        bf16x4 ph, pl;
+                        split4(dec * PT, sm, ph, pl);
+                        *reinterpret_cast<bf16x4 *>(sPh[m & 1] + tpos<C>(r, i0)) = ph;
+                        *reinterpret_cast<bf16x4 *>(sPl[m & 1] + tpos<C>(r, i0)) = pl;
+                    }
+                    if (!doA) {
+                    } else if (ti > tj) {
                         bf16x4 ah, al;
                         split4(br * dec * G, sm, ah, al);
                         *reinterpret_cast<bf16x4 *>(sA + r * LDC + i0) = ah;
@@ -493,31 +500,40 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                         *reinterpret_cast<f32x4 *>(sAd + ti * BLK + lm * 16 + 4 * lg) = d4;
                     }
                 };
+                // Each wave: its diagonal tile first (its inverse follows), one
+                // more full tile, and one half of a third, so that every wave
+                // forms five of the twenty A or P 16 x 16 blocks.
+                const IntC<1> A_ONLY;
+                const IntC<2> P_ONLY;
+                const IntC<3> BOTH;
                 if (pw == 0) {
-                    Frag k0, q0, k3, q3;
+                    Frag k0, q0, k1, k3, q3;
                     load_k(0, k0); load_q(0, q0);
-                    load_k(3, k3); load_q(3, q3);
-                    tile(0, 0, k0, k0, q0);
-                    tile(3, 0, k0, k3, q3);
+                    load_k(3, k3); load_q(3, q3); load_k(1, k1);
+                    tile(0, 0, k0, k0, q0, BOTH);
+                    tile(3, 0, k0, k3, q3, BOTH);
+                    tile(3, 1, k1, k3, q3, P_ONLY);
                 } else if (pw == 1) {
-                    Frag k0, k1, q1, k3, q3;
-                    load_k(0, k0); load_k(1, k1); load_q(1, q1);
-                    load_k(3, k3); load_q(3, q3);
-                    tile(1, 0, k0, k1, q1);
-                    tile(1, 1, k1, k1, q1);
-                    tile(3, 1, k1, k3, q3);
+                    Frag k0, k1, q1, k3;
+                    load_k(1, k1); load_q(1, q1);
+                    load_k(0, k0); load_k(3, k3);
+                    tile(1, 1, k1, k1, q1, BOTH);
+                    tile(1, 0, k0, k1, q1, BOTH);
+                    tile(3, 1, k1, k3, q1, A_ONLY);
                 } else if (pw == 2) {
                     Frag k0, k1, k2, q2;
-                    load_k(0, k0); load_k(1, k1);
                     load_k(2, k2); load_q(2, q2);
-                    tile(2, 0, k0, k2, q2);
-                    tile(2, 1, k1, k2, q2);
-                    tile(2, 2, k2, k2, q2);
+                    load_k(1, k1); load_k(0, k0);
+                    tile(2, 2, k2, k2, q2, BOTH);
+                    tile(2, 1, k1, k2, q2, BOTH);
+                    tile(2, 0, k0, k2, q2, A_ONLY);
                 } else {
-                    Frag k2, k3, q3;
-                    load_k(2, k2); load_k(3, k3); load_q(3, q3);
-                    tile(3, 2, k2, k3, q3);
-                    tile(3, 3, k3, k3, q3);
+                    Frag k0, k2, k3, q2, q3;
+                    load_k(3, k3); load_q(3, q3);
+                    load_k(2, k2); load_k(0, k0); load_q(2, q2);
+                    tile(3, 3, k3, k3, q3, BOTH);
+                    tile(3, 2, k2, k3, q3, BOTH);
+                    tile(2, 0, k0, k2, q2, P_ONLY);
                 }
                 // Diagonal blocks: this wave computed tile (pw, pw) of A above and
                 // inverts and converts that block itself (no barrier needed).
@@ -547,7 +563,9 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                         for (int c = 0; c < 3; ++c)
 #pragma unroll
                             for (int rr = c + 1; rr < 4; ++rr) t[rr] -= col[c][rr] * t[c];
-                        if (g == sb) x = t;
+                        const bool mine = g == sb, later = g > sb;   // lane-varying: selects, not branches
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) x[rr] = mine ? t[rr] : x[rr];
                         if constexpr (sb < 3) {
                             f32x4 xb;   // the solved rows 4 sb..4 sb+3 of this column
 #pragma unroll
@@ -555,11 +573,11 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                                 xb[kk] = __int_as_float(__builtin_amdgcn_mov_dpp(
                                     __float_as_int(x[kk]), sb * 0x55, 0xf, 0xf, false));
                             // later groups subtract their rows' share of it
-                            if (g > sb) {
 #pragma unroll
-                                for (int rr = 0; rr < 4; ++rr)
-                                    x[rr] -= (col[0][rr] * xb[0] + col[1][rr] * xb[1]) +
-                                             (col[2][rr] * xb[2] + col[3][rr] * xb[3]);
+                            for (int rr = 0; rr < 4; ++rr) {
+                                const float y = x[rr] - ((col[0][rr] * xb[0] + col[1][rr] * xb[1]) +
+                                                         (col[2][rr] * xb[2] + col[3][rr] * xb[3]));
+                                x[rr] = later ? y : x[rr];
                             }
                         }
                     };
