@@ -78,11 +78,17 @@ PREHEAT_MS = 250.0   # GPU time run before each leg's counted warm-up
 MIN_TIMED = 10       # timed calls of every sub-leg, at least
 
 
-def preheat(torch, fn, min_ms=PREHEAT_MS):
+def set_preheat(ms: float) -> None:
+    global PREHEAT_MS
+    PREHEAT_MS = ms
+
+
+def preheat(torch, fn, min_ms=None):
     """Run fn back to back until at least min_ms of GPU time has passed.  The
     GPU needs tens of milliseconds of sustained load to reach its steady
     clock; without this a short counted warm-up ends while the clock is still
     ramping.  Returns (GPU ms, calls)."""
+    min_ms = PREHEAT_MS if min_ms is None else min_ms
     stream = torch.cuda.current_stream()
     total, calls = 0.0, 0
     while total < min_ms:
@@ -482,10 +488,14 @@ def main():
                     help="repeat the CPU oracle until it has run this long")
     ap.add_argument("--only", choices=["all", "chunk", "decode"], default="all",
                     help="run one part only (for profiling); the JSON line needs 'all'")
+    ap.add_argument("--preheat-ms", type=float, default=PREHEAT_MS,
+                    help="GPU time run before each leg's counted warm-up (0 for counter "
+                         "passes, which should see few dispatches)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a device-to-device copy of this many MiB (a "
                          "known-size kernel for calibrating HBM byte counters)")
     args = ap.parse_args()
+    set_preheat(args.preheat_ms)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the "
               "path has no multi-GPU component to measure.", file=sys.stderr)

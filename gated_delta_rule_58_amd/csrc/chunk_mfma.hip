@@ -29,16 +29,15 @@
 // accumulators; S^T, Y and Delta feed the next MFMA straight from registers
 // (layouts in gdn_common.h).  An iteration has three barrier-separated
 // phases; every LDS buffer is written by one phase and read in later ones
-// before it is overwritten (P, K^T and the gates are double-buffered):
+// before it is overwritten (K^T and the gates are double-buffered):
 //   phase  producers (chunk n+1)               consumers (chunk n)
 //   1      store q,k; each wave forms K^T of   Delta = T diag(beta) Z, Delta~
 //          its own 16 tokens; prefetch q,k
-//   2      store v, prefetch v; K K^T, Q K^T   S <- e^{g_C} S + K^T Delta~,
-//          -> A, P; each wave inverts and      P Delta, write o
-//          converts the diagonal block of A
-//          it computed
+//   2      store v, prefetch v; K K^T -> A;    S <- e^{g_C} S + K^T Delta~,
+//          each wave inverts and converts      P Delta, write o
+//          the diagonal block of A it formed
 //   3      off-diagonal T and its conversion,  Q S^T, Y = K S^T and
-//          gate prefix of chunk n+2            Z = V - diag(e^g) Y, chunk n+1
+//          Q K^T -> P, gate prefix of n+2      Z = V - diag(e^g) Y, chunk n+1
 // Global loads and stores go through buffer resources sized to the valid
 // rows of the chunk: rows past a ragged end read as zero and their stores
 // are dropped by the hardware range check, so no lane branches on bounds.
@@ -219,8 +218,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
     __shared__ __attribute__((aligned(16))) bf16 sTU[C * C];        // T diag(beta), hi
     __shared__ __attribute__((aligned(16))) bf16 sTUl[C * C];       //   lo
     // P = tril(QK^T) o decay as hi + lo, chunks m and m-1
-    __shared__ __attribute__((aligned(16))) bf16 sPh[2][C * C];
-    __shared__ __attribute__((aligned(16))) bf16 sPl[2][C * C];
+    __shared__ __attribute__((aligned(16))) bf16 sPh[C * C];
+    __shared__ __attribute__((aligned(16))) bf16 sPl[C * C];
     // per-token values of a chunk, double-buffered: g, e^g, beta,
     // e^{g_C - g}, and (prologue) 1/|q|, 1/|k|
     __shared__ __attribute__((aligned(16))) float sG[2][6][C];
@@ -282,8 +281,10 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
         reinterpret_cast<uint32_t *>(sTUl)[e] = 0u;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-            reinterpret_cast<uint32_t *>(sPh[b])[e] = 0u;
-            reinterpret_cast<uint32_t *>(sPl[b])[e] = 0u;
+            if (b == 0) {
+                reinterpret_cast<uint32_t *>(sPh)[e] = 0u;
+                reinterpret_cast<uint32_t *>(sPl)[e] = 0u;
+            }
         }
     }
     __syncthreads();
@@ -429,6 +430,68 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 *reinterpret_cast<bf16x4 *>(sTU + off) = uh;
                 *reinterpret_cast<bf16x4 *>(sTUl + off) = ul;
             };
+            // K K^T and Q K^T tiles (ti, tj), tj <= ti, 10 of each: the K K^T
+            // part (A) in phase 2, the Q K^T part (P) in phase 3 (the consumers
+            // read P of chunk m in phase 2 of the next iteration); a wave loads
+            // each 16-row block of K or Q it needs once.
+            typedef bf16x8 Frag[NKS];
+            auto load_q = [&](int blk, Frag &f) {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) f[ks] = tfrag<DK>(sQ, 16 * blk, ks, lane);
+            };
+            auto load_k = [&](int blk, Frag &f) {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) f[ks] = tfrag<DK>(sK, 16 * blk, ks, lane);
+            };
+            // A tile forms both its K K^T part (A) and its Q K^T part (P), or
+            // one of them (DO: 1 = A only, 2 = P only, 3 = both).
+            const IntC<1> A_ONLY;
+            const IntC<2> P_ONLY;
+            auto tile = [&](const int ti, const int tj, const Frag &fKj, const Frag &fKi,
+                            const Frag &fQi, auto doc) {
+                constexpr int DO = decltype(doc)::value;
+                constexpr bool doA = (DO & 1) != 0, doP = (DO & 2) != 0;
+                f32x4 G = zero4(), PT = zero4();
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    if constexpr (doA) G = mfma32(fKj[ks], fKi[ks], G);    // k_i . k_r,  i = 16 tj + 4 lg + j, r = 16 ti + lm
+                    if constexpr (doP) PT = mfma32(fKj[ks], fQi[ks], PT);  // k_i . q_r
+                }
+                const int r = 16 * ti + lm, i0 = 16 * tj + 4 * lg;
+                const float gr = sG[gb][0][r], br = sG[gb][2][r];
+                const f32x4 gi = ld4(&sG[gb][0][i0]);
+                if constexpr (NQK) {   // normalised rows: scale the Gram entries
+                    const f32x4 iki = ld4(&sG[gb][5][i0]);
+                    G = G * (sG[gb][5][r] * iki);
+                    PT = PT * (sG[gb][4][r] * iki);
+                }
+                f32x4 dec;   // e^{g_r - g_i} on and below the diagonal, else 0
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dec[j] = (i0 + j <= r) ? exp_neg(gr - gi[j]) : 0.f;
+                if constexpr (doP) {
+                    bf16x4 ph, pl;
+                    split4(dec * PT, sm, ph, pl);
+                    *reinterpret_cast<bf16x4 *>(sPh + tpos<C>(r, i0)) = ph;
+                    *reinterpret_cast<bf16x4 *>(sPl + tpos<C>(r, i0)) = pl;
+                }
+                if (!doA) {
+                } else if (ti > tj) {
+                    bf16x4 ah, al;
+                    split4(br * dec * G, sm, ah, al);
+                    *reinterpret_cast<bf16x4 *>(sA + r * LDC + i0) = ah;
+                    *reinterpret_cast<bf16x4 *>(sAl + r * LDC + i0) = al;
+                } else {
+                    // Diagonal tile: K K^T is symmetric, so the registers also
+                    // hold rows rr = i0 + j of column r; store A's block
+                    // transposed (column contiguous) for the substitution.
+                    const f32x4 brr = ld4(&sG[gb][2][i0]);
+                    f32x4 d4;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        d4[j] = (i0 + j > r) ? brr[j] * exp_neg(gi[j] - gr) * G[j] : 0.f;
+                    *reinterpret_cast<f32x4 *>(sAd + ti * BLK + lm * 16 + 4 * lg) = d4;
+                }
+            };
             // ================================ phase 2
             if (prep) {
                 // V slice of chunk m (the consumers read chunk n's in phase 1),
@@ -442,98 +505,30 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     *reinterpret_cast<bf16x4 *>(dv + 4 * ((2 * p + 1) ^ f)) = bf16x4{pv[i][4], pv[i][5], pv[i][6], pv[i][7]};
                 }
                 prefetch_v(m + 1);
-                // K K^T and Q K^T tiles (ti, tj), tj <= ti, 10 in all, 2-3 per wave;
-                // a wave loads each 16-row block of K or Q it needs once.
-                typedef bf16x8 Frag[NKS];
-                auto load_q = [&](int blk, Frag &f) {
-#pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) f[ks] = tfrag<DK>(sQ, 16 * blk, ks, lane);
-                };
-                auto load_k = [&](int blk, Frag &f) {
-#pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) f[ks] = tfrag<DK>(sK, 16 * blk, ks, lane);
-                };
-                // A tile forms both its K K^T part (A) and its Q K^T part (P), or
-                // one of them (DO: 1 = A only, 2 = P only, 3 = both).
-                auto tile = [&](const int ti, const int tj, const Frag &fKj, const Frag &fKi,
-                                const Frag &fQi, auto doc) {
-                    constexpr int DO = decltype(doc)::value;
-                    constexpr bool doA = (DO & 1) != 0, doP = (DO & 2) != 0;
-                    f32x4 G = zero4(), PT = zero4();
-#pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) {
-                        if constexpr (doA) G = mfma32(fKj[ks], fKi[ks], G);    // k_i . k_r,  i = 16 tj + 4 lg + j, r = 16 ti + lm
-                        if constexpr (doP) PT = mfma32(fKj[ks], fQi[ks], PT);  // k_i . q_r
-                    }
-                    const int r = 16 * ti + lm, i0 = 16 * tj + 4 * lg;
-                    const float gr = sG[gb][0][r], br = sG[gb][2][r];
-                    const f32x4 gi = ld4(&sG[gb][0][i0]);
-                    if constexpr (NQK) {   // normalised rows: scale the Gram entries
-                        const f32x4 iki = ld4(&sG[gb][5][i0]);
-                        G = G * (sG[gb][5][r] * iki);
-                        PT = PT * (sG[gb][4][r] * iki);
-                    }
-                    f32x4 dec;   // e^{g_r - g_i} on and below the diagonal, else 0
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) dec[j] = (i0 + j <= r) ? exp_neg(gr - gi[j]) : 0.f;
-                    if constexpr (doP) {
-                        bf16x4 ph, pl;
-                        split4(dec * PT, sm, ph, pl);
-                        *reinterpret_cast<bf16x4 *>(sPh[m & 1] + tpos<C>(r, i0)) = ph;
-                        *reinterpret_cast<bf16x4 *>(sPl[m & 1] + tpos<C>(r, i0)) = pl;
-                    }
-                    if (!doA) {
-                    } else if (ti > tj) {
-                        bf16x4 ah, al;
-                        split4(br * dec * G, sm, ah, al);
-                        *reinterpret_cast<bf16x4 *>(sA + r * LDC + i0) = ah;
-                        *reinterpret_cast<bf16x4 *>(sAl + r * LDC + i0) = al;
-                    } else {
-                        // Diagonal tile: K K^T is symmetric, so the registers also
-                        // hold rows rr = i0 + j of column r; store A's block
-                        // transposed (column contiguous) for the substitution.
-                        const f32x4 brr = ld4(&sG[gb][2][i0]);
-                        f32x4 d4;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            d4[j] = (i0 + j > r) ? brr[j] * exp_neg(gi[j] - gr) * G[j] : 0.f;
-                        *reinterpret_cast<f32x4 *>(sAd + ti * BLK + lm * 16 + 4 * lg) = d4;
-                    }
-                };
-                // Each wave: its diagonal tile first (its inverse follows), one
-                // more full tile, and one half of a third, so that every wave
-                // forms five of the twenty A or P 16 x 16 blocks.
-                const IntC<1> A_ONLY;
-                const IntC<2> P_ONLY;
-                const IntC<3> BOTH;
+                // The ten A blocks: each wave its diagonal block first (its
+                // inverse follows), and one or two below the diagonal.
                 if (pw == 0) {
-                    Frag k0, q0, k1, k3, q3;
-                    load_k(0, k0); load_q(0, q0);
-                    load_k(3, k3); load_q(3, q3); load_k(1, k1);
-                    tile(0, 0, k0, k0, q0, BOTH);
-                    tile(3, 0, k0, k3, q3, BOTH);
-                    tile(3, 1, k1, k3, q3, P_ONLY);
+                    Frag k0, k1, k3;
+                    load_k(0, k0); load_k(1, k1); load_k(3, k3);
+                    tile(0, 0, k0, k0, k0, A_ONLY);
+                    tile(1, 0, k0, k1, k1, A_ONLY);
+                    tile(3, 0, k0, k3, k3, A_ONLY);
                 } else if (pw == 1) {
-                    Frag k0, k1, q1, k3;
-                    load_k(1, k1); load_q(1, q1);
-                    load_k(0, k0); load_k(3, k3);
-                    tile(1, 1, k1, k1, q1, BOTH);
-                    tile(1, 0, k0, k1, q1, BOTH);
-                    tile(3, 1, k1, k3, q1, A_ONLY);
+                    Frag k1, k2, k3;
+                    load_k(1, k1); load_k(2, k2); load_k(3, k3);
+                    tile(1, 1, k1, k1, k1, A_ONLY);
+                    tile(2, 1, k1, k2, k2, A_ONLY);
+                    tile(3, 2, k2, k3, k3, A_ONLY);
                 } else if (pw == 2) {
-                    Frag k0, k1, k2, q2;
-                    load_k(2, k2); load_q(2, q2);
-                    load_k(1, k1); load_k(0, k0);
-                    tile(2, 2, k2, k2, q2, BOTH);
-                    tile(2, 1, k1, k2, q2, BOTH);
-                    tile(2, 0, k0, k2, q2, A_ONLY);
+                    Frag k0, k2;
+                    load_k(2, k2); load_k(0, k0);
+                    tile(2, 2, k2, k2, k2, A_ONLY);
+                    tile(2, 0, k0, k2, k2, A_ONLY);
                 } else {
-                    Frag k0, k2, k3, q2, q3;
-                    load_k(3, k3); load_q(3, q3);
-                    load_k(2, k2); load_k(0, k0); load_q(2, q2);
-                    tile(3, 3, k3, k3, q3, BOTH);
-                    tile(3, 2, k2, k3, q3, BOTH);
-                    tile(2, 0, k0, k2, q2, P_ONLY);
+                    Frag k1, k3;
+                    load_k(3, k3); load_k(1, k1);
+                    tile(3, 3, k3, k3, k3, A_ONLY);
+                    tile(3, 1, k1, k3, k3, A_ONLY);
                 }
                 // Diagonal blocks: this wave computed tile (pw, pw) of A above and
                 // inverts and converts that block itself (no barrier needed).
@@ -660,12 +655,39 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 }
             };
             if (prep) {
-                if (pw == 0) column(IntC<0>{});
-                else if (pw == 1) column(IntC<1>{});
-                else if (pw == 2) column(IntC<2>{});
-                // chunk m+1's gates go to the buffer chunk n used (the consumers
-                // are done with it; past the last chunk they are unused)
-                else scan_gates(gb ^ 1);
+                // T's block column j on wave j < 3 (column 0 is the longest), the
+                // ten P blocks spread the other way round (wave w forms w + 1 of
+                // them), and chunk m+1's gate prefix on wave 3, into the buffer
+                // chunk n used (the consumers are done with it; past the last
+                // chunk it is unused)
+                if (pw == 0) {
+                    column(IntC<0>{});
+                    Frag k0, q0;
+                    load_k(0, k0); load_q(0, q0);
+                    tile(0, 0, k0, k0, q0, P_ONLY);
+                } else if (pw == 1) {
+                    column(IntC<1>{});
+                    Frag k0, k1, q1;
+                    load_k(0, k0); load_k(1, k1); load_q(1, q1);
+                    tile(1, 0, k0, k1, q1, P_ONLY);
+                    tile(1, 1, k1, k1, q1, P_ONLY);
+                } else if (pw == 2) {
+                    column(IntC<2>{});
+                    Frag k0, k1, k2, q2;
+                    load_k(0, k0); load_k(1, k1); load_k(2, k2); load_q(2, q2);
+                    tile(2, 0, k0, k2, q2, P_ONLY);
+                    tile(2, 1, k1, k2, q2, P_ONLY);
+                    tile(2, 2, k2, k2, q2, P_ONLY);
+                } else {
+                    scan_gates(gb ^ 1);
+                    Frag kj, q3;
+                    load_q(3, q3);
+#pragma unroll
+                    for (int tj = 0; tj < 4; ++tj) {
+                        load_k(tj, kj);
+                        tile(3, tj, kj, kj, q3, P_ONLY);
+                    }
+                }
             }
             __syncthreads();
         }
@@ -761,8 +783,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             for (int mr = 0, f = 0; mr < 4; ++mr)
 #pragma unroll
                 for (int ks = 0; ks <= mr / 2; ++ks, ++f) {
-                    fPh[f] = tfrag<C>(sPh[n & 1], 16 * mr, ks, lane);
-                    fPl[f] = tfrag<C>(sPl[n & 1], 16 * mr, ks, lane);
+                    fPh[f] = tfrag<C>(sPh, 16 * mr, ks, lane);
+                    fPl[f] = tfrag<C>(sPl, 16 * mr, ks, lane);
                 }
             const size_t t0 = crow(n);
             const rsrc_t ro = make_rsrc(o + (t0 * H + h) * DV + dv0 + cw,
