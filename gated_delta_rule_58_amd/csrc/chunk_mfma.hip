@@ -656,15 +656,12 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
             };
             if (prep) {
                 // T's block column j on wave j < 3 (column 0 is the longest), the
-                // ten P blocks spread the other way round (wave w forms w + 1 of
-                // them), and chunk m+1's gate prefix on wave 3, into the buffer
-                // chunk n used (the consumers are done with it; past the last
-                // chunk it is unused)
+                // ten P blocks on the other waves (none on wave 0, two on wave
+                // 1, four on waves 2 and 3), and chunk m+1's gate prefix on
+                // wave 3, into the buffer chunk n used (the consumers are done
+                // with it; past the last chunk it is unused)
                 if (pw == 0) {
                     column(IntC<0>{});
-                    Frag k0, q0;
-                    load_k(0, k0); load_q(0, q0);
-                    tile(0, 0, k0, k0, q0, P_ONLY);
                 } else if (pw == 1) {
                     column(IntC<1>{});
                     Frag k0, k1, q1;
@@ -673,8 +670,10 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                     tile(1, 1, k1, k1, q1, P_ONLY);
                 } else if (pw == 2) {
                     column(IntC<2>{});
-                    Frag k0, k1, k2, q2;
-                    load_k(0, k0); load_k(1, k1); load_k(2, k2); load_q(2, q2);
+                    Frag k0, k1, k2, q0, q2;
+                    load_k(0, k0); load_q(0, q0);
+                    tile(0, 0, k0, k0, q0, P_ONLY);
+                    load_k(1, k1); load_k(2, k2); load_q(2, q2);
                     tile(2, 0, k0, k2, q2, P_ONLY);
                     tile(2, 1, k1, k2, q2, P_ONLY);
                     tile(2, 2, k2, k2, q2, P_ONLY);
