@@ -270,6 +270,25 @@ def kda_flops_per_chunk_head(d: int, C: int = 64) -> float:
     return prep + 2 * cdd + 2 * ccd + cdd
 
 
+def channel_fwd_bytes(B, T, H, dk, dv, gate_floats_per_th, io_bytes=2, o_bytes=4):
+    """Algorithmic HBM bytes of a channel-wise forward: q, k, v once, the
+    fp32 gates once (gate_floats_per_th per token-head: d_k for KDA's decay
+    and beta; d_k + d_k + d_v for GDN-2's decay, erase and write), o once, the
+    final states once.  The workspace its two launches pass between them is
+    not algorithmic and is reported beside it."""
+    per_th = (2 * dk + dv) * io_bytes + dv * o_bytes + 4 * gate_floats_per_th
+    return B * T * H * per_th + B * H * dv * dk * 4
+
+
+def hbm_roofline(nbytes, ms, ws_bytes):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
+            "workspace_bytes_written_and_read": ws_bytes,
+            "frac_with_workspace": round((nbytes + 2 * ws_bytes) / (ms * 1e-3) / 1e9
+                                         / HBM_PEAK_GBS, 4)}
+
+
 def run_kda(args, torch, gi, gdn, dev, w):
     """Time gdn_kda_fwd on the headline shape with channel-wise decays
     (log alpha = -softplus(N(1,1)) per channel), inputs resident."""
@@ -290,8 +309,9 @@ def run_kda(args, torch, gi, gdn, dev, w):
     ms = time_calls(torch, step, steps, warm)
     fl = kda_flops_per_chunk_head(dk, C) * B * H * ((T + C - 1) // C)
     tfs = fl / (ms * 1e-3) / 1e12
+    hbm = hbm_roofline(channel_fwd_bytes(B, T, H, dk, dv, dk + 1), ms, ws.numel())
     return {"ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
-            "steps": steps,
+            "steps": steps, "hbm_roofline": hbm,
             "roofline": {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_FP32_PEAK_TFS,
                          "unit": "TFLOP/s", "frac": round(tfs / MFMA_FP32_PEAK_TFS, 4),
                          "dtype": "f32", "flops_per_step": fl},
@@ -332,8 +352,9 @@ def run_gdn2(args, torch, gi, gdn, dev, w):
     ms = time_calls(torch, step, steps, warm)
     fl = gdn2_flops_per_chunk_head(dk, C) * B * H * ((T + C - 1) // C)
     tfs = fl / (ms * 1e-3) / 1e12
+    hbm = hbm_roofline(channel_fwd_bytes(B, T, H, dk, dv, 2 * dk + dv), ms, ws.numel())
     return {"ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
-            "steps": steps,
+            "steps": steps, "hbm_roofline": hbm,
             "roofline": {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_FP32_PEAK_TFS,
                          "unit": "TFLOP/s", "frac": round(tfs / MFMA_FP32_PEAK_TFS, 4),
                          "dtype": "f32", "flops_per_step": fl},
