@@ -142,3 +142,15 @@ def test_bwd_headline_full():
         rng.standard_normal((w["B"], w["T"], w["H"], w["dv"])).astype(np.float32))
     inp["dS_T"] = None
     compare("bwd headline full", inp)
+
+
+@pytest.mark.parametrize("mode,param,shift", [("repeat", 16, 0.0), ("cluster", 1, 1.0)])
+def test_bwd_structured_keys(mode, param, shift):
+    """Keys repeated or nearly collinear inside a chunk (the worst-conditioned
+    UT transforms; beta in (1, 2) with the clustered keys), weak decay."""
+    inp = gi.structured_chunk_inputs(2, 300, 2, 128, 128, mode, param, "bf16", alpha_mu=-4.0,
+                                     s0_std=0.1, beta_shift=shift, seed=71)
+    rng = np.random.default_rng(72)
+    inp["dO"] = torch.from_numpy(rng.standard_normal((2, 300, 2, 128))).float()
+    inp["dS_T"] = torch.from_numpy(rng.standard_normal((2, 2, 128, 128)) * 0.1).float()
+    compare(f"bwd keys {mode}({param}) beta+{shift}", inp)

@@ -95,3 +95,11 @@ def test_gdn2_headline_shape_full():
     say("gdn2 full: generating inputs")
     inp = gi.gdn2_inputs(8, 4096, 16, 128, 128, "bf16", alpha_mu=1.0, seed=gi.SEED_BASE + 40)
     compare("gdn2 full 1.3b-layer shape", inp)
+
+
+@pytest.mark.parametrize("mode,param", [("repeat", 16), ("cluster", 1)])
+def test_gdn2_structured_keys(mode, param):
+    """Keys repeated or nearly collinear inside a chunk, weak channel decays."""
+    inp = gi.gdn2_inputs(2, 300, 2, 128, 128, "bf16", alpha_mu=-4.0, s0_std=0.1, seed=75)
+    inp["k"] = gi.structured_chunk_inputs(2, 300, 2, 128, 128, mode, param, "bf16", seed=76)["k"]
+    compare(f"gdn2 keys {mode}({param})", inp)

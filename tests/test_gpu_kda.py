@@ -92,3 +92,13 @@ def test_kda_headline_shape_full():
     say("kda full: generating inputs")
     inp = gi.kda_inputs(8, 4096, 16, 128, 128, "bf16", alpha_mu=1.0, seed=gi.SEED_BASE + 30)
     compare("kda full 1.3b-layer shape", inp)
+
+
+@pytest.mark.parametrize("mode,param,shift", [("repeat", 16, 0.0), ("cluster", 1, 1.0)])
+def test_kda_structured_keys(mode, param, shift):
+    """Keys repeated or nearly collinear inside a chunk, weak channel decays."""
+    inp = gi.kda_inputs(2, 300, 2, 128, 128, "bf16", alpha_mu=-4.0, s0_std=0.1, seed=73)
+    sk = gi.structured_chunk_inputs(2, 300, 2, 128, 128, mode, param, "bf16", seed=74,
+                                    beta_shift=shift)
+    inp["k"], inp["beta"] = sk["k"], sk["beta"]
+    compare(f"kda keys {mode}({param}) beta+{shift}", inp)
