@@ -258,16 +258,19 @@ def run_backward(args, torch, gi, gdn, dev, w, host):
                     "dO fp32 ~ N(0,1), dS_T = 0"}
 
 
-def kda_flops_per_chunk_head(d: int, C: int = 64) -> float:
-    """fp32 MFMA flops of gdn_kda_fwd per (chunk, head): prep -- the 6 blocks
-    below the diagonal of A and of P (C/4 x C/4 x d each ... 16 x 16 x d) --
-    and the sequential launch: (K o e^G) S^T and (Q o e^G) S^T (C x d x d
-    each), T Z and P Delta (C x C x d each), the state update (d x C x d).
-    The diagonal blocks of A and P (term-by-term VALU) are not counted."""
+def kda_flops_per_chunk_head(d: int, C: int = 64):
+    """MFMA flops of gdn_kda_fwd per (chunk, head), as (fp32 products of the
+    prep, fp32-accurate products of the sequential launch).  Prep: the 6
+    blocks below the diagonal of A and of P (16 x 16 x d each), on the fp32
+    MFMA.  Sequential launch: (K o e^G) S^T and (Q o e^G) S^T (C x d x d
+    each), T diag(beta) Z and P Delta (C x C x d each), the state update
+    (d x C x d); each runs on the bf16 MFMA as three piece products of hi + lo
+    pairs.  The diagonal blocks of A and P (term-by-term VALU) are not
+    counted."""
     cdd = 2.0 * C * d * d
     ccd = 2.0 * C * C * d
     prep = 2 * 6 * 2.0 * 16 * 16 * d
-    return prep + 2 * cdd + 2 * ccd + cdd
+    return prep, 2 * cdd + 2 * ccd + cdd
 
 
 def channel_fwd_bytes(B, T, H, dk, dv, gate_floats_per_th, io_bytes=2, o_bytes=4):
@@ -307,15 +310,22 @@ def run_kda(args, torch, gi, gdn, dev, w):
                     S_T=st, workspace=ws)
 
     ms = time_calls(torch, step, steps, warm)
-    fl = kda_flops_per_chunk_head(dk, C) * B * H * ((T + C - 1) // C)
-    tfs = fl / (ms * 1e-3) / 1e12
+    nch = B * H * ((T + C - 1) // C)
+    f_prep, f_seq = kda_flops_per_chunk_head(dk, C)
     hbm = hbm_roofline(channel_fwd_bytes(B, T, H, dk, dv, dk + 1), ms, ws.numel())
+    bf16_tfs = 3 * f_seq * nch / (ms * 1e-3) / 1e12
     return {"ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
-            "steps": steps, "hbm_roofline": hbm,
-            "roofline": {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_FP32_PEAK_TFS,
-                         "unit": "TFLOP/s", "frac": round(tfs / MFMA_FP32_PEAK_TFS, 4),
-                         "dtype": "f32", "flops_per_step": fl},
-            "note": "gdn_kda_fwd = prep + sequential launch, fp32 MFMA; bf16 q/k/v, fp32 "
+            "steps": steps, "roofline": hbm,
+            "mfma_executed": {"bf16_piece_products_tflops": round(bf16_tfs, 1),
+                              "frac_of_bf16_peak": round(bf16_tfs / MFMA_BF16_PEAK_TFS, 4),
+                              "prep_f32_tflops": round(f_prep * nch / (ms * 1e-3) / 1e12, 1),
+                              "flops_per_step": {"prep_f32": f_prep * nch,
+                                                 "sequential_fp32_accurate": f_seq * nch}},
+            "note": "gdn_kda_fwd = prep (fp32 MFMA blocks of A and P, T by the blocked "
+                    "inverse; writes the sequential launch's operands as bf16 hi + lo pairs in "
+                    "its LDS layout) + sequential launch (bf16 MFMA, three piece products per "
+                    "product; operand regions copied global->LDS three phases ahead). HBM-bound "
+                    "on the workspace round trip: see frac_with_workspace. bf16 q/k/v, fp32 "
                     "channel-wise log alpha [B,T,H,d_k], fp32 o and state"}
 
 
@@ -507,7 +517,8 @@ def main():
                     help="batch rows of the workload the CPU oracle runs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU oracle until it has run this long")
-    ap.add_argument("--only", choices=["all", "chunk", "decode"], default="all",
+    ap.add_argument("--only", choices=["all", "chunk", "decode", "kda", "gdn2", "bwd"],
+                    default="all",
                     help="run one part only (for profiling); the JSON line needs 'all'")
     ap.add_argument("--preheat-ms", type=float, default=PREHEAT_MS,
                     help="GPU time run before each leg's counted warm-up (0 for counter "
@@ -541,6 +552,13 @@ def main():
         run_decode(args, torch, gi, gdn, dev)
         return
     w = gi.WORKLOADS[2]
+    if args.only in ("kda", "gdn2", "bwd"):   # one leg alone (for profiling)
+        if args.only == "bwd":
+            leg = run_backward(args, torch, gi, gdn, dev, w, gi.workload_inputs(2))
+        else:
+            leg = (run_kda if args.only == "kda" else run_gdn2)(args, torch, gi, gdn, dev, w)
+        print(json.dumps(leg))
+        return
     B, T, H, dk, dv, C = w["B"], w["T"], w["H"], w["dk"], w["dv"], w["chunk"]
     print(f"[bench] inputs: workload 2 {w['name']} B={B} T={T} H={H} d={dk}", file=sys.stderr,
           flush=True)

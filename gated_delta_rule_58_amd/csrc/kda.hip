@@ -1,5 +1,5 @@
 // Chunkwise forward of the delta rule with channel-wise decay (KDA) on
-// gfx950, fp32 MFMA.
+// gfx950.
 //
 // "Gated DeltaNet-2: Decoupling Erase and Write in Linear Attention"
 // (abstract) describes Kimi Delta Attention as the delta rule with
@@ -19,13 +19,18 @@
 //   S'     = S Diag(e^{G_n}) + Delta^T (K o e^{G_n - G})
 //
 // Two launches:
-//   1. kda_prep (one workgroup per chunk and head): G, then A and P -- the
-//      blocks below the diagonal as MFMA products of operands rescaled to a
-//      reference token between the two blocks (every factor e^{<= 0}), the
-//      diagonal blocks term by term -- T by the blocked inverse, and the
-//      rescaled K o e^G, Q o e^G, K o e^{G_n - G}, e^{G_n};
+//   1. kda_prep (one workgroup per chunk and head, fp32 arithmetic): G, then
+//      A and P -- the blocks below the diagonal as fp32 MFMA products of
+//      operands rescaled to a reference token between the two blocks (every
+//      factor e^{<= 0}), the diagonal blocks term by term -- T by the blocked
+//      inverse; it writes K o e^G, Q o e^G, T diag(beta), P,
+//      (K o e^{G_n - G})^T and e^{G_n} as bf16 hi + lo pairs, laid out as the
+//      second launch keeps them in LDS;
 //   2. kda_fwd (one workgroup per sequence, head and 64-column d_v slice,
-//      chunks in order): the state recurrence and the outputs.
+//      chunks in order): the state recurrence and the outputs, every product
+//      on the bf16 MFMA as three piece products (about 2^-16 relative, so
+//      fp32-accurate to the precision the parity bar asks), its operand
+//      regions copied global -> LDS by four loader waves three phases ahead.
 #include "fp32_tiles.h"
 
 #include <mutex>
@@ -36,19 +41,75 @@ namespace {
 using namespace tiles;
 
 
-// Workspace block sizes (floats) per chunk and head.
+// Workspace of one chunk and head: every operand of the sequential launch as
+// a bf16 hi + lo pair (hi = x rounded to bf16, lo = bf16(x - hi); about 16
+// mantissa bits of x), in exactly the layout the sequential launch keeps in
+// LDS, so that it copies each region with direct global-to-LDS loads: rows
+// padded by 8 elements, each 32-wide block of columns in D-order (see
+// dpos) so an operand fragment is one 16-byte read.  Offsets in bf16
+// elements.  Four regions of whole KB, in the order the sequential launch
+// consumes them: K o e^G and Q o e^G; T diag(beta); P;
+// (K o e^{G_n - G})^T and e^{G_n}.
 template <int D> struct KdaWs {
-    static constexpr size_t T = BC * BC, P = BC * BC, KG = BC * D, QG = BC * D, KT = BC * D,
-                            EG = D, BETA = BC;
-    static constexpr size_t total = T + P + KG + QG + KT + EG + BETA;
+    static constexpr int LK = D + 8, LC = BC + 8;   // row strides of the 64 x D and x 64 blocks
+    static constexpr size_t up(size_t x) { return (x + 511) / 512 * 512; }
+    static constexpr size_t KG = 0,                         // K o e^G, 64 x D: hi, lo
+                            QG = KG + 2 * BC * LK,          // Q o e^G, 64 x D: hi, lo
+                            TB = up(QG + 2 * BC * LK),      // T diag(beta), 64 x 64: hi, lo
+                            P = up(TB + 2 * BC * LC),       // P, 64 x 64: hi, lo
+                            KT = up(P + 2 * BC * LC),       // (K o e^{G_n - G})^T, D x 64: hi, lo
+                            EG = KT + 2 * D * LC,           // e^{G_n}: D floats
+                            total = up(EG + 2 * D);
+    static_assert(TB == QG + 2 * BC * LK && P == TB + 2 * BC * LC && KT == P + 2 * BC * LC,
+                  "regions are contiguous");
 };
+
+// Stored position of column k: within each 32-wide block, lane group g of a
+// 16x16x32 MFMA operand takes k = 4g..4g+3 and 16+4g..16+4g+3 (the k order of
+// two stacked accumulator tiles), kept together at 8g..8g+7.
+__device__ __forceinline__ int dpos(int k) {
+    return (k & ~31) + ((k & 16) >> 2) + 2 * (k & 12) + (k & 3);
+}
+
+// Four consecutive values as hi and lo bf16 (8-byte stores).
+__device__ __forceinline__ void put_pair4(bf16 *hi, bf16 *lo, f32x4 x) {
+    bf16x4 h, l;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        h[j] = (bf16)x[j];
+        l[j] = (bf16)(x[j] - (float)h[j]);
+    }
+    *reinterpret_cast<bf16x4 *>(hi) = h;
+    *reinterpret_cast<bf16x4 *>(lo) = l;
+}
+// Eight values (D-order group: two runs of four) as hi and lo bf16 (16-byte stores).
+__device__ __forceinline__ void put_pair8(bf16 *hi, bf16 *lo, f32x4 x0, f32x4 x1) {
+    bf16x8 h, l;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        h[j] = (bf16)x0[j];
+        l[j] = (bf16)(x0[j] - (float)h[j]);
+        h[4 + j] = (bf16)x1[j];
+        l[4 + j] = (bf16)(x1[j] - (float)h[4 + j]);
+    }
+    *reinterpret_cast<bf16x8 *>(hi) = h;
+    *reinterpret_cast<bf16x8 *>(lo) = l;
+}
+__device__ __forceinline__ void put_pair1(bf16 *hi, bf16 *lo, float x) {
+    const bf16 h = (bf16)x;
+    *hi = h;
+    *lo = (bf16)(x - (float)h);
+}
+
+__device__ __forceinline__ bf16x8 ld8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
 // ---------------------------------------------------------------- 1. prep
 template <int D, typename TI>
 __global__ __launch_bounds__(512) void kda_prep_kernel(
     int T, int H, int units, int NC, int varlen, const int32_t *__restrict__ cu,
     const TI *__restrict__ q, const TI *__restrict__ k, const float *__restrict__ la,
-    const float *__restrict__ beta, float *__restrict__ ws) {
+    const float *__restrict__ beta, bf16 *__restrict__ ws) {
+    typedef KdaWs<D> WS;
     constexpr int LI = ldx<TI, D>(), LF = D + 4;
     // K, Q and G, then A over G and T over Q once those are consumed (68 KB
     // for d = 128, so two workgroups share a CU)
@@ -58,24 +119,24 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
     TI *sK = reinterpret_cast<TI *>(smem), *sQ = reinterpret_cast<TI *>(smem + BK);
     float *sG = reinterpret_cast<float *>(smem + BK + BQ);
     float *sA = sG, *sX = reinterpret_cast<float *>(smem + BK);
-    __shared__ float sb[BC];
+    // P is gathered over K once that is consumed, when it fits, and written
+    // row by row with the other 16-byte stores (written block by block it
+    // leaves lines to be written more than once)
+    constexpr bool kStageP = BK >= BC * LDN * 4;
+    float *sP = reinterpret_cast<float *>(smem);
+    __shared__ __attribute__((aligned(16))) float sb[BC];
     const int slot = blockIdx.x / H, h = blockIdx.x % H;
     long row0;
     int n;
     if (!slot_chunk(slot, units, T, NC, varlen, cu, row0, n)) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lq = lane >> 4;
-    float *W = ws + (size_t)blockIdx.x * KdaWs<D>::total;
-    float *wT = W, *wP = wT + KdaWs<D>::T, *wKG = wP + KdaWs<D>::P, *wQG = wKG + KdaWs<D>::KG;
-    float *wKT = wQG + KdaWs<D>::QG, *wEG = wKT + KdaWs<D>::KT, *wB = wEG + KdaWs<D>::EG;
+    bf16 *W = ws + (size_t)blockIdx.x * WS::total;
+    float *wEG = reinterpret_cast<float *>(W + WS::EG);
     load_rows<D>(sK, LI, k, row0, n, H, h, 0, D, tid, 512);
     load_rows<D>(sQ, LI, q, row0, n, H, h, 0, D, tid, 512);
     load_rows<D>(sG, LF, la, row0, n, H, h, 0, D, tid, 512);
-    if (tid < BC) {
-        const float b = tid < n ? beta[(size_t)(row0 + tid) * H + h] : 0.f;
-        sb[tid] = b;
-        wB[tid] = b;
-    }
+    if (tid < BC) sb[tid] = tid < n ? beta[(size_t)(row0 + tid) * H + h] : 0.f;
     __syncthreads();
     if (tid < D) {   // prefix over the chunk per channel (padded rows add 0)
         float g = 0.f;
@@ -86,32 +147,74 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
         wEG[tid] = expf(g);
     }
     __syncthreads();
-    // rescaled operands for the sequential kernel
-    for (int e = tid; e < BC * D / 4; e += 512) {
-        const int r = e / (D / 4), c = (e % (D / 4)) * 4;
-        const f32x4 g = *reinterpret_cast<const f32x4 *>(sG + r * LF + c);
-        const f32x4 gn = *reinterpret_cast<const f32x4 *>(sG + (BC - 1) * LF + c);
-        f32x4 kg, qg, kt;
-        const f32x4 k4 = ld4f(sK + r * LI + c), q4 = ld4f(sQ + r * LI + c);
+    // rescaled operands of the sequential launch, one D-order group of 8
+    // (16-byte stores) per item: K o e^G and Q o e^G along rows,
+    // (K o e^{G_n - G})^T along the tokens of one channel
+    for (int e = tid; e < BC * D / 8; e += 512) {
+        const int r = e / (D / 8), p = 8 * (e % (D / 8));   // stored positions p..p+7
+        const int c0 = (p & ~31) + (p & 31) / 2, c1 = c0 + 16;   // columns c0..+3, c1..+3
+        const f32x4 g0 = *reinterpret_cast<const f32x4 *>(sG + r * LF + c0);
+        const f32x4 g1 = *reinterpret_cast<const f32x4 *>(sG + r * LF + c1);
+        const f32x4 k0 = ld4f(sK + r * LI + c0), k1 = ld4f(sK + r * LI + c1);
+        const f32x4 q0 = ld4f(sQ + r * LI + c0), q1 = ld4f(sQ + r * LI + c1);
+        f32x4 kg0, kg1, qg0, qg1;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float kv = k4[j], qv = q4[j];
-            const float eg = __expf(g[j]);
-            kg[j] = kv * eg;
-            qg[j] = qv * eg;
-            kt[j] = kv * __expf(gn[j] - g[j]);
+            const float e0 = __expf(g0[j]), e1 = __expf(g1[j]);
+            kg0[j] = k0[j] * e0;
+            qg0[j] = q0[j] * e0;
+            kg1[j] = k1[j] * e1;
+            qg1[j] = q1[j] * e1;
         }
-        *reinterpret_cast<f32x4 *>(wKG + 4 * e) = kg;
-        *reinterpret_cast<f32x4 *>(wQG + 4 * e) = qg;
-        *reinterpret_cast<f32x4 *>(wKT + 4 * e) = kt;
+        const int off = r * WS::LK + p;
+        put_pair8(W + WS::KG + off, W + WS::KG + BC * WS::LK + off, kg0, kg1);
+        put_pair8(W + WS::QG + off, W + WS::QG + BC * WS::LK + off, qg0, qg1);
+    }
+    for (int e = tid; e < D * BC / 8; e += 512) {
+        const int c = e / (BC / 8), p = 8 * (e % (BC / 8));
+        const int r0 = (p & ~31) + (p & 31) / 2, r1 = r0 + 16;   // tokens r0..+3, r1..+3
+        const float gn = sG[(BC - 1) * LF + c];
+        f32x4 t0, t1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            t0[j] = to_f32(sK[(r0 + j) * LI + c]) * __expf(gn - sG[(r0 + j) * LF + c]);
+            t1[j] = to_f32(sK[(r1 + j) * LI + c]) * __expf(gn - sG[(r1 + j) * LF + c]);
+        }
+        const int off = c * WS::LC + p;
+        put_pair8(W + WS::KT + off, W + WS::KT + D * WS::LC + off, t0, t1);
+    }
+    // row padding and the tail of region B are written too (zeros), so
+    // every cache line of the workspace is written whole
+    {
+        constexpr int NR = 4 * BC + 4 * BC + 2 * D;              // padded rows
+        constexpr int NT = (int)(WS::total - WS::EG - 2 * D) / 8;   // 16-byte tail pieces
+        for (int e = tid; e < NR + NT; e += 512) {
+            size_t off;
+            if (e < 4 * BC) off = WS::KG + (size_t)e * WS::LK + D;                  // K/Q o e^G
+            else if (e < 8 * BC) off = WS::TB + (size_t)(e - 4 * BC) * WS::LC + BC;  // T, P
+            else if (e < NR) off = WS::KT + (size_t)(e - 8 * BC) * WS::LC + BC;      // K^T
+            else off = WS::EG + 2 * D + (size_t)(e - NR) * 8;   // tail of the last region
+            *reinterpret_cast<bf16x8 *>(W + off) = bf16x8{};
+        }
+    }
+    // blocks of P above the diagonal are zero
+    if constexpr (!kStageP)
+    for (int e = tid; e < BC * BC / 4; e += 512) {
+        const int r = e >> 4, i = (e & 15) * 4;
+        if ((i >> 4) > (r >> 4)) {
+            const int off = r * WS::LC + dpos(i);
+            put_pair4(W + WS::P + off, W + WS::P + BC * WS::LC + off, zero4());
+        }
     }
     // A and P, 16 x 16 blocks (br, bi), bi <= br: 10 blocks each.  The 8
     // diagonal blocks (one per wave) by diag_block; the 12 blocks below the
     // diagonal are MFMA products whose operands
     // are rescaled to the last token of block br - 1 (G_i >= G_ref >= G_r
-    // channel by channel, so both factors are e^{<= 0}).
+    // channel by channel, so both factors are e^{<= 0}).  P goes straight
+    // to the workspace; A stays in registers until G is consumed.
     f32x4 adiag, aoff = zero4();   // this wave's A entries (diagonal block; a block below,
                                    // waves 0-5: A's six blocks below are tasks 0-5)
+    f32x4 pdiag = zero4(), poff = zero4();   // and P entries (waves 4-7; tasks 6-11)
     {
         const bool isP = wave >= 4;
         const int b = wave & 3;
@@ -121,7 +224,14 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * b + 4 * lq + j;
-            if (isP) wP[r * BC + i] = i <= r ? acc[j] : 0.f;
+            if (isP) {
+                if constexpr (kStageP) {
+                    pdiag[j] = i <= r ? acc[j] : 0.f;
+                } else {
+                    const int off = r * WS::LC + dpos(i);
+                    put_pair1(W + WS::P + off, W + WS::P + BC * WS::LC + off, i <= r ? acc[j] : 0.f);
+                }
+            }
             adiag[j] = i < r ? sb[r] * acc[j] : 0.f;
         }
     }
@@ -140,26 +250,43 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
             const float gr = gref[c];
             const float a = to_f32(X[ra * LI + c]) * __expf(sG[ra * LF + c] - gr);
             const float bb = to_f32(sK[rb * LI + c]) * __expf(gr - sG[rb * LF + c]);
-            acc = mfma_f32(a, bb, acc);
+            // A: lane holds rows 16 br + 4 lq + j of column 16 bi + li; P is
+            // formed transposed, so a lane holds row 16 br + li, columns
+            // 16 bi + 4 lq + j (four consecutive stored positions)
+            acc = isP ? mfma_f32(bb, a, acc) : mfma_f32(a, bb, acc);
         }
+        if (isP) {
+            if constexpr (kStageP) {
+                poff = acc;
+            } else {
+                const int off = (16 * br + li) * WS::LC + dpos(16 * bi + 4 * lq);
+                put_pair4(W + WS::P + off, W + WS::P + BC * WS::LC + off, acc);
+            }
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * br + 4 * lq + j, ii = 16 * bi + li;
-            if (isP) wP[r * BC + ii] = acc[j];
-            if (!isP) aoff[j] = sb[r] * acc[j];
+            for (int j = 0; j < 4; ++j) aoff[j] = sb[16 * br + 4 * lq + j] * acc[j];
         }
-    }
-    // upper blocks of P are zero
-    for (int e = tid; e < BC * BC; e += 512) {
-        const int r = e >> 6, i = e & 63;
-        if ((i >> 4) > (r >> 4)) wP[e] = 0.f;
     }
     __syncthreads();   // G, K, Q consumed: A goes over G, T over Q
     for (int e = tid; e < BC * LDN; e += 512) {
         sA[e] = 0.f;
         sX[e] = 0.f;
+        if constexpr (kStageP) sP[e] = 0.f;
     }
     __syncthreads();
+    if constexpr (kStageP) {
+        if (wave >= 4) {
+            const int b = wave & 3;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sP[(16 * b + 4 * lq + j) * LDN + 16 * b + li] = pdiag[j];
+        }
+        const int task = wave < 4 ? wave + 8 : wave;
+        if (task >= 6) {
+            int blk = task - 6, br = 1;
+            while (blk >= br) blk -= br++;
+            *reinterpret_cast<f32x4 *>(sP + (16 * br + li) * LDN + 16 * blk + 4 * lq) = poff;
+        }
+    }
     if (wave < 4) {
         const int b = wave;
 #pragma unroll
@@ -173,156 +300,302 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
     }
     __syncthreads();
     block_inverse64(sA, sX, wave, lane);
-    for (int e = tid; e < BC * BC / 4; e += 512)
-        *reinterpret_cast<f32x4 *>(wT + 4 * e) =
-            *reinterpret_cast<const f32x4 *>(sX + (e >> 4) * LDN + (e & 15) * 4);
+    for (int e = tid; e < BC * BC / 8; e += 512) {   // T diag(beta) (and P)
+        const int r = e >> 3, p = 8 * (e & 7);
+        const int i0 = (p & ~31) + (p & 31) / 2, i1 = i0 + 16;
+        const f32x4 t0 = *reinterpret_cast<const f32x4 *>(sX + r * LDN + i0) *
+                         *reinterpret_cast<const f32x4 *>(sb + i0);
+        const f32x4 t1 = *reinterpret_cast<const f32x4 *>(sX + r * LDN + i1) *
+                         *reinterpret_cast<const f32x4 *>(sb + i1);
+        const int off = r * WS::LC + p;
+        put_pair8(W + WS::TB + off, W + WS::TB + BC * WS::LC + off, t0, t1);
+        if constexpr (kStageP)
+            put_pair8(W + WS::P + off, W + WS::P + BC * WS::LC + off,
+                      *reinterpret_cast<const f32x4 *>(sP + r * LDN + i0),
+                      *reinterpret_cast<const f32x4 *>(sP + r * LDN + i1));
+    }
 }
 
 // ---------------------------------------------------------------- 2. fwd
+// Direct global-to-LDS copy of 16 bytes per lane: lane l's bytes land at
+// dst + 16 l (dst is the wave's base address), so a wave moves 1 KB.
+__device__ __forceinline__ void lds_dma16(void *dst, const void *src) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N): wait until at most N of this wave's vector memory
+// operations are outstanding (they complete in issue order).
+template <int N> __device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One workgroup per (sequence, head, 64 columns of d_v), chunks in order,
+// four phases per chunk:
+//   1. Y = (K o e^G) S^T and QS = (Q o e^G) S^T        (region 1)
+//   2. Delta = T diag(beta) (V - Y)                      (region 2 and V)
+//   3. O = QS + P Delta                                  (region 3)
+//   4. S^T <- Diag(e^{G_n}) S^T + (K o e^{G_n - G})^T Delta   (region 4)
+// Waves 0-3 copy each region of the next chunk into LDS with direct
+// global-to-LDS loads as soon as the consumers are done with the current
+// one (region 1 of chunk c + 1 during phase 2 of chunk c, and so on), and
+// before each barrier wait only until the region the next phase reads has
+// landed: every copy has three phases to arrive.  Waves 4-7 each own 16
+// columns of d_v: S^T (d_k x 16, fp32) in accumulator tiles, every product
+// on the bf16 MFMA as the three piece products hi*hi + lo*hi + hi*lo of
+// hi + lo pairs.
 template <int D, typename TI, typename TO>
-__global__ __launch_bounds__(512) void kda_fwd_kernel(
-    int T, int H, int NC, int varlen, const int32_t *__restrict__ cu,
-    const TI *__restrict__ v, const float *__restrict__ S0, const float *__restrict__ ws,
+__global__ __launch_bounds__(512, 1) void kda_fwd_kernel(
+    int T, int H, int NC, int varlen, int xcd_map, const int32_t *__restrict__ cu,
+    const TI *__restrict__ v, const float *__restrict__ S0, const bf16 *__restrict__ ws,
     TO *__restrict__ o, float *__restrict__ S_T) {
-    constexpr int LF = D + 4, NTC = D / 32, NSL = D / 64;
-    __shared__ __attribute__((aligned(16))) float sX1[BC * LF];   // K o e^G, then K o e^{G_n - G}
-    __shared__ __attribute__((aligned(16))) float sX2[BC * LF];   // Q o e^G
-    __shared__ __attribute__((aligned(16))) float sS[BC * LF];    // state slice: d_v rows x d_k
-    __shared__ __attribute__((aligned(16))) float sT[BC * LDN];
-    __shared__ __attribute__((aligned(16))) float sZ[BC * LDN];   // V slice, then Z
-    __shared__ __attribute__((aligned(16))) float sD[BC * LDN];   // Delta
-    __shared__ float sb[BC], seg[D];
-    const int uh = blockIdx.x / NSL, dv0 = 64 * (blockIdx.x % NSL);
-    const int u = uh / H, h = uh % H;
+    typedef KdaWs<D> WS;
+    constexpr int NSL = D / 64, NKS = D / 32, NCT = D / 16;
+    constexpr int LK = WS::LK, LC = WS::LC;
+    constexpr int VP = 16 / sizeof(TI);               // V elements per 16-byte piece
+    constexpr int VROWS = 1024 / (64 * sizeof(TI));   // V rows per KB
+    // KB per region, and the fewest 1 KB copies any loader wave issues for it
+    constexpr int K1 = WS::TB / 512, K2 = (WS::P - WS::TB) / 512, K3 = (WS::KT - WS::P) / 512,
+                  K4 = (WS::total - WS::KT) / 512;
+    constexpr int C1 = K1 / 4, C2 = K2 / 4 + BC / VROWS / 4, C3 = K3 / 4, C4 = K4 / 4;
+    static_assert(BC / VROWS % 4 == 0 && C1 + C2 + C3 + C4 < 64, "copy counts");
+    __shared__ __attribute__((aligned(16))) bf16 sKQ[WS::TB];             // region 1
+    __shared__ __attribute__((aligned(16))) bf16 sTB[WS::P - WS::TB];     // region 2
+    __shared__ __attribute__((aligned(16))) bf16 sP[WS::KT - WS::P];      // region 3
+    __shared__ __attribute__((aligned(16))) bf16 sKT[WS::total - WS::KT]; // region 4
+    __shared__ __attribute__((aligned(16))) TI sV[BC * 64];               // V slice
+    const bf16 *sKG = sKQ + WS::KG, *sQG = sKQ + WS::QG;
+    const float *sEG = reinterpret_cast<const float *>(sKT + (WS::EG - WS::KT));
+
+    // Workgroup -> (unit, head, d_v slice); with xcd_map the slices of one
+    // (unit, head) land on the same XCD (workgroups are dealt to the 8 XCDs
+    // round-robin) and share its L2.
+    const int b = blockIdx.x;
+    int uh, sl;
+    if (xcd_map) {
+        uh = (b & 7) + 8 * (b / (8 * NSL));
+        sl = (b >> 3) % NSL;
+    } else {
+        uh = b / NSL;
+        sl = b % NSL;
+    }
+    const int u = uh / H, h = uh % H, dv0 = 64 * sl;
     long start, L;
     unit_span(u, T, varlen, cu, start, L);
     const int N = (int)((L + BC - 1) / BC);
     const int base = unit_base(u, NC, varlen, cu);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15, lq = lane >> 4;
-    const int tr = wave & 3, tc0 = (wave >> 2) * NTC;   // state tiles
-    const int ty = wave & 3, tx0 = 2 * (wave >> 2);     // 64 x 64 tiles
-    f32x4 st[NTC];   // st[t][j] = S[dv0 + 16 tr + 4 lq + j][16 (tc0 + t) + li]
-#pragma unroll
-    for (int t = 0; t < NTC; ++t)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-            st[t][j] = S0 ? S0[((size_t)uh * D + dv0 + row) * D + col] : 0.f;
-        }
-    Prefetch<D, float> pkg, pqg, pkt;
-    Prefetch<BC, float> pt;
-    Prefetch<64, TI> pv;
-    float pP[16];   // P[16 ty + li][4 m + lq], this lane's operand of P Delta
-    float pb = 0.f, pe0 = 0.f;
-    auto wsof = [&](int c) { return ws + ((size_t)(base + c) * H + h) * KdaWs<D>::total; };
-    auto fetch_next = [&](int c) {   // operands of chunk c used in its first phases
+    auto wsof = [&](int c) { return ws + ((size_t)(base + c) * H + h) * WS::total; };
+
+    // ---- loaders (waves 0-3): wave w copies the KB pieces w, w + 4, ...
+    auto copy_region = [&](bf16 *dst, const bf16 *src, int kb) {
+        for (int i = wave; i < kb; i += 4)
+            lds_dma16(reinterpret_cast<char *>(dst) + 1024 * i,
+                      reinterpret_cast<const char *>(src) + 1024 * i + 16 * lane);
+    };
+    auto copy_v = [&](int c) {   // rows past the chunk repeat its last token (their
+                                 // T diag(beta) columns are zero)
         const long row0 = start + (long)c * BC;
         const int n = (int)min((long)BC, L - (long)c * BC);
-        const float *W = wsof(c);
-        pt.fetch(W, BC, BC, tid);
-        pkg.fetch(W + KdaWs<D>::T + KdaWs<D>::P, D, BC, tid);
-        pqg.fetch(W + KdaWs<D>::T + KdaWs<D>::P + KdaWs<D>::KG, D, BC, tid);
-        pv.fetch(v + ((size_t)row0 * H + h) * D + dv0, (size_t)H * D, n, tid);
-        const float *we = W + KdaWs<D>::T + KdaWs<D>::P + 3 * KdaWs<D>::KG;
-        if (tid < BC) pb = we[D + tid];
-        if (tid < D) pe0 = we[tid];
+        for (int i = wave; i < BC / VROWS; i += 4) {
+            const int r = min(VROWS * i + lane / (64 / VROWS), n - 1);
+            const TI *src = v + ((size_t)(row0 + r) * H + h) * D + dv0 + VP * (lane % (64 / VROWS));
+            lds_dma16(sV + 1024 / sizeof(TI) * i, src);
+        }
     };
-    auto fetch_late = [&](int c) {   // operands of chunk c used in its last phases
-        const float *W = wsof(c);
-        pkt.fetch(W + KdaWs<D>::T + KdaWs<D>::P + 2 * KdaWs<D>::KG, D, BC, tid);
-        const float *P = W + KdaWs<D>::T;
+    auto copy1 = [&](int c) { copy_region(sKQ, wsof(c), K1); };
+    auto copy2 = [&](int c) { copy_region(sTB, wsof(c) + WS::TB, K2); copy_v(c); };
+    auto copy3 = [&](int c) { copy_region(sP, wsof(c) + WS::P, K3); };
+    auto copy4 = [&](int c) { copy_region(sKT, wsof(c) + WS::KT, K4); };
+
+    // A loader wave's barrier: its copies for the next phase are waited for
+    // by count (wait_vm) beforehand, and nothing is moved across it; a full
+    // __syncthreads would wait for every copy in flight.
+    auto loader_barrier = [&]() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    if (wave < 4) {
+        // ---- loaders.  Copies in issue order: 1(0) 2(0) 3(0) 4(0) | per
+        // chunk c: 1(c+1) in phase 2, 2(c+1) in phase 3, 3(c+1) in phase 4,
+        // 4(c+1) in phase 1 of chunk c + 1.  Before each barrier a wave waits
+        // until the region the next phase reads has landed: the copies issued
+        // after it may still be in flight.
+        if (N > 0) {
+            copy1(0);
+            copy2(0);
+            copy3(0);
+            copy4(0);
+            wait_vm<C2 + C3 + C4>();   // region 1 of chunk 0
+        }
+        loader_barrier();
+        for (int c = 0; c < N; ++c) {
+            const bool more = c + 1 < N;
+            if (c > 0) copy4(c);
+            wait_vm<C3 + C4>();        // region 2 of chunk c
+            loader_barrier();
+            if (more) {
+                copy1(c + 1);
+                wait_vm<C4 + C1>();    // region 3 of chunk c
+            } else {
+                wait_vm<C4>();
+            }
+            loader_barrier();
+            if (more) {
+                copy2(c + 1);
+                wait_vm<C1 + C2>();    // region 4 of chunk c
+            } else {
+                wait_vm<0>();
+            }
+            loader_barrier();
+            if (more) {
+                copy3(c + 1);
+                wait_vm<C2 + C3>();    // region 1 of chunk c + 1
+            }
+            loader_barrier();
+        }
+        return;
+    }
+
+    // ---- consumers (waves 4-7): d_v columns dv0 + 16 cw + li
+    const int cw = wave - 4;
+    const int vcol = dv0 + 16 * cw + li;
+    f32x4 st[NCT];   // st[t][j] = S^T[16 t + 4 lq + j][vcol]
 #pragma unroll
-        for (int m = 0; m < 16; ++m) pP[m] = P[(16 * ty + li) * BC + 4 * m + lq];
-    };
-    if (N > 0) fetch_next(0);
+    for (int t = 0; t < NCT; ++t)
+        st[t] = S0 ? *reinterpret_cast<const f32x4 *>(S0 + ((size_t)uh * D + vcol) * D + 16 * t + 4 * lq)
+                   : zero4();
+    __syncthreads();
     for (int c = 0; c < N; ++c) {
-        const long row0 = start + (long)c * BC;
-        const int n = (int)min((long)BC, L - (long)c * BC);
-#pragma unroll
-        for (int t = 0; t < NTC; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-                sS[row * LF + col] = st[t][j];
-            }
-        pt.commit(sT, LDN, tid);
-        pkg.commit(sX1, LF, tid);
-        pqg.commit(sX2, LF, tid);
-        pv.commit(sZ, LDN, tid);
-        if (tid < BC) sb[tid] = pb;
-        if (tid < D) seg[tid] = pe0;
-        __syncthreads();
-        fetch_late(c);
-        if (c + 1 < N) fetch_next(c + 1);
-        // Z = diag(beta) (V - (K o e^G) S^T) in place of V; QS = (Q o e^G) S^T
-        f32x4 y[2], qs[2];
-        zero_n(y);
-        zero_n(qs);
-        mm_rows2<D, 2>(sX1 + 16 * ty * LF, sX2 + 16 * ty * LF, LF, sS + 16 * tx0 * LF, LF, y, qs,
-                       lane);
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * ty + 4 * lq + j, col = 16 * (tx0 + x) + li;
-                float *z = sZ + r * LDN + col;
-                *z = sb[r] * (*z - y[x][j]);
-            }
-        __syncthreads();
-        // Delta = T Z; K o e^{G_n - G} replaces K o e^G
+        // ---- phase 1: Y = (K o e^G) S^T, QS = (Q o e^G) S^T
+        f32x4 y[4], qs[4];
         {
-            f32x4 d[2];
-            zero_n(d);
-            mmn<BC, 2>(sT + 16 * ty * LDN, LDN, 1, sZ + 16 * tx0, LDN, 1, 16, d, lane);
-            for (int x = 0; x < 2; ++x)
+            bf16x8 sh[NKS], sl_[NKS];
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    sD[(16 * ty + 4 * lq + j) * LDN + 16 * (tx0 + x) + li] = d[x][j];
-        }
-        pkt.commit(sX1, LF, tid);
-        __syncthreads();
-        // O = QS + P Delta (P from registers)
+            for (int ks = 0; ks < NKS; ++ks) split_op(st[2 * ks], st[2 * ks + 1], sh[ks], sl_[ks]);
 #pragma unroll
-        for (int m = 0; m < 16; ++m)
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 yy = zero4(), a = zero4();
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
-                qs[x] = mfma_f32(pP[m], sD[(4 * m + lq) * LDN + 16 * (tx0 + x) + li], qs[x]);
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * ty + 4 * lq + j, col = 16 * (tx0 + x) + li;
-                if (r < n) o[((size_t)(row0 + r) * H + h) * D + dv0 + col] = cvt<TO>(qs[x][j]);
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int off = (16 * rt + li) * LK + 32 * ks + 8 * lq;
+                    const bf16x8 kh = ld8(sKG + off), kl = ld8(sKG + BC * LK + off);
+                    const bf16x8 qh = ld8(sQG + off), ql = ld8(sQG + BC * LK + off);
+                    yy = mfma32(kh, sh[ks], yy);
+                    a = mfma32(qh, sh[ks], a);
+                    yy = mfma32(kl, sh[ks], yy);
+                    a = mfma32(ql, sh[ks], a);
+                    yy = mfma32(kh, sl_[ks], yy);
+                    a = mfma32(qh, sl_[ks], a);
+                }
+                y[rt] = yy;
+                qs[rt] = a;
             }
-        // S <- S Diag(e^{G_n}) + Delta^T (K o e^{G_n - G})
+        }
+        __syncthreads();
+        // ---- phase 2: Delta = T diag(beta) (V - Y)
+        bf16x8 dh[2], dl[2];   // Delta as D-order B operands (tokens 0-31, 32-63)
+        {
+            f32x4 z[4];
 #pragma unroll
-        for (int t = 0; t < NTC; ++t) st[t] = st[t] * seg[16 * (tc0 + t) + li];
-        mmn<BC, NTC>(sD + 16 * tr, 1, LDN, sX1 + 16 * tc0, LF, 1, 16, st, lane);
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 vv;
+                if constexpr (sizeof(TI) == 2) {
+                    const bf16x4 x = lds_read_tr(sV + (16 * rt + 4 * lq + (li >> 2)) * 64 + 16 * cw +
+                                                 4 * (li & 3));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) vv[j] = (float)x[j];
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) vv[j] = to_f32(sV[(16 * rt + 4 * lq + j) * 64 + 16 * cw + li]);
+                }
+                z[rt] = vv - y[rt];
+            }
+            bf16x8 zh[2], zl[2];
+            split_op(z[0], z[1], zh[0], zl[0]);
+            split_op(z[2], z[3], zh[1], zl[1]);
+            f32x4 dd[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int off = (16 * rt + li) * LC + 32 * ks + 8 * lq;
+                    const bf16x8 th = ld8(sTB + off), tl = ld8(sTB + BC * LC + off);
+                    acc = mfma32(th, zh[ks], acc);
+                    acc = mfma32(tl, zh[ks], acc);
+                    acc = mfma32(th, zl[ks], acc);
+                }
+                dd[rt] = acc;
+            }
+            split_op(dd[0], dd[1], dh[0], dl[0]);
+            split_op(dd[2], dd[3], dh[1], dl[1]);
+        }
+        __syncthreads();
+        // ---- phase 3: O = QS + P Delta
+        {
+            const long row0 = start + (long)c * BC;
+            const int n = (int)min((long)BC, L - (long)c * BC);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 acc = qs[rt];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int off = (16 * rt + li) * LC + 32 * ks + 8 * lq;
+                    const bf16x8 ph = ld8(sP + off), pl = ld8(sP + BC * LC + off);
+                    acc = mfma32(ph, dh[ks], acc);
+                    acc = mfma32(pl, dh[ks], acc);
+                    acc = mfma32(ph, dl[ks], acc);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * rt + 4 * lq + j;
+                    if (r < n) o[((size_t)(row0 + r) * H + h) * D + vcol] = cvt<TO>(acc[j]);
+                }
+            }
+        }
+        __syncthreads();
+        // ---- phase 4: S^T <- Diag(e^{G_n}) S^T + (K o e^{G_n - G})^T Delta
+#pragma unroll
+        for (int t = 0; t < NCT; ++t) {
+            f32x4 acc = st[t] * *reinterpret_cast<const f32x4 *>(sEG + 16 * t + 4 * lq);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int off = (16 * t + li) * LC + 32 * ks + 8 * lq;
+                const bf16x8 kh = ld8(sKT + off), kl = ld8(sKT + D * LC + off);
+                acc = mfma32(kh, dh[ks], acc);
+                acc = mfma32(kl, dh[ks], acc);
+                acc = mfma32(kh, dl[ks], acc);
+            }
+            st[t] = acc;
+        }
         __syncthreads();
     }
     if (S_T) {
 #pragma unroll
-        for (int t = 0; t < NTC; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-                S_T[((size_t)uh * D + dv0 + row) * D + col] = st[t][j];
-            }
+        for (int t = 0; t < NCT; ++t)
+            *reinterpret_cast<f32x4 *>(S_T + ((size_t)uh * D + vcol) * D + 16 * t + 4 * lq) = st[t];
     }
 }
 
 template <int D, typename TI, typename TO>
 hipError_t launch_kda_t(int units, int T, int H, const int32_t *cu, const void *q, const void *k,
                         const void *v, const float *la, const float *beta, const float *S0,
-                        void *o, float *S_T, float *ws, long nslots, hipStream_t st) {
+                        void *o, float *S_T, bf16 *ws, long nslots, hipStream_t st) {
     const int varlen = cu != nullptr;
     const int NC = varlen ? 0 : (T + BC - 1) / BC;
     const size_t nch = (size_t)nslots * H;
     if (nch > 0)
         hipLaunchKernelGGL((kda_prep_kernel<D, TI>), dim3((unsigned)nch), dim3(512), 0, st, T, H,
                            units, NC, varlen, cu, (const TI *)q, (const TI *)k, la, beta, ws);
-    hipLaunchKernelGGL((kda_fwd_kernel<D, TI, TO>), dim3((unsigned)((long)units * H * (D / 64))),
-                       dim3(512), 0, st, T, H, NC, varlen, cu, (const TI *)v, S0, ws, (TO *)o,
-                       S_T);
+    const long nuh = (long)units * H;
+    const int xcd_map = nuh % 8 == 0 ? 1 : 0;
+    hipLaunchKernelGGL((kda_fwd_kernel<D, TI, TO>), dim3((unsigned)(nuh * (D / 64))), dim3(512),
+                       0, st, T, H, NC, varlen, xcd_map, cu, (const TI *)v, S0, ws, (TO *)o, S_T);
     return hipGetLastError();
 }
 
@@ -336,7 +609,7 @@ bool kda_supported(int dk, int dv, int chunk, bool io_bf16) {
 size_t kda_ws_bytes(int units, int T, int H, int d, bool varlen) {
     const long nslots = varlen ? (long)T / BC + units + 1 : (long)units * ((T + BC - 1) / BC);
     const size_t per = d == 128 ? KdaWs<128>::total : KdaWs<64>::total;
-    return sizeof(float) * (size_t)nslots * H * per;
+    return sizeof(bf16) * (size_t)nslots * H * per;
 }
 
 // ---------------------------------------------------------------- no allocation
@@ -376,7 +649,7 @@ hipError_t launch_kda_fwd(int units, int T, int H, int d, bool io_bf16, bool o_b
                           const float *la, const float *beta, const float *S0, void *o,
                           float *S_T, void *ws, hipStream_t st) {
     const long nslots = cu ? (long)T / BC + units + 1 : (long)units * ((T + BC - 1) / BC);
-    float *w = (float *)ws;
+    bf16 *w = (bf16 *)ws;
 #define GDN_KDA(DV, TI, TO) \
     return launch_kda_t<DV, TI, TO>(units, T, H, cu, q, k, v, la, beta, S0, o, S_T, w, nslots, st)
     if (io_bf16) {

@@ -189,7 +189,13 @@ def test_kda_workspace_and_rejects():
         return B.lib().gdn_kda_fwd_workspace_size(ctypes.byref(s), ctypes.byref(out)), out.value
     rc, nb = kws(shape(T=130))
     nch = 2 * 3 * 4
-    assert rc == OK and nb == 4 * nch * (2 * 64 * 64 + 3 * 64 * 128 + 128 + 64)
+    # per chunk and head, bf16 hi + lo pairs in four regions of whole KB (512
+    # elements): K o e^G and Q o e^G (rows of d + 8), T diag(beta), P (rows of
+    # 72), (K o e^{G_n - G})^T (d rows of 72) with e^{G_n} (d floats)
+    up = lambda x: (x + 511) // 512 * 512
+    d = 128
+    per = up(4 * 64 * (d + 8)) + 2 * up(2 * 64 * 72) + up(2 * d * 72 + 2 * d)
+    assert rc == OK and nb == 2 * nch * per
     assert kws(shape(prologue=2))[0] == UNSUPPORTED
     assert kws(shape(io_dtype=0))[0] == UNSUPPORTED
     assert kws(shape(chunk=16))[0] == UNSUPPORTED

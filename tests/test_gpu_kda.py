@@ -1,8 +1,10 @@
 """Parity of the channel-wise decay (KDA) forward, through the C ABI, with
 the fp64 oracle ``oracle.kda_fwd`` (pins in tests/test_oracle_kda.py).
 
-The GPU computes in fp32 from inputs exact in fp32 (bf16 upcast), so the bar
-is max |gpu - oracle| <= 1e-3 * RMS(oracle) on o and on the final states.
+The GPU computes A, P and T in fp32 and every product of the sequential
+launch from hi + lo bf16 pairs (about 16 mantissa bits per operand, three
+piece products), so the bar is max |gpu - oracle| <= 1e-3 * RMS(oracle) on o
+and on the final states.
 """
 import os
 
