@@ -329,17 +329,19 @@ def run_kda(args, torch, gi, gdn, dev, w):
                     "channel-wise log alpha [B,T,H,d_k], fp32 o and state"}
 
 
-def gdn2_flops_per_chunk_head(d: int, C: int = 64) -> float:
-    """fp32 MFMA flops of gdn_gdn2_fwd per (chunk, head): prep -- the 6
-    blocks below the diagonal of each of A_e, A_k, P_e, P_k, the folds
-    M = P_e T_e, N1 = T_e A_k, N2 (C^3 each), F1 and Qh (C x C x d each) --
-    and the sequential launch: F1 S^T, Qh S^T (C x d x d), N1 Z, N2 Z (C^2 x d)
-    and the two update products (d x C x d).  Diagonal blocks (term-by-term
-    VALU) are not counted."""
+def gdn2_flops_per_chunk_head(d: int, C: int = 64):
+    """MFMA flops of gdn_gdn2_fwd per (chunk, head), as (fp32 products of the
+    prep, fp32-accurate products of the sequential launch).  Prep, on the fp32
+    MFMA: the 6 blocks below the diagonal of each of A_e, A_k, P_e, P_k, the
+    folds M = P_e T_e, N1 = T_e A_k, N2 (C^3 each), F1 and Qh (C x C x d
+    each).  Sequential launch, each product as three bf16 piece products of
+    hi + lo pairs: F1 S^T, Qh S^T (C x d x d), N1 Z, N2 Z (C^2 x d) and the two
+    update products (d x C x d).  Diagonal blocks (term-by-term VALU) are not
+    counted."""
     cdd = 2.0 * C * d * d
     ccd = 2.0 * C * C * d
     prep = 4 * 6 * 2.0 * 16 * 16 * d + 3 * 2.0 * C ** 3 + 2 * ccd
-    return prep + 2 * cdd + 2 * ccd + 2 * cdd
+    return prep, 2 * cdd + 2 * ccd + 2 * cdd
 
 
 def run_gdn2(args, torch, gi, gdn, dev, w):
@@ -360,16 +362,25 @@ def run_gdn2(args, torch, gi, gdn, dev, w):
                      chunk=C, o=o, S_T=st, workspace=ws)
 
     ms = time_calls(torch, step, steps, warm)
-    fl = gdn2_flops_per_chunk_head(dk, C) * B * H * ((T + C - 1) // C)
-    tfs = fl / (ms * 1e-3) / 1e12
+    nch = B * H * ((T + C - 1) // C)
+    f_prep, f_seq = gdn2_flops_per_chunk_head(dk, C)
     hbm = hbm_roofline(channel_fwd_bytes(B, T, H, dk, dv, 2 * dk + dv), ms, ws.numel())
+    bf16_tfs = 3 * f_seq * nch / (ms * 1e-3) / 1e12
     return {"ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
-            "steps": steps, "hbm_roofline": hbm,
-            "roofline": {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_FP32_PEAK_TFS,
-                         "unit": "TFLOP/s", "frac": round(tfs / MFMA_FP32_PEAK_TFS, 4),
-                         "dtype": "f32", "flops_per_step": fl},
-            "note": "gdn_gdn2_fwd = prep + sequential launch, fp32 MFMA; bf16 q/k/v, fp32 "
-                    "log alpha and erase gates [B,T,H,d_k], write gates [B,T,H,d_v]"}
+            "steps": steps, "roofline": hbm,
+            "mfma_executed": {"bf16_piece_products_tflops": round(bf16_tfs, 1),
+                              "frac_of_bf16_peak": round(bf16_tfs / MFMA_BF16_PEAK_TFS, 4),
+                              "prep_f32_tflops": round(f_prep * nch / (ms * 1e-3) / 1e12, 1),
+                              "frac_of_f32_peak_prep": round(f_prep * nch / (ms * 1e-3) / 1e12
+                                                             / MFMA_FP32_PEAK_TFS, 4),
+                              "flops_per_step": {"prep_f32": f_prep * nch,
+                                                 "sequential_fp32_accurate": f_seq * nch}},
+            "note": "gdn_gdn2_fwd = prep (fp32 MFMA: channel-weighted blocks, T_e, the folds "
+                    "F1, Qh, N1, N2; writes the sequential launch's operands as bf16 hi + lo "
+                    "pairs in its LDS layout) + sequential launch (bf16 MFMA, three piece "
+                    "products per product, five phases, operand regions copied global->LDS "
+                    "ahead of use). bf16 q/k/v, fp32 log alpha and erase gates [B,T,H,d_k], "
+                    "write gates [B,T,H,d_v]"}
 
 
 def run_prologue(args, torch, gi, gdn, dev, w, plain_ms):

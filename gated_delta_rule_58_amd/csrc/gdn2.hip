@@ -1,4 +1,4 @@
-// Gated DeltaNet-2 forward on gfx950 (fp32 MFMA): channel-wise decay with a
+// Gated DeltaNet-2 forward on gfx950: channel-wise decay with a
 // channel-wise erase gate on the key side and a write gate on the value side.
 //
 // "Gated DeltaNet-2: Decoupling Erase and Write in Linear Attention"
@@ -20,22 +20,39 @@
 //   F1 = T_e (K o e^G),  N1 = T_e A_k,  M = P_e T_e,
 //   Qh = Q o e^G - M (K o e^G),  N2 = P_k - M A_k,
 // leaves the sequential launch X = -(F1 S^T + N1 Z), O = Qh S^T + N2 Z and the
-// state update.
+// state update.  The prep works in fp32 (fp32 MFMA); the sequential launch
+// multiplies operand images the prep writes as bf16 hi + lo pairs on the
+// bf16 MFMA (img_tiles.h).
 #include "fp32_tiles.h"
+#include "img_tiles.h"
 
 namespace gdn {
 namespace {
 
 using namespace tiles;
+using namespace img;
 
 
-// Workspace blocks (floats) per chunk and head.
+// Workspace of one chunk and head: the operands of the sequential launch as
+// bf16 hi + lo pairs in the layout it keeps in LDS (rows padded by 8, each
+// 32-wide column block in D-order; img_tiles.h), offsets in bf16 elements.
+// Five regions of whole KB in the order the sequential launch reads them:
+// F1, Qh (64 x D each), (E o e^{G_n - G})^T with e^{G_n}, (K o e^{G_n - G})^T
+// (D x 64 each), and N1 with N2 (64 x 64 each).
 template <int D> struct G2Ws {
-    static constexpr size_t N1 = BC * BC, N2 = BC * BC, F1 = BC * D, QH = BC * D, ET = BC * D,
-                            KT = BC * D, EG = D;
-    static constexpr size_t total = N1 + N2 + F1 + QH + ET + KT + EG;
-    static constexpr size_t oN1 = 0, oN2 = N1, oF1 = oN2 + N2, oQH = oF1 + F1, oET = oQH + QH,
-                            oKT = oET + ET, oEG = oKT + KT;
+    static constexpr int LK = D + 8, LC = BC + 8;   // row strides of the 64 x D and x 64 blocks
+    static constexpr size_t up(size_t x) { return (x + 511) / 512 * 512; }
+    static constexpr size_t F1 = 0,                       // T_e (K o e^G): hi, lo
+                            QH = up(2 * BC * LK),         // Q o e^G - M (K o e^G): hi, lo
+                            ET = QH + up(2 * BC * LK),    // (E o e^{G_n - G})^T: hi, lo
+                            EG = ET + 2 * D * LC,         // e^{G_n}: D floats
+                            KT = up(EG + 2 * D),          // (K o e^{G_n - G})^T: hi, lo
+                            N1 = KT + up(2 * D * LC),     // T_e A_k: hi, lo
+                            N2 = N1 + 2 * BC * LC,        // P_k - M A_k: hi, lo
+                            total = up(N2 + 2 * BC * LC);
+    static_assert(QH == 2 * BC * LK && KT - (EG + 2 * D) < 512 && N1 == KT + 2 * D * LC &&
+                      total == N2 + 2 * BC * LC,
+                  "regions are contiguous");
 };
 
 // ---------------------------------------------------------------- 1. prep
@@ -43,7 +60,7 @@ template <int D, typename TI>
 __global__ __launch_bounds__(512) void gdn2_prep_kernel(
     int T, int H, int units, int NC, int varlen, const int32_t *__restrict__ cu,
     const TI *__restrict__ q, const TI *__restrict__ k, const float *__restrict__ la,
-    const float *__restrict__ erase, float *__restrict__ ws, int nch) {
+    const float *__restrict__ erase, bf16 *__restrict__ ws, int nch) {
     constexpr int LI = ldx<TI, D>(), LF = D + 4, LE = D + 8;
     constexpr int NE = BC * LE > 2 * BC * LDN ? BC * LE : 2 * BC * LDN;   // E, then A_e | A_k
     __shared__ __attribute__((aligned(16))) TI sK[BC * LI];
@@ -81,7 +98,9 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
     int lane = tid & 63;
     asm volatile("" : "+v"(lane));
     const int li = lane & 15, lq = lane >> 4;
-    float *W = ws + (size_t)ci * G2Ws<D>::total;
+    typedef G2Ws<D> WS;
+    bf16 *W = ws + (size_t)ci * WS::total;
+    float *wEG = reinterpret_cast<float *>(W + WS::EG);
     pk.commit(sK, LI, tid);
     pq.commit(sQ, LI, tid);
     pg.commit(sG, LF, tid);
@@ -95,7 +114,7 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
             g += sG[r * LF + tid];
             sG[r * LF + tid] = g;
         }
-        W[G2Ws<D>::oEG + tid] = expf(g);
+        wEG[tid] = expf(g);
     }
     for (int e = tid; e < BC * D / 4; e += 512) {   // E = b o k
         const int r = e / (D / 4), c = (e % (D / 4)) * 4;
@@ -104,22 +123,35 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
         *pe = *pe * kv;
     }
     __syncthreads();
-    // E o e^{G_n - G} and K o e^{G_n - G} for the state update
-    for (int e = tid; e < BC * D / 4; e += 512) {
-        const int r = e / (D / 4), c = (e % (D / 4)) * 4;
-        const f32x4 g = *reinterpret_cast<const f32x4 *>(sG + r * LF + c);
-        const f32x4 gn = *reinterpret_cast<const f32x4 *>(sG + (BC - 1) * LF + c);
-        const f32x4 kv = ld4f(sK + r * LI + c);
-        const f32x4 ev = *reinterpret_cast<const f32x4 *>(sE + r * LE + c);
-        f32x4 et, kt;
+    // (E o e^{G_n - G})^T and (K o e^{G_n - G})^T for the state update, one
+    // D-order group of 8 tokens of one channel per item (16-byte stores)
+    for (int e = tid; e < D * BC / 8; e += 512) {
+        const int c = e / (BC / 8), p = 8 * (e % (BC / 8));
+        const int r0 = (p & ~31) + (p & 31) / 2, r1 = r0 + 16;   // tokens r0..+3, r1..+3
+        const float gn = sG[(BC - 1) * LF + c];
+        f32x4 e0, e1, k0, k1;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float t = __expf(gn[j] - g[j]);
-            et[j] = ev[j] * t;
-            kt[j] = kv[j] * t;
+            const float t0 = __expf(gn - sG[(r0 + j) * LF + c]), t1 = __expf(gn - sG[(r1 + j) * LF + c]);
+            e0[j] = sE[(r0 + j) * LE + c] * t0;
+            e1[j] = sE[(r1 + j) * LE + c] * t1;
+            k0[j] = to_f32(sK[(r0 + j) * LI + c]) * t0;
+            k1[j] = to_f32(sK[(r1 + j) * LI + c]) * t1;
         }
-        *reinterpret_cast<f32x4 *>(W + G2Ws<D>::oET + 4 * e) = et;
-        *reinterpret_cast<f32x4 *>(W + G2Ws<D>::oKT + 4 * e) = kt;
+        const int off = c * WS::LC + p;
+        put_pair8(W + WS::ET + off, W + WS::ET + D * WS::LC + off, e0, e1);
+        put_pair8(W + WS::KT + off, W + WS::KT + D * WS::LC + off, k0, k1);
+    }
+    // row padding and the tail after e^{G_n} are written too (zeros), so every
+    // cache line of the workspace is written whole
+    for (int e = tid; e < 8 * BC + 4 * D + (int)(WS::KT - WS::EG - 2 * D) / 8; e += 512) {
+        size_t off;
+        if (e < 4 * BC) off = WS::F1 + (size_t)e * WS::LK + D;                        // F1, Qh
+        else if (e < 8 * BC) off = WS::N1 + (size_t)(e - 4 * BC) * WS::LC + BC;       // N1, N2
+        else if (e < 8 * BC + 2 * D) off = WS::ET + (size_t)(e - 8 * BC) * WS::LC + BC;
+        else if (e < 8 * BC + 4 * D) off = WS::KT + (size_t)(e - 8 * BC - 2 * D) * WS::LC + BC;
+        else off = WS::EG + 2 * D + (size_t)(e - 8 * BC - 4 * D) * 8;
+        *reinterpret_cast<bf16x8 *>(W + off) = bf16x8{};
     }
     // The four channel-weighted products, 16 x 16 blocks (br, bi), bi <= br:
     // matrix mx = 0 A_e (rows K, columns E), 1 A_k (K, K), 2 P_e (Q, E),
@@ -210,7 +242,8 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * ty + 4 * lq + j, c = 16 * (tx0 + x) + li;
                 sAe[r * LDN + c] = m[x][j];
-                W[G2Ws<D>::oN1 + r * BC + c] = n1[x][j];
+                const int off = r * WS::LC + dpos(c);
+                put_pair1(W + WS::N1 + off, W + WS::N1 + BC * WS::LC + off, n1[x][j]);
             }
     }
     __syncthreads();
@@ -223,11 +256,14 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * ty + 4 * lq + j, c = 16 * (tx0 + x) + li;
-                W[G2Ws<D>::oN2 + r * BC + c] = sPk[r * LDN + c] - n2[x][j];
+                const int off = r * WS::LC + dpos(c);
+                put_pair1(W + WS::N2 + off, W + WS::N2 + BC * WS::LC + off,
+                          sPk[r * LDN + c] - n2[x][j]);
             }
     }
     // F1 = T_e (K o e^G) and Qh = Q o e^G - M (K o e^G), with K o e^G formed
-    // in the operand reads; 64 x D tiles, row tr, columns tc0..
+    // in the operand reads; 64 x D tiles, row tr, columns tc0.., formed
+    // transposed so that a lane holds four consecutive columns of one row
     {
         constexpr int NTC = D / 32;
         const int tr = wave & 3, tc0 = (wave >> 2) * NTC;
@@ -243,19 +279,22 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
             for (int t = 0; t < NTC; ++t) {
                 const int c = 16 * (tc0 + t) + li;
                 const float b = to_f32(sK[kr * LI + c]) * __expf(sG[kr * LF + c]);
-                f1[t] = mfma_f32(a1, b, f1[t]);
-                qh[t] = mfma_f32(a2, b, qh[t]);
+                f1[t] = mfma_f32(b, a1, f1[t]);
+                qh[t] = mfma_f32(b, a2, qh[t]);
             }
         }
 #pragma unroll
-        for (int t = 0; t < NTC; ++t)
+        for (int t = 0; t < NTC; ++t) {
+            const int r = 16 * tr + li, c = 16 * (tc0 + t) + 4 * lq;   // columns c..c+3
+            const f32x4 g = *reinterpret_cast<const f32x4 *>(sG + r * LF + c);
+            const f32x4 qv = ld4f(sQ + r * LI + c);
+            f32x4 qg;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * tr + 4 * lq + j, c = 16 * (tc0 + t) + li;
-                W[G2Ws<D>::oF1 + r * D + c] = f1[t][j];
-                W[G2Ws<D>::oQH + r * D + c] =
-                    to_f32(sQ[r * LI + c]) * __expf(sG[r * LF + c]) - qh[t][j];
-            }
+            for (int j = 0; j < 4; ++j) qg[j] = qv[j] * __expf(g[j]) - qh[t][j];
+            const int off = r * WS::LK + dpos(c);
+            put_pair4(W + WS::F1 + off, W + WS::F1 + BC * WS::LK + off, f1[t]);
+            put_pair4(W + WS::QH + off, W + WS::QH + BC * WS::LK + off, qg);
+        }
     }
     __syncthreads();   // every LDS operand consumed before the next pair's commit
     ci = cn;
@@ -263,133 +302,246 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
 }
 
 // ---------------------------------------------------------------- 2. fwd
+// One workgroup per (sequence, head, 64 columns of d_v), chunks in order,
+// five phases per chunk:
+//   1. a = F1 S^T                                   (F1 in buffer U)
+//   2. b = Qh S^T                                   (Qh in buffer W)
+//   3. Z = w o v; X = -(a + N1 Z), O = b + N2 Z     (N1, N2, w, v)
+//   4. S^T <- Diag(e^{G_n}) S^T + (E o e^{G_n - G})^T X   (buffer U)
+//   5. S^T <- S^T + (K o e^{G_n - G})^T Z                  (buffer W)
+// Waves 0-3 copy each region into LDS with direct global-to-LDS loads as
+// soon as its buffer is free (buffer U takes (E o e^{G_n - G})^T during
+// phase 2 and the next F1 during phase 5; buffer W takes (K o e^{G_n - G})^T
+// during phase 3 and the next Qh during the next phase 1; N1, N2, w and v of
+// the next chunk load during phase 4), and before each barrier wait by count
+// for the region the next phase reads.  Waves 4-7 each own 16 columns of
+// d_v: S^T (d_k x 16, fp32) in accumulator tiles, every product on the bf16
+// MFMA as the three piece products of hi + lo pairs.
 template <int D, typename TI, typename TO>
-__global__ __launch_bounds__(512) void gdn2_fwd_kernel(
-    int T, int H, int NC, int varlen, const int32_t *__restrict__ cu,
+__global__ __launch_bounds__(512, 1) void gdn2_fwd_kernel(
+    int T, int H, int NC, int varlen, int xcd_map, const int32_t *__restrict__ cu,
     const TI *__restrict__ v, const float *__restrict__ write, const float *__restrict__ S0,
-    const float *__restrict__ ws, TO *__restrict__ o, float *__restrict__ S_T) {
-    constexpr int LF = D + 4, NTC = D / 32, NSL = D / 64;
-    __shared__ __attribute__((aligned(16))) float sX1[BC * LF];   // F1, then E o e^{G_n - G}
-    __shared__ __attribute__((aligned(16))) float sX2[BC * LF];   // Qh, then K o e^{G_n - G}
-    __shared__ __attribute__((aligned(16))) float sS[BC * LF];    // state slice: d_v rows x d_k
-    __shared__ __attribute__((aligned(16))) float sZ[BC * LDN];   // Z = w o v (slice)
-    __shared__ __attribute__((aligned(16))) float sX[BC * LDN];   // X (erased reads, slice)
-    __shared__ float seg[D];
-    const int uh = blockIdx.x / NSL, dv0 = 64 * (blockIdx.x % NSL);
-    const int u = uh / H, h = uh % H;
+    const bf16 *__restrict__ ws, TO *__restrict__ o, float *__restrict__ S_T) {
+    typedef G2Ws<D> WS;
+    constexpr int NSL = D / 64, NKS = D / 32, NCT = D / 16;
+    constexpr int LK = WS::LK, LC = WS::LC;
+    constexpr int VP = 16 / sizeof(TI);               // V elements per 16-byte piece
+    constexpr int VROWS = 1024 / (64 * sizeof(TI));   // V rows per KB
+    constexpr int WROWS = 4;                          // w (fp32) rows per KB
+    // KB per region, and the fewest 1 KB copies any loader wave issues for it
+    constexpr int KU1 = (WS::QH - WS::F1) / 512, KW1 = (WS::ET - WS::QH) / 512,
+                  KU2 = (WS::KT - WS::ET) / 512, KW2 = (WS::N1 - WS::KT) / 512,
+                  KR = (WS::total - WS::N1) / 512;
+    constexpr int CU2 = KU2 / 4, CW1 = KW1 / 4, CW2 = KW2 / 4,
+                  CR = KR / 4 + BC / WROWS / 4 + BC / VROWS / 4;
+    static_assert(BC / VROWS % 4 == 0 && CU2 + CW2 + CR < 64, "copy counts");
+    constexpr int BU = KU1 > KU2 ? KU1 : KU2, BW = KW1 > KW2 ? KW1 : KW2;
+    __shared__ __attribute__((aligned(16))) bf16 sU[BU * 512];     // F1, then E^T and e^{G_n}
+    __shared__ __attribute__((aligned(16))) bf16 sW[BW * 512];     // Qh, then K^T
+    __shared__ __attribute__((aligned(16))) bf16 sN[KR * 512];     // N1, N2
+    __shared__ __attribute__((aligned(16))) float sWg[BC * 64];    // write gate slice
+    __shared__ __attribute__((aligned(16))) TI sV[BC * 64];        // V slice
+    const float *sEG = reinterpret_cast<const float *>(sU + (WS::EG - WS::ET));
+
+    // Workgroup -> (unit, head, d_v slice); with xcd_map the slices of one
+    // (unit, head) land on the same XCD (workgroups are dealt to the 8 XCDs
+    // round-robin) and share its L2.
+    const int b = blockIdx.x;
+    int uh, sl;
+    if (xcd_map) {
+        uh = (b & 7) + 8 * (b / (8 * NSL));
+        sl = (b >> 3) % NSL;
+    } else {
+        uh = b / NSL;
+        sl = b % NSL;
+    }
+    const int u = uh / H, h = uh % H, dv0 = 64 * sl;
     long start, L;
     unit_span(u, T, varlen, cu, start, L);
     const int N = (int)((L + BC - 1) / BC);
     const int base = unit_base(u, NC, varlen, cu);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15, lq = lane >> 4;
-    const int tr = wave & 3, tc0 = (wave >> 2) * NTC;
-    const int ty = wave & 3, tx0 = 2 * (wave >> 2);
-    f32x4 st[NTC];
-#pragma unroll
-    for (int t = 0; t < NTC; ++t)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-            st[t][j] = S0 ? S0[((size_t)uh * D + dv0 + row) * D + col] : 0.f;
+    auto wsof = [&](int c) { return ws + ((size_t)(base + c) * H + h) * WS::total; };
+
+    if (wave < 4) {
+        // ---- loaders: wave w copies the KB pieces w, w + 4, ...
+        auto copy_region = [&](bf16 *dst, const bf16 *src, int kb) {
+            for (int i = wave; i < kb; i += 4)
+                lds_dma16(reinterpret_cast<char *>(dst) + 1024 * i,
+                          reinterpret_cast<const char *>(src) + 1024 * i + 16 * lane);
+        };
+        // v and w rows past the chunk repeat its last token: the columns of
+        // N1, N2 and the rows of (K o e^{G_n - G})^T they meet are zero
+        auto copy_r = [&](int c) {
+            copy_region(sN, wsof(c) + WS::N1, KR);
+            const long row0 = start + (long)c * BC;
+            const int n = (int)min((long)BC, L - (long)c * BC);
+            for (int i = wave; i < BC / VROWS; i += 4) {
+                const int r = min(VROWS * i + lane / (64 / VROWS), n - 1);
+                lds_dma16(sV + 1024 / sizeof(TI) * i,
+                          v + ((size_t)(row0 + r) * H + h) * D + dv0 + VP * (lane % (64 / VROWS)));
+            }
+            for (int i = wave; i < BC / WROWS; i += 4) {
+                const int r = min(WROWS * i + lane / 16, n - 1);
+                lds_dma16(sWg + 256 * i, write + ((size_t)(row0 + r) * H + h) * D + dv0 + 4 * (lane % 16));
+            }
+        };
+        auto loader_barrier = [&]() {   // the copies are waited for by count beforehand
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        // Copies in issue order: U1(0) W1(0) R(0) | per chunk c: W1(c) (c > 0)
+        // in phase 1, U2(c) in 2, W2(c) in 3, R(c+1) in 4, U1(c+1) in 5.
+        if (N > 0) {
+            copy_region(sU, wsof(0) + WS::F1, KU1);
+            copy_region(sW, wsof(0) + WS::QH, KW1);
+            copy_r(0);
+            wait_vm<CW1 + CR>();   // F1 of chunk 0
         }
-    Prefetch<D, float> pf1, pqh, pet, pkt;
-    Prefetch<64, TI> pv;
-    Prefetch<64, float> pw;
-    float n1[16], n2[16];   // rows 16 ty + li of N1, N2: this lane's MFMA A operands
-    float pe = 0.f;
-    auto wsof = [&](int c) { return ws + ((size_t)(base + c) * H + h) * G2Ws<D>::total; };
-    auto fetch_next = [&](int c) {
-        const long row0 = start + (long)c * BC;
-        const int n = (int)min((long)BC, L - (long)c * BC);
-        const float *Wc = wsof(c);
-        pf1.fetch(Wc + G2Ws<D>::oF1, D, BC, tid);
-        pqh.fetch(Wc + G2Ws<D>::oQH, D, BC, tid);
-        pv.fetch(v + ((size_t)row0 * H + h) * D + dv0, (size_t)H * D, n, tid);
-        pw.fetch(write + ((size_t)row0 * H + h) * D + dv0, (size_t)H * D, n, tid);
-        if (tid < D) pe = Wc[G2Ws<D>::oEG + tid];
-    };
-    auto fetch_late = [&](int c) {
-        const float *Wc = wsof(c);
-        pet.fetch(Wc + G2Ws<D>::oET, D, BC, tid);
-        pkt.fetch(Wc + G2Ws<D>::oKT, D, BC, tid);
+        loader_barrier();
+        for (int c = 0; c < N; ++c) {
+            const bool more = c + 1 < N;
+            if (c > 0) copy_region(sW, wsof(c) + WS::QH, KW1);
+            wait_vm<0>();          // Qh of chunk c (and N1, N2, w, v before it)
+            loader_barrier();
+            copy_region(sU, wsof(c) + WS::ET, KU2);
+            wait_vm<CU2>();
+            loader_barrier();
+            copy_region(sW, wsof(c) + WS::KT, KW2);
+            wait_vm<CW2>();        // E^T of chunk c
+            loader_barrier();
+            if (more) {
+                copy_r(c + 1);
+                wait_vm<CR>();     // K^T of chunk c
+            } else {
+                wait_vm<0>();
+            }
+            loader_barrier();
+            if (more) {
+                copy_region(sU, wsof(c + 1) + WS::F1, KU1);
+                wait_vm<0>();      // F1 of chunk c + 1
+            }
+            loader_barrier();
+        }
+        return;
+    }
+
+    // ---- consumers (waves 4-7): d_v columns dv0 + 16 cw + li
+    const int cw = wave - 4;
+    const int vcol = dv0 + 16 * cw + li;
+    f32x4 st[NCT];   // st[t][j] = S^T[16 t + 4 lq + j][vcol]
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            n1[m] = Wc[G2Ws<D>::oN1 + (16 * ty + li) * BC + 4 * m + lq];
-            n2[m] = Wc[G2Ws<D>::oN2 + (16 * ty + li) * BC + 4 * m + lq];
+    for (int t = 0; t < NCT; ++t)
+        st[t] = S0 ? *reinterpret_cast<const f32x4 *>(S0 + ((size_t)uh * D + vcol) * D + 16 * t + 4 * lq)
+                   : zero4();
+    __syncthreads();
+    // A x S^T over 64 rows and d_k (A: hi at p, lo at p + lo_off; rows of lda)
+    auto rows_st = [&](const bf16 *p, int lda, int lo_off, const bf16x8 (&sh)[NKS],
+                       const bf16x8 (&sl)[NKS], f32x4 (&acc)[4]) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            f32x4 a = zero4();
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int off = (16 * rt + li) * lda + 32 * ks + 8 * lq;
+                const bf16x8 xh = ld8(p + off), xl = ld8(p + lo_off + off);
+                a = mfma32(xh, sh[ks], a);
+                a = mfma32(xl, sh[ks], a);
+                a = mfma32(xh, sl[ks], a);
+            }
+            acc[rt] = a;
         }
     };
-    if (N > 0) fetch_next(0);
+    // acc[t] += A_t B over 64 tokens (A: rows 16 t + li at p, lo at + lo_off;
+    // B: D-order pairs over tokens 0-31, 32-63)
+    auto tok_prod = [&](const bf16 *p, int lo_off, const bf16x8 (&bh)[2], const bf16x8 (&bl)[2],
+                        f32x4 &acc, int t) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int off = (16 * t + li) * LC + 32 * ks + 8 * lq;
+            const bf16x8 xh = ld8(p + off), xl = ld8(p + lo_off + off);
+            acc = mfma32(xh, bh[ks], acc);
+            acc = mfma32(xl, bh[ks], acc);
+            acc = mfma32(xh, bl[ks], acc);
+        }
+    };
     for (int c = 0; c < N; ++c) {
-        const long row0 = start + (long)c * BC;
-        const int n = (int)min((long)BC, L - (long)c * BC);
+        f32x4 a[4], bq[4];
+        {
+            bf16x8 sh[NKS], sl_[NKS];
 #pragma unroll
-        for (int t = 0; t < NTC; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-                sS[row * LF + col] = st[t][j];
-            }
-        pf1.commit(sX1, LF, tid);
-        pqh.commit(sX2, LF, tid);
-        pv.commit(sZ, LDN, tid);   // V slice; times w below
-        pw.commit(sX, LDN, tid);   // w slice (scratch until X is formed)
-        if (tid < D) seg[tid] = pe;
-        __syncthreads();
-        for (int e = tid; e < BC * 64; e += 512) {
-            const int r = e >> 6, cc = e & 63;
-            sZ[r * LDN + cc] *= sX[r * LDN + cc];
+            for (int ks = 0; ks < NKS; ++ks) split_op(st[2 * ks], st[2 * ks + 1], sh[ks], sl_[ks]);
+            rows_st(sU, LK, BC * LK, sh, sl_, a);     // phase 1: F1 S^T
+            __syncthreads();
+            rows_st(sW, LK, BC * LK, sh, sl_, bq);    // phase 2: Qh S^T
         }
-        fetch_late(c);
-        if (c + 1 < N) fetch_next(c + 1);
         __syncthreads();
-        // X = -(F1 S^T + N1 Z), O = Qh S^T + N2 Z (64 tokens x 64 slice columns)
-        f32x4 xa[2], oa[2];
-        zero_n(xa);
-        zero_n(oa);
-        mm_rows2<D, 2>(sX1 + 16 * ty * LF, sX2 + 16 * ty * LF, LF, sS + 16 * tx0 * LF, LF, xa, oa,
-                       lane);
+        // ---- phase 3: Z = w o v, X = -(F1 S^T + N1 Z), O = Qh S^T + N2 Z
+        bf16x8 zh[2], zl[2], xh[2], xl[2];
+        {
+            f32x4 z[4];
 #pragma unroll
-        for (int m = 0; m < 16; ++m)
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 vv;
+                if constexpr (sizeof(TI) == 2) {
+                    const bf16x4 x = lds_read_tr(sV + (16 * rt + 4 * lq + (li >> 2)) * 64 + 16 * cw +
+                                                 4 * (li & 3));
 #pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const float zb = sZ[(4 * m + lq) * LDN + 16 * (tx0 + x) + li];
-                xa[x] = mfma_f32(n1[m], zb, xa[x]);
-                oa[x] = mfma_f32(n2[m], zb, oa[x]);
+                    for (int j = 0; j < 4; ++j) vv[j] = (float)x[j];
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) vv[j] = to_f32(sV[(16 * rt + 4 * lq + j) * 64 + 16 * cw + li]);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) z[rt][j] = vv[j] * sWg[(16 * rt + 4 * lq + j) * 64 + 16 * cw + li];
             }
-        __syncthreads();   // F1, Qh and the w scratch consumed
-        for (int x = 0; x < 2; ++x)
+            split_op(z[0], z[1], zh[0], zl[0]);
+            split_op(z[2], z[3], zh[1], zl[1]);
+            const long row0 = start + (long)c * BC;
+            const int n = (int)min((long)BC, L - (long)c * BC);
+            f32x4 x[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * ty + 4 * lq + j, col = 16 * (tx0 + x) + li;
-                sX[r * LDN + col] = -xa[x][j];
-                if (r < n) o[((size_t)(row0 + r) * H + h) * D + dv0 + col] = cvt<TO>(oa[x][j]);
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 xa = a[rt], oa = bq[rt];
+                tok_prod(sN, BC * LC, zh, zl, xa, rt);
+                tok_prod(sN + 2 * BC * LC, BC * LC, zh, zl, oa, rt);
+                x[rt] = -xa;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * rt + 4 * lq + j;
+                    if (r < n) o[((size_t)(row0 + r) * H + h) * D + vcol] = cvt<TO>(oa[j]);
+                }
             }
-        pet.commit(sX1, LF, tid);
-        pkt.commit(sX2, LF, tid);
+            split_op(x[0], x[1], xh[0], xl[0]);
+            split_op(x[2], x[3], xh[1], xl[1]);
+        }
         __syncthreads();
-        // S <- S Diag(e^{G_n}) + X^T (E o e^{G_n - G}) + Z^T (K o e^{G_n - G})
+        // ---- phase 4: S^T <- Diag(e^{G_n}) S^T + (E o e^{G_n - G})^T X
 #pragma unroll
-        for (int t = 0; t < NTC; ++t) st[t] = st[t] * seg[16 * (tc0 + t) + li];
-        mmn<BC, NTC>(sX + 16 * tr, 1, LDN, sX1 + 16 * tc0, LF, 1, 16, st, lane);
-        mmn<BC, NTC>(sZ + 16 * tr, 1, LDN, sX2 + 16 * tc0, LF, 1, 16, st, lane);
+        for (int t = 0; t < NCT; ++t) {
+            st[t] = st[t] * *reinterpret_cast<const f32x4 *>(sEG + 16 * t + 4 * lq);
+            tok_prod(sU, D * LC, xh, xl, st[t], t);
+        }
+        __syncthreads();
+        // ---- phase 5: S^T <- S^T + (K o e^{G_n - G})^T Z
+#pragma unroll
+        for (int t = 0; t < NCT; ++t) tok_prod(sW, D * LC, zh, zl, st[t], t);
         __syncthreads();
     }
     if (S_T) {
 #pragma unroll
-        for (int t = 0; t < NTC; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-                S_T[((size_t)uh * D + dv0 + row) * D + col] = st[t][j];
-            }
+        for (int t = 0; t < NCT; ++t)
+            *reinterpret_cast<f32x4 *>(S_T + ((size_t)uh * D + vcol) * D + 16 * t + 4 * lq) = st[t];
     }
 }
 
 template <int D, typename TI, typename TO>
 hipError_t launch_gdn2_t(int units, int T, int H, const int32_t *cu, const void *q,
                          const void *k, const void *v, const float *la, const float *erase,
-                         const float *write, const float *S0, void *o, float *S_T, float *ws,
+                         const float *write, const float *S0, void *o, float *S_T, bf16 *ws,
                          long nslots, hipStream_t st) {
     const int varlen = cu != nullptr;
     const int NC = varlen ? 0 : (T + BC - 1) / BC;
@@ -398,8 +550,10 @@ hipError_t launch_gdn2_t(int units, int T, int H, const int32_t *cu, const void 
         hipLaunchKernelGGL((gdn2_prep_kernel<D, TI>), dim3((unsigned)std::min<size_t>(nch, 256)),
                            dim3(512), 0, st, T, H, units, NC, varlen, cu, (const TI *)q,
                            (const TI *)k, la, erase, ws, (int)nch);
-    hipLaunchKernelGGL((gdn2_fwd_kernel<D, TI, TO>), dim3((unsigned)((long)units * H * (D / 64))),
-                       dim3(512), 0, st, T, H, NC, varlen, cu, (const TI *)v, write, S0, ws,
+    const long nuh = (long)units * H;
+    const int xcd_map = nuh % 8 == 0 ? 1 : 0;
+    hipLaunchKernelGGL((gdn2_fwd_kernel<D, TI, TO>), dim3((unsigned)(nuh * (D / 64))), dim3(512),
+                       0, st, T, H, NC, varlen, xcd_map, cu, (const TI *)v, write, S0, ws,
                        (TO *)o, S_T);
     return hipGetLastError();
 }
@@ -414,7 +568,7 @@ bool gdn2_supported(int dk, int dv, int chunk, bool io_bf16) {
 size_t gdn2_ws_bytes(int units, int T, int H, int d, bool varlen) {
     const long nslots = varlen ? (long)T / BC + units + 1 : (long)units * ((T + BC - 1) / BC);
     const size_t per = d == 128 ? G2Ws<128>::total : G2Ws<64>::total;
-    return sizeof(float) * (size_t)nslots * H * per;
+    return sizeof(bf16) * (size_t)nslots * H * per;
 }
 
 hipError_t launch_gdn2_fwd(int units, int T, int H, int d, bool io_bf16, bool o_bf16,
@@ -422,7 +576,7 @@ hipError_t launch_gdn2_fwd(int units, int T, int H, int d, bool io_bf16, bool o_
                            const float *la, const float *erase, const float *write,
                            const float *S0, void *o, float *S_T, void *ws, hipStream_t st) {
     const long nslots = cu ? (long)T / BC + units + 1 : (long)units * ((T + BC - 1) / BC);
-    float *w = (float *)ws;
+    bf16 *w = (bf16 *)ws;
 #define GDN_G2(DV, TI, TO)                                                                    \
     return launch_gdn2_t<DV, TI, TO>(units, T, H, cu, q, k, v, la, erase, write, S0, o, S_T, w, \
                                      nslots, st)

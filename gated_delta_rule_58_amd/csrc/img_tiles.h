@@ -1,0 +1,67 @@
+// Operand images shared by the channel-wise decay kernels (KDA, GDN-2): a
+// prep launch writes each operand of the sequential launch as a bf16 hi + lo
+// pair (hi = x rounded to bf16, lo = bf16(x - hi): about 16 mantissa bits of
+// x) in exactly the layout the sequential launch keeps in LDS, which copies it
+// with direct global-to-LDS loads and multiplies on the 16x16x32 bf16 MFMA as
+// the three piece products hi*hi + lo*hi + hi*lo.
+#pragma once
+
+#include "gdn_common.h"
+
+namespace gdn {
+namespace img {
+
+// Stored position of column k: within each 32-wide block, lane group g of a
+// 16x16x32 MFMA operand takes k = 4g..4g+3 and 16+4g..16+4g+3 (the k order of
+// two stacked accumulator tiles), kept together at 8g..8g+7.
+__device__ __forceinline__ int dpos(int k) {
+    return (k & ~31) + ((k & 16) >> 2) + 2 * (k & 12) + (k & 3);
+}
+
+// Four consecutive values as hi and lo bf16 (8-byte stores).
+__device__ __forceinline__ void put_pair4(bf16 *hi, bf16 *lo, f32x4 x) {
+    bf16x4 h, l;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        h[j] = (bf16)x[j];
+        l[j] = (bf16)(x[j] - (float)h[j]);
+    }
+    *reinterpret_cast<bf16x4 *>(hi) = h;
+    *reinterpret_cast<bf16x4 *>(lo) = l;
+}
+// Eight values (D-order group: two runs of four) as hi and lo bf16 (16-byte stores).
+__device__ __forceinline__ void put_pair8(bf16 *hi, bf16 *lo, f32x4 x0, f32x4 x1) {
+    bf16x8 h, l;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        h[j] = (bf16)x0[j];
+        l[j] = (bf16)(x0[j] - (float)h[j]);
+        h[4 + j] = (bf16)x1[j];
+        l[4 + j] = (bf16)(x1[j] - (float)h[4 + j]);
+    }
+    *reinterpret_cast<bf16x8 *>(hi) = h;
+    *reinterpret_cast<bf16x8 *>(lo) = l;
+}
+__device__ __forceinline__ void put_pair1(bf16 *hi, bf16 *lo, float x) {
+    const bf16 h = (bf16)x;
+    *hi = h;
+    *lo = (bf16)(x - (float)h);
+}
+
+__device__ __forceinline__ bf16x8 ld8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+// Direct global-to-LDS copy of 16 bytes per lane: lane l's bytes land at
+// dst + 16 l (dst is the wave's base address), so a wave moves 1 KB.
+__device__ __forceinline__ void lds_dma16(void *dst, const void *src) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N): wait until at most N of this wave's vector memory
+// operations are outstanding (they complete in issue order).
+template <int N> __device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+}  // namespace img
+}  // namespace gdn

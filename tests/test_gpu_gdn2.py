@@ -1,8 +1,10 @@
 """Parity of the Gated DeltaNet-2 forward, through the C ABI, with the fp64
 oracle ``oracle.gdn2_fwd`` (pins in tests/test_oracle_gdn2.py).
 
-The GPU computes in fp32 from inputs exact in fp32 (bf16 upcast), so the bar
-is max |gpu - oracle| <= 1e-3 * RMS(oracle) on o and on the final states.
+The GPU computes the chunk factors in fp32 and every product of the
+sequential launch from hi + lo bf16 pairs (about 16 mantissa bits per
+operand, three piece products), so the bar is max |gpu - oracle| <= 1e-3 *
+RMS(oracle) on o and on the final states.
 """
 import os
 
@@ -75,7 +77,10 @@ def test_gdn2_extreme_channels():
 
 def test_gdn2_scalar_gates_match_kda():
     """b_t = w_t = beta_t in every channel: gdn_kda_fwd's rule (both GPU runs
-    against each other; each is checked against its oracle elsewhere)."""
+    against each other; each is checked against its oracle elsewhere).  The
+    two launches factor the chunk differently and form their products from
+    hi + lo bf16 pairs, so they agree to the sum of their own errors (each
+    about 1e-4 of RMS here), held to the parity bar."""
     inp = gi.kda_inputs(1, 200, 2, 128, 128, "bf16", s0_std=0.1, seed=6)
     b = inp["beta"][..., None]
     g2 = dict(inp, erase=b.expand(1, 200, 2, 128).contiguous(),
@@ -87,7 +92,7 @@ def test_gdn2_scalar_gates_match_kda():
     torch.cuda.synchronize()
     e1, e2 = gi.max_rel_err(o2.cpu(), ok.cpu()), gi.max_rel_err(s2.cpu(), sk.cpu())
     say(f"gdn2 vs kda: o {e1:.2e}, S {e2:.2e}")
-    assert e1 <= 1e-4 and e2 <= 1e-4
+    assert e1 <= TAU and e2 <= TAU
 
 
 @pytest.mark.slow
