@@ -155,61 +155,71 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
     }
     // The four channel-weighted products, 16 x 16 blocks (br, bi), bi <= br:
     // matrix mx = 0 A_e (rows K, columns E), 1 A_k (K, K), 2 P_e (Q, E),
-    // 3 P_k (Q, K).  40 tasks, 5 per wave (2 diagonal, 3 below): waves 0-3
-    // the E-column matrices, waves 4-7 the K-column ones.  Each block is one
-    // MFMA product of operands rescaled to the prefix just before block br
-    // (the last token of block br - 1, or 0): every factor is e^{<= 0} below
-    // the diagonal, and on it too unless the block's decay span exceeds 60,
-    // when the block is formed term by term instead.  The wave's five
-    // chains run interleaved, one MFMA of each per channel step.
-    f32x4 res[5];
+    // 3 P_k (Q, K).  Each block is one MFMA product of operands rescaled to
+    // the prefix just before block br (the last token of block br - 1, or 0):
+    // every factor is e^{<= 0} below the diagonal, and on it too unless the
+    // block's decay span exceeds 60, when the block is formed term by term
+    // instead.  The four matrices of one block share both factors, so wave w
+    // forms all four of block w (blocks numbered row by row: (0,0) (1,0)
+    // (1,1) (2,0) ...) -- two exponentials per channel step for four
+    // products -- and one matrix of block 8 or 9, five interleaved chains in
+    // all.
+    f32x4 res[5];   // res[mx]: block w, matrix mx; res[4]: block 8 + w / 4, matrix w % 4
+    auto blk_of = [](int e, int &br, int &bi) {
+        int blk = e, r = 0;
+        while (blk > r) blk -= ++r;
+        br = r;
+        bi = blk;
+    };
+    int bmr, bmi, bxr, bxi;
+    blk_of(wave, bmr, bmi);
+    blk_of(8 + (wave >> 2), bxr, bxi);
+    const int mxx = wave & 3;
     {
-        const int half = wave >> 2, w4 = wave & 3;   // half 0: E columns, 1: K columns
-        int ra[5], rb[5], gro[5], mxs[5];
-        float gon[5];
-        bool terms[5];
+        const int ram = 16 * bmr + li, rbm = 16 * bmi + li, grm = bmr > 0 ? 16 * bmr - 1 : 0;
+        const float gonm = bmr > 0 ? 1.f : 0.f;   // reference prefix 0 for the first block row
+        const int rax = 16 * bxr + li, rbx = 16 * bxi + li, grx = 16 * bxr - 1;
+        const bool termsm = bmi == bmr && diag_span<D>(sG, LF, bmr, lane) > 60.f;
+        const bool termsx = bxi == bxr && diag_span<D>(sG, LF, bxr, lane) > 60.f;
+        const TI *Xx = mxx < 2 ? sK : sQ;   // the extra chain's rows
+        const bool colE = (mxx & 1) == 0;   // and its columns: E (A_e, P_e) or K
 #pragma unroll
-        for (int s = 0; s < 5; ++s) {
-            const int e = w4 + 4 * s;   // 0..19 within the half
-            int blk = e % 10, br = 0;
-            while (blk > br) blk -= ++br;
-            mxs[s] = 2 * (e / 10) + half;
-            ra[s] = 16 * br + li;
-            rb[s] = 16 * blk + li;
-            gro[s] = br > 0 ? 16 * br - 1 : 0;
-            gon[s] = br > 0 ? 1.f : 0.f;   // reference prefix 0 for the first block
-            terms[s] = blk == br && diag_span<D>(sG, LF, br, lane) > 60.f;
-        }
-        auto chains = [&](const auto *Y, int ly) {
-#pragma unroll
-            for (int s = 0; s < 5; ++s) res[s] = zero4();
+        for (int s = 0; s < 5; ++s) res[s] = zero4();
 #pragma unroll 2
-            for (int c0 = 0; c0 < D; c0 += 4) {
-                const int c = c0 + lq;
-#pragma unroll
-                for (int s = 0; s < 5; ++s) {
-                    const float gr = gon[s] * sG[gro[s] * LF + c];
-                    const TI *Xr = mxs[s] < 2 ? sK : sQ;
-                    const float a = to_f32(Xr[ra[s] * LI + c]) * __expf(sG[ra[s] * LF + c] - gr);
-                    const float y = to_f32(Y[rb[s] * ly + c]) * __expf(gr - sG[rb[s] * LF + c]);
-                    res[s] = mfma_f32(a, y, res[s]);
-                }
-            }
-#pragma unroll
-            for (int s = 0; s < 5; ++s)
-                if (terms[s])
-                    res[s] = diag_terms<D>(mxs[s] < 2 ? sK : sQ, LI, Y, ly, sG, LF, (ra[s] - li) / 16, lane);
-        };
-        if (half == 0) chains(static_cast<const float *>(sE), LE);
-        else chains(static_cast<const TI *>(sK), LI);
+        for (int c0 = 0; c0 < D; c0 += 4) {
+            const int c = c0 + lq;
+            const float gr = gonm * sG[grm * LF + c];
+            const float ea = __expf(sG[ram * LF + c] - gr), eb = __expf(gr - sG[rbm * LF + c]);
+            const float ak = to_f32(sK[ram * LI + c]) * ea, aq = to_f32(sQ[ram * LI + c]) * ea;
+            const float be = sE[rbm * LE + c] * eb, bk = to_f32(sK[rbm * LI + c]) * eb;
+            res[0] = mfma_f32(ak, be, res[0]);
+            res[1] = mfma_f32(ak, bk, res[1]);
+            res[2] = mfma_f32(aq, be, res[2]);
+            res[3] = mfma_f32(aq, bk, res[3]);
+            const float gx = sG[grx * LF + c];
+            const float ax = to_f32(Xx[rax * LI + c]) * __expf(sG[rax * LF + c] - gx);
+            const float yv = colE ? sE[rbx * LE + c] : to_f32(sK[rbx * LI + c]);
+            res[4] = mfma_f32(ax, yv * __expf(gx - sG[rbx * LF + c]), res[4]);
+        }
+        if (termsm) {
+            res[0] = diag_terms<D>(sK, LI, sE, LE, sG, LF, bmr, lane);
+            res[1] = diag_terms<D>(sK, LI, sK, LI, sG, LF, bmr, lane);
+            res[2] = diag_terms<D>(sQ, LI, sE, LE, sG, LF, bmr, lane);
+            res[3] = diag_terms<D>(sQ, LI, sK, LI, sG, LF, bmr, lane);
+        }
+        if (termsx)
+            res[4] = colE ? diag_terms<D>(Xx, LI, sE, LE, sG, LF, bxr, lane)
+                          : diag_terms<D>(Xx, LI, sK, LI, sG, LF, bxr, lane);
         // keep strict (A) or inclusive (P) lower entries
 #pragma unroll
-        for (int s = 0; s < 5; ++s)
+        for (int s = 0; s < 5; ++s) {
+            const int mx = s < 4 ? s : mxx, br = s < 4 ? bmr : bxr, bi = s < 4 ? bmi : bxi;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = ra[s] - li + 4 * lq + j, i = rb[s];
-                if (mxs[s] < 2 ? i >= r : i > r) res[s][j] = 0.f;
+                const int r = 16 * br + 4 * lq + j, i = 16 * bi + li;
+                if (mx < 2 ? i >= r : i > r) res[s][j] = 0.f;
             }
+        }
     }
     __syncthreads();   // E consumed: A_e and A_k go over it
     for (int e = tid; e < 2 * BC * LDN; e += 512) sE[e] = 0.f;
@@ -220,12 +230,10 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < 5; ++s) {
-        const int e = (wave & 3) + 4 * s, mx = 2 * (e / 10) + (wave >> 2);
-        int blk = e % 10, br = 0;
-        while (blk > br) blk -= ++br;
+        const int mx = s < 4 ? s : mxx, br = s < 4 ? bmr : bxr, bi = s < 4 ? bmi : bxi;
         float *dst = mx == 0 ? sAe : mx == 1 ? sAk : mx == 2 ? sPe : sPk;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dst[(16 * br + 4 * lq + j) * LDN + 16 * blk + li] = res[s][j];
+        for (int j = 0; j < 4; ++j) dst[(16 * br + 4 * lq + j) * LDN + 16 * bi + li] = res[s][j];
     }
     __syncthreads();
     block_inverse64(sAe, sTe, wave, lane);   // T_e (ends with a barrier)
