@@ -35,7 +35,9 @@
 // sprod products split both fp32 operands so and sum six piece products:
 //   1. prep     (one workgroup per chunk and head): T and P;
 //   2. states   (one per sequence, head and 64-column d_v slice, chunks in
-//               order): the state entering every chunk and Delta;
+//               order): the state entering every chunk and Delta (bf16
+//               inputs: loader waves copy the next chunk into LDS while
+//               consumer waves run the current one);
 //   3. dstates  (same grid, chunks in reverse): dS' of every chunk, dDelta,
 //               and dS0;
 //   4. sprod    (per chunk and head): dO S, -dDelta S, Delta dS', <dS', S>;
@@ -45,11 +47,13 @@
 // fp32 MFMA layout (v_mfma_f32_16x16x4_f32): lane l supplies A[l & 15][l >> 4]
 // and B[l >> 4][l & 15] and holds D[4 (l >> 4) + j][l & 15], j = 0..3.
 #include "fp32_tiles.h"
+#include "img_tiles.h"
 
 namespace gdn {
 namespace {
 
 using namespace tiles;
+using namespace img;
 
 // ---------------------------------------------------------------- 1. prep
 template <int D, typename TI>
@@ -259,137 +263,258 @@ __device__ __forceinline__ void split3(float x, bf16 &h, bf16 &m, bf16 &l) {
     l = (bf16)(r - (float)m);
 }
 
+// Two D tiles (rows 0-15 and 16-31 of a 32-row block) as a D-order operand
+// in three bf16 pieces that add up to it exactly.
+__device__ __forceinline__ void split3_op(f32x4 d0, f32x4 d1, bf16x8 (&p)[3]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        bf16 h, m, l;
+        split3(e < 4 ? d0[e] : d1[e - 4], h, m, l);
+        p[0][e] = h;
+        p[1][e] = m;
+        p[2][e] = l;
+    }
+}
+
+// The six piece products of X Y that reach 2^-16 of the leading one (the
+// three left out are below 2^-23 of it).
+__device__ __forceinline__ f32x4 mfma_x6(const bf16x8 (&x)[3], const bf16x8 (&y)[3], f32x4 acc) {
+    acc = mfma32(x[0], y[0], acc);
+    acc = mfma32(x[0], y[1], acc);
+    acc = mfma32(x[1], y[0], acc);
+    acc = mfma32(x[0], y[2], acc);
+    acc = mfma32(x[1], y[1], acc);
+    acc = mfma32(x[2], y[0], acc);
+    return acc;
+}
+
+// The states launch with bf16 inputs: one workgroup per (sequence, head,
+// 64 columns of d_v), chunks in order, two phases per chunk:
+//   A. store the state entering the chunk; Y = K S^T (S^T in its three
+//      exact pieces against exact bf16 K); Z = diag(beta)(V - diag(e^g) Y);
+//      Delta = T Z over the six piece products of T and Z; store Delta;
+//   B. S <- e^{g_n} S + (diag(e^{g_n - g}) Delta)^T K (exact pieces of
+//      Delta~ against K, read transposed).
+// Waves 0-3 load the next chunk meanwhile: K, the V slice and T by direct
+// global-to-LDS copies into the other of two buffers (K rows XOR-swizzled by
+// 16-byte piece through the copy's source addresses, so fragment reads of
+// 16 rows hit distinct banks), the gates by a scan in wave 0, and in phase B
+// each wave splits the rows of T it copied into T's three exact pieces.
+// Waves 4-7 own 16 columns of d_v each, S^T (d_k x 16, fp32) in
+// accumulator tiles.
 template <int D>
-__global__ __launch_bounds__(512) void bwd_states_x3_kernel(
-    int T, int H, int NC, int varlen, const int32_t *__restrict__ cu,
+__global__ __launch_bounds__(512, 1) void bwd_states_pipe_kernel(
+    int T, int H, int NC, int varlen, int xcd_map, const int32_t *__restrict__ cu,
     const bf16 *__restrict__ k, const bf16 *__restrict__ v, const float *__restrict__ la,
     const float *__restrict__ beta, const float *__restrict__ S0, const float *__restrict__ wsT,
     float *__restrict__ wsH, float *__restrict__ wsDl) {
-    constexpr int LI = D + 8, LT = BC + 8, NTC = D / 32, NSL = D / 64;
-    __shared__ __attribute__((aligned(16))) bf16 sK[BC * LI];        // K rows
-    __shared__ __attribute__((aligned(16))) bf16 sKT[D * LT];        // K^T rows (d_k x tokens)
-    __shared__ __attribute__((aligned(16))) bf16 sS3[3][BC * LI];    // S slice pieces, d_v rows x d_k
-    __shared__ __attribute__((aligned(16))) bf16 sD3[3][BC * LT];    // Delta~^T pieces, d_v rows x tokens
-    __shared__ __attribute__((aligned(16))) bf16 sV[BC * LT];        // V slice
-    __shared__ __attribute__((aligned(16))) float sT[BC * LDN];
-    __shared__ __attribute__((aligned(16))) float sZ[BC * LDN];
-    __shared__ float sg[4][BC];
-    const int uh = blockIdx.x / NSL, dv0 = 64 * (blockIdx.x % NSL);
-    const int u = uh / H, h = uh % H;
+    constexpr int NSL = D / 64, NKS = D / 32, NCT = D / 16;
+    constexpr int LC = BC + 8;                 // row stride of T's pieces
+    constexpr int KP = D / 8;                  // 16-byte pieces per K row
+    constexpr int KROWS = 64 / KP;             // K rows per KB
+    constexpr int NKI = BC / KROWS / 4, NVI = BC / 8 / 4, NTI = BC * BC * 4 / 1024 / 4;
+    static_assert(NKI * KROWS * 4 == BC && NTI * 4 * 1024 == BC * BC * 4, "copy split");
+    __shared__ __attribute__((aligned(16))) bf16 sK[2][BC * D];     // K rows, swizzled
+    __shared__ __attribute__((aligned(16))) bf16 sV[2][BC * 64];    // V slice rows
+    __shared__ __attribute__((aligned(16))) float sTf[2][BC * BC];  // T as copied
+    __shared__ __attribute__((aligned(16))) bf16 sT3[3][BC * LC];   // T's pieces, D-order rows
+    __shared__ __attribute__((aligned(16))) float sg[2][4][BC];     // g, e^g, beta, e^{g_n - g}
+    // element (r, c) of a K buffer: 16-byte piece c / 8 stored at piece (c / 8) ^ (r % KP)
+    auto kidx = [](int r, int c) { return r * D + 8 * ((c >> 3) ^ (r & (KP - 1))) + (c & 7); };
+
+    const int b = blockIdx.x;
+    int uh, sl;
+    if (xcd_map) {
+        uh = (b & 7) + 8 * (b / (8 * NSL));
+        sl = (b >> 3) % NSL;
+    } else {
+        uh = b / NSL;
+        sl = b % NSL;
+    }
+    const int u = uh / H, h = uh % H, dv0 = 64 * sl;
     long start, L;
     unit_span(u, T, varlen, cu, start, L);
     const int N = (int)((L + BC - 1) / BC);
     const int base = unit_base(u, NC, varlen, cu);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15, lq = lane >> 4;
-    const int tr = wave & 3, tc0 = (wave >> 2) * NTC;
-    const int ty = tr, tx0 = 2 * (wave >> 2);
-    f32x4 st[NTC];   // st[t][j] = S[dv0 + 16 tr + 4 lq + j][16 (tc0 + t) + li]
+
+    if (wave < 4) {
+        // ---- loaders
+        auto loader_barrier = [&]() {   // copies are waited for by count beforehand
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // this wave's LDS writes done
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        // rows past the chunk repeat its last token (beta is 0 there)
+        auto copy_chunk = [&](int c, int buf) {
+            const long row0 = start + (long)c * BC;
+            const int n = (int)min((long)BC, L - (long)c * BC);
+            const size_t ch = (size_t)(base + c) * H + h;
 #pragma unroll
-    for (int t = 0; t < NTC; ++t)
+            for (int s = 0; s < NKI; ++s) {
+                const int i = wave + 4 * s, r = KROWS * i + lane / KP, pl = lane % KP;
+                lds_dma16(sK[buf] + 512 * i,
+                          k + ((size_t)(row0 + min(r, n - 1)) * H + h) * D + 8 * (pl ^ (r & (KP - 1))));
+            }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-            st[t][j] = S0 ? S0[((size_t)uh * D + dv0 + row) * D + col] : 0.f;
+            for (int s = 0; s < NVI; ++s) {
+                const int i = wave + 4 * s, r = 8 * i + lane / 8;
+                lds_dma16(sV[buf] + 512 * i,
+                          v + ((size_t)(row0 + min(r, n - 1)) * H + h) * D + dv0 + 8 * (lane % 8));
+            }
+#pragma unroll
+            for (int s = 0; s < NTI; ++s) {
+                const int i = wave + 4 * s;
+                lds_dma16(sTf[buf] + 256 * i, wsT + ch * BC * BC + 256 * i + 4 * lane);
+            }
+        };
+        // T's pieces from the rows this wave copied: KB piece i = wave + 4 s holds
+        // rows 4 i .. 4 i + 3, 32 D-order groups of 8; the wave's 32 NTI groups
+        // are spread over its 64 lanes
+        static_assert(NTI * 32 % 64 == 0, "whole groups per lane");
+        auto split_t = [&](int buf) {
+#pragma unroll
+            for (int hh = 0; hh < NTI * 32 / 64; ++hh) {
+                const int gi = lane + 64 * hh, s = gi / 32, loc = gi % 32;
+                const int r = 4 * (wave + 4 * s) + loc / 8, p = 8 * (loc % 8);
+                const int i0 = (p & ~31) + (p & 31) / 2;
+                const f32x4 x0 = *reinterpret_cast<const f32x4 *>(sTf[buf] + r * BC + i0);
+                const f32x4 x1 = *reinterpret_cast<const f32x4 *>(sTf[buf] + r * BC + i0 + 16);
+                bf16x8 pc[3];
+                split3_op(x0, x1, pc);
+#pragma unroll
+                for (int q = 0; q < 3; ++q) *reinterpret_cast<bf16x8 *>(sT3[q] + r * LC + p) = pc[q];
+            }
+        };
+        auto gates = [&](int c, int buf) {   // wave 0, after its gate loads have landed
+            float x, bt;
+            const long row0 = start + (long)c * BC;
+            const int n = (int)min((long)BC, L - (long)c * BC);
+            gate_fetch(la, beta, row0, n, H, h, lane, x, bt);
+            return f32x4{x, bt, 0.f, 0.f};
+        };
+        if (N > 0) {
+            f32x4 gx = wave == 0 ? gates(0, 0) : zero4();
+            copy_chunk(0, 0);
+            wait_vm<0>();
+            if (wave == 0) gate_scan(sg[0], gx[0], gx[1], lane);
+            split_t(0);
         }
-    Prefetch<D, bf16> pk;
-    Prefetch<64, bf16> pv;
-    Prefetch<BC, float> pt;
-    float gx = 0.f, gb = 0.f;
-    auto fetch = [&](int c) {
-        const long row0 = start + (long)c * BC;
-        const int n = (int)min((long)BC, L - (long)c * BC);
-        const size_t ch = (size_t)(base + c) * H + h;
-        pk.fetch(k + ((size_t)row0 * H + h) * D, (size_t)H * D, n, tid);
-        pv.fetch(v + ((size_t)row0 * H + h) * D + dv0, (size_t)H * D, n, tid);
-        pt.fetch(wsT + ch * BC * BC, BC, BC, tid);
-        if (wave == 0) gate_fetch(la, beta, row0, n, H, h, lane, gx, gb);
-    };
-    if (N > 0) fetch(0);
+        loader_barrier();
+        for (int c = 0; c < N; ++c) {
+            const int nb = (c + 1) & 1;
+            if (c + 1 < N) {   // phase A: the next chunk's copies and gates
+                f32x4 gx = zero4();
+                if (wave == 0) gx = gates(c + 1, nb);
+                copy_chunk(c + 1, nb);
+                if (wave == 0) {
+                    wait_vm<NKI + NVI + NTI>();
+                    gate_scan(sg[nb], gx[0], gx[1], lane);
+                }
+            }
+            loader_barrier();
+            if (c + 1 < N) {   // phase B: T's pieces of the next chunk
+                wait_vm<0>();
+                split_t(nb);
+            }
+            loader_barrier();
+        }
+        return;
+    }
+
+    // ---- consumers: d_v columns dv0 + 16 cw + li
+    const int cw = wave - 4;
+    const int vcol = dv0 + 16 * cw + li;
+    f32x4 st[NCT];   // st[t][j] = S^T[16 t + 4 lq + j][vcol] = S[vcol][16 t + 4 lq + j]
+#pragma unroll
+    for (int t = 0; t < NCT; ++t)
+        st[t] = S0 ? *reinterpret_cast<const f32x4 *>(S0 + ((size_t)uh * D + vcol) * D + 16 * t + 4 * lq)
+                   : zero4();
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     for (int c = 0; c < N; ++c) {
+        const int cb = c & 1;
         const size_t ch = (size_t)(base + c) * H + h;
         const int n = (int)min((long)BC, L - (long)c * BC);
-        float *Hm = wsH + ch * D * D;
-        // the state entering chunk c: to the workspace, and as pieces to LDS
-#pragma unroll
-        for (int t = 0; t < NTC; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-                Hm[(size_t)(dv0 + row) * D + col] = st[t][j];
-                bf16 a, b, e;
-                split3(st[t][j], a, b, e);
-                sS3[0][row * LI + col] = a;
-                sS3[1][row * LI + col] = b;
-                sS3[2][row * LI + col] = e;
-            }
-        pk.commit(sK, LI, tid);
-#pragma unroll
-        for (int i = 0; i < Prefetch<D, bf16>::NP; ++i) {   // and transposed
-            const int e = tid + 512 * i, r = e / (D / 8), c8 = (e % (D / 8)) * 8;
-            if (e < BC * D / 8)
-#pragma unroll
-                for (int m = 0; m < 8; ++m) sKT[(c8 + m) * LT + r] = pk.buf[i][m];
-        }
-        pv.commit(sV, LT, tid);
-        pt.commit(sT, LDN, tid);
-        if (wave == 0) gate_scan(sg, gx, gb, lane);
-        __syncthreads();
-        if (c + 1 < N) fetch(c + 1);   // next chunk's operands load during this one
-        // Z = diag(beta) (V - diag(e^g) K S^T), 64 tokens x 64 slice columns
+        const bf16 *K = sK[cb];
+        const float(*g)[BC] = sg[cb];
+        // ---- phase A
+        bf16x8 dp[2][3];   // Delta~ = diag(e^{g_n - g}) Delta: exact pieces, D-order over tokens
         {
-            f32x4 y[2];
-            zero_n(y);
+            float *Hm = wsH + ch * D * D + (size_t)vcol * D;
 #pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sK + (16 * ty + li) * LI + 32 * ks + 8 * lq);
+            for (int t = 0; t < NCT; ++t) *reinterpret_cast<f32x4 *>(Hm + 16 * t + 4 * lq) = st[t];
+            f32x4 y[4];
 #pragma unroll
-                for (int x = 0; x < 2; ++x)
+            for (int rt = 0; rt < 4; ++rt) y[rt] = zero4();
 #pragma unroll
-                    for (int p = 0; p < 3; ++p)
-                        y[x] = mfma32(a, *reinterpret_cast<const bf16x8 *>(
-                                             sS3[p] + (16 * (tx0 + x) + li) * LI + 32 * ks + 8 * lq), y[x]);
+            for (int ks = 0; ks < NKS; ++ks) {
+                bf16x8 sp[3];
+                split3_op(st[2 * ks], st[2 * ks + 1], sp);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    const int r = 16 * rt + li;
+                    const bf16x8 a = cat(*reinterpret_cast<const bf16x4 *>(K + kidx(r, 32 * ks + 4 * lq)),
+                                         *reinterpret_cast<const bf16x4 *>(K + kidx(r, 32 * ks + 16 + 4 * lq)));
+#pragma unroll
+                    for (int q = 0; q < 3; ++q) y[rt] = mfma32(a, sp[q], y[rt]);
+                }
             }
-            for (int x = 0; x < 2; ++x)
+            f32x4 z[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const bf16x4 vx = lds_read_tr(sV[cb] + (16 * rt + 4 * lq + (li >> 2)) * 64 + 16 * cw + 4 * (li & 3));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * ty + 4 * lq + j, col = 16 * (tx0 + x) + li;
-                    sZ[r * LDN + col] = sg[2][r] * ((float)sV[r * LT + col] - sg[1][r] * y[x][j]);
+                    const int r = 16 * rt + 4 * lq + j;
+                    z[rt][j] = g[2][r] * ((float)vx[j] - g[1][r] * y[rt][j]);
                 }
-        }
-        __syncthreads();
-        // Delta = T Z (fp32); the state update uses diag(e^{g_n - g}) Delta
-        {
-            f32x4 d[2];
-            zero_n(d);
-            mmn<BC, 2>(sT + 16 * ty * LDN, LDN, 1, sZ + 16 * tx0, LDN, 1, 16, d, lane);
-            for (int x = 0; x < 2; ++x)
+            }
+            bf16x8 zp[2][3];
+            split3_op(z[0], z[1], zp[0]);
+            split3_op(z[2], z[3], zp[1]);
+            f32x4 dd[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int off = (16 * rt + li) * LC + 32 * ks + 8 * lq;
+                    const bf16x8 tp[3] = {ld8(sT3[0] + off), ld8(sT3[1] + off), ld8(sT3[2] + off)};
+                    acc = mfma_x6(tp, zp[ks], acc);
+                }
+                dd[rt] = acc;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * ty + 4 * lq + j, col = 16 * (tx0 + x) + li;
-                    if (r < n) wsDl[(ch * BC + r) * D + dv0 + col] = d[x][j];
-                    bf16 a, b, e;
-                    split3(d[x][j] * sg[3][r], a, b, e);
-                    sD3[0][col * LT + r] = a;
-                    sD3[1][col * LT + r] = b;
-                    sD3[2][col * LT + r] = e;
+                    const int r = 16 * rt + 4 * lq + j;
+                    if (r < n) wsDl[(ch * BC + r) * D + vcol] = acc[j];
+                    dd[rt][j] = acc[j] * g[3][r];
                 }
+            }
+            split3_op(dd[0], dd[1], dp[0]);
+            split3_op(dd[2], dd[3], dp[1]);
         }
         __syncthreads();
-        // S <- e^{g_n} S + (diag(e^{g_n - g}) Delta)^T K
-        const float egn = sg[1][BC - 1];
+        // ---- phase B: S^T <- e^{g_n} S^T + K^T Delta~
+        {
+            const float egn = g[1][BC - 1];
 #pragma unroll
-        for (int t = 0; t < NTC; ++t) st[t] = st[t] * egn;
+            for (int t = 0; t < NCT; ++t) {
+                f32x4 acc = st[t] * egn;
 #pragma unroll
-        for (int ks = 0; ks < BC / 32; ++ks)
+                for (int ks = 0; ks < 2; ++ks) {
+                    // K^T rows 16 t + li, tokens 32 ks + 4 lq + j (+ 16): column gathers
+                    const int r = 32 * ks + 4 * lq + (li >> 2), cc = 16 * t + 4 * (li & 3);
+                    const bf16x8 a = cat(lds_read_tr(K + kidx(r, cc)), lds_read_tr(K + kidx(r + 16, cc)));
 #pragma unroll
-            for (int p = 0; p < 3; ++p) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sD3[p] + (16 * tr + li) * LT + 32 * ks + 8 * lq);
-#pragma unroll
-                for (int t = 0; t < NTC; ++t)
-                    st[t] = mfma32(a, *reinterpret_cast<const bf16x8 *>(
-                                          sKT + (16 * (tc0 + t) + li) * LT + 32 * ks + 8 * lq), st[t]);
+                    for (int q = 0; q < 3; ++q) acc = mfma32(a, dp[ks][q], acc);
+                }
+                st[t] = acc;
             }
+        }
         __syncthreads();
     }
 }
@@ -525,9 +650,9 @@ __global__ __launch_bounds__(512) void bwd_dstates_kernel(
 }
 
 // The same launch for bf16 inputs: K dS'^T, F^T K and (e^g dO)^T Q on bf16
-// MFMA over three exact bf16 pieces of their fp32 operand (as in
-// bwd_states_x3_kernel; Q reaches the last one by column gathers, transpose
-// reads of its rows); P^T dO and T^T dDelta stay fp32.  dDelta goes over the
+// MFMA over three exact bf16 pieces of their fp32 operand (split3; Q reaches
+// the last one by column gathers, transpose reads of its rows); P^T dO and
+// T^T dDelta stay fp32.  dDelta goes over the
 // K rows once those are consumed, and the pieces of F over those of dS'.
 template <int D, typename TG>
 __global__ __launch_bounds__(512) void bwd_dstates_x3_kernel(
@@ -1415,6 +1540,7 @@ hipError_t launch_bwd_t(int units, int T, int H, const int32_t *cu, const void *
     const TI *qi = (const TI *)q, *ki = (const TI *)k, *vi = (const TI *)v;
     const TG *dOg = (const TG *)dO;
     const unsigned seq_grid = (unsigned)((long)units * H * (D / 64));
+    const int xcd_map = ((long)units * H) % 8 == 0 ? 1 : 0;   // d_v slices of a head on one XCD
     if (nch > 0)
         // persistent: two workgroups per CU (70 KB of LDS each)
         hipLaunchKernelGGL((bwd_prep_kernel<D, TI>), dim3((unsigned)std::min<size_t>(nch, 512)),
@@ -1422,8 +1548,8 @@ hipError_t launch_bwd_t(int units, int T, int H, const int32_t *cu, const void *
                            wsP, (int)nch);
     if (nch > 0) {
         if constexpr (sizeof(TI) == 2)
-            hipLaunchKernelGGL((bwd_states_x3_kernel<D>), dim3(seq_grid), dim3(512), 0, st, T, H,
-                               NC, varlen, cu, ki, vi, la, beta, S0, wsT, wsH, wsDl);
+            hipLaunchKernelGGL((bwd_states_pipe_kernel<D>), dim3(seq_grid), dim3(512), 0, st, T,
+                               H, NC, varlen, xcd_map, cu, ki, vi, la, beta, S0, wsT, wsH, wsDl);
         else
             hipLaunchKernelGGL((bwd_states_kernel<D, TI>), dim3(seq_grid), dim3(512), 0, st, T, H,
                                NC, varlen, cu, ki, vi, la, beta, S0, wsT, wsH, wsDl);
