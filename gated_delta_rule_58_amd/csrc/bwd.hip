@@ -39,7 +39,7 @@
 //               inputs: loader waves copy the next chunk into LDS while
 //               consumer waves run the current one);
 //   3. dstates  (same grid, chunks in reverse): dS' of every chunk, dDelta,
-//               and dS0;
+//               and dS0 (bf16 inputs: split by role like states);
 //   4. sprod    (per chunk and head): dO S, -dDelta S, Delta dS', <dS', S>;
 //   5. grads    (per chunk and head): dq, dk, dv, dlog_alpha, dbeta.
 // Intermediates go through the caller's workspace (layout in bwd_ws_bytes).
@@ -649,193 +649,317 @@ __global__ __launch_bounds__(512) void bwd_dstates_kernel(
     }
 }
 
-// The same launch for bf16 inputs: K dS'^T, F^T K and (e^g dO)^T Q on bf16
-// MFMA over three exact bf16 pieces of their fp32 operand (split3; Q reaches
-// the last one by column gathers, transpose reads of its rows); P^T dO and
-// T^T dDelta stay fp32.  dDelta goes over the
-// K rows once those are consumed, and the pieces of F over those of dS'.
+// The dstates launch with bf16 inputs, split by role like the states launch:
+// one workgroup per (sequence, head, 64 columns of d_v), chunks in reverse,
+// three phases per chunk c:
+//   1. store dS' (the gradient of the state leaving chunk c); dDelta =
+//      P^T dO + diag(e^{g_n - g}) K dS'^T (exact pieces of dS' against
+//      exact K; the six piece products of P^T and dO); store dDelta;
+//      F = diag(beta e^g) T^T dDelta (six piece products);
+//   2. dS <- e^{g_n} dS' - F^T K   (exact pieces of F against K^T);
+//   3. dS <- dS + (e^g dO)^T Q     (exact pieces against Q^T).
+// Waves 0-3 load chunk c - 1 meanwhile: K (double-buffered) and the gates
+// in phase 1, Q of chunk c itself in phase 1 (Q is read in phase 3 only),
+// dO, P and T in phase 2 (each wave waits for its own copies before the
+// barrier), and in phase 3, when every copy is visible, P^T and T^T in their
+// three exact pieces.  K and Q rows are XOR-swizzled by 16-byte piece
+// through the copies' source addresses.  Waves 4-7 own 16 columns of d_v
+// each, dS^T (d_k x 16, fp32) in accumulator tiles.
 template <int D, typename TG>
-__global__ __launch_bounds__(512) void bwd_dstates_x3_kernel(
-    int T, int H, int NC, int varlen, const int32_t *__restrict__ cu,
+__global__ __launch_bounds__(512, 1) void bwd_dstates_pipe_kernel(
+    int T, int H, int NC, int varlen, int xcd_map, const int32_t *__restrict__ cu,
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const TG *__restrict__ dO,
     const float *__restrict__ la, const float *__restrict__ beta, const float *__restrict__ dST,
     const float *__restrict__ wsT, const float *__restrict__ wsP, float *__restrict__ wsDH,
     float *__restrict__ wsE, float *__restrict__ dS0) {
-    constexpr int LI = D + 8, LT = BC + 8, NTC = D / 32, NSL = D / 64;
-    constexpr int NKE = BC * LI > 2 * BC * LDN ? BC * LI : 2 * BC * LDN;   // bf16 elements
-    static_assert(LI >= LT, "a piece of F^T fits a piece of dS'");
-    __shared__ __attribute__((aligned(16))) bf16 sKE[NKE];
-    __shared__ __attribute__((aligned(16))) bf16 sKT[D * LT];        // K^T rows (d_k x tokens)
-    __shared__ __attribute__((aligned(16))) bf16 sQ[BC * LI];        // Q rows
-    __shared__ __attribute__((aligned(16))) bf16 sG3[3][BC * LI];    // dS' slice pieces, then F^T pieces
-    __shared__ __attribute__((aligned(16))) float sP[BC * LDN];
-    __shared__ __attribute__((aligned(16))) float sT[BC * LDN];
-    __shared__ __attribute__((aligned(16))) float sO[BC * LDN];      // dO slice, then e^g dO
-    __shared__ float sg[4][BC];
-    bf16 *const sK = sKE;                                // K rows, then
-    float *const sE = reinterpret_cast<float *>(sKE);    // dDelta
-    const int uh = blockIdx.x / NSL, dv0 = 64 * (blockIdx.x % NSL);
-    const int u = uh / H, h = uh % H;
+    constexpr int NSL = D / 64, NKS = D / 32, NCT = D / 16;
+    constexpr int LC = BC + 8;                 // row stride of the pieces of P^T and T^T
+    constexpr int KP = D / 8;                  // 16-byte pieces per K or Q row
+    constexpr int KROWS = 64 / KP;             // K or Q rows per KB
+    constexpr int NKI = BC / KROWS / 4;        // KB copies per loader wave: K, Q
+    constexpr int OROWS = 1024 / (64 * (int)sizeof(TG));   // dO rows per KB
+    constexpr int NOI = BC / OROWS / 4, NPI = BC * BC * 4 / 1024 / 4;
+    static_assert(NKI * KROWS * 4 == BC && NOI * OROWS * 4 == BC && NPI * 4096 == BC * BC * 4,
+                  "copy split");
+    __shared__ __attribute__((aligned(16))) bf16 sK[2][BC * D];     // K rows, swizzled
+    __shared__ __attribute__((aligned(16))) bf16 sQ[BC * D];        // Q rows, swizzled
+    __shared__ __attribute__((aligned(16))) TG sO[BC * 64];         // dO slice rows
+    __shared__ __attribute__((aligned(16))) float sPf[BC * BC];     // P as copied
+    __shared__ __attribute__((aligned(16))) float sTf[BC * BC];     // T as copied
+    __shared__ __attribute__((aligned(16))) bf16 sPT[3][BC * LC];   // P^T pieces, D-order rows
+    __shared__ __attribute__((aligned(16))) bf16 sTT[3][BC * LC];   // T^T pieces, D-order rows
+    __shared__ __attribute__((aligned(16))) float sg[2][4][BC];     // g, e^g, beta, e^{g_n - g}
+    auto kidx = [](int r, int c) { return r * D + 8 * ((c >> 3) ^ (r & (KP - 1))) + (c & 7); };
+
+    const int b = blockIdx.x;
+    int uh, sl;
+    if (xcd_map) {
+        uh = (b & 7) + 8 * (b / (8 * NSL));
+        sl = (b >> 3) % NSL;
+    } else {
+        uh = b / NSL;
+        sl = b % NSL;
+    }
+    const int u = uh / H, h = uh % H, dv0 = 64 * sl;
     long start, L;
     unit_span(u, T, varlen, cu, start, L);
     const int N = (int)((L + BC - 1) / BC);
     const int base = unit_base(u, NC, varlen, cu);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15, lq = lane >> 4;
-    const int tr = wave & 3, tc0 = (wave >> 2) * NTC;
-    const int ty = tr, tx0 = 2 * (wave >> 2);
-    f32x4 st[NTC];   // st[t][j] = dS'[dv0 + 16 tr + 4 lq + j][16 (tc0 + t) + li]
-#pragma unroll
-    for (int t = 0; t < NTC; ++t)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-            st[t][j] = dST ? dST[((size_t)uh * D + dv0 + row) * D + col] : 0.f;
-        }
-    Prefetch<D, bf16> pk, pq;
-    Prefetch<64, TG> po;
-    Prefetch<BC, float> pp, pt;
-    float gx = 0.f, gb = 0.f;
-    auto fetch = [&](int c) {
-        const long row0 = start + (long)c * BC;
-        const int n = (int)min((long)BC, L - (long)c * BC);
-        const size_t ch = (size_t)(base + c) * H + h;
-        pk.fetch(k + ((size_t)row0 * H + h) * D, (size_t)H * D, n, tid);
-        pq.fetch(q + ((size_t)row0 * H + h) * D, (size_t)H * D, n, tid);
-        po.fetch(dO + ((size_t)row0 * H + h) * D + dv0, (size_t)H * D, n, tid);
-        pp.fetch(wsP + ch * BC * BC, BC, BC, tid);
-        pt.fetch(wsT + ch * BC * BC, BC, BC, tid);
-        if (wave == 0) gate_fetch(la, beta, row0, n, H, h, lane, gx, gb);
+    auto rows_of = [&](int c, long &row0, int &n) {
+        row0 = start + (long)c * BC;
+        n = (int)min((long)BC, L - (long)c * BC);
     };
-    if (N > 0) fetch(N - 1);
-    for (int c = N - 1; c >= 0; --c) {
-        const size_t ch = (size_t)(base + c) * H + h;
-        const int n = (int)min((long)BC, L - (long)c * BC);
-        float *DHm = wsDH + ch * D * D;
-        // gradient of the state leaving chunk c: to the workspace, and as pieces
+
+    if (wave < 4) {
+        // ---- loaders
+        auto loader_barrier = [&]() {   // copies are waited for by count beforehand
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // this wave's LDS writes done
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        // rows past the chunk repeat its last token; the consumers zero what
+        // those rows would add
+        auto copy_rows = [&](bf16 *dst, const bf16 *src, int c) {   // K or Q, swizzled
+            long row0;
+            int n;
+            rows_of(c, row0, n);
 #pragma unroll
-        for (int t = 0; t < NTC; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-                DHm[(size_t)(dv0 + row) * D + col] = st[t][j];
-                bf16 a, b, e;
-                split3(st[t][j], a, b, e);
-                sG3[0][row * LI + col] = a;
-                sG3[1][row * LI + col] = b;
-                sG3[2][row * LI + col] = e;
+            for (int s = 0; s < NKI; ++s) {
+                const int i = wave + 4 * s, r = KROWS * i + lane / KP, pl = lane % KP;
+                lds_dma16(dst + 512 * i,
+                          src + ((size_t)(row0 + min(r, n - 1)) * H + h) * D + 8 * (pl ^ (r & (KP - 1))));
             }
-        pk.commit(sK, LI, tid);
+        };
+        auto copy_o = [&](int c) {   // dO slice
+            long row0;
+            int n;
+            rows_of(c, row0, n);
+            constexpr int OP = 64 / OROWS;   // 16-byte pieces per dO row
 #pragma unroll
-        for (int i = 0; i < Prefetch<D, bf16>::NP; ++i) {   // and transposed
-            const int e = tid + 512 * i, r = e / (D / 8), c8 = (e % (D / 8)) * 8;
-            if (e < BC * D / 8)
-#pragma unroll
-                for (int m = 0; m < 8; ++m) sKT[(c8 + m) * LT + r] = pk.buf[i][m];
-        }
-        pq.commit(sQ, LI, tid);
-        po.commit(sO, LDN, tid);
-        pp.commit(sP, LDN, tid);
-        pt.commit(sT, LDN, tid);
-        if (wave == 0) gate_scan(sg, gx, gb, lane);
-        __syncthreads();
-        if (c > 0) fetch(c - 1);   // previous chunk's operands load during this one
-        // dDelta = P^T dO + diag(e^{g_n - g}) K dS'^T
-        f32x4 e1[2], e2[2];
-        zero_n(e1);
-        zero_n(e2);
-        mmn<BC, 2>(sP + 16 * ty, 1, LDN, sO + 16 * tx0, LDN, 1, 16, e1, lane);
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sK + (16 * ty + li) * LI + 32 * ks + 8 * lq);
-#pragma unroll
-            for (int x = 0; x < 2; ++x)
-#pragma unroll
-                for (int p = 0; p < 3; ++p)
-                    e2[x] = mfma32(a, *reinterpret_cast<const bf16x8 *>(
-                                          sG3[p] + (16 * (tx0 + x) + li) * LI + 32 * ks + 8 * lq), e2[x]);
-        }
-        __syncthreads();   // K rows consumed: dDelta goes over them
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * ty + 4 * lq + j, col = 16 * (tx0 + x) + li;
-                const float e = e1[x][j] + sg[3][r] * e2[x][j];
-                sE[r * LDN + col] = e;
-                if (r < n) wsE[(ch * BC + r) * D + dv0 + col] = e;
+            for (int s = 0; s < NOI; ++s) {
+                const int i = wave + 4 * s, r = OROWS * i + lane / OP;
+                lds_dma16(sO + 1024 / sizeof(TG) * i,
+                          dO + ((size_t)(row0 + min(r, n - 1)) * H + h) * D + dv0 +
+                              (16 / sizeof(TG)) * (lane % OP));
             }
-        __syncthreads();
-        // F = diag(beta e^g) T^T dDelta, as pieces of F^T over those of dS';
-        // dO rows scaled by e^g
-        {
-            f32x4 f[2];
-            zero_n(f);
-            mmn<BC, 2>(sT + 16 * ty, 1, LDN, sE + 16 * tx0, LDN, 1, 16, f, lane);
-            for (int x = 0; x < 2; ++x)
+        };
+        auto copy_pt = [&](int c) {   // P and T
+            const size_t ch = (size_t)(base + c) * H + h;
+#pragma unroll
+            for (int s = 0; s < NPI; ++s) {
+                const int i = wave + 4 * s;
+                lds_dma16(sPf + 256 * i, wsP + ch * BC * BC + 256 * i + 4 * lane);
+                lds_dma16(sTf + 256 * i, wsT + ch * BC * BC + 256 * i + 4 * lane);
+            }
+        };
+        // P^T and T^T pieces: row r, D-order group p of columns i0..i0+3,
+        // i0+16..i0+19 holds X[i][r] (any wave: every copy is visible)
+        auto split_pt = [&]() {
+#pragma unroll
+            for (int s = 0; s < 2 * BC * 8 / 256; ++s) {
+                // consecutive lanes take consecutive rows r: the column reads
+                // below are then consecutive words
+                const int e = (tid & 255) + 256 * s, mx = e / (BC * 8), loc = e % (BC * 8);
+                const int r = loc % BC, p = 8 * (loc / BC), i0 = (p & ~31) + (p & 31) / 2;
+                const float *X = mx == 0 ? sPf : sTf;
+                f32x4 x0, x1;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * ty + 4 * lq + j, col = 16 * (tx0 + x) + li;
-                    bf16 a, b, e;
-                    split3(sg[2][r] * sg[1][r] * f[x][j], a, b, e);
-                    sG3[0][col * LT + r] = a;
-                    sG3[1][col * LT + r] = b;
-                    sG3[2][col * LT + r] = e;
-                    sO[r * LDN + col] *= sg[1][r];
+                    x0[j] = X[(i0 + j) * BC + r];
+                    x1[j] = X[(i0 + 16 + j) * BC + r];
                 }
+                bf16x8 pc[3];
+                split3_op(x0, x1, pc);
+#pragma unroll
+                for (int qq = 0; qq < 3; ++qq)
+                    *reinterpret_cast<bf16x8 *>((mx == 0 ? sPT[qq] : sTT[qq]) + r * LC + p) = pc[qq];
+            }
+        };
+        // wave 0: the gate loads are issued before the copies and waited for
+        // (by the compiler, by count) at the scan
+        auto gate_load = [&](int c, float &x, float &bt) {
+            long row0;
+            int n;
+            rows_of(c, row0, n);
+            gate_fetch(la, beta, row0, n, H, h, lane, x, bt);
+        };
+        if (N > 0) {
+            float x = 0.f, bt = 0.f;
+            if (wave == 0) gate_load(N - 1, x, bt);
+            copy_rows(sK[(N - 1) & 1], k, N - 1);
+            copy_pt(N - 1);
+            copy_o(N - 1);
+            wait_vm<0>();
+            if (wave == 0) gate_scan(sg[(N - 1) & 1], x, bt, lane);
+        }
+        loader_barrier();
+        if (N > 0) split_pt();
+        loader_barrier();
+        // Copies in issue order per chunk c: K(c-1) Q(c) P,T(c-1) in phase 1,
+        // dO(c-1) in phase 2.  Phase 3 needs Q(c) and P,T(c-1) (the split);
+        // phase 1 of chunk c-1 needs K(c-1) and dO(c-1).
+        for (int c = N - 1; c >= 0; --c) {
+            // phase 1
+            float x = 0.f, bt = 0.f;
+            if (c > 0 && wave == 0) gate_load(c - 1, x, bt);
+            if (c > 0) copy_rows(sK[(c - 1) & 1], k, c - 1);
+            copy_rows(sQ, q, c);
+            if (c > 0) {
+                copy_pt(c - 1);
+                if (wave == 0) gate_scan(sg[(c - 1) & 1], x, bt, lane);
+            }
+            loader_barrier();
+            // phase 2
+            if (c > 0) {
+                copy_o(c - 1);
+                wait_vm<NOI>();   // Q(c), P and T of chunk c - 1
+            } else {
+                wait_vm<0>();
+            }
+            loader_barrier();
+            // phase 3: the pieces of P^T and T^T of chunk c - 1
+            if (c > 0) split_pt();
+            wait_vm<0>();         // dO of chunk c - 1
+            loader_barrier();
+        }
+        return;
+    }
+
+    // ---- consumers: d_v columns dv0 + 16 cw + li
+    const int cw = wave - 4;
+    const int vcol = dv0 + 16 * cw + li;
+    f32x4 ut[NCT];   // ut[t][j] = dS^T[16 t + 4 lq + j][vcol] = dS[vcol][16 t + 4 lq + j]
+#pragma unroll
+    for (int t = 0; t < NCT; ++t)
+        ut[t] = dST ? *reinterpret_cast<const f32x4 *>(dST + ((size_t)uh * D + vcol) * D + 16 * t + 4 * lq)
+                    : zero4();
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    __syncthreads();
+    for (int c = N - 1; c >= 0; --c) {
+        const int cb = c & 1;
+        const size_t ch = (size_t)(base + c) * H + h;
+        long row0;
+        int n;
+        rows_of(c, row0, n);
+        const bf16 *K = sK[cb];
+        const float(*g)[BC] = sg[cb];
+        bf16x8 fp[2][3], ep[2][3];   // pieces of F and of e^g dO, D-order over tokens
+        // ---- phase 1
+        {
+            float *DHm = wsDH + ch * D * D + (size_t)vcol * D;
+#pragma unroll
+            for (int t = 0; t < NCT; ++t) *reinterpret_cast<f32x4 *>(DHm + 16 * t + 4 * lq) = ut[t];
+            f32x4 e2[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) e2[rt] = zero4();
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                bf16x8 up[3];
+                split3_op(ut[2 * ks], ut[2 * ks + 1], up);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    const int r = 16 * rt + li;
+                    const bf16x8 a = cat(*reinterpret_cast<const bf16x4 *>(K + kidx(r, 32 * ks + 4 * lq)),
+                                         *reinterpret_cast<const bf16x4 *>(K + kidx(r, 32 * ks + 16 + 4 * lq)));
+#pragma unroll
+                    for (int qq = 0; qq < 3; ++qq) e2[rt] = mfma32(a, up[qq], e2[rt]);
+                }
+            }
+            // dO at tokens 32 ks + 4 lq + j (+ 16) of this column, zero past the chunk
+            bf16x8 op[2][3];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                f32x4 o0, o1, s0, s1;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r0 = 32 * ks + 4 * lq + j, r1 = r0 + 16;
+                    o0[j] = r0 < n ? to_f32(sO[r0 * 64 + 16 * cw + li]) : 0.f;
+                    o1[j] = r1 < n ? to_f32(sO[r1 * 64 + 16 * cw + li]) : 0.f;
+                    s0[j] = o0[j] * g[1][r0];
+                    s1[j] = o1[j] * g[1][r1];
+                }
+                split3_op(o0, o1, op[ks]);
+                split3_op(s0, s1, ep[ks]);
+            }
+            f32x4 dd[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int off = (16 * rt + li) * LC + 32 * ks + 8 * lq;
+                    const bf16x8 xp[3] = {ld8(sPT[0] + off), ld8(sPT[1] + off), ld8(sPT[2] + off)};
+                    acc = mfma_x6(xp, op[ks], acc);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * rt + 4 * lq + j;
+                    dd[rt][j] = acc[j] + g[3][r] * e2[rt][j];
+                    if (r < n) wsE[(ch * BC + r) * D + vcol] = dd[rt][j];
+                }
+            }
+            bf16x8 dp[2][3];
+            split3_op(dd[0], dd[1], dp[0]);
+            split3_op(dd[2], dd[3], dp[1]);
+            f32x4 f[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int off = (16 * rt + li) * LC + 32 * ks + 8 * lq;
+                    const bf16x8 xp[3] = {ld8(sTT[0] + off), ld8(sTT[1] + off), ld8(sTT[2] + off)};
+                    acc = mfma_x6(xp, dp[ks], acc);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * rt + 4 * lq + j;
+                    f[rt][j] = g[2][r] * g[1][r] * acc[j];
+                }
+            }
+            split3_op(f[0], f[1], fp[0]);
+            split3_op(f[2], f[3], fp[1]);
         }
         __syncthreads();
-        // dS <- e^{g_n} dS' + (e^g dO)^T Q - F^T K
-        const float egn = sg[1][BC - 1];
-        f32x4 fk[NTC];
+        // ---- phase 2: dS^T <- e^{g_n} dS'^T - K^T F
+        {
+            const float egn = g[1][BC - 1];
 #pragma unroll
-        for (int t = 0; t < NTC; ++t) st[t] = st[t] * egn;
-        zero_n(fk);
-        // (e^g dO)^T Q: rows 16 tr + li of (e^g dO)^T are columns of sO, taken
-        // in the k order of the transpose reads of Q (tokens 4 lq + j, then
-        // 16 + 4 lq + j, of each 32-token step)
+            for (int t = 0; t < NCT; ++t) {
+                f32x4 acc = zero4();
 #pragma unroll
-        for (int ks = 0; ks < BC / 32; ++ks) {
-            bf16x8 ao[3];
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int r = 32 * ks + 4 * lq + (li >> 2), cc = 16 * t + 4 * (li & 3);
+                    const bf16x8 a = cat(lds_read_tr(K + kidx(r, cc)), lds_read_tr(K + kidx(r + 16, cc)));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int tok = 32 * ks + 4 * lq + (e & 3) + (e < 4 ? 0 : 16);
-                bf16 x0, x1, x2;
-                split3(sO[tok * LDN + 16 * tr + li], x0, x1, x2);
-                ao[0][e] = x0;
-                ao[1][e] = x1;
-                ao[2][e] = x2;
-            }
-            const int tq = 32 * ks + 4 * lq + (li >> 2);
-#pragma unroll
-            for (int t = 0; t < NTC; ++t) {
-                const bf16 *pq = sQ + tq * LI + 16 * (tc0 + t) + 4 * (li & 3);
-                const bf16x8 bq = cat(lds_read_tr(pq), lds_read_tr(pq + 16 * LI));
-#pragma unroll
-                for (int pc = 0; pc < 3; ++pc) st[t] = mfma32(ao[pc], bq, st[t]);
+                    for (int qq = 0; qq < 3; ++qq) acc = mfma32(a, fp[ks][qq], acc);
+                }
+                ut[t] = ut[t] * egn - acc;
             }
         }
+        __syncthreads();
+        // ---- phase 3: dS^T <- dS^T + Q^T (e^g dO)
 #pragma unroll
-        for (int ks = 0; ks < BC / 32; ++ks)
+        for (int t = 0; t < NCT; ++t) {
 #pragma unroll
-            for (int p = 0; p < 3; ++p) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sG3[p] + (16 * tr + li) * LT + 32 * ks + 8 * lq);
+            for (int ks = 0; ks < 2; ++ks) {
+                const int r = 32 * ks + 4 * lq + (li >> 2), cc = 16 * t + 4 * (li & 3);
+                const bf16x8 a = cat(lds_read_tr(sQ + kidx(r, cc)), lds_read_tr(sQ + kidx(r + 16, cc)));
 #pragma unroll
-                for (int t = 0; t < NTC; ++t)
-                    fk[t] = mfma32(a, *reinterpret_cast<const bf16x8 *>(
-                                          sKT + (16 * (tc0 + t) + li) * LT + 32 * ks + 8 * lq), fk[t]);
+                for (int qq = 0; qq < 3; ++qq) ut[t] = mfma32(a, ep[ks][qq], ut[t]);
             }
-#pragma unroll
-        for (int t = 0; t < NTC; ++t) st[t] = st[t] - fk[t];
+        }
         __syncthreads();
     }
     if (dS0) {
 #pragma unroll
-        for (int t = 0; t < NTC; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 16 * tr + 4 * lq + j, col = 16 * (tc0 + t) + li;
-                dS0[((size_t)uh * D + dv0 + row) * D + col] = st[t][j];
-            }
+        for (int t = 0; t < NCT; ++t)
+            *reinterpret_cast<f32x4 *>(dS0 + ((size_t)uh * D + vcol) * D + 16 * t + 4 * lq) = ut[t];
     }
 }
 
@@ -1555,8 +1679,9 @@ hipError_t launch_bwd_t(int units, int T, int H, const int32_t *cu, const void *
                                NC, varlen, cu, ki, vi, la, beta, S0, wsT, wsH, wsDl);
     }
     if constexpr (sizeof(TI) == 2)
-        hipLaunchKernelGGL((bwd_dstates_x3_kernel<D, TG>), dim3(seq_grid), dim3(512), 0, st, T,
-                           H, NC, varlen, cu, qi, ki, dOg, la, beta, dST, wsT, wsP, wsDH, wsE, dS0);
+        hipLaunchKernelGGL((bwd_dstates_pipe_kernel<D, TG>), dim3(seq_grid), dim3(512), 0, st,
+                           T, H, NC, varlen, xcd_map, cu, qi, ki, dOg, la, beta, dST, wsT, wsP,
+                           wsDH, wsE, dS0);
     else
         hipLaunchKernelGGL((bwd_dstates_kernel<D, TI, TG>), dim3(seq_grid), dim3(512), 0, st, T,
                            H, NC, varlen, cu, qi, ki, dOg, la, beta, dST, wsT, wsP, wsDH, wsE, dS0);
