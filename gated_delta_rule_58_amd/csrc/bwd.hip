@@ -651,18 +651,18 @@ __global__ __launch_bounds__(512) void bwd_dstates_kernel(
 
 // The dstates launch with bf16 inputs, split by role like the states launch:
 // one workgroup per (sequence, head, 64 columns of d_v), chunks in reverse,
-// three phases per chunk c:
+// two phases per chunk c:
 //   1. store dS' (the gradient of the state leaving chunk c); dDelta =
 //      P^T dO + diag(e^{g_n - g}) K dS'^T (exact pieces of dS' against
 //      exact K; the six piece products of P^T and dO); store dDelta;
 //      F = diag(beta e^g) T^T dDelta (six piece products);
-//   2. dS <- e^{g_n} dS' - F^T K   (exact pieces of F against K^T);
-//   3. dS <- dS + (e^g dO)^T Q     (exact pieces against Q^T).
-// Waves 0-3 load chunk c - 1 meanwhile: K (double-buffered) and the gates
-// in phase 1, Q of chunk c itself in phase 1 (Q is read in phase 3 only),
-// dO, P and T in phase 2 (each wave waits for its own copies before the
-// barrier), and in phase 3, when every copy is visible, P^T and T^T in their
-// three exact pieces.  K and Q rows are XOR-swizzled by 16-byte piece
+//   2. dS <- e^{g_n} dS' - F^T K + (e^g dO)^T Q   (exact pieces of F and of
+//      e^g dO against K^T and Q^T).
+// Waves 0-3 load meanwhile: in phase 1 Q of chunk c (read in phase 2 only)
+// and K (double-buffered), the gates, P and T of chunk c - 1, each wave
+// waiting for its own copies before the barrier; in phase 2, when every copy
+// is visible, P^T and T^T of chunk c - 1 in their three exact pieces, and dO
+// of chunk c - 1.  K and Q rows are XOR-swizzled by 16-byte piece
 // through the copies' source addresses.  Waves 4-7 own 16 columns of d_v
 // each, dS^T (d_k x 16, fp32) in accumulator tiles.
 template <int D, typename TG>
@@ -799,31 +799,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dstates_pipe_kernel(
         loader_barrier();
         if (N > 0) split_pt();
         loader_barrier();
-        // Copies in issue order per chunk c: K(c-1) Q(c) P,T(c-1) in phase 1,
-        // dO(c-1) in phase 2.  Phase 3 needs Q(c) and P,T(c-1) (the split);
-        // phase 1 of chunk c-1 needs K(c-1) and dO(c-1).
         for (int c = N - 1; c >= 0; --c) {
             // phase 1
             float x = 0.f, bt = 0.f;
             if (c > 0 && wave == 0) gate_load(c - 1, x, bt);
-            if (c > 0) copy_rows(sK[(c - 1) & 1], k, c - 1);
             copy_rows(sQ, q, c);
             if (c > 0) {
+                copy_rows(sK[(c - 1) & 1], k, c - 1);
                 copy_pt(c - 1);
                 if (wave == 0) gate_scan(sg[(c - 1) & 1], x, bt, lane);
             }
+            wait_vm<0>();   // Q(c), and K, P, T of chunk c - 1
             loader_barrier();
-            // phase 2
+            // phase 2: the pieces of P^T and T^T of chunk c - 1, and its dO
             if (c > 0) {
+                split_pt();
                 copy_o(c - 1);
-                wait_vm<NOI>();   // Q(c), P and T of chunk c - 1
-            } else {
-                wait_vm<0>();
             }
-            loader_barrier();
-            // phase 3: the pieces of P^T and T^T of chunk c - 1
-            if (c > 0) split_pt();
-            wait_vm<0>();         // dO of chunk c - 1
+            wait_vm<0>();
             loader_barrier();
         }
         return;
@@ -846,7 +839,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dstates_pipe_kernel(
         long row0;
         int n;
         rows_of(c, row0, n);
-        const bf16 *K = sK[cb];
+        const bf16 *K = sK[cb];   // Q (single buffer) is read in phase 2 only
         const float(*g)[BC] = sg[cb];
         bf16x8 fp[2][3], ep[2][3];   // pieces of F and of e^g dO, D-order over tokens
         // ---- phase 1
@@ -926,32 +919,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dstates_pipe_kernel(
             split3_op(f[2], f[3], fp[1]);
         }
         __syncthreads();
-        // ---- phase 2: dS^T <- e^{g_n} dS'^T - K^T F
+        // ---- phase 2: dS^T <- e^{g_n} dS'^T - K^T F + Q^T (e^g dO)
         {
             const float egn = g[1][BC - 1];
 #pragma unroll
             for (int t = 0; t < NCT; ++t) {
-                f32x4 acc = zero4();
+                f32x4 kf = zero4(), qe = ut[t] * egn;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     const int r = 32 * ks + 4 * lq + (li >> 2), cc = 16 * t + 4 * (li & 3);
                     const bf16x8 a = cat(lds_read_tr(K + kidx(r, cc)), lds_read_tr(K + kidx(r + 16, cc)));
+                    const bf16x8 aq = cat(lds_read_tr(sQ + kidx(r, cc)), lds_read_tr(sQ + kidx(r + 16, cc)));
 #pragma unroll
-                    for (int qq = 0; qq < 3; ++qq) acc = mfma32(a, fp[ks][qq], acc);
+                    for (int qq = 0; qq < 3; ++qq) {
+                        kf = mfma32(a, fp[ks][qq], kf);
+                        qe = mfma32(aq, ep[ks][qq], qe);
+                    }
                 }
-                ut[t] = ut[t] * egn - acc;
-            }
-        }
-        __syncthreads();
-        // ---- phase 3: dS^T <- dS^T + Q^T (e^g dO)
-#pragma unroll
-        for (int t = 0; t < NCT; ++t) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int r = 32 * ks + 4 * lq + (li >> 2), cc = 16 * t + 4 * (li & 3);
-                const bf16x8 a = cat(lds_read_tr(sQ + kidx(r, cc)), lds_read_tr(sQ + kidx(r + 16, cc)));
-#pragma unroll
-                for (int qq = 0; qq < 3; ++qq) ut[t] = mfma32(a, ep[ks][qq], ut[t]);
+                ut[t] = qe - kf;
             }
         }
         __syncthreads();
