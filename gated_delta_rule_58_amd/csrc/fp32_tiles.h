@@ -237,27 +237,63 @@ __device__ __forceinline__ void load_nn(float *dst, const float *src, int tid, i
         put4(dst + (e >> 4) * LDN + (e & 15) * 4, *reinterpret_cast<const f32x4 *>(src + 4 * e));
 }
 
+// Lane S of each group of four lanes, to all four (DPP quad permutation).
+template <int S> __device__ __forceinline__ float quad_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), S * 0x55, 0xf, 0xf, false));
+}
+
 // T = (I + A)^{-1} for a strictly lower 64 x 64 A in LDS (row stride LDN)
 // into X (zeroed by the caller; row stride LDN), by all 512 threads of the
 // workgroup (it contains workgroup barriers): the four 16 x 16 diagonal
-// blocks by forward substitution (wave b inverts block b: column j on 4
-// lanes, lane part p sums i = p mod 4; the lanes of a column are in one
-// wave, whose LDS accesses complete in order, and the wave barrier keeps the
-// compiler from moving them), then the blocks below the diagonal level by
-// level, T_ij = -T_ii sum_{j <= k < i} A_ik T_kj, on MFMA.
+// blocks by forward substitution in registers (wave b inverts block b), then
+// the blocks below the diagonal level by level,
+// T_ij = -T_ii sum_{j <= k < i} A_ik T_kj, on MFMA.
+//
+// Diagonal block: lane (column cl = lane / 4, row group q = lane % 4) holds
+// rows 4q..4q+3 of column cl of the block's inverse.  The four row groups are
+// solved in order: group s solves its 4 x 4 unit lower system, its rows are
+// broadcast to the other lanes of the quad (same column) by DPP, and the
+// later groups subtract their rows' share of them.
 __device__ __forceinline__ void block_inverse64(const float *sA, float *sX, int wave, int lane) {
     if (wave < 4) {
-        const int b = wave, j = lane >> 2, p = lane & 3;
+        const int b = wave, cl = lane >> 2, q = lane & 3;
         const float *Ab = sA + 16 * b * LDN + 16 * b;
-        float *Xb = sX + 16 * b * LDN + 16 * b;
-        for (int r = 0; r < 16; ++r) {
-            float sum = 0.f;
-            for (int i = p; i < r; i += 4) sum += Ab[r * LDN + i] * Xb[i * LDN + j];
-            sum += __shfl_xor(sum, 1);
-            sum += __shfl_xor(sum, 2);
-            if (p == 0) Xb[r * LDN + j] = r == j ? 1.f : -sum;
-            __builtin_amdgcn_wave_barrier();
+        f32x4 x;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) x[rr] = (4 * q + rr == cl) ? 1.f : 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            f32x4 acol[4];   // acol[k][rr] = A_bb[4 q + rr][4 s + k]
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const f32x4 row = *reinterpret_cast<const f32x4 *>(Ab + (4 * q + rr) * LDN + 4 * s);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) acol[k][rr] = row[k];
+            }
+            f32x4 t = x;   // group s: rows 4 s .. 4 s + 3, unit lower 4 x 4 solve
+#pragma unroll
+            for (int c = 0; c < 3; ++c)
+#pragma unroll
+                for (int rr = c + 1; rr < 4; ++rr) t[rr] -= acol[c][rr] * t[c];
+            const bool mine = q == s, later = q > s;   // lane-varying: selects, not branches
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) x[rr] = mine ? t[rr] : x[rr];
+            if (s < 3) {
+                f32x4 xb;   // the solved rows 4 s .. 4 s + 3 of this column
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    xb[k] = s == 0 ? quad_bcast<0>(x[k]) : s == 1 ? quad_bcast<1>(x[k]) : quad_bcast<2>(x[k]);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const float y = x[rr] - ((acol[0][rr] * xb[0] + acol[1][rr] * xb[1]) +
+                                             (acol[2][rr] * xb[2] + acol[3][rr] * xb[3]));
+                    x[rr] = later ? y : x[rr];
+                }
+            }
         }
+        float *Xb = sX + 16 * b * LDN + 16 * b;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) Xb[(4 * q + rr) * LDN + cl] = x[rr];
     }
     __syncthreads();
 #pragma unroll
