@@ -232,6 +232,36 @@ __device__ __forceinline__ void gate_scan(float (*sg)[BC], float x, float b, int
     sg[3][lane] = expf(gn - x);
 }
 
+// In-place prefix over the BC rows of each of the D columns of an fp32 LDS
+// tile (row stride ld), by all 512 threads (every lane must call it): column
+// c = tid / SEG is cut into SEG = 512 / D segments of rows, lane tid % SEG
+// sums its segment in registers, and the segment totals are combined across
+// the SEG lanes of the column by shuffles.  Each thread rewrites only the
+// elements it read.  Returns the column's total (the prefix at the last row)
+// in every lane of the column's group.
+template <int D> __device__ __forceinline__ float column_prefix(float *s, int ld, int tid) {
+    constexpr int SEG = 512 / D, RS = BC / SEG;
+    static_assert(SEG * D == 512 && RS * SEG == BC, "512 threads cover the tile");
+    const int c = tid / SEG, sg = tid % SEG;
+    float *col = s + sg * RS * ld + c;
+    float v[RS];
+#pragma unroll
+    for (int j = 0; j < RS; ++j) v[j] = col[j * ld];
+#pragma unroll
+    for (int j = 1; j < RS; ++j) v[j] += v[j - 1];
+    float incl = v[RS - 1];   // inclusive scan of the segment totals
+#pragma unroll
+    for (int o = 1; o < SEG; o <<= 1) {
+        const float y = __shfl_up(incl, o, SEG);
+        if (sg >= o) incl += y;
+    }
+    float off = __shfl_up(incl, 1, SEG);
+    off = sg > 0 ? off : 0.f;
+#pragma unroll
+    for (int j = 0; j < RS; ++j) col[j * ld] = v[j] + off;
+    return __shfl(incl, SEG - 1, SEG);
+}
+
 __device__ __forceinline__ void load_nn(float *dst, const float *src, int tid, int nthr) {
     for (int e = tid; e < BC * BC / 4; e += nthr)
         put4(dst + (e >> 4) * LDN + (e & 15) * 4, *reinterpret_cast<const f32x4 *>(src + 4 * e));
@@ -401,16 +431,20 @@ __device__ __forceinline__ f32x4 diag_block(const TX *X, int lx, const TY *Y, in
                                             const float *G, int lg, int b, int lane) {
     const int li = lane & 15, lq = lane >> 4;
     if (diag_span<D>(G, lg, b, lane) > 60.f) return diag_terms<D>(X, lx, Y, ly, G, lg, b, lane);
-    const float *gref = b > 0 ? G + (16 * b - 1) * lg : nullptr;
+    const float gon = b > 0 ? 1.f : 0.f;   // reference prefix 0 for the first block
+    const float *gref = G + (b > 0 ? 16 * b - 1 : 0) * lg;
     f32x4 acc = zero4();
     const int rw = 16 * b + li;
-#pragma unroll 4
-    for (int c0 = 0; c0 < D; c0 += 4) {
-        const int c = c0 + lq;
-        const float gr = gref ? gref[c] : 0.f, gw = G[rw * lg + c];
-        const float a = to_f32(X[rw * lx + c]) * __expf(gw - gr);
-        const float y = to_f32(Y[rw * ly + c]) * __expf(gr - gw);
-        acc = mfma_f32(a, y, acc);
+    // step j of channel group c0: lane (li, lq) supplies channel c0 + 4 lq + j
+#pragma unroll 2
+    for (int c0 = 0; c0 < D; c0 += 16) {
+        const int cb = c0 + 4 * lq;
+        const f32x4 gr = *reinterpret_cast<const f32x4 *>(gref + cb) * gon;
+        const f32x4 gw = *reinterpret_cast<const f32x4 *>(G + rw * lg + cb);
+        const f32x4 xa = ld4f(X + rw * lx + cb), ya = ld4f(Y + rw * ly + cb);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc = mfma_f32(xa[j] * __expf(gw[j] - gr[j]), ya[j] * __expf(gr[j] - gw[j]), acc);
     }
     return acc;
 }

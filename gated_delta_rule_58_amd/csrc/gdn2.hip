@@ -107,14 +107,9 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
     pe.commit(sE, LE, tid);
     for (int e = tid; e < BC * LDN; e += 512) sTe[e] = 0.f;
     __syncthreads();
-    const int cn = next(ci + gridDim.x);
-    if (tid < D) {   // prefix over the chunk per channel (padded rows add 0)
-        float g = 0.f;
-        for (int r = 0; r < BC; ++r) {
-            g += sG[r * LF + tid];
-            sG[r * LF + tid] = g;
-        }
-        wEG[tid] = expf(g);
+    {   // prefix over the chunk per channel (padded rows add 0)
+        const float gn = column_prefix<D>(sG, LF, tid);
+        if (tid % (512 / D) == 0) wEG[tid / (512 / D)] = expf(gn);
     }
     for (int e = tid; e < BC * D / 4; e += 512) {   // E = b o k
         const int r = e / (D / 4), c = (e % (D / 4)) * 4;
@@ -164,6 +159,7 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
     // (1,1) (2,0) ...) -- two exponentials per channel step for four
     // products -- and one matrix of block 8 or 9, five interleaved chains in
     // all.
+    int cn;
     f32x4 res[5];   // res[mx]: block w, matrix mx; res[4]: block 8 + w / 4, matrix w % 4
     auto blk_of = [](int e, int &br, int &bi) {
         int blk = e, r = 0;
@@ -185,21 +181,34 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
         const bool colE = (mxx & 1) == 0;   // and its columns: E (A_e, P_e) or K
 #pragma unroll
         for (int s = 0; s < 5; ++s) res[s] = zero4();
+        // Step j of channel group c0 gives lane (li, lq) the k slot of
+        // channel c0 + 4 lq + j (both operands alike), so a lane reads its
+        // four channels of a row with one 16-byte (fp32) or 8-byte (bf16) read.
 #pragma unroll 2
-        for (int c0 = 0; c0 < D; c0 += 4) {
-            const int c = c0 + lq;
-            const float gr = gonm * sG[grm * LF + c];
-            const float ea = __expf(sG[ram * LF + c] - gr), eb = __expf(gr - sG[rbm * LF + c]);
-            const float ak = to_f32(sK[ram * LI + c]) * ea, aq = to_f32(sQ[ram * LI + c]) * ea;
-            const float be = sE[rbm * LE + c] * eb, bk = to_f32(sK[rbm * LI + c]) * eb;
-            res[0] = mfma_f32(ak, be, res[0]);
-            res[1] = mfma_f32(ak, bk, res[1]);
-            res[2] = mfma_f32(aq, be, res[2]);
-            res[3] = mfma_f32(aq, bk, res[3]);
-            const float gx = sG[grx * LF + c];
-            const float ax = to_f32(Xx[rax * LI + c]) * __expf(sG[rax * LF + c] - gx);
-            const float yv = colE ? sE[rbx * LE + c] : to_f32(sK[rbx * LI + c]);
-            res[4] = mfma_f32(ax, yv * __expf(gx - sG[rbx * LF + c]), res[4]);
+        for (int c0 = 0; c0 < D; c0 += 16) {
+            const int cb = c0 + 4 * lq;
+            const f32x4 gr4 = *reinterpret_cast<const f32x4 *>(sG + grm * LF + cb) * gonm;
+            const f32x4 ga = *reinterpret_cast<const f32x4 *>(sG + ram * LF + cb);
+            const f32x4 gb = *reinterpret_cast<const f32x4 *>(sG + rbm * LF + cb);
+            const f32x4 ka = ld4f(sK + ram * LI + cb), qa = ld4f(sQ + ram * LI + cb);
+            const f32x4 eb4 = *reinterpret_cast<const f32x4 *>(sE + rbm * LE + cb);
+            const f32x4 kb = ld4f(sK + rbm * LI + cb);
+            const f32x4 gx4 = *reinterpret_cast<const f32x4 *>(sG + grx * LF + cb);
+            const f32x4 xa = ld4f(Xx + rax * LI + cb);
+            const f32x4 gxa = *reinterpret_cast<const f32x4 *>(sG + rax * LF + cb);
+            const f32x4 yb =
+                colE ? *reinterpret_cast<const f32x4 *>(sE + rbx * LE + cb) : ld4f(sK + rbx * LI + cb);
+            const f32x4 gxb = *reinterpret_cast<const f32x4 *>(sG + rbx * LF + cb);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float ea = __expf(ga[j] - gr4[j]), eb = __expf(gr4[j] - gb[j]);
+                const float ak = ka[j] * ea, aq = qa[j] * ea, be = eb4[j] * eb, bk = kb[j] * eb;
+                res[0] = mfma_f32(ak, be, res[0]);
+                res[1] = mfma_f32(ak, bk, res[1]);
+                res[2] = mfma_f32(aq, be, res[2]);
+                res[3] = mfma_f32(aq, bk, res[3]);
+                res[4] = mfma_f32(xa[j] * __expf(gxa[j] - gx4[j]), yb[j] * __expf(gx4[j] - gxb[j]), res[4]);
+            }
         }
         if (termsm) {
             res[0] = diag_terms<D>(sK, LI, sE, LE, sG, LF, bmr, lane);
@@ -210,6 +219,10 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
         if (termsx)
             res[4] = colE ? diag_terms<D>(Xx, LI, sE, LE, sG, LF, bxr, lane)
                           : diag_terms<D>(Xx, LI, sK, LI, sG, LF, bxr, lane);
+        // the next pair's inputs: issued here, where the waves of the
+        // lighter block products would wait at the barrier anyway, rather
+        // than all at once at the top of the pair
+        cn = next(ci + gridDim.x);
         // keep strict (A) or inclusive (P) lower entries
 #pragma unroll
         for (int s = 0; s < 5; ++s) {
@@ -226,6 +239,13 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
     for (int e = tid; e < BC * LDN; e += 512) {
         sPe[e] = 0.f;
         sPk[e] = 0.f;
+    }
+    for (int e = tid; e < BC * D / 4; e += 512) {   // G -> e^G: only F1 and Qh read it from here on
+        f32x4 *pg = reinterpret_cast<f32x4 *>(sG + (e / (D / 4)) * LF + (e % (D / 4)) * 4);
+        f32x4 x = *pg;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = __expf(x[j]);
+        *pg = x;
     }
     __syncthreads();
 #pragma unroll
@@ -286,7 +306,7 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
 #pragma unroll
             for (int t = 0; t < NTC; ++t) {
                 const int c = 16 * (tc0 + t) + li;
-                const float b = to_f32(sK[kr * LI + c]) * __expf(sG[kr * LF + c]);
+                const float b = to_f32(sK[kr * LI + c]) * sG[kr * LF + c];
                 f1[t] = mfma_f32(b, a1, f1[t]);
                 qh[t] = mfma_f32(b, a2, qh[t]);
             }
@@ -294,11 +314,11 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
 #pragma unroll
         for (int t = 0; t < NTC; ++t) {
             const int r = 16 * tr + li, c = 16 * (tc0 + t) + 4 * lq;   // columns c..c+3
-            const f32x4 g = *reinterpret_cast<const f32x4 *>(sG + r * LF + c);
+            const f32x4 g = *reinterpret_cast<const f32x4 *>(sG + r * LF + c);   // e^G
             const f32x4 qv = ld4f(sQ + r * LI + c);
             f32x4 qg;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) qg[j] = qv[j] * __expf(g[j]) - qh[t][j];
+            for (int j = 0; j < 4; ++j) qg[j] = qv[j] * g[j] - qh[t][j];
             const int off = r * WS::LK + dpos(c);
             put_pair4(W + WS::F1 + off, W + WS::F1 + BC * WS::LK + off, f1[t]);
             put_pair4(W + WS::QH + off, W + WS::QH + BC * WS::LK + off, qg);

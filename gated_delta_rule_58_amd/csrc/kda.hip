@@ -207,16 +207,23 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
         f32x4 acc = zero4();
         const float *gref = sG + (16 * br - 1) * LF;
         const int ra = 16 * br + li, rb = 16 * bi + li;
-#pragma unroll 4
-        for (int c0 = 0; c0 < D; c0 += 4) {
-            const int c = c0 + lq;
-            const float gr = gref[c];
-            const float a = to_f32(X[ra * LI + c]) * __expf(sG[ra * LF + c] - gr);
-            const float bb = to_f32(sK[rb * LI + c]) * __expf(gr - sG[rb * LF + c]);
-            // A: lane holds rows 16 br + 4 lq + j of column 16 bi + li; P is
-            // formed transposed, so a lane holds row 16 br + li, columns
-            // 16 bi + 4 lq + j (four consecutive stored positions)
-            acc = isP ? mfma_f32(bb, a, acc) : mfma_f32(a, bb, acc);
+        // step j of channel group c0: lane (li, lq) supplies channel
+        // c0 + 4 lq + j, so it reads its four channels with one vector read.
+        // A: lane holds rows 16 br + 4 lq + j of column 16 bi + li; P is
+        // formed transposed, so a lane holds row 16 br + li, columns
+        // 16 bi + 4 lq + j (four consecutive stored positions)
+#pragma unroll 2
+        for (int c0 = 0; c0 < D; c0 += 16) {
+            const int cb = c0 + 4 * lq;
+            const f32x4 gr = *reinterpret_cast<const f32x4 *>(gref + cb);
+            const f32x4 ga = *reinterpret_cast<const f32x4 *>(sG + ra * LF + cb);
+            const f32x4 gb = *reinterpret_cast<const f32x4 *>(sG + rb * LF + cb);
+            const f32x4 xa = ld4f(X + ra * LI + cb), kb = ld4f(sK + rb * LI + cb);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float a = xa[j] * __expf(ga[j] - gr[j]), bb = kb[j] * __expf(gr[j] - gb[j]);
+                acc = isP ? mfma_f32(bb, a, acc) : mfma_f32(a, bb, acc);
+            }
         }
         if (isP) {
             if constexpr (kStageP) {
