@@ -94,7 +94,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(
     const size_t ch = ci;
     pk.commit(sK, LI, tid);
     pq.commit(sQ, LI, tid);
-    for (int e = tid; e < BC * LDN; e += 512) sX[e] = 0.f;
+    zero_upper(sX, tid);   // the inverse writes the rest of T
     if (wave == 0) gate_scan(sg, gx, gb, lane);
     __syncthreads();
     const int cn = next(ci + (int)gridDim.x);

@@ -232,6 +232,17 @@ __device__ __forceinline__ void gate_scan(float (*sg)[BC], float x, float b, int
     sg[3][lane] = expf(gn - x);
 }
 
+// Zero the six 16 x 16 blocks above the diagonal of a 64 x 64 fp32 LDS
+// matrix (row stride LDN), one 16-byte store per item: the rest of such a
+// matrix is written whole (its diagonal blocks masked) before it is read.
+__device__ __forceinline__ void zero_upper(float *m, int tid) {
+    for (int e = tid; e < 6 * 64; e += 512) {
+        const int blk = e >> 6, w = e & 63;   // blocks (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+        const int rb = blk < 3 ? 0 : blk < 5 ? 1 : 2, cb = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
+        *reinterpret_cast<f32x4 *>(m + (16 * rb + (w >> 2)) * LDN + 16 * cb + 4 * (w & 3)) = zero4();
+    }
+}
+
 // In-place prefix over the BC rows of each of the D columns of an fp32 LDS
 // tile (row stride ld), by all 512 threads (every lane must call it): column
 // c = tid / SEG is cut into SEG = 512 / D segments of rows, lane tid % SEG
@@ -272,9 +283,11 @@ template <int S> __device__ __forceinline__ float quad_bcast(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), S * 0x55, 0xf, 0xf, false));
 }
 
-// T = (I + A)^{-1} for a strictly lower 64 x 64 A in LDS (row stride LDN)
-// into X (zeroed by the caller; row stride LDN), by all 512 threads of the
-// workgroup (it contains workgroup barriers): the four 16 x 16 diagonal
+// T = (I + A)^{-1} for a strictly lower 64 x 64 A in LDS (row stride LDN;
+// only its diagonal and lower blocks are read) into X (row stride LDN; the
+// diagonal and lower blocks are written whole, the caller zeroes the blocks
+// above), by all 512 threads of the workgroup (it contains workgroup
+// barriers): the four 16 x 16 diagonal
 // blocks by forward substitution in registers (wave b inverts block b), then
 // the blocks below the diagonal level by level,
 // T_ij = -T_ii sum_{j <= k < i} A_ik T_kj, on MFMA.

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
     pq.commit(sQ, LI, tid);
     pg.commit(sG, LF, tid);
     pe.commit(sE, LE, tid);
-    for (int e = tid; e < BC * LDN; e += 512) sTe[e] = 0.f;
+    zero_upper(sTe, tid);   // the inverse writes the rest of T_e
     __syncthreads();
     {   // prefix over the chunk per channel (padded rows add 0)
         const float gn = column_prefix<D>(sG, LF, tid);
@@ -235,11 +235,10 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
         }
     }
     __syncthreads();   // E consumed: A_e and A_k go over it
-    for (int e = tid; e < 2 * BC * LDN; e += 512) sE[e] = 0.f;
-    for (int e = tid; e < BC * LDN; e += 512) {
-        sPe[e] = 0.f;
-        sPk[e] = 0.f;
-    }
+    // blocks above the diagonal of A_k, P_e, P_k (A_e's are never read)
+    zero_upper(sAk, tid);
+    zero_upper(sPe, tid);
+    zero_upper(sPk, tid);
     for (int e = tid; e < BC * D / 4; e += 512) {   // G -> e^G: only F1 and Qh read it from here on
         f32x4 *pg = reinterpret_cast<f32x4 *>(sG + (e / (D / 4)) * LF + (e % (D / 4)) * 4);
         f32x4 x = *pg;

@@ -238,11 +238,10 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
         }
     }
     __syncthreads();   // G, K, Q consumed: A goes over G, T over Q
-    for (int e = tid; e < BC * LDN; e += 512) {
-        sA[e] = 0.f;
-        sX[e] = 0.f;
-        if constexpr (kStageP) sP[e] = 0.f;
-    }
+    // blocks above the diagonal of T and P (A's are never read; the rest of
+    // each is written whole below)
+    zero_upper(sX, tid);
+    if constexpr (kStageP) zero_upper(sP, tid);
     __syncthreads();
     if constexpr (kStageP) {
         if (wave >= 4) {
