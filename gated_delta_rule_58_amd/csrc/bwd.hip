@@ -1137,8 +1137,7 @@ __global__ __launch_bounds__(512, 2) void bwd_sprod_kernel(
     for (int t = 0; t < NTC; ++t)   // Delta dS', lane-blocked as dO S
         *reinterpret_cast<f32x4 *>(wsKt + ch * BC * D + 4 * (tid * NTC + t)) = a[t];
     dot = sum16(dot);
-    dot += __shfl_xor(dot, 16);
-    dot += __shfl_xor(dot, 32);
+    dot = sum_rows(dot);
     if (lane == 0) sred[wave] = dot;
     __syncthreads();
     if (tid == 0) {
@@ -1339,8 +1338,7 @@ __global__ __launch_bounds__(512, 4) void bwd_grads_kernel(
             if (li == 0) ADDG(r, rs);
             col += m;
         }
-        col += __shfl_xor(col, 16);
-        col += __shfl_xor(col, 32);
+        col = sum_rows(col);
         if (lq == 0) ADDG(16 * tx + li, -col);
     }
     typename RowVec<TI, WI>::type fb[2][D / (4 * WI)];
@@ -1370,8 +1368,7 @@ __global__ __launch_bounds__(512, 4) void bwd_grads_kernel(
         float cs = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) cs += sT[(16 * ty + 4 * lq + j) * LDN + 16 * (tx0 + x) + li] * w[x][j];
-        cs += __shfl_xor(cs, 16);
-        cs += __shfl_xor(cs, 32);
+        cs = sum_rows(cs);
         return cs;   // for column r = 16 (tx0 + x) + li, in every lane group
     };
     // dbeta += rows(T^T dDelta . V) = column sums of T o (dDelta V^T)
@@ -1487,8 +1484,7 @@ __global__ __launch_bounds__(512, 4) void bwd_grads_kernel(
             }
             col += m;
         }
-        col += __shfl_xor(col, 16);
-        col += __shfl_xor(col, 32);
+        col = sum_rows(col);
         if (lq == 0) ADDG(16 * tx + li, -col);
     }
     // this lane's elements of dO S and Delta dS' (stored lane-blocked by the
@@ -1594,8 +1590,7 @@ __global__ __launch_bounds__(512, 4) void bwd_grads_kernel(
                 dqc[r * HD + col] = cvt<TG>(an[t][j]);
             }
         }
-    ssum += __shfl_xor(ssum, 16);
-    ssum += __shfl_xor(ssum, 32);
+    ssum = sum_rows(ssum);
     if (lane == 0 && n > 0) ADDG(n - 1, ssum);
 #undef ADDG
 #undef ADDB

@@ -44,12 +44,29 @@ template <int NT> __device__ __forceinline__ void zero_n(f32x4 (&acc)[NT]) {
     for (int t = 0; t < NT; ++t) acc[t] = zero4();
 }
 
-__device__ __forceinline__ float sum16(float x) {   // over the 16 lanes of a row group
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    x += __shfl_xor(x, 8);
+// Lane data moved by DPP (all lanes active): quad permutations and row mirrors.
+template <int CTRL> __device__ __forceinline__ float dppf(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// Sum over the 16 lanes of a row group, in every lane: the partner of each
+// step is lane ^ 1, lane ^ 2 (quad permutations), the other quad of the
+// half-row, the other half-row (mirrors) -- the same pairs of partial sums as
+// a butterfly over lane ^ 1, ^ 2, ^ 4, ^ 8, without a trip through LDS.
+__device__ __forceinline__ float sum16(float x) {
+    x += dppf<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+    x += dppf<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+    x += dppf<0x141>(x);   // row_half_mirror
+    x += dppf<0x140>(x);   // row_mirror
     return x;
+}
+// x + x[lane ^ 16], then the same with lane ^ 32: a sum over the four row
+// groups, in every lane (gfx950 permlane swaps; each sum adds the same two
+// values in every lane, as the butterfly does).
+__device__ __forceinline__ float sum_rows(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <typename X> __device__ __forceinline__ X cvt(float x);

@@ -40,11 +40,17 @@ __device__ __forceinline__ f32x4 load4(const float *p) {
     return *reinterpret_cast<const f32x4 *>(p);
 }
 
+// Sum over the 16 lanes of a row group, in every lane, by DPP (all lanes
+// active): partners lane ^ 1, lane ^ 2 (quad permutations), then the other
+// quad of the half-row and the other half-row (mirrors).
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float sum16(float x) {
-    x += __shfl_xor(x, 8, 16);
-    x += __shfl_xor(x, 4, 16);
-    x += __shfl_xor(x, 2, 16);
-    x += __shfl_xor(x, 1, 16);
+    x += dpp_mov<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+    x += dpp_mov<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+    x += dpp_mov<0x141>(x);   // row_half_mirror
+    x += dpp_mov<0x140>(x);   // row_mirror
     return x;
 }
 
