@@ -331,12 +331,8 @@ __global__ __launch_bounds__(512, 1) void chunk_mfma_kernel(
                 x = pvalid ? neg_softplus_hw(x) : 0.f;
                 b = pvalid ? sigmoid_hw(b) : 0.f;
             }
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off);
-                if (lane >= off) x += y;
-            }
-            const float gC = __shfl(x, 63);
+            x = wave_scan64(x);
+            const float gC = lane63(x);
             sG[buf][0][lane] = x;
             sG[buf][1][lane] = exp_neg(x);
             sG[buf][2][lane] = b;

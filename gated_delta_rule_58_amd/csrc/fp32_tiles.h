@@ -128,12 +128,8 @@ __device__ __forceinline__ void chunk_gates(float (*sg)[BC], const float *la, co
         x = la[idx];
         b = beta[idx];
     }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    const float gn = __shfl(x, 63);
+    x = wave_scan64(x);
+    const float gn = lane63(x);
     sg[0][lane] = x;
     sg[1][lane] = expf(x);
     sg[2][lane] = b;
@@ -237,12 +233,8 @@ __device__ __forceinline__ void gate_fetch(const float *la, const float *beta, l
     }
 }
 __device__ __forceinline__ void gate_scan(float (*sg)[BC], float x, float b, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    const float gn = __shfl(x, 63);
+    x = wave_scan64(x);
+    const float gn = lane63(x);
     sg[0][lane] = x;
     sg[1][lane] = expf(x);
     sg[2][lane] = b;

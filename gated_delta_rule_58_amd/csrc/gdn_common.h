@@ -121,6 +121,27 @@ __device__ __forceinline__ bf16x8 frag_cols_d(const bf16 *base, int ld, int m0,
     return r;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active) by
+// DPP: row shifts by 1, 2, 4 and 8 scan each row of 16 lanes (lanes without
+// a source add 0), then the last lane of rows 0 and 2 is added to rows 1 and
+// 3, then lane 31 to rows 2 and 3.
+template <int CTRL, int ROWS> __device__ __forceinline__ float dpp_add_src(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, false));
+}
+__device__ __forceinline__ float wave_scan64(float x) {
+    x += dpp_add_src<0x111, 0xf>(x);   // row_shr:1
+    x += dpp_add_src<0x112, 0xf>(x);   // row_shr:2
+    x += dpp_add_src<0x114, 0xf>(x);   // row_shr:4
+    x += dpp_add_src<0x118, 0xf>(x);   // row_shr:8
+    x += dpp_add_src<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+    x += dpp_add_src<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
+    return x;
+}
+// The value of lane 63 (wave-uniform).
+__device__ __forceinline__ float lane63(float x) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
 // LDS transpose read of 16-bit elements (gfx950 ds_read_b64_tr_b16).  Within
 // each group of 16 lanes, lane 4j + q passes the address of 4 consecutive
 // elements (8 bytes); lane i of the group gets, as its element j, element i % 4
