@@ -68,6 +68,18 @@ __device__ __forceinline__ float sum_rows(float x) {
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+// Maximum over the 64 lanes of a wave, in every lane: the butterfly of
+// sum16 and sum_rows with fmaxf.
+__device__ __forceinline__ float max64(float x) {
+    x = fmaxf(x, dppf<0xB1>(x));
+    x = fmaxf(x, dppf<0x4E>(x));
+    x = fmaxf(x, dppf<0x141>(x));
+    x = fmaxf(x, dppf<0x140>(x));
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 template <typename X> __device__ __forceinline__ X cvt(float x);
 template <> __device__ __forceinline__ float cvt<float>(float x) { return x; }
@@ -423,9 +435,7 @@ __device__ __forceinline__ float diag_span(const float *G, int lg, int b, int la
     const float *glast = G + (16 * b + 15) * lg;
     float span = 0.f;
     for (int c = lane; c < D; c += 64) span = fmaxf(span, (gref ? gref[c] : 0.f) - glast[c]);
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) span = fmaxf(span, __shfl_xor(span, off));
-    return span;
+    return max64(span);
 }
 // The same block term by term (exponentials of r >= i only), for any span.
 template <int D, typename TX, typename TY>
