@@ -235,7 +235,9 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
         }
     }
     __syncthreads();   // E consumed: A_e and A_k go over it
-    // blocks above the diagonal of A_k, P_e, P_k (A_e's are never read)
+    // blocks above the diagonal of A_k, P_e, P_k, and of A_e (never read by
+    // the inverse; M, stored over A_e, is lower triangular)
+    zero_upper(sAe, tid);
     zero_upper(sAk, tid);
     zero_upper(sPe, tid);
     zero_upper(sPk, tid);
@@ -256,70 +258,111 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
     }
     __syncthreads();
     block_inverse64(sAe, sTe, wave, lane);   // T_e (ends with a barrier)
-    // M = P_e T_e (over A_e) and N1 = T_e A_k (to the workspace)
-    const int ty = wave & 3, tx0 = 2 * (wave >> 2);
-    {
-        f32x4 m[2], n1[2];
-        zero_n(m);
-        zero_n(n1);
-        mmn<BC, 2>(sPe + 16 * ty * LDN, LDN, 1, sTe + 16 * tx0, LDN, 1, 16, m, lane);
-        mmn<BC, 2>(sTe + 16 * ty * LDN, LDN, 1, sAk + 16 * tx0, LDN, 1, 16, n1, lane);
-        for (int x = 0; x < 2; ++x)
+    // The folds multiply lower triangular 64 x 64 factors (T_e, P_e, P_k, M
+    // lower, A_k strictly lower), so 16 x 16 output block (rb, cb) of M, N1
+    // and N2 is zero above the diagonal and sums only over the k blocks
+    // cb..rb, and row block rb of F1 and Qh over the k blocks 0..rb.  The
+    // blocks are dealt to the waves so that each forms about as many block
+    // products.
+    // tile (rb, cb) of X Y, k blocks cb..rb (X, Y 64 x 64 in LDS, row stride LDN)
+    auto tile_mm = [&](const float *X, const float *Y, int rb, int cb) {
+        f32x4 acc[1];
+        zero_n(acc);
+        for (int kb = cb; kb <= rb; ++kb)
+            mmn<16, 1>(X + 16 * rb * LDN + 16 * kb, LDN, 1, Y + 16 * kb * LDN + 16 * cb, LDN, 1, 0, acc, lane);
+        return acc[0];
+    };
+    // a zero block of a 64 x 64 image (rows 16 rb.., columns 16 cb..), 8-byte stores
+    auto zero_img = [&](bf16 *img, int rb, int cb) {
+        const int off = (16 * rb + li) * WS::LC + dpos(16 * cb + 4 * lq);
+        put_pair4(img + off, img + BC * WS::LC + off, zero4());
+    };
+    // blocks (rb, cb) encoded rb * 4 + cb; lists end with -1
+    constexpr signed char kMN[4][5] = {{12, 0, -1}, {13, 4, -1}, {8, 14, -1}, {9, 5, 10, 15, -1}};
+    constexpr signed char kN1z[4][3] = {{1, 2, -1}, {3, 6, -1}, {7, 11, -1}, {-1}};
+    constexpr signed char kN2[8][3] = {{12, -1}, {13, -1}, {8, -1}, {9, 0, -1},
+                                       {14, 5, -1}, {4, 10, -1}, {15, -1}, {-1}};
+    constexpr signed char kN2z[8][2] = {{-1}, {1, -1}, {2, -1}, {3, -1}, {6, -1}, {7, -1}, {11, -1}, {-1}};
+    {   // M = P_e T_e (even waves, over A_e) and N1 = T_e A_k (odd waves, to the workspace)
+        const int m = wave >> 1;
+        const bool isN1 = wave & 1;
+        for (int e = 0; kMN[m][e] >= 0; ++e) {
+            const int rb = kMN[m][e] >> 2, cb = kMN[m][e] & 3;
+            const f32x4 acc = isN1 ? tile_mm(sTe, sAk, rb, cb) : tile_mm(sPe, sTe, rb, cb);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 16 * ty + 4 * lq + j, c = 16 * (tx0 + x) + li;
-                sAe[r * LDN + c] = m[x][j];
-                const int off = r * WS::LC + dpos(c);
-                put_pair1(W + WS::N1 + off, W + WS::N1 + BC * WS::LC + off, n1[x][j]);
+                const int r = 16 * rb + 4 * lq + j, c = 16 * cb + li;
+                if (isN1) {
+                    const int off = r * WS::LC + dpos(c);
+                    put_pair1(W + WS::N1 + off, W + WS::N1 + BC * WS::LC + off, acc[j]);
+                } else {
+                    sAe[r * LDN + c] = acc[j];
+                }
             }
+        }
+        if (!isN1)
+            for (int e = 0; kN1z[m][e] >= 0; ++e) zero_img(W + WS::N1, kN1z[m][e] >> 2, kN1z[m][e] & 3);
     }
     __syncthreads();
     float *sM = sAe;
-    {   // N2 = P_k - M A_k
-        f32x4 n2[2];
-        zero_n(n2);
-        mmn<BC, 2>(sM + 16 * ty * LDN, LDN, 1, sAk + 16 * tx0, LDN, 1, 16, n2, lane);
-        for (int x = 0; x < 2; ++x)
+    // N2 = P_k - M A_k
+    for (int e = 0; kN2[wave][e] >= 0; ++e) {
+        const int rb = kN2[wave][e] >> 2, cb = kN2[wave][e] & 3;
+        const f32x4 acc = tile_mm(sM, sAk, rb, cb);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * ty + 4 * lq + j, c = 16 * (tx0 + x) + li;
-                const int off = r * WS::LC + dpos(c);
-                put_pair1(W + WS::N2 + off, W + WS::N2 + BC * WS::LC + off,
-                          sPk[r * LDN + c] - n2[x][j]);
-            }
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * rb + 4 * lq + j, c = 16 * cb + li;
+            const int off = r * WS::LC + dpos(c);
+            put_pair1(W + WS::N2 + off, W + WS::N2 + BC * WS::LC + off, sPk[r * LDN + c] - acc[j]);
+        }
     }
+    for (int e = 0; kN2z[wave][e] >= 0; ++e) zero_img(W + WS::N2, kN2z[wave][e] >> 2, kN2z[wave][e] & 3);
     // F1 = T_e (K o e^G) and Qh = Q o e^G - M (K o e^G), with K o e^G formed
-    // in the operand reads; 64 x D tiles, row tr, columns tc0.., formed
-    // transposed so that a lane holds four consecutive columns of one row
+    // in the operand reads.  Wave w takes 16 columns (column tile ct) and
+    // the row blocks in rbs: all four for d = 128; for d = 64 two waves share
+    // a column tile, rows {3, 0} and {2, 1}.  Formed transposed, so that a
+    // lane holds four consecutive columns of one row.
     {
-        constexpr int NTC = D / 32;
-        const int tr = wave & 3, tc0 = (wave >> 2) * NTC;
-        f32x4 f1[NTC], qh[NTC];
+        constexpr int NCT = D / 16, NRB = NCT == 8 ? 4 : 2;
+        static_assert(NCT == 8 || NCT == 4, "d = 64 or 128");
+        const int ct = wave % NCT;
+        int rbs[NRB];
+        if constexpr (NRB == 4) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) rbs[x] = x;
+        } else {
+            rbs[0] = wave < 4 ? 0 : 1;
+            rbs[1] = wave < 4 ? 3 : 2;
+        }
+        f32x4 f1[NRB], qh[NRB];
         zero_n(f1);
         zero_n(qh);
-#pragma unroll 4
-        for (int kk = 0; kk < BC; kk += 4) {
-            const int kr = kk + lq;
-            const float a1 = sTe[(16 * tr + li) * LDN + kr];
-            const float a2 = sM[(16 * tr + li) * LDN + kr];
+        const int c = 16 * ct + li;
 #pragma unroll
-            for (int t = 0; t < NTC; ++t) {
-                const int c = 16 * (tc0 + t) + li;
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+            for (int kk = 0; kk < 16; kk += 4) {
+                const int kr = 16 * kb + kk + lq;
                 const float b = to_f32(sK[kr * LI + c]) * sG[kr * LF + c];
-                f1[t] = mfma_f32(b, a1, f1[t]);
-                qh[t] = mfma_f32(b, a2, qh[t]);
+#pragma unroll
+                for (int x = 0; x < NRB; ++x) {
+                    if (rbs[x] < kb) continue;   // wave-uniform
+                    const int rw = (16 * rbs[x] + li) * LDN + kr;
+                    f1[x] = mfma_f32(b, sTe[rw], f1[x]);
+                    qh[x] = mfma_f32(b, sM[rw], qh[x]);
+                }
             }
         }
 #pragma unroll
-        for (int t = 0; t < NTC; ++t) {
-            const int r = 16 * tr + li, c = 16 * (tc0 + t) + 4 * lq;   // columns c..c+3
-            const f32x4 g = *reinterpret_cast<const f32x4 *>(sG + r * LF + c);   // e^G
-            const f32x4 qv = ld4f(sQ + r * LI + c);
+        for (int x = 0; x < NRB; ++x) {
+            const int r = 16 * rbs[x] + li, c4 = 16 * ct + 4 * lq;   // columns c4..c4+3
+            const f32x4 g = *reinterpret_cast<const f32x4 *>(sG + r * LF + c4);   // e^G
+            const f32x4 qv = ld4f(sQ + r * LI + c4);
             f32x4 qg;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) qg[j] = qv[j] * g[j] - qh[t][j];
-            const int off = r * WS::LK + dpos(c);
-            put_pair4(W + WS::F1 + off, W + WS::F1 + BC * WS::LK + off, f1[t]);
+            for (int j = 0; j < 4; ++j) qg[j] = qv[j] * g[j] - qh[x][j];
+            const int off = r * WS::LK + dpos(c4);
+            put_pair4(W + WS::F1 + off, W + WS::F1 + BC * WS::LK + off, f1[x]);
             put_pair4(W + WS::QH + off, W + WS::QH + BC * WS::LK + off, qg);
         }
     }
