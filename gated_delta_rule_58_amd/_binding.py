@@ -263,13 +263,9 @@ def kda_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, chunk=64,
     dv = v.shape[-1]
     io = q.dtype
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _need_cuda(name, t, io)
-    _need_cuda("log_alpha", log_alpha, torch.float32)
-    if tuple(log_alpha.shape) != (B, T, H, dk):
-        raise ValueError("log_alpha must be [B,T,H,dk]")
-    _need_cuda("beta", beta, torch.float32)
-    if tuple(beta.shape) != (B, T, H):
-        raise ValueError("beta must be [B,T,H]")
+        _need_shape(name, t, (B, T, H, dk if name != "v" else dv), io, q.device)
+    _need_shape("log_alpha", log_alpha, (B, T, H, dk), torch.float32, q.device)
+    _need_shape("beta", beta, (B, T, H), torch.float32, q.device)
     n_seqs = 0
     if cu_seqlens is not None:
         _need_cuda("cu_seqlens", cu_seqlens, torch.int32)

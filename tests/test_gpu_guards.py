@@ -144,6 +144,10 @@ def test_binding_rejects_bad_state_shapes():
             gdn.kda_fwd(ka["q"], ka["k"], ka["v"], ka["log_alpha"], ka["beta"], S0)
     with pytest.raises(ValueError):
         gdn.kda_fwd(ka["q"], ka["k"], ka["v"], ka["log_alpha"], ka["beta"], ka["S0"], S_T=bad)
+    with pytest.raises(ValueError):   # k of another sequence length than q
+        gdn.kda_fwd(ka["q"], ka["k"][:, :64].contiguous(), ka["v"], ka["log_alpha"], ka["beta"])
+    with pytest.raises(ValueError):   # log alpha per head instead of per channel
+        gdn.kda_fwd(ka["q"], ka["k"], ka["v"], ka["log_alpha"][..., 0].contiguous(), ka["beta"])
     g2 = {k: dev(v) for k, v in gi.gdn2_inputs(2, 70, 2, 128, 128, "bf16", s0_std=0.1,
                                               seed=47).items()}
     with pytest.raises(ValueError):
