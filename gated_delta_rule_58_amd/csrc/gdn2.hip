@@ -277,17 +277,29 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
         const int off = (16 * rb + li) * WS::LC + dpos(16 * cb + 4 * lq);
         put_pair4(img + off, img + BC * WS::LC + off, zero4());
     };
-    // blocks (rb, cb) encoded rb * 4 + cb; lists end with -1
-    constexpr signed char kMN[4][5] = {{12, 0, -1}, {13, 4, -1}, {8, 14, -1}, {9, 5, 10, 15, -1}};
-    constexpr signed char kN1z[4][3] = {{1, 2, -1}, {3, 6, -1}, {7, 11, -1}, {-1}};
-    constexpr signed char kN2[8][3] = {{12, -1}, {13, -1}, {8, -1}, {9, 0, -1},
-                                       {14, 5, -1}, {4, 10, -1}, {15, -1}, {-1}};
-    constexpr signed char kN2z[8][2] = {{-1}, {1, -1}, {2, -1}, {3, -1}, {6, -1}, {7, -1}, {11, -1}, {-1}};
+    // Block lists as 32-bit constants picked by the (wave-uniform) wave index,
+    // so they stay in scalar registers: entry e in bits 4e..4e+3 encodes block
+    // (rb, cb) as 4 rb + cb, the count is in bits 28-31.
+    auto blist = [](unsigned n, unsigned a, unsigned b = 0, unsigned c = 0, unsigned d = 0) {
+        return (n << 28) | a | (b << 4) | (c << 8) | (d << 12);
+    };
+    const int uw = __builtin_amdgcn_readfirstlane(wave);
+    const int m = uw >> 1;
+    const bool isN1 = uw & 1;
+    const unsigned kMN = m == 0 ? blist(2, 12, 0) : m == 1 ? blist(2, 13, 4)
+                       : m == 2 ? blist(2, 8, 14) : blist(4, 9, 5, 10, 15);
+    const unsigned kN1z = m == 0 ? blist(2, 1, 2) : m == 1 ? blist(2, 3, 6)
+                        : m == 2 ? blist(2, 7, 11) : 0u;
+    const unsigned kN2 = uw == 0 ? blist(1, 12) : uw == 1 ? blist(1, 13) : uw == 2 ? blist(1, 8)
+                       : uw == 3 ? blist(2, 9, 0) : uw == 4 ? blist(2, 14, 5)
+                       : uw == 5 ? blist(2, 4, 10) : uw == 6 ? blist(1, 15) : 0u;
+    const unsigned kN2z = uw == 1 ? blist(1, 1) : uw == 2 ? blist(1, 2) : uw == 3 ? blist(1, 3)
+                        : uw == 4 ? blist(1, 6) : uw == 5 ? blist(1, 7) : uw == 6 ? blist(1, 11) : 0u;
+    auto nblk = [](unsigned l) { return (int)(l >> 28); };
+    auto blk = [](unsigned l, int e) { return (int)((l >> (4 * e)) & 15); };
     {   // M = P_e T_e (even waves, over A_e) and N1 = T_e A_k (odd waves, to the workspace)
-        const int m = wave >> 1;
-        const bool isN1 = wave & 1;
-        for (int e = 0; kMN[m][e] >= 0; ++e) {
-            const int rb = kMN[m][e] >> 2, cb = kMN[m][e] & 3;
+        for (int e = 0; e < nblk(kMN); ++e) {
+            const int rb = blk(kMN, e) >> 2, cb = blk(kMN, e) & 3;
             const f32x4 acc = isN1 ? tile_mm(sTe, sAk, rb, cb) : tile_mm(sPe, sTe, rb, cb);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -301,13 +313,13 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
             }
         }
         if (!isN1)
-            for (int e = 0; kN1z[m][e] >= 0; ++e) zero_img(W + WS::N1, kN1z[m][e] >> 2, kN1z[m][e] & 3);
+            for (int e = 0; e < nblk(kN1z); ++e) zero_img(W + WS::N1, blk(kN1z, e) >> 2, blk(kN1z, e) & 3);
     }
     __syncthreads();
     float *sM = sAe;
     // N2 = P_k - M A_k
-    for (int e = 0; kN2[wave][e] >= 0; ++e) {
-        const int rb = kN2[wave][e] >> 2, cb = kN2[wave][e] & 3;
+    for (int e = 0; e < nblk(kN2); ++e) {
+        const int rb = blk(kN2, e) >> 2, cb = blk(kN2, e) & 3;
         const f32x4 acc = tile_mm(sM, sAk, rb, cb);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -316,7 +328,7 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
             put_pair1(W + WS::N2 + off, W + WS::N2 + BC * WS::LC + off, sPk[r * LDN + c] - acc[j]);
         }
     }
-    for (int e = 0; kN2z[wave][e] >= 0; ++e) zero_img(W + WS::N2, kN2z[wave][e] >> 2, kN2z[wave][e] & 3);
+    for (int e = 0; e < nblk(kN2z); ++e) zero_img(W + WS::N2, blk(kN2z, e) >> 2, blk(kN2z, e) & 3);
     // F1 = T_e (K o e^G) and Qh = Q o e^G - M (K o e^G), with K o e^G formed
     // in the operand reads.  Wave w takes 16 columns (column tile ct) and
     // the row blocks in rbs: all four for d = 128; for d = 64 two waves share
