@@ -270,15 +270,16 @@ __device__ __forceinline__ void zero_upper(float *m, int tid) {
 // sums its segment in registers, and the segment totals are combined across
 // the SEG lanes of the column by shuffles.  Each thread rewrites only the
 // elements it read.  Returns the column's total (the prefix at the last row)
-// in every lane of the column's group.
-template <int D> __device__ __forceinline__ float column_prefix(float *s, int ld, int tid) {
+// in every lane of the column's group.  Each element is multiplied by
+// `scale` as it is read (a change of units, e.g. to base-2 exponents).
+template <int D> __device__ __forceinline__ float column_prefix(float *s, int ld, int tid, float scale = 1.f) {
     constexpr int SEG = 512 / D, RS = BC / SEG;
     static_assert(SEG * D == 512 && RS * SEG == BC, "512 threads cover the tile");
     const int c = tid / SEG, sg = tid % SEG;
     float *col = s + sg * RS * ld + c;
     float v[RS];
 #pragma unroll
-    for (int j = 0; j < RS; ++j) v[j] = col[j * ld];
+    for (int j = 0; j < RS; ++j) v[j] = col[j * ld] * scale;
 #pragma unroll
     for (int j = 1; j < RS; ++j) v[j] += v[j - 1];
     float incl = v[RS - 1];   // inclusive scan of the segment totals
@@ -437,8 +438,9 @@ __device__ __forceinline__ float diag_span(const float *G, int lg, int b, int la
     for (int c = lane; c < D; c += 64) span = fmaxf(span, (gref ? gref[c] : 0.f) - glast[c]);
     return max64(span);
 }
-// The same block term by term (exponentials of r >= i only), for any span.
-template <int D, typename TX, typename TY>
+// The same block term by term (exponentials of r >= i only), for any span;
+// with BASE2 the prefixes G are in base-2 units (log2 e times the natural).
+template <int D, bool BASE2 = false, typename TX, typename TY>
 __device__ __forceinline__ f32x4 diag_terms(const TX *X, int lx, const TY *Y, int ly,
                                             const float *G, int lg, int b, int lane) {
     const int li = lane & 15, lq = lane >> 4;
@@ -453,7 +455,10 @@ __device__ __forceinline__ f32x4 diag_terms(const TX *X, int lx, const TY *Y, in
             const f32x4 gr = *reinterpret_cast<const f32x4 *>(G + r * lg + c);
             const f32x4 xr = ld4f(X + r * lx + c);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[j] += xr[e] * yi[e] * __expf(fminf(gr[e] - gi[e], 0.f));
+            for (int e = 0; e < 4; ++e) {
+                const float x = fminf(gr[e] - gi[e], 0.f);
+                acc[j] += xr[e] * yi[e] * (BASE2 ? __builtin_amdgcn_exp2f(x) : __expf(x));
+            }
         }
     }
     return acc;

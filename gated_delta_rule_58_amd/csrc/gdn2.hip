@@ -32,6 +32,11 @@ namespace {
 using namespace tiles;
 using namespace img;
 
+constexpr float kLog2e = 1.4426950408889634f;
+// 2^x by the hardware exponential (inputs here are differences of base-2
+// prefixes, <= 0 or bounded by the decay-span limit)
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 
 // Workspace of one chunk and head: the operands of the sequential launch as
 // bf16 hi + lo pairs in the layout it keeps in LDS (rows padded by 8, each
@@ -108,8 +113,10 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
     zero_upper(sTe, tid);   // the inverse writes the rest of T_e
     __syncthreads();
     {   // prefix over the chunk per channel (padded rows add 0)
-        const float gn = column_prefix<D>(sG, LF, tid);
-        if (tid % (512 / D) == 0) wEG[tid / (512 / D)] = expf(gn);
+        // G is kept in base-2 units (log2 e times the natural prefix), so that
+        // every exponential below is one v_exp_f32 of a difference
+        const float gn = column_prefix<D>(sG, LF, tid, kLog2e);
+        if (tid % (512 / D) == 0) wEG[tid / (512 / D)] = exp2f(gn);
     }
     for (int e = tid; e < BC * D / 4; e += 512) {   // E = b o k
         const int r = e / (D / 4), c = (e % (D / 4)) * 4;
@@ -127,7 +134,7 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
         f32x4 e0, e1, k0, k1;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float t0 = __expf(gn - sG[(r0 + j) * LF + c]), t1 = __expf(gn - sG[(r1 + j) * LF + c]);
+            const float t0 = exp2_fast(gn - sG[(r0 + j) * LF + c]), t1 = exp2_fast(gn - sG[(r1 + j) * LF + c]);
             e0[j] = sE[(r0 + j) * LE + c] * t0;
             e1[j] = sE[(r1 + j) * LE + c] * t1;
             k0[j] = to_f32(sK[(r0 + j) * LI + c]) * t0;
@@ -175,8 +182,8 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
         const int ram = 16 * bmr + li, rbm = 16 * bmi + li, grm = bmr > 0 ? 16 * bmr - 1 : 0;
         const float gonm = bmr > 0 ? 1.f : 0.f;   // reference prefix 0 for the first block row
         const int rax = 16 * bxr + li, rbx = 16 * bxi + li, grx = 16 * bxr - 1;
-        const bool termsm = bmi == bmr && diag_span<D>(sG, LF, bmr, lane) > 60.f;
-        const bool termsx = bxi == bxr && diag_span<D>(sG, LF, bxr, lane) > 60.f;
+        const bool termsm = bmi == bmr && diag_span<D>(sG, LF, bmr, lane) > 60.f * kLog2e;
+        const bool termsx = bxi == bxr && diag_span<D>(sG, LF, bxr, lane) > 60.f * kLog2e;
         const TI *Xx = mxx < 2 ? sK : sQ;   // the extra chain's rows
         const bool colE = (mxx & 1) == 0;   // and its columns: E (A_e, P_e) or K
 #pragma unroll
@@ -201,24 +208,24 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
             const f32x4 gxb = *reinterpret_cast<const f32x4 *>(sG + rbx * LF + cb);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float ea = __expf(ga[j] - gr4[j]), eb = __expf(gr4[j] - gb[j]);
+                const float ea = exp2_fast(ga[j] - gr4[j]), eb = exp2_fast(gr4[j] - gb[j]);
                 const float ak = ka[j] * ea, aq = qa[j] * ea, be = eb4[j] * eb, bk = kb[j] * eb;
                 res[0] = mfma_f32(ak, be, res[0]);
                 res[1] = mfma_f32(ak, bk, res[1]);
                 res[2] = mfma_f32(aq, be, res[2]);
                 res[3] = mfma_f32(aq, bk, res[3]);
-                res[4] = mfma_f32(xa[j] * __expf(gxa[j] - gx4[j]), yb[j] * __expf(gx4[j] - gxb[j]), res[4]);
+                res[4] = mfma_f32(xa[j] * exp2_fast(gxa[j] - gx4[j]), yb[j] * exp2_fast(gx4[j] - gxb[j]), res[4]);
             }
         }
         if (termsm) {
-            res[0] = diag_terms<D>(sK, LI, sE, LE, sG, LF, bmr, lane);
-            res[1] = diag_terms<D>(sK, LI, sK, LI, sG, LF, bmr, lane);
-            res[2] = diag_terms<D>(sQ, LI, sE, LE, sG, LF, bmr, lane);
-            res[3] = diag_terms<D>(sQ, LI, sK, LI, sG, LF, bmr, lane);
+            res[0] = diag_terms<D, true>(sK, LI, sE, LE, sG, LF, bmr, lane);
+            res[1] = diag_terms<D, true>(sK, LI, sK, LI, sG, LF, bmr, lane);
+            res[2] = diag_terms<D, true>(sQ, LI, sE, LE, sG, LF, bmr, lane);
+            res[3] = diag_terms<D, true>(sQ, LI, sK, LI, sG, LF, bmr, lane);
         }
         if (termsx)
-            res[4] = colE ? diag_terms<D>(Xx, LI, sE, LE, sG, LF, bxr, lane)
-                          : diag_terms<D>(Xx, LI, sK, LI, sG, LF, bxr, lane);
+            res[4] = colE ? diag_terms<D, true>(Xx, LI, sE, LE, sG, LF, bxr, lane)
+                          : diag_terms<D, true>(Xx, LI, sK, LI, sG, LF, bxr, lane);
         // the next pair's inputs: issued here, where the waves of the
         // lighter block products would wait at the barrier anyway, rather
         // than all at once at the top of the pair
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
         f32x4 *pg = reinterpret_cast<f32x4 *>(sG + (e / (D / 4)) * LF + (e % (D / 4)) * 4);
         f32x4 x = *pg;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = __expf(x[j]);
+        for (int j = 0; j < 4; ++j) x[j] = exp2_fast(x[j]);
         *pg = x;
     }
     __syncthreads();
@@ -270,6 +277,15 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
         zero_n(acc);
         for (int kb = cb; kb <= rb; ++kb)
             mmn<16, 1>(X + 16 * rb * LDN + 16 * kb, LDN, 1, Y + 16 * kb * LDN + 16 * cb, LDN, 1, 0, acc, lane);
+        return acc[0];
+    };
+    // the same block transposed: lane (i, q) gets rows 16 rb + i, columns
+    // 16 cb + 4 q .. + 3 of X Y (four consecutive columns of one row)
+    auto tile_mm_t = [&](const float *X, const float *Y, int rb, int cb) {
+        f32x4 acc[1];
+        zero_n(acc);
+        for (int kb = cb; kb <= rb; ++kb)
+            mmn<16, 1>(Y + 16 * kb * LDN + 16 * cb, 1, LDN, X + 16 * rb * LDN + 16 * kb, 1, LDN, 0, acc, lane);
         return acc[0];
     };
     // a zero block of a 64 x 64 image (rows 16 rb.., columns 16 cb..), 8-byte stores
@@ -300,16 +316,14 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
     {   // M = P_e T_e (even waves, over A_e) and N1 = T_e A_k (odd waves, to the workspace)
         for (int e = 0; e < nblk(kMN); ++e) {
             const int rb = blk(kMN, e) >> 2, cb = blk(kMN, e) & 3;
-            const f32x4 acc = isN1 ? tile_mm(sTe, sAk, rb, cb) : tile_mm(sPe, sTe, rb, cb);
+            if (isN1) {
+                const f32x4 acc = tile_mm_t(sTe, sAk, rb, cb);
+                const int off = (16 * rb + li) * WS::LC + dpos(16 * cb + 4 * lq);
+                put_pair4(W + WS::N1 + off, W + WS::N1 + BC * WS::LC + off, acc);
+            } else {
+                const f32x4 acc = tile_mm(sPe, sTe, rb, cb);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * rb + 4 * lq + j, c = 16 * cb + li;
-                if (isN1) {
-                    const int off = r * WS::LC + dpos(c);
-                    put_pair1(W + WS::N1 + off, W + WS::N1 + BC * WS::LC + off, acc[j]);
-                } else {
-                    sAe[r * LDN + c] = acc[j];
-                }
+                for (int j = 0; j < 4; ++j) sAe[(16 * rb + 4 * lq + j) * LDN + 16 * cb + li] = acc[j];
             }
         }
         if (!isN1)
@@ -320,13 +334,11 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
     // N2 = P_k - M A_k
     for (int e = 0; e < nblk(kN2); ++e) {
         const int rb = blk(kN2, e) >> 2, cb = blk(kN2, e) & 3;
-        const f32x4 acc = tile_mm(sM, sAk, rb, cb);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * rb + 4 * lq + j, c = 16 * cb + li;
-            const int off = r * WS::LC + dpos(c);
-            put_pair1(W + WS::N2 + off, W + WS::N2 + BC * WS::LC + off, sPk[r * LDN + c] - acc[j]);
-        }
+        const f32x4 acc = tile_mm_t(sM, sAk, rb, cb);
+        const int r = 16 * rb + li, c = 16 * cb + 4 * lq;
+        const int off = r * WS::LC + dpos(c);
+        put_pair4(W + WS::N2 + off, W + WS::N2 + BC * WS::LC + off,
+                  *reinterpret_cast<const f32x4 *>(sPk + r * LDN + c) - acc);
     }
     for (int e = 0; e < nblk(kN2z); ++e) zero_img(W + WS::N2, blk(kN2z, e) >> 2, blk(kN2z, e) & 3);
     // F1 = T_e (K o e^G) and Qh = Q o e^G - M (K o e^G), with K o e^G formed
