@@ -463,11 +463,14 @@ __device__ __forceinline__ f32x4 diag_terms(const TX *X, int lx, const TY *Y, in
     }
     return acc;
 }
-template <int D, typename TX, typename TY>
+// (BASE2: the prefixes G in base-2 units, as for diag_terms.)
+template <int D, bool BASE2 = false, typename TX, typename TY>
 __device__ __forceinline__ f32x4 diag_block(const TX *X, int lx, const TY *Y, int ly,
                                             const float *G, int lg, int b, int lane) {
     const int li = lane & 15, lq = lane >> 4;
-    if (diag_span<D>(G, lg, b, lane) > 60.f) return diag_terms<D>(X, lx, Y, ly, G, lg, b, lane);
+    constexpr float kSpan = BASE2 ? 60.f * 1.4426950408889634f : 60.f;
+    if (diag_span<D>(G, lg, b, lane) > kSpan) return diag_terms<D, BASE2>(X, lx, Y, ly, G, lg, b, lane);
+    auto ex = [](float x) { return BASE2 ? __builtin_amdgcn_exp2f(x) : __expf(x); };
     const float gon = b > 0 ? 1.f : 0.f;   // reference prefix 0 for the first block
     const float *gref = G + (b > 0 ? 16 * b - 1 : 0) * lg;
     f32x4 acc = zero4();
@@ -481,7 +484,7 @@ __device__ __forceinline__ f32x4 diag_block(const TX *X, int lx, const TY *Y, in
         const f32x4 xa = ld4f(X + rw * lx + cb), ya = ld4f(Y + rw * ly + cb);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            acc = mfma_f32(xa[j] * __expf(gw[j] - gr[j]), ya[j] * __expf(gr[j] - gw[j]), acc);
+            acc = mfma_f32(xa[j] * ex(gw[j] - gr[j]), ya[j] * ex(gr[j] - gw[j]), acc);
     }
     return acc;
 }

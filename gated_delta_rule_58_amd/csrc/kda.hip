@@ -42,6 +42,12 @@ namespace {
 using namespace tiles;
 using namespace img;
 
+constexpr float kLog2e = 1.4426950408889634f;
+// 2^x by the hardware exponential (the prep keeps the gate prefix G in base-2
+// units, log2 e times the natural prefix, so that each exponential is one
+// v_exp_f32 of a difference)
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 
 // Workspace of one chunk and head: every operand of the sequential launch as
 // a bf16 hi + lo pair (hi = x rounded to bf16, lo = bf16(x - hi); about 16
@@ -101,13 +107,13 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
     load_rows<D>(sG, LF, la, row0, n, H, h, 0, D, tid, 512);
     if (tid < BC) sb[tid] = tid < n ? beta[(size_t)(row0 + tid) * H + h] : 0.f;
     __syncthreads();
-    if (tid < D) {   // prefix over the chunk per channel (padded rows add 0)
+    if (tid < D) {   // prefix over the chunk per channel, base-2 units (padded rows add 0)
         float g = 0.f;
         for (int r = 0; r < BC; ++r) {
-            g += sG[r * LF + tid];
+            g += sG[r * LF + tid] * kLog2e;
             sG[r * LF + tid] = g;
         }
-        wEG[tid] = expf(g);
+        wEG[tid] = exp2f(g);
     }
     __syncthreads();
     // rescaled operands of the sequential launch, one D-order group of 8
@@ -123,7 +129,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
         f32x4 kg0, kg1, qg0, qg1;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float e0 = __expf(g0[j]), e1 = __expf(g1[j]);
+            const float e0 = exp2_fast(g0[j]), e1 = exp2_fast(g1[j]);
             kg0[j] = k0[j] * e0;
             qg0[j] = q0[j] * e0;
             kg1[j] = k1[j] * e1;
@@ -140,8 +146,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
         f32x4 t0, t1;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            t0[j] = to_f32(sK[(r0 + j) * LI + c]) * __expf(gn - sG[(r0 + j) * LF + c]);
-            t1[j] = to_f32(sK[(r1 + j) * LI + c]) * __expf(gn - sG[(r1 + j) * LF + c]);
+            t0[j] = to_f32(sK[(r0 + j) * LI + c]) * exp2_fast(gn - sG[(r0 + j) * LF + c]);
+            t1[j] = to_f32(sK[(r1 + j) * LI + c]) * exp2_fast(gn - sG[(r1 + j) * LF + c]);
         }
         const int off = c * WS::LC + p;
         put_pair8(W + WS::KT + off, W + WS::KT + D * WS::LC + off, t0, t1);
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
         const int b = wave & 3;
         const TI *X = isP ? sQ : sK;
         const int i = 16 * b + li;
-        const f32x4 acc = diag_block<D>(X, LI, sK, LI, sG, LF, b, lane);
+        const f32x4 acc = diag_block<D, true>(X, LI, sK, LI, sG, LF, b, lane);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * b + 4 * lq + j;
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
             const f32x4 xa = ld4f(X + ra * LI + cb), kb = ld4f(sK + rb * LI + cb);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float a = xa[j] * __expf(ga[j] - gr[j]), bb = kb[j] * __expf(gr[j] - gb[j]);
+                const float a = xa[j] * exp2_fast(ga[j] - gr[j]), bb = kb[j] * exp2_fast(gr[j] - gb[j]);
                 acc = isP ? mfma_f32(bb, a, acc) : mfma_f32(a, bb, acc);
             }
         }
