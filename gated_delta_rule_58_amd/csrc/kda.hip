@@ -102,10 +102,20 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
     const int li = lane & 15, lq = lane >> 4;
     bf16 *W = ws + (size_t)blockIdx.x * WS::total;
     float *wEG = reinterpret_cast<float *>(W + WS::EG);
-    load_rows<D>(sK, LI, k, row0, n, H, h, 0, D, tid, 512);
-    load_rows<D>(sQ, LI, q, row0, n, H, h, 0, D, tid, 512);
-    load_rows<D>(sG, LF, la, row0, n, H, h, 0, D, tid, 512);
-    if (tid < BC) sb[tid] = tid < n ? beta[(size_t)(row0 + tid) * H + h] : 0.f;
+    {   // every load in flight before the first LDS store (a loop that stores
+        // each load waits for the memory round trip of each in turn)
+        const size_t g0 = (size_t)row0 * H * D + (size_t)h * D;
+        Prefetch<D, TI> pk, pq;
+        Prefetch<D, float> pg;
+        pk.fetch(k + g0, (size_t)H * D, n, tid);
+        pq.fetch(q + g0, (size_t)H * D, n, tid);
+        pg.fetch(la + g0, (size_t)H * D, n, tid);
+        const float bv = tid < n ? beta[(size_t)(row0 + tid) * H + h] : 0.f;
+        pk.commit(sK, LI, tid);
+        pq.commit(sQ, LI, tid);
+        pg.commit(sG, LF, tid);
+        if (tid < BC) sb[tid] = bv;
+    }
     __syncthreads();
     if (tid < D) {   // prefix over the chunk per channel, base-2 units (padded rows add 0)
         float g = 0.f;
