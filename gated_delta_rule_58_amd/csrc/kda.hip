@@ -149,18 +149,27 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
         put_pair8(W + WS::KG + off, W + WS::KG + BC * WS::LK + off, kg0, kg1);
         put_pair8(W + WS::QG + off, W + WS::QG + BC * WS::LK + off, qg0, qg1);
     }
-    for (int e = tid; e < D * BC / 8; e += 512) {
-        const int c = e / (BC / 8), p = 8 * (e % (BC / 8));
-        const int r0 = (p & ~31) + (p & 31) / 2, r1 = r0 + 16;   // tokens r0..+3, r1..+3
-        const float gn = sG[(BC - 1) * LF + c];
-        f32x4 t0, t1;
+    // (K o e^{G_n - G})^T: an item is four channels of one run of 4 tokens
+    // (half of a D-order group of 8; the two halves go to neighbouring lanes,
+    // whose 8-byte stores are adjacent), read as one piece of each token's row
+    for (int e = tid; e < (D / 4) * (BC / 4); e += 512) {
+        const int half = e & 1, grp = e >> 1;
+        const int c4 = 4 * (grp / (BC / 8)), p = 8 * (grp % (BC / 8));
+        const int rt = (p & ~31) + (p & 31) / 2 + 16 * half;   // tokens rt..rt+3
+        const f32x4 gn = *reinterpret_cast<const f32x4 *>(sG + (BC - 1) * LF + c4);
+        f32x4 kv[4];   // [channel][token]
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            t0[j] = to_f32(sK[(r0 + j) * LI + c]) * exp2_fast(gn - sG[(r0 + j) * LF + c]);
-            t1[j] = to_f32(sK[(r1 + j) * LI + c]) * exp2_fast(gn - sG[(r1 + j) * LF + c]);
+            const f32x4 g = *reinterpret_cast<const f32x4 *>(sG + (rt + j) * LF + c4);
+            const f32x4 kk = ld4f(sK + (rt + j) * LI + c4);
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) kv[ch][j] = kk[ch] * exp2_fast(gn[ch] - g[ch]);
         }
-        const int off = c * WS::LC + p;
-        put_pair8(W + WS::KT + off, W + WS::KT + D * WS::LC + off, t0, t1);
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+            const int off = (c4 + ch) * WS::LC + p + 4 * half;
+            put_pair4(W + WS::KT + off, W + WS::KT + D * WS::LC + off, kv[ch]);
+        }
     }
     // row padding and the tail of region B are written too (zeros), so
     // every cache line of the workspace is written whole
