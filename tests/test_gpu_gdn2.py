@@ -75,6 +75,16 @@ def test_gdn2_extreme_channels():
     compare("gdn2 extreme channel decays", inp)
 
 
+def test_gdn2_decays_at_the_term_threshold():
+    """Per-channel decays of about e^-3 per token put the decay span of a
+    16-token diagonal block around e^-60, the limit above which the prep
+    forms the block term by term: in one launch some diagonal blocks take the
+    rescaled product and the others the term-by-term path (19 of 64 here)."""
+    inp = gi.gdn2_inputs(1, 512, 2, 128, 128, "bf16", alpha_mu=3.0, alpha_sd=1.0, s0_std=0.1,
+                         seed=81)
+    compare("gdn2 decays at the term threshold", inp)
+
+
 def test_gdn2_scalar_gates_match_kda():
     """b_t = w_t = beta_t in every channel: gdn_kda_fwd's rule (both GPU runs
     against each other; each is checked against its oracle elsewhere).  The

@@ -71,6 +71,16 @@ def test_kda_strong_and_weak_channels():
     compare("kda extreme channel decays", inp)
 
 
+def test_kda_decays_at_the_term_threshold():
+    """Per-channel decays of about e^-3 per token put the decay span of a
+    16-token diagonal block around e^-60, the limit above which the prep
+    forms the block term by term: in one launch some diagonal blocks take the
+    rescaled product and the others the term-by-term path (19 of 64 here)."""
+    inp = gi.kda_inputs(1, 512, 2, 128, 128, "bf16", alpha_mu=3.0, alpha_sd=1.0, s0_std=0.1,
+                        seed=81)
+    compare("kda decays at the term threshold", inp)
+
+
 def test_kda_uniform_channels_match_scalar_rule():
     """Equal channels: the same rule as gdn_chunk_fwd (both against the oracle)."""
     inp = gi.chunk_inputs(2, 200, 2, 128, 128, "bf16", s0_std=0.1, seed=6)
