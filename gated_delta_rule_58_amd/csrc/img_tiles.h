@@ -50,6 +50,24 @@ __device__ __forceinline__ void put_pair1(bf16 *hi, bf16 *lo, float x) {
 
 __device__ __forceinline__ bf16x8 ld8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
+// A region of operand images whose rows are padded by 8 bf16 (one 16-byte
+// chunk) in LDS but dense in the workspace: M x R rows of W bf16, then E
+// more 16-byte chunks (stored alike in both), then the tail of the region's
+// whole KB in LDS.  src_chunk(q) is the chunk of the dense image that LDS
+// chunk q holds; a row's pad chunk and the tail read chunk 0 (never read
+// back from LDS), so every source address lies inside the image.
+template <int M, int R, int W, int E> struct PaddedRegion {
+    static constexpr int DC = W / 8, PC = DC + 1, NM = M * R * PC;
+    static_assert(W % 8 == 0, "whole 16-byte chunks per row");
+    __device__ static __forceinline__ int src_chunk(int q) {
+        if (q < NM) {
+            const int row = q / PC, ch = q - row * PC;
+            return row * DC + (ch < DC ? ch : 0);
+        }
+        return q < NM + E ? M * R * DC + (q - NM) : 0;
+    }
+};
+
 // Direct global-to-LDS copy of 16 bytes per lane: lane l's bytes land at
 // dst + 16 l (dst is the wave's base address), so a wave moves 1 KB.
 __device__ __forceinline__ void lds_dma16(void *dst, const void *src) {

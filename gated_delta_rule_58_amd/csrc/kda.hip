@@ -49,16 +49,17 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 
-// Workspace of one chunk and head: every operand of the sequential launch as
-// a bf16 hi + lo pair (hi = x rounded to bf16, lo = bf16(x - hi); about 16
-// mantissa bits of x), in exactly the layout the sequential launch keeps in
-// LDS, so that it copies each region with direct global-to-LDS loads: rows
-// padded by 8 elements, each 32-wide block of columns in D-order (see
-// dpos) so an operand fragment is one 16-byte read.  Offsets in bf16
-// elements.  Four regions of whole KB, in the order the sequential launch
-// consumes them: K o e^G and Q o e^G; T diag(beta); P;
-// (K o e^{G_n - G})^T and e^{G_n}.
-template <int D> struct KdaWs {
+// The operands of the sequential launch, per chunk and head, as bf16 hi + lo
+// pairs: K o e^G, Q o e^G (64 x D each), T diag(beta), P (64 x 64 each),
+// (K o e^{G_n - G})^T (D x 64) and e^{G_n} (D floats).  Each row's 32-wide
+// column blocks are in the D-order the MFMA fragments read (img_tiles.h).
+// In LDS (KdaLds, offsets in bf16 elements) rows are padded by 8 elements so
+// that the fragment reads are free of bank conflicts, in four regions of
+// whole KB -- K o e^G | Q o e^G, T diag(beta), P, (K o e^{G_n - G})^T with
+// e^{G_n} -- that the sequential launch copies one after another.  In the
+// workspace (KdaWs) the same rows are dense: the pads would be 8.5% of the
+// bytes written and read back.
+template <int D> struct KdaLds {
     static constexpr int LK = D + 8, LC = BC + 8;   // row strides of the 64 x D and x 64 blocks
     static constexpr size_t up(size_t x) { return (x + 511) / 512 * 512; }
     static constexpr size_t KG = 0,                         // K o e^G, 64 x D: hi, lo
@@ -70,6 +71,12 @@ template <int D> struct KdaWs {
                             total = up(EG + 2 * D);
     static_assert(TB == QG + 2 * BC * LK && P == TB + 2 * BC * LC && KT == P + 2 * BC * LC,
                   "regions are contiguous");
+};
+template <int D> struct KdaWs {
+    static constexpr size_t KG = 0, QG = KG + 2 * BC * D, TB = QG + 2 * BC * D,
+                            P = TB + 2 * BC * BC, KT = P + 2 * BC * BC, EG = KT + 2 * D * BC,
+                            total = EG + 2 * D;
+    static_assert(total % 64 == 0, "chunk-head images start on 128-byte lines");
 };
 
 // ---------------------------------------------------------------- 1. prep
@@ -145,9 +152,9 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
             kg1[j] = k1[j] * e1;
             qg1[j] = q1[j] * e1;
         }
-        const int off = r * WS::LK + p;
-        put_pair8(W + WS::KG + off, W + WS::KG + BC * WS::LK + off, kg0, kg1);
-        put_pair8(W + WS::QG + off, W + WS::QG + BC * WS::LK + off, qg0, qg1);
+        const int off = r * D + p;
+        put_pair8(W + WS::KG + off, W + WS::KG + BC * D + off, kg0, kg1);
+        put_pair8(W + WS::QG + off, W + WS::QG + BC * D + off, qg0, qg1);
     }
     // (K o e^{G_n - G})^T: an item is four channels of one run of 4 tokens
     // (half of a D-order group of 8; the two halves go to neighbouring lanes,
@@ -167,22 +174,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
         }
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch) {
-            const int off = (c4 + ch) * WS::LC + p + 4 * half;
-            put_pair4(W + WS::KT + off, W + WS::KT + D * WS::LC + off, kv[ch]);
-        }
-    }
-    // row padding and the tail of region B are written too (zeros), so
-    // every cache line of the workspace is written whole
-    {
-        constexpr int NR = 4 * BC + 4 * BC + 2 * D;              // padded rows
-        constexpr int NT = (int)(WS::total - WS::EG - 2 * D) / 8;   // 16-byte tail pieces
-        for (int e = tid; e < NR + NT; e += 512) {
-            size_t off;
-            if (e < 4 * BC) off = WS::KG + (size_t)e * WS::LK + D;                  // K/Q o e^G
-            else if (e < 8 * BC) off = WS::TB + (size_t)(e - 4 * BC) * WS::LC + BC;  // T, P
-            else if (e < NR) off = WS::KT + (size_t)(e - 8 * BC) * WS::LC + BC;      // K^T
-            else off = WS::EG + 2 * D + (size_t)(e - NR) * 8;   // tail of the last region
-            *reinterpret_cast<bf16x8 *>(W + off) = bf16x8{};
+            const int off = (c4 + ch) * BC + p + 4 * half;
+            put_pair4(W + WS::KT + off, W + WS::KT + D * BC + off, kv[ch]);
         }
     }
     // blocks of P above the diagonal are zero
@@ -190,8 +183,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
     for (int e = tid; e < BC * BC / 4; e += 512) {
         const int r = e >> 4, i = (e & 15) * 4;
         if ((i >> 4) > (r >> 4)) {
-            const int off = r * WS::LC + dpos(i);
-            put_pair4(W + WS::P + off, W + WS::P + BC * WS::LC + off, zero4());
+            const int off = r * BC + dpos(i);
+            put_pair4(W + WS::P + off, W + WS::P + BC * BC + off, zero4());
         }
     }
     // A and P, 16 x 16 blocks (br, bi), bi <= br: 10 blocks each.  The 8
@@ -216,8 +209,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
                 if constexpr (kStageP) {
                     pdiag[j] = i <= r ? acc[j] : 0.f;
                 } else {
-                    const int off = r * WS::LC + dpos(i);
-                    put_pair1(W + WS::P + off, W + WS::P + BC * WS::LC + off, i <= r ? acc[j] : 0.f);
+                    const int off = r * BC + dpos(i);
+                    put_pair1(W + WS::P + off, W + WS::P + BC * BC + off, i <= r ? acc[j] : 0.f);
                 }
             }
             adiag[j] = i < r ? sb[r] * acc[j] : 0.f;
@@ -254,8 +247,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
             if constexpr (kStageP) {
                 poff = acc;
             } else {
-                const int off = (16 * br + li) * WS::LC + dpos(16 * bi + 4 * lq);
-                put_pair4(W + WS::P + off, W + WS::P + BC * WS::LC + off, acc);
+                const int off = (16 * br + li) * BC + dpos(16 * bi + 4 * lq);
+                put_pair4(W + WS::P + off, W + WS::P + BC * BC + off, acc);
             }
         } else {
 #pragma unroll
@@ -301,10 +294,10 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(
                          *reinterpret_cast<const f32x4 *>(sb + i0);
         const f32x4 t1 = *reinterpret_cast<const f32x4 *>(sX + r * LDN + i1) *
                          *reinterpret_cast<const f32x4 *>(sb + i1);
-        const int off = r * WS::LC + p;
-        put_pair8(W + WS::TB + off, W + WS::TB + BC * WS::LC + off, t0, t1);
+        const int off = r * BC + p;
+        put_pair8(W + WS::TB + off, W + WS::TB + BC * BC + off, t0, t1);
         if constexpr (kStageP)
-            put_pair8(W + WS::P + off, W + WS::P + BC * WS::LC + off,
+            put_pair8(W + WS::P + off, W + WS::P + BC * BC + off,
                       *reinterpret_cast<const f32x4 *>(sP + r * LDN + i0),
                       *reinterpret_cast<const f32x4 *>(sP + r * LDN + i1));
     }
@@ -330,7 +323,8 @@ __global__ __launch_bounds__(512, 1) void kda_fwd_kernel(
     int T, int H, int NC, int varlen, int xcd_map, const int32_t *__restrict__ cu,
     const TI *__restrict__ v, const float *__restrict__ S0, const bf16 *__restrict__ ws,
     TO *__restrict__ o, float *__restrict__ S_T) {
-    typedef KdaWs<D> WS;
+    typedef KdaLds<D> WS;   // the LDS layout (padded rows)
+    typedef KdaWs<D> WD;    // the workspace layout (dense rows)
     constexpr int NSL = D / 64, NKS = D / 32, NCT = D / 16;
     constexpr int LK = WS::LK, LC = WS::LC;
     constexpr int VP = 16 / sizeof(TI);               // V elements per 16-byte piece
@@ -368,13 +362,15 @@ __global__ __launch_bounds__(512, 1) void kda_fwd_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15, lq = lane >> 4;
-    auto wsof = [&](int c) { return ws + ((size_t)(base + c) * H + h) * WS::total; };
+    auto wsof = [&](int c) { return ws + ((size_t)(base + c) * H + h) * WD::total; };
 
-    // ---- loaders (waves 0-3): wave w copies the KB pieces w, w + 4, ...
-    auto copy_region = [&](bf16 *dst, const bf16 *src, int kb) {
+    // ---- loaders (waves 0-3): wave w copies the KB pieces w, w + 4, ... of
+    // a region's LDS image, each lane's 16 bytes from the dense workspace
+    auto copy_region = [&](auto reg, bf16 *dst, const bf16 *src, int kb) {
+        typedef decltype(reg) RG;
         for (int i = wave; i < kb; i += 4)
             lds_dma16(reinterpret_cast<char *>(dst) + 1024 * i,
-                      reinterpret_cast<const char *>(src) + 1024 * i + 16 * lane);
+                      reinterpret_cast<const char *>(src) + 16 * RG::src_chunk(64 * i + lane));
     };
     auto copy_v = [&](int c) {   // rows past the chunk repeat its last token (their
                                  // T diag(beta) columns are zero)
@@ -386,10 +382,15 @@ __global__ __launch_bounds__(512, 1) void kda_fwd_kernel(
             lds_dma16(sV + 1024 / sizeof(TI) * i, src);
         }
     };
-    auto copy1 = [&](int c) { copy_region(sKQ, wsof(c), K1); };
-    auto copy2 = [&](int c) { copy_region(sTB, wsof(c) + WS::TB, K2); copy_v(c); };
-    auto copy3 = [&](int c) { copy_region(sP, wsof(c) + WS::P, K3); };
-    auto copy4 = [&](int c) { copy_region(sKT, wsof(c) + WS::KT, K4); };
+    auto copy1 = [&](int c) { copy_region(PaddedRegion<4, BC, D, 0>{}, sKQ, wsof(c) + WD::KG, K1); };
+    auto copy2 = [&](int c) {
+        copy_region(PaddedRegion<2, BC, BC, 0>{}, sTB, wsof(c) + WD::TB, K2);
+        copy_v(c);
+    };
+    auto copy3 = [&](int c) { copy_region(PaddedRegion<2, BC, BC, 0>{}, sP, wsof(c) + WD::P, K3); };
+    auto copy4 = [&](int c) {
+        copy_region(PaddedRegion<2, D, BC, D / 4>{}, sKT, wsof(c) + WD::KT, K4);   // with e^{G_n}
+    };
 
     // A loader wave's barrier: its copies for the next phase are waited for
     // by count (wait_vm) beforehand, and nothing is moved across it; a full

@@ -189,12 +189,11 @@ def test_kda_workspace_and_rejects():
         return B.lib().gdn_kda_fwd_workspace_size(ctypes.byref(s), ctypes.byref(out)), out.value
     rc, nb = kws(shape(T=130))
     nch = 2 * 3 * 4
-    # per chunk and head, bf16 hi + lo pairs in four regions of whole KB (512
-    # elements): K o e^G and Q o e^G (rows of d + 8), T diag(beta), P (rows of
-    # 72), (K o e^{G_n - G})^T (d rows of 72) with e^{G_n} (d floats)
-    up = lambda x: (x + 511) // 512 * 512
+    # per chunk and head, bf16 hi + lo pairs with dense rows: K o e^G and
+    # Q o e^G (64 x d each), T diag(beta) and P (64 x 64 each),
+    # (K o e^{G_n - G})^T (d x 64), then e^{G_n} (d floats)
     d = 128
-    per = up(4 * 64 * (d + 8)) + 2 * up(2 * 64 * 72) + up(2 * d * 72 + 2 * d)
+    per = 2 * 2 * 64 * d + 2 * 2 * 64 * 64 + 2 * d * 64 + 2 * d
     assert rc == OK and nb == 2 * nch * per
     assert kws(shape(prologue=2))[0] == UNSUPPORTED
     assert kws(shape(io_dtype=0))[0] == UNSUPPORTED
