@@ -38,13 +38,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 
-// Workspace of one chunk and head: the operands of the sequential launch as
-// bf16 hi + lo pairs in the layout it keeps in LDS (rows padded by 8, each
-// 32-wide column block in D-order; img_tiles.h), offsets in bf16 elements.
-// Five regions of whole KB in the order the sequential launch reads them:
-// F1, Qh (64 x D each), (E o e^{G_n - G})^T with e^{G_n}, (K o e^{G_n - G})^T
-// (D x 64 each), and N1 with N2 (64 x 64 each).
-template <int D> struct G2Ws {
+// The operands of the sequential launch, per chunk and head, as bf16 hi + lo
+// pairs: F1, Qh (64 x D each), (E o e^{G_n - G})^T with e^{G_n},
+// (K o e^{G_n - G})^T (D x 64 each), and N1 with N2 (64 x 64 each).  Each
+// row's 32-wide column blocks are in the D-order the MFMA fragments read
+// (img_tiles.h).  In LDS (G2Lds, offsets in bf16 elements) rows are padded by
+// 8 elements so that the fragment reads are free of bank conflicts, in five
+// regions of whole KB in the order the sequential launch reads them.  In the
+// workspace (G2Ws) the same rows are dense: the pads would be 9-12% of the
+// bytes written and read back.
+template <int D> struct G2Lds {
     static constexpr int LK = D + 8, LC = BC + 8;   // row strides of the 64 x D and x 64 blocks
     static constexpr size_t up(size_t x) { return (x + 511) / 512 * 512; }
     static constexpr size_t F1 = 0,                       // T_e (K o e^G): hi, lo
@@ -58,6 +61,12 @@ template <int D> struct G2Ws {
     static_assert(QH == 2 * BC * LK && KT - (EG + 2 * D) < 512 && N1 == KT + 2 * D * LC &&
                       total == N2 + 2 * BC * LC,
                   "regions are contiguous");
+};
+template <int D> struct G2Ws {
+    static constexpr size_t F1 = 0, QH = F1 + 2 * BC * D, ET = QH + 2 * BC * D,
+                            EG = ET + 2 * D * BC, KT = EG + 2 * D, N1 = KT + 2 * D * BC,
+                            N2 = N1 + 2 * BC * BC, total = N2 + 2 * BC * BC;
+    static_assert(total % 64 == 0, "chunk-head images start on 128-byte lines");
 };
 
 // ---------------------------------------------------------------- 1. prep
@@ -140,20 +149,9 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
             k0[j] = to_f32(sK[(r0 + j) * LI + c]) * t0;
             k1[j] = to_f32(sK[(r1 + j) * LI + c]) * t1;
         }
-        const int off = c * WS::LC + p;
-        put_pair8(W + WS::ET + off, W + WS::ET + D * WS::LC + off, e0, e1);
-        put_pair8(W + WS::KT + off, W + WS::KT + D * WS::LC + off, k0, k1);
-    }
-    // row padding and the tail after e^{G_n} are written too (zeros), so every
-    // cache line of the workspace is written whole
-    for (int e = tid; e < 8 * BC + 4 * D + (int)(WS::KT - WS::EG - 2 * D) / 8; e += 512) {
-        size_t off;
-        if (e < 4 * BC) off = WS::F1 + (size_t)e * WS::LK + D;                        // F1, Qh
-        else if (e < 8 * BC) off = WS::N1 + (size_t)(e - 4 * BC) * WS::LC + BC;       // N1, N2
-        else if (e < 8 * BC + 2 * D) off = WS::ET + (size_t)(e - 8 * BC) * WS::LC + BC;
-        else if (e < 8 * BC + 4 * D) off = WS::KT + (size_t)(e - 8 * BC - 2 * D) * WS::LC + BC;
-        else off = WS::EG + 2 * D + (size_t)(e - 8 * BC - 4 * D) * 8;
-        *reinterpret_cast<bf16x8 *>(W + off) = bf16x8{};
+        const int off = c * BC + p;
+        put_pair8(W + WS::ET + off, W + WS::ET + D * BC + off, e0, e1);
+        put_pair8(W + WS::KT + off, W + WS::KT + D * BC + off, k0, k1);
     }
     // The four channel-weighted products, 16 x 16 blocks (br, bi), bi <= br:
     // matrix mx = 0 A_e (rows K, columns E), 1 A_k (K, K), 2 P_e (Q, E),
@@ -290,8 +288,8 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
     };
     // a zero block of a 64 x 64 image (rows 16 rb.., columns 16 cb..), 8-byte stores
     auto zero_img = [&](bf16 *img, int rb, int cb) {
-        const int off = (16 * rb + li) * WS::LC + dpos(16 * cb + 4 * lq);
-        put_pair4(img + off, img + BC * WS::LC + off, zero4());
+        const int off = (16 * rb + li) * BC + dpos(16 * cb + 4 * lq);
+        put_pair4(img + off, img + BC * BC + off, zero4());
     };
     // Block lists as 32-bit constants picked by the (wave-uniform) wave index,
     // so they stay in scalar registers: entry e in bits 4e..4e+3 encodes block
@@ -318,8 +316,8 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
             const int rb = blk(kMN, e) >> 2, cb = blk(kMN, e) & 3;
             if (isN1) {
                 const f32x4 acc = tile_mm_t(sTe, sAk, rb, cb);
-                const int off = (16 * rb + li) * WS::LC + dpos(16 * cb + 4 * lq);
-                put_pair4(W + WS::N1 + off, W + WS::N1 + BC * WS::LC + off, acc);
+                const int off = (16 * rb + li) * BC + dpos(16 * cb + 4 * lq);
+                put_pair4(W + WS::N1 + off, W + WS::N1 + BC * BC + off, acc);
             } else {
                 const f32x4 acc = tile_mm(sPe, sTe, rb, cb);
 #pragma unroll
@@ -336,8 +334,8 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
         const int rb = blk(kN2, e) >> 2, cb = blk(kN2, e) & 3;
         const f32x4 acc = tile_mm_t(sM, sAk, rb, cb);
         const int r = 16 * rb + li, c = 16 * cb + 4 * lq;
-        const int off = r * WS::LC + dpos(c);
-        put_pair4(W + WS::N2 + off, W + WS::N2 + BC * WS::LC + off,
+        const int off = r * BC + dpos(c);
+        put_pair4(W + WS::N2 + off, W + WS::N2 + BC * BC + off,
                   *reinterpret_cast<const f32x4 *>(sPk + r * LDN + c) - acc);
     }
     for (int e = 0; e < nblk(kN2z); ++e) zero_img(W + WS::N2, blk(kN2z, e) >> 2, blk(kN2z, e) & 3);
@@ -385,9 +383,9 @@ __global__ __launch_bounds__(512) void gdn2_prep_kernel(
             f32x4 qg;
 #pragma unroll
             for (int j = 0; j < 4; ++j) qg[j] = qv[j] * g[j] - qh[x][j];
-            const int off = r * WS::LK + dpos(c4);
-            put_pair4(W + WS::F1 + off, W + WS::F1 + BC * WS::LK + off, f1[x]);
-            put_pair4(W + WS::QH + off, W + WS::QH + BC * WS::LK + off, qg);
+            const int off = r * D + dpos(c4);
+            put_pair4(W + WS::F1 + off, W + WS::F1 + BC * D + off, f1[x]);
+            put_pair4(W + WS::QH + off, W + WS::QH + BC * D + off, qg);
         }
     }
     __syncthreads();   // every LDS operand consumed before the next pair's commit
@@ -416,7 +414,8 @@ __global__ __launch_bounds__(512, 1) void gdn2_fwd_kernel(
     int T, int H, int NC, int varlen, int xcd_map, const int32_t *__restrict__ cu,
     const TI *__restrict__ v, const float *__restrict__ write, const float *__restrict__ S0,
     const bf16 *__restrict__ ws, TO *__restrict__ o, float *__restrict__ S_T) {
-    typedef G2Ws<D> WS;
+    typedef G2Lds<D> WS;   // the LDS layout (padded rows)
+    typedef G2Ws<D> WD;    // the workspace layout (dense rows)
     constexpr int NSL = D / 64, NKS = D / 32, NCT = D / 16;
     constexpr int LK = WS::LK, LC = WS::LC;
     constexpr int VP = 16 / sizeof(TI);               // V elements per 16-byte piece
@@ -457,19 +456,25 @@ __global__ __launch_bounds__(512, 1) void gdn2_fwd_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15, lq = lane >> 4;
-    auto wsof = [&](int c) { return ws + ((size_t)(base + c) * H + h) * WS::total; };
+    auto wsof = [&](int c) { return ws + ((size_t)(base + c) * H + h) * WD::total; };
 
     if (wave < 4) {
-        // ---- loaders: wave w copies the KB pieces w, w + 4, ...
-        auto copy_region = [&](bf16 *dst, const bf16 *src, int kb) {
+        // ---- loaders: wave w copies the KB pieces w, w + 4, ... of a
+        // region's LDS image, each lane's 16 bytes from the dense workspace
+        auto copy_region = [&](auto reg, bf16 *dst, const bf16 *src, int kb) {
+            typedef decltype(reg) RG;
             for (int i = wave; i < kb; i += 4)
                 lds_dma16(reinterpret_cast<char *>(dst) + 1024 * i,
-                          reinterpret_cast<const char *>(src) + 1024 * i + 16 * lane);
+                          reinterpret_cast<const char *>(src) + 16 * RG::src_chunk(64 * i + lane));
         };
+        typedef PaddedRegion<2, BC, D, 0> RgF;        // F1 or Qh
+        typedef PaddedRegion<2, D, BC, D / 4> RgE;    // (E o e^{G_n - G})^T with e^{G_n}
+        typedef PaddedRegion<2, D, BC, 0> RgK;        // (K o e^{G_n - G})^T
+        typedef PaddedRegion<4, BC, BC, 0> RgN;       // N1, N2
         // v and w rows past the chunk repeat its last token: the columns of
         // N1, N2 and the rows of (K o e^{G_n - G})^T they meet are zero
         auto copy_r = [&](int c) {
-            copy_region(sN, wsof(c) + WS::N1, KR);
+            copy_region(RgN{}, sN, wsof(c) + WD::N1, KR);
             const long row0 = start + (long)c * BC;
             const int n = (int)min((long)BC, L - (long)c * BC);
             for (int i = wave; i < BC / VROWS; i += 4) {
@@ -490,21 +495,21 @@ __global__ __launch_bounds__(512, 1) void gdn2_fwd_kernel(
         // Copies in issue order: U1(0) W1(0) R(0) | per chunk c: W1(c) (c > 0)
         // in phase 1, U2(c) in 2, W2(c) in 3, R(c+1) in 4, U1(c+1) in 5.
         if (N > 0) {
-            copy_region(sU, wsof(0) + WS::F1, KU1);
-            copy_region(sW, wsof(0) + WS::QH, KW1);
+            copy_region(RgF{}, sU, wsof(0) + WD::F1, KU1);
+            copy_region(RgF{}, sW, wsof(0) + WD::QH, KW1);
             copy_r(0);
             wait_vm<CW1 + CR>();   // F1 of chunk 0
         }
         loader_barrier();
         for (int c = 0; c < N; ++c) {
             const bool more = c + 1 < N;
-            if (c > 0) copy_region(sW, wsof(c) + WS::QH, KW1);
+            if (c > 0) copy_region(RgF{}, sW, wsof(c) + WD::QH, KW1);
             wait_vm<0>();          // Qh of chunk c (and N1, N2, w, v before it)
             loader_barrier();
-            copy_region(sU, wsof(c) + WS::ET, KU2);
+            copy_region(RgE{}, sU, wsof(c) + WD::ET, KU2);
             wait_vm<CU2>();
             loader_barrier();
-            copy_region(sW, wsof(c) + WS::KT, KW2);
+            copy_region(RgK{}, sW, wsof(c) + WD::KT, KW2);
             wait_vm<CW2>();        // E^T of chunk c
             loader_barrier();
             if (more) {
@@ -515,7 +520,7 @@ __global__ __launch_bounds__(512, 1) void gdn2_fwd_kernel(
             }
             loader_barrier();
             if (more) {
-                copy_region(sU, wsof(c + 1) + WS::F1, KU1);
+                copy_region(RgF{}, sU, wsof(c + 1) + WD::F1, KU1);
                 wait_vm<0>();      // F1 of chunk c + 1
             }
             loader_barrier();

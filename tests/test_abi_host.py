@@ -212,12 +212,11 @@ def test_gdn2_workspace_and_rejects():
         out = ctypes.c_size_t(7)
         return B.lib().gdn_gdn2_fwd_workspace_size(ctypes.byref(s), ctypes.byref(out)), out.value
     rc, nb = gws(shape(T=130))
-    # per chunk and head, bf16 hi + lo pairs in five regions of whole KB:
-    # F1 and Qh (rows of d + 8), (E o e^{G_n - G})^T with e^{G_n},
-    # (K o e^{G_n - G})^T (d rows of 72), N1 and N2 (64 rows of 72)
-    up = lambda x: (x + 511) // 512 * 512
+    # per chunk and head, bf16 hi + lo pairs with dense rows: F1 and Qh
+    # (64 x d each), (E o e^{G_n - G})^T (d x 64), e^{G_n} (d floats),
+    # (K o e^{G_n - G})^T (d x 64), N1 and N2 (64 x 64 each)
     d = 128
-    per = 2 * up(2 * 64 * (d + 8)) + up(2 * d * 72 + 2 * d) + up(2 * d * 72) + up(4 * 64 * 72)
+    per = 2 * 2 * 64 * d + 2 * d * 64 + 2 * d + 2 * d * 64 + 2 * 2 * 64 * 64
     assert rc == OK and nb == 2 * 2 * 3 * 4 * per
     assert gws(shape(prologue=1))[0] == UNSUPPORTED
     assert gws(shape(io_dtype=0))[0] == UNSUPPORTED
