@@ -322,8 +322,8 @@ def run_kda(args, torch, gi, gdn, dev, w):
                               "flops_per_step": {"prep_f32": f_prep * nch,
                                                  "sequential_fp32_accurate": f_seq * nch}},
             "note": "gdn_kda_fwd = prep (fp32 MFMA blocks of A and P, T by the blocked "
-                    "inverse; writes the sequential launch's operands as bf16 hi + lo pairs in "
-                    "its LDS layout) + sequential launch (bf16 MFMA, three piece products per "
+                    "inverse; writes the sequential launch's operands as bf16 hi + lo pairs, "
+                    "rows dense) + sequential launch (bf16 MFMA, three piece products per "
                     "product; operand regions copied global->LDS three phases ahead). HBM-bound "
                     "on the workspace round trip: see frac_with_workspace. bf16 q/k/v, fp32 "
                     "channel-wise log alpha [B,T,H,d_k], fp32 o and state"}
@@ -377,7 +377,7 @@ def run_gdn2(args, torch, gi, gdn, dev, w):
                                                  "sequential_fp32_accurate": f_seq * nch}},
             "note": "gdn_gdn2_fwd = prep (fp32 MFMA: channel-weighted blocks, T_e, the folds "
                     "F1, Qh, N1, N2; writes the sequential launch's operands as bf16 hi + lo "
-                    "pairs in its LDS layout) + sequential launch (bf16 MFMA, three piece "
+                    "pairs, rows dense) + sequential launch (bf16 MFMA, three piece "
                     "products per product, five phases, operand regions copied global->LDS "
                     "ahead of use). bf16 q/k/v, fp32 log alpha and erase gates [B,T,H,d_k], "
                     "write gates [B,T,H,d_v]"}

@@ -1,9 +1,10 @@
 // Operand images shared by the channel-wise decay kernels (KDA, GDN-2): a
 // prep launch writes each operand of the sequential launch as a bf16 hi + lo
 // pair (hi = x rounded to bf16, lo = bf16(x - hi): about 16 mantissa bits of
-// x) in exactly the layout the sequential launch keeps in LDS, which copies it
-// with direct global-to-LDS loads and multiplies on the 16x16x32 bf16 MFMA as
-// the three piece products hi*hi + lo*hi + hi*lo.
+// x) with its columns in the order the sequential launch keeps in LDS (rows
+// dense in the workspace, padded in LDS); the sequential launch copies it with
+// direct global-to-LDS loads and multiplies on the 16x16x32 bf16 MFMA as the
+// three piece products hi*hi + lo*hi + hi*lo.
 #pragma once
 
 #include "gdn_common.h"

@@ -57,7 +57,7 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // that the fragment reads are free of bank conflicts, in four regions of
 // whole KB -- K o e^G | Q o e^G, T diag(beta), P, (K o e^{G_n - G})^T with
 // e^{G_n} -- that the sequential launch copies one after another.  In the
-// workspace (KdaWs) the same rows are dense: the pads would be 8.5% of the
+// workspace (KdaWs) the same rows are dense: the pads would be 9-12% of the
 // bytes written and read back.
 template <int D> struct KdaLds {
     static constexpr int LK = D + 8, LC = BC + 8;   // row strides of the 64 x D and x 64 blocks
