@@ -331,6 +331,8 @@ def gdn2_fwd(q, k, v, log_alpha, erase, write, S0=None, cu_seqlens=None, chunk=6
     io = q.dtype
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need_cuda(name, t, io)
+    if tuple(k.shape) != (B, T, H, dk) or tuple(v.shape[:3]) != (B, T, H):
+        raise ValueError("q, k, v shapes disagree")
     for name, t, last in (("log_alpha", log_alpha, dk), ("erase", erase, dk),
                           ("write", write, dv)):
         _need_cuda(name, t, torch.float32)

@@ -155,6 +155,12 @@ def test_binding_rejects_bad_state_shapes():
     with pytest.raises(ValueError):
         gdn.gdn2_fwd(g2["q"], g2["k"], g2["v"], g2["log_alpha"], g2["erase"], g2["write"],
                      g2["S0"], o=torch.zeros((2, 70, 2, 128), device=DEV, dtype=torch.float16))
+    with pytest.raises(ValueError):   # k of another sequence length than q
+        gdn.gdn2_fwd(g2["q"], g2["k"][:, :64].contiguous(), g2["v"], g2["log_alpha"],
+                     g2["erase"], g2["write"])
+    with pytest.raises(ValueError):   # v of another batch than q
+        gdn.gdn2_fwd(g2["q"], g2["k"], g2["v"][:1].contiguous(), g2["log_alpha"],
+                     g2["erase"], g2["write"])
 
 
 def test_binding_rejects_bad_step_shapes():
