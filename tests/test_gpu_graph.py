@@ -129,3 +129,41 @@ def test_chunk_bwd_graph_replay():
         torch.cuda.synchronize()
         for name, a, b in zip(("dq", "dk", "dv", "dlog_alpha", "dbeta", "dS0"), out["g"], eager):
             assert torch.equal(a, b), f"replay {rep}: {name}"
+
+
+@pytest.mark.parametrize("which", ["kda", "kda_noalloc", "gdn2"])
+def test_channel_forward_graph_replay(which):
+    B, T, H, d = 2, 200, 3, 128
+    if which == "gdn2":
+        inp = gi.gdn2_inputs(B, T, H, d, d, "bf16", s0_std=0.1, seed=35)
+        keys = ("q", "k", "v", "log_alpha", "erase", "write")
+        fwd, size = gdn.gdn2_fwd, gdn.gdn2_fwd_workspace_size
+    else:
+        inp = gi.kda_inputs(B, T, H, d, d, "bf16", s0_std=0.1, seed=34)
+        keys = ("q", "k", "v", "log_alpha", "beta")
+        fwd, size = gdn.kda_fwd, gdn.kda_fwd_workspace_size
+    x = {n: dev(t) for n, t in inp.items()}
+    args = tuple(x[n] for n in keys)
+    say(f"{which} graph: B={B} T={T} H={H} d={d}")
+    o_e, S_e = fwd(*args, x["S0"])
+    torch.cuda.synchronize()
+    o_g = torch.empty_like(o_e)
+    S_g = torch.empty_like(S_e)
+    ws = torch.empty(size(B, T, H, d, d), dtype=torch.uint8, device=DEV)
+
+    def run():
+        if which == "kda_noalloc":   # workspace from the library's device array
+            gdn.kda_fwd_noalloc(*args, x["S0"], o=o_g, S_T=S_g)
+        else:
+            fwd(*args, x["S0"], o=o_g, S_T=S_g, workspace=ws)
+
+    g = capture(run)
+    for rep in range(3):
+        o_g.fill_(float("nan"))
+        S_g.fill_(float("nan"))
+        ws.fill_(255)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e), f"replay {rep}: o"
+        assert torch.equal(S_g, S_e), f"replay {rep}: S_T"
