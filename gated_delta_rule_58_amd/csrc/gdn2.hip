@@ -601,6 +601,8 @@ __global__ __launch_bounds__(512, 1) void gdn2_fwd_kernel(
             split_op(z[2], z[3], zh[1], zl[1]);
             const long row0 = start + (long)c * BC;
             const int n = (int)min((long)BC, L - (long)c * BC);
+            const rsrc_t ro = rows_rsrc(o + ((size_t)row0 * H + h) * D + dv0 + 16 * cw,
+                                        (uint32_t)n * H * D * (uint32_t)sizeof(TO));
             f32x4 x[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
@@ -611,7 +613,7 @@ __global__ __launch_bounds__(512, 1) void gdn2_fwd_kernel(
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 16 * rt + 4 * lq + j;
-                    if (r < n) o[((size_t)(row0 + r) * H + h) * D + vcol] = cvt<TO>(oa[j]);
+                    rsrc_store(cvt<TO>(oa[j]), ro, (uint32_t)(r * H * D + li) * (uint32_t)sizeof(TO));
                 }
             }
             split_op(x[0], x[1], xh[0], xl[0]);

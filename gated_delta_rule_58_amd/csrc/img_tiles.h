@@ -69,6 +69,22 @@ template <int M, int R, int W, int E> struct PaddedRegion {
     }
 };
 
+// Stores of output rows through a raw buffer resource whose size covers only
+// the valid rows of a chunk: stores past them (ragged last chunk) are dropped
+// by the hardware range check, so no lane branches on the row.  The base
+// address must be wave-uniform; lanes differ by their byte offsets.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t rows_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);   // raw, 32-bit data format
+}
+__device__ __forceinline__ void rsrc_store(float x, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, off, 0, 0);
+}
+__device__ __forceinline__ void rsrc_store(bf16 x, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), r, off, 0, 0);
+}
+
 // Direct global-to-LDS copy of 16 bytes per lane: lane l's bytes land at
 // dst + 16 l (dst is the wave's base address), so a wave moves 1 KB.
 __device__ __forceinline__ void lds_dma16(void *dst, const void *src) {

@@ -522,6 +522,8 @@ __global__ __launch_bounds__(512, 1) void kda_fwd_kernel(
         {
             const long row0 = start + (long)c * BC;
             const int n = (int)min((long)BC, L - (long)c * BC);
+            const rsrc_t ro = rows_rsrc(o + ((size_t)row0 * H + h) * D + dv0 + 16 * cw,
+                                        (uint32_t)n * H * D * (uint32_t)sizeof(TO));
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 f32x4 acc = qs[rt];
@@ -536,7 +538,7 @@ __global__ __launch_bounds__(512, 1) void kda_fwd_kernel(
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 16 * rt + 4 * lq + j;
-                    if (r < n) o[((size_t)(row0 + r) * H + h) * D + vcol] = cvt<TO>(acc[j]);
+                    rsrc_store(cvt<TO>(acc[j]), ro, (uint32_t)(r * H * D + li) * (uint32_t)sizeof(TO));
                 }
             }
         }
