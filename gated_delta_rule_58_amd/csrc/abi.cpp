@@ -129,6 +129,8 @@ int check_fp32tile_shape(const gdn_shape *s, int kind) {   // 0 bwd, 1 KDA, 2 GD
     if (s->prologue != 0)
         return fail(GDN_ERR_UNSUPPORTED, "%s takes no input prologue (prologue=%d)",
                     entry, s->prologue);
+    if (s->H > 32768)   // keeps the 32-bit row offsets of the kernels' buffer stores in range
+        return fail(GDN_ERR_UNSUPPORTED, "H=%d exceeds the supported 32768 heads", s->H);
     const long units = s->n_seqs > 0 ? s->n_seqs : s->B;
     if ((long)units * s->H > (1L << 24) || (long)s->T * s->H > (1L << 31) / 64)
         return fail(GDN_ERR_INVALID_ARG,

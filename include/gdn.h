@@ -62,7 +62,8 @@ typedef enum gdn_status {
     GDN_OK = 0,
     GDN_ERR_INVALID_ARG = 1,  /* null required pointer, negative/zero dims, varlen with B != 1,
                                  unknown prologue bits */
-    GDN_ERR_UNSUPPORTED = 2,  /* (d_k, d_v, chunk, dtype) with no compiled kernel */
+    GDN_ERR_UNSUPPORTED = 2,  /* (d_k, d_v, chunk, dtype) with no compiled kernel, or
+                                 H > 32768 (the kernels' 32-bit row offsets) */
     GDN_ERR_ALIGNMENT = 3,    /* a pointer not 16-byte aligned */
     GDN_ERR_WORKSPACE = 4,    /* workspace smaller than gdn_chunk_fwd_workspace_size */
     GDN_ERR_HIP = 5           /* a HIP launch error */

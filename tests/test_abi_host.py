@@ -78,6 +78,7 @@ def test_workspace_query_supported(kw):
     (dict(d_k=96, d_v=96), UNSUPPORTED), (dict(d_k=128, d_v=64), UNSUPPORTED),
     (dict(chunk=32), UNSUPPORTED), (dict(d_k=128, d_v=128, io_dtype=0), UNSUPPORTED),
     (dict(d_k=16, d_v=16, chunk=8, io_dtype=0), UNSUPPORTED),
+    (dict(B=1, T=1, H=32769), UNSUPPORTED),
 ])
 def test_workspace_query_rejects(kw, code):
     rc, _ = ws_size(shape(**kw))
@@ -198,6 +199,7 @@ def test_kda_workspace_and_rejects():
     assert kws(shape(prologue=2))[0] == UNSUPPORTED
     assert kws(shape(io_dtype=0))[0] == UNSUPPORTED
     assert kws(shape(chunk=16))[0] == UNSUPPORTED
+    assert kws(shape(B=1, T=1, H=32769))[0] == UNSUPPORTED   # 32-bit store offsets
     s = shape()
     call = lambda **kw: B.lib().gdn_kda_fwd(
         ctypes.byref(s), kw.get("q", P), P, P, P, P, None, None, kw.get("o", P2), None,
@@ -220,6 +222,7 @@ def test_gdn2_workspace_and_rejects():
     assert rc == OK and nb == 2 * 2 * 3 * 4 * per
     assert gws(shape(prologue=1))[0] == UNSUPPORTED
     assert gws(shape(io_dtype=0))[0] == UNSUPPORTED
+    assert gws(shape(B=1, T=1, H=32769))[0] == UNSUPPORTED
     s = shape()
     call = lambda **kw: B.lib().gdn_gdn2_fwd(
         ctypes.byref(s), P, P, P, P, kw.get("erase", P), P, None, None, kw.get("o", P2), None,
