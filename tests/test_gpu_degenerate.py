@@ -1,0 +1,137 @@
+"""Degenerate gates on the GPU: no decay and nothing written.
+
+With log alpha = 0 and beta = 0 (for Gated DeltaNet-2: erase = write = 0)
+every term of the update vanishes, so the state passes through unchanged
+and each read-out is o_t = S0 q_t ("Gated Delta Networks: Improving Mamba2
+with Delta Rule", research-map summary, section "Approach": alpha_t = 1
+keeps the state and beta_t = 0 writes nothing; "Gated DeltaNet-2:
+Decoupling Erase and Write in Linear Attention", abstract: the erase and
+write gates scale the removed and the added terms).  In the kernels every
+decay is then exp2(0) = 1 exactly and the factors that carry beta (erase,
+write) are exactly zero, so the final state must equal S0 bit for bit; o is
+checked against S0 q computed in fp64 and against the oracle, at the
+parity bars of each path.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+import gated_delta_rule_58_amd as gdn
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+THREADS = min(16, os.cpu_count() or 1)
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def dev(x):
+    return None if x is None else x.to(DEV)
+
+
+def frozen(inp):
+    """The same inputs with log alpha = 0 and every write gate 0."""
+    out = dict(inp)
+    for name in ("log_alpha", "beta", "erase", "write"):
+        if out.get(name) is not None:
+            out[name] = torch.zeros_like(out[name])
+    return out
+
+
+def s0_q(inp):
+    """o_t = S0 q_t in fp64, per sequence (S0 [U, H, dv, dk], q [B, T, H, dk])."""
+    q = inp["q"].double().numpy()
+    S0 = inp["S0"].double().numpy()
+    o = np.zeros(q.shape[:3] + (S0.shape[2],))
+    cu = inp["cu_seqlens"]
+    if cu is None:
+        return np.einsum("bhvk,bthk->bthv", S0, q)
+    cu = [int(x) for x in cu]
+    for u in range(len(cu) - 1):
+        o[0, cu[u]:cu[u + 1]] = np.einsum("hvk,thk->thv", S0[u], q[0, cu[u]:cu[u + 1]])
+    return o
+
+
+def check(tag, o, st, inp, ref_o, tau):
+    S0 = inp["S0"]
+    assert torch.equal(st.cpu(), S0), f"{tag}: S_T differs from S0"
+    for name, want in (("o vs S0 q", s0_q(inp)), ("o vs oracle", ref_o)):
+        err = gi.max_rel_err(o.cpu(), want)
+        say(f"{tag} {name}: max err / RMS = {err:.3e} (bar {tau:g})")
+        assert err <= tau, f"{tag} {name}: {err:.3e} > {tau:g}"
+
+
+@pytest.mark.parametrize("io,d,chunk,tau", [("bf16", 128, 64, 2e-2), ("bf16", 64, 64, 2e-2),
+                                            ("f32", 32, 32, 1e-4)])
+def test_chunk_fwd_frozen_state(io, d, chunk, tau):
+    inp = frozen(gi.chunk_inputs(2, 150, 3, d, d, io, s0_std=0.5, seed=71))
+    tag = f"chunk_fwd {io} d={d} C={chunk}"
+    say(f"{tag}: launch")
+    o, st = gdn.chunk_fwd(*(dev(inp[n]) for n in ("q", "k", "v", "log_alpha", "beta", "S0")),
+                          chunk=chunk)
+    torch.cuda.synchronize()
+    ro, _ = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S0"],
+                       threads=THREADS)
+    check(tag, o, st, inp, ro, tau)
+
+
+def test_chunk_fwd_frozen_state_varlen():
+    lens = [70, 0, 130, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    inp = frozen(gi.chunk_inputs(1, cu[-1], 2, 128, 128, "bf16", s0_std=0.5, seed=72,
+                                 cu_seqlens=cu))
+    say("chunk_fwd varlen: launch")
+    o, st = gdn.chunk_fwd(*(dev(inp[n]) for n in ("q", "k", "v", "log_alpha", "beta", "S0")),
+                          dev(inp["cu_seqlens"]))
+    torch.cuda.synchronize()
+    ro, _ = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S0"],
+                       inp["cu_seqlens"], threads=THREADS)
+    check("chunk_fwd varlen", o, st, inp, ro, 2e-2)
+
+
+def test_kda_fwd_frozen_state():
+    inp = frozen(gi.kda_inputs(2, 150, 3, 128, 128, "bf16", s0_std=0.5, seed=73))
+    say("kda_fwd: launch")
+    o, st = gdn.kda_fwd(*(dev(inp[n]) for n in ("q", "k", "v", "log_alpha", "beta", "S0")))
+    torch.cuda.synchronize()
+    ro, _ = oracle.kda_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                           inp["S0"], threads=THREADS)
+    check("kda_fwd", o, st, inp, ro, 1e-3)
+
+
+def test_gdn2_fwd_frozen_state():
+    inp = frozen(gi.gdn2_inputs(2, 150, 3, 128, 128, "bf16", s0_std=0.5, seed=74))
+    say("gdn2_fwd: launch")
+    o, st = gdn.gdn2_fwd(*(dev(inp[n]) for n in ("q", "k", "v", "log_alpha", "erase", "write",
+                                                 "S0")))
+    torch.cuda.synchronize()
+    ro, _ = oracle.gdn2_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["erase"],
+                            inp["write"], inp["S0"], threads=THREADS)
+    check("gdn2_fwd", o, st, inp, ro, 1e-3)
+
+
+def test_step_frozen_state():
+    rng = np.random.default_rng(75)
+    B, H, d = 3, 4, 128
+    k = rng.standard_normal((B, H, d))
+    q = torch.from_numpy(rng.standard_normal((B, H, d))).to(torch.bfloat16)
+    kk = torch.from_numpy(k / np.linalg.norm(k, axis=-1, keepdims=True)).to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((B, H, d))).to(torch.bfloat16)
+    zeros = torch.zeros((B, H), dtype=torch.float32)
+    S0 = torch.from_numpy(rng.standard_normal((B, H, d, d)) * 0.5).float()
+    S = dev(S0).clone()
+    say("step: launch")
+    o = gdn.step(dev(q), dev(kk), dev(v), dev(zeros), dev(zeros), S)
+    torch.cuda.synchronize()
+    assert torch.equal(S.cpu(), S0), "step: S differs from S0"
+    want = np.einsum("bhvk,bhk->bhv", S0.double().numpy(), q.double().numpy())
+    err = gi.max_rel_err(o.cpu(), want)
+    say(f"step o vs S0 q: max err / RMS = {err:.3e} (bar 1e-4)")
+    assert err <= 1e-4
