@@ -189,3 +189,71 @@ def test_pure_decay_matches_closed_form(which):
         err = gi.max_rel_err(got.cpu(), want)
         say(f"{which} pure decay {name}: max err / RMS = {err:.3e} (bar {tau:g})")
         assert err <= tau, f"{which} pure decay {name}: {err:.3e} > {tau:g}"
+
+
+def overwrite_inputs(which, B, T, H, d, seed):
+    """alpha = 1, beta = 1 (GDN-2: erase = write = 1) and keys that are
+    distinct basis vectors e_j of the key space: each token replaces column j
+    of the state by its value, S <- S (I - e_j e_j^T) + v e_j^T (the delta
+    rule's exact overwrite).  Returns the inputs and the basis index of every
+    token, [B, T, H]."""
+    rng = np.random.default_rng(seed)
+    idx = np.stack([np.stack([rng.permutation(d)[:T] for _ in range(H)], axis=-1)
+                    for _ in range(B)])                       # [B, T, H]
+    k = np.zeros((B, T, H, d))
+    np.put_along_axis(k, idx[..., None], 1.0, axis=-1)
+    bf = torch.bfloat16
+    inp = dict(q=torch.from_numpy(rng.standard_normal((B, T, H, d))).to(bf),
+               k=torch.from_numpy(k).to(bf),
+               v=torch.from_numpy(rng.standard_normal((B, T, H, d))).to(bf),
+               S0=torch.from_numpy(rng.standard_normal((B, H, d, d)) * 0.5).float(),
+               cu_seqlens=None)
+    if which == "chunk":
+        inp["log_alpha"] = torch.zeros((B, T, H))
+        inp["beta"] = torch.ones((B, T, H))
+    else:
+        inp["log_alpha"] = torch.zeros((B, T, H, d))
+        if which == "kda":
+            inp["beta"] = torch.ones((B, T, H))
+        else:
+            inp["erase"] = torch.ones((B, T, H, d))
+            inp["write"] = torch.ones((B, T, H, d))
+    return inp, idx
+
+
+def overwritten(inp, idx):
+    """Token by token in fp64: column idx[t] of S becomes v_t; o_t = S_t q_t."""
+    q = inp["q"].double().numpy()
+    v = inp["v"].double().numpy()
+    S = inp["S0"].double().numpy().copy()
+    B, T, H, _ = q.shape
+    o = np.zeros(v.shape)
+    for t in range(T):
+        for b in range(B):
+            for h in range(H):
+                S[b, h, :, idx[b, t, h]] = v[b, t, h]
+                o[b, t, h] = S[b, h] @ q[b, t, h]
+    return o, S
+
+
+@pytest.mark.parametrize("which,d,T,tau", [("chunk", 128, 100, 2e-2), ("chunk", 64, 60, 2e-2),
+                                           ("kda", 128, 100, 1e-3), ("gdn2", 128, 100, 1e-3)])
+def test_exact_overwrite_with_basis_keys(which, d, T, tau):
+    # The scalar-gate chunk kernel forms K S^T from the hi (bf16) part of the
+    # state only, so an overwritten column keeps its old lo part, about 2^-9
+    # of |S0|: some 1e-2 of RMS at most, inside that path's bar.  The KDA and
+    # GDN-2 launches carry every operand as a hi + lo pair (near 1e-5).
+    inp, idx = overwrite_inputs(which, 2, T, 2, d, seed=79 + d)
+    if which == "gdn2":
+        args, fwd = ("q", "k", "v", "log_alpha", "erase", "write", "S0"), gdn.gdn2_fwd
+    else:
+        args = ("q", "k", "v", "log_alpha", "beta", "S0")
+        fwd = gdn.chunk_fwd if which == "chunk" else gdn.kda_fwd
+    say(f"{which} exact overwrite d={d} T={T}: launch")
+    o, st = fwd(*(dev(inp[n]) for n in args))
+    torch.cuda.synchronize()
+    want_o, want_s = overwritten(inp, idx)
+    for name, got, want in (("o", o, want_o), ("S_T", st, want_s)):
+        err = gi.max_rel_err(got.cpu(), want)
+        say(f"{which} exact overwrite {name}: max err / RMS = {err:.3e} (bar {tau:g})")
+        assert err <= tau, f"{which} exact overwrite {name}: {err:.3e} > {tau:g}"
