@@ -257,3 +257,53 @@ def test_exact_overwrite_with_basis_keys(which, d, T, tau):
         err = gi.max_rel_err(got.cpu(), want)
         say(f"{which} exact overwrite {name}: max err / RMS = {err:.3e} (bar {tau:g})")
         assert err <= tau, f"{which} exact overwrite {name}: {err:.3e} > {tau:g}"
+
+
+def frozen_grads(inp, dO, dS_T):
+    """Gradients of <dO, o> + <dS_T, S_T> at alpha = 1, beta = 0, in fp64.
+    There o_t = S0 q_t and S_T = S0, so dq_t = S0^T dO_t, dS0 = sum_t dO_t
+    q_t^T + dS_T, and every path to k or v carries a factor beta: dk = dv =
+    0.  d log alpha_s scales S_t for t >= s: dla_s = sum_{t>=s} <dO_t, o_t>
+    + <dS_T, S0>.  d beta_s adds (v_s - S0 k_s) k_s^T to every later state:
+    dbeta_s = sum_{t>=s} (dO_t . u_s)(k_s . q_t) + u_s^T dS_T k_s with
+    u_s = v_s - S0 k_s."""
+    q, k, v = (inp[n].double().numpy() for n in ("q", "k", "v"))
+    S0 = inp["S0"].double().numpy()
+    dO = dO.double().numpy()
+    dST = dS_T.double().numpy()
+    o = np.einsum("bhvk,bthk->bthv", S0, q)
+    dq = np.einsum("bhvk,bthv->bthk", S0, dO)
+    dS0 = np.einsum("bthv,bthk->bhvk", dO, q) + dST
+    c = np.einsum("bthv,bthv->bth", dO, o)                       # <dO_t, o_t>
+    tail = np.flip(np.cumsum(np.flip(c, 1), 1), 1)              # sum over t >= s
+    dla = tail + np.einsum("bhvk,bhvk->bh", dST, S0)[:, None, :]
+    u = v - np.einsum("bhvk,bshk->bshv", S0, k)                  # u_s
+    du = np.einsum("bthv,bshv->bsth", dO, u)                     # dO_t . u_s  [b, s, t, h]
+    kq = np.einsum("bshk,bthk->bsth", k, q)                      # k_s . q_t
+    T = q.shape[1]
+    later = np.triu(np.ones((T, T)))[None, :, :, None]           # t >= s
+    dbeta = (du * kq * later).sum(2) + np.einsum("bshv,bhvk,bshk->bsh", u, dST, k)
+    return dq, dla, dbeta, dS0
+
+
+def test_bwd_frozen_state_closed_form():
+    B, T, H, d = 2, 150, 2, 128
+    inp = frozen(gi.chunk_inputs(B, T, H, d, d, "bf16", s0_std=0.5, seed=83))
+    rng = np.random.default_rng(84)
+    dO = torch.from_numpy(rng.standard_normal((B, T, H, d))).float()
+    dS_T = torch.from_numpy(rng.standard_normal((B, H, d, d)) * 0.1).float()
+    say(f"chunk_bwd alpha=1 beta=0 B={B} T={T} H={H} d={d}: launch")
+    g = gdn.chunk_bwd(*(dev(inp[n]) for n in ("q", "k", "v", "log_alpha", "beta")), dev(dO),
+                      S0=dev(inp["S0"]), dS_T=dev(dS_T))
+    torch.cuda.synchronize()
+    dq, dk, dv, dla, dbeta, dS0 = (x.cpu() for x in g)
+    want = dict(zip(("dq", "dlog_alpha", "dbeta", "dS0"), frozen_grads(inp, dO, dS_T)))
+    for name, got in (("dq", dq), ("dlog_alpha", dla), ("dbeta", dbeta), ("dS0", dS0)):
+        err = gi.max_rel_err(got, want[name])
+        say(f"bwd frozen {name}: max err / RMS = {err:.3e} (bar 1e-3)")
+        assert err <= 1e-3, f"bwd frozen {name}: {err:.3e} > 1e-3"
+    scale = float(np.sqrt(np.mean(want["dq"] ** 2)))
+    for name, got in (("dk", dk), ("dv", dv)):
+        m = float(got.abs().max())
+        say(f"bwd frozen {name}: max |x| = {m:.3e} (zero expected)")
+        assert m <= 1e-6 * scale, f"bwd frozen {name}: {m:.3e} is not zero"
